@@ -1,0 +1,178 @@
+"""Quantize, pack, score and reconstruct (oracle side).
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+Each function follows one stage of the method in the pages' order.  All
+arithmetic is float64; the two decisions that produce integers (the stage-1
+code and the QJL sign) are taken on the float32 rounding of the float64
+value, the precision in which the library takes them.
+
+Stages (page, section):
+
+1. norm and direction: the length of the vector is kept at higher precision
+   and only its direction is quantized ("TurboQuant tutorial", Cartesian to
+   polar part of the PolarQuant section).  n = ||k||, u = k / n (u = 0 when
+   n = 0, so the pipeline runs literally on a zero key).
+2. rotation: z = Pi u ("TurboQuant digest" section 2; "TurboQuant tutorial",
+   PolarQuant 4-D example).
+3. scalar quantization: each z_j becomes the nearest allowed value; the
+   index is the number of thresholds t_i <= z_j (a tie goes to the upper
+   cell) ("TurboQuant tutorial", QJL section, first paragraph).
+4. residual: r = z - c[idx], rho = ||r|| ("TurboQuant tutorial", QJL step 1).
+5. Gaussian projection and 1-bit signs: p = G r, beta_j = 1 iff p_j > 0
+   ("TurboQuant tutorial", QJL steps 1-2: positive -> 1, negative -> 0;
+   p_j = 0 gives 0).
+6. asymmetric score of a full-precision query q against the stored key:
+   v = Pi q, w = G v (= S q with S = G Pi), and
+       s = n * ( <v, c[idx]> + rho * sqrt(pi/2) / d * <w, 2 beta - 1> )
+   ("TurboQuant digest" section 2 and "TurboQuant deep review", error
+   compensation section: 1-bit residual signs combined with a high-precision
+   query give an estimate with zero bias; the constant sqrt(pi/2)/d is what
+   makes it unbiased: E[x sign(y)] = sqrt(2/pi) Cov(x, y) / sd(y)).
+7. stage-1 reconstruction: k_hat = n * Pi^T c[idx] ("TurboQuant tutorial",
+   end of the polar part: codes plus the kept length map back to a vector).
+
+Packed layout (bit planes): ``codes[n][B][W]`` and ``signs[n][W]`` as
+uint32 with W = ceil(d / 32); bit p of the index of coordinate j is bit
+(j mod 32) of word (j div 32) of plane p (LSB first); padding bits are 0.
+"""
+from dataclasses import dataclass
+
+import numpy as np
+
+from .params import Params
+
+QJL_CONST = np.sqrt(np.pi / 2.0)
+
+
+@dataclass
+class Quantized:
+    """Unpacked quantizer output for n keys plus the pre-decision values."""
+    idx: np.ndarray      # (n, d) int64 codebook indices
+    beta: np.ndarray     # (n, d) bool QJL sign bits
+    norms: np.ndarray    # (n,) float64, ||k||
+    rnorms: np.ndarray   # (n,) float64, ||r||
+    z: np.ndarray        # (n, d) float64 rotated unit-vector coordinates
+    p: np.ndarray        # (n, d) float64 projected residual
+
+
+def normalize(keys):
+    """Stage 1: (norms, unit directions); zero keys give a zero direction."""
+    k = np.asarray(keys, dtype=np.float64)
+    norms = np.sqrt(np.sum(k * k, axis=1))
+    safe = np.where(norms > 0.0, norms, 1.0)
+    u = np.where((norms > 0.0)[:, None], k / safe[:, None], 0.0)
+    return norms, u
+
+
+def rotate(params: Params, u):
+    """Stage 2: z = Pi u for each row u."""
+    return u @ params.pi.T
+
+
+def bucketize(params: Params, z):
+    """Stage 3: index = #{i : t_i <= fp32(z)} (upper cell on a tie)."""
+    z32 = np.asarray(z, dtype=np.float64).astype(np.float32).astype(np.float64)
+    return np.searchsorted(params.thresholds, z32, side="right").astype(np.int64)
+
+
+def residual(params: Params, z, idx):
+    """Stage 4: r = z - c[idx] and its norm."""
+    r = z - params.centroids[idx]
+    return r, np.sqrt(np.sum(r * r, axis=1))
+
+
+def project_signs(params: Params, r):
+    """Stage 5: p = G r and beta = [fp32(p) > 0]."""
+    p = r @ params.g.T
+    beta = p.astype(np.float32) > 0
+    return p, beta
+
+
+def quantize(params: Params, keys):
+    """Stages 1-5 for a batch of keys of shape (n, d)."""
+    keys = np.asarray(keys, dtype=np.float64)
+    assert keys.ndim == 2 and keys.shape[1] == params.d
+    norms, u = normalize(keys)
+    z = rotate(params, u)
+    idx = bucketize(params, z)
+    r, rnorms = residual(params, z, idx)
+    p, beta = project_signs(params, r)
+    return Quantized(idx, beta, norms, rnorms, z, p)
+
+
+def query_transform(params: Params, queries):
+    """Stage 6, query side: v = Pi q and w = G v for each row q."""
+    q = np.asarray(queries, dtype=np.float64)
+    v = q @ params.pi.T
+    w = v @ params.g.T
+    return v, w
+
+
+def scores(params: Params, queries, idx, beta, norms, rnorms):
+    """Stage 6: (m, n) matrix of estimates <q_a, k_hat_b>."""
+    v, w = query_transform(params, queries)
+    chat = params.centroids[np.asarray(idx)]                  # (n, d)
+    signs = np.where(np.asarray(beta), 1.0, -1.0)             # (n, d)
+    stage1 = v @ chat.T                                       # (m, n)
+    qjl = w @ signs.T                                         # (m, n)
+    scale = np.asarray(rnorms, dtype=np.float64) * QJL_CONST / params.d
+    return np.asarray(norms, dtype=np.float64)[None, :] * (stage1 + scale[None, :] * qjl)
+
+
+def dequant_mse(params: Params, idx, norms):
+    """Stage 7: k_hat = n * Pi^T c[idx] for each key."""
+    chat = params.centroids[np.asarray(idx)]
+    return np.asarray(norms, dtype=np.float64)[:, None] * (chat @ params.pi)
+
+
+# ----------------------------------------------------------------------------
+# bit-plane packing
+# ----------------------------------------------------------------------------
+
+def words_per_plane(d):
+    return (d + 31) // 32
+
+
+def pack_bits(bits):
+    """(n, d) bool -> (n, W) uint32, coordinate j at word j//32, bit j%32."""
+    bits = np.asarray(bits, dtype=bool)
+    n, d = bits.shape
+    w = words_per_plane(d)
+    padded = np.zeros((n, w * 32), dtype=np.uint64)
+    padded[:, :d] = bits
+    weights = np.uint64(1) << np.arange(32, dtype=np.uint64)
+    words = (padded.reshape(n, w, 32) * weights[None, None, :]).sum(axis=2)
+    return words.astype(np.uint32)
+
+
+def unpack_bits(words, d):
+    """(n, W) uint32 -> (n, d) bool (inverse of pack_bits)."""
+    words = np.asarray(words, dtype=np.uint32)
+    n, w = words.shape
+    shifts = np.arange(32, dtype=np.uint32)
+    bits = (words[:, :, None] >> shifts[None, None, :]) & np.uint32(1)
+    return bits.reshape(n, w * 32)[:, :d].astype(bool)
+
+
+def pack_codes(idx, code_bits):
+    """(n, d) indices -> (n, B, W) uint32 bit planes (plane p = bit p)."""
+    idx = np.asarray(idx, dtype=np.int64)
+    planes = [pack_bits((idx >> p) & 1) for p in range(code_bits)]
+    return np.stack(planes, axis=1)
+
+
+def unpack_codes(codes, d):
+    """(n, B, W) uint32 -> (n, d) indices."""
+    codes = np.asarray(codes, dtype=np.uint32)
+    n, b, _ = codes.shape
+    idx = np.zeros((n, d), dtype=np.int64)
+    for p in range(b):
+        idx |= unpack_bits(codes[:, p, :], d).astype(np.int64) << p
+    return idx
+
+
+def pack(params: Params, qz: Quantized):
+    """Packed buffers (codes, signs, norms fp32, rnorms fp32) of a batch."""
+    return (pack_codes(qz.idx, params.code_bits), pack_bits(qz.beta),
+            qz.norms.astype(np.float32), qz.rnorms.astype(np.float32))

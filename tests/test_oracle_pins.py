@@ -1,0 +1,399 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself.
+
+Each test names the part of the oracle it pins and the source of the
+expected value: a worked example printed on the pages, a published table, a
+closed form, an invariant or brute force.  A plausible slip in the oracle (a
+dropped term, a wrong sign, a transposed operand, a wrong index) fails at
+least one of them.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy import integrate, stats
+
+from oracle import params as P
+from oracle import rng
+from oracle import tq
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# generator
+# ---------------------------------------------------------------------------
+
+def test_splitmix64_reference_outputs():
+    """fmix64 + counter match the published SplitMix64 outputs for state 0."""
+    g = _golden("splitmix64_seed0.json")
+    out = rng.splitmix64_sequence(g["state"], len(g["first_outputs_hex"]))
+    assert [int(x) for x in out] == [int(h, 16) for h in g["first_outputs_hex"]]
+
+
+def test_normals_are_standard_normal():
+    """Box-Muller pairs: both the cosine and the sine halves are N(0, 1)."""
+    x = rng.normals(7, 0, 200000)
+    for half in (x[0::2], x[1::2]):
+        assert stats.kstest(half, "norm").pvalue > 1e-3
+    # the two members of a pair are uncorrelated
+    assert abs(np.corrcoef(x[0::2], x[1::2])[0, 1]) < 0.02
+
+
+def test_normals_counter_based_prefix_and_streams():
+    a = rng.normals(3, 1, 1001)
+    assert np.array_equal(a[:500], rng.normals(3, 1, 500))
+    b = rng.normals(3, 0, 1001)
+    assert not np.allclose(a, b)
+    assert abs(np.corrcoef(a, b)[0, 1]) < 0.1
+
+
+# ---------------------------------------------------------------------------
+# rotation (Haar)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [4, 33, 128])
+def test_rotation_is_orthogonal(d):
+    """P1: Pi Pi^T = I and ||Pi x|| = ||x|| (float32-rounded Pi)."""
+    pr = P.init(d, 3, 11)
+    assert np.max(np.abs(pr.pi @ pr.pi.T - np.eye(d))) <= 1e-6
+    x = np.random.default_rng(0).standard_normal((16, d))
+    ratio = np.linalg.norm(x @ pr.pi.T, axis=1) / np.linalg.norm(x, axis=1)
+    assert np.max(np.abs(ratio - 1.0)) <= 1e-6
+
+
+def test_pages_4d_rotation_example():
+    """P2: the pages' 4-D example, rotating a one-axis vector to [5,5,5,5]."""
+    g = _golden("polarquant_4d_example.json")
+    q = np.array(g["rotation"])
+    x = np.array(g["input"])
+    assert np.max(np.abs(q @ q.T - np.eye(4))) == 0.0
+    pr = P.explicit(4, 3, q, np.eye(4))
+    norms, u = tq.normalize(x[None, :])
+    z = tq.rotate(pr, u)
+    assert norms[0] == 10.0
+    assert np.array_equal(norms[0] * z[0], np.array(g["expected"]))
+
+
+def test_haar_spreads_one_axis_fourth_moment():
+    """P3: sum_j (Pi e1)_j^4 averages 3/(d+2) for a uniform unit vector."""
+    d = 16
+    vals = []
+    for seed in range(300):
+        col = P.haar_rotation(d, seed)[:, 0]
+        vals.append(np.sum(col ** 4))
+    vals = np.array(vals)
+    expect = 3.0 / (d + 2)
+    assert abs(vals.mean() - expect) < 4 * vals.std() / math.sqrt(len(vals))
+
+
+def test_haar_sign_fix_centres_diagonal():
+    """Without the sign fix a QR factor has a biased diagonal; Haar has mean 0."""
+    d = 8
+    diag = np.array([np.diag(P.haar_rotation(d, s)) for s in range(400)])
+    sd = diag.std(axis=0) / math.sqrt(diag.shape[0])
+    assert np.all(np.abs(diag.mean(axis=0)) < 4.5 * sd)
+
+
+def test_rotated_coordinate_marginal_matches_beta_law():
+    """P4: pooled coordinates of Pi u follow f_d (its CDF is a beta CDF)."""
+    d = 12
+    # one coordinate of Pi e_1 per seed: independent draws of f_d
+    z = np.array([P.haar_rotation(d, seed)[seed % d, 0] for seed in range(3000)])
+    assert stats.kstest(z, lambda t: P.sphere_marginal_cdf(t, d)).pvalue > 1e-3
+    # and not merely the large-d normal limit it resembles
+    assert stats.kstest(z * math.sqrt(d), "norm").pvalue < stats.kstest(
+        z, lambda t: P.sphere_marginal_cdf(t, d)).pvalue
+
+
+def test_projection_is_iid_standard_normal():
+    pr = P.init(64, 3, 2)
+    g = pr.g.ravel()
+    assert stats.kstest(g, "norm").pvalue > 1e-3
+    assert not np.allclose(np.abs(pr.g[:4, :4]), np.abs(pr.pi[:4, :4]) * 8)
+
+
+# ---------------------------------------------------------------------------
+# codebook (Lloyd-Max)
+# ---------------------------------------------------------------------------
+
+def _gauss_mse(c):
+    t = np.concatenate(([-np.inf], 0.5 * (c[:-1] + c[1:]), [np.inf]))
+    m0 = stats.norm.cdf(t[1:]) - stats.norm.cdf(t[:-1])
+    m1 = stats.norm.pdf(t[:-1]) - stats.norm.pdf(t[1:])
+    return 1.0 - np.sum(c * (2 * m1 - c * m0))
+
+
+@pytest.mark.parametrize("levels", [2, 4, 8, 16])
+def test_lloyd_max_reproduces_max_1960(levels):
+    """P5: the Lloyd-Max routine on N(0,1) gives Max's published quantizers."""
+    g = _golden("max1960_gaussian.json")
+    row = g["levels"][str(levels)]
+    tol = g["tolerance"]
+    c, _ = P.gaussian_codebook_fp64(levels)
+    pos = c[levels // 2:]
+    assert np.max(np.abs(pos - np.array(row["outputs"]))) <= tol * max(1.0, pos.max())
+    t = 0.5 * (c[:-1] + c[1:])
+    tpos = t[levels // 2:]
+    if row["thresholds"]:
+        assert np.max(np.abs(tpos - np.array(row["thresholds"]))) <= tol * max(1.0, tpos.max())
+    assert abs(_gauss_mse(c) - row["mse"]) <= 2e-4 * max(1.0, row["mse"] * 10)
+
+
+@pytest.mark.parametrize("levels", [2, 4, 8])
+def test_codebook_d3_is_uniform_quantizer(levels):
+    """P5: at d = 3 the marginal is uniform on [-1,1]; Lloyd-Max is uniform."""
+    c, _ = P.sphere_codebook_fp64(3, levels)
+    expect = -1.0 + (2.0 * np.arange(levels) + 1.0) / levels
+    assert np.max(np.abs(c - expect)) < 1e-12
+    assert abs(3 * P.codebook_mse(c, 3) - 4.0 ** -int(math.log2(levels))) < 1e-12
+
+
+def test_codebook_large_d_tends_to_gaussian():
+    """sqrt(d) c(d) tends to the N(0,1) quantizer as d grows."""
+    cg, _ = P.gaussian_codebook_fp64(8)
+    c, _ = P.sphere_codebook_fp64(4096, 8)
+    assert np.max(np.abs(np.sqrt(4096) * c - cg)) < 2e-3
+
+
+@pytest.mark.parametrize("d,levels", [(5, 4), (128, 4), (200, 8), (1536, 8)])
+def test_codebook_fixed_point_by_quadrature(d, levels):
+    """P6: each level is the conditional mean of its cell (independent quad)."""
+    c, _ = P.sphere_codebook_fp64(d, levels)
+    t = np.concatenate(([-1.0], 0.5 * (c[:-1] + c[1:]), [1.0]))
+    s = 1.0 / math.sqrt(d)
+    for i in range(levels):
+        a, b = max(t[i], -40 * s), min(t[i + 1], 40 * s)
+        m0 = integrate.quad(lambda z: P.sphere_marginal_pdf(z, d), a, b, epsabs=0, epsrel=1e-12, limit=200)[0]
+        m1 = integrate.quad(lambda z: z * P.sphere_marginal_pdf(z, d), a, b, epsabs=0, epsrel=1e-12, limit=200)[0]
+        assert abs(m1 / m0 - c[i]) <= 1e-9 * s
+    assert np.array_equal(c, -c[::-1])
+
+
+def test_marginal_pdf_normalised_and_moment_formula():
+    for d in (2, 3, 9, 128):
+        tot = integrate.quad(lambda z: P.sphere_marginal_pdf(z, d), -1, 1, limit=200)[0]
+        assert abs(tot - 1.0) < 1e-8
+        m = integrate.quad(lambda z: z * P.sphere_marginal_pdf(z, d), 0.1, 0.4, limit=200)[0]
+        assert abs(m - P.sphere_marginal_moment(0.1, 0.4, d)) < 1e-12
+        var = integrate.quad(lambda z: z * z * P.sphere_marginal_pdf(z, d), -1, 1, limit=200)[0]
+        assert abs(var - 1.0 / d) < 1e-9
+
+
+def test_mse_falls_about_4x_per_bit_and_within_27x_of_bound():
+    """P7: d*MSE ratios per added bit in [3, 4.2]; d*MSE*4^B <= sqrt(3)pi/2."""
+    d = 128
+    mses = []
+    for b in (1, 2, 3, 4):
+        c, _ = P.sphere_codebook_fp64(d, 1 << b)
+        mses.append(d * P.codebook_mse(c, d))
+    ratios = [mses[i] / mses[i + 1] for i in range(3)]
+    assert all(3.0 <= r <= 4.2 for r in ratios), ratios
+    for b, m in zip((1, 2, 3, 4), mses):
+        assert m * 4.0 ** b <= math.sqrt(3) * math.pi / 2 + 1e-9
+
+
+def test_monte_carlo_mse_matches_closed_form():
+    """P7: the quantizer's empirical MSE on rotated keys equals the formula."""
+    pr = P.init(64, 3, 4)
+    keys = np.random.default_rng(1).standard_normal((20000, 64))
+    qz = tq.quantize(pr, keys)
+    emp = np.mean(qz.rnorms ** 2)          # = d * per-coordinate MSE
+    c = pr.centroids
+    assert abs(emp - 64 * P.codebook_mse(c, 64)) / emp < 0.015
+
+
+def test_thresholds_are_midpoints_and_ties_go_up():
+    pr = P.init(16, 4, 0)
+    c = pr.centroids
+    assert np.array_equal(pr.thresholds, (0.5 * (c[:-1] + c[1:])).astype(np.float32).astype(np.float64))
+    z = pr.thresholds[None, :]
+    assert np.array_equal(tq.bucketize(pr, z)[0], np.arange(1, len(c)))
+    assert tq.bucketize(pr, np.array([[-0.9999]]))[0, 0] == 0
+    assert tq.bucketize(pr, np.array([[0.9999]]))[0, 0] == len(c) - 1
+
+
+def test_bit_split():
+    """2-bit stage + 1 QJL bit = 3 bits; 3-bit stage + 1 = 4 bits."""
+    assert P.init(8, 3, 0).levels == 4
+    assert P.init(8, 4, 0).levels == 8
+    assert P.init(8, 3, 0).code_bits == 2
+
+
+# ---------------------------------------------------------------------------
+# quantize / residual / signs
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,bits", [(2, 2), (3, 3), (5, 3), (8, 2)])
+def test_brute_force_nearest_codeword(d, bits):
+    """P11: per-coordinate bucketize = global argmin over all (2^B)^d words."""
+    pr = P.init(d, bits, 9)
+    keys = np.random.default_rng(d).standard_normal((20, d))
+    qz = tq.quantize(pr, keys)
+    words = np.array(list(itertools.product(pr.centroids, repeat=d)))
+    for i in range(len(keys)):
+        dist = np.sum((words - qz.z[i][None, :]) ** 2, axis=1)
+        best = words[np.argmin(dist)]
+        assert np.array_equal(pr.centroids[qz.idx[i]], best)
+
+
+def test_sign_convention():
+    """Positive projection -> 1, negative -> 0, exactly zero -> 0."""
+    pr = P.explicit(3, 2, np.eye(3), np.eye(3))
+    r = np.array([[0.25, -0.25, 0.0]])
+    p, beta = tq.project_signs(pr, r)
+    assert beta.tolist() == [[True, False, False]]
+
+
+@pytest.mark.parametrize("d,bits", [(7, 3), (128, 3), (200, 4)])
+def test_isometry_identities(d, bits):
+    """P8: ||u - Pi^T c[idx]|| = rho and ||k - k_hat|| = n rho."""
+    pr = P.init(d, bits, 3)
+    keys = np.random.default_rng(2).standard_normal((50, d)) * 3.0
+    qz = tq.quantize(pr, keys)
+    norms, u = tq.normalize(keys)
+    recon_u = pr.centroids[qz.idx] @ pr.pi
+    # Pi is float32-rounded, orthogonal to ~1e-7: the identity holds to that
+    assert np.max(np.abs(np.linalg.norm(u - recon_u, axis=1) - qz.rnorms)) < 1e-6
+    khat = tq.dequant_mse(pr, qz.idx, qz.norms)
+    err = np.linalg.norm(keys - khat, axis=1)
+    assert np.max(np.abs(err - qz.norms * qz.rnorms) / qz.norms) < 1e-6
+    # with an exactly orthogonal rotation the identities are exact
+    q, _ = np.linalg.qr(np.random.default_rng(4).standard_normal((d, d)))
+    pe = P.Params(d, bits, 0, q, pr.g, pr.centroids, pr.thresholds)
+    qe = tq.quantize(pe, keys)
+    recon = pe.centroids[qe.idx] @ pe.pi
+    assert np.max(np.abs(np.linalg.norm(u - recon, axis=1) - qe.rnorms)) < 1e-12
+
+
+def test_zero_key_runs_literally():
+    pr = P.init(16, 3, 0)
+    keys = np.zeros((1, 16))
+    qz = tq.quantize(pr, keys)
+    assert qz.norms[0] == 0.0
+    # z = 0 sits on the middle threshold: upper cell
+    assert np.all(qz.idx == len(pr.centroids) // 2)
+    assert np.all(tq.dequant_mse(pr, qz.idx, qz.norms) == 0.0)
+    s = tq.scores(pr, np.ones((2, 16)), qz.idx, qz.beta, qz.norms, qz.rnorms)
+    assert np.all(s == 0.0)
+
+
+def test_scale_invariance():
+    """P12: k -> 2^e k leaves codes, signs, rho identical; n scales exactly."""
+    pr = P.init(64, 4, 1)
+    keys = np.random.default_rng(3).standard_normal((40, 64))
+    a = tq.quantize(pr, keys)
+    b = tq.quantize(pr, keys * 8.0)
+    assert np.array_equal(a.idx, b.idx) and np.array_equal(a.beta, b.beta)
+    assert np.array_equal(a.rnorms, b.rnorms)
+    assert np.array_equal(a.norms * 8.0, b.norms)
+
+
+# ---------------------------------------------------------------------------
+# estimator
+# ---------------------------------------------------------------------------
+
+def test_estimator_equals_dense_formula():
+    """P11: s = <q, n Pi^T (c[idx] + rho sqrt(pi/2)/d G^T (2 beta - 1))>."""
+    d = 6
+    pr = P.init(d, 3, 5)
+    rs = np.random.default_rng(6)
+    keys = rs.standard_normal((9, d))
+    qs = rs.standard_normal((4, d))
+    qz = tq.quantize(pr, keys)
+    s = tq.scores(pr, qs, qz.idx, qz.beta, qz.norms, qz.rnorms)
+    for a in range(4):
+        for b in range(9):
+            sg = np.where(qz.beta[b], 1.0, -1.0)
+            corr = qz.rnorms[b] * math.sqrt(math.pi / 2) / d * (pr.g.T @ sg)
+            khat = qz.norms[b] * (pr.pi.T @ (pr.centroids[qz.idx[b]] + corr))
+            assert abs(s[a, b] - qs[a] @ khat) < 1e-12 * max(1.0, abs(s[a, b]))
+
+
+def test_estimator_linear_in_query():
+    """P13."""
+    pr = P.init(32, 3, 2)
+    rs = np.random.default_rng(7)
+    keys = rs.standard_normal((10, 32))
+    q1, q2 = rs.standard_normal((2, 32))
+    qz = tq.quantize(pr, keys)
+    f = lambda q: tq.scores(pr, q[None, :], qz.idx, qz.beta, qz.norms, qz.rnorms)[0]
+    assert np.allclose(f(2.5 * q1), 2.5 * f(q1), rtol=1e-12, atol=1e-12)
+    assert np.allclose(f(q1 + q2), f(q1) + f(q2), rtol=1e-12, atol=1e-12)
+
+
+def test_qjl_correction_unbiased_over_projections():
+    """P9: averaged over Gaussian G, rho sqrt(pi/2)/d <G v, sign(G r)> -> <v, r>.
+
+    Pi and the key are fixed; only G varies.  The spread also matches the
+    closed-form variance ((pi/2) |v|^2 rho^2 - <v,r>^2) / d.
+    """
+    d = 48
+    base = P.init(d, 3, 0)
+    rs = np.random.default_rng(8)
+    key = rs.standard_normal((1, d))
+    q = rs.standard_normal((1, d))
+    qz0 = tq.quantize(base, key)
+    norms, u = tq.normalize(key)
+    z = tq.rotate(base, u)
+    r, rho = tq.residual(base, z, qz0.idx)
+    v, _ = tq.query_transform(base, q)
+    target = float(v[0] @ r[0])
+    trials = 6000
+    est = np.empty(trials)
+    for t in range(trials):
+        g = rs.standard_normal((d, d))
+        pr = P.Params(d, 3, 0, base.pi, g, base.centroids, base.thresholds)
+        qz = tq.quantize(pr, key)
+        s = tq.scores(pr, q, qz.idx, qz.beta, qz.norms, qz.rnorms)[0, 0]
+        stage1 = qz.norms[0] * float(v[0] @ pr.centroids[qz.idx[0]])
+        est[t] = (s - stage1) / qz.norms[0]
+    sem = est.std() / math.sqrt(trials)
+    assert abs(est.mean() - target) < 4 * sem
+    var_cf = (math.pi / 2 * float(v[0] @ v[0]) * rho[0] ** 2 - target ** 2) / d
+    assert abs(est.var() / var_cf - 1.0) < 0.08
+
+
+def test_full_estimator_unbiased_over_seeds():
+    """P10: averaged over seeds of (Pi, G), the score estimates <q, k>."""
+    d = 24
+    rs = np.random.default_rng(9)
+    key = rs.standard_normal((1, d))
+    q = rs.standard_normal((1, d))
+    est = np.array([tq.scores(pr, q, *(lambda z: (z.idx, z.beta, z.norms, z.rnorms))(tq.quantize(pr, key)))[0, 0]
+                    for pr in (P.init(d, 2, s) for s in range(1500))])
+    sem = est.std() / math.sqrt(len(est))
+    assert abs(est.mean() - float(q[0] @ key[0])) < 4 * sem
+
+
+# ---------------------------------------------------------------------------
+# packing
+# ---------------------------------------------------------------------------
+
+def test_pack_bit_positions():
+    bits = np.zeros((1, 70), dtype=bool)
+    bits[0, [0, 5, 31, 32, 69]] = True
+    w = tq.pack_bits(bits)
+    assert w.shape == (1, 3)
+    assert w[0, 0] == (1 | (1 << 5) | (1 << 31))
+    assert w[0, 1] == 1
+    assert w[0, 2] == (1 << 5)           # coordinate 69 = word 2, bit 5; padding 0
+
+
+def test_pack_round_trip():
+    rs = np.random.default_rng(1)
+    idx = rs.integers(0, 8, (13, 77))
+    codes = tq.pack_codes(idx, 3)
+    assert codes.shape == (13, 3, 3)
+    assert np.array_equal(tq.unpack_codes(codes, 77), idx)
+    # plane p holds bit p of the index
+    assert np.array_equal(tq.unpack_bits(codes[:, 1, :], 77), ((idx >> 1) & 1).astype(bool))
+    beta = rs.random((13, 77)) > 0.5
+    assert np.array_equal(tq.unpack_bits(tq.pack_bits(beta), 77), beta)
