@@ -1,0 +1,175 @@
+/*
+ * tq.h - C ABI of libtq, a gfx950 (AMD Instinct MI355X) implementation of the
+ * TurboQuant quantize / score path.
+ *
+ * The method (sources are web pages about TurboQuant, cited by title and
+ * section):
+ *   - "TurboQuant digest" (juejin.cn), section 2: a key is randomly rotated so
+ *     that a scalar quantizer suits every coordinate; this stage spends most
+ *     of the bits.  About one more bit per coordinate is a QJL sign sketch of
+ *     the residual, read back by an asymmetric estimator that pairs the
+ *     low-bit key with a high-precision query.
+ *   - "TurboQuant tutorial" (gitcode.csdn.net), sections PolarQuant and QJL:
+ *     the length is kept at higher precision; each rotated coordinate is
+ *     replaced by the nearest allowed value; the residual is multiplied by a
+ *     Gaussian JL matrix with as many outputs as inputs and only the signs
+ *     are kept (positive -> 1, negative -> 0); a 2-bit (3-bit) first stage
+ *     makes 3 (4) bits in all, one of them the QJL bit.
+ *   - "TurboQuant deep review" (freelamp.com), breakthrough and error
+ *     compensation sections: random orthogonal preconditioning, no per-block
+ *     scale constants, and a zero-bias estimate of the attention score.
+ *
+ * Concretely, with B = bits - 1 codebook bits, L = 2^B levels, a key k in R^d
+ * and W = ceil(d / 32):
+ *   n    = ||k||_2,  u = k / n  (u = 0 when n = 0)
+ *   z    = Pi u                      Pi: d x d Haar rotation from the seed
+ *   idx  = #{ i : t_i <= z_j }       t: L-1 float32 thresholds (midpoints of
+ *                                    the float32 Lloyd-Max levels c for the
+ *                                    law of one coordinate of a uniform unit
+ *                                    vector in R^d)
+ *   r    = z - c[idx],  rho = ||r||_2
+ *   p    = G r,  beta_j = [p_j > 0]  G: d x d iid N(0,1) from the seed
+ *   score(q) = n * ( <Pi q, c[idx]> + rho * sqrt(pi/2) / d * <G Pi q, 2 beta - 1> )
+ *   k_hat    = n * Pi^T c[idx]       (stage-1 reconstruction)
+ *
+ * Seeded draws: SplitMix64 (Steele, Lea & Flood 2014) with golden gamma
+ * g = 0x9E3779B97F4A7C15.  Stream s (0 = Pi, 1 = G) of seed x starts from
+ * state fmix(x + (s+1) g); its counter c (0-based) is fmix(state + (c+1) g).
+ * Normal pair i of a stream uses counters 2i, 2i+1 in Box-Muller form
+ * (u1 = ((a>>11)+1) 2^-53, u2 = (b>>11) 2^-53, R = sqrt(-2 ln u1); element
+ * 2i = R cos(2 pi u2), 2i+1 = R sin(2 pi u2)), filling a d x d matrix in row
+ * order.  Pi = Q diag(sign(diag R)) from the Householder QR of the stream-0
+ * matrix, in float64, then rounded to float32; G is the stream-1 matrix
+ * rounded to float32.
+ *
+ * Packed layout (format version 1), all arrays dense and 4-byte aligned:
+ *   codes [n][B][W] uint32   bit p of idx_j at plane p, word j/32, bit j%32
+ *   signs [n][W]    uint32   beta_j at word j/32, bit j%32
+ *   norms [n]       float32  n
+ *   rnorms[n]       float32  rho
+ * Bits past d in the last word are 0.
+ *
+ * Conventions for every entry point:
+ *   - Return 0 (TQ_OK) or a negative TQ_E* code; nothing aborts and no C++
+ *     exception crosses the ABI.  tq_strerror() names a code.
+ *   - "device" pointers are HIP device memory of the device the handle was
+ *     created on (hipGetDevice() at tq_init); "host" pointers are ordinary
+ *     host memory.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Device work is
+ *     enqueued asynchronously on it; launch errors are returned, faults
+ *     surface at the caller's synchronisation.
+ *   - The caller owns every buffer passed in; the library owns only what
+ *     tq_init allocates (the rotation, projection and codebook tables) and
+ *     frees it in tq_destroy.  A handle is read-only after tq_init, so calls
+ *     on different streams may share it.
+ *   - n = 0 (or groups = 0, nq = 0) is a successful no-op.  NaN or Inf in
+ *     inputs gives unspecified codes and scores.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define TQ_API __attribute__((visibility("default")))
+#else
+#define TQ_API
+#endif
+
+#define TQ_OK 0
+#define TQ_EINVAL (-1)       /* bad argument (null pointer, size, range)   */
+#define TQ_EUNSUPPORTED (-2) /* valid but not implemented                  */
+#define TQ_EHIP (-3)         /* a HIP runtime call or kernel launch failed */
+#define TQ_ENOMEM (-4)       /* host or device allocation failed           */
+
+#define TQ_FORMAT_VERSION 1
+
+/* element type of the keys given to tq_quantize */
+#define TQ_F32 0
+#define TQ_BF16 1
+
+typedef struct tq_ctx* tq_handle;
+
+typedef struct {
+  int32_t d;              /* vector dimension                                 */
+  int32_t bits;           /* total bits per coordinate (B + 1)                */
+  int32_t code_bits;      /* B                                                */
+  int32_t levels;         /* L = 2^B                                          */
+  int32_t words;          /* W = ceil(d / 32)                                 */
+  int32_t format_version; /* TQ_FORMAT_VERSION                                */
+  int64_t code_bytes;     /* bytes of codes per key  = 4 B W                  */
+  int64_t sign_bytes;     /* bytes of signs per key  = 4 W                    */
+  int64_t key_bytes;      /* code_bytes + sign_bytes + 8 (norm and rnorm)     */
+} tq_layout;
+
+/* Build the method for (d, bits, seed) on the current HIP device: rotation,
+ * projection and codebook as described above.  2 <= d <= 4096,
+ * 2 <= bits <= 5.  Synchronous.  *out receives the handle. */
+TQ_API int tq_init(int32_t d, int32_t bits, uint64_t seed, tq_handle* out);
+
+/* As tq_init but with caller-given float32 matrices (host, row-major d x d):
+ * `pi` is used as the rotation, `g` as the projection; the codebook still
+ * depends only on (d, bits).  For tests that need a known rotation, e.g. the
+ * tutorial page's 4-D example.  Orthogonality of `pi` is not checked. */
+TQ_API int tq_init_explicit(int32_t d, int32_t bits, const float* pi, const float* g, tq_handle* out);
+
+/* Release the handle and its device tables.  NULL is accepted. */
+TQ_API int tq_destroy(tq_handle h);
+
+/* Sizes of the packed layout for this handle (host struct). */
+TQ_API int tq_get_layout(tq_handle h, tq_layout* out);
+
+/* Host only, no HIP call: the parameters tq_init(d, bits, seed) uses.
+ * pi, g: host float[d*d] row-major (either may be NULL to skip it);
+ * centroids: host float[2^(bits-1)] ascending; thresholds: host
+ * float[2^(bits-1) - 1] ascending (either may be NULL). */
+TQ_API int tq_host_params(int32_t d, int32_t bits, uint64_t seed, float* pi, float* g,
+                   float* centroids, float* thresholds);
+
+/* FNV-1a 64 hash of the handle's float32 Pi, G and centroids (host copies);
+ * equal handles on different processes or GPUs hash equal.  0 on a NULL
+ * handle. */
+TQ_API uint64_t tq_params_hash(tq_handle h);
+
+/* Quantize n keys.  keys: device, n rows of d elements of type key_dtype
+ * (TQ_F32 or TQ_BF16), row i at keys + i*ldk elements (ldk >= d).
+ * Outputs (device): codes [n][B][W], signs [n][W], norms [n], rnorms [n] as
+ * in the packed layout.  Asynchronous on `stream`. */
+TQ_API int tq_quantize(tq_handle h, const void* keys, int32_t key_dtype, int64_t n, int64_t ldk,
+                uint32_t* codes, uint32_t* signs, float* norms, float* rnorms, void* stream);
+
+/* Bytes of device workspace tq_logits needs for `groups` x `nq` queries. */
+TQ_API size_t tq_logits_workspace_size(tq_handle h, int64_t groups, int64_t nq);
+
+/* Asymmetric scores of full-precision queries against packed keys.
+ * queries: device float [groups][nq][d]; the packed arrays hold groups*n keys
+ * ordered [groups][n] (key t of group g is key g*n + t); group g's queries
+ * score only group g's keys (grouped-query attention: the nq query heads
+ * that share one key head form a group).  scores: device float
+ * [groups][nq][n].  workspace: device, at least
+ * tq_logits_workspace_size(h, groups, nq) bytes, 256-byte aligned.  Raw
+ * inner products, no 1/sqrt(d) scaling.  Asynchronous on `stream`. */
+TQ_API int tq_logits(tq_handle h, const float* queries, int64_t groups, int64_t nq,
+              const uint32_t* codes, const uint32_t* signs, const float* norms,
+              const float* rnorms, int64_t n, float* scores, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/* Stage-1 reconstruction k_hat = n * Pi^T c[idx] of n packed keys.
+ * codes, norms: device as in the packed layout; khat: device float [n][d].
+ * Asynchronous on `stream`. */
+TQ_API int tq_dequant_mse(tq_handle h, const uint32_t* codes, const float* norms, int64_t n,
+                   float* khat, void* stream);
+
+/* Static string naming an error code. */
+TQ_API const char* tq_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

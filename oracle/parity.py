@@ -1,0 +1,132 @@
+"""Comparison rules between the library's outputs and the oracle's.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+Rules (all derived from the float32 arithmetic of the library against the
+float64 oracle; the window and the rate come with the method's statement of
+parity):
+
+* codes: bit-exact, except that an index may differ where the oracle's
+  rotated coordinate z_j lies within 1e-6 of a threshold.  Such mismatches
+  are counted and must stay below 1e-5 of all coordinates.
+* signs: bit-exact, except where the oracle's projected residual lies within
+  1e-6 of zero in JL-normalised units, |p_j| / sqrt(d) < 1e-6.  (sign(p) does
+  not depend on the scale of the projection; with the JL normalisation
+  S / sqrt(d) the projected value has the same scale as a rotated
+  coordinate, so the window means the same for both decisions.)  A key whose
+  code changed inside the window has a different residual, so its signs
+  and rho are not compared; such keys are counted.
+* norms: |n_gpu - n| <= d 2^-24 n (float32 sum of d squares, worst case).
+* rnorms: |rho_gpu - rho| <= sqrt(d) 1e-6 + d 2^-24 rho.
+* scores: |s_gpu - s| <= 1e-3 ||q|| n_k per score.
+* stage-1 reconstruction: ||k_hat_gpu - k_hat|| <= 1e-5 ||k_hat|| per key.
+* padding bits past d are zero.
+"""
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from . import tq
+
+CODE_WINDOW = 1e-6
+SIGN_WINDOW = 1e-6
+MISMATCH_RATE = 1e-5
+SCORE_TOL = 1e-3
+DEQUANT_TOL = 1e-5
+
+
+@dataclass
+class QuantizeReport:
+    elements: int = 0
+    code_mismatch: int = 0
+    code_bad: int = 0
+    sign_mismatch: int = 0
+    sign_bad: int = 0
+    cascade_keys: int = 0
+    norm_bad: int = 0
+    rnorm_bad: int = 0
+    padding_bad: int = 0
+    worst: dict = field(default_factory=dict)
+
+    @property
+    def mismatch_rate(self):
+        return (self.code_mismatch + self.sign_mismatch) / max(self.elements, 1)
+
+    def ok(self):
+        return (self.code_bad == 0 and self.sign_bad == 0 and self.norm_bad == 0 and self.rnorm_bad == 0
+                and self.padding_bad == 0 and self.mismatch_rate < MISMATCH_RATE)
+
+    def cascade(self):
+        return self.cascade_keys
+
+
+def _padding_zero(words, d):
+    extra = words.shape[-1] * 32 - d
+    if extra == 0:
+        return 0
+    mask = np.uint32(((1 << extra) - 1) << (32 - extra))
+    return int(np.count_nonzero(words[..., -1].astype(np.uint32) & mask))
+
+
+def compare_quantize(params, qz, codes, signs, norms, rnorms):
+    """qz: oracle ``tq.Quantized``; the rest: library outputs as numpy."""
+    d = params.d
+    codes = np.asarray(codes).view(np.uint32)
+    signs = np.asarray(signs).view(np.uint32)
+    norms = np.asarray(norms, dtype=np.float64)
+    rnorms = np.asarray(rnorms, dtype=np.float64)
+    rep = QuantizeReport(elements=2 * qz.idx.size)
+    rep.padding_bad = _padding_zero(codes, d) + _padding_zero(signs, d)
+
+    idx = tq.unpack_codes(codes, d)
+    cmis = idx != qz.idx
+    dist = np.min(np.abs(qz.z[:, :, None] - params.thresholds[None, None, :]), axis=2) \
+        if len(params.thresholds) else np.full(qz.z.shape, np.inf)
+    rep.code_mismatch = int(cmis.sum())
+    rep.code_bad = int((cmis & (dist >= CODE_WINDOW)).sum())
+    flipped = cmis.any(axis=1)
+    rep.cascade_keys = int(flipped.sum())
+
+    beta = tq.unpack_bits(signs, d)
+    keep = ~flipped
+    smis = (beta != qz.beta) & keep[:, None]
+    pn = np.abs(qz.p) / np.sqrt(d)
+    rep.sign_mismatch = int(smis.sum())
+    rep.sign_bad = int((smis & (pn >= SIGN_WINDOW)).sum())
+
+    ntol = d * 2.0 ** -24 * qz.norms
+    rep.norm_bad = int((np.abs(norms - qz.norms) > ntol).sum())
+    rtol = np.sqrt(d) * 1e-6 + d * 2.0 ** -24 * qz.rnorms
+    rep.rnorm_bad = int(((np.abs(rnorms - qz.rnorms) > rtol) & keep).sum())
+    if rep.code_bad:
+        i = np.argwhere(cmis & (dist >= CODE_WINDOW))[0]
+        rep.worst["code"] = (tuple(int(x) for x in i), float(dist[tuple(i)]))
+    if rep.sign_bad:
+        i = np.argwhere(smis & (pn >= SIGN_WINDOW))[0]
+        rep.worst["sign"] = (tuple(int(x) for x in i), float(pn[tuple(i)]))
+    return rep
+
+
+def score_violations(s_gpu, s_ref, queries, norms, keep=None):
+    """Count of scores outside 1e-3 ||q|| n_k; s arrays are (m, n)."""
+    s_gpu = np.asarray(s_gpu, dtype=np.float64)
+    s_ref = np.asarray(s_ref, dtype=np.float64)
+    qn = np.linalg.norm(np.asarray(queries, dtype=np.float64), axis=1)
+    tol = SCORE_TOL * qn[:, None] * np.asarray(norms, dtype=np.float64)[None, :]
+    bad = np.abs(s_gpu - s_ref) > tol
+    if keep is not None:
+        bad &= np.asarray(keep)[None, :]
+    ratio = np.abs(s_gpu - s_ref) / np.maximum(tol, 1e-300)
+    if keep is not None:
+        ratio = ratio[:, np.asarray(keep)]
+    return int(bad.sum()), float(ratio.max()) if ratio.size else 0.0
+
+
+def dequant_violations(k_gpu, k_ref):
+    k_gpu = np.asarray(k_gpu, dtype=np.float64)
+    k_ref = np.asarray(k_ref, dtype=np.float64)
+    err = np.linalg.norm(k_gpu - k_ref, axis=1)
+    ref = np.linalg.norm(k_ref, axis=1)
+    bad = err > DEQUANT_TOL * ref
+    ratio = err / np.maximum(DEQUANT_TOL * ref, 1e-300)
+    return int(bad.sum()), float(ratio.max()) if ratio.size else 0.0

@@ -1,0 +1,229 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Every case prints what names it before touching the GPU.  Inputs come from
+the seeded generators in ``vector_quantization_quantize_amd.workloads``;
+expected values only from ``oracle``.  Rules: ``oracle.parity``.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import params as P
+from oracle import parity
+from oracle import tq
+
+pytestmark = pytest.mark.gpu
+
+_PARAMS = {}
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import vector_quantization_quantize_amd as tqm
+    from vector_quantization_quantize_amd import workloads as wl
+    return torch, tqm, wl
+
+
+def _params(d, bits, seed=0):
+    key = (d, bits, seed)
+    if key not in _PARAMS:
+        _PARAMS[key] = P.init(d, bits, seed)
+    return _PARAMS[key]
+
+
+def _dev(torch, a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def _packed_to_dev(torch, packed):
+    codes, signs, norms, rnorms = packed
+    return (_dev(torch, codes.view(np.int32)), _dev(torch, signs.view(np.int32)),
+            _dev(torch, norms.astype(np.float32)), _dev(torch, rnorms.astype(np.float32)))
+
+
+def _cpu(t):
+    return t.detach().cpu().numpy()
+
+
+def check_full(env, d, bits, keys, queries, key_dtype="f32", seed=0, h=None, pr=None):
+    """Quantize all keys on both sides; compare codes/signs/norms, scores
+    (decode parity on the oracle's packed keys and end to end), and the
+    stage-1 reconstruction.  keys (groups*n, d); queries (groups, nq, d)."""
+    torch, tqm, _ = env
+    pr = pr or _params(d, bits, seed)
+    h = h or tqm.tq_init(d, bits, seed)
+    groups, nq, _ = queries.shape
+    n = keys.shape[0] // groups
+    kd = _dev(torch, keys, torch.bfloat16 if key_dtype == "bf16" else torch.float32)
+    codes, signs, norms, rnorms = tqm.tq_quantize(h, kd)
+    torch.cuda.synchronize()
+    qz = tq.quantize(pr, keys.astype(np.float64))
+    rep = parity.compare_quantize(pr, qz, _cpu(codes), _cpu(signs), _cpu(norms), _cpu(rnorms))
+    assert rep.ok(), rep
+    # decode parity: the oracle's packed keys through the library's scorer
+    packed = tq.pack(pr, qz)
+    pdev = _packed_to_dev(torch, packed)
+    qd = _dev(torch, queries.astype(np.float32))
+    s_dec = _cpu(tqm.tq_logits(h, qd, *pdev, n=n))
+    s_e2e = _cpu(tqm.tq_logits(h, qd, codes, signs, norms, rnorms, n=n))
+    idx_gpu = tq.unpack_codes(_cpu(codes).view(np.uint32), d)
+    keep = ~(idx_gpu != qz.idx).any(axis=1)
+    for g in range(groups):
+        sl = slice(g * n, (g + 1) * n)
+        ref = tq.scores(pr, queries[g], qz.idx[sl], qz.beta[sl], packed[2][sl].astype(np.float64),
+                        packed[3][sl].astype(np.float64))
+        bad, worst = parity.score_violations(s_dec[g], ref, queries[g], packed[2][sl])
+        assert bad == 0, (g, worst)
+        bad, worst = parity.score_violations(s_e2e[g], ref, queries[g], packed[2][sl], keep=keep[sl])
+        assert bad == 0, (g, worst)
+    # stage-1 reconstruction of the oracle's packed keys and of the library's
+    kh = _cpu(tqm.tq_dequant_mse(h, pdev[0], pdev[2]))
+    ref = tq.dequant_mse(pr, qz.idx, packed[2].astype(np.float64))
+    bad, worst = parity.dequant_violations(kh, ref)
+    assert bad == 0, worst
+    kh2 = _cpu(tqm.tq_dequant_mse(h, codes, norms))
+    ref2 = tq.dequant_mse(pr, idx_gpu, _cpu(norms).astype(np.float64))
+    bad, worst = parity.dequant_violations(kh2, ref2)
+    assert bad == 0, worst
+    return rep
+
+
+def test_toy_full(env):
+    _, _, wl = env
+    w = wl.WORKLOADS["toy"]
+    _announce(f"toy full: n={w.n} d={w.d} bits={w.bits}")
+    rep = check_full(env, w.d, w.bits, wl.keys(w), wl.queries(w))
+    print("toy mismatches", rep.code_mismatch, rep.sign_mismatch, "cascade keys", rep.cascade_keys)
+
+
+@pytest.mark.parametrize("d,bits,groups,n,nq", [
+    (2, 2, 1, 1, 1), (3, 3, 2, 7, 3), (4, 5, 1, 65, 2), (5, 4, 3, 33, 5), (8, 3, 1, 333, 4),
+    (31, 2, 2, 100, 7), (33, 3, 1, 257, 4), (64, 4, 2, 129, 9), (100, 5, 1, 300, 4), (128, 2, 1, 1000, 1),
+    (200, 4, 1, 500, 6), (257, 3, 1, 70, 4)])
+def test_ragged_shapes(env, d, bits, groups, n, nq):
+    _announce(f"ragged d={d} bits={bits} groups={groups} n={n} nq={nq}")
+    rs = np.random.default_rng(d * 100 + bits)
+    keys = (rs.standard_normal((groups * n, d)) * np.exp(rs.standard_normal((groups * n, 1)))).astype(np.float32)
+    queries = rs.standard_normal((groups, nq, d)).astype(np.float32)
+    check_full(env, d, bits, keys, queries, seed=d)
+
+
+def test_bf16_keys_and_strided_rows(env):
+    torch, tqm, _ = env
+    _announce("bf16 keys with a row stride")
+    d, bits = 96, 3
+    rs = np.random.default_rng(3)
+    keys = rs.standard_normal((500, d)).astype(np.float32)
+    check_full(env, d, bits, np.asarray(torch.tensor(keys).bfloat16().float().numpy()),
+               rs.standard_normal((1, 4, d)).astype(np.float32), key_dtype="bf16")
+    # row stride ldk > d: quantize a column slice of a wider matrix
+    h = tqm.tq_init(d, bits, 0)
+    wide = _dev(torch, np.concatenate([keys, rs.standard_normal((500, 32)).astype(np.float32)], axis=1))
+    a = tqm.tq_quantize(h, wide[:, :d])
+    b = tqm.tq_quantize(h, _dev(torch, keys))
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_zero_key_and_scale_invariance(env):
+    torch, tqm, _ = env
+    _announce("zero key + exact power-of-two scaling")
+    d, bits = 64, 4
+    rs = np.random.default_rng(4)
+    keys = rs.standard_normal((300, d)).astype(np.float32)
+    keys[7] = 0.0
+    check_full(env, d, bits, keys, rs.standard_normal((1, 3, d)).astype(np.float32))
+    h = tqm.tq_init(d, bits, 0)
+    a = tqm.tq_quantize(h, _dev(torch, keys))
+    b = tqm.tq_quantize(h, _dev(torch, keys * np.float32(2.0 ** 20)))
+    c = tqm.tq_quantize(h, _dev(torch, keys * np.float32(2.0 ** -20)))
+    for x, y, z in zip(a[:2], b[:2], c[:2]):
+        assert torch.equal(x, y) and torch.equal(x, z)
+    assert torch.equal(a[3], b[3]) and torch.equal(a[3], c[3])
+    assert torch.equal(a[2] * 2.0 ** 20, b[2]) and torch.equal(a[2] * 2.0 ** -20, c[2])
+
+
+def test_pages_4d_example_on_gpu(env):
+    """The tutorial page's 4-D rotation, through tq_init_explicit."""
+    torch, tqm, _ = env
+    _announce("4-D rotation example")
+    import json
+    import os
+    ex = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "polarquant_4d_example.json")))
+    q = np.array(ex["rotation"], dtype=np.float32)
+    g = np.random.default_rng(0).standard_normal((4, 4)).astype(np.float32)
+    h = tqm.tq_init_explicit(4, 3, q, g)
+    pr = P.explicit(4, 3, q, g)
+    keys = np.array([ex["input"]], dtype=np.float32)
+    rep = check_full(env, 4, 3, keys, np.ones((1, 1, 4), dtype=np.float32), h=h, pr=pr)
+    assert rep.code_mismatch == 0
+    codes, signs, norms, rnorms = tqm.tq_quantize(h, _dev(torch, keys))
+    # z = [0.5, 0.5, 0.5, 0.5]: every coordinate gets the same code
+    idx = tq.unpack_codes(_cpu(codes).view(np.uint32), 4)[0]
+    assert len(set(idx.tolist())) == 1 and float(_cpu(norms)[0]) == 10.0
+
+
+def _sampled_check(env, w, sample=2048, nq_cap=None, seed=0):
+    """Full-size quantize and score; oracle on a random sample of keys."""
+    torch, tqm, wl = env
+    if nq_cap:
+        w = w.scaled(nq=min(w.nq, nq_cap))
+    _announce(f"{w.name} full size: keys={w.total_keys} d={w.d} bits={w.bits} groups={w.groups} nq={w.nq}")
+    keys = wl.keys(w, seed)
+    queries = wl.queries(w, seed)
+    h = tqm.tq_init(w.d, w.bits, 0)
+    pr = _params(w.d, w.bits)
+    kd = _dev(torch, keys, torch.bfloat16 if w.key_dtype == "bf16" else torch.float32)
+    codes, signs, norms, rnorms = tqm.tq_quantize(h, kd)
+    scores = tqm.tq_logits(h, _dev(torch, queries), codes, signs, norms, rnorms, n=w.n)
+    torch.cuda.synchronize()
+    pick = np.sort(np.random.default_rng(1).choice(w.total_keys, size=min(sample, w.total_keys), replace=False))
+    sub = keys[pick].astype(np.float64)
+    qz = tq.quantize(pr, sub)
+    pk = torch.from_numpy(pick).cuda()
+    rep = parity.compare_quantize(pr, qz, _cpu(codes[pk]), _cpu(signs[pk]), _cpu(norms[pk]), _cpu(rnorms[pk]))
+    assert rep.ok(), rep
+    idx_gpu = tq.unpack_codes(_cpu(codes[pk]).view(np.uint32), w.d)
+    keep = ~(idx_gpu != qz.idx).any(axis=1)
+    groups = pick // w.n
+    t = pick % w.n
+    s_gpu = _cpu(scores)
+    for g in np.unique(groups):
+        m = groups == g
+        ref = tq.scores(pr, queries[g], qz.idx[m], qz.beta[m], qz.norms[m], qz.rnorms[m])
+        bad, worst = parity.score_violations(s_gpu[g][:, t[m]], ref, queries[g], qz.norms[m], keep=keep[m])
+        assert bad == 0, (g, worst)
+    kh = _cpu(tqm.tq_dequant_mse(h, codes[pk].contiguous(), norms[pk].contiguous()))
+    bad, worst = parity.dequant_violations(kh, tq.dequant_mse(pr, idx_gpu, _cpu(norms[pk]).astype(np.float64)))
+    assert bad == 0, worst
+    print(w.name, "mismatches", rep.code_mismatch, rep.sign_mismatch, "cascade", rep.cascade_keys)
+
+
+def test_llama_decode_full_size(env):
+    _sampled_check(env, env[2].WORKLOADS["llama_decode"])
+
+
+def test_long_context_full_size(env):
+    _sampled_check(env, env[2].WORKLOADS["long_context"])
+
+
+@pytest.mark.parametrize("name", ["search_b2", "search_b4"])
+def test_search_full_keys(env, name):
+    _sampled_check(env, env[2].WORKLOADS[name], nq_cap=64)
+
+
+def test_cone_subset(env):
+    w = env[2].WORKLOADS["cone"].scaled(n=20000, nq=16)
+    _sampled_check(env, w, sample=1024)

@@ -1,0 +1,84 @@
+"""CPU checks of libtq: it loads, exports every declared symbol, builds the
+same parameters as the oracle, and rejects bad arguments without a GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import params as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tq.h")
+
+
+@pytest.fixture(scope="module")
+def tqm():
+    import vector_quantization_quantize_amd as tqm
+    return tqm
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"TQ_API\s+[\w\s\*]+?\b(tq_\w+)\s*\(", text)))
+
+
+def test_header_declares_and_library_exports_everything(tqm):
+    names = _declared()
+    assert len(names) == len(tqm.EXPORTS) and sorted(tqm.EXPORTS) == names
+    lib = ctypes.CDLL(tqm.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def _ulps(a, b):
+    a = np.asarray(a, dtype=np.float32).view(np.int32).astype(np.int64)
+    b = np.asarray(b, dtype=np.float32).view(np.int32).astype(np.int64)
+    return np.abs(a - b)
+
+
+@pytest.mark.parametrize("d,bits,seed", [(2, 2, 0), (4, 3, 1), (33, 5, 2), (128, 3, 0), (128, 4, 0),
+                                         (200, 2, 0), (200, 4, 0)])
+def test_host_params_match_oracle(tqm, d, bits, seed):
+    """The C++ builder (Householder QR, Gauss-Legendre Lloyd-Max) and the
+    oracle (LAPACK QR, incomplete-beta Lloyd-Max) agree to <= 1 float32 ulp."""
+    pi, g, c, t = tqm.tq_host_params(d, bits, seed)
+    pr = P.init(d, bits, seed)
+    assert _ulps(pi, pr.pi).max() <= 1
+    assert (_ulps(pi, pr.pi) > 0).mean() < 1e-4
+    assert np.array_equal(g, pr.g.astype(np.float32))
+    assert _ulps(c, pr.centroids).max() <= 1
+    assert _ulps(t, pr.thresholds).max() <= 1
+
+
+def test_host_params_d1536(tqm):
+    pi, g, c, t = tqm.tq_host_params(1536, 4, 0)
+    pr = P.init(1536, 4, 0)
+    assert _ulps(pi, pr.pi).max() <= 1
+    assert (_ulps(pi, pr.pi) > 0).sum() <= 8
+    assert np.array_equal(c, pr.centroids.astype(np.float32))
+
+
+def test_bad_arguments_are_rejected(tqm):
+    lib = tqm._lib()
+    out = ctypes.c_void_p()
+    for d, bits in [(1, 3), (4097, 3), (128, 1), (128, 6)]:
+        assert lib.tq_init(d, bits, 0, ctypes.byref(out)) == tqm.TQ_EINVAL
+    assert lib.tq_init(128, 3, 0, None) == tqm.TQ_EINVAL
+    assert lib.tq_host_params(0, 3, 0, None, None, None, None) == tqm.TQ_EINVAL
+    assert lib.tq_quantize(None, None, 0, 1, 128, None, None, None, None, None) == tqm.TQ_EINVAL
+    assert lib.tq_logits(None, None, 1, 1, None, None, None, None, 1, None, None, 0, None) == tqm.TQ_EINVAL
+    assert lib.tq_dequant_mse(None, None, None, 1, None, None) == tqm.TQ_EINVAL
+    assert lib.tq_destroy(None) == tqm.TQ_OK
+    assert lib.tq_params_hash(None) == 0
+    assert lib.tq_logits_workspace_size(None, 1, 1) == 0
+    assert lib.tq_strerror(tqm.TQ_EINVAL) == b"invalid argument"
+    assert lib.tq_strerror(12345) == b"unknown error"
+
+
+def test_host_params_null_outputs_skip(tqm):
+    lib = tqm._lib()
+    c = np.empty(4, dtype=np.float32)
+    assert lib.tq_host_params(16, 3, 0, None, None, c.ctypes.data, None) == 0
+    assert np.array_equal(c, P.init(16, 3, 0).centroids.astype(np.float32))

@@ -1,0 +1,28 @@
+// Host-side parameter construction (float64, no HIP calls).
+#pragma once
+#include <cstddef>
+#include <cstdint>
+
+namespace tqhost {
+
+// State of SplitMix64 stream `stream` of `seed`.
+uint64_t stream_state(uint64_t seed, uint32_t stream);
+
+// `count` standard normal draws of the stream, Box-Muller on counter pairs.
+void normal_draws(uint64_t seed, uint32_t stream, size_t count, double* out);
+
+// Householder QR of the row-major d x d matrix `a`; writes Q diag(sign(diag R))
+// row-major into `q`.
+void haar_from_gaussian(int d, const double* a, double* q);
+
+// Lloyd-Max levels (ascending, symmetric) for the law of one coordinate of a
+// uniform unit vector in R^d.  Returns 0 on convergence.
+int lloyd_max_sphere(int d, int levels, double* c);
+
+// Fill any of pi, g (float[d*d]), centroids (float[L]), thresholds
+// (float[L-1]); NULL outputs are skipped.  Returns 0, or < 0 on bad
+// arguments / non-convergence.
+int build_params(int d, int bits, uint64_t seed, float* pi, float* g, float* centroids,
+                 float* thresholds);
+
+}  // namespace tqhost

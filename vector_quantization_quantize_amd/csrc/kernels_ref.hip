@@ -1,0 +1,356 @@
+// Straightforward gfx950 kernels for every stage of the path (fp32 VALU,
+// any d in [2, 4096], any bits in [2, 5]).  They are the general fallback
+// and the baseline the tuned kernels are checked against.
+//
+// Stages (web pages about TurboQuant, by title and section):
+//   quantize  - "TurboQuant tutorial" (gitcode.csdn.net), PolarQuant and QJL
+//               sections; "TurboQuant digest" (juejin.cn) section 2.
+//   score     - "TurboQuant digest" section 2 and "TurboQuant deep review"
+//               (freelamp.com), error-compensation section: high-precision
+//               query against 1-bit residual signs, zero-bias estimate.
+//   dequant   - "TurboQuant tutorial", polar part: codes and the kept length
+//               map back to a vector (stage 1 only).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "tq_internal.h"
+
+namespace tqdev {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float load_key(const void* keys, int key_dtype, int64_t off) {
+  if (key_dtype == TQ_BF16) {
+    const uint16_t b = static_cast<const uint16_t*>(keys)[off];
+    return __uint_as_float(uint32_t(b) << 16);
+  }
+  return static_cast<const float*>(keys)[off];
+}
+
+// idx = #{ i : t_i <= z }  (a tie goes to the upper cell)
+__device__ __forceinline__ int bucket(float z, const float* t, int levels) {
+  int idx = 0;
+  for (int i = 0; i + 1 < levels; ++i) idx += (t[i] <= z) ? 1 : 0;
+  return idx;
+}
+
+// ---------------------------------------------------------------------------
+// quantize: one block per tile of `tk` keys, two LDS buffers of tk x (d+1).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads)
+quantize_ref_kernel(const void* __restrict__ keys, int key_dtype, int64_t n, int64_t ldk, int d,
+                    int code_bits, int words, int tk, const float* __restrict__ piT,
+                    const float* __restrict__ gT, Codebook cb, uint32_t* __restrict__ codes,
+                    uint32_t* __restrict__ signs, float* __restrict__ norms,
+                    float* __restrict__ rnorms) {
+  extern __shared__ float smem[];
+  const int ds = d + 1;  // padded row stride
+  float* buf0 = smem;
+  float* buf1 = smem + size_t(tk) * ds;
+  float* nrm = buf1 + size_t(tk) * ds;
+  float* lvl = nrm + tk;           // levels
+  float* thr = lvl + kMaxLevels;   // thresholds
+  const int tid = threadIdx.x;
+  const int64_t base = int64_t(blockIdx.x) * tk;
+  const int levels = cb.levels;
+  if (tid < kMaxLevels) {
+    lvl[tid] = cb.c[tid];
+    thr[tid] = cb.t[tid];
+  }
+  // keys -> buf0 (fp32)
+  for (int p = tid; p < tk * d; p += kThreads) {
+    const int k = p / d, i = p - k * d;
+    const int64_t key = base + k;
+    buf0[k * ds + i] = key < n ? load_key(keys, key_dtype, key * ldk + i) : 0.0f;
+  }
+  __syncthreads();
+  // norms
+  for (int k = tid; k < tk; k += kThreads) {
+    float s = 0.0f;
+    for (int i = 0; i < d; ++i) s = fmaf(buf0[k * ds + i], buf0[k * ds + i], s);
+    const float nk = sqrtf(s);
+    nrm[k] = nk;
+    if (base + k < n) norms[base + k] = nk;
+  }
+  __syncthreads();
+  // z = (Pi k) / n, four keys per thread per output coordinate
+  const int groups = tk / 4;
+  for (int p = tid; p < groups * d; p += kThreads) {
+    const int kg = p / d, j = p - kg * d;
+    const float* k0 = buf0 + (4 * kg) * ds;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int i = 0; i < d; ++i) {
+      const float w = piT[size_t(i) * d + j];
+      a0 = fmaf(w, k0[i], a0);
+      a1 = fmaf(w, k0[ds + i], a1);
+      a2 = fmaf(w, k0[2 * ds + i], a2);
+      a3 = fmaf(w, k0[3 * ds + i], a3);
+    }
+    const float acc[4] = {a0, a1, a2, a3};
+    for (int r = 0; r < 4; ++r) {
+      const float nk = nrm[4 * kg + r];
+      buf1[(4 * kg + r) * ds + j] = nk > 0.0f ? acc[r] / nk : 0.0f;
+    }
+  }
+  __syncthreads();
+  // bucketize, residual in place, code planes
+  for (int p = tid; p < tk * words; p += kThreads) {
+    const int k = p / words, w = p - k * words;
+    uint32_t plane[4] = {0u, 0u, 0u, 0u};
+    for (int b = 0; b < 32; ++b) {
+      const int j = 32 * w + b;
+      if (j >= d) break;
+      const float z = buf1[k * ds + j];
+      const int idx = bucket(z, thr, levels);
+      buf1[k * ds + j] = z - lvl[idx];
+      for (int q = 0; q < code_bits; ++q) plane[q] |= uint32_t((idx >> q) & 1) << b;
+    }
+    const int64_t key = base + k;
+    if (key < n)
+      for (int q = 0; q < code_bits; ++q) codes[(key * code_bits + q) * words + w] = plane[q];
+  }
+  __syncthreads();
+  for (int k = tid; k < tk; k += kThreads) {
+    float s = 0.0f;
+    for (int i = 0; i < d; ++i) s = fmaf(buf1[k * ds + i], buf1[k * ds + i], s);
+    if (base + k < n) rnorms[base + k] = sqrtf(s);
+  }
+  // p = G r -> buf0
+  for (int p = tid; p < groups * d; p += kThreads) {
+    const int kg = p / d, j = p - kg * d;
+    const float* r0 = buf1 + (4 * kg) * ds;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int i = 0; i < d; ++i) {
+      const float w = gT[size_t(i) * d + j];
+      a0 = fmaf(w, r0[i], a0);
+      a1 = fmaf(w, r0[ds + i], a1);
+      a2 = fmaf(w, r0[2 * ds + i], a2);
+      a3 = fmaf(w, r0[3 * ds + i], a3);
+    }
+    buf0[(4 * kg) * ds + j] = a0;
+    buf0[(4 * kg + 1) * ds + j] = a1;
+    buf0[(4 * kg + 2) * ds + j] = a2;
+    buf0[(4 * kg + 3) * ds + j] = a3;
+  }
+  __syncthreads();
+  for (int p = tid; p < tk * words; p += kThreads) {
+    const int k = p / words, w = p - k * words;
+    uint32_t word = 0u;
+    for (int b = 0; b < 32; ++b) {
+      const int j = 32 * w + b;
+      if (j >= d) break;
+      word |= uint32_t(buf0[k * ds + j] > 0.0f) << b;
+    }
+    const int64_t key = base + k;
+    if (key < n) signs[key * words + w] = word;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// query prep: v = Pi q, w = G v, one block per query
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads)
+query_prep_kernel(const float* __restrict__ queries, int d, const float* __restrict__ piT,
+                  const float* __restrict__ gT, float* __restrict__ vw, int64_t stride, int64_t half) {
+  extern __shared__ float smem[];
+  float* qs = smem;
+  float* vs = smem + d;
+  const int64_t qi = blockIdx.x;
+  for (int i = threadIdx.x; i < d; i += kThreads) qs[i] = queries[qi * d + i];
+  __syncthreads();
+  float* out = vw + qi * stride;
+  for (int j = threadIdx.x; j < half; j += kThreads) {
+    float a = 0.0f;
+    if (j < d)
+      for (int i = 0; i < d; ++i) a = fmaf(piT[size_t(i) * d + j], qs[i], a);
+    if (j < d) vs[j] = a;
+    out[j] = a;  // zero padding past d
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < half; j += kThreads) {
+    float a = 0.0f;
+    if (j < d)
+      for (int i = 0; i < d; ++i) a = fmaf(gT[size_t(i) * d + j], vs[i], a);
+    out[half + j] = a;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// scores: one thread per key, queries of the group in chunks of 4
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads)
+logits_ref_kernel(const float* __restrict__ vw, int64_t nq, int d, int code_bits, int words,
+                  int64_t n, int64_t stride, int64_t half, const uint32_t* __restrict__ codes,
+                  const uint32_t* __restrict__ signs, const float* __restrict__ norms,
+                  const float* __restrict__ rnorms, float* __restrict__ scores, Codebook cb) {
+  extern __shared__ float smem[];
+  float* lvl = smem;
+  float* qv = smem + kMaxLevels;  // [4][d] v then [4][d] w
+  const int64_t g = blockIdx.y;
+  const int64_t t = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t key = g * n + t;
+  if (threadIdx.x < kMaxLevels) lvl[threadIdx.x] = cb.c[threadIdx.x];
+  const float kappa = 1.2533141373155002512f / float(d);  // sqrt(pi/2) / d
+  float nk = 0.f, rho = 0.f;
+  if (t < n) {
+    nk = norms[key];
+    rho = rnorms[key];
+  }
+  for (int64_t q0 = 0; q0 < nq; q0 += 4) {
+    const int qc = int(nq - q0 < 4 ? nq - q0 : 4);
+    __syncthreads();
+    for (int p = threadIdx.x; p < 4 * d; p += kThreads) {
+      const int q = p / d, j = p - q * d;
+      const float* src = vw + (g * nq + q0 + (q < qc ? q : 0)) * stride;
+      qv[q * d + j] = q < qc ? src[j] : 0.f;
+      qv[4 * d + q * d + j] = q < qc ? src[half + j] : 0.f;
+    }
+    __syncthreads();
+    if (t >= n) continue;
+    float a1[4] = {0.f, 0.f, 0.f, 0.f}, a2[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int w = 0; w < words; ++w) {
+      uint32_t plane[4] = {0u, 0u, 0u, 0u};
+      for (int q = 0; q < code_bits; ++q) plane[q] = codes[(key * code_bits + q) * words + w];
+      const uint32_t sw = signs[key * words + w];
+      for (int b = 0; b < 32; ++b) {
+        const int j = 32 * w + b;
+        if (j >= d) break;
+        int idx = 0;
+        for (int q = 0; q < code_bits; ++q) idx |= int((plane[q] >> b) & 1u) << q;
+        const float cv = lvl[idx];
+        const float sg = ((sw >> b) & 1u) ? 1.0f : -1.0f;
+        for (int q = 0; q < 4; ++q) {
+          a1[q] = fmaf(qv[q * d + j], cv, a1[q]);
+          a2[q] = fmaf(qv[4 * d + q * d + j], sg, a2[q]);
+        }
+      }
+    }
+    const float corr = rho * kappa;
+    for (int q = 0; q < qc; ++q)
+      scores[(g * nq + q0 + q) * n + t] = nk * fmaf(corr, a2[q], a1[q]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dequant: k_hat = n Pi^T c[idx]; block per tile of tk keys
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads)
+dequant_ref_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ norms, int64_t n, int d,
+                   int code_bits, int words, int tk, const float* __restrict__ pi, Codebook cb,
+                   float* __restrict__ khat) {
+  extern __shared__ float smem[];
+  const int ds = d + 1;
+  float* ch = smem;                    // [tk][ds] c[idx]
+  float* lvl = smem + size_t(tk) * ds;
+  const int tid = threadIdx.x;
+  const int64_t base = int64_t(blockIdx.x) * tk;
+  if (tid < kMaxLevels) lvl[tid] = cb.c[tid];
+  __syncthreads();
+  for (int p = tid; p < tk * words; p += kThreads) {
+    const int k = p / words, w = p - k * words;
+    const int64_t key = base + k;
+    uint32_t plane[4] = {0u, 0u, 0u, 0u};
+    if (key < n)
+      for (int q = 0; q < code_bits; ++q) plane[q] = codes[(key * code_bits + q) * words + w];
+    for (int b = 0; b < 32; ++b) {
+      const int j = 32 * w + b;
+      if (j >= d) break;
+      int idx = 0;
+      for (int q = 0; q < code_bits; ++q) idx |= int((plane[q] >> b) & 1u) << q;
+      ch[k * ds + j] = lvl[idx];
+    }
+  }
+  __syncthreads();
+  const int groups = tk / 4;
+  for (int p = tid; p < groups * d; p += kThreads) {
+    const int kg = p / d, j = p - kg * d;
+    const float* c0 = ch + (4 * kg) * ds;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int i = 0; i < d; ++i) {
+      const float w = pi[size_t(i) * d + j];  // (Pi^T c)_j = sum_i Pi[i][j] c_i
+      a0 = fmaf(w, c0[i], a0);
+      a1 = fmaf(w, c0[ds + i], a1);
+      a2 = fmaf(w, c0[2 * ds + i], a2);
+      a3 = fmaf(w, c0[3 * ds + i], a3);
+    }
+    const float acc[4] = {a0, a1, a2, a3};
+    for (int r = 0; r < 4; ++r) {
+      const int64_t key = base + 4 * kg + r;
+      if (key < n) khat[key * d + j] = norms[key] * acc[r];
+    }
+  }
+}
+
+// keys per tile so that `buffers` LDS arrays of tk x (d+1) floats fit in
+// `budget` bytes; a multiple of 4, at least 4
+int tile_keys(int d, int buffers, size_t budget, int cap) {
+  size_t per = size_t(buffers) * (d + 1) * sizeof(float);
+  int tk = int(budget / per);
+  tk = tk / 4 * 4;
+  if (tk > cap) tk = cap;
+  if (tk < 4) tk = 4;
+  return tk;
+}
+
+template <class K>
+hipError_t allow_lds(K kernel, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
+}
+
+}  // namespace
+
+hipError_t launch_quantize_v1(const tq_ctx* h, const void* keys, int key_dtype, int64_t n, int64_t ldk,
+                              uint32_t* codes, uint32_t* signs, float* norms, float* rnorms,
+                              hipStream_t stream) {
+  const int d = h->d;
+  const int tk = tile_keys(d, 2, 64 * 1024, 64);
+  const size_t lds = (size_t(2) * tk * (d + 1) + tk + 2 * kMaxLevels) * sizeof(float);
+  hipError_t e = allow_lds(quantize_ref_kernel, lds);
+  if (e != hipSuccess) return e;
+  const int64_t blocks = (n + tk - 1) / tk;
+  hipLaunchKernelGGL(quantize_ref_kernel, dim3(unsigned(blocks)), dim3(kThreads), lds, stream, keys,
+                     key_dtype, n, ldk, d, h->code_bits, h->words, tk, h->d_piT, h->d_gT, h->cb, codes,
+                     signs, norms, rnorms);
+  return hipGetLastError();
+}
+
+hipError_t launch_query_prep(const tq_ctx* h, const float* queries, int64_t count, float* vw,
+                             hipStream_t stream) {
+  const int d = h->d;
+  const size_t lds = size_t(2) * d * sizeof(float);
+  hipLaunchKernelGGL(query_prep_kernel, dim3(unsigned(count)), dim3(kThreads), lds, stream, queries, d,
+                     h->d_piT, h->d_gT, vw, vw_stride(d), vw_half(d));
+  return hipGetLastError();
+}
+
+hipError_t launch_logits_v1(const tq_ctx* h, const float* vw, int64_t groups, int64_t nq,
+                            const uint32_t* codes, const uint32_t* signs, const float* norms,
+                            const float* rnorms, int64_t n, float* scores, hipStream_t stream) {
+  const int d = h->d;
+  const size_t lds = (kMaxLevels + size_t(8) * d) * sizeof(float);
+  hipError_t e = allow_lds(logits_ref_kernel, lds);
+  if (e != hipSuccess) return e;
+  dim3 grid(unsigned((n + kThreads - 1) / kThreads), unsigned(groups));
+  hipLaunchKernelGGL(logits_ref_kernel, grid, dim3(kThreads), lds, stream, vw, nq, d, h->code_bits,
+                     h->words, n, vw_stride(d), vw_half(d), codes, signs, norms, rnorms, scores, h->cb);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_v1(const tq_ctx* h, const uint32_t* codes, const float* norms, int64_t n,
+                             float* khat, hipStream_t stream) {
+  const int d = h->d;
+  const int tk = tile_keys(d, 1, 64 * 1024, 64);
+  const size_t lds = (size_t(tk) * (d + 1) + kMaxLevels) * sizeof(float);
+  hipError_t e = allow_lds(dequant_ref_kernel, lds);
+  if (e != hipSuccess) return e;
+  const int64_t blocks = (n + tk - 1) / tk;
+  hipLaunchKernelGGL(dequant_ref_kernel, dim3(unsigned(blocks)), dim3(kThreads), lds, stream, codes, norms,
+                     n, d, h->code_bits, h->words, tk, h->d_pi, h->cb, khat);
+  return hipGetLastError();
+}
+
+}  // namespace tqdev

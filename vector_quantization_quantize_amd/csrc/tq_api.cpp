@@ -1,0 +1,265 @@
+// C ABI of libtq: argument checking, handle management and dispatch to the
+// HIP kernels.  See include/tq.h for the contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "host_params.h"
+#include "tq_internal.h"
+
+namespace {
+
+bool trace_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("TQ_TRACE");
+    return v && v[0] && v[0] != '0';
+  }();
+  return on;
+}
+
+void free_device(tq_ctx* h) {
+  float** ptrs[] = {&h->d_pi, &h->d_piT, &h->d_g, &h->d_gT};
+  for (float** p : ptrs) {
+    if (*p) (void)hipFree(*p);
+    *p = nullptr;
+  }
+}
+
+int upload(float** dst, const std::vector<float>& src) {
+  if (hipMalloc(reinterpret_cast<void**>(dst), src.size() * sizeof(float)) != hipSuccess) {
+    *dst = nullptr;
+    return TQ_ENOMEM;
+  }
+  if (hipMemcpy(*dst, src.data(), src.size() * sizeof(float), hipMemcpyHostToDevice) != hipSuccess)
+    return TQ_EHIP;
+  return TQ_OK;
+}
+
+std::vector<float> transpose(const std::vector<float>& a, int d) {
+  std::vector<float> t(a.size());
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j) t[size_t(j) * d + i] = a[size_t(i) * d + j];
+  return t;
+}
+
+// alpha_S = 2^-B sum_idx c[idx] prod_{p in S} s_p(idx), for odd |S| <= 3
+void plane_expansion(const std::vector<float>& c, int code_bits, tqdev::PlaneExpansion* out) {
+  const int levels = 1 << code_bits;
+  out->count = 0;
+  for (uint32_t mask = 1; mask < uint32_t(levels); ++mask) {
+    const int size = __builtin_popcount(mask);
+    if (size != 1 && size != 3) continue;
+    double acc = 0.0;
+    for (int idx = 0; idx < levels; ++idx) {
+      double s = 1.0;
+      for (int p = 0; p < code_bits; ++p)
+        if (mask & (1u << p)) s *= ((idx >> p) & 1) ? 1.0 : -1.0;
+      acc += double(c[idx]) * s;
+    }
+    out->mask[out->count] = mask;
+    out->alpha[out->count] = float(acc / levels);
+    ++out->count;
+  }
+}
+
+int finish_init(tq_ctx* h) {
+  const int d = h->d;
+  h->code_bits = h->bits - 1;
+  h->levels = 1 << h->code_bits;
+  h->words = (d + 31) / 32;
+  if (hipGetDevice(&h->device) != hipSuccess) return TQ_EHIP;
+  for (int i = 0; i < tqdev::kMaxLevels; ++i) {
+    h->cb.c[i] = i < h->levels ? h->centroids[i] : 0.0f;
+    h->cb.t[i] = i + 1 < h->levels ? h->thresholds[i] : INFINITY;
+  }
+  h->cb.levels = h->levels;
+  plane_expansion(h->centroids, h->code_bits, &h->planes);
+  int rc;
+  if ((rc = upload(&h->d_pi, h->pi)) != TQ_OK) return rc;
+  if ((rc = upload(&h->d_piT, transpose(h->pi, d))) != TQ_OK) return rc;
+  if ((rc = upload(&h->d_g, h->g)) != TQ_OK) return rc;
+  if ((rc = upload(&h->d_gT, transpose(h->g, d))) != TQ_OK) return rc;
+  return TQ_OK;
+}
+
+int check_device(const tq_ctx* h) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return TQ_EHIP;
+  return dev == h->device ? TQ_OK : TQ_EINVAL;
+}
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* tq_strerror(int code) {
+  switch (code) {
+    case TQ_OK: return "success";
+    case TQ_EINVAL: return "invalid argument";
+    case TQ_EUNSUPPORTED: return "unsupported configuration";
+    case TQ_EHIP: return "HIP runtime error";
+    case TQ_ENOMEM: return "out of memory";
+    default: return "unknown error";
+  }
+}
+
+int tq_host_params(int32_t d, int32_t bits, uint64_t seed, float* pi, float* g, float* centroids,
+                   float* thresholds) {
+  if (d < 2 || d > 4096 || bits < 2 || bits > 5) return TQ_EINVAL;
+  try {
+    const int rc = tqhost::build_params(d, bits, seed, pi, g, centroids, thresholds);
+    return rc == 0 ? TQ_OK : TQ_EUNSUPPORTED;
+  } catch (const std::bad_alloc&) {
+    return TQ_ENOMEM;
+  } catch (...) {
+    return TQ_EUNSUPPORTED;
+  }
+}
+
+static int init_common(int32_t d, int32_t bits, const float* pi_in, const float* g_in, uint64_t seed,
+                       tq_handle* out) {
+  if (!out) return TQ_EINVAL;
+  *out = nullptr;
+  if (d < 2 || d > 4096 || bits < 2 || bits > 5) return TQ_EINVAL;
+  tq_ctx* h = nullptr;
+  try {
+    h = new tq_ctx();
+    h->d = d;
+    h->bits = bits;
+    const size_t dd = size_t(d) * d;
+    const int levels = 1 << (bits - 1);
+    h->pi.resize(dd);
+    h->g.resize(dd);
+    h->centroids.resize(levels);
+    h->thresholds.resize(levels - 1 > 0 ? levels - 1 : 1);
+    int rc;
+    if (pi_in) {
+      std::memcpy(h->pi.data(), pi_in, dd * sizeof(float));
+      std::memcpy(h->g.data(), g_in, dd * sizeof(float));
+      rc = tqhost::build_params(d, bits, 0, nullptr, nullptr, h->centroids.data(), h->thresholds.data());
+    } else {
+      rc = tqhost::build_params(d, bits, seed, h->pi.data(), h->g.data(), h->centroids.data(),
+                                h->thresholds.data());
+    }
+    if (rc != 0) {
+      delete h;
+      return TQ_EUNSUPPORTED;
+    }
+  } catch (const std::bad_alloc&) {
+    delete h;
+    return TQ_ENOMEM;
+  } catch (...) {
+    delete h;
+    return TQ_EUNSUPPORTED;
+  }
+  const int rc = finish_init(h);
+  if (rc != TQ_OK) {
+    free_device(h);
+    delete h;
+    return rc;
+  }
+  if (trace_enabled())
+    std::fprintf(stderr, "[tq] init d=%d bits=%d device=%d\n", h->d, h->bits, h->device);
+  *out = h;
+  return TQ_OK;
+}
+
+int tq_init(int32_t d, int32_t bits, uint64_t seed, tq_handle* out) {
+  return init_common(d, bits, nullptr, nullptr, seed, out);
+}
+
+int tq_init_explicit(int32_t d, int32_t bits, const float* pi, const float* g, tq_handle* out) {
+  if (!pi || !g) return TQ_EINVAL;
+  return init_common(d, bits, pi, g, 0, out);
+}
+
+int tq_destroy(tq_handle h) {
+  if (!h) return TQ_OK;
+  free_device(h);
+  delete h;
+  return TQ_OK;
+}
+
+int tq_get_layout(tq_handle h, tq_layout* out) {
+  if (!h || !out) return TQ_EINVAL;
+  out->d = h->d;
+  out->bits = h->bits;
+  out->code_bits = h->code_bits;
+  out->levels = h->levels;
+  out->words = h->words;
+  out->format_version = TQ_FORMAT_VERSION;
+  out->code_bytes = int64_t(4) * h->code_bits * h->words;
+  out->sign_bytes = int64_t(4) * h->words;
+  out->key_bytes = out->code_bytes + out->sign_bytes + 8;
+  return TQ_OK;
+}
+
+uint64_t tq_params_hash(tq_handle h) {
+  if (!h) return 0;
+  uint64_t x = 0xcbf29ce484222325ull;
+  auto eat = [&x](const std::vector<float>& v) {
+    const unsigned char* p = reinterpret_cast<const unsigned char*>(v.data());
+    for (size_t i = 0; i < v.size() * sizeof(float); ++i) {
+      x ^= p[i];
+      x *= 0x100000001b3ull;
+    }
+  };
+  eat(h->pi);
+  eat(h->g);
+  eat(h->centroids);
+  return x;
+}
+
+int tq_quantize(tq_handle h, const void* keys, int32_t key_dtype, int64_t n, int64_t ldk, uint32_t* codes,
+                uint32_t* signs, float* norms, float* rnorms, void* stream) {
+  if (!h || n < 0) return TQ_EINVAL;
+  if (key_dtype != TQ_F32 && key_dtype != TQ_BF16) return TQ_EINVAL;
+  if (n == 0) return TQ_OK;
+  if (!keys || !codes || !signs || !norms || !rnorms || ldk < h->d) return TQ_EINVAL;
+  if (!aligned4(codes) || !aligned4(signs) || !aligned4(norms) || !aligned4(rnorms)) return TQ_EINVAL;
+  if (check_device(h) != TQ_OK) return TQ_EINVAL;
+  const hipError_t e = tqdev::launch_quantize_v1(h, keys, key_dtype, n, ldk, codes, signs, norms, rnorms,
+                                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : TQ_EHIP;
+}
+
+size_t tq_logits_workspace_size(tq_handle h, int64_t groups, int64_t nq) {
+  if (!h || groups < 0 || nq < 0) return 0;
+  return size_t(groups) * size_t(nq) * size_t(tqdev::vw_stride(h->d)) * sizeof(float);
+}
+
+int tq_logits(tq_handle h, const float* queries, int64_t groups, int64_t nq, const uint32_t* codes,
+              const uint32_t* signs, const float* norms, const float* rnorms, int64_t n, float* scores,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!h || groups < 0 || nq < 0 || n < 0) return TQ_EINVAL;
+  if (groups == 0 || nq == 0 || n == 0) return TQ_OK;
+  if (!queries || !codes || !signs || !norms || !rnorms || !scores || !workspace) return TQ_EINVAL;
+  if (workspace_bytes < tq_logits_workspace_size(h, groups, nq)) return TQ_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return TQ_EINVAL;
+  if (groups > 65535) return TQ_EUNSUPPORTED;
+  if (check_device(h) != TQ_OK) return TQ_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* vw = static_cast<float*>(workspace);
+  hipError_t e = tqdev::launch_query_prep(h, queries, groups * nq, vw, s);
+  if (e != hipSuccess) return TQ_EHIP;
+  e = tqdev::launch_logits_v1(h, vw, groups, nq, codes, signs, norms, rnorms, n, scores, s);
+  return e == hipSuccess ? TQ_OK : TQ_EHIP;
+}
+
+int tq_dequant_mse(tq_handle h, const uint32_t* codes, const float* norms, int64_t n, float* khat,
+                   void* stream) {
+  if (!h || n < 0) return TQ_EINVAL;
+  if (n == 0) return TQ_OK;
+  if (!codes || !norms || !khat) return TQ_EINVAL;
+  if (check_device(h) != TQ_OK) return TQ_EINVAL;
+  const hipError_t e = tqdev::launch_dequant_v1(h, codes, norms, n, khat, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : TQ_EHIP;
+}
+
+}  // extern "C"

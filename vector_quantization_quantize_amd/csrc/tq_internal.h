@@ -1,0 +1,69 @@
+// Internal declarations shared by the C-ABI layer and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <vector>
+
+#include "../../include/tq.h"
+
+namespace tqdev {
+
+constexpr int kMaxLevels = 16;  // bits <= 5  ->  B <= 4  ->  L <= 16
+
+// Codebook passed by value to kernels; copied to LDS before use.
+struct Codebook {
+  float c[kMaxLevels];  // ascending levels
+  float t[kMaxLevels];  // t[0 .. L-2] thresholds, rest +inf
+  int levels;
+};
+
+// Coefficients of the level as a multilinear function of the plane signs.
+// With s_p = 2 b_p - 1 (b_p = bit p of the index), a symmetric level set
+// satisfies c[idx] = sum over odd-size plane subsets S of alpha_S prod s_p.
+// For B <= 4 the odd subsets are: the B singletons and the C(B,3) triples.
+struct PlaneExpansion {
+  int count;            // number of terms
+  uint32_t mask[8];     // plane subset of each term (bit p = plane p)
+  float alpha[8];       // coefficient of each term
+};
+
+}  // namespace tqdev
+
+struct tq_ctx {
+  int d = 0, bits = 0, code_bits = 0, levels = 0, words = 0;
+  int device = -1;
+  // host copies (float32), row-major d x d
+  std::vector<float> pi, g, centroids, thresholds;
+  // device tables
+  float* d_pi = nullptr;   // Pi  row-major: d_pi[j*d + i] = Pi[j][i]
+  float* d_piT = nullptr;  // Pi^T row-major: d_piT[i*d + j] = Pi[j][i]
+  float* d_g = nullptr;    // G   row-major
+  float* d_gT = nullptr;   // G^T row-major
+  tqdev::Codebook cb{};
+  tqdev::PlaneExpansion planes{};
+};
+
+namespace tqdev {
+
+// launchers (return hipError_t of the launch)
+hipError_t launch_quantize_v1(const tq_ctx* h, const void* keys, int key_dtype, int64_t n, int64_t ldk,
+                              uint32_t* codes, uint32_t* signs, float* norms, float* rnorms,
+                              hipStream_t stream);
+
+hipError_t launch_query_prep(const tq_ctx* h, const float* queries, int64_t count, float* vw,
+                             hipStream_t stream);
+
+hipError_t launch_logits_v1(const tq_ctx* h, const float* vw, int64_t groups, int64_t nq,
+                            const uint32_t* codes, const uint32_t* signs, const float* norms,
+                            const float* rnorms, int64_t n, float* scores, hipStream_t stream);
+
+hipError_t launch_dequant_v1(const tq_ctx* h, const uint32_t* codes, const float* norms, int64_t n,
+                             float* khat, hipStream_t stream);
+
+// float offset between a query's v and w vectors in the workspace, and the
+// stride between queries: v at q*vw_stride, w at q*vw_stride + vw_half
+inline int64_t vw_half(int d) { return (int64_t(d) + 63) / 64 * 64; }
+inline int64_t vw_stride(int d) { return 2 * vw_half(d); }
+
+}  // namespace tqdev
