@@ -1,0 +1,219 @@
+"""Throughput of the TurboQuant quantize / score path on one MI355X.
+
+One step = the whole path over one batch of the long-context workload
+(batch 4 x 8 KV heads x 131072 bf16 keys, d = 128, 3 bits, 32 query heads per
+batch entry, 4 per KV head):
+  tq_quantize     the full key cache -> packed codes, signs, norms
+  tq_logits       every query head against its KV head's packed keys
+  tq_dequant_mse  stage-1 reconstruction of the full cache
+All inputs are synthetic (seeded), resident in HBM before timing starts.
+
+Prints one JSON line.  ``value`` = (query, key) scores produced per second of
+step time.  Per-kernel times come from HIP events recorded on the stream the
+library launches on; ``roofline`` is for the kernel with the largest share of
+the step.  ``cpu_baseline`` times the CPU oracle on a bounded sample of the
+same workload on the host cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "tq_logits keys scored/s + % HBM roofline (d=128, 3-bit); tq_quantize Mkeys/s"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+FP32_VALU_PEAK_TFLOPS = 157.3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long_context")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cold-reps", type=int, default=10, help="flushed-cache reps per kernel")
+    ap.add_argument("--cpu-groups", type=int, default=2, help="key groups timed on the CPU oracle")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_models(w):
+    """Algorithmic bytes / flops per key of each entry point (see the roofline
+    table in the design notes): packed bytes = 4 B W + 4 W + 8."""
+    words = (w.d + 31) // 32
+    packed = 4 * (w.bits - 1) * words + 4 * words + 8
+    key_in = w.d * (2 if w.key_dtype == "bf16" else 4)
+    return {
+        "tq_quantize": {"bytes": key_in + packed, "flops": 4 * w.d * w.d},
+        "tq_logits": {"bytes": packed + 4 * w.nq, "flops": 4 * w.d * w.nq},
+        "tq_dequant_mse": {"bytes": 4 * (w.bits - 1) * words + 4 + 4 * w.d, "flops": 2 * w.d * w.d},
+    }
+
+
+def cpu_baseline(w, keys_np, queries_np, groups, seed):
+    """Oracle (numpy float64) on the first `groups` key groups."""
+    import numpy as np
+    from oracle import params as P
+    from oracle import tq
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    pr = P.init(w.d, w.bits, seed)
+    t0 = time.perf_counter()
+    scored = 0
+    for g in range(groups):
+        k = keys_np[g * w.n:(g + 1) * w.n].astype(np.float64)
+        qz = tq.quantize(pr, k)
+        s = tq.scores(pr, queries_np[g], qz.idx, qz.beta, qz.norms, qz.rnorms)
+        tq.dequant_mse(pr, qz.idx, qz.norms)
+        scored += s.size
+    dt = time.perf_counter() - t0
+    return {"value": scored / dt, "unit": "keys scored/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{groups} of {w.groups} key groups ({groups * w.n} keys x {w.nq} queries): quantize + "
+                      f"score + stage-1 reconstruction in numpy float64, {dt:.1f} s; cores = BLAS threads "
+                      f"(elementwise numpy runs on one)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(keys shard by KV head with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import vector_quantization_quantize_amd as tqm
+    from vector_quantization_quantize_amd import workloads as wl
+
+    torch.cuda.set_device(0)
+    w = wl.WORKLOADS[args.workload]
+    keys_np = wl.keys(w, args.seed)
+    queries_np = wl.queries(w, args.seed)
+    kdtype = torch.bfloat16 if w.key_dtype == "bf16" else torch.float32
+    keys = torch.from_numpy(keys_np).to(kdtype).cuda()
+    queries = torch.from_numpy(queries_np).cuda()
+    h = tqm.tq_init(w.d, w.bits, 0)
+    total = w.total_keys
+    packed = tqm.empty_packed(h, total)
+    scores = torch.empty((w.groups, w.nq, w.n), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tqm.tq_logits_workspace_size(h, w.groups, w.nq) // 4 + 64, dtype=torch.float32,
+                     device="cuda")
+    khat = torch.empty((total, w.d), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    names = ("tq_quantize", "tq_logits", "tq_dequant_mse")
+
+    def calls():
+        return (lambda: tqm.tq_quantize(h, keys, out=packed, stream=stream),
+                lambda: tqm.tq_logits(h, queries, *packed, n=w.n, scores=scores, workspace=ws, stream=stream),
+                lambda: tqm.tq_dequant_mse(h, packed[0], packed[2], khat=khat, stream=stream))
+
+    fns = calls()
+    for _ in range(args.warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in names]
+          for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for s in range(args.steps):
+        for i, f in enumerate(fns):
+            ev[s][i][0].record(stream)
+            f()
+            ev[s][i][1].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = start.elapsed_time(stop) / args.steps
+    per = {n: float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]))
+           for i, n in enumerate(names)}
+
+    # each kernel again with the caches flushed before every launch
+    flush = torch.empty(1 << 28, dtype=torch.int32, device="cuda")  # 1 GiB > L2 + MALL
+    cold = {}
+    for i, n in enumerate(names):
+        times = []
+        for _ in range(args.cold_reps):
+            flush.zero_()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fns[i]()
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        cold[n] = float(np.median(times))
+    del flush
+
+    models = kernel_models(w)
+    scored = w.groups * w.nq * w.n
+    kern = {}
+    for n in names:
+        units = total  # every entry point processes the whole cache once
+        gbs = models[n]["bytes"] * units / (per[n] * 1e-3) / 1e9
+        tfl = models[n]["flops"] * units / (per[n] * 1e-3) / 1e12
+        gbs_cold = models[n]["bytes"] * units / (cold[n] * 1e-3) / 1e9
+        kern[n] = {"ms": round(per[n], 4), "ms_cold": round(cold[n], 4), "GBps": round(gbs, 1),
+                   "GBps_cold": round(gbs_cold, 1), "TFLOPs": round(tfl, 2),
+                   "bytes_per_key": models[n]["bytes"], "flops_per_key": models[n]["flops"]}
+    kern["tq_quantize"]["Mkeys_per_s"] = round(total / (per["tq_quantize"] * 1e-3) / 1e6, 1)
+    kern["tq_logits"]["keys_scored_per_s"] = scored / (per["tq_logits"] * 1e-3)
+    kern["tq_logits"]["keys_scored_per_s_cold"] = scored / (cold["tq_logits"] * 1e-3)
+
+    # which resource bounds each kernel as built: logits streams bytes; the
+    # quantize and reconstruction kernels run their projections on fp32 VALU
+    bound = {"tq_quantize": ("alu", FP32_VALU_PEAK_TFLOPS), "tq_logits": ("hbm", HBM_PEAK_GBS),
+             "tq_dequant_mse": ("alu", FP32_VALU_PEAK_TFLOPS)}
+    bound.update(json.loads(os.environ.get("TQ_BENCH_BOUNDS", "{}")))
+
+    def roofline(n):
+        kind, peak = bound[n]
+        if kind == "hbm":
+            ach, ach_cold, unit = kern[n]["GBps"], kern[n]["GBps_cold"], "GB/s"
+        else:
+            ach, unit = kern[n]["TFLOPs"], "TFLOP/s"
+            ach_cold = round(models[n]["flops"] * total / (cold[n] * 1e-3) / 1e12, 2)
+        return {"kernel": n, "bound": kind, "achieved": ach, "peak": peak, "unit": unit,
+                "frac": round(ach / peak, 4), "traffic": None,
+                "achieved_cold": ach_cold, "frac_cold": round(ach_cold / peak, 4)}
+
+    dominant = max(names, key=lambda n: per[n])
+    line = {
+        "metric": METRIC,
+        "value": scored / (step_ms * 1e-3),
+        "unit": "keys scored/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.description}", "keys": total, "d": w.d, "bits": w.bits,
+                   "queries": w.groups * w.nq, "key_dtype": w.key_dtype,
+                   "step": "tq_quantize + tq_logits + tq_dequant_mse over the full cache"},
+        "wall_s": round(wall, 3),
+        "kernels": kern,
+        "roofline": roofline(dominant),
+        "roofline_logits": roofline("tq_logits"),
+        "roofline_by_kernel": {n: roofline(n) for n in names},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, keys_np, queries_np, min(args.cpu_groups, w.groups), args.seed)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -334,7 +334,7 @@ hipError_t launch_logits_v1(const tq_ctx* h, const float* vw, int64_t groups, in
   const size_t lds = (kMaxLevels + size_t(8) * d) * sizeof(float);
   hipError_t e = allow_lds(logits_ref_kernel, lds);
   if (e != hipSuccess) return e;
-  dim3 grid(unsigned((n + kThreads - 1) / kThreads), unsigned(groups));
+  const dim3 grid(static_cast<uint32_t>((n + kThreads - 1) / kThreads), static_cast<uint32_t>(groups));
   hipLaunchKernelGGL(logits_ref_kernel, grid, dim3(kThreads), lds, stream, vw, nq, d, h->code_bits,
                      h->words, n, vw_stride(d), vw_half(d), codes, signs, norms, rnorms, scores, h->cb);
   return hipGetLastError();

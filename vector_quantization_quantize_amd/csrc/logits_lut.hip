@@ -1,0 +1,364 @@
+// Decode-style scoring kernel for d in (96, 128] (four 32-bit words per bit
+// plane): streams packed keys once, one key per lane, and scores the 4
+// queries of a (group, quad) per pass with byte-indexed lookup tables in LDS.
+//
+// Method ("TurboQuant digest" (juejin.cn) section 2; "TurboQuant deep review"
+// (freelamp.com), error-compensation section): the score of query q against a
+// packed key is
+//     n * ( <v, c[idx]> + rho * sqrt(pi/2) / d * <w, 2 beta - 1> ),
+// v = Pi q, w = G v.  A symmetric level set is an odd multilinear function of
+// the plane signs s_p = 2 b_p - 1, c[idx] = sum_S alpha_S prod_{p in S} s_p
+// over odd-size plane subsets S, and prod_{p in S} s_p = 2 (XOR_{p in S} b_p) - 1.
+// So every term is a signed sum <x, 2 b - 1> of a vector x (v or w) over one bit
+// word b, which a table indexed by one byte of b evaluates 8 coordinates at a
+// time:  T_x[g][byte] = sum_{i<8} (bit i of byte ? +1 : -1) x[8 g + i].
+//
+// Each workgroup first computes v and w of its 4 queries, scales each by a
+// power of two so that its norm lies in [1, 2), and stores the tables as
+// float16 (4 queries per 8-byte entry):
+//   entry (byte x, table tab (0 = v, 1 = w), position g) at x*256 + tab*128 + g*8.
+// Lane l walks the 16 byte positions starting at g = l mod 16 (its bit planes
+// are rotated by l mod 16 bytes), so the 16 lanes served by one LDS pass read
+// 16 distinct positions whose entries fill the 32 banks exactly, whatever the
+// key bytes are.  One v_perm builds the byte address (key byte -> bits 8..15,
+// 8 g -> bits 0..7).  Lookups of one word (32 coordinates) are summed in
+// float16 pairs and then added into float32 accumulators with v_dot2_f32_f16.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "tq_internal.h"
+
+namespace tqdev {
+namespace {
+
+constexpr int kLutThreads = 512;
+constexpr int kDim = 128;                 // padded vector length handled here
+constexpr int kTableBytes = 256 * 256;    // [x][tab][g] x 8 bytes = 64 KiB
+constexpr int kNibbleFloats = 16 * 2 * 16 * 4;  // one table at a time
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// stage-1 terms for B code planes, in the host's enumeration order
+// (ascending plane mask, popcount 1 or 3)
+template <int B>
+struct Terms;
+template <>
+struct Terms<1> {
+  static constexpr int count = 1;
+  static constexpr uint32_t mask[1] = {1};
+};
+template <>
+struct Terms<2> {
+  static constexpr int count = 2;
+  static constexpr uint32_t mask[2] = {1, 2};
+};
+template <>
+struct Terms<3> {
+  static constexpr int count = 4;
+  static constexpr uint32_t mask[4] = {1, 2, 4, 7};
+};
+template <>
+struct Terms<4> {
+  static constexpr int count = 8;
+  static constexpr uint32_t mask[8] = {1, 2, 4, 7, 8, 11, 13, 14};
+};
+
+struct Words {
+  uint32_t w[4];
+};
+
+template <int B>
+struct Packed {
+  uint4 plane[B];
+  uint4 sign;
+  float n, rho;
+};
+
+template <int B>
+__device__ __forceinline__ Packed<B> load_key(const uint32_t* __restrict__ codes, const uint32_t* __restrict__ signs,
+                                              const float* __restrict__ norms, const float* __restrict__ rnorms,
+                                              int64_t key) {
+  Packed<B> k;
+#pragma unroll
+  for (int p = 0; p < B; ++p) k.plane[p] = *reinterpret_cast<const uint4*>(codes + (key * B + p) * 4);
+  k.sign = *reinterpret_cast<const uint4*>(signs + key * 4);
+  k.n = norms[key];
+  k.rho = rnorms[key];
+  return k;
+}
+
+// rotate the 16-byte plane right by r bytes: out.byte[k] = in.byte[(k + r) & 15]
+__device__ __forceinline__ Words rotate(const uint4& in, bool w1, bool w2, uint32_t bs) {
+  const uint32_t a0 = w1 ? in.y : in.x;
+  const uint32_t a1 = w1 ? in.z : in.y;
+  const uint32_t a2 = w1 ? in.w : in.z;
+  const uint32_t a3 = w1 ? in.x : in.w;
+  const uint32_t u0 = w2 ? a2 : a0;
+  const uint32_t u1 = w2 ? a3 : a1;
+  const uint32_t u2 = w2 ? a0 : a2;
+  const uint32_t u3 = w2 ? a1 : a3;
+  Words out;
+  out.w[0] = __builtin_amdgcn_alignbyte(u1, u0, bs);
+  out.w[1] = __builtin_amdgcn_alignbyte(u2, u1, bs);
+  out.w[2] = __builtin_amdgcn_alignbyte(u3, u2, bs);
+  out.w[3] = __builtin_amdgcn_alignbyte(u0, u3, bs);
+  return out;
+}
+
+// v_perm selector: result byte0 = lane base byte (t & 1) of the LB word,
+// byte1 = byte (t & 3) of the plane word, bytes 2-3 = zero
+template <int t>
+__device__ __forceinline__ constexpr uint32_t perm_sel() {
+  return 0x0C0C0000u | ((4u + (t & 3)) << 8) | uint32_t(t & 1);
+}
+
+struct Entry {
+  half2_t q01, q23;
+};
+
+template <int tab>
+__device__ __forceinline__ Entry lut(const unsigned char* base, uint32_t addr) {
+  // every entry address is a multiple of 8 bytes
+  __builtin_assume((addr & 7u) == 0u);
+  const uint2 e = *reinterpret_cast<const uint2*>(base + addr + tab * 128);
+  Entry out;
+  out.q01 = __builtin_bit_cast(half2_t, e.x);
+  out.q23 = __builtin_bit_cast(half2_t, e.y);
+  return out;
+}
+
+// Empty asm that reads and rewrites the accumulators: the additions before
+// it must be issued here, so the compiler cannot defer them (keeping every
+// looked-up entry alive) to the end of the unrolled key body.
+template <int N>
+__device__ __forceinline__ void pin(half2_t (&p)[N][2]) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) asm volatile("" : "+v"(p[j][0]), "+v"(p[j][1])::"memory");
+}
+
+// copy the d x d row-major matrix `src` (d <= 128) into LDS as a zero-padded
+// 128 x 128 row-major matrix; every load of a batch issued before its stores
+__device__ __forceinline__ void stage_matrix(float* dst, const float* __restrict__ src, int d, int tid) {
+#pragma unroll
+  for (int k0 = 0; k0 < kDim * kDim / kLutThreads; k0 += 16) {
+    float tmp[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int e = tid + (k0 + k) * kLutThreads;
+      const int i = e >> 7, j = e & (kDim - 1);
+      tmp[k] = (i < d && j < d) ? src[i * d + j] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) dst[tid + (k0 + k) * kLutThreads] = tmp[k];
+  }
+}
+
+template <int B>
+__global__ void __launch_bounds__(kLutThreads, 2)
+logits_lut128_kernel(const float* __restrict__ queries, int quads, int64_t nq, int64_t n, int d,
+                     const float* __restrict__ piT, const float* __restrict__ gT,
+                     const uint32_t* __restrict__ codes, const uint32_t* __restrict__ signs,
+                     const float* __restrict__ norms, const float* __restrict__ rnorms,
+                     float* __restrict__ scores, PlaneExpansion pe, float kappa, int64_t keys_per_block) {
+  using TT = Terms<B>;
+  constexpr int NT = TT::count;
+  __shared__ __align__(16) unsigned char tabs[kTableBytes];
+  __shared__ __align__(16) float nib[kNibbleFloats];
+  __shared__ float qs[4][kDim];
+  __shared__ float vec[2][4][kDim];  // scaled v and w
+  __shared__ float scale[2][4];
+  const int tid = threadIdx.x;
+  const int64_t grp = blockIdx.y / quads;
+  const int64_t q0 = int64_t(blockIdx.y % quads) * 4;
+
+  // ---- queries -> v = Pi q -> w = G v (float32) ----
+  // Pi^T and then G^T (d x d <= 64 KiB) are staged through the table region,
+  // which is free until the tables are built; thread (q, j, hf) sums half hf
+  // of the d terms of output j of query q
+  for (int e = tid; e < 4 * kDim; e += kLutThreads) {
+    const int q = e >> 7, i = e & (kDim - 1);
+    qs[q][i] = (q0 + q < nq && i < d) ? queries[(grp * nq + q0 + q) * d + i] : 0.0f;
+  }
+  float* stage = reinterpret_cast<float*>(tabs);
+#pragma unroll
+  for (int tab = 0; tab < 2; ++tab) {
+    stage_matrix(stage, tab == 0 ? piT : gT, d, tid);
+    __syncthreads();
+    // output (q, j) for q = 0..3, j = tid mod 128: 4 chains of 128 terms
+    const int j = tid & (kDim - 1), qsel = tid >> 7;
+    const float* x = tab == 0 ? qs[qsel] : vec[0][qsel];
+    float a = 0.0f;
+#pragma unroll 16
+    for (int i = 0; i < kDim; ++i) a = fmaf(stage[i * kDim + j], x[i], a);
+    vec[tab][qsel][j] = a;
+    __syncthreads();
+  }
+  // power-of-two scale per (table, query): scaled norm in [1, 2); wave w < 8
+  // reduces vector (w >> 2, w & 3)
+  if (tid < 8 * 64) {
+    const int wv = tid >> 6, lane = tid & 63, tab = wv >> 2, q = wv & 3;
+    const float x0 = vec[tab][q][lane], x1 = vec[tab][q][lane + 64];
+    float ss = fmaf(x0, x0, x1 * x1);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+    if (lane == 0) {
+      int e = 0;
+      (void)frexpf(sqrtf(ss), &e);
+      scale[tab][q] = ss > 0.0f ? ldexpf(1.0f, 1 - e) : 1.0f;
+    }
+  }
+  __syncthreads();
+  // tables, one at a time (tab 0 = v, 1 = w).  Half-byte sums (float32):
+  // entry (hf*16 + y)*16 + g, 4 queries each, consecutive g adjacent so the
+  // byte pass reads them without bank conflicts; byte entry (x, tab, g) =
+  // low-half sum + high-half sum, rounded to float16.
+#pragma unroll
+  for (int tab = 0; tab < 2; ++tab) {
+    for (int e = tid; e < kNibbleFloats; e += kLutThreads) {
+      const int q = e & 3, gg = (e >> 2) & 15, y = (e >> 6) & 15, hf = e >> 10;
+      const float* x = &vec[tab][q][8 * gg + 4 * hf];
+      float sum = 0.0f;
+      for (int b = 0; b < 4; ++b) sum += ((y >> b) & 1) ? x[b] : -x[b];
+      nib[e] = sum * scale[tab][q];
+    }
+    __syncthreads();
+    for (int e = tid; e < 256 * 16; e += kLutThreads) {
+      const int gg = e & 15, x = e >> 4;
+      const float4 lo = *reinterpret_cast<const float4*>(nib + ((0 * 16 + (x & 15)) * 16 + gg) * 4);
+      const float4 hi = *reinterpret_cast<const float4*>(nib + ((1 * 16 + (x >> 4)) * 16 + gg) * 4);
+      const half2_t q01 = {(_Float16)(lo.x + hi.x), (_Float16)(lo.y + hi.y)};
+      const half2_t q23 = {(_Float16)(lo.z + hi.z), (_Float16)(lo.w + hi.w)};
+      *reinterpret_cast<uint2*>(tabs + x * 256 + tab * 128 + gg * 8) =
+          make_uint2(__builtin_bit_cast(uint32_t, q01), __builtin_bit_cast(uint32_t, q23));
+    }
+    __syncthreads();
+  }
+
+  // per-lane rotation and address bases
+  const uint32_t r = uint32_t(tid) & 15u;
+  const bool w1 = (r >> 2) & 1u, w2 = (r >> 3) & 1u;
+  const uint32_t bs = r & 3u;
+  uint32_t lb[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) lb[k] = (((2u * k + r) & 15u) * 8u) | ((((2u * k + 1u + r) & 15u) * 8u) << 8);
+  float inv_v[4], inv_w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    inv_v[q] = 1.0f / scale[0][q];
+    inv_w[q] = kappa / scale[1][q];
+  }
+  const half2_t pick_lo = {(_Float16)1.0f, (_Float16)0.0f};
+  const half2_t pick_hi = {(_Float16)0.0f, (_Float16)1.0f};
+
+  const int qc = int(nq - q0 < 4 ? nq - q0 : 4);
+  const int64_t kbeg = int64_t(blockIdx.x) * keys_per_block;
+  const int64_t kend = kbeg + keys_per_block < n ? kbeg + keys_per_block : n;
+  int64_t t = kbeg + tid;
+  Packed<B> cur;
+  if (t < kend) cur = load_key<B>(codes, signs, norms, rnorms, grp * n + t);
+  for (; t < kend; t += kLutThreads) {
+    Packed<B> nxt;
+    if (t + kLutThreads < kend) nxt = load_key<B>(codes, signs, norms, rnorms, grp * n + t + kLutThreads);
+    Words pl[B];
+#pragma unroll
+    for (int p = 0; p < B; ++p) pl[p] = rotate(cur.plane[p], w1, w2, bs);
+    const Words sg = rotate(cur.sign, w1, w2, bs);
+    Words term[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t x = 0;
+#pragma unroll
+        for (int p = 0; p < B; ++p)
+          if (TT::mask[j] & (1u << p)) x ^= pl[p].w[i];
+        term[j].w[i] = x;
+      }
+    }
+    float acc[NT + 1][4];
+#pragma unroll
+    for (int j = 0; j <= NT; ++j) acc[j][0] = acc[j][1] = acc[j][2] = acc[j][3] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // one 32-bit word (4 byte steps) at a time
+      half2_t part[NT + 1][2];
+#pragma unroll
+      for (int j = 0; j <= NT; ++j) part[j][0] = part[j][1] = half2_t{(_Float16)0.0f, (_Float16)0.0f};
+#define TQ_STEP(T)                                                                                   \
+  {                                                                                                  \
+    _Pragma("unroll") for (int j = 0; j < NT; ++j) {                                                 \
+      const Entry e = lut<0>(tabs, __builtin_amdgcn_perm(term[j].w[i], lb[(T) >> 1], perm_sel<(T)>())); \
+      part[j][0] += e.q01;                                                                           \
+      part[j][1] += e.q23;                                                                           \
+    }                                                                                                \
+    const Entry e = lut<1>(tabs, __builtin_amdgcn_perm(sg.w[i], lb[(T) >> 1], perm_sel<(T)>()));     \
+    part[NT][0] += e.q01;                                                                            \
+    part[NT][1] += e.q23;                                                                            \
+    if ((T) & 1) pin<NT + 1>(part);                                                                  \
+  }
+      // steps 4i .. 4i+3; lb and the selector depend only on (T & 3) and (T >> 1)
+      if (i == 0) { TQ_STEP(0) TQ_STEP(1) TQ_STEP(2) TQ_STEP(3) }
+      if (i == 1) { TQ_STEP(4) TQ_STEP(5) TQ_STEP(6) TQ_STEP(7) }
+      if (i == 2) { TQ_STEP(8) TQ_STEP(9) TQ_STEP(10) TQ_STEP(11) }
+      if (i == 3) { TQ_STEP(12) TQ_STEP(13) TQ_STEP(14) TQ_STEP(15) }
+#undef TQ_STEP
+#pragma unroll
+      for (int j = 0; j <= NT; ++j) {
+        acc[j][0] = __builtin_amdgcn_fdot2(part[j][0], pick_lo, acc[j][0], false);
+        acc[j][1] = __builtin_amdgcn_fdot2(part[j][0], pick_hi, acc[j][1], false);
+        acc[j][2] = __builtin_amdgcn_fdot2(part[j][1], pick_lo, acc[j][2], false);
+        acc[j][3] = __builtin_amdgcn_fdot2(part[j][1], pick_hi, acc[j][3], false);
+      }
+    }
+    const float corr = cur.rho;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float s1 = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NT; ++j) s1 = fmaf(pe.alpha[j], acc[j][q], s1);
+      const float sw = acc[NT][q] * inv_w[q];
+      if (q < qc) scores[(grp * nq + q0 + q) * n + t] = cur.n * fmaf(corr, sw, s1 * inv_v[q]);
+    }
+    cur = nxt;
+  }
+}
+
+template <int B>
+hipError_t launch_b(const tq_ctx* h, const float* queries, int64_t groups, int64_t nq, const uint32_t* codes,
+                    const uint32_t* signs, const float* norms, const float* rnorms, int64_t n, float* scores,
+                    hipStream_t stream) {
+  const int64_t quads = (nq + 3) / 4;
+  const int64_t ys = groups * quads;
+  if (ys > 65535) return hipErrorInvalidConfiguration;
+  // about two blocks per CU (256 CUs), whole multiples of the block size
+  int64_t chunks = (512 + ys - 1) / ys;
+  int64_t kpb = (n + chunks - 1) / chunks;
+  kpb = (kpb + kLutThreads - 1) / kLutThreads * kLutThreads;
+  if (kpb < kLutThreads) kpb = kLutThreads;
+  chunks = (n + kpb - 1) / kpb;
+  const float kappa = 1.2533141373155002512f / float(h->d);
+  const dim3 grid(static_cast<uint32_t>(chunks), static_cast<uint32_t>(ys));
+  hipLaunchKernelGGL(logits_lut128_kernel<B>, grid, dim3(kLutThreads), 0, stream, queries, int(quads), nq, n,
+                     h->d, h->d_piT, h->d_gT, codes, signs, norms, rnorms, scores, h->planes, kappa, kpb);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool logits_lut128_supported(const tq_ctx* h) {
+  return h->words == 4 && h->d <= kDim && h->code_bits >= 1 && h->code_bits <= 4;
+}
+
+hipError_t launch_logits_lut128(const tq_ctx* h, const float* queries, int64_t groups, int64_t nq,
+                                const uint32_t* codes, const uint32_t* signs, const float* norms,
+                                const float* rnorms, int64_t n, float* scores, hipStream_t stream) {
+  switch (h->code_bits) {
+    case 1: return launch_b<1>(h, queries, groups, nq, codes, signs, norms, rnorms, n, scores, stream);
+    case 2: return launch_b<2>(h, queries, groups, nq, codes, signs, norms, rnorms, n, scores, stream);
+    case 3: return launch_b<3>(h, queries, groups, nq, codes, signs, norms, rnorms, n, scores, stream);
+    case 4: return launch_b<4>(h, queries, groups, nq, codes, signs, norms, rnorms, n, scores, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace tqdev

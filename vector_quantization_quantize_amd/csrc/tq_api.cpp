@@ -96,6 +96,11 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 }  // namespace
 
+bool tqdev::force_reference_kernels() {
+  const char* v = std::getenv("TQ_KERNELS");
+  return v && std::strcmp(v, "ref") == 0;
+}
+
 extern "C" {
 
 const char* tq_strerror(int code) {
@@ -245,10 +250,16 @@ int tq_logits(tq_handle h, const float* queries, int64_t groups, int64_t nq, con
   if (groups > 65535) return TQ_EUNSUPPORTED;
   if (check_device(h) != TQ_OK) return TQ_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float* vw = static_cast<float*>(workspace);
-  hipError_t e = tqdev::launch_query_prep(h, queries, groups * nq, vw, s);
-  if (e != hipSuccess) return TQ_EHIP;
-  e = tqdev::launch_logits_v1(h, vw, groups, nq, codes, signs, norms, rnorms, n, scores, s);
+  hipError_t e;
+  if (!tqdev::force_reference_kernels() && tqdev::logits_lut128_supported(h)) {
+    // query transform fused into the scoring kernel; workspace unused
+    e = tqdev::launch_logits_lut128(h, queries, groups, nq, codes, signs, norms, rnorms, n, scores, s);
+  } else {
+    float* vw = static_cast<float*>(workspace);
+    e = tqdev::launch_query_prep(h, queries, groups * nq, vw, s);
+    if (e != hipSuccess) return TQ_EHIP;
+    e = tqdev::launch_logits_v1(h, vw, groups, nq, codes, signs, norms, rnorms, n, scores, s);
+  }
   return e == hipSuccess ? TQ_OK : TQ_EHIP;
 }
 

@@ -58,6 +58,14 @@ hipError_t launch_logits_v1(const tq_ctx* h, const float* vw, int64_t groups, in
                             const uint32_t* codes, const uint32_t* signs, const float* norms,
                             const float* rnorms, int64_t n, float* scores, hipStream_t stream);
 
+bool logits_lut128_supported(const tq_ctx* h);
+hipError_t launch_logits_lut128(const tq_ctx* h, const float* queries, int64_t groups, int64_t nq,
+                                const uint32_t* codes, const uint32_t* signs, const float* norms,
+                                const float* rnorms, int64_t n, float* scores, hipStream_t stream);
+
+// TQ_KERNELS=ref selects the straightforward kernels everywhere (A/B checks)
+bool force_reference_kernels();
+
 hipError_t launch_dequant_v1(const tq_ctx* h, const uint32_t* codes, const float* norms, int64_t n,
                              float* khat, hipStream_t stream);
 
