@@ -1,0 +1,86 @@
+"""Parity of the tuned d = 128 kernels (matrix-core quantize for bf16 keys,
+lookup-table scorer) with the CPU oracle, on ragged tile counts, every bit
+width, zero keys, exact rescaling and strided rows.  Expected values come only
+from ``oracle``; rules from ``oracle.parity``."""
+import os
+
+import numpy as np
+import pytest
+
+from oracle import params as P
+from oracle import tq
+from tests.test_gpu_parity import _announce, _cpu, _dev, check_full
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import vector_quantization_quantize_amd as tqm
+    from vector_quantization_quantize_amd import workloads as wl
+    return torch, tqm, wl
+
+
+def _bf16_keys(torch, rs, n, d, scale_spread=1.0):
+    k = rs.standard_normal((n, d)) * np.exp(scale_spread * rs.standard_normal((n, 1)))
+    return torch.tensor(k, dtype=torch.float32).bfloat16().float().numpy()
+
+
+@pytest.mark.parametrize("bits,groups,n,nq", [(2, 1, 1, 1), (3, 2, 31, 4), (3, 1, 33, 5), (4, 3, 1000, 4),
+                                              (5, 1, 257, 8), (3, 1, 4097, 2)])
+def test_d128_bf16_fast_path(env, bits, groups, n, nq):
+    torch, tqm, _ = env
+    _announce(f"fast path d=128 bf16 bits={bits} groups={groups} n={n} nq={nq}")
+    rs = np.random.default_rng(bits * 1000 + n)
+    keys = _bf16_keys(torch, rs, groups * n, 128)
+    keys[0] = 0.0
+    queries = rs.standard_normal((groups, nq, 128)).astype(np.float32)
+    rep = check_full(env, 128, bits, keys, queries, key_dtype="bf16", seed=bits)
+    print("mismatches", rep.code_mismatch, rep.sign_mismatch, "cascade", rep.cascade_keys)
+
+
+def test_fast_quantize_exact_rescaling_and_strides(env):
+    torch, tqm, _ = env
+    _announce("fast path: power-of-two rescaling and row strides")
+    rs = np.random.default_rng(11)
+    keys = _bf16_keys(torch, rs, 999, 128)
+    h = tqm.tq_init(128, 3, 0)
+    base = torch.from_numpy(keys).bfloat16().cuda()
+    a = tqm.tq_quantize(h, base)
+    b = tqm.tq_quantize(h, base * 2.0 ** 40)
+    c = tqm.tq_quantize(h, base * 2.0 ** -40)
+    for x, y, z in zip(a[:2], b[:2], c[:2]):
+        assert torch.equal(x, y) and torch.equal(x, z)
+    assert torch.equal(a[3], b[3]) and torch.equal(a[3], c[3])
+    assert torch.equal(a[2] * 2.0 ** 40, b[2]) and torch.equal(a[2] * 2.0 ** -40, c[2])
+    # aligned row stride (fast path) and an odd one (general path) agree
+    wide = torch.zeros((999, 136), dtype=torch.bfloat16, device="cuda")
+    wide[:, :128] = base
+    odd = torch.zeros((999, 131), dtype=torch.bfloat16, device="cuda")
+    odd[:, :128] = base
+    d1 = tqm.tq_quantize(h, wide[:, :128])
+    d2 = tqm.tq_quantize(h, odd[:, :128])
+    for x, y in zip(a, d1):
+        assert torch.equal(x, y)
+    pr = P.init(128, 3, 0)
+    from oracle import parity
+    qz = tq.quantize(pr, keys.astype(np.float64))
+    rep = parity.compare_quantize(pr, qz, *(_cpu(t) for t in d2))
+    assert rep.ok(), rep
+
+
+def test_reference_and_fast_kernels_both_match_oracle(env):
+    torch, tqm, wl = env
+    _announce("reference kernels (TQ_KERNELS=ref) on the long-context generator")
+    w = wl.WORKLOADS["long_context"].scaled(n=2048, groups=2)
+    keys = wl.keys(w)
+    queries = wl.queries(w)
+    os.environ["TQ_KERNELS"] = "ref"
+    try:
+        check_full(env, w.d, w.bits, keys, queries, key_dtype="bf16")
+    finally:
+        del os.environ["TQ_KERNELS"]
+    check_full(env, w.d, w.bits, keys, queries, key_dtype="bf16")

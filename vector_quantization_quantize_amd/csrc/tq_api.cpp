@@ -27,6 +27,94 @@ void free_device(tq_ctx* h) {
     if (*p) (void)hipFree(*p);
     *p = nullptr;
   }
+  uint16_t** frags[] = {&h->d_pi_frag, &h->d_g_frag, &h->d_dq_frag};
+  for (uint16_t** p : frags) {
+    if (*p) (void)hipFree(*p);
+    *p = nullptr;
+  }
+}
+
+uint16_t bf16_rne(float x) {
+  uint32_t u;
+  std::memcpy(&u, &x, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+float bf16_value(uint16_t b) {
+  const uint32_t u = uint32_t(b) << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+uint16_t f16_bits(float x) {
+  const _Float16 h = static_cast<_Float16>(x);
+  uint16_t b;
+  std::memcpy(&b, &h, 2);
+  return b;
+}
+
+float f16_value(uint16_t b) {
+  _Float16 h;
+  std::memcpy(&h, &b, 2);
+  return static_cast<float>(h);
+}
+
+int upload_u16(uint16_t** dst, const std::vector<uint16_t>& src) {
+  const size_t bytes = src.size() * sizeof(uint16_t);
+  if (hipMalloc(reinterpret_cast<void**>(dst), bytes) != hipSuccess) {
+    *dst = nullptr;
+    return TQ_ENOMEM;
+  }
+  return hipMemcpy(*dst, src.data(), bytes, hipMemcpyHostToDevice) == hipSuccess ? TQ_OK : TQ_EHIP;
+}
+
+// Register fragments of the d = 128 matrix-core quantize kernel (see
+// quantize_mfma.hip).  Pi: three bf16 pieces with hi + mid + lo == Pi
+// exactly; lane l of word w, step s holds Pi[32w + l%32][16s + 8(l/32) + e].
+// G: two f16 pieces of 2^10 G; lane l holds G[32w + l%32][j(s, l/32, e)] with
+// j(s, g, e) = 32(s/2) + 16(s%2) + 8(e/4) + 4g + e%4, the coordinate that lane
+// group g holds in accumulator element 8(s%2) + e of word s/2.
+int build_fragments(tq_ctx* h) {
+  const int d = h->d;
+  if (d != 128) return TQ_OK;
+  std::vector<uint16_t> pf(size_t(4) * 8 * 3 * 64 * 8), gf(size_t(4) * 8 * 2 * 64 * 8);
+  for (int w = 0; w < 4; ++w)
+    for (int s = 0; s < 8; ++s)
+      for (int l = 0; l < 64; ++l)
+        for (int e = 0; e < 8; ++e) {
+          const int row = 32 * w + (l & 31);
+          const float x = h->pi[size_t(row) * d + 16 * s + 8 * (l >> 5) + e];
+          const uint16_t hi = bf16_rne(x);
+          const float r1 = x - bf16_value(hi);
+          const uint16_t mid = bf16_rne(r1);
+          const uint16_t lo = bf16_rne(r1 - bf16_value(mid));
+          const uint16_t pieces[3] = {hi, mid, lo};
+          for (int q = 0; q < 3; ++q) pf[(((size_t(w) * 8 + s) * 3 + q) * 64 + l) * 8 + e] = pieces[q];
+          const int j = 32 * (s >> 1) + 16 * (s & 1) + 8 * (e >> 2) + 4 * (l >> 5) + (e & 3);
+          const float gs = h->g[size_t(row) * d + j] * 1024.0f;
+          const uint16_t ghi = f16_bits(gs);
+          const uint16_t glo = f16_bits(gs - f16_value(ghi));
+          gf[(((size_t(w) * 8 + s) * 2 + 0) * 64 + l) * 8 + e] = ghi;
+          gf[(((size_t(w) * 8 + s) * 2 + 1) * 64 + l) * 8 + e] = glo;
+        }
+  // stage-1 reconstruction: lane l of word w, step s holds
+  // 2^12 Pi[16s + 8(l/32) + e][32w + l%32] (B operand, N = output coordinate)
+  std::vector<uint16_t> df(size_t(4) * 8 * 2 * 64 * 8);
+  for (int w = 0; w < 4; ++w)
+    for (int s = 0; s < 8; ++s)
+      for (int l = 0; l < 64; ++l)
+        for (int e = 0; e < 8; ++e) {
+          const float x = h->pi[size_t(16 * s + 8 * (l >> 5) + e) * d + 32 * w + (l & 31)] * 4096.0f;
+          const uint16_t hi = f16_bits(x);
+          df[(((size_t(w) * 8 + s) * 2 + 0) * 64 + l) * 8 + e] = hi;
+          df[(((size_t(w) * 8 + s) * 2 + 1) * 64 + l) * 8 + e] = f16_bits(x - f16_value(hi));
+        }
+  int rc = upload_u16(&h->d_pi_frag, pf);
+  if (rc != TQ_OK) return rc;
+  if ((rc = upload_u16(&h->d_g_frag, gf)) != TQ_OK) return rc;
+  return upload_u16(&h->d_dq_frag, df);
 }
 
 int upload(float** dst, const std::vector<float>& src) {
@@ -83,7 +171,7 @@ int finish_init(tq_ctx* h) {
   if ((rc = upload(&h->d_piT, transpose(h->pi, d))) != TQ_OK) return rc;
   if ((rc = upload(&h->d_g, h->g)) != TQ_OK) return rc;
   if ((rc = upload(&h->d_gT, transpose(h->g, d))) != TQ_OK) return rc;
-  return TQ_OK;
+  return build_fragments(h);
 }
 
 int check_device(const tq_ctx* h) {
@@ -229,8 +317,11 @@ int tq_quantize(tq_handle h, const void* keys, int32_t key_dtype, int64_t n, int
   if (!keys || !codes || !signs || !norms || !rnorms || ldk < h->d) return TQ_EINVAL;
   if (!aligned4(codes) || !aligned4(signs) || !aligned4(norms) || !aligned4(rnorms)) return TQ_EINVAL;
   if (check_device(h) != TQ_OK) return TQ_EINVAL;
-  const hipError_t e = tqdev::launch_quantize_v1(h, keys, key_dtype, n, ldk, codes, signs, norms, rnorms,
-                                                 static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e =
+      (!tqdev::force_reference_kernels() && tqdev::quantize_mfma128_supported(h, keys, key_dtype, ldk))
+          ? tqdev::launch_quantize_mfma128(h, keys, n, ldk, codes, signs, norms, rnorms, s)
+          : tqdev::launch_quantize_v1(h, keys, key_dtype, n, ldk, codes, signs, norms, rnorms, s);
   return e == hipSuccess ? TQ_OK : TQ_EHIP;
 }
 
@@ -269,7 +360,10 @@ int tq_dequant_mse(tq_handle h, const uint32_t* codes, const float* norms, int64
   if (n == 0) return TQ_OK;
   if (!codes || !norms || !khat) return TQ_EINVAL;
   if (check_device(h) != TQ_OK) return TQ_EINVAL;
-  const hipError_t e = tqdev::launch_dequant_v1(h, codes, norms, n, khat, static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = (!tqdev::force_reference_kernels() && tqdev::dequant_mfma128_supported(h))
+                           ? tqdev::launch_dequant_mfma128(h, codes, norms, n, khat, s)
+                           : tqdev::launch_dequant_v1(h, codes, norms, n, khat, s);
   return e == hipSuccess ? TQ_OK : TQ_EHIP;
 }
 

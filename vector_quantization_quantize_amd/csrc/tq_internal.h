@@ -40,6 +40,10 @@ struct tq_ctx {
   float* d_piT = nullptr;  // Pi^T row-major: d_piT[i*d + j] = Pi[j][i]
   float* d_g = nullptr;    // G   row-major
   float* d_gT = nullptr;   // G^T row-major
+  // d = 128 only: register fragments of the matrix-core quantize kernel
+  uint16_t* d_pi_frag = nullptr;  // [word 4][step 8][piece 3][lane 64][8] bf16 pieces of Pi
+  uint16_t* d_g_frag = nullptr;   // [word 4][step 8][piece 2][lane 64][8] f16 pieces of 2^10 G
+  uint16_t* d_dq_frag = nullptr;  // [word 4][step 8][piece 2][lane 64][8] f16 pieces of 2^12 Pi (B operand)
   tqdev::Codebook cb{};
   tqdev::PlaneExpansion planes{};
 };
@@ -62,6 +66,14 @@ bool logits_lut128_supported(const tq_ctx* h);
 hipError_t launch_logits_lut128(const tq_ctx* h, const float* queries, int64_t groups, int64_t nq,
                                 const uint32_t* codes, const uint32_t* signs, const float* norms,
                                 const float* rnorms, int64_t n, float* scores, hipStream_t stream);
+
+bool quantize_mfma128_supported(const tq_ctx* h, const void* keys, int key_dtype, int64_t ldk);
+hipError_t launch_quantize_mfma128(const tq_ctx* h, const void* keys, int64_t n, int64_t ldk, uint32_t* codes,
+                                   uint32_t* signs, float* norms, float* rnorms, hipStream_t stream);
+
+bool dequant_mfma128_supported(const tq_ctx* h);
+hipError_t launch_dequant_mfma128(const tq_ctx* h, const uint32_t* codes, const float* norms, int64_t n,
+                                  float* khat, hipStream_t stream);
 
 // TQ_KERNELS=ref selects the straightforward kernels everywhere (A/B checks)
 bool force_reference_kernels();
