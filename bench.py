@@ -38,9 +38,27 @@ def parse():
     ap.add_argument("--workload", default="long_context")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cold-reps", type=int, default=10, help="flushed-cache reps per kernel")
-    ap.add_argument("--cpu-groups", type=int, default=2, help="key groups timed on the CPU oracle")
+    ap.add_argument("--cpu-groups", type=int, default=24, help="key groups timed on the CPU oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain device-to-device copy of exactly 1 GiB, five times: under
+    rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE per dispatch give the factor
+    between counter readings and bytes moved."""
+    import torch
+    torch.cuda.set_device(0)
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": nbytes, "copy_calibration_bytes_written": nbytes,
+                      "dispatches": 5}), flush=True)
 
 
 def kernel_models(w):
@@ -54,6 +72,25 @@ def kernel_models(w):
         "tq_logits": {"bytes": packed + 4 * w.nq, "flops": 4 * w.d * w.nq},
         "tq_dequant_mse": {"bytes": 4 * (w.bits - 1) * words + 4 + 4 * w.d, "flops": 2 * w.d * w.d},
     }
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary, for every kernel whose source is unchanged since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    out = {}
+    if not os.path.exists(path):
+        return out
+    for line in open(path):
+        if line.startswith("#") or not line.strip():
+            continue
+        fields = dict(f.split("=", 1) for f in line.split()[1:])
+        entry = line.split()[0]
+        src = os.path.join(ROOT, fields["source"])
+        if os.path.exists(src) and hashlib.sha1(open(src, "rb").read()).hexdigest() == fields["sha1"]:
+            out[entry] = int(float(fields["fetch_bytes"]) + float(fields["write_bytes"]))
+    return out
 
 
 def cpu_baseline(w, keys_np, queries_np, groups, seed):
@@ -84,6 +121,9 @@ def cpu_baseline(w, keys_np, queries_np, groups, seed):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(keys shard by KV head with no exchange; see the design notes)", file=sys.stderr)
@@ -170,11 +210,16 @@ def main():
     kern["tq_logits"]["keys_scored_per_s"] = scored / (per["tq_logits"] * 1e-3)
     kern["tq_logits"]["keys_scored_per_s_cold"] = scored / (cold["tq_logits"] * 1e-3)
 
-    # which resource bounds each kernel as built: logits streams bytes; the
-    # quantize and reconstruction kernels run their projections on fp32 VALU
-    bound = {"tq_quantize": ("alu", FP32_VALU_PEAK_TFLOPS), "tq_logits": ("hbm", HBM_PEAK_GBS),
-             "tq_dequant_mse": ("alu", FP32_VALU_PEAK_TFLOPS)}
-    bound.update(json.loads(os.environ.get("TQ_BENCH_BOUNDS", "{}")))
+    # which resource bounds each kernel as built at d = 128: logits streams
+    # bytes; quantize runs its two projections on the matrix cores (6 f16/bf16
+    # passes of 2 d^2 for 4 d^2 useful flops per key); the reconstruction
+    # writes 512 B per key and is bound by HBM writes
+    bound = {"tq_quantize": ("mfma", BF16_MFMA_PEAK_TFLOPS), "tq_logits": ("hbm", HBM_PEAK_GBS),
+             "tq_dequant_mse": ("hbm", HBM_PEAK_GBS)}
+    terms = {1: 1, 2: 2, 3: 4, 4: 8}[w.bits - 1]  # sign-plane terms of the level set
+    raw_passes = {"tq_quantize": 12 * w.d * w.d, "tq_dequant_mse": terms * 4 * w.d * w.d}
+    for n, f in raw_passes.items():
+        kern[n]["raw_mfma_TFLOPs"] = round(f * total / (per[n] * 1e-3) / 1e12, 2)
 
     def roofline(n):
         kind, peak = bound[n]
@@ -184,9 +229,10 @@ def main():
             ach, unit = kern[n]["TFLOPs"], "TFLOP/s"
             ach_cold = round(models[n]["flops"] * total / (cold[n] * 1e-3) / 1e12, 2)
         return {"kernel": n, "bound": kind, "achieved": ach, "peak": peak, "unit": unit,
-                "frac": round(ach / peak, 4), "traffic": None,
+                "frac": round(ach / peak, 4), "traffic": traffic.get(n),
                 "achieved_cold": ach_cold, "frac_cold": round(ach_cold / peak, 4)}
 
+    traffic = measured_traffic(args.workload)
     dominant = max(names, key=lambda n: per[n])
     line = {
         "metric": METRIC,
