@@ -93,19 +93,29 @@ dequant_mfma128_kernel(const uint32_t* __restrict__ codes, const float* __restri
 #pragma unroll
   for (int j = 0; j < NT; ++j) alpha[j] = pe.alpha[j] * kPiScaleInv;
 
-  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+  // packed codes and norm of this lane's key, one tile ahead
+  auto fetch = [&](int64_t tile, uint4 (&v)[B], float& nv) {
     const int64_t key = tile * 32 + kl;
-    const bool valid = key < n;
+    const bool ok = tile < tiles && key < n;
+#pragma unroll
+    for (int p = 0; p < B; ++p)
+      v[p] = ok ? *reinterpret_cast<const uint4*>(codes + (key * B + p) * 4) : make_uint4(0u, 0u, 0u, 0u);
+    nv = ok ? norms[key] : 0.0f;
+  };
+  uint4 nxt[B];
+  float nxt_n;
+  fetch(blockIdx.x, nxt, nxt_n);
+  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
     uint32_t pl[B][4];
 #pragma unroll
     for (int p = 0; p < B; ++p) {
-      const uint4 v = valid ? *reinterpret_cast<const uint4*>(codes + (key * B + p) * 4) : make_uint4(0u, 0u, 0u, 0u);
-      pl[p][0] = v.x;
-      pl[p][1] = v.y;
-      pl[p][2] = v.z;
-      pl[p][3] = v.w;
+      pl[p][0] = nxt[p].x;
+      pl[p][1] = nxt[p].y;
+      pl[p][2] = nxt[p].z;
+      pl[p][3] = nxt[p].w;
     }
-    const float nk = valid ? norms[key] : 0.0f;
+    const float nk = nxt_n;
+    fetch(tile + gridDim.x, nxt, nxt_n);
     f32x16 acc[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[j] = f32x16{};

@@ -44,69 +44,27 @@ constexpr int kQThreads = 256;
 constexpr int kSteps = 8;            // K = 128 in steps of 16
 constexpr float kResidualScale = 4096.0f;
 
-// Codebook values held in scalar registers.  Reading them through
-// readfirstlane keeps them out of memory, so the per-lane selects below stay
-// v_cndmask instructions instead of being folded into indexed loads from the
-// kernel-argument segment.
-struct RegCodebook {
-  float c[kMaxLevels];
-  float t[kMaxLevels];
-};
-
-__device__ __forceinline__ float uniform(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
-}
-
-__device__ __forceinline__ RegCodebook to_registers(const Codebook& cb, int levels) {
-  RegCodebook r;
+// Binary descent over the ascending thresholds held in LDS: at level p the
+// candidate index is idx + 2^p and its lower threshold t[idx + 2^p - 1]
+// (a tie goes to the upper cell), so idx = #{ i : t_i <= z } after B
+// levels.  Per-lane LDS reads keep the descent free of selects, which the
+// compiler would otherwise turn into divergent branches; the 31 table
+// entries sit in distinct banks.
+template <int B>
+__device__ __forceinline__ int descend(float z, const float* tt) {
+  int idx = 0;
 #pragma unroll
-  for (int i = 0; i < kMaxLevels; ++i) {
-    r.c[i] = i < levels ? uniform(cb.c[i]) : 0.0f;
-    r.t[i] = i + 1 < levels ? uniform(cb.t[i]) : 0.0f;
-  }
-  return r;
+  for (int p = B - 1; p >= 0; --p) idx += (z >= tt[idx + (1 << p) - 1]) ? (1 << p) : 0;
+  return idx;
 }
 
-// Binary descent over the ascending thresholds: idx = #{ i : t_i <= z }
-// (a tie goes to the upper cell), and the level c[idx] picked by a select
-// tree over the same bit decisions.  Both are written as trees of
-// independent conditions so that they stay v_cndmask instructions.
-template <int B>
-struct Decision {
-  int idx;
-  float level;
-};
-
-template <int B>
-__device__ __forceinline__ Decision<B> decide(float z, const RegCodebook& cb) {
-  if constexpr (B == 1) {
-    const bool b0 = z >= cb.t[0];
-    return {int(b0), b0 ? cb.c[1] : cb.c[0]};
-  } else if constexpr (B == 2) {
-    const bool b1 = z >= cb.t[1];
-    const bool b0 = z >= (b1 ? cb.t[2] : cb.t[0]);
-    const float c = b1 ? (b0 ? cb.c[3] : cb.c[2]) : (b0 ? cb.c[1] : cb.c[0]);
-    return {2 * int(b1) + int(b0), c};
-  } else if constexpr (B == 3) {
-    const bool b2 = z >= cb.t[3];
-    const bool b1 = z >= (b2 ? cb.t[5] : cb.t[1]);
-    const bool b0 = z >= (b2 ? (b1 ? cb.t[6] : cb.t[4]) : (b1 ? cb.t[2] : cb.t[0]));
-    const float c = b2 ? (b1 ? (b0 ? cb.c[7] : cb.c[6]) : (b0 ? cb.c[5] : cb.c[4]))
-                       : (b1 ? (b0 ? cb.c[3] : cb.c[2]) : (b0 ? cb.c[1] : cb.c[0]));
-    return {4 * int(b2) + 2 * int(b1) + int(b0), c};
-  } else {
-    const bool b3 = z >= cb.t[7];
-    const bool b2 = z >= (b3 ? cb.t[11] : cb.t[3]);
-    const bool b1 = z >= (b3 ? (b2 ? cb.t[13] : cb.t[9]) : (b2 ? cb.t[5] : cb.t[1]));
-    const float t0 = b3 ? (b2 ? (b1 ? cb.t[14] : cb.t[12]) : (b1 ? cb.t[10] : cb.t[8]))
-                        : (b2 ? (b1 ? cb.t[6] : cb.t[4]) : (b1 ? cb.t[2] : cb.t[0]));
-    const bool b0 = z >= t0;
-    const float c8 = b2 ? (b1 ? (b0 ? cb.c[15] : cb.c[14]) : (b0 ? cb.c[13] : cb.c[12]))
-                        : (b1 ? (b0 ? cb.c[11] : cb.c[10]) : (b0 ? cb.c[9] : cb.c[8]));
-    const float c0 = b2 ? (b1 ? (b0 ? cb.c[7] : cb.c[6]) : (b0 ? cb.c[5] : cb.c[4]))
-                        : (b1 ? (b0 ? cb.c[3] : cb.c[2]) : (b0 ? cb.c[1] : cb.c[0]));
-    return {8 * int(b3) + 4 * int(b2) + 2 * int(b1) + int(b0), b3 ? c8 : c0};
-  }
+// Lane bits are gathered in accumulator order (element r at bit r); element
+// r sits at row 8(r/4) + 4g + r%4 of the word, so nibble j moves to bits
+// [8j + 4g, 8j + 4g + 4).  The partner lane (g ^ 1) fills the other nibbles.
+__device__ __forceinline__ uint32_t spread_nibbles(uint32_t x, int g) {
+  x = (x | (x << 8)) & 0x00FF00FFu;
+  x = (x | (x << 4)) & 0x0F0F0F0Fu;
+  return x << (4 * g);
 }
 
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
@@ -117,7 +75,7 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
 template <int B>
 __global__ void __launch_bounds__(kQThreads, 2)
 quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ldk,
-                        const uint4* __restrict__ pi_frag, const uint4* __restrict__ g_frag, Codebook cb_arg,
+                        const uint4* __restrict__ pi_frag, const uint4* __restrict__ g_frag, Codebook cb,
                         uint32_t* __restrict__ codes, uint32_t* __restrict__ signs, float* __restrict__ norms,
                         float* __restrict__ rnorms, int64_t tiles) {
   // residual exchange [buf][piece][step][lane group][key] (8 halves each)
@@ -127,8 +85,8 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
   // key tiles, double buffered: 32 rows of 128 bf16, row stride 272 bytes so
   // that the 8 lanes of one LDS pass (8 consecutive keys) hit distinct banks
   __shared__ uint4 ktile[2][32][17];
+  __shared__ float tabc[kMaxLevels], tabt[kMaxLevels];
 
-  const RegCodebook rcb = to_registers(cb_arg, 1 << B);
   const int w = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int kl = lane & 31;
@@ -144,6 +102,10 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
     for (int q = 0; q < 2; ++q) ag[s][q] = __builtin_bit_cast(f16x8, g_frag[((w * kSteps + s) * 2 + q) * 64 + lane]);
   }
 
+  if (threadIdx.x < kMaxLevels) {
+    tabc[threadIdx.x] = cb.c[threadIdx.x];
+    tabt[threadIdx.x] = cb.t[threadIdx.x];
+  }
   // thread t stages bytes [32 (t % 8), +32) of key t / 8 of a tile
   const int sk = threadIdx.x >> 3, sc = threadIdx.x & 7;
   auto fetch = [&](int64_t tile, uint4& a, uint4& b) {
@@ -206,13 +168,11 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int r = 8 * h + e + u;
-          const int bit = 8 * (r >> 2) + 4 * g + (r & 3);
           const float z = acc[r] * inv;
-          const Decision<B> dec = decide<B>(z, rcb);
-          const int idx = dec.idx;
-          const float res = z - dec.level;
+          const int idx = descend<B>(z, tabt);
+          const float res = z - tabc[idx];
 #pragma unroll
-          for (int p = 0; p < B; ++p) cw[p] |= uint32_t((idx >> p) & 1) << bit;
+          for (int p = 0; p < B; ++p) cw[p] |= uint32_t((idx >> p) & 1) << r;
           rr = fmaf(res, res, rr);
           rs[u] = res * kResidualScale;
         }
@@ -224,7 +184,10 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
       xb[buf][1][2 * w + h][g][kl] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     }
 #pragma unroll
-    for (int p = 0; p < B; ++p) cw[p] |= __shfl_xor(cw[p], 32);
+    for (int p = 0; p < B; ++p) {
+      cw[p] = spread_nibbles(cw[p], g);
+      cw[p] |= __shfl_xor(cw[p], 32);
+    }
     rr += __shfl_xor(rr, 32);
     if (g == 0) {
       rsq[buf][w][kl] = rr;
@@ -251,7 +214,8 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
     }
     uint32_t sw = 0u;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sw |= uint32_t(acc2[r] > 0.0f) << (8 * (r >> 2) + 4 * g + (r & 3));
+    for (int r = 0; r < 16; ++r) sw |= uint32_t(acc2[r] > 0.0f) << r;
+    sw = spread_nibbles(sw, g);
     sw |= __shfl_xor(sw, 32);
     if (g == 0 && valid) signs[key * 4 + w] = sw;
     buf ^= 1;
