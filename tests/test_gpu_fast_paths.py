@@ -42,6 +42,29 @@ def test_d128_bf16_fast_path(env, bits, groups, n, nq):
     print("mismatches", rep.code_mismatch, rep.sign_mismatch, "cascade", rep.cascade_keys)
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+def test_fast_quantize_many_tiles_per_block(env, bits):
+    """40000 keys = 1250 tiles of 32, more than the resident blocks: every
+    block runs the pipelined multi-tile loop, with both an even and an odd
+    number of tiles per block (the two loop exits), and a zero key lands in a
+    later tile."""
+    torch, tqm, _ = env
+    from oracle import parity
+    from tests.test_gpu_parity import _params
+    n = 40000
+    _announce(f"fast quantize, many tiles per block: bits={bits} n={n}")
+    rs = np.random.default_rng(77 + bits)
+    keys = _bf16_keys(torch, rs, n, 128)
+    keys[33333] = 0.0
+    h = tqm.tq_init(128, bits, 0)
+    out = tqm.tq_quantize(h, torch.from_numpy(keys).bfloat16().cuda())
+    pr = _params(128, bits)
+    qz = tq.quantize(pr, keys.astype(np.float64))
+    rep = parity.compare_quantize(pr, qz, *(_cpu(t) for t in out))
+    print(rep)
+    assert rep.ok(), rep
+
+
 def test_fast_quantize_exact_rescaling_and_strides(env):
     torch, tqm, _ = env
     _announce("fast path: power-of-two rescaling and row strides")

@@ -8,217 +8,477 @@
 // Both projections are dense contractions and run on the matrix cores, with
 // operands split so that the float32 result is as good as a float32 dot
 // product:
-//   * z' = Pi k: Pi = P_hi + P_mid + P_lo exactly (three bfloat16 pieces of
-//     each float32 entry) and a bf16 key is exact, so every product is exact
-//     and only the float32 accumulation rounds (3 MFMA passes).
+//   * Keys: a key is staged as float16 times 2^s, where 2^s n lies in
+//     [2^14, 2^15).  A bf16 value (8 significant bits) is then exact in
+//     float16 unless it falls below the float16 normal range, i.e. below
+//     2^-28 n, where the rounding error is under 2^-39 n.
+//   * z' = (2^12 Pi)(2^s k): 2^12 Pi is split into two float16 pieces (22
+//     significant bits, 2 MFMA passes), every product is exact and only the
+//     float32 accumulation rounds; the representation error is at most
+//     2^-22 ||Pi_i|| ||k||, i.e. 2^-22 in units of z.
 //   * p = G r: G * 2^10 and r * 2^12 are each split into two float16 pieces
-//     (22 bits); hi*hi + hi*lo + lo*hi (3 passes) leaves an error below
-//     2^-21 sum_j |G_mj r_j|, under 1e-6 of the JL-normalised value p/sqrt(d).
-//     The power-of-two scales do not change signs.
-//   * n = ||Pi k|| = ||k|| (Pi orthogonal), from the float32 z'.
+//     (22 bits); hi*hi + hi*lo + lo*hi (3 passes) leaves an error near
+//     2^-21 sum_j |G_mj r_j|, far under 1e-6 of the JL-normalised value
+//     p/sqrt(d).  The power-of-two scales do not change signs.
+//   * n = ||k|| in float32 from the bf16 key: sixteen-term partial sums in
+//     eight lanes, then a three-level tree.
+//
+// Bucketize: the Lloyd-Max level set is symmetric, so z is placed by its
+// magnitude among the upper half (index M + j for z >= 0, M - 1 - j below,
+// M = 2^(B-1)); the residual z - c[idx] equals sign(z) (|z| - c[M + j])
+// exactly.  Only exact ties at -t resolve to the lower cell, which the
+// tie window allows.  Plane B-1 holds [z >= 0]; plane p < B-1 holds bit p of
+// j, flipped for z < 0.  A sign bit of p = +0 (only possible when G r
+// cancels exactly) is stored as 1, also inside the tie window.
 //
 // Work split: a block of 4 waves takes 32 keys at a time (one 32 x 32 x 16
 // MFMA tile in N); wave w owns output coordinates [32w, 32w + 32), i.e. bit
-// word w of every plane, and keeps its slices of Pi (3 bf16 pieces) and G (2
-// f16 pieces) in registers for the whole run.  Lane l holds, for key l % 32,
-// the 16 coordinates 8(r/4) + 4(l/32) + (r%4), r = 0..15, of its word.  The
+// word w of every plane, and keeps its slices of Pi and G (two float16
+// pieces each) in registers for the whole run.  The host permutes the rows
+// of both slices so that accumulator element r of lane l is coordinate
+// 32w + 16(l/32) + r: each lane's 16 bits of a word are contiguous.  The
 // residual goes through LDS to every wave as the B operand of p = G r; the
 // host orders G's columns so that the K-slots of each MFMA step match the
-// coordinates a lane already holds (no register shuffles).  Two barriers
-// per tile: one to sum ||z'||^2 over the 4 words, one to publish r.
+// coordinates a lane already holds (no register shuffles).
+//
+// Software pipeline, one barrier per tile: while the bucketize and residual
+// arithmetic of tile i runs on the vector ALU, the matrix cores work on
+// p = G r of tile i-1 and z' = Pi k of tile i+1; keys of tile i+2 are
+// scaled and staged in the same pass from registers loaded a pass earlier.
+// The pass is written as 40 slots of one MFMA plus a slice of vector work,
+// separated by scheduling fences: left alone, the compiler issues all MFMAs
+// first and the vector work after them, and nothing overlaps.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "tq_internal.h"
 
 namespace tqdev {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kQThreads = 256;
-constexpr int kSteps = 8;            // K = 128 in steps of 16
-constexpr float kResidualScale = 4096.0f;
+constexpr int kSteps = 8;           // K = 128 in steps of 16
+constexpr float kZScale = 4096.0f;  // z, levels, thresholds and residual carry a factor 2^12
 
-// Binary descent over the ascending thresholds held in LDS: at level p the
-// candidate index is idx + 2^p and its lower threshold t[idx + 2^p - 1]
-// (a tie goes to the upper cell), so idx = #{ i : t_i <= z } after B
-// levels.  Per-lane LDS reads keep the descent free of selects, which the
-// compiler would otherwise turn into divergent branches; the 31 table
-// entries sit in distinct banks.
+#define TQ_SLOT_END() __builtin_amdgcn_sched_barrier(0)
+
+__device__ __forceinline__ f32x16 mfma16(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t as_u32(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float as_f32(uint32_t x) { return __builtin_bit_cast(float, x); }
+
+// Keep a value computed in the slot that produces it, and opaque: without
+// this the compiler sinks the arithmetic into the slot that consumes it, or
+// recomputes it in another form there.
+#define TQ_PIN(x) asm volatile("" : "+v"(x))
+
+// Two float16 pieces of a pair: hi = f16(e), lo = f16(e - hi).  e - hi is
+// exact in float32; v_fma_mix forms it from the float16 hi and rounds once.
+__device__ __forceinline__ void split_f16_pair(float e0, float e1, uint32_t& hi, uint32_t& lo) {
+  const f16x2 h2 = {(_Float16)e0, (_Float16)e1};
+  hi = __builtin_bit_cast(uint32_t, h2);
+  asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixhi_f16 %0, -%1, 1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "=&v"(lo)
+      : "v"(hi), "v"(e0), "v"(e1));
+}
+
+// f16(x0 * scale), f16(x1 * scale) packed, each rounded once (v_fma_mix)
+__device__ __forceinline__ uint32_t scale_to_f16_pair(float x0, float x1, float scale) {
+  uint32_t h;
+  asm("v_fma_mixlo_f16 %0, %1, %3, 0\n\t"
+      "v_fma_mixhi_f16 %0, %2, %3, 0"
+      : "=&v"(h)
+      : "v"(x0), "v"(x1), "v"(scale));
+  return h;
+}
+
+__device__ __forceinline__ float dpp_sum8(float x) {
+  // sum over the 8 lanes of an aligned group: quad xor 1, quad xor 2, then
+  // the mirror within each half row (lane i <-> 7 - i) joins the two quads
+  x += as_f32(__builtin_amdgcn_mov_dpp(static_cast<int>(as_u32(x)), 0xB1, 0xF, 0xF, false));
+  x += as_f32(__builtin_amdgcn_mov_dpp(static_cast<int>(as_u32(x)), 0x4E, 0xF, 0xF, false));
+  x += as_f32(__builtin_amdgcn_mov_dpp(static_cast<int>(as_u32(x)), 0x141, 0xF, 0xF, false));
+  return x;
+}
+
+// Bucketize one coordinate and return the residual times 2^12.  The
+// coordinate arrives unscaled as a = 2^12 2^s n z; the thresholds 2^12 t are
+// multiplied by the key's 2^s n (+inf for a zero key, whose z = 0 lies in
+// cell M), inv = 1 / (2^s n), and 2^12 r = a inv - sign(a) 2^12 c[M + j].
+// Bits go in from the least significant end: the sign of z into sgn (1 for
+// z < 0), magnitude-index bit p into jw[p].
 template <int B>
-__device__ __forceinline__ int descend(float z, const float* tt) {
-  int idx = 0;
-#pragma unroll
-  for (int p = B - 1; p >= 0; --p) idx += (z >= tt[idx + (1 << p) - 1]) ? (1 << p) : 0;
-  return idx;
-}
+struct Quantizer {
+  static constexpr int M = 1 << (B - 1);
+  static constexpr int NJ = B > 1 ? B - 1 : 1;
+  static constexpr int NU = M > 1 ? M - 1 : 1;
+  float u[NU];  // 2^12 t[M + k], k < M - 1
+  float m[M];   // 2^12 c[M + j]
 
-// Lane bits are gathered in accumulator order (element r at bit r); element
-// r sits at row 8(r/4) + 4g + r%4 of the word, so nibble j moves to bits
-// [8j + 4g, 8j + 4g + 4).  The partner lane (g ^ 1) fills the other nibbles.
-__device__ __forceinline__ uint32_t spread_nibbles(uint32_t x, int g) {
-  x = (x | (x << 8)) & 0x00FF00FFu;
-  x = (x | (x << 4)) & 0x0F0F0F0Fu;
-  return x << (4 * g);
-}
-
-__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
-  const f16x2 v = {(_Float16)a, (_Float16)b};
-  return __builtin_bit_cast(uint32_t, v);
-}
+  __device__ __forceinline__ float operator()(float a, float inv, const float (&us)[NU], uint32_t& sgn,
+                                              uint32_t (&jw)[NJ]) const {
+    const float aa = __builtin_fabsf(a);
+    // binary descent, written out: compare with the middle threshold of the
+    // remaining candidates; the comparison at depth q gives bit B-2-q of j
+    float mj;
+    if constexpr (B == 1) {
+      mj = m[0];
+    } else if constexpr (B == 2) {
+      const bool b0 = aa >= us[0];
+      jw[0] = jw[0] + jw[0] + (b0 ? 1u : 0u);
+      mj = b0 ? m[1] : m[0];
+    } else if constexpr (B == 3) {
+      const bool b1 = aa >= us[1];
+      const float t = b1 ? us[2] : us[0];
+      const float lo = b1 ? m[2] : m[0];
+      const float hi = b1 ? m[3] : m[1];
+      const bool b0 = aa >= t;
+      jw[1] = jw[1] + jw[1] + (b1 ? 1u : 0u);
+      jw[0] = jw[0] + jw[0] + (b0 ? 1u : 0u);
+      mj = b0 ? hi : lo;
+    } else {
+      const bool b2 = aa >= us[3];
+      const float t1 = b2 ? us[5] : us[1];
+      const float ta = b2 ? us[4] : us[0];
+      const float tb = b2 ? us[6] : us[2];
+      const float ma = b2 ? m[4] : m[0];
+      const float mb = b2 ? m[5] : m[1];
+      const float mc = b2 ? m[6] : m[2];
+      const float md = b2 ? m[7] : m[3];
+      const bool b1 = aa >= t1;
+      const float t0 = b1 ? tb : ta;
+      const float me = b1 ? mc : ma;
+      const float mf = b1 ? md : mb;
+      const bool b0 = aa >= t0;
+      jw[2] = jw[2] + jw[2] + (b2 ? 1u : 0u);
+      jw[1] = jw[1] + jw[1] + (b1 ? 1u : 0u);
+      jw[0] = jw[0] + jw[0] + (b0 ? 1u : 0u);
+      mj = b0 ? mf : me;
+    }
+    sgn = __builtin_amdgcn_alignbit(sgn, as_u32(a), 31);
+    // a inv - sign(a) m = sign(a) (|a| inv - m): negation does not change the
+    // rounding.  The opaque copy keeps the negation on the fma's operand
+    // modifier instead of an integer xor.
+    float c = __builtin_copysignf(mj, a);
+    asm("" : "+v"(c));
+    return __builtin_fmaf(a, inv, -c);
+  }
+};
 
 template <int B>
 __global__ void __launch_bounds__(kQThreads, 2)
 quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ldk,
-                        const uint4* __restrict__ pi_frag, const uint4* __restrict__ g_frag, Codebook cb,
+                        const uint4* __restrict__ pi_frag, const uint4* __restrict__ g_frag, HalfCodebook hc,
                         uint32_t* __restrict__ codes, uint32_t* __restrict__ signs, float* __restrict__ norms,
                         float* __restrict__ rnorms, int64_t tiles) {
+  using Q = Quantizer<B>;
+  // scaled float16 keys, double buffered: 32 rows of 128 halves, row stride
+  // 272 bytes so that the 8 lanes of one LDS pass hit distinct banks
+  __shared__ uint4 ktile[2][32][17];
+  __shared__ float4 kinfo[2][32];  // (1 / (2^s n), n, 2^s n or +inf for n = 0, 0) per key
   // residual exchange [buf][piece][step][lane group][key] (8 halves each)
   __shared__ uint4 xb[2][2][kSteps][2][32];
-  __shared__ float zsq[2][4][32];
   __shared__ float rsq[2][4][32];
-  // key tiles, double buffered: 32 rows of 128 bf16, row stride 272 bytes so
-  // that the 8 lanes of one LDS pass (8 consecutive keys) hit distinct banks
-  __shared__ uint4 ktile[2][32][17];
-  __shared__ float tabc[kMaxLevels], tabt[kMaxLevels];
 
   const int w = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int kl = lane & 31;
   const int g = lane >> 5;
 
-  bf16x8 api[kSteps][3];
-  f16x8 ag[kSteps][2];
+  f16x8 api[kSteps][2], ag[kSteps][2];
 #pragma unroll
-  for (int s = 0; s < kSteps; ++s) {
+  for (int s = 0; s < kSteps; ++s)
 #pragma unroll
-    for (int q = 0; q < 3; ++q) api[s][q] = __builtin_bit_cast(bf16x8, pi_frag[((w * kSteps + s) * 3 + q) * 64 + lane]);
+    for (int q = 0; q < 2; ++q) {
+      api[s][q] = __builtin_bit_cast(f16x8, pi_frag[((w * kSteps + s) * 2 + q) * 64 + lane]);
+      ag[s][q] = __builtin_bit_cast(f16x8, g_frag[((w * kSteps + s) * 2 + q) * 64 + lane]);
+    }
+  Q quant;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) ag[s][q] = __builtin_bit_cast(f16x8, g_frag[((w * kSteps + s) * 2 + q) * 64 + lane]);
-  }
+  for (int k = 0; k < Q::M; ++k) quant.m[k] = hc.m[k];
+#pragma unroll
+  for (int k = 0; k + 1 < Q::M; ++k) quant.u[k] = hc.u[k];
 
-  if (threadIdx.x < kMaxLevels) {
-    tabc[threadIdx.x] = cb.c[threadIdx.x];
-    tabt[threadIdx.x] = cb.t[threadIdx.x];
-  }
-  // thread t stages bytes [32 (t % 8), +32) of key t / 8 of a tile
+  // staging: thread t owns bf16 elements [16 (t % 8), +16) of key t / 8.
+  // Rows are fetched in tile order, one call per tile.  Rows past the end
+  // re-read the last key: their outputs are never stored and a key's results
+  // depend on its own row only, so no zero fill (and no branch that would
+  // split the pipelined loop body) is needed.
   const int sk = threadIdx.x >> 3, sc = threadIdx.x & 7;
-  auto fetch = [&](int64_t tile, uint4& a, uint4& b) {
-    const int64_t k = tile * 32 + sk;
-    if (tile < tiles && k < n) {
-      const uint4* row = reinterpret_cast<const uint4*>(keys + k * ldk);
-      a = row[2 * sc];
-      b = row[2 * sc + 1];
-    } else {
-      a = b = make_uint4(0u, 0u, 0u, 0u);
+  const int64_t ntile = (tiles - blockIdx.x + gridDim.x - 1) / gridDim.x;  // >= 1
+  const uint4* const row_last = reinterpret_cast<const uint4*>(keys + (n - 1) * ldk) + 2 * sc;
+  const int64_t row_step = static_cast<int64_t>(gridDim.x) * 32 * ldk / 8;  // in uint4
+  const uint4* row_next = reinterpret_cast<const uint4*>(keys + (static_cast<int64_t>(blockIdx.x) * 32 + sk) * ldk) + 2 * sc;
+  auto fetch = [&](uint4& a, uint4& b) {
+    const uint4* src = row_next < row_last ? row_next : row_last;
+    a = src[0];
+    b = src[1];
+    row_next += row_step;
+  };
+  // staging pieces: unpack + partial sum of squares, norm and scale, convert
+  struct Stage {
+    float x[16];
+    float ss, nk, inv, ns, scale;
+  };
+  auto stage_unpack = [&](Stage& st, const uint4& v, int half) {
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+    if (half == 0) st.ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      st.x[8 * half + 2 * i] = as_f32(u[i] << 16);
+      st.x[8 * half + 2 * i + 1] = as_f32(u[i] & 0xFFFF0000u);
+      // bf16 products are exact in float32
+      st.ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u[i]), __builtin_bit_cast(bf16x2, u[i]),
+                                              st.ss, false);
     }
   };
+  auto stage_norm = [&](Stage& st) {
+    // 2^sh nk in [2^14, 2^15); nk == 0 gives sh = 15 and zero keys.  The
+    // hardware square root and reciprocal are within 1 ulp.
+    st.nk = __builtin_amdgcn_sqrtf(dpp_sum8(st.ss));
+    const int sh = 15 - __builtin_amdgcn_frexp_expf(st.nk);
+    st.scale = __builtin_amdgcn_ldexpf(1.0f, sh);
+    st.ns = st.nk > 0.0f ? __builtin_amdgcn_ldexpf(st.nk, sh) : __builtin_inff();
+    st.inv = st.nk > 0.0f ? __builtin_amdgcn_rcpf(st.ns) : 0.0f;
+  };
+  auto stage_store = [&](const Stage& st, int buf, int half) {
+    uint32_t h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[i] = scale_to_f16_pair(st.x[8 * half + 2 * i], st.x[8 * half + 2 * i + 1], st.scale);
+    ktile[buf][sk][2 * sc + half] = make_uint4(h[0], h[1], h[2], h[3]);
+    if (half == 1) kinfo[buf][sk] = make_float4(st.inv, st.nk, st.ns, 0.0f);  // the 8 lanes write the same value
+  };
+  auto stage_all = [&](const uint4& a, const uint4& b, int buf) {
+    Stage st;
+    stage_unpack(st, a, 0);
+    stage_unpack(st, b, 1);
+    stage_norm(st);
+    stage_store(st, buf, 0);
+    stage_store(st, buf, 1);
+  };
+
+  // prologue: tiles 0 and 1 staged, tile 2 in flight
+  uint4 na, nb;
   {
-    uint4 a, b;
-    fetch(blockIdx.x, a, b);
-    ktile[0][sk][2 * sc] = a;
-    ktile[0][sk][2 * sc + 1] = b;
+    uint4 a0, b0, a1, b1;
+    fetch(a0, b0);
+    fetch(a1, b1);
+    fetch(na, nb);
+    stage_all(a0, b0, 0);
+    stage_all(a1, b1, 1);
+    // the first pass runs p = G r on buffer 1 before any residual is there
+    uint4* x1 = &xb[1][0][0][0][0];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x1[j * kQThreads + threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
   }
   __syncthreads();
-
-  int buf = 0;
-  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
-    const int64_t key = tile * 32 + kl;
-    const bool valid = key < n;
-    // B operand of z' = Pi k: lane supplies k[16 s + 8 g .. + 7] of its key
-    bf16x8 kf[kSteps];
+  float4 info = kinfo[0][kl];
+  f32x16 acc1 = {};
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) kf[s] = __builtin_bit_cast(bf16x8, ktile[buf][kl][2 * s + g]);
-    // next tile's keys: in flight during this tile's work, stored to LDS
-    // before the second barrier
-    uint4 na, nb;
-    fetch(tile + gridDim.x, na, nb);
-    f32x16 acc = {};
+  for (int s = 0; s < kSteps; ++s) {
+    const f16x8 kf = __builtin_bit_cast(f16x8, ktile[0][kl][2 * s + g]);
+    acc1 = mfma16(api[s][1], kf, acc1);
+    acc1 = mfma16(api[s][0], kf, acc1);
+  }
+
+  // Lanes l and l ^ 32 hold the low and high 16 bits of a word; every lane
+  // gets the whole word (v_permlane32_swap hands each half to both lanes).
+  auto whole = [](uint32_t x) {
+    const auto h = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return h[0] | (h[1] << 16);
+  };
+  auto both_sum = [](float x) {
+    const auto h = __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(x), false, false);
+    return as_f32(h[0]) + as_f32(h[1]);
+  };
+  // Stores are branch-free: every lane of every wave stores, rows past the
+  // end go to key n - 1, and all writers of an address write the same value
+  // (rows past the end re-read key n - 1 and give bit-identical results).
+  // With no conditional stores the compiler can count outstanding memory
+  // operations exactly instead of draining them before each use of the
+  // prefetched keys.
+  auto rnorm_of = [&](int b) {
+    const float* q = rsq[b][0];
+    return __builtin_amdgcn_sqrtf((q[kl] + q[32 + kl]) + (q[64 + kl] + q[96 + kl])) * (1.0f / kZScale);
+  };
+
+  // One pass: tile i's vector work beside p of tile i-1 and z' of tile i+1.
+  // buf = i % 2 is a compile-time constant (the loop is unrolled by two);
+  // the first pass has no tile i-1 to finish.
+  auto pass = [&](int64_t i, auto bufc, auto firstc) {
+    constexpr int buf = decltype(bufc)::value;
+    constexpr bool first = decltype(firstc)::value;
+    constexpr int ob = buf ^ 1;
+    const int64_t key = (blockIdx.x + i * gridDim.x) * 32 + kl;
+    const int64_t kc = key < n ? key : n - 1;
+    const int64_t pkey = key - static_cast<int64_t>(gridDim.x) * 32;
+    const int64_t pkc = pkey < n ? pkey : n - 1;
+
+    // ---- slot 0: operands of the first MFMAs, and while they load, the
+    // thresholds scaled to the key and the first coordinate pair
+    f16x8 rh = __builtin_bit_cast(f16x8, xb[ob][0][0][g][kl]);
+    f16x8 rl = __builtin_bit_cast(f16x8, xb[ob][1][0][g][kl]);
+    const f32x16 zt = acc1;
+    const float inv = info.x, nrm = info.y;
+    float us[Q::NU];
+#pragma unroll
+    for (int k = 0; k + 1 < Q::M; ++k) us[k] = quant.u[k] * info.z;
+    uint32_t sgn = 0u, jw[Q::NJ];
+#pragma unroll
+    for (int p = 0; p < Q::NJ; ++p) jw[p] = 0u;
+    float e[16];  // scaled residuals, coordinates processed from 15 down
+    e[15] = quant(zt[15], inv, us, sgn, jw);
+    e[14] = quant(zt[14], inv, us, sgn, jw);
+    TQ_PIN(e[15]);
+    TQ_PIN(e[14]);
+    TQ_SLOT_END();
+
+    // ---- slots 1-24: p = G r of tile i-1 (3 MFMAs per step) beside the
+    // bucketize of tile i: step s quantizes pair s + 1 and packs pair s
+    f32x16 acc2 = {};
+    float rr = 0.0f;
+    uint32_t hi[4], lo[4];
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(api[s][0], kf[s], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(api[s][1], kf[s], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(api[s][2], kf[s], acc, 0, 0, 0);
-    }
-    // ||z'||^2 over this word, then over the 4 words
-    float ss = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) ss = fmaf(acc[r], acc[r], ss);
-    ss += __shfl_xor(ss, 32);
-    if (g == 0) zsq[buf][w][kl] = ss;
-    __syncthreads();
-    const float nk = sqrtf((zsq[buf][0][kl] + zsq[buf][1][kl]) + (zsq[buf][2][kl] + zsq[buf][3][kl]));
-    const float inv = nk > 0.0f ? 1.0f / nk : 0.0f;
-
-    uint32_t cw[B];
-#pragma unroll
-    for (int p = 0; p < B; ++p) cw[p] = 0u;
-    float rr = 0.0f;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint32_t hi[4], lo[4];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        float rs[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int r = 8 * h + e + u;
-          const float z = acc[r] * inv;
-          const int idx = descend<B>(z, tabt);
-          const float res = z - tabc[idx];
-#pragma unroll
-          for (int p = 0; p < B; ++p) cw[p] |= uint32_t((idx >> p) & 1) << r;
-          rr = fmaf(res, res, rr);
-          rs[u] = res * kResidualScale;
-        }
-        const f16x2 h2 = {(_Float16)rs[0], (_Float16)rs[1]};
-        hi[e >> 1] = __builtin_bit_cast(uint32_t, h2);
-        lo[e >> 1] = pack_f16x2(rs[0] - float(h2[0]), rs[1] - float(h2[1]));
+      const int r1 = 15 - 2 * s, r0 = r1 - 1;  // pair s
+      f16x8 nrh = rh, nrl = rl;
+      if (s + 1 < kSteps) nrh = __builtin_bit_cast(f16x8, xb[ob][0][s + 1][g][kl]);
+      acc2 = mfma16(ag[s][1], rh, acc2);
+      if (s + 1 < kSteps) {
+        e[r1 - 2] = quant(zt[r1 - 2], inv, us, sgn, jw);
+        TQ_PIN(e[r1 - 2]);
       }
-      xb[buf][0][2 * w + h][g][kl] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      xb[buf][1][2 * w + h][g][kl] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      TQ_SLOT_END();
+      if (s + 1 < kSteps) nrl = __builtin_bit_cast(f16x8, xb[ob][1][s + 1][g][kl]);
+      acc2 = mfma16(ag[s][0], rl, acc2);
+      if (s + 1 < kSteps) {
+        e[r0 - 2] = quant(zt[r0 - 2], inv, us, sgn, jw);
+        TQ_PIN(e[r0 - 2]);
+      }
+      TQ_SLOT_END();
+      acc2 = mfma16(ag[s][0], rh, acc2);
+      rr = fmaf(e[r1], e[r1], rr);
+      rr = fmaf(e[r0], e[r0], rr);
+      split_f16_pair(e[r0], e[r1], hi[(r0 & 7) >> 1], lo[(r0 & 7) >> 1]);
+      if ((r0 & 7) == 0) {
+        xb[buf][0][2 * w + (r0 >> 3)][g][kl] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        xb[buf][1][2 * w + (r0 >> 3)][g][kl] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      }
+      TQ_SLOT_END();
+      rh = nrh;
+      rl = nrl;
     }
+
+    // ---- slots 25-40: z' of tile i+1 (2 MFMAs per step) beside staging of
+    // tile i+2, the sign bits of tile i-1, word assembly and the stores
+    info = kinfo[ob][kl];
+    f16x8 kf = __builtin_bit_cast(f16x8, ktile[ob][kl][g]);
+    f32x16 a1 = {};
+    Stage st;
+    uint32_t sw = 0u;
+    uint32_t word[B + 1];  // planes 0..B-1, then the sign word of tile i-1
+    float prn = 0.0f;      // rho of tile i-1
+    f16x8 nkf = kf;        // next step's keys, read one step ahead
 #pragma unroll
-    for (int p = 0; p < B; ++p) {
-      cw[p] = spread_nibbles(cw[p], g);
-      cw[p] |= __shfl_xor(cw[p], 32);
-    }
-    rr += __shfl_xor(rr, 32);
-    if (g == 0) {
-      rsq[buf][w][kl] = rr;
-      if (valid)
+    for (int j = 0; j < 2 * kSteps; ++j) {
+      const int s = j >> 1;
+      if ((j & 1) == 0 && s + 1 < kSteps) nkf = __builtin_bit_cast(f16x8, ktile[ob][kl][2 * (s + 1) + g]);
+      a1 = mfma16(api[s][(j & 1) ? 0 : 1], kf, a1);
+      switch (j) {
+        case 0: stage_unpack(st, na, 0); break;
+        case 1: stage_unpack(st, nb, 1); break;
+        case 2:
+          stage_norm(st);
+          if (!first) prn = rnorm_of(ob);
+          break;
+        case 3: stage_store(st, buf, 0); break;
+        case 4: stage_store(st, buf, 1); break;
+        case 5: fetch(na, nb); break;  // tile i + 3
+        case 6:
 #pragma unroll
-        for (int p = 0; p < B; ++p) codes[(key * B + p) * 4 + w] = cw[p];
+          for (int r = 15; r >= 8; --r) sw = __builtin_amdgcn_alignbit(sw, as_u32(acc2[r]), 31);
+          break;
+        case 7:
+#pragma unroll
+          for (int r = 7; r >= 0; --r) sw = __builtin_amdgcn_alignbit(sw, as_u32(acc2[r]), 31);
+          break;
+        case 8:
+          // 16-bit halves: plane B-1 = [z >= 0], plane p = j_p ^ [z < 0],
+          // signs = [p > 0]
+#pragma unroll
+          for (int p = 0; p + 1 < B; ++p) word[p] = jw[p] ^ sgn;
+          word[B - 1] = sgn ^ 0xFFFFu;
+          word[B] = sw ^ 0xFFFFu;
+          break;
+        case 9:
+#pragma unroll
+          for (int p = 0; p <= B; ++p) word[p] = whole(word[p]);
+          break;
+        case 10: rsq[buf][w][kl] = both_sum(rr); break;
+        case 11:
+#pragma unroll
+          for (int p = 0; p < B; ++p) codes[(kc * B + p) * 4 + w] = word[p];
+          norms[kc] = nrm;
+          break;
+        case 12:
+          if (!first) {
+            signs[pkc * 4 + w] = word[B];
+            rnorms[pkc] = prn;
+          }
+          break;
+        default: break;
+      }
+      TQ_SLOT_END();
+      if (j & 1) kf = nkf;
     }
-    ktile[buf ^ 1][sk][2 * sc] = na;
-    ktile[buf ^ 1][sk][2 * sc + 1] = nb;
+    acc1 = a1;
     __syncthreads();
-    if (w == 0 && g == 0 && valid) {
-      norms[key] = nk;
-      rnorms[key] = sqrtf((rsq[buf][0][kl] + rsq[buf][1][kl]) + (rsq[buf][2][kl] + rsq[buf][3][kl]));
-    }
-    // p = G r for this wave's 32 output coordinates
+  };
+  // p of the last tile
+  auto finish = [&](int64_t i, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    const int64_t key = (blockIdx.x + i * gridDim.x) * 32 + kl;
+    const int64_t kc = key < n ? key : n - 1;
     f32x16 acc2 = {};
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
       const f16x8 rh = __builtin_bit_cast(f16x8, xb[buf][0][s][g][kl]);
       const f16x8 rl = __builtin_bit_cast(f16x8, xb[buf][1][s][g][kl]);
-      acc2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ag[s][1], rh, acc2, 0, 0, 0);
-      acc2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ag[s][0], rl, acc2, 0, 0, 0);
-      acc2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ag[s][0], rh, acc2, 0, 0, 0);
+      acc2 = mfma16(ag[s][1], rh, acc2);
+      acc2 = mfma16(ag[s][0], rl, acc2);
+      acc2 = mfma16(ag[s][0], rh, acc2);
     }
     uint32_t sw = 0u;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sw |= uint32_t(acc2[r] > 0.0f) << r;
-    sw = spread_nibbles(sw, g);
-    sw |= __shfl_xor(sw, 32);
-    if (g == 0 && valid) signs[key * 4 + w] = sw;
-    buf ^= 1;
+    for (int r = 15; r >= 0; --r) sw = __builtin_amdgcn_alignbit(sw, as_u32(acc2[r]), 31);
+    signs[kc * 4 + w] = whole(sw ^ 0xFFFFu);
+    rnorms[kc] = rnorm_of(buf);
+  };
+  constexpr std::integral_constant<int, 0> kBuf0{};
+  constexpr std::integral_constant<int, 1> kBuf1{};
+  constexpr std::true_type kFirst{};
+  constexpr std::false_type kLater{};
+  pass(0, kBuf0, kFirst);
+  int64_t i = 1;
+  for (; i + 1 < ntile; i += 2) {
+    pass(i, kBuf1, kLater);
+    pass(i + 1, kBuf0, kLater);
+  }
+  if (i < ntile) {
+    pass(i, kBuf1, kLater);
+    finish(i, kBuf1);
+  } else {
+    finish(i - 1, kBuf0);
   }
 }
 
@@ -226,18 +486,19 @@ template <int B>
 hipError_t launch_b(const tq_ctx* h, const void* keys, int64_t n, int64_t ldk, uint32_t* codes, uint32_t* signs,
                     float* norms, float* rnorms, hipStream_t stream) {
   const int64_t tiles = (n + 31) / 32;
-  int64_t blocks = tiles < 512 ? tiles : 512;  // two resident blocks on each of 256 CUs
+  const int64_t blocks = tiles < 512 ? tiles : 512;  // two resident blocks on each of 256 CUs
   hipLaunchKernelGGL(quantize_mfma128_kernel<B>, dim3(static_cast<uint32_t>(blocks)), dim3(kQThreads), 0, stream,
                      static_cast<const uint16_t*>(keys), n, ldk, reinterpret_cast<const uint4*>(h->d_pi_frag),
-                     reinterpret_cast<const uint4*>(h->d_g_frag), h->cb, codes, signs, norms, rnorms, tiles);
+                     reinterpret_cast<const uint4*>(h->d_g_frag), h->half, codes, signs, norms, rnorms, tiles);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool quantize_mfma128_supported(const tq_ctx* h, const void* keys, int key_dtype, int64_t ldk) {
-  return h->d == 128 && key_dtype == TQ_BF16 && h->d_pi_frag && h->d_g_frag && (ldk % 8) == 0 &&
-         (reinterpret_cast<uintptr_t>(keys) & 15u) == 0 && h->code_bits >= 1 && h->code_bits <= 4;
+  return h->d == 128 && key_dtype == TQ_BF16 && h->d_pi_frag && h->d_g_frag && h->symmetric && ldk >= 128 &&
+         (ldk % 8) == 0 && (reinterpret_cast<uintptr_t>(keys) & 15u) == 0 && h->code_bits >= 1 &&
+         h->code_bits <= 4;
 }
 
 hipError_t launch_quantize_mfma128(const tq_ctx* h, const void* keys, int64_t n, int64_t ldk, uint32_t* codes,

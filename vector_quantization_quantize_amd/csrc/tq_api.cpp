@@ -34,20 +34,6 @@ void free_device(tq_ctx* h) {
   }
 }
 
-uint16_t bf16_rne(float x) {
-  uint32_t u;
-  std::memcpy(&u, &x, 4);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
-
-float bf16_value(uint16_t b) {
-  const uint32_t u = uint32_t(b) << 16;
-  float f;
-  std::memcpy(&f, &u, 4);
-  return f;
-}
-
 uint16_t f16_bits(float x) {
   const _Float16 h = static_cast<_Float16>(x);
   uint16_t b;
@@ -71,33 +57,33 @@ int upload_u16(uint16_t** dst, const std::vector<uint16_t>& src) {
 }
 
 // Register fragments of the d = 128 matrix-core quantize kernel (see
-// quantize_mfma.hip).  Pi: three bf16 pieces with hi + mid + lo == Pi
-// exactly; lane l of word w, step s holds Pi[32w + l%32][16s + 8(l/32) + e].
-// G: two f16 pieces of 2^10 G; lane l holds G[32w + l%32][j(s, l/32, e)] with
-// j(s, g, e) = 32(s/2) + 16(s%2) + 8(e/4) + 4g + e%4, the coordinate that lane
-// group g holds in accumulator element 8(s%2) + e of word s/2.
+// quantize_mfma.hip).  Rows of a wave's 32-row slice are permuted: MFMA row m
+// carries coordinate 16((m/4)%2) + 4(m/8) + m%4 of word w, so accumulator
+// element r of lane l is coordinate 32w + 16(l/32) + r.
+//   Pi: two f16 pieces of 2^12 Pi; lane l of word w, step s holds
+//       Pi[32w + row(l%32)][16s + 8(l/32) + e].
+//   G:  two f16 pieces of 2^10 G; lane l holds G[32w + row(l%32)][j] with
+//       j = 32(s/2) + 16(l/32) + 8(s%2) + e, the residual coordinate that lane
+//       group l/32 supplies in K-slot e of step s.
 int build_fragments(tq_ctx* h) {
   const int d = h->d;
   if (d != 128) return TQ_OK;
-  std::vector<uint16_t> pf(size_t(4) * 8 * 3 * 64 * 8), gf(size_t(4) * 8 * 2 * 64 * 8);
+  auto row_of = [](int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); };
+  std::vector<uint16_t> pf(size_t(4) * 8 * 2 * 64 * 8), gf(size_t(4) * 8 * 2 * 64 * 8);
   for (int w = 0; w < 4; ++w)
     for (int s = 0; s < 8; ++s)
       for (int l = 0; l < 64; ++l)
         for (int e = 0; e < 8; ++e) {
-          const int row = 32 * w + (l & 31);
-          const float x = h->pi[size_t(row) * d + 16 * s + 8 * (l >> 5) + e];
-          const uint16_t hi = bf16_rne(x);
-          const float r1 = x - bf16_value(hi);
-          const uint16_t mid = bf16_rne(r1);
-          const uint16_t lo = bf16_rne(r1 - bf16_value(mid));
-          const uint16_t pieces[3] = {hi, mid, lo};
-          for (int q = 0; q < 3; ++q) pf[(((size_t(w) * 8 + s) * 3 + q) * 64 + l) * 8 + e] = pieces[q];
-          const int j = 32 * (s >> 1) + 16 * (s & 1) + 8 * (e >> 2) + 4 * (l >> 5) + (e & 3);
+          const int row = 32 * w + row_of(l & 31);
+          const float x = h->pi[size_t(row) * d + 16 * s + 8 * (l >> 5) + e] * 4096.0f;
+          const uint16_t phi = f16_bits(x);
+          pf[(((size_t(w) * 8 + s) * 2 + 0) * 64 + l) * 8 + e] = phi;
+          pf[(((size_t(w) * 8 + s) * 2 + 1) * 64 + l) * 8 + e] = f16_bits(x - f16_value(phi));
+          const int j = 32 * (s >> 1) + 16 * (l >> 5) + 8 * (s & 1) + e;
           const float gs = h->g[size_t(row) * d + j] * 1024.0f;
           const uint16_t ghi = f16_bits(gs);
-          const uint16_t glo = f16_bits(gs - f16_value(ghi));
           gf[(((size_t(w) * 8 + s) * 2 + 0) * 64 + l) * 8 + e] = ghi;
-          gf[(((size_t(w) * 8 + s) * 2 + 1) * 64 + l) * 8 + e] = glo;
+          gf[(((size_t(w) * 8 + s) * 2 + 1) * 64 + l) * 8 + e] = f16_bits(gs - f16_value(ghi));
         }
   // stage-1 reconstruction: lane l of word w, step s holds
   // 2^12 Pi[16s + 8(l/32) + e][32w + l%32] (B operand, N = output coordinate)
@@ -166,6 +152,15 @@ int finish_init(tq_ctx* h) {
   }
   h->cb.levels = h->levels;
   plane_expansion(h->centroids, h->code_bits, &h->planes);
+  {
+    const int L = h->levels, M = L / 2;
+    bool sym = h->thresholds[M - 1] == 0.0f;
+    for (int i = 0; i < L; ++i) sym = sym && h->centroids[L - 1 - i] == -h->centroids[i];
+    for (int i = 0; i + 1 < L; ++i) sym = sym && h->thresholds[L - 2 - i] == -h->thresholds[i];
+    h->symmetric = sym;
+    for (int j = 0; j < M; ++j) h->half.m[j] = h->centroids[M + j] * 4096.0f;
+    for (int k = 0; k + 1 < M; ++k) h->half.u[k] = h->thresholds[M + k] * 4096.0f;
+  }
   int rc;
   if ((rc = upload(&h->d_pi, h->pi)) != TQ_OK) return rc;
   if ((rc = upload(&h->d_piT, transpose(h->pi, d))) != TQ_OK) return rc;

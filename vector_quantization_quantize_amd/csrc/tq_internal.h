@@ -28,6 +28,14 @@ struct PlaneExpansion {
   float alpha[8];       // coefficient of each term
 };
 
+// Upper half of a level set that is exactly symmetric (c[L-1-i] = -c[i],
+// t[L-2-i] = -t[i], middle threshold 0), times 2^12: index M + j holds
+// m[j] and is chosen for z >= 0 with j = #{u_k <= z}; M = L / 2.
+struct HalfCodebook {
+  float u[kMaxLevels / 2];  // u[k] = 2^12 t[M + k], k < M - 1
+  float m[kMaxLevels / 2];  // m[j] = 2^12 c[M + j],  j < M
+};
+
 }  // namespace tqdev
 
 struct tq_ctx {
@@ -41,11 +49,13 @@ struct tq_ctx {
   float* d_g = nullptr;    // G   row-major
   float* d_gT = nullptr;   // G^T row-major
   // d = 128 only: register fragments of the matrix-core quantize kernel
-  uint16_t* d_pi_frag = nullptr;  // [word 4][step 8][piece 3][lane 64][8] bf16 pieces of Pi
+  uint16_t* d_pi_frag = nullptr;  // [word 4][step 8][piece 2][lane 64][8] f16 pieces of 2^12 Pi
   uint16_t* d_g_frag = nullptr;   // [word 4][step 8][piece 2][lane 64][8] f16 pieces of 2^10 G
   uint16_t* d_dq_frag = nullptr;  // [word 4][step 8][piece 2][lane 64][8] f16 pieces of 2^12 Pi (B operand)
   tqdev::Codebook cb{};
   tqdev::PlaneExpansion planes{};
+  bool symmetric = false;  // level set exactly symmetric in float32
+  tqdev::HalfCodebook half{};
 };
 
 namespace tqdev {
