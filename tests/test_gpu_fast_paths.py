@@ -43,16 +43,16 @@ def test_d128_bf16_fast_path(env, bits, groups, n, nq):
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 5])
-def test_fast_quantize_many_tiles_per_block(env, bits):
-    """40000 keys = 1250 tiles of 32, more than the resident blocks: every
-    block runs the pipelined multi-tile loop, with both an even and an odd
-    number of tiles per block (the two loop exits), and a zero key lands in a
-    later tile."""
+def test_fast_paths_many_tiles_per_block(env, bits):
+    """40007 keys = 1251 tiles of 32 (the last one ragged), more than the
+    resident blocks: every block of the quantize and reconstruction kernels
+    runs its multi-tile loop, with both an even and an odd number of tiles
+    per block, and a zero key lands in a later tile."""
     torch, tqm, _ = env
     from oracle import parity
     from tests.test_gpu_parity import _params
-    n = 40000
-    _announce(f"fast quantize, many tiles per block: bits={bits} n={n}")
+    n = 40007
+    _announce(f"fast quantize + dequant, many tiles per block: bits={bits} n={n}")
     rs = np.random.default_rng(77 + bits)
     keys = _bf16_keys(torch, rs, n, 128)
     keys[33333] = 0.0
@@ -63,6 +63,11 @@ def test_fast_quantize_many_tiles_per_block(env, bits):
     rep = parity.compare_quantize(pr, qz, *(_cpu(t) for t in out))
     print(rep)
     assert rep.ok(), rep
+    # reconstruction of every key from the GPU's own codes and norms
+    kh = _cpu(tqm.tq_dequant_mse(h, out[0], out[2]))
+    idx_gpu = tq.unpack_codes(_cpu(out[0]).view(np.uint32), 128)
+    bad, worst = parity.dequant_violations(kh, tq.dequant_mse(pr, idx_gpu, _cpu(out[2]).astype(np.float64)))
+    assert bad == 0, (bad, worst)
 
 
 def test_fast_quantize_exact_rescaling_and_strides(env):

@@ -3,22 +3,30 @@
 // "TurboQuant tutorial" (gitcode.csdn.net), polar part: the codes and the
 // kept length map back to a vector, k_hat = n Pi^T c[idx].
 //
-// A symmetric level set is an odd multilinear function of the plane signs,
-// c[idx] = sum_S alpha_S prod_{p in S} s_p (odd-size plane subsets S), so
-//     k_hat = n sum_S alpha_S (s_S^T Pi),   s_S in {-1, +1}^d,
-// and every s_S^T Pi is a product with a +-1 matrix: exact in float16.  Pi
-// scaled by 2^12 is split into two float16 pieces (22 bits) held in
-// registers; each term takes 2 MFMA passes per K step into its own float32
-// accumulator, and the epilogue forms n * sum_S alpha_S acc_S / 2^12.
+// Values, not signs: an LDS table turns the packed indices of E consecutive
+// coordinates (E B bits) straight into float16 pieces of 2^12 c[idx] (hi and
+// lo, 22 significant bits), and with Pi scaled by 2^12 also split into two
+// float16 pieces held in registers, k_hat = n 2^-24 (c_hi Pi_hi + c_hi Pi_lo
+// + c_lo Pi_hi) takes three MFMA passes per K step into one float32
+// accumulator.  The dropped c_lo Pi_lo term and the pieces' rounding are
+// near 2^-21 relative, far under the 1e-5 bound.  E = 8 / B coordinates per
+// lookup (B = 3 uses E = 4, a 4096-entry table), so a step of 8 coordinates
+// takes 8 / E lookups.
 //
 // Work split: wave w of a 4-wave block owns output coordinates [32w, 32w+32)
 // and walks tiles of 32 keys (one 32 x 32 x 16 MFMA tile: M = keys,
 // N = coordinates, K = 128 input coordinates in 8 steps).  Lane l supplies,
-// for key l % 32, the signs of coordinates 16 s + 8 (l/32) .. +7 of step s:
-// one byte of a term word, expanded to 8 float16 values +-1 through a
-// 256-entry LDS table.  Lane l's results are coordinate 32w + l % 32 of keys
-// 8(r/4) + 4(l/32) + r%4, r = 0..15, so each output row is written as a
-// contiguous 128-byte segment.  Waves never wait on each other.
+// for key l % 32, the values of coordinates 16 s + 8 (l/32) .. +7 of step s:
+// byte 2 (s % 2) + l/32 of word s/2 of each plane.  Lane l's results are
+// coordinate 32w + l % 32 of keys 8(r/4) + 4(l/32) + r%4, r = 0..15, so each
+// output row is written as a contiguous 128-byte segment.  Waves never wait
+// on each other.
+//
+// Keys past the end of the last tile load key n - 1 instead (codes and
+// norm), so their rows equal row n - 1 and are stored there: the same value
+// twice, and no per-row branch.  Norms reach the lanes that need them
+// through a per-wave LDS row (one write, four 16-byte reads; within one
+// wave, so no barrier).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -33,51 +41,85 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kDqThreads = 256;
 constexpr int kSteps = 8;
-constexpr float kPiScaleInv = 1.0f / 4096.0f;
+constexpr float kOutScale = 1.0f / (4096.0f * 4096.0f);  // undoes 2^12 on c and on Pi
 
+// coordinates per table lookup and table geometry
 template <int B>
-struct Terms;
-template <>
-struct Terms<1> {
-  static constexpr int count = 1;
-  static constexpr uint32_t mask[1] = {1};
+struct Lookup {
+  static constexpr int E = B == 3 ? 4 : 8 / B;
+  static constexpr int K = 8 / E;                  // lookups per step
+  static constexpr int kEntries = 1 << (E * B);
+  static constexpr int kDwords = E;                // E hi halves + E lo halves
 };
-template <>
-struct Terms<2> {
-  static constexpr int count = 2;
-  static constexpr uint32_t mask[2] = {1, 2};
-};
-template <>
-struct Terms<3> {
-  static constexpr int count = 4;
-  static constexpr uint32_t mask[4] = {1, 2, 4, 7};
-};
-template <>
-struct Terms<4> {
-  static constexpr int count = 8;
-  static constexpr uint32_t mask[8] = {1, 2, 4, 7, 8, 11, 13, 14};
-};
+
+// Entry layout: dwords [0, E/2) hold the hi halves of coordinates 0..E-1,
+// dwords [E/2, E) the lo halves.  Index bit p E + e is bit p of the level
+// index of coordinate e.
+template <int B>
+__device__ void build_table(uint32_t* tab, const Codebook& cb) {
+  using L = Lookup<B>;
+  for (int idx = threadIdx.x; idx < L::kEntries; idx += kDqThreads) {
+    _Float16 hv[L::E], lv[L::E];
+#pragma unroll
+    for (int e = 0; e < L::E; ++e) {
+      int level = 0;
+#pragma unroll
+      for (int p = 0; p < B; ++p) level |= ((idx >> (p * L::E + e)) & 1) << p;
+      const float x = cb.c[level] * 4096.0f;  // exact
+      hv[e] = static_cast<_Float16>(x);
+      lv[e] = static_cast<_Float16>(x - static_cast<float>(hv[e]));
+    }
+#pragma unroll
+    for (int k = 0; k < L::E / 2; ++k) {
+      tab[idx * L::kDwords + k] =
+          __builtin_bit_cast(uint16_t, hv[2 * k]) | (uint32_t(__builtin_bit_cast(uint16_t, hv[2 * k + 1])) << 16);
+      tab[idx * L::kDwords + L::E / 2 + k] =
+          __builtin_bit_cast(uint16_t, lv[2 * k]) | (uint32_t(__builtin_bit_cast(uint16_t, lv[2 * k + 1])) << 16);
+    }
+  }
+}
+
+// A operands (hi and lo pieces) of step s for this lane, from the plane
+// words holding the step's coordinates
+template <int B>
+__device__ __forceinline__ void load_a(const uint32_t* tab, const uint32_t (&wp)[B], int shift, f16x8& ahi,
+                                       f16x8& alo) {
+  using L = Lookup<B>;
+  uint32_t hi[4], lo[4];
+#pragma unroll
+  for (int k = 0; k < L::K; ++k) {
+    uint32_t idx = 0;
+#pragma unroll
+    for (int p = 0; p < B; ++p) idx |= __builtin_amdgcn_ubfe(wp[p], shift + k * L::E, L::E) << (p * L::E);
+    const uint32_t* ent = tab + idx * L::kDwords;
+    if constexpr (L::E == 8) {
+      const uint4 h = reinterpret_cast<const uint4*>(ent)[0];
+      const uint4 l = reinterpret_cast<const uint4*>(ent)[1];
+      hi[0] = h.x; hi[1] = h.y; hi[2] = h.z; hi[3] = h.w;
+      lo[0] = l.x; lo[1] = l.y; lo[2] = l.z; lo[3] = l.w;
+    } else if constexpr (L::E == 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(ent);
+      hi[2 * k] = v.x; hi[2 * k + 1] = v.y;
+      lo[2 * k] = v.z; lo[2 * k + 1] = v.w;
+    } else {
+      const uint2 v = *reinterpret_cast<const uint2*>(ent);
+      hi[k] = v.x;
+      lo[k] = v.y;
+    }
+  }
+  ahi = __builtin_bit_cast(f16x8, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+  alo = __builtin_bit_cast(f16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+}
 
 template <int B>
 __global__ void __launch_bounds__(kDqThreads, 2)
 dequant_mfma128_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ norms, int64_t n,
-                       const uint4* __restrict__ pi_frag, PlaneExpansion pe, float* __restrict__ khat,
-                       int64_t tiles) {
-  using TT = Terms<B>;
-  constexpr int NT = TT::count;
-  // byte -> 8 float16 values (bit e set -> +1, clear -> -1)
-  __shared__ uint4 spread[256];
-  {
-    const uint32_t x = threadIdx.x;  // 256 threads, one entry each
-    uint32_t d[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t lo = ((x >> (2 * k)) & 1u) ? 0x3C00u : 0xBC00u;
-      const uint32_t hi = ((x >> (2 * k + 1)) & 1u) ? 0x3C00u : 0xBC00u;
-      d[k] = lo | (hi << 16);
-    }
-    spread[x] = make_uint4(d[0], d[1], d[2], d[3]);
-  }
+                       const uint4* __restrict__ pi_frag, Codebook cb, float* __restrict__ khat, int64_t tiles) {
+  using L = Lookup<B>;
+  __shared__ uint4 tab4[L::kEntries * L::kDwords / 4];
+  __shared__ float4 nrow[4][8];  // per wave: the tile's 32 norms
+  uint32_t* tab = reinterpret_cast<uint32_t*>(tab4);
+  build_table<B>(tab, cb);
   __syncthreads();
 
   const int w = threadIdx.x >> 6;
@@ -89,18 +131,15 @@ dequant_mfma128_kernel(const uint32_t* __restrict__ codes, const float* __restri
   for (int s = 0; s < kSteps; ++s)
 #pragma unroll
     for (int q = 0; q < 2; ++q) bpi[s][q] = __builtin_bit_cast(f16x8, pi_frag[((w * kSteps + s) * 2 + q) * 64 + lane]);
-  float alpha[NT];
-#pragma unroll
-  for (int j = 0; j < NT; ++j) alpha[j] = pe.alpha[j] * kPiScaleInv;
 
-  // packed codes and norm of this lane's key, one tile ahead
+  // packed codes and norm of this lane's key (clamped to n - 1), one tile
+  // ahead; a fetch past the last tile also reads key n - 1 and is unused
   auto fetch = [&](int64_t tile, uint4 (&v)[B], float& nv) {
-    const int64_t key = tile * 32 + kl;
-    const bool ok = tile < tiles && key < n;
+    int64_t key = tile * 32 + kl;
+    key = key < n ? key : n - 1;
 #pragma unroll
-    for (int p = 0; p < B; ++p)
-      v[p] = ok ? *reinterpret_cast<const uint4*>(codes + (key * B + p) * 4) : make_uint4(0u, 0u, 0u, 0u);
-    nv = ok ? norms[key] : 0.0f;
+    for (int p = 0; p < B; ++p) v[p] = *reinterpret_cast<const uint4*>(codes + (key * B + p) * 4);
+    nv = norms[key];
   };
   uint4 nxt[B];
   float nxt_n;
@@ -116,33 +155,40 @@ dequant_mfma128_kernel(const uint32_t* __restrict__ codes, const float* __restri
     }
     const float nk = nxt_n;
     fetch(tile + gridDim.x, nxt, nxt_n);
-    f32x16 acc[NT];
-#pragma unroll
-    for (int j = 0; j < NT; ++j) acc[j] = f32x16{};
+    f32x16 acc = {};
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      const int shift = 8 * (2 * (s & 1) + g);
+      uint32_t wp[B];
 #pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int p = 0; p < B; ++p)
-          if (TT::mask[j] & (1u << p)) word ^= pl[p][s >> 1];
-        const f16x8 a = __builtin_bit_cast(f16x8, spread[(word >> shift) & 0xFFu]);
-        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bpi[s][1], acc[j], 0, 0, 0);
-        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bpi[s][0], acc[j], 0, 0, 0);
-      }
+      for (int p = 0; p < B; ++p) wp[p] = pl[p][s >> 1];
+      f16x8 ahi, alo;
+      load_a<B>(tab, wp, 8 * (2 * (s & 1) + g), ahi, alo);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, bpi[s][0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, bpi[s][1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, bpi[s][0], acc, 0, 0, 0);
     }
     // lane holds coordinate 32w + kl of keys 8(r/4) + 4g + r%4
+    reinterpret_cast<float*>(nrow[w])[kl] = nk * kOutScale;  // both lane groups hold key kl
+    float o[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = nrow[w][2 * q + g];
+      o[4 * q] = v.x * acc[4 * q];
+      o[4 * q + 1] = v.y * acc[4 * q + 1];
+      o[4 * q + 2] = v.z * acc[4 * q + 2];
+      o[4 * q + 3] = v.w * acc[4 * q + 3];
+    }
     float* out = khat + tile * 32 * 128 + 32 * w + kl;
+    if (tile * 32 + 32 <= n) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kr = 8 * (r >> 2) + 4 * g + (r & 3);
-      const float nr = __shfl(nk, kr);
-      float v = 0.0f;
+      for (int r = 0; r < 16; ++r) __builtin_nontemporal_store(o[r], out + (8 * (r >> 2) + 4 * g + (r & 3)) * 128);
+    } else {
+      const int last = static_cast<int>(n - 1 - tile * 32);  // rows past it repeat row n - 1
 #pragma unroll
-      for (int j = 0; j < NT; ++j) v = fmaf(alpha[j], acc[j][r], v);
-      if (tile * 32 + kr < n) __builtin_nontemporal_store(nr * v, out + kr * 128);
+      for (int r = 0; r < 16; ++r) {
+        const int kr = 8 * (r >> 2) + 4 * g + (r & 3);
+        __builtin_nontemporal_store(o[r], out + (kr < last ? kr : last) * 128);
+      }
     }
   }
 }
@@ -151,9 +197,12 @@ template <int B>
 hipError_t launch_b(const tq_ctx* h, const uint32_t* codes, const float* norms, int64_t n, float* khat,
                     hipStream_t stream) {
   const int64_t tiles = (n + 31) / 32;
-  const int64_t blocks = tiles < 1024 ? tiles : 1024;
+  // one resident wave of blocks (3 per CU when registers and the table
+  // allow, else 2; 256 CUs); the tile loop is grid-strided
+  const int64_t resident = 256 * (B == 3 ? 2 : 3);
+  const int64_t blocks = tiles < resident ? tiles : resident;
   hipLaunchKernelGGL(dequant_mfma128_kernel<B>, dim3(static_cast<uint32_t>(blocks)), dim3(kDqThreads), 0, stream,
-                     codes, norms, n, reinterpret_cast<const uint4*>(h->d_dq_frag), h->planes, khat, tiles);
+                     codes, norms, n, reinterpret_cast<const uint4*>(h->d_dq_frag), h->cb, khat, tiles);
   return hipGetLastError();
 }
 
