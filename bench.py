@@ -179,13 +179,18 @@ def main():
     per = {n: float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]))
            for i, n in enumerate(names)}
 
-    # each kernel again with the caches flushed before every launch
-    flush = torch.empty(1 << 28, dtype=torch.int32, device="cuda")  # 1 GiB > L2 + MALL
+    # each kernel again with the caches flushed before every launch: reading
+    # 1 GiB (> L2 + MALL) leaves only clean lines behind.  A write-based flush
+    # would leave up to the MALL's size of dirty lines whose write-back lands
+    # inside the timed kernel and roughly halves its apparent read rate.
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.zeros((), dtype=torch.float32, device="cuda")
     cold = {}
     for i, n in enumerate(names):
         times = []
         for _ in range(args.cold_reps):
-            flush.zero_()
+            torch.sum(flush, dim=0, out=sink)
+            torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             fns[i]()
@@ -193,7 +198,7 @@ def main():
             torch.cuda.synchronize()
             times.append(a.elapsed_time(b))
         cold[n] = float(np.median(times))
-    del flush
+    del flush, sink
 
     models = kernel_models(w)
     scored = w.groups * w.nq * w.n

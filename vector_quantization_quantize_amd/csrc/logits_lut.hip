@@ -13,9 +13,11 @@
 // word b, which a table indexed by one byte of b evaluates 8 coordinates at a
 // time:  T_x[g][byte] = sum_{i<8} (bit i of byte ? +1 : -1) x[8 g + i].
 //
-// Each workgroup first computes v and w of its 4 queries, scales each by a
-// power of two so that its norm lies in [1, 2), and stores the tables as
-// float16 (4 queries per 8-byte entry):
+// Each workgroup first computes v = Pi q and w = S q (S = G Pi, formed on the
+// host) of its 4 queries, reading the matrices straight from L2 (the first
+// keys are already loading), scales each vector by a power of two so that
+// its norm lies in [1, 2), and stores the tables as float16 (4 queries per
+// 8-byte entry):
 //   entry (byte x, table tab (0 = v, 1 = w), position g) at x*256 + tab*128 + g*8.
 // Lane l walks the 16 byte positions starting at g = l mod 16 (its bit planes
 // are rotated by l mod 16 bytes), so the 16 lanes served by one LDS pass read
@@ -35,7 +37,6 @@ namespace {
 constexpr int kLutThreads = 512;
 constexpr int kDim = 128;                 // padded vector length handled here
 constexpr int kTableBytes = 256 * 256;    // [x][tab][g] x 8 bytes = 64 KiB
-constexpr int kNibbleFloats = 16 * 2 * 16 * 4;  // one table at a time
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
@@ -137,63 +138,93 @@ __device__ __forceinline__ void pin(half2_t (&p)[N][2]) {
   for (int j = 0; j < N; ++j) asm volatile("" : "+v"(p[j][0]), "+v"(p[j][1])::"memory");
 }
 
-// copy the d x d row-major matrix `src` (d <= 128) into LDS as a zero-padded
-// 128 x 128 row-major matrix; every load of a batch issued before its stores
-__device__ __forceinline__ void stage_matrix(float* dst, const float* __restrict__ src, int d, int tid) {
-#pragma unroll
-  for (int k0 = 0; k0 < kDim * kDim / kLutThreads; k0 += 16) {
-    float tmp[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int e = tid + (k0 + k) * kLutThreads;
-      const int i = e >> 7, j = e & (kDim - 1);
-      tmp[k] = (i < d && j < d) ? src[i * d + j] : 0.0f;
-    }
-#pragma unroll
-    for (int k = 0; k < 16; ++k) dst[tid + (k0 + k) * kLutThreads] = tmp[k];
-  }
-}
-
 template <int B>
 __global__ void __launch_bounds__(kLutThreads, 2)
 logits_lut128_kernel(const float* __restrict__ queries, int quads, int64_t nq, int64_t n, int d,
-                     const float* __restrict__ piT, const float* __restrict__ gT,
+                     const float* __restrict__ piT, const float* __restrict__ sT,  // 128 x 128, zero-padded
                      const uint32_t* __restrict__ codes, const uint32_t* __restrict__ signs,
                      const float* __restrict__ norms, const float* __restrict__ rnorms,
                      float* __restrict__ scores, PlaneExpansion pe, float kappa, int64_t keys_per_block) {
   using TT = Terms<B>;
   constexpr int NT = TT::count;
   __shared__ __align__(16) unsigned char tabs[kTableBytes];
-  __shared__ __align__(16) float nib[kNibbleFloats];
-  __shared__ float qs[4][kDim];
+  __shared__ float4 qs[kDim];  // the 4 queries, coordinate-major
   __shared__ float vec[2][4][kDim];  // scaled v and w
   __shared__ float scale[2][4];
   const int tid = threadIdx.x;
   const int64_t grp = blockIdx.y / quads;
   const int64_t q0 = int64_t(blockIdx.y % quads) * 4;
 
-  // ---- queries -> v = Pi q -> w = G v (float32) ----
-  // Pi^T and then G^T (d x d <= 64 KiB) are staged through the table region,
-  // which is free until the tables are built; thread (q, j, hf) sums half hf
-  // of the d terms of output j of query q
-  for (int e = tid; e < 4 * kDim; e += kLutThreads) {
-    const int q = e >> 7, i = e & (kDim - 1);
-    qs[q][i] = (q0 + q < nq && i < d) ? queries[(grp * nq + q0 + q) * d + i] : 0.0f;
-  }
-  float* stage = reinterpret_cast<float*>(tabs);
+  const int qc = int(nq - q0 < 4 ? nq - q0 : 4);
+  const int64_t kbeg = int64_t(blockIdx.x) * keys_per_block;
+  const int64_t kend = kbeg + keys_per_block < n ? kbeg + keys_per_block : n;
+  int64_t t = kbeg + tid;
+
+  // ---- v = Pi q and w = S q (float32) ----
+  // Thread (part, j) sums i in [32 part, 32 part + 32) of output j for the 4
+  // queries and both matrices, in two batches of 16 loads per matrix; the
+  // first batch is in flight while the queries are staged.  The tables'
+  // space holds the partial sums [part][tab][q][j] until the four parts are
+  // added.
+  const int mj = tid & (kDim - 1), part = tid >> 7;
+  // the matrices are zero-padded to 128 x 128: no bounds checks
+  const float* pcol = piT + 32 * part * kDim + mj;
+  const float* scol = sT + 32 * part * kDim + mj;
+  auto load_batch = [&](int i0, float (&pv)[16], float (&pw)[16]) {
 #pragma unroll
-  for (int tab = 0; tab < 2; ++tab) {
-    stage_matrix(stage, tab == 0 ? piT : gT, d, tid);
-    __syncthreads();
-    // output (q, j) for q = 0..3, j = tid mod 128: 4 chains of 128 terms
-    const int j = tid & (kDim - 1), qsel = tid >> 7;
-    const float* x = tab == 0 ? qs[qsel] : vec[0][qsel];
-    float a = 0.0f;
-#pragma unroll 16
-    for (int i = 0; i < kDim; ++i) a = fmaf(stage[i * kDim + j], x[i], a);
-    vec[tab][qsel][j] = a;
-    __syncthreads();
+    for (int k = 0; k < 16; ++k) {
+      pv[k] = pcol[(i0 + k) * kDim];
+      pw[k] = scol[(i0 + k) * kDim];
+    }
+  };
+  // Loads complete in issue order, so the order below lets each wait cover
+  // only what it needs: queries, the first matrix batch, the second batch,
+  // then the block's first keys (they arrive while the tables are built).
+  // thread tid loads coordinate tid % 128 of query tid / 128 (addresses
+  // clamped in range, values past d or nq zeroed): no branches
+  const int qi = tid & (kDim - 1), qq = tid >> 7;
+  const bool qok = q0 + qq < nq && qi < d;
+  const float qraw = queries[(grp * nq + (q0 + qq < nq ? q0 + qq : nq - 1)) * d + (qi < d ? qi : d - 1)];
+  float pv0[16], pw0[16];
+  load_batch(0, pv0, pw0);
+  reinterpret_cast<float*>(qs)[qi * 4 + qq] = qok ? qraw : 0.0f;
+  __syncthreads();
+  Packed<B> cur;
+  {
+    float pv1[16], pw1[16];
+    load_batch(16, pv1, pw1);
+    cur = load_key<B>(codes, signs, norms, rnorms, grp * n + (t < kend ? t : kend - 1));
+    float av[4] = {0.0f, 0.0f, 0.0f, 0.0f}, aw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto accumulate = [&](int i0, const float (&pv)[16], const float (&pw)[16]) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float4 x = qs[32 * part + i0 + k];
+        av[0] = fmaf(pv[k], x.x, av[0]);
+        av[1] = fmaf(pv[k], x.y, av[1]);
+        av[2] = fmaf(pv[k], x.z, av[2]);
+        av[3] = fmaf(pv[k], x.w, av[3]);
+        aw[0] = fmaf(pw[k], x.x, aw[0]);
+        aw[1] = fmaf(pw[k], x.y, aw[1]);
+        aw[2] = fmaf(pw[k], x.z, aw[2]);
+        aw[3] = fmaf(pw[k], x.w, aw[3]);
+      }
+    };
+    accumulate(0, pv0, pw0);
+    accumulate(16, pv1, pw1);
+    const int j = mj;
+    float* red = reinterpret_cast<float*>(tabs);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      red[((part * 2 + 0) * 4 + q) * kDim + j] = av[q];
+      red[((part * 2 + 1) * 4 + q) * kDim + j] = aw[q];
+    }
   }
+  __syncthreads();
+  for (int e = tid; e < 2 * 4 * kDim; e += kLutThreads) {  // e = (tab * 4 + q) * kDim + j
+    const float* red = reinterpret_cast<const float*>(tabs);
+    vec[e >> 9][(e >> 7) & 3][e & (kDim - 1)] = (red[e] + red[1024 + e]) + (red[2048 + e] + red[3072 + e]);
+  }
+  __syncthreads();
   // power-of-two scale per (table, query): scaled norm in [1, 2); wave w < 8
   // reduces vector (w >> 2, w & 3)
   if (tid < 8 * 64) {
@@ -209,31 +240,35 @@ logits_lut128_kernel(const float* __restrict__ queries, int quads, int64_t nq, i
     }
   }
   __syncthreads();
-  // tables, one at a time (tab 0 = v, 1 = w).  Half-byte sums (float32):
-  // entry (hf*16 + y)*16 + g, 4 queries each, consecutive g adjacent so the
-  // byte pass reads them without bank conflicts; byte entry (x, tab, g) =
-  // low-half sum + high-half sum, rounded to float16.
+  // Byte tables (tab 0 = v, 1 = w) by Gray-code walks: thread (tab, seg,
+  // position g, query q) = tid bits (8, 7..6, 5..2, 1..0) visits the 64
+  // bytes x = rank ^ (rank >> 1), rank in [64 seg, 64 seg + 64).  Successive
+  // bytes differ in one bit b, so each entry is the previous one plus or
+  // minus twice coordinate 8 g + b; a wave writes 128 contiguous bytes per
+  // step.  The running float32 sum drifts by well under the float16
+  // rounding of the stored entry.
+  {
+    const int q = tid & 3, gg = (tid >> 2) & 15, seg = (tid >> 6) & 3, tab = tid >> 8;
+    const float sc = scale[tab][q];
+    float xs[8];
 #pragma unroll
-  for (int tab = 0; tab < 2; ++tab) {
-    for (int e = tid; e < kNibbleFloats; e += kLutThreads) {
-      const int q = e & 3, gg = (e >> 2) & 15, y = (e >> 6) & 15, hf = e >> 10;
-      const float* x = &vec[tab][q][8 * gg + 4 * hf];
-      float sum = 0.0f;
-      for (int b = 0; b < 4; ++b) sum += ((y >> b) & 1) ? x[b] : -x[b];
-      nib[e] = sum * scale[tab][q];
+    for (int i = 0; i < 8; ++i) xs[i] = sc * vec[tab][q][8 * gg + i];
+    unsigned char* col = tabs + tab * 128 + gg * 8 + q * 2;
+    const int rank0 = 64 * seg;
+    const int x0 = rank0 ^ (rank0 >> 1);
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc += ((x0 >> i) & 1) ? xs[i] : -xs[i];
+    *reinterpret_cast<_Float16*>(col + x0 * 256) = static_cast<_Float16>(acc);
+#pragma unroll
+    for (int m = 1; m < 64; ++m) {
+      const int rank = rank0 + m, x = rank ^ (rank >> 1);
+      const int b = __builtin_ctz(m);
+      acc += ((x >> b) & 1) ? 2.0f * xs[b] : -2.0f * xs[b];
+      *reinterpret_cast<_Float16*>(col + x * 256) = static_cast<_Float16>(acc);
     }
-    __syncthreads();
-    for (int e = tid; e < 256 * 16; e += kLutThreads) {
-      const int gg = e & 15, x = e >> 4;
-      const float4 lo = *reinterpret_cast<const float4*>(nib + ((0 * 16 + (x & 15)) * 16 + gg) * 4);
-      const float4 hi = *reinterpret_cast<const float4*>(nib + ((1 * 16 + (x >> 4)) * 16 + gg) * 4);
-      const half2_t q01 = {(_Float16)(lo.x + hi.x), (_Float16)(lo.y + hi.y)};
-      const half2_t q23 = {(_Float16)(lo.z + hi.z), (_Float16)(lo.w + hi.w)};
-      *reinterpret_cast<uint2*>(tabs + x * 256 + tab * 128 + gg * 8) =
-          make_uint2(__builtin_bit_cast(uint32_t, q01), __builtin_bit_cast(uint32_t, q23));
-    }
-    __syncthreads();
   }
+  __syncthreads();
 
   // per-lane rotation and address bases
   const uint32_t r = uint32_t(tid) & 15u;
@@ -251,15 +286,10 @@ logits_lut128_kernel(const float* __restrict__ queries, int quads, int64_t nq, i
   const half2_t pick_lo = {(_Float16)1.0f, (_Float16)0.0f};
   const half2_t pick_hi = {(_Float16)0.0f, (_Float16)1.0f};
 
-  const int qc = int(nq - q0 < 4 ? nq - q0 : 4);
-  const int64_t kbeg = int64_t(blockIdx.x) * keys_per_block;
-  const int64_t kend = kbeg + keys_per_block < n ? kbeg + keys_per_block : n;
-  int64_t t = kbeg + tid;
-  Packed<B> cur;
-  if (t < kend) cur = load_key<B>(codes, signs, norms, rnorms, grp * n + t);
   for (; t < kend; t += kLutThreads) {
-    Packed<B> nxt;
-    if (t + kLutThreads < kend) nxt = load_key<B>(codes, signs, norms, rnorms, grp * n + t + kLutThreads);
+    // next keys, clamped into the block's range (a load past it is unused)
+    const int64_t tn = t + kLutThreads < kend ? t + kLutThreads : kend - 1;
+    const Packed<B> nxt = load_key<B>(codes, signs, norms, rnorms, grp * n + tn);
     Words pl[B];
 #pragma unroll
     for (int p = 0; p < B; ++p) pl[p] = rotate(cur.plane[p], w1, w2, bs);
@@ -339,14 +369,14 @@ hipError_t launch_b(const tq_ctx* h, const float* queries, int64_t groups, int64
   const float kappa = 1.2533141373155002512f / float(h->d);
   const dim3 grid(static_cast<uint32_t>(chunks), static_cast<uint32_t>(ys));
   hipLaunchKernelGGL(logits_lut128_kernel<B>, grid, dim3(kLutThreads), 0, stream, queries, int(quads), nq, n,
-                     h->d, h->d_piT, h->d_gT, codes, signs, norms, rnorms, scores, h->planes, kappa, kpb);
+                     h->d, h->d_piT128, h->d_sT128, codes, signs, norms, rnorms, scores, h->planes, kappa, kpb);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool logits_lut128_supported(const tq_ctx* h) {
-  return h->words == 4 && h->d <= kDim && h->code_bits >= 1 && h->code_bits <= 4;
+  return h->words == 4 && h->d <= kDim && h->d_piT128 && h->d_sT128 && h->code_bits >= 1 && h->code_bits <= 4;
 }
 
 hipError_t launch_logits_lut128(const tq_ctx* h, const float* queries, int64_t groups, int64_t nq,

@@ -22,7 +22,7 @@ bool trace_enabled() {
 }
 
 void free_device(tq_ctx* h) {
-  float** ptrs[] = {&h->d_pi, &h->d_piT, &h->d_g, &h->d_gT};
+  float** ptrs[] = {&h->d_pi, &h->d_piT, &h->d_g, &h->d_gT, &h->d_piT128, &h->d_sT128};
   for (float** p : ptrs) {
     if (*p) (void)hipFree(*p);
     *p = nullptr;
@@ -166,6 +166,21 @@ int finish_init(tq_ctx* h) {
   if ((rc = upload(&h->d_piT, transpose(h->pi, d))) != TQ_OK) return rc;
   if ((rc = upload(&h->d_g, h->g)) != TQ_OK) return rc;
   if ((rc = upload(&h->d_gT, transpose(h->g, d))) != TQ_OK) return rc;
+  if (d <= 128) {
+    // For the lookup-table scorer: Pi^T and S^T with S = G Pi (float64
+    // products, one rounding; w = S q = G (Pi q) in one matrix-vector
+    // product), both zero-padded to 128 x 128 row-major
+    std::vector<float> pt(size_t(128) * 128, 0.0f), st(size_t(128) * 128, 0.0f);
+    for (int j = 0; j < d; ++j)
+      for (int i = 0; i < d; ++i) {
+        double acc = 0.0;
+        for (int k = 0; k < d; ++k) acc += double(h->g[size_t(j) * d + k]) * double(h->pi[size_t(k) * d + i]);
+        st[size_t(i) * 128 + j] = float(acc);
+        pt[size_t(i) * 128 + j] = h->pi[size_t(j) * d + i];
+      }
+    if ((rc = upload(&h->d_piT128, pt)) != TQ_OK) return rc;
+    if ((rc = upload(&h->d_sT128, st)) != TQ_OK) return rc;
+  }
   return build_fragments(h);
 }
 

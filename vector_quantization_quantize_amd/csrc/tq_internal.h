@@ -48,6 +48,8 @@ struct tq_ctx {
   float* d_piT = nullptr;  // Pi^T row-major: d_piT[i*d + j] = Pi[j][i]
   float* d_g = nullptr;    // G   row-major
   float* d_gT = nullptr;   // G^T row-major
+  float* d_piT128 = nullptr;  // Pi^T zero-padded to 128 x 128, d <= 128 only
+  float* d_sT128 = nullptr;   // (G Pi)^T zero-padded to 128 x 128, d <= 128 only
   // d = 128 only: register fragments of the matrix-core quantize kernel
   uint16_t* d_pi_frag = nullptr;  // [word 4][step 8][piece 2][lane 64][8] f16 pieces of 2^12 Pi
   uint16_t* d_g_frag = nullptr;   // [word 4][step 8][piece 2][lane 64][8] f16 pieces of 2^10 G
