@@ -254,18 +254,22 @@ logits_lut128_kernel(const float* __restrict__ queries, int quads, int64_t nq, i
 #pragma unroll
     for (int i = 0; i < 8; ++i) xs[i] = sc * vec[tab][q][8 * gg + i];
     unsigned char* col = tabs + tab * 128 + gg * 8 + q * 2;
-    const int rank0 = 64 * seg;
-    const int x0 = rank0 ^ (rank0 >> 1);
+    // x(rank0 + m) = gb ^ gray(m) with gb = gray(64 seg) a multiple of 32:
+    // only bit 5 of gray(m) interacts with gb, so two bases and a
+    // compile-time offset address every entry
+    const int rank0 = 64 * seg, gb = rank0 ^ (rank0 >> 1);
+    unsigned char* base0 = col + 256 * gb;
+    unsigned char* base1 = col + 256 * (gb ^ 32);
     float acc = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc += ((x0 >> i) & 1) ? xs[i] : -xs[i];
-    *reinterpret_cast<_Float16*>(col + x0 * 256) = static_cast<_Float16>(acc);
+    for (int i = 0; i < 8; ++i) acc += ((gb >> i) & 1) ? xs[i] : -xs[i];
+    *reinterpret_cast<_Float16*>(base0) = static_cast<_Float16>(acc);
 #pragma unroll
     for (int m = 1; m < 64; ++m) {
-      const int rank = rank0 + m, x = rank ^ (rank >> 1);
-      const int b = __builtin_ctz(m);
-      acc += ((x >> b) & 1) ? 2.0f * xs[b] : -2.0f * xs[b];
-      *reinterpret_cast<_Float16*>(col + x * 256) = static_cast<_Float16>(acc);
+      const int gm = m ^ (m >> 1), b = __builtin_ctz(m);
+      const bool up = b == 5 ? (((gb ^ gm) >> 5) & 1) != 0 : ((gm >> b) & 1) != 0;
+      acc += up ? 2.0f * xs[b] : -2.0f * xs[b];
+      *reinterpret_cast<_Float16*>(((gm & 32) ? base1 : base0) + 256 * (gm & 31)) = static_cast<_Float16>(acc);
     }
   }
   __syncthreads();
