@@ -216,13 +216,13 @@ def main():
     kern["tq_logits"]["keys_scored_per_s_cold"] = scored / (cold["tq_logits"] * 1e-3)
 
     # which resource bounds each kernel as built at d = 128: logits streams
-    # bytes; quantize runs its two projections on the matrix cores (6 f16/bf16
-    # passes of 2 d^2 for 4 d^2 useful flops per key); the reconstruction
+    # bytes; quantize runs its two projections on the matrix cores (2 f16
+    # passes for Pi k on power-of-two scaled keys + 3 for G r, each 2 d^2, for
+    # 4 d^2 useful flops per key); the reconstruction (3 passes of 2 d^2)
     # writes 512 B per key and is bound by HBM writes
     bound = {"tq_quantize": ("mfma", BF16_MFMA_PEAK_TFLOPS), "tq_logits": ("hbm", HBM_PEAK_GBS),
              "tq_dequant_mse": ("hbm", HBM_PEAK_GBS)}
-    terms = {1: 1, 2: 2, 3: 4, 4: 8}[w.bits - 1]  # sign-plane terms of the level set
-    raw_passes = {"tq_quantize": 12 * w.d * w.d, "tq_dequant_mse": terms * 4 * w.d * w.d}
+    raw_passes = {"tq_quantize": 10 * w.d * w.d, "tq_dequant_mse": 6 * w.d * w.d}
     for n, f in raw_passes.items():
         kern[n]["raw_mfma_TFLOPs"] = round(f * total / (per[n] * 1e-3) / 1e12, 2)
 
