@@ -139,9 +139,12 @@ TQ_API uint64_t tq_params_hash(tq_handle h);
 /* Quantize n keys.  keys: device, n rows of d elements of type key_dtype
  * (TQ_F32 or TQ_BF16), row i at keys + i*ldk elements (ldk >= d).
  * Outputs (device): codes [n][B][W], signs [n][W], norms [n], rnorms [n] as
- * in the packed layout.  Asynchronous on `stream`.  Norms are computed in
- * float32: a key whose squared norm overflows float32 (||k|| above about
- * 1.8e19) gives an infinite norm; NaN/Inf inputs are undefined. */
+ * in the packed layout, 4-byte aligned.  Asynchronous on `stream`.  Norms
+ * are computed in float32: a key whose squared norm overflows float32
+ * (||k|| above about 1.8e19) gives an infinite norm; NaN/Inf inputs are
+ * undefined.  The fast d = 128 path for bf16 keys needs keys and all four
+ * outputs 16-byte aligned and ldk a multiple of 8; other calls take the
+ * general kernels (same results within the parity bounds). */
 TQ_API int tq_quantize(tq_handle h, const void* keys, int32_t key_dtype, int64_t n, int64_t ldk,
                 uint32_t* codes, uint32_t* signs, float* norms, float* rnorms, void* stream);
 

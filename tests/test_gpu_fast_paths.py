@@ -42,22 +42,29 @@ def test_d128_bf16_fast_path(env, bits, groups, n, nq):
     print("mismatches", rep.code_mismatch, rep.sign_mismatch, "cascade", rep.cascade_keys)
 
 
+@pytest.mark.parametrize("n", [40007, 82697])
 @pytest.mark.parametrize("bits", [2, 3, 4, 5])
-def test_fast_paths_many_tiles_per_block(env, bits):
-    """40007 keys = 1251 tiles of 32 (the last one ragged), more than the
-    resident blocks: every block of the quantize and reconstruction kernels
-    runs its multi-tile loop, with both an even and an odd number of tiles
-    per block, and a zero key lands in a later tile."""
+def test_fast_paths_many_tiles_per_block(env, bits, n):
+    """More tiles of 32 keys than resident blocks, the last tile ragged:
+    40007 keys give the quantize kernel's blocks 2 or 3 tiles (first and
+    second pass, then the last pass on either buffer), 82697 keys give 5 or 6
+    (the unrolled loop, ending on either buffer); the reconstruction kernel
+    loops too.  A zero key lands in a later tile.  The outputs start out as
+    sentinels, so a row the kernel never writes cannot pass."""
     torch, tqm, _ = env
     from oracle import parity
     from tests.test_gpu_parity import _params
-    n = 40007
     _announce(f"fast quantize + dequant, many tiles per block: bits={bits} n={n}")
-    rs = np.random.default_rng(77 + bits)
+    rs = np.random.default_rng(77 + bits + n)
     keys = _bf16_keys(torch, rs, n, 128)
     keys[33333] = 0.0
     h = tqm.tq_init(128, bits, 0)
-    out = tqm.tq_quantize(h, torch.from_numpy(keys).bfloat16().cuda())
+    out = tqm.empty_packed(h, n, "cuda")
+    for t in out[:2]:
+        t.fill_(-1)
+    for t in out[2:]:
+        t.fill_(float("nan"))
+    out = tqm.tq_quantize(h, torch.from_numpy(keys).bfloat16().cuda(), out=out)
     pr = _params(128, bits)
     qz = tq.quantize(pr, keys.astype(np.float64))
     rep = parity.compare_quantize(pr, qz, *(_cpu(t) for t in out))
@@ -93,11 +100,17 @@ def test_fast_quantize_exact_rescaling_and_strides(env):
     d2 = tqm.tq_quantize(h, odd[:, :128])
     for x, y in zip(a, d1):
         assert torch.equal(x, y)
+    # outputs that are not 16-byte aligned (norms one float into a buffer)
+    # take the general path
+    nbuf = torch.empty(1000, dtype=torch.float32, device="cuda")
+    d3 = tqm.empty_packed(h, 999, "cuda")
+    d3 = tqm.tq_quantize(h, base, out=(d3[0], d3[1], nbuf[1:], d3[3]))
     pr = P.init(128, 3, 0)
     from oracle import parity
     qz = tq.quantize(pr, keys.astype(np.float64))
-    rep = parity.compare_quantize(pr, qz, *(_cpu(t) for t in d2))
-    assert rep.ok(), rep
+    for d in (d2, d3):
+        rep = parity.compare_quantize(pr, qz, *(_cpu(t) for t in d))
+        assert rep.ok(), rep
 
 
 def test_reference_and_fast_kernels_both_match_oracle(env):

@@ -48,6 +48,13 @@
 // The pass is written as 40 slots of one MFMA plus a slice of vector work,
 // separated by scheduling fences: left alone, the compiler issues all MFMAs
 // first and the vector work after them, and nothing overlaps.
+//
+// Outputs go through LDS: each wave writes its words of a tile's rows (code
+// rows, sign rows, norms and rnorms, 16 bytes each, in their memory order)
+// to a staging area, and the next pass copies the area out with one 16-byte
+// store per lane.  Written directly, every wave would issue B + 3 stores of
+// 4-byte words strided by the row length, all in the same slots of every
+// wave on the CU, and the store path would stall the pass.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -102,14 +109,6 @@ __device__ __forceinline__ uint32_t scale_to_f16_pair(float x0, float x1, float 
   return h;
 }
 
-__device__ __forceinline__ float dpp_sum8(float x) {
-  // sum over the 8 lanes of an aligned group: quad xor 1, quad xor 2, then
-  // the mirror within each half row (lane i <-> 7 - i) joins the two quads
-  x += as_f32(__builtin_amdgcn_mov_dpp(static_cast<int>(as_u32(x)), 0xB1, 0xF, 0xF, false));
-  x += as_f32(__builtin_amdgcn_mov_dpp(static_cast<int>(as_u32(x)), 0x4E, 0xF, 0xF, false));
-  x += as_f32(__builtin_amdgcn_mov_dpp(static_cast<int>(as_u32(x)), 0x141, 0xF, 0xF, false));
-  return x;
-}
 
 // Bucketize one coordinate and return the residual times 2^12.  The
 // coordinate arrives unscaled as a = 2^12 2^s n z; the thresholds 2^12 t are
@@ -189,6 +188,12 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
   // residual exchange [buf][piece][step][lane group][key] (8 halves each)
   __shared__ uint4 xb[2][2][kSteps][2][32];
   __shared__ float rsq[2][4][32];
+  // output staging, by tile parity: the tile's 32 B code rows, the previous
+  // tile's 32 sign rows, 8 rows of this tile's norms, 8 rows of the previous
+  // tile's rnorms (16 bytes each, the order they have in memory)
+  constexpr int kOutRows = 32 * B + 48;
+  constexpr int kRowS = 32 * B, kRowN = kRowS + 32, kRowR = kRowN + 8;
+  __shared__ uint4 ost[2][kOutRows];
 
   const int w = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -226,26 +231,41 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
     row_next += row_step;
   };
   // staging pieces: unpack + partial sum of squares, norm and scale, convert
+  // Staging is one dependency chain (unpack, sum of squares, 8-lane
+  // reduction, square root, scale, convert); its steps are small functions
+  // so that the pipelined pass can put each in its own slot, away from the
+  // step it waits for.
   struct Stage {
     float x[16];
+    float part[4];  // partial sums of squares: two chains per 8 values
     float ss, nk, inv, ns, scale;
   };
   auto stage_unpack = [&](Stage& st, const uint4& v, int half) {
     const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-    if (half == 0) st.ss = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       st.x[8 * half + 2 * i] = as_f32(u[i] << 16);
       st.x[8 * half + 2 * i + 1] = as_f32(u[i] & 0xFFFF0000u);
       // bf16 products are exact in float32
-      st.ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u[i]), __builtin_bit_cast(bf16x2, u[i]),
-                                              st.ss, false);
+      const bf16x2 b2 = __builtin_bit_cast(bf16x2, u[i]);
+      float& acc = st.part[2 * half + (i & 1)];
+      acc = __builtin_amdgcn_fdot2_f32_bf16(b2, b2, i < 2 ? 0.0f : acc, false);
     }
+  };
+  auto stage_sum = [&](Stage& st) { st.ss = (st.part[0] + st.part[1]) + (st.part[2] + st.part[3]); };
+  // one level of the sum over the 8 lanes of an aligned group: quad xor 1,
+  // quad xor 2, then the mirror within each half row (lane i <-> 7 - i)
+  auto stage_reduce = [&](Stage& st, int level) {
+    const int x = static_cast<int>(as_u32(st.ss));
+    const int y = level == 0   ? __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false)
+                  : level == 1 ? __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false)
+                               : __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);
+    st.ss += as_f32(static_cast<uint32_t>(y));
   };
   auto stage_norm = [&](Stage& st) {
     // 2^sh nk in [2^14, 2^15); nk == 0 gives sh = 15 and zero keys.  The
     // hardware square root and reciprocal are within 1 ulp.
-    st.nk = __builtin_amdgcn_sqrtf(dpp_sum8(st.ss));
+    st.nk = __builtin_amdgcn_sqrtf(st.ss);
     const int sh = 15 - __builtin_amdgcn_frexp_expf(st.nk);
     st.scale = __builtin_amdgcn_ldexpf(1.0f, sh);
     st.ns = st.nk > 0.0f ? __builtin_amdgcn_ldexpf(st.nk, sh) : __builtin_inff();
@@ -262,6 +282,10 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
     Stage st;
     stage_unpack(st, a, 0);
     stage_unpack(st, b, 1);
+    stage_sum(st);
+    stage_reduce(st, 0);
+    stage_reduce(st, 1);
+    stage_reduce(st, 2);
     stage_norm(st);
     stage_store(st, buf, 0);
     stage_store(st, buf, 1);
@@ -291,6 +315,29 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
     acc1 = mfma16(api[s][0], kf, acc1);
   }
 
+  // Copy-out: wave w moves rows [w R, w R + R) of a staged tile, R = kOutRows
+  // / 4, one per lane (lanes past R repeat the last one: same address, same
+  // value).  Code rows and norms belong to the tile of the previous pass
+  // (tile c), sign rows and rnorms to the tile before it (c - 1 of this
+  // block), which a lane's store pointer lags by.
+  constexpr int kOutWave = kOutRows / 4;
+  const int orow = w * kOutWave + (lane < kOutWave ? lane : kOutWave - 1);
+  uint4* const codes4 = reinterpret_cast<uint4*>(codes);
+  uint4* const signs4 = reinterpret_cast<uint4*>(signs);
+  uint4* const norms4 = reinterpret_cast<uint4*>(norms);
+  uint4* const rnorms4 = reinterpret_cast<uint4*>(rnorms);
+  // destination of staged row r when tile c (global tile index) is the tile
+  // of the code rows
+  auto out_ptr = [&](int r, int64_t c) -> uint4* {
+    const int64_t pc = c - static_cast<int64_t>(gridDim.x);
+    if (r < kRowS) return codes4 + c * (32 * B) + r;
+    if (r < kRowN) return signs4 + pc * 32 + (r - kRowS);
+    if (r < kRowR) return norms4 + c * 8 + (r - kRowN);
+    return rnorms4 + pc * 8 + (r - kRowR);
+  };
+  const int ostep = (orow < kRowS ? 32 * B : orow < kRowN ? 32 : 8) * static_cast<int>(gridDim.x);
+  uint4* optr = nullptr;  // this lane's destination in the next copy-out (from the third pass on)
+
   // Lanes l and l ^ 32 hold the low and high 16 bits of a word; every lane
   // gets the whole word (v_permlane32_swap hands each half to both lanes).
   auto whole = [](uint32_t x) {
@@ -301,28 +348,26 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
     const auto h = __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(x), false, false);
     return as_f32(h[0]) + as_f32(h[1]);
   };
-  // Stores are branch-free: every lane of every wave stores, rows past the
-  // end go to key n - 1, and all writers of an address write the same value
-  // (rows past the end re-read key n - 1 and give bit-identical results).
-  // With no conditional stores the compiler can count outstanding memory
-  // operations exactly instead of draining them before each use of the
-  // prefetched keys.
   auto rnorm_of = [&](int b) {
     const float* q = rsq[b][0];
     return __builtin_amdgcn_sqrtf((q[kl] + q[32 + kl]) + (q[64 + kl] + q[96 + kl])) * (1.0f / kZScale);
   };
 
-  // One pass: tile i's vector work beside p of tile i-1 and z' of tile i+1.
-  // buf = i % 2 is a compile-time constant (the loop is unrolled by two);
-  // the first pass has no tile i-1 to finish.
-  auto pass = [&](int64_t i, auto bufc, auto firstc) {
+  // One pass: tile i's vector work beside p of tile i-1 and z' of tile i+1,
+  // and the copy-out of the rows staged by pass i-1.  buf = i % 2 is a
+  // compile-time constant (the loop is unrolled by two), and so is the phase:
+  // 0 for the first pass (no tile i-1, nothing staged), 1 for the second
+  // (staged sign rows and rnorms belong to no tile: those lanes repeat a code
+  // or norm row instead), 2 after.  Every tile but the last of the block is
+  // full, so copy-outs need no bounds.
+  auto pass = [&](int64_t i, auto bufc, auto phasec) {
     constexpr int buf = decltype(bufc)::value;
-    constexpr bool first = decltype(firstc)::value;
+    constexpr int phase = decltype(phasec)::value;
+    constexpr bool first = phase == 0;
     constexpr int ob = buf ^ 1;
-    const int64_t key = (blockIdx.x + i * gridDim.x) * 32 + kl;
-    const int64_t kc = key < n ? key : n - 1;
-    const int64_t pkey = key - static_cast<int64_t>(gridDim.x) * 32;
-    const int64_t pkc = pkey < n ? pkey : n - 1;
+    uint4 ov;       // staged row of this lane
+    uint4* odst;    // and where it goes
+    int lrow = orow;
 
     // ---- slot 0: operands of the first MFMAs, and while they load, the
     // thresholds scaled to the key and the first coordinate pair
@@ -357,6 +402,23 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
       if (s + 1 < kSteps) {
         e[r1 - 2] = quant(zt[r1 - 2], inv, us, sgn, jw);
         TQ_PIN(e[r1 - 2]);
+      }
+      if constexpr (phase == 1) {
+        if (s == 0) {
+          // the staged tile is this block's first: no previous tile
+          lrow = orow < kRowS ? orow : orow < kRowN ? orow - kRowS : orow < kRowR ? orow : orow - 8;
+          odst = out_ptr(lrow, blockIdx.x);
+          optr = out_ptr(orow, static_cast<int64_t>(blockIdx.x) + gridDim.x);
+        }
+      } else if constexpr (phase == 2) {
+        if (s == 0) {
+          odst = optr;
+          optr += ostep;
+        }
+      }
+      if constexpr (!first) {
+        if (s == 1) ov = ost[ob][lrow];
+        if (s == 3) *odst = ov;
       }
       TQ_SLOT_END();
       if (s + 1 < kSteps) nrl = __builtin_bit_cast(f16x8, xb[ob][1][s + 1][g][kl]);
@@ -394,48 +456,57 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
       const int s = j >> 1;
       if ((j & 1) == 0 && s + 1 < kSteps) nkf = __builtin_bit_cast(f16x8, ktile[ob][kl][2 * (s + 1) + g]);
       a1 = mfma16(api[s][(j & 1) ? 0 : 1], kf, a1);
+      // dependent staging steps sit at least one slot apart, with independent
+      // work (sign bits, word assembly, stores) between them
       switch (j) {
         case 0: stage_unpack(st, na, 0); break;
         case 1: stage_unpack(st, nb, 1); break;
         case 2:
-          stage_norm(st);
-          if (!first) prn = rnorm_of(ob);
-          break;
-        case 3: stage_store(st, buf, 0); break;
-        case 4: stage_store(st, buf, 1); break;
-        case 5: fetch(na, nb); break;  // tile i + 3
-        case 6:
 #pragma unroll
           for (int r = 15; r >= 8; --r) sw = __builtin_amdgcn_alignbit(sw, as_u32(acc2[r]), 31);
           break;
-        case 7:
+        case 3: stage_sum(st); break;
+        case 4:
 #pragma unroll
           for (int r = 7; r >= 0; --r) sw = __builtin_amdgcn_alignbit(sw, as_u32(acc2[r]), 31);
           break;
-        case 8:
+        case 5: stage_reduce(st, 0); break;
+        case 6:
           // 16-bit halves: plane B-1 = [z >= 0], plane p = j_p ^ [z < 0],
           // signs = [p > 0]
 #pragma unroll
           for (int p = 0; p + 1 < B; ++p) word[p] = jw[p] ^ sgn;
           word[B - 1] = sgn ^ 0xFFFFu;
           word[B] = sw ^ 0xFFFFu;
+          if (!first) prn = rnorm_of(ob);
           break;
-        case 9:
+        case 7: stage_reduce(st, 1); break;
+        case 8:
 #pragma unroll
           for (int p = 0; p <= B; ++p) word[p] = whole(word[p]);
           break;
+        case 9: stage_reduce(st, 2); break;
         case 10: rsq[buf][w][kl] = both_sum(rr); break;
-        case 11:
+        case 11: stage_norm(st); break;
+        case 12: {
+          // word w of this tile's code rows and of the previous tile's sign
+          // rows (lane group g takes every other word; with B even the last
+          // word goes twice), this tile's norm (g = 0) and the previous
+          // tile's rho (g = 1)
+          uint32_t* o32 = reinterpret_cast<uint32_t*>(ost[buf]);
 #pragma unroll
-          for (int p = 0; p < B; ++p) codes[(kc * B + p) * 4 + w] = word[p];
-          norms[kc] = nrm;
-          break;
-        case 12:
-          if (!first) {
-            signs[pkc * 4 + w] = word[B];
-            rnorms[pkc] = prn;
+          for (int q = 0; 2 * q <= B; ++q) {
+            const int p0 = 2 * q, p1 = 2 * q + 1 <= B ? 2 * q + 1 : B;
+            const int a0 = (p0 < B ? kl * B + p0 : kRowS + kl) * 4 + w;
+            const int a1 = (p1 < B ? kl * B + p1 : kRowS + kl) * 4 + w;
+            o32[g ? a1 : a0] = g ? word[p1] : word[p0];
           }
+          reinterpret_cast<float*>(&ost[buf][kRowN])[32 * g + kl] = g ? prn : nrm;
           break;
+        }
+        case 13: stage_store(st, buf, 0); break;
+        case 14: stage_store(st, buf, 1); break;
+        case 15: fetch(na, nb); break;  // tile i + 3
         default: break;
       }
       TQ_SLOT_END();
@@ -444,10 +515,28 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
     acc1 = a1;
     __syncthreads();
   };
-  // p of the last tile
+  // After the last pass (tile i): the rows it staged, bounded by n since its
+  // tile may be the ragged last one, then p of tile i and its sign words and
+  // rho, written directly (rows past the end go to key n - 1, same value).
   auto finish = [&](int64_t i, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
-    const int64_t key = (blockIdx.x + i * gridDim.x) * 32 + kl;
+    const int64_t c = blockIdx.x + i * gridDim.x;
+    const int64_t left = n - c * 32;
+    const int vk = left < 32 ? static_cast<int>(left) : 32;  // keys of tile c
+    const uint4 v = ost[buf][orow];
+    if (orow < kRowS) {
+      if (orow < vk * B) *out_ptr(orow, c) = v;
+    } else if (orow < kRowN || orow >= kRowR) {
+      if (i > 0) *out_ptr(orow, c) = v;  // the tile before c, if any
+    } else {
+      const int k0 = 4 * (orow - kRowN);
+      float* dn = norms + c * 32 + k0;
+      const float nv[4] = {as_f32(v.x), as_f32(v.y), as_f32(v.z), as_f32(v.w)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (k0 + e < vk) dn[e] = nv[e];
+    }
+    const int64_t key = c * 32 + kl;
     const int64_t kc = key < n ? key : n - 1;
     f32x16 acc2 = {};
 #pragma unroll
@@ -466,19 +555,25 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
   };
   constexpr std::integral_constant<int, 0> kBuf0{};
   constexpr std::integral_constant<int, 1> kBuf1{};
-  constexpr std::true_type kFirst{};
-  constexpr std::false_type kLater{};
+  constexpr std::integral_constant<int, 0> kFirst{};
+  constexpr std::integral_constant<int, 1> kSecond{};
+  constexpr std::integral_constant<int, 2> kLater{};
   pass(0, kBuf0, kFirst);
-  int64_t i = 1;
+  if (ntile == 1) {
+    finish(0, kBuf0);
+    return;
+  }
+  pass(1, kBuf1, kSecond);
+  int64_t i = 2;
   for (; i + 1 < ntile; i += 2) {
-    pass(i, kBuf1, kLater);
-    pass(i + 1, kBuf0, kLater);
+    pass(i, kBuf0, kLater);
+    pass(i + 1, kBuf1, kLater);
   }
   if (i < ntile) {
-    pass(i, kBuf1, kLater);
-    finish(i, kBuf1);
+    pass(i, kBuf0, kLater);
+    finish(i, kBuf0);
   } else {
-    finish(i - 1, kBuf0);
+    finish(i - 1, kBuf1);
   }
 }
 
@@ -495,10 +590,12 @@ hipError_t launch_b(const tq_ctx* h, const void* keys, int64_t n, int64_t ldk, u
 
 }  // namespace
 
-bool quantize_mfma128_supported(const tq_ctx* h, const void* keys, int key_dtype, int64_t ldk) {
+bool quantize_mfma128_supported(const tq_ctx* h, const void* keys, int key_dtype, int64_t ldk,
+                                const void* codes, const void* signs, const void* norms, const void* rnorms) {
+  auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
   return h->d == 128 && key_dtype == TQ_BF16 && h->d_pi_frag && h->d_g_frag && h->symmetric && ldk >= 128 &&
-         (ldk % 8) == 0 && (reinterpret_cast<uintptr_t>(keys) & 15u) == 0 && h->code_bits >= 1 &&
-         h->code_bits <= 4;
+         (ldk % 8) == 0 && a16(keys) && a16(codes) && a16(signs) && a16(norms) && a16(rnorms) &&
+         h->code_bits >= 1 && h->code_bits <= 4;
 }
 
 hipError_t launch_quantize_mfma128(const tq_ctx* h, const void* keys, int64_t n, int64_t ldk, uint32_t* codes,

@@ -329,7 +329,7 @@ int tq_quantize(tq_handle h, const void* keys, int32_t key_dtype, int64_t n, int
   if (check_device(h) != TQ_OK) return TQ_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e =
-      (!tqdev::force_reference_kernels() && tqdev::quantize_mfma128_supported(h, keys, key_dtype, ldk))
+      (!tqdev::force_reference_kernels() && tqdev::quantize_mfma128_supported(h, keys, key_dtype, ldk, codes, signs, norms, rnorms))
           ? tqdev::launch_quantize_mfma128(h, keys, n, ldk, codes, signs, norms, rnorms, s)
           : tqdev::launch_quantize_v1(h, keys, key_dtype, n, ldk, codes, signs, norms, rnorms, s);
   return e == hipSuccess ? TQ_OK : TQ_EHIP;
