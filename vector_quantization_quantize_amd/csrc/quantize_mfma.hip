@@ -179,7 +179,7 @@ __global__ void __launch_bounds__(kQThreads, 2)
 quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ldk,
                         const uint4* __restrict__ pi_frag, const uint4* __restrict__ g_frag, HalfCodebook hc,
                         uint32_t* __restrict__ codes, uint32_t* __restrict__ signs, float* __restrict__ norms,
-                        float* __restrict__ rnorms, int64_t tiles) {
+                        float* __restrict__ rnorms, int64_t tiles, int64_t half, int64_t lead_tiles) {
   using Q = Quantizer<B>;
   // scaled float16 keys, double buffered: 32 rows of 128 halves, row stride
   // 272 bytes so that the 8 lanes of one LDS pass hit distinct banks
@@ -220,10 +220,16 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
   // depend on its own row only, so no zero fill (and no branch that would
   // split the pipelined loop body) is needed.
   const int sk = threadIdx.x >> 3, sc = threadIdx.x & 7;
-  const int64_t ntile = (tiles - blockIdx.x + gridDim.x - 1) / gridDim.x;  // >= 1
+  // This block's tiles: tstart, tstart + tstride, ... (ntile >= 1 of them).
+  // Blocks [0, half) walk the tiles [0, lead_tiles), the others the rest.
+  const int64_t bid = blockIdx.x;
+  const bool leads = bid < half;
+  const int64_t tstart = leads ? bid : lead_tiles + (bid - half);
+  const int64_t tstride = half;
+  const int64_t ntile = ((leads ? lead_tiles : tiles) - tstart + tstride - 1) / tstride;
   const uint4* const row_last = reinterpret_cast<const uint4*>(keys + (n - 1) * ldk) + 2 * sc;
-  const int64_t row_step = static_cast<int64_t>(gridDim.x) * 32 * ldk / 8;  // in uint4
-  const uint4* row_next = reinterpret_cast<const uint4*>(keys + (static_cast<int64_t>(blockIdx.x) * 32 + sk) * ldk) + 2 * sc;
+  const int64_t row_step = tstride * 32 * ldk / 8;  // in uint4
+  const uint4* row_next = reinterpret_cast<const uint4*>(keys + (tstart * 32 + sk) * ldk) + 2 * sc;
   auto fetch = [&](uint4& a, uint4& b) {
     const uint4* src = row_next < row_last ? row_next : row_last;
     a = src[0];
@@ -329,13 +335,13 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
   // destination of staged row r when tile c (global tile index) is the tile
   // of the code rows
   auto out_ptr = [&](int r, int64_t c) -> uint4* {
-    const int64_t pc = c - static_cast<int64_t>(gridDim.x);
+    const int64_t pc = c - tstride;
     if (r < kRowS) return codes4 + c * (32 * B) + r;
     if (r < kRowN) return signs4 + pc * 32 + (r - kRowS);
     if (r < kRowR) return norms4 + c * 8 + (r - kRowN);
     return rnorms4 + pc * 8 + (r - kRowR);
   };
-  const int ostep = (orow < kRowS ? 32 * B : orow < kRowN ? 32 : 8) * static_cast<int>(gridDim.x);
+  const int64_t ostep = (orow < kRowS ? 32 * B : orow < kRowN ? 32 : 8) * tstride;
   uint4* optr = nullptr;  // this lane's destination in the next copy-out (from the third pass on)
 
   // Lanes l and l ^ 32 hold the low and high 16 bits of a word; every lane
@@ -407,8 +413,8 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
         if (s == 0) {
           // the staged tile is this block's first: no previous tile
           lrow = orow < kRowS ? orow : orow < kRowN ? orow - kRowS : orow < kRowR ? orow : orow - 8;
-          odst = out_ptr(lrow, blockIdx.x);
-          optr = out_ptr(orow, static_cast<int64_t>(blockIdx.x) + gridDim.x);
+          odst = out_ptr(lrow, tstart);
+          optr = out_ptr(orow, tstart + tstride);
         }
       } else if constexpr (phase == 2) {
         if (s == 0) {
@@ -520,7 +526,7 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
   // rho, written directly (rows past the end go to key n - 1, same value).
   auto finish = [&](int64_t i, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
-    const int64_t c = blockIdx.x + i * gridDim.x;
+    const int64_t c = tstart + i * tstride;
     const int64_t left = n - c * 32;
     const int vk = left < 32 ? static_cast<int>(left) : 32;  // keys of tile c
     const uint4 v = ost[buf][orow];
@@ -577,14 +583,36 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
   }
 }
 
+// share of the tiles taken by the first-dispatched half of the grid, by B
+constexpr double kLeadShare[4] = {0.65, 0.65, 0.65, 0.65};
+
 template <int B>
 hipError_t launch_b(const tq_ctx* h, const void* keys, int64_t n, int64_t ldk, uint32_t* codes, uint32_t* signs,
                     float* norms, float* rnorms, hipStream_t stream) {
   const int64_t tiles = (n + 31) / 32;
-  const int64_t blocks = tiles < 512 ? tiles : 512;  // two resident blocks on each of 256 CUs
+  // Two blocks fit on a CU, and the grid is one resident wave of them.  The
+  // CU's wave arbiter favours older waves, so the block dispatched first to a
+  // CU (the grid's first half, one per CU) runs well ahead of its partner;
+  // with equal shares the partner finishes long after it, alone on the CU.
+  // The first half therefore takes a fixed larger share of the tiles (the
+  // front range), the second half the rest.  The split only moves work
+  // between blocks; any dispatch order gives the same results.
+  const int64_t slots = 2 * static_cast<int64_t>(h->cus);
+  int64_t blocks, half, lead;
+  if (tiles >= 4 * slots) {
+    blocks = slots;
+    half = slots / 2;
+    lead = static_cast<int64_t>(static_cast<double>(tiles) * kLeadShare[B - 1] + 0.5);
+    lead = lead < half ? half : lead > tiles - half ? tiles - half : lead;
+  } else {  // few tiles per block: equal shares, one sequence
+    blocks = tiles < slots ? tiles : slots;
+    half = blocks;
+    lead = tiles;
+  }
   hipLaunchKernelGGL(quantize_mfma128_kernel<B>, dim3(static_cast<uint32_t>(blocks)), dim3(kQThreads), 0, stream,
                      static_cast<const uint16_t*>(keys), n, ldk, reinterpret_cast<const uint4*>(h->d_pi_frag),
-                     reinterpret_cast<const uint4*>(h->d_g_frag), h->half, codes, signs, norms, rnorms, tiles);
+                     reinterpret_cast<const uint4*>(h->d_g_frag), h->half, codes, signs, norms, rnorms, tiles, half,
+                     lead);
   return hipGetLastError();
 }
 

@@ -146,6 +146,9 @@ int finish_init(tq_ctx* h) {
   h->levels = 1 << h->code_bits;
   h->words = (d + 31) / 32;
   if (hipGetDevice(&h->device) != hipSuccess) return TQ_EHIP;
+  if (hipDeviceGetAttribute(&h->cus, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess ||
+      h->cus <= 0)
+    return TQ_EHIP;
   for (int i = 0; i < tqdev::kMaxLevels; ++i) {
     h->cb.c[i] = i < h->levels ? h->centroids[i] : 0.0f;
     h->cb.t[i] = i + 1 < h->levels ? h->thresholds[i] : INFINITY;

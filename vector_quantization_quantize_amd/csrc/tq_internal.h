@@ -41,6 +41,7 @@ struct HalfCodebook {
 struct tq_ctx {
   int d = 0, bits = 0, code_bits = 0, levels = 0, words = 0;
   int device = -1;
+  int cus = 0;  // compute units of the device
   // host copies (float32), row-major d x d
   std::vector<float> pi, g, centroids, thresholds;
   // device tables
