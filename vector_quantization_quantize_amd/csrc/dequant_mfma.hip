@@ -114,7 +114,8 @@ __device__ __forceinline__ void load_a(const uint32_t* tab, const uint32_t (&wp)
 template <int B>
 __global__ void __launch_bounds__(kDqThreads, 2)
 dequant_mfma128_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ norms, int64_t n,
-                       const uint4* __restrict__ pi_frag, Codebook cb, float* __restrict__ khat, int64_t tiles) {
+                       const uint4* __restrict__ pi_frag, Codebook cb, float* __restrict__ khat, int64_t tiles,
+                       int64_t stride, int64_t bound1, int64_t bound2) {
   using L = Lookup<B>;
   __shared__ uint4 tab4[L::kEntries * L::kDwords / 4];
   __shared__ float4 nrow[4][8];  // per wave: the tile's 32 norms
@@ -141,10 +142,17 @@ dequant_mfma128_kernel(const uint32_t* __restrict__ codes, const float* __restri
     for (int p = 0; p < B; ++p) v[p] = *reinterpret_cast<const uint4*>(codes + (key * B + p) * 4);
     nv = norms[key];
   };
+  // This block's tiles: tier t = blockIdx.x / stride walks the range
+  // [bound_t, bound_t+1) (bound_0 = 0, bound_3 = tiles) from its offset
+  // blockIdx.x % stride, in steps of stride.
+  const int64_t bid = blockIdx.x;
+  const int64_t tier = bid / stride;
+  const int64_t tbeg = tier == 0 ? 0 : tier == 1 ? bound1 : bound2;
+  const int64_t tend = tier == 0 ? bound1 : tier == 1 ? bound2 : tiles;
   uint4 nxt[B];
   float nxt_n;
-  fetch(blockIdx.x, nxt, nxt_n);
-  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+  fetch(tbeg + bid % stride, nxt, nxt_n);
+  for (int64_t tile = tbeg + bid % stride; tile < tend; tile += stride) {
     uint32_t pl[B][4];
 #pragma unroll
     for (int p = 0; p < B; ++p) {
@@ -154,7 +162,7 @@ dequant_mfma128_kernel(const uint32_t* __restrict__ codes, const float* __restri
       pl[p][3] = nxt[p].w;
     }
     const float nk = nxt_n;
-    fetch(tile + gridDim.x, nxt, nxt_n);
+    fetch(tile + stride, nxt, nxt_n);
     f32x16 acc = {};
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
@@ -193,16 +201,42 @@ dequant_mfma128_kernel(const uint32_t* __restrict__ codes, const float* __restri
   }
 }
 
+// share of the tiles taken by each tier of the grid (dispatch order), by B
+constexpr double kTierShare[4][3] = {
+    {0.385, 0.33, 0.285}, {0.385, 0.33, 0.285}, {0.55, 0.45, 0.0}, {0.42, 0.33, 0.25}};
+
 template <int B>
 hipError_t launch_b(const tq_ctx* h, const uint32_t* codes, const float* norms, int64_t n, float* khat,
                     hipStream_t stream) {
   const int64_t tiles = (n + 31) / 32;
-  // one resident wave of blocks (3 per CU when registers and the table
-  // allow, else 2; 256 CUs); the tile loop is grid-strided
-  const int64_t resident = 256 * (B == 3 ? 2 : 3);
-  const int64_t blocks = tiles < resident ? tiles : resident;
+  // One resident wave of blocks: R per CU (3 when registers and the table
+  // allow, else 2).  The CU's wave arbiter favours older waves, so the
+  // blocks dispatched first (one per CU in each tier of the grid) run ahead
+  // of those dispatched after them; tier t of the grid takes a contiguous
+  // tile range sized by kTierShare, so that the tiers finish together.  The
+  // split only moves work between blocks; any dispatch order gives the same
+  // results.
+  constexpr int R = B == 3 ? 2 : 3;
+  const int64_t cus = h->cus;
+  int64_t blocks, stride, bound1, bound2;
+  if (tiles >= 4 * R * cus) {
+    blocks = R * cus;
+    stride = cus;
+    const double* sh = kTierShare[B - 1];
+    auto clamp = [](int64_t x, int64_t lo, int64_t hi) { return x < lo ? lo : x > hi ? hi : x; };
+    // every tier's range holds at least cus tiles: one or more per block
+    bound1 = clamp(static_cast<int64_t>(static_cast<double>(tiles) * sh[0] + 0.5), cus, tiles - (R - 1) * cus);
+    bound2 = R == 2 ? tiles
+                    : clamp(static_cast<int64_t>(static_cast<double>(tiles) * (sh[0] + sh[1]) + 0.5), bound1 + cus,
+                            tiles - cus);
+  } else {  // few tiles per block: equal shares, one tier
+    blocks = tiles < R * cus ? tiles : R * cus;
+    stride = blocks;
+    bound1 = bound2 = tiles;
+  }
   hipLaunchKernelGGL(dequant_mfma128_kernel<B>, dim3(static_cast<uint32_t>(blocks)), dim3(kDqThreads), 0, stream,
-                     codes, norms, n, reinterpret_cast<const uint4*>(h->d_dq_frag), h->cb, khat, tiles);
+                     codes, norms, n, reinterpret_cast<const uint4*>(h->d_dq_frag), h->cb, khat, tiles, stride,
+                     bound1, bound2);
   return hipGetLastError();
 }
 
