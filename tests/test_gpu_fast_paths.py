@@ -125,3 +125,34 @@ def test_reference_and_fast_kernels_both_match_oracle(env):
     finally:
         del os.environ["TQ_KERNELS"]
     check_full(env, w.d, w.bits, keys, queries, key_dtype="bf16")
+
+
+def test_logits_two_tier_key_split(env):
+    """32 groups x 4 queries x 32768 keys: the scorer's grid is two blocks per
+    CU on a 256-CU device, so every group's keys are cut unevenly between the
+    first- and second-dispatched halves of the grid (on other CU counts the
+    split is even; the results must not depend on it).  Random packed words
+    (every code and sign pattern); every score is checked against the
+    oracle's estimator on the same packed keys."""
+    torch, tqm, _ = env
+    from tests.test_gpu_parity import _params
+    from oracle import parity
+    d, bits, groups, nq, n = 128, 3, 32, 4, 32768
+    _announce(f"logits, uneven key split: groups={groups} nq={nq} n={n} bits={bits}")
+    pr = _params(d, bits)
+    h = tqm.tq_init(d, bits, 0)
+    rs = np.random.default_rng(4242)
+    total = groups * n
+    codes = rs.integers(0, 2 ** 32, size=(total, bits - 1, 4), dtype=np.uint64).astype(np.uint32)
+    signs = rs.integers(0, 2 ** 32, size=(total, 4), dtype=np.uint64).astype(np.uint32)
+    norms = rs.uniform(0.1, 10.0, size=total).astype(np.float32)
+    rnorms = rs.uniform(0.0, 0.5, size=total).astype(np.float32)
+    queries = rs.standard_normal((groups, nq, d))
+    s = _cpu(tqm.tq_logits(h, _dev(torch, queries.astype(np.float32)), _dev(torch, codes.view(np.int32)),
+                           _dev(torch, signs.view(np.int32)), _dev(torch, norms), _dev(torch, rnorms), n=n))
+    for g in range(groups):
+        sl = slice(g * n, (g + 1) * n)
+        ref = tq.scores(pr, queries[g], tq.unpack_codes(codes[sl], d), tq.unpack_bits(signs[sl], d),
+                        norms[sl].astype(np.float64), rnorms[sl].astype(np.float64))
+        bad, worst = parity.score_violations(s[g], ref, queries[g], norms[sl])
+        assert bad == 0, (g, worst)

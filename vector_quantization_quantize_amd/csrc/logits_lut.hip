@@ -118,6 +118,13 @@ struct Entry {
   half2_t q01, q23;
 };
 
+// How the keys of each (group, query quad) pair are cut into block ranges:
+// tier 0 (the grid's first chunks * pairs blocks) covers [0, split) in
+// chunks of k0 keys, tier 1 (the rest) covers [split, n) in chunks of k1.
+struct KeySplit {
+  int64_t pairs, chunks, split, k0, k1;
+};
+
 template <int tab>
 __device__ __forceinline__ Entry lut(const unsigned char* base, uint32_t addr) {
   // every entry address is a multiple of 8 bytes
@@ -144,7 +151,7 @@ logits_lut128_kernel(const float* __restrict__ queries, int quads, int64_t nq, i
                      const float* __restrict__ piT, const float* __restrict__ sT,  // 128 x 128, zero-padded
                      const uint32_t* __restrict__ codes, const uint32_t* __restrict__ signs,
                      const float* __restrict__ norms, const float* __restrict__ rnorms,
-                     float* __restrict__ scores, PlaneExpansion pe, float kappa, int64_t keys_per_block) {
+                     float* __restrict__ scores, PlaneExpansion pe, float kappa, KeySplit ks) {
   using TT = Terms<B>;
   constexpr int NT = TT::count;
   __shared__ __align__(16) unsigned char tabs[kTableBytes];
@@ -152,12 +159,22 @@ logits_lut128_kernel(const float* __restrict__ queries, int quads, int64_t nq, i
   __shared__ float vec[2][4][kDim];  // scaled v and w
   __shared__ float scale[2][4];
   const int tid = threadIdx.x;
-  const int64_t grp = blockIdx.y / quads;
-  const int64_t q0 = int64_t(blockIdx.y % quads) * 4;
-
+  // block -> (tier, chunk c, pair = group * quads + quad); tier 0 takes keys
+  // [c k0, (c + 1) k0) of [0, split), tier 1 keys [split + c k1, ...) of
+  // [split, n)
+  const int64_t L = blockIdx.x;
+  const int64_t tier = L / (ks.chunks * ks.pairs);
+  const int64_t lt = L - tier * ks.chunks * ks.pairs;
+  // chunk index fastest: a pair's chunks go to consecutive blocks, which the
+  // dispatcher deals out over the XCDs in turn
+  const int64_t pair = lt / ks.chunks, c = lt % ks.chunks;
+  const int64_t grp = pair / quads;
+  const int64_t q0 = (pair % quads) * 4;
   const int qc = int(nq - q0 < 4 ? nq - q0 : 4);
-  const int64_t kbeg = int64_t(blockIdx.x) * keys_per_block;
-  const int64_t kend = kbeg + keys_per_block < n ? kbeg + keys_per_block : n;
+  const int64_t kbeg = tier == 0 ? c * ks.k0 : ks.split + c * ks.k1;
+  const int64_t klim = tier == 0 ? ks.split : n;
+  const int64_t kend = kbeg + (tier == 0 ? ks.k0 : ks.k1) < klim ? kbeg + (tier == 0 ? ks.k0 : ks.k1) : klim;
+  if (kbeg >= kend) return;  // whole block: no keys in its range
   int64_t t = kbeg + tid;
 
   // ---- v = Pi q and w = S q (float32) ----
@@ -357,23 +374,44 @@ logits_lut128_kernel(const float* __restrict__ queries, int quads, int64_t nq, i
   }
 }
 
+// share of every pair's keys taken by the first-dispatched half of the grid
+constexpr double kFrontShare = 0.70;
+
 template <int B>
 hipError_t launch_b(const tq_ctx* h, const float* queries, int64_t groups, int64_t nq, const uint32_t* codes,
                     const uint32_t* signs, const float* norms, const float* rnorms, int64_t n, float* scores,
                     hipStream_t stream) {
   const int64_t quads = (nq + 3) / 4;
-  const int64_t ys = groups * quads;
-  if (ys > 65535) return hipErrorInvalidConfiguration;
-  // about two blocks per CU (256 CUs), whole multiples of the block size
-  int64_t chunks = (512 + ys - 1) / ys;
+  const int64_t pairs = groups * quads;
+  // About two blocks per CU, whole multiples of the block size per range.
+  const int64_t slots = 2 * static_cast<int64_t>(h->cus);
+  int64_t chunks = (slots + pairs - 1) / pairs;
   int64_t kpb = (n + chunks - 1) / chunks;
   kpb = (kpb + kLutThreads - 1) / kLutThreads * kLutThreads;
   if (kpb < kLutThreads) kpb = kLutThreads;
   chunks = (n + kpb - 1) / kpb;
+  KeySplit ks{pairs, chunks, n, kpb, kpb};
+  int64_t blocks = chunks * pairs;
+  // When the grid is exactly two blocks per CU, the first half is dispatched
+  // one block per CU ahead of the second, and the CU's wave arbiter favours
+  // the older waves: the first half then takes the larger share kFrontShare
+  // of every pair's keys.  Only the work split changes, never the results.
+  if (blocks == slots && chunks % 2 == 0 && n >= 4 * chunks * kLutThreads) {
+    // tier-0 chunks of k0 keys (a multiple of the block size), tier 1 the
+    // rest in equal whole-block chunks
+    const int64_t half = chunks / 2, unit = half * kLutThreads;
+    int64_t m = static_cast<int64_t>(static_cast<double>(n) * kFrontShare / static_cast<double>(unit) + 0.5);
+    const int64_t mmax = (n - unit) / unit;  // leaves tier 1 at least one block's keys per chunk
+    m = m < 1 ? 1 : m > mmax ? mmax : m;
+    const int64_t k0 = m * kLutThreads, split = m * unit;
+    const int64_t k1 = ((n - split + half - 1) / half + kLutThreads - 1) / kLutThreads * kLutThreads;
+    ks = KeySplit{pairs, half, split, k0, k1};
+  }
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const float kappa = 1.2533141373155002512f / float(h->d);
-  const dim3 grid(static_cast<uint32_t>(chunks), static_cast<uint32_t>(ys));
-  hipLaunchKernelGGL(logits_lut128_kernel<B>, grid, dim3(kLutThreads), 0, stream, queries, int(quads), nq, n,
-                     h->d, h->d_piT128, h->d_sT128, codes, signs, norms, rnorms, scores, h->planes, kappa, kpb);
+  hipLaunchKernelGGL(logits_lut128_kernel<B>, dim3(static_cast<uint32_t>(blocks)), dim3(kLutThreads), 0, stream,
+                     queries, int(quads), nq, n, h->d, h->d_piT128, h->d_sT128, codes, signs, norms, rnorms, scores,
+                     h->planes, kappa, ks);
   return hipGetLastError();
 }
 
