@@ -13,9 +13,10 @@
 // word b, which a table indexed by one byte of b evaluates 8 coordinates at a
 // time:  T_x[g][byte] = sum_{i<8} (bit i of byte ? +1 : -1) x[8 g + i].
 //
-// Each workgroup first computes v = Pi q and w = S q (S = G Pi, formed on the
-// host) of its 4 queries, reading the matrices straight from L2 (the first
-// keys are already loading), scales each vector by a power of two so that
+// One workgroup per CU takes a range of one (group, quad)'s keys.  It first
+// computes v = Pi q and w = S q (S = G Pi, formed on the host) of its 4
+// queries, reading the matrices straight from L2 (the first keys are already
+// loading), scales each vector by a power of two so that
 // its norm lies in [1, 2), and stores the tables as float16 (4 queries per
 // 8-byte entry):
 //   entry (byte x, table tab (0 = v, 1 = w), position g) at x*256 + tab*128 + g*8.
@@ -25,6 +26,8 @@
 // key bytes are.  One v_perm builds the byte address (key byte -> bits 8..15,
 // 8 g -> bits 0..7).  Lookups of one word (32 coordinates) are summed in
 // float16 pairs and then added into float32 accumulators with v_dot2_f32_f16.
+// Waves take the keys in batches of 64 from a counter in LDS, so that the
+// waves sharing a CU finish together whichever of them the arbiter favours.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -34,7 +37,6 @@
 namespace tqdev {
 namespace {
 
-constexpr int kLutThreads = 512;
 constexpr int kDim = 128;                 // padded vector length handled here
 constexpr int kTableBytes = 256 * 256;    // [x][tab][g] x 8 bytes = 64 KiB
 
@@ -118,13 +120,6 @@ struct Entry {
   half2_t q01, q23;
 };
 
-// How the keys of each (group, query quad) pair are cut into block ranges:
-// tier 0 (the grid's first chunks * pairs blocks) covers [0, split) in
-// chunks of k0 keys, tier 1 (the rest) covers [split, n) in chunks of k1.
-struct KeySplit {
-  int64_t pairs, chunks, split, k0, k1;
-};
-
 template <int tab>
 __device__ __forceinline__ Entry lut(const unsigned char* base, uint32_t addr) {
   // every entry address is a multiple of 8 bytes
@@ -145,48 +140,62 @@ __device__ __forceinline__ void pin(half2_t (&p)[N][2]) {
   for (int j = 0; j < N; ++j) asm volatile("" : "+v"(p[j][0]), "+v"(p[j][1])::"memory");
 }
 
+// Block size: 16 waves (one block per CU) while the key loop fits 128
+// registers, else 8.
 template <int B>
-__global__ void __launch_bounds__(kLutThreads, 2)
+struct Shape {
+  static constexpr int kThreads = B == 4 ? 512 : 1024;
+  static constexpr int kParts = kThreads / kDim;        // row slices of the query transform
+  static constexpr int kRows = kDim / kParts;           // rows per slice
+  static constexpr int kWalk = 256 * 2 * 16 * 4 / kThreads;  // table entries per thread
+};
+
+template <int B>
+__global__ void __launch_bounds__(Shape<B>::kThreads, 1)
 logits_lut128_kernel(const float* __restrict__ queries, int quads, int64_t nq, int64_t n, int d,
                      const float* __restrict__ piT, const float* __restrict__ sT,  // 128 x 128, zero-padded
                      const uint32_t* __restrict__ codes, const uint32_t* __restrict__ signs,
                      const float* __restrict__ norms, const float* __restrict__ rnorms,
-                     float* __restrict__ scores, PlaneExpansion pe, float kappa, KeySplit ks) {
+                     float* __restrict__ scores, PlaneExpansion pe, float kappa, int chunks,
+                     int64_t keys_per_block) {
   using TT = Terms<B>;
+  using SH = Shape<B>;
   constexpr int NT = TT::count;
+  constexpr int kThreads = SH::kThreads, kWaves = kThreads / 64;
   __shared__ __align__(16) unsigned char tabs[kTableBytes];
   __shared__ float4 qs[kDim];  // the 4 queries, coordinate-major
   __shared__ float vec[2][4][kDim];  // scaled v and w
   __shared__ float scale[2][4];
+  __shared__ uint32_t next_batch;
   const int tid = threadIdx.x;
-  // block -> (tier, chunk c, pair = group * quads + quad); tier 0 takes keys
-  // [c k0, (c + 1) k0) of [0, split), tier 1 keys [split + c k1, ...) of
-  // [split, n)
-  const int64_t L = blockIdx.x;
-  const int64_t tier = L / (ks.chunks * ks.pairs);
-  const int64_t lt = L - tier * ks.chunks * ks.pairs;
-  // chunk index fastest: a pair's chunks go to consecutive blocks, which the
-  // dispatcher deals out over the XCDs in turn
-  const int64_t pair = lt / ks.chunks, c = lt % ks.chunks;
+  const int64_t pair = blockIdx.x / chunks, c = blockIdx.x % chunks;
   const int64_t grp = pair / quads;
   const int64_t q0 = (pair % quads) * 4;
   const int qc = int(nq - q0 < 4 ? nq - q0 : 4);
-  const int64_t kbeg = tier == 0 ? c * ks.k0 : ks.split + c * ks.k1;
-  const int64_t klim = tier == 0 ? ks.split : n;
-  const int64_t kend = kbeg + (tier == 0 ? ks.k0 : ks.k1) < klim ? kbeg + (tier == 0 ? ks.k0 : ks.k1) : klim;
+  const int64_t kbeg = c * keys_per_block;
+  const int64_t kend = kbeg + keys_per_block < n ? kbeg + keys_per_block : n;
   if (kbeg >= kend) return;  // whole block: no keys in its range
-  int64_t t = kbeg + tid;
+  // keys go out in batches of 64 (one per lane); wave w starts on batch w
+  // and then takes the next unclaimed batch from a counter in LDS, so the
+  // waves of the CU finish together however its arbiter favours them
+  const int wave = tid >> 6, lane = tid & 63;
+  const int64_t nbatch = (kend - kbeg + 63) / 64;
+  // this lane's key of a batch, within the group; past the end: the last key
+  auto key_of = [&](int64_t batch) {
+    const int64_t k = kbeg + batch * 64 + lane;
+    return k < kend ? k : kend - 1;
+  };
 
   // ---- v = Pi q and w = S q (float32) ----
-  // Thread (part, j) sums i in [32 part, 32 part + 32) of output j for the 4
-  // queries and both matrices, in two batches of 16 loads per matrix; the
-  // first batch is in flight while the queries are staged.  The tables'
-  // space holds the partial sums [part][tab][q][j] until the four parts are
-  // added.
-  const int mj = tid & (kDim - 1), part = tid >> 7;
+  // Thread (part, j) sums rows i in [kRows part, kRows part + kRows) of
+  // output j for the 4 queries and both matrices, loading them in batches of
+  // 16 rows per matrix; the first batch is in flight while the queries are
+  // staged.  The tables' space holds the partial sums [part][tab][q][j]
+  // until the parts are added.
+  const int mj = tid & (kDim - 1), part = tid / kDim;
   // the matrices are zero-padded to 128 x 128: no bounds checks
-  const float* pcol = piT + 32 * part * kDim + mj;
-  const float* scol = sT + 32 * part * kDim + mj;
+  const float* pcol = piT + SH::kRows * part * kDim + mj;
+  const float* scol = sT + SH::kRows * part * kDim + mj;
   auto load_batch = [&](int i0, float (&pv)[16], float (&pw)[16]) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
@@ -195,27 +204,25 @@ logits_lut128_kernel(const float* __restrict__ queries, int quads, int64_t nq, i
     }
   };
   // Loads complete in issue order, so the order below lets each wait cover
-  // only what it needs: queries, the first matrix batch, the second batch,
-  // then the block's first keys (they arrive while the tables are built).
-  // thread tid loads coordinate tid % 128 of query tid / 128 (addresses
-  // clamped in range, values past d or nq zeroed): no branches
-  const int qi = tid & (kDim - 1), qq = tid >> 7;
+  // only what it needs: queries, the first matrix batch, then the wave's
+  // first keys (they arrive while the tables are built).  Threads below 512
+  // load coordinate tid % 128 of query tid / 128 (addresses clamped in
+  // range, values past d or nq zeroed).
+  const int qi = tid & (kDim - 1), qq = (tid >> 7) & 3;
   const bool qok = q0 + qq < nq && qi < d;
   const float qraw = queries[(grp * nq + (q0 + qq < nq ? q0 + qq : nq - 1)) * d + (qi < d ? qi : d - 1)];
   float pv0[16], pw0[16];
   load_batch(0, pv0, pw0);
-  reinterpret_cast<float*>(qs)[qi * 4 + qq] = qok ? qraw : 0.0f;
+  if (tid < 4 * kDim) reinterpret_cast<float*>(qs)[qi * 4 + qq] = qok ? qraw : 0.0f;
+  if (tid == 0) next_batch = kWaves;
   __syncthreads();
-  Packed<B> cur;
+  Packed<B> cur = load_key<B>(codes, signs, norms, rnorms, grp * n + key_of(wave));
   {
-    float pv1[16], pw1[16];
-    load_batch(16, pv1, pw1);
-    cur = load_key<B>(codes, signs, norms, rnorms, grp * n + (t < kend ? t : kend - 1));
     float av[4] = {0.0f, 0.0f, 0.0f, 0.0f}, aw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     auto accumulate = [&](int i0, const float (&pv)[16], const float (&pw)[16]) {
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
-        const float4 x = qs[32 * part + i0 + k];
+        const float4 x = qs[SH::kRows * part + i0 + k];
         av[0] = fmaf(pv[k], x.x, av[0]);
         av[1] = fmaf(pv[k], x.y, av[1]);
         av[2] = fmaf(pv[k], x.z, av[2]);
@@ -227,25 +234,31 @@ logits_lut128_kernel(const float* __restrict__ queries, int quads, int64_t nq, i
       }
     };
     accumulate(0, pv0, pw0);
-    accumulate(16, pv1, pw1);
-    const int j = mj;
+    if constexpr (SH::kRows > 16) {
+      float pv1[16], pw1[16];
+      load_batch(16, pv1, pw1);
+      accumulate(16, pv1, pw1);
+    }
     float* red = reinterpret_cast<float*>(tabs);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      red[((part * 2 + 0) * 4 + q) * kDim + j] = av[q];
-      red[((part * 2 + 1) * 4 + q) * kDim + j] = aw[q];
+      red[((part * 2 + 0) * 4 + q) * kDim + mj] = av[q];
+      red[((part * 2 + 1) * 4 + q) * kDim + mj] = aw[q];
     }
   }
   __syncthreads();
-  for (int e = tid; e < 2 * 4 * kDim; e += kLutThreads) {  // e = (tab * 4 + q) * kDim + j
+  for (int e = tid; e < 2 * 4 * kDim; e += kThreads) {  // e = (tab * 4 + q) * kDim + j
     const float* red = reinterpret_cast<const float*>(tabs);
-    vec[e >> 9][(e >> 7) & 3][e & (kDim - 1)] = (red[e] + red[1024 + e]) + (red[2048 + e] + red[3072 + e]);
+    float sum = 0.0f;
+#pragma unroll
+    for (int pp = 0; pp < SH::kParts; ++pp) sum += red[pp * 1024 + e];
+    vec[e >> 9][(e >> 7) & 3][e & (kDim - 1)] = sum;
   }
   __syncthreads();
   // power-of-two scale per (table, query): scaled norm in [1, 2); wave w < 8
   // reduces vector (w >> 2, w & 3)
   if (tid < 8 * 64) {
-    const int wv = tid >> 6, lane = tid & 63, tab = wv >> 2, q = wv & 3;
+    const int tab = wave >> 2, q = wave & 3;
     const float x0 = vec[tab][q][lane], x1 = vec[tab][q][lane + 64];
     float ss = fmaf(x0, x0, x1 * x1);
 #pragma unroll
@@ -258,35 +271,37 @@ logits_lut128_kernel(const float* __restrict__ queries, int quads, int64_t nq, i
   }
   __syncthreads();
   // Byte tables (tab 0 = v, 1 = w) by Gray-code walks: thread (tab, seg,
-  // position g, query q) = tid bits (8, 7..6, 5..2, 1..0) visits the 64
-  // bytes x = rank ^ (rank >> 1), rank in [64 seg, 64 seg + 64).  Successive
-  // bytes differ in one bit b, so each entry is the previous one plus or
-  // minus twice coordinate 8 g + b; a wave writes 128 contiguous bytes per
-  // step.  The running float32 sum drifts by well under the float16
-  // rounding of the stored entry.
+  // position g, query q) = tid bits (top, middle, 5..2, 1..0) visits the kWalk
+  // bytes x = rank ^ (rank >> 1), rank in [kWalk seg, kWalk seg + kWalk).
+  // Successive bytes differ in one bit b, so each entry is the previous one
+  // plus or minus twice coordinate 8 g + b; a wave writes 128 contiguous
+  // bytes per step.  The running float32 sum drifts by well under the
+  // float16 rounding of the stored entry.
   {
-    const int q = tid & 3, gg = (tid >> 2) & 15, seg = (tid >> 6) & 3, tab = tid >> 8;
+    constexpr int kW = SH::kWalk, kSegs = 256 / kW, kHi = kW / 2;
+    const int q = tid & 3, gg = (tid >> 2) & 15, seg = (tid >> 6) & (kSegs - 1), tab = tid / (64 * kSegs);
     const float sc = scale[tab][q];
     float xs[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) xs[i] = sc * vec[tab][q][8 * gg + i];
     unsigned char* col = tabs + tab * 128 + gg * 8 + q * 2;
-    // x(rank0 + m) = gb ^ gray(m) with gb = gray(64 seg) a multiple of 32:
-    // only bit 5 of gray(m) interacts with gb, so two bases and a
+    // x(rank0 + m) = gb ^ gray(m) with gb = gray(kW seg) a multiple of kW / 2:
+    // only bit kW / 2 of gray(m) interacts with gb, so two bases and a
     // compile-time offset address every entry
-    const int rank0 = 64 * seg, gb = rank0 ^ (rank0 >> 1);
+    const int rank0 = kW * seg, gb = rank0 ^ (rank0 >> 1);
     unsigned char* base0 = col + 256 * gb;
-    unsigned char* base1 = col + 256 * (gb ^ 32);
+    unsigned char* base1 = col + 256 * (gb ^ kHi);
     float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc += ((gb >> i) & 1) ? xs[i] : -xs[i];
     *reinterpret_cast<_Float16*>(base0) = static_cast<_Float16>(acc);
 #pragma unroll
-    for (int m = 1; m < 64; ++m) {
+    for (int m = 1; m < kW; ++m) {
       const int gm = m ^ (m >> 1), b = __builtin_ctz(m);
-      const bool up = b == 5 ? (((gb ^ gm) >> 5) & 1) != 0 : ((gm >> b) & 1) != 0;
+      const bool up = (1 << b) == kHi ? (((gb ^ gm) >> b) & 1) != 0 : ((gm >> b) & 1) != 0;
       acc += up ? 2.0f * xs[b] : -2.0f * xs[b];
-      *reinterpret_cast<_Float16*>(((gm & 32) ? base1 : base0) + 256 * (gm & 31)) = static_cast<_Float16>(acc);
+      *reinterpret_cast<_Float16*>(((gm & kHi) ? base1 : base0) + 256 * (gm & (kHi - 1))) =
+          static_cast<_Float16>(acc);
     }
   }
   __syncthreads();
@@ -306,11 +321,18 @@ logits_lut128_kernel(const float* __restrict__ queries, int quads, int64_t nq, i
   }
   const half2_t pick_lo = {(_Float16)1.0f, (_Float16)0.0f};
   const half2_t pick_hi = {(_Float16)0.0f, (_Float16)1.0f};
+  // claims: one LDS add per batch, made a batch ahead of the load it feeds
+  auto claim = [&]() -> int64_t {
+    uint32_t v = 0;
+    if (lane == 0) v = atomicAdd(&next_batch, 1u);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
 
-  for (; t < kend; t += kLutThreads) {
-    // next keys, clamped into the block's range (a load past it is unused)
-    const int64_t tn = t + kLutThreads < kend ? t + kLutThreads : kend - 1;
-    const Packed<B> nxt = load_key<B>(codes, signs, norms, rnorms, grp * n + tn);
+  int64_t b = wave;         // batch being scored
+  int64_t bn = claim();     // the one after it
+  while (b < nbatch) {
+    const int64_t bnn = claim();
+    const Packed<B> nxt = load_key<B>(codes, signs, norms, rnorms, grp * n + key_of(bn));  // unused past the end
     Words pl[B];
 #pragma unroll
     for (int p = 0; p < B; ++p) pl[p] = rotate(cur.plane[p], w1, w2, bs);
@@ -361,6 +383,9 @@ logits_lut128_kernel(const float* __restrict__ queries, int quads, int64_t nq, i
         acc[j][3] = __builtin_amdgcn_fdot2(part[j][1], pick_hi, acc[j][3], false);
       }
     }
+    // lanes past the end scored key kend - 1 again and store the same value
+    // there: no branch around the stores
+    const int64_t key = key_of(b);
     const float corr = cur.rho;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -368,14 +393,13 @@ logits_lut128_kernel(const float* __restrict__ queries, int quads, int64_t nq, i
 #pragma unroll
       for (int j = 0; j < NT; ++j) s1 = fmaf(pe.alpha[j], acc[j][q], s1);
       const float sw = acc[NT][q] * inv_w[q];
-      if (q < qc) scores[(grp * nq + q0 + q) * n + t] = cur.n * fmaf(corr, sw, s1 * inv_v[q]);
+      if (q < qc) scores[(grp * nq + q0 + q) * n + key] = cur.n * fmaf(corr, sw, s1 * inv_v[q]);
     }
     cur = nxt;
+    b = bn;
+    bn = bnn;
   }
 }
-
-// share of every pair's keys taken by the first-dispatched half of the grid
-constexpr double kFrontShare = 0.70;
 
 template <int B>
 hipError_t launch_b(const tq_ctx* h, const float* queries, int64_t groups, int64_t nq, const uint32_t* codes,
@@ -383,35 +407,19 @@ hipError_t launch_b(const tq_ctx* h, const float* queries, int64_t groups, int64
                     hipStream_t stream) {
   const int64_t quads = (nq + 3) / 4;
   const int64_t pairs = groups * quads;
-  // About two blocks per CU, whole multiples of the block size per range.
-  const int64_t slots = 2 * static_cast<int64_t>(h->cus);
-  int64_t chunks = (slots + pairs - 1) / pairs;
+  // about one block per CU, each on one (group, query quad) pair's range of
+  // keys (a multiple of 64)
+  const int64_t cus = h->cus;
+  int64_t chunks = (cus + pairs - 1) / pairs;
   int64_t kpb = (n + chunks - 1) / chunks;
-  kpb = (kpb + kLutThreads - 1) / kLutThreads * kLutThreads;
-  if (kpb < kLutThreads) kpb = kLutThreads;
+  kpb = (kpb + 63) / 64 * 64;
   chunks = (n + kpb - 1) / kpb;
-  KeySplit ks{pairs, chunks, n, kpb, kpb};
-  int64_t blocks = chunks * pairs;
-  // When the grid is exactly two blocks per CU, the first half is dispatched
-  // one block per CU ahead of the second, and the CU's wave arbiter favours
-  // the older waves: the first half then takes the larger share kFrontShare
-  // of every pair's keys.  Only the work split changes, never the results.
-  if (blocks == slots && chunks % 2 == 0 && n >= 4 * chunks * kLutThreads) {
-    // tier-0 chunks of k0 keys (a multiple of the block size), tier 1 the
-    // rest in equal whole-block chunks
-    const int64_t half = chunks / 2, unit = half * kLutThreads;
-    int64_t m = static_cast<int64_t>(static_cast<double>(n) * kFrontShare / static_cast<double>(unit) + 0.5);
-    const int64_t mmax = (n - unit) / unit;  // leaves tier 1 at least one block's keys per chunk
-    m = m < 1 ? 1 : m > mmax ? mmax : m;
-    const int64_t k0 = m * kLutThreads, split = m * unit;
-    const int64_t k1 = ((n - split + half - 1) / half + kLutThreads - 1) / kLutThreads * kLutThreads;
-    ks = KeySplit{pairs, half, split, k0, k1};
-  }
-  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const int64_t blocks = chunks * pairs;
+  if (blocks > 0x7FFFFFFF || chunks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const float kappa = 1.2533141373155002512f / float(h->d);
-  hipLaunchKernelGGL(logits_lut128_kernel<B>, dim3(static_cast<uint32_t>(blocks)), dim3(kLutThreads), 0, stream,
-                     queries, int(quads), nq, n, h->d, h->d_piT128, h->d_sT128, codes, signs, norms, rnorms, scores,
-                     h->planes, kappa, ks);
+  hipLaunchKernelGGL(logits_lut128_kernel<B>, dim3(static_cast<uint32_t>(blocks)), dim3(Shape<B>::kThreads), 0,
+                     stream, queries, int(quads), nq, n, h->d, h->d_piT128, h->d_sT128, codes, signs, norms,
+                     rnorms, scores, h->planes, kappa, static_cast<int>(chunks), kpb);
   return hipGetLastError();
 }
 
