@@ -13,6 +13,13 @@
 // lookup (B = 3 uses E = 4, a 4096-entry table), so a step of 8 coordinates
 // takes 8 / E lookups.
 //
+// Two-pass form: when the level set has at most two magnitudes (B <= 2 and
+// symmetric), the host finds a scale sigma that makes every sigma c[level] a
+// float16 number to within 2^-19 relative.  The table then holds one piece
+// per value, the products are exact, and k_hat = n (sigma 2^12)^-1
+// (sigma c)(Pi_hi + Pi_lo) takes two passes; at the board power limit the
+// matrix work is a large part of the kernel's energy.
+//
 // Work split: wave w of a 4-wave block owns output coordinates [32w, 32w+32)
 // and walks tiles of 32 keys (one 32 x 32 x 16 MFMA tile: M = keys,
 // N = coordinates, K = 128 input coordinates in 8 steps).  Lane l supplies,
@@ -44,20 +51,20 @@ constexpr int kSteps = 8;
 constexpr float kOutScale = 1.0f / (4096.0f * 4096.0f);  // undoes 2^12 on c and on Pi
 
 // coordinates per table lookup and table geometry
-template <int B>
+template <int B, bool kTwo>
 struct Lookup {
   static constexpr int E = B == 3 ? 4 : 8 / B;
   static constexpr int K = 8 / E;                  // lookups per step
   static constexpr int kEntries = 1 << (E * B);
-  static constexpr int kDwords = E;                // E hi halves + E lo halves
+  static constexpr int kDwords = kTwo ? E / 2 : E;  // E values, or E hi halves + E lo halves
 };
 
 // Entry layout: dwords [0, E/2) hold the hi halves of coordinates 0..E-1,
-// dwords [E/2, E) the lo halves.  Index bit p E + e is bit p of the level
-// index of coordinate e.
-template <int B>
-__device__ void build_table(uint32_t* tab, const Codebook& cb) {
-  using L = Lookup<B>;
+// dwords [E/2, E) the lo halves (three-pass form only).  Index bit p E + e is
+// bit p of the level index of coordinate e.
+template <int B, bool kTwo>
+__device__ void build_table(uint32_t* tab, const Codebook& cb, const DequantTable& dqt) {
+  using L = Lookup<B, kTwo>;
   for (int idx = threadIdx.x; idx < L::kEntries; idx += kDqThreads) {
     _Float16 hv[L::E], lv[L::E];
 #pragma unroll
@@ -65,34 +72,50 @@ __device__ void build_table(uint32_t* tab, const Codebook& cb) {
       int level = 0;
 #pragma unroll
       for (int p = 0; p < B; ++p) level |= ((idx >> (p * L::E + e)) & 1) << p;
-      const float x = cb.c[level] * 4096.0f;  // exact
-      hv[e] = static_cast<_Float16>(x);
-      lv[e] = static_cast<_Float16>(x - static_cast<float>(hv[e]));
+      if constexpr (kTwo) {
+        hv[e] = static_cast<_Float16>(dqt.v[level]);  // exact
+        lv[e] = static_cast<_Float16>(0.0f);
+      } else {
+        const float x = cb.c[level] * 4096.0f;  // exact
+        hv[e] = static_cast<_Float16>(x);
+        lv[e] = static_cast<_Float16>(x - static_cast<float>(hv[e]));
+      }
     }
 #pragma unroll
     for (int k = 0; k < L::E / 2; ++k) {
       tab[idx * L::kDwords + k] =
           __builtin_bit_cast(uint16_t, hv[2 * k]) | (uint32_t(__builtin_bit_cast(uint16_t, hv[2 * k + 1])) << 16);
-      tab[idx * L::kDwords + L::E / 2 + k] =
-          __builtin_bit_cast(uint16_t, lv[2 * k]) | (uint32_t(__builtin_bit_cast(uint16_t, lv[2 * k + 1])) << 16);
+      if constexpr (!kTwo)
+        tab[idx * L::kDwords + L::E / 2 + k] =
+            __builtin_bit_cast(uint16_t, lv[2 * k]) | (uint32_t(__builtin_bit_cast(uint16_t, lv[2 * k + 1])) << 16);
     }
   }
 }
 
-// A operands (hi and lo pieces) of step s for this lane, from the plane
-// words holding the step's coordinates
-template <int B>
+// A operands (hi and lo pieces; hi only in the two-pass form) of step s for
+// this lane, from the plane words holding the step's coordinates
+template <int B, bool kTwo>
 __device__ __forceinline__ void load_a(const uint32_t* tab, const uint32_t (&wp)[B], int shift, f16x8& ahi,
                                        f16x8& alo) {
-  using L = Lookup<B>;
-  uint32_t hi[4], lo[4];
+  using L = Lookup<B, kTwo>;
+  uint32_t hi[4], lo[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int k = 0; k < L::K; ++k) {
     uint32_t idx = 0;
 #pragma unroll
     for (int p = 0; p < B; ++p) idx |= __builtin_amdgcn_ubfe(wp[p], shift + k * L::E, L::E) << (p * L::E);
     const uint32_t* ent = tab + idx * L::kDwords;
-    if constexpr (L::E == 8) {
+    if constexpr (kTwo) {
+      if constexpr (L::E == 8) {
+        const uint4 h = *reinterpret_cast<const uint4*>(ent);
+        hi[0] = h.x; hi[1] = h.y; hi[2] = h.z; hi[3] = h.w;
+      } else if constexpr (L::E == 4) {
+        const uint2 h = *reinterpret_cast<const uint2*>(ent);
+        hi[2 * k] = h.x; hi[2 * k + 1] = h.y;
+      } else {
+        hi[k] = ent[0];
+      }
+    } else if constexpr (L::E == 8) {
       const uint4 h = reinterpret_cast<const uint4*>(ent)[0];
       const uint4 l = reinterpret_cast<const uint4*>(ent)[1];
       hi[0] = h.x; hi[1] = h.y; hi[2] = h.z; hi[3] = h.w;
@@ -111,16 +134,17 @@ __device__ __forceinline__ void load_a(const uint32_t* tab, const uint32_t (&wp)
   alo = __builtin_bit_cast(f16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
 }
 
-template <int B>
+template <int B, bool kTwo>
 __global__ void __launch_bounds__(kDqThreads, 2)
 dequant_mfma128_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ norms, int64_t n,
-                       const uint4* __restrict__ pi_frag, Codebook cb, float* __restrict__ khat, int64_t tiles,
-                       int64_t stride, int64_t bound1, int64_t bound2) {
-  using L = Lookup<B>;
+                       const uint4* __restrict__ pi_frag, Codebook cb, DequantTable dqt, float* __restrict__ khat,
+                       int64_t tiles, int64_t stride, int64_t bound1, int64_t bound2) {
+  using L = Lookup<B, kTwo>;
   __shared__ uint4 tab4[L::kEntries * L::kDwords / 4];
   __shared__ float4 nrow[4][8];  // per wave: the tile's 32 norms
   uint32_t* tab = reinterpret_cast<uint32_t*>(tab4);
-  build_table<B>(tab, cb);
+  build_table<B, kTwo>(tab, cb, dqt);
+  const float out_scale = kTwo ? dqt.out_scale : kOutScale;
   __syncthreads();
 
   const int w = threadIdx.x >> 6;
@@ -170,13 +194,13 @@ dequant_mfma128_kernel(const uint32_t* __restrict__ codes, const float* __restri
 #pragma unroll
       for (int p = 0; p < B; ++p) wp[p] = pl[p][s >> 1];
       f16x8 ahi, alo;
-      load_a<B>(tab, wp, 8 * (2 * (s & 1) + g), ahi, alo);
+      load_a<B, kTwo>(tab, wp, 8 * (2 * (s & 1) + g), ahi, alo);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, bpi[s][0], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, bpi[s][1], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, bpi[s][0], acc, 0, 0, 0);
+      if constexpr (!kTwo) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, bpi[s][0], acc, 0, 0, 0);
     }
     // lane holds coordinate 32w + kl of keys 8(r/4) + 4g + r%4
-    reinterpret_cast<float*>(nrow[w])[kl] = nk * kOutScale;  // both lane groups hold key kl
+    reinterpret_cast<float*>(nrow[w])[kl] = nk * out_scale;  // both lane groups hold key kl
     float o[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -205,7 +229,7 @@ dequant_mfma128_kernel(const uint32_t* __restrict__ codes, const float* __restri
 constexpr double kTierShare[4][3] = {
     {0.385, 0.33, 0.285}, {0.385, 0.33, 0.285}, {0.55, 0.45, 0.0}, {0.42, 0.33, 0.25}};
 
-template <int B>
+template <int B, bool kTwo>
 hipError_t launch_b(const tq_ctx* h, const uint32_t* codes, const float* norms, int64_t n, float* khat,
                     hipStream_t stream) {
   const int64_t tiles = (n + 31) / 32;
@@ -234,9 +258,10 @@ hipError_t launch_b(const tq_ctx* h, const uint32_t* codes, const float* norms, 
     stride = blocks;
     bound1 = bound2 = tiles;
   }
-  hipLaunchKernelGGL(dequant_mfma128_kernel<B>, dim3(static_cast<uint32_t>(blocks)), dim3(kDqThreads), 0, stream,
-                     codes, norms, n, reinterpret_cast<const uint4*>(h->d_dq_frag), h->cb, khat, tiles, stride,
-                     bound1, bound2);
+  const auto kernel = dequant_mfma128_kernel<B, kTwo>;
+  hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kDqThreads), 0, stream, codes, norms, n,
+                     reinterpret_cast<const uint4*>(h->d_dq_frag), h->cb, h->dqt, khat, tiles, stride, bound1,
+                     bound2);
   return hipGetLastError();
 }
 
@@ -248,11 +273,16 @@ bool dequant_mfma128_supported(const tq_ctx* h) {
 
 hipError_t launch_dequant_mfma128(const tq_ctx* h, const uint32_t* codes, const float* norms, int64_t n,
                                   float* khat, hipStream_t stream) {
+  const bool two = h->dqt.two_pass != 0;
   switch (h->code_bits) {
-    case 1: return launch_b<1>(h, codes, norms, n, khat, stream);
-    case 2: return launch_b<2>(h, codes, norms, n, khat, stream);
-    case 3: return launch_b<3>(h, codes, norms, n, khat, stream);
-    case 4: return launch_b<4>(h, codes, norms, n, khat, stream);
+    case 1:
+      return two ? launch_b<1, true>(h, codes, norms, n, khat, stream)
+                 : launch_b<1, false>(h, codes, norms, n, khat, stream);
+    case 2:
+      return two ? launch_b<2, true>(h, codes, norms, n, khat, stream)
+                 : launch_b<2, false>(h, codes, norms, n, khat, stream);
+    case 3: return launch_b<3, false>(h, codes, norms, n, khat, stream);
+    case 4: return launch_b<4, false>(h, codes, norms, n, khat, stream);
     default: return hipErrorInvalidValue;
   }
 }

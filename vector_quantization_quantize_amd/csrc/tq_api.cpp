@@ -2,6 +2,7 @@
 // HIP kernels.  See include/tq.h for the contract of every entry point.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -140,6 +141,40 @@ void plane_expansion(const std::vector<float>& c, int code_bits, tqdev::PlaneExp
   }
 }
 
+// Scale sigma for the two-pass reconstruction table (tqdev::DequantTable):
+// with magnitudes m1 > m0 > 0, sigma = S / m1 for the integer S in
+// [1024, 2048) whose sigma m0 lies closest, relatively, to a float16 number
+// (sigma m1 = S is one exactly); a single magnitude takes sigma = 1024 / m1.
+// More than two magnitudes, or no S within 2^-19: three-pass form.
+void dequant_table(const std::vector<float>& c, tqdev::DequantTable* out) {
+  out->two_pass = 0;
+  std::vector<double> mags;
+  for (float x : c) {
+    const double m = std::fabs(double(x));
+    if (m > 0.0 && std::find(mags.begin(), mags.end(), m) == mags.end()) mags.push_back(m);
+  }
+  if (mags.empty() || mags.size() > 2) return;
+  std::sort(mags.begin(), mags.end());
+  const double m1 = mags.back();
+  double sigma = 1024.0 / m1, best = 0.0;
+  if (mags.size() == 2) {
+    best = 1.0;
+    for (int s = 1024; s < 2048; ++s) {
+      const double v = double(s) / m1 * mags[0];
+      const double err = std::fabs(double(f16_value(f16_bits(float(v)))) - v) / v;
+      if (err < best) {
+        best = err;
+        sigma = double(s) / m1;
+      }
+    }
+  }
+  if (best > std::ldexp(1.0, -19)) return;
+  for (size_t i = 0; i < c.size() && i < size_t(tqdev::kMaxLevels); ++i)
+    out->v[i] = f16_value(f16_bits(float(sigma * double(c[i]))));
+  out->out_scale = float(1.0 / (sigma * 4096.0));
+  out->two_pass = 1;
+}
+
 int finish_init(tq_ctx* h) {
   const int d = h->d;
   h->code_bits = h->bits - 1;
@@ -155,6 +190,7 @@ int finish_init(tq_ctx* h) {
   }
   h->cb.levels = h->levels;
   plane_expansion(h->centroids, h->code_bits, &h->planes);
+  dequant_table(h->centroids, &h->dqt);
   {
     const int L = h->levels, M = L / 2;
     bool sym = h->thresholds[M - 1] == 0.0f;

@@ -36,6 +36,17 @@ struct HalfCodebook {
   float m[kMaxLevels / 2];  // m[j] = 2^12 c[M + j],  j < M
 };
 
+// Level values the reconstruction's lookup table holds.  When the level set
+// has at most two distinct magnitudes, a scale sigma (found at init) makes
+// sigma c[level] a float16 number for every level, to within 2^-19 relative:
+// one float16 piece per value is then enough and k_hat takes two matrix-core
+// passes instead of three.
+struct DequantTable {
+  float v[kMaxLevels];  // sigma c[level], exactly representable in float16
+  float out_scale;      // 1 / (sigma 2^12)
+  int two_pass;         // 1 when v is in use
+};
+
 }  // namespace tqdev
 
 struct tq_ctx {
@@ -59,6 +70,7 @@ struct tq_ctx {
   tqdev::PlaneExpansion planes{};
   bool symmetric = false;  // level set exactly symmetric in float32
   tqdev::HalfCodebook half{};
+  tqdev::DequantTable dqt{};
 };
 
 namespace tqdev {
