@@ -222,7 +222,9 @@ def main():
     # writes 512 B per key and is bound by HBM writes
     bound = {"tq_quantize": ("mfma", BF16_MFMA_PEAK_TFLOPS), "tq_logits": ("hbm", HBM_PEAK_GBS),
              "tq_dequant_mse": ("hbm", HBM_PEAK_GBS)}
-    raw_passes = {"tq_quantize": 10 * w.d * w.d, "tq_dequant_mse": 6 * w.d * w.d}
+    # reconstruction: 2 passes when the level set has at most two magnitudes
+    # (B <= 2 at d = 128), else 3
+    raw_passes = {"tq_quantize": 10 * w.d * w.d, "tq_dequant_mse": (4 if w.bits <= 3 else 6) * w.d * w.d}
     for n, f in raw_passes.items():
         kern[n]["raw_mfma_TFLOPs"] = round(f * total / (per[n] * 1e-3) / 1e12, 2)
 
