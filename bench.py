@@ -74,14 +74,15 @@ def kernel_models(w):
     }
 
 
-def measured_traffic(workload):
-    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    summary, for every kernel whose source is unchanged since it was taken."""
+def measured_profile(workload):
+    """From the committed rocprofv3 summary, for every kernel whose source is
+    unchanged since it was taken: HBM bytes per launch (FETCH_SIZE and
+    WRITE_SIZE, calibrated) and the matrix cores' busy share of its cycles."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
-    out = {}
+    traffic, mfma_busy = {}, {}
     if not os.path.exists(path):
-        return out
+        return traffic, mfma_busy
     for line in open(path):
         if line.startswith("#") or not line.strip():
             continue
@@ -89,8 +90,10 @@ def measured_traffic(workload):
         entry = line.split()[0]
         src = os.path.join(ROOT, fields["source"])
         if os.path.exists(src) and hashlib.sha1(open(src, "rb").read()).hexdigest() == fields["sha1"]:
-            out[entry] = int(float(fields["fetch_bytes"]) + float(fields["write_bytes"]))
-    return out
+            traffic[entry] = int(float(fields["fetch_bytes"]) + float(fields["write_bytes"]))
+            if "mfma_busy_pct" in fields:
+                mfma_busy[entry] = float(fields["mfma_busy_pct"])
+    return traffic, mfma_busy
 
 
 def cpu_baseline(w, keys_np, queries_np, groups, seed):
@@ -237,9 +240,10 @@ def main():
             ach_cold = round(models[n]["flops"] * total / (cold[n] * 1e-3) / 1e12, 2)
         return {"kernel": n, "bound": kind, "achieved": ach, "peak": peak, "unit": unit,
                 "frac": round(ach / peak, 4), "traffic": traffic.get(n),
-                "achieved_cold": ach_cold, "frac_cold": round(ach_cold / peak, 4)}
+                "achieved_cold": ach_cold, "frac_cold": round(ach_cold / peak, 4),
+                "mfma_busy_pct": mfma_busy.get(n)}
 
-    traffic = measured_traffic(args.workload)
+    traffic, mfma_busy = measured_profile(args.workload)
     dominant = max(names, key=lambda n: per[n])
     line = {
         "metric": METRIC,
