@@ -21,6 +21,13 @@ parity):
 * scores: |s_gpu - s| <= 1e-3 ||q|| n_k per score.
 * stage-1 reconstruction: ||k_hat_gpu - k_hat|| <= 1e-5 ||k_hat|| per key.
 * padding bits past d are zero.
+* top-k per query: the k indices are distinct and in range, and the scores
+  come best first (ties in ascending index).  Each returned score is within
+  the score tolerance of the oracle's score for that key.  The set may
+  differ from the oracle's only near the k-th score: a returned key's oracle
+  score is at least the oracle's k-th score minus twice the row's largest
+  score tolerance, and every key whose oracle score exceeds the k-th by more
+  than that is returned.
 """
 from dataclasses import dataclass, field
 
@@ -130,3 +137,47 @@ def dequant_violations(k_gpu, k_ref):
     bad = err > DEQUANT_TOL * ref
     ratio = err / np.maximum(DEQUANT_TOL * ref, 1e-300)
     return int(bad.sum()), float(ratio.max()) if ratio.size else 0.0
+
+
+@dataclass
+class TopkReport:
+    rows: int = 0
+    swapped: int = 0        # keys in one set and not the other (both near the k-th score)
+    bad: list = field(default_factory=list)
+
+    def ok(self):
+        return not self.bad
+
+
+def compare_topk(idx_gpu, s_gpu, s_ref, queries, norms, k):
+    """Check (m, k') GPU top-k lists against the oracle's (m, n) scores."""
+    idx_gpu = np.asarray(idx_gpu, dtype=np.int64)
+    s_gpu = np.asarray(s_gpu, dtype=np.float64)
+    s_ref = np.asarray(s_ref, dtype=np.float64)
+    m, n = s_ref.shape
+    kk = min(int(k), n)
+    norms = np.asarray(norms, dtype=np.float64)
+    qn = np.linalg.norm(np.asarray(queries, dtype=np.float64), axis=1)
+    rep = TopkReport(rows=m)
+    ref_idx, ref_s = tq.topk(s_ref, kk)
+    for i in range(m):
+        ids, vals = idx_gpu[i, :kk], s_gpu[i, :kk]
+        tol = SCORE_TOL * qn[i] * norms
+        if len(set(ids.tolist())) != kk or ids.min() < 0 or ids.max() >= n:
+            rep.bad.append((i, "indices not distinct or out of range"))
+            continue
+        order_ok = all(vals[j] > vals[j + 1] or (vals[j] == vals[j + 1] and ids[j] < ids[j + 1])
+                       for j in range(kk - 1))
+        if not order_ok:
+            rep.bad.append((i, "not best first"))
+        if np.any(np.abs(vals - s_ref[i, ids]) > tol[ids]):
+            rep.bad.append((i, "returned score off"))
+        kth = ref_s[i, -1]
+        slack = 2.0 * tol.max()
+        if np.any(s_ref[i, ids] < kth - slack):
+            rep.bad.append((i, "returned key well below the k-th score"))
+        must = np.nonzero(s_ref[i] > kth + slack)[0]
+        if not set(must.tolist()) <= set(ids.tolist()):
+            rep.bad.append((i, "missed a key well above the k-th score"))
+        rep.swapped += len(set(ids.tolist()) ^ set(ref_idx[i].tolist())) // 2
+    return rep

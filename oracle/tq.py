@@ -31,6 +31,13 @@ Stages (page, section):
    makes it unbiased: E[x sign(y)] = sqrt(2/pi) Cov(x, y) / sd(y)).
 7. stage-1 reconstruction: k_hat = n * Pi^T c[idx] ("TurboQuant tutorial",
    end of the polar part: codes plus the kept length map back to a vector).
+8. search: brute-force scores of every query against every stored key, then
+   the k best keys per query ("TurboQuant digest" section 3, the vector
+   search comparison by recall).  Best = largest estimated score; equal
+   scores go in ascending key order (the pages do not order ties).  Recall
+   compares those keys with the k best by the exact inner product of the
+   unquantized vectors: recall@k is the shared fraction, and Recall@1@k the
+   share of queries whose exact best key is among the k found.
 
 Packed layout (bit planes): ``codes[n][B][W]`` and ``signs[n][W]`` as
 uint32 with W = ceil(d / 32); bit p of the index of coordinate j is bit
@@ -124,6 +131,36 @@ def dequant_mse(params: Params, idx, norms):
     """Stage 7: k_hat = n * Pi^T c[idx] for each key."""
     chat = params.centroids[np.asarray(idx)]
     return np.asarray(norms, dtype=np.float64)[:, None] * (chat @ params.pi)
+
+
+def topk(scores, k):
+    """Stage 8: (indices, scores) of the k largest entries of each row of an
+    (m, n) score matrix, best first; equal scores in ascending column order.
+    k is capped at n."""
+    s = np.asarray(scores, dtype=np.float64)
+    k = min(int(k), s.shape[1])
+    order = np.argsort(-s, axis=1, kind="stable")[:, :k]
+    return order, np.take_along_axis(s, order, axis=1)
+
+
+def exact_inner_products(queries, keys):
+    """<q, k> of the unquantized vectors, float64, (m, n)."""
+    return np.asarray(queries, dtype=np.float64) @ np.asarray(keys, dtype=np.float64).T
+
+
+def recall_at_k(found, exact):
+    """Mean over rows of |found_row & exact_row| / k (both (m, k) index arrays)."""
+    found = np.asarray(found)
+    exact = np.asarray(exact)
+    k = exact.shape[1]
+    return float(np.mean([len(set(f.tolist()) & set(e.tolist())) / k for f, e in zip(found, exact)]))
+
+
+def recall_1_at_k(found, exact_best):
+    """Share of rows whose exact best key (exact_best, shape (m,)) is in the
+    row's found indices."""
+    found = np.asarray(found)
+    return float(np.mean([b in set(f.tolist()) for f, b in zip(found, np.asarray(exact_best))]))
 
 
 # ----------------------------------------------------------------------------

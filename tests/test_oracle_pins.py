@@ -397,3 +397,75 @@ def test_pack_round_trip():
     assert np.array_equal(tq.unpack_bits(codes[:, 1, :], 77), ((idx >> 1) & 1).astype(bool))
     beta = rs.random((13, 77)) > 0.5
     assert np.array_equal(tq.unpack_bits(tq.pack_bits(beta), 77), beta)
+
+
+# ----------------------------------------------------------------------------
+# stage 8: search (top-k per query, recall)
+# ----------------------------------------------------------------------------
+
+def test_topk_matches_brute_force_sort():
+    """Against a plain sort of (-score, index) pairs, with many ties (small
+    integer scores), for k below, at and above the row length."""
+    rs = np.random.default_rng(5)
+    for m, n, k in ((3, 1, 1), (4, 7, 3), (5, 16, 16), (2, 9, 20), (6, 33, 10)):
+        s = rs.integers(-3, 4, size=(m, n)).astype(np.float64)
+        idx, vals = tq.topk(s, k)
+        for i in range(m):
+            want = [j for _, j in sorted((-s[i, j], j) for j in range(n))][:min(k, n)]
+            assert idx[i].tolist() == want
+            assert vals[i].tolist() == [s[i, j] for j in want]
+
+
+def test_topk_invariants():
+    rs = np.random.default_rng(6)
+    s = rs.standard_normal((8, 50))
+    idx, vals = tq.topk(s, 10)
+    assert np.array_equal(idx[:, 0], np.argmax(s, axis=1))
+    assert np.all(np.diff(vals, axis=1) <= 0)
+    for i in range(8):
+        rest = np.setdiff1d(np.arange(50), idx[i])
+        assert np.all(s[i, rest] <= vals[i, -1])
+    full, _ = tq.topk(s, 50)
+    assert all(sorted(r.tolist()) == list(range(50)) for r in full)
+
+
+def test_recall_definitions():
+    found = np.array([[0, 1, 2], [5, 6, 7]])
+    exact = np.array([[2, 3, 4], [7, 6, 5]])
+    assert tq.recall_at_k(found, exact) == pytest.approx((1 / 3 + 1) / 2)
+    assert tq.recall_1_at_k(found, np.array([2, 9])) == 0.5
+    q = np.array([[1.0, 0.0], [0.0, 1.0]])
+    k = np.array([[3.0, 0.0], [0.0, 2.0], [1.0, 1.0]])
+    assert np.array_equal(tq.exact_inner_products(q, k), [[3.0, 0.0, 1.0], [0.0, 2.0, 1.0]])
+
+
+def test_compare_topk_flags_planted_mistakes():
+    """The rule accepts the oracle's own lists and a swap at the k-th score
+    within tolerance, and rejects a duplicate, a wrong order, a far miss and
+    an off score (mistakes planted on the CPU)."""
+    from oracle import parity
+    rs = np.random.default_rng(7)
+    m, n, k = 4, 40, 5
+    q = rs.standard_normal((m, 8))
+    norms = np.ones(n)
+    s = rs.standard_normal((m, n)) * 10.0
+    s[0, 7] = s[0, 3] = 50.0                         # tie at the top of row 0
+    idx, vals = tq.topk(s, k)
+    assert parity.compare_topk(idx, vals, s, q, norms, k).ok()
+    # row 1: the (k+1)-th key within tolerance of the k-th may replace it
+    order = np.argsort(-s[1], kind="stable")
+    s[1, order[k]] = s[1, order[k - 1]] - 1e-4 * np.linalg.norm(q[1])
+    idx, vals = tq.topk(s, k)
+    near = idx.copy(); nv = vals.copy()
+    near[1, -1] = order[k]; nv[1, -1] = s[1, order[k]]
+    assert parity.compare_topk(near, nv, s, q, norms, k).ok()
+    bad = idx.copy(); bad[2, 1] = bad[2, 0]
+    assert not parity.compare_topk(bad, vals, s, q, norms, k).ok()
+    swapped = idx.copy(); sv = vals.copy()
+    swapped[3, [0, 1]] = swapped[3, [1, 0]]; sv[3, [0, 1]] = sv[3, [1, 0]]
+    assert not parity.compare_topk(swapped, sv, s, q, norms, k).ok()
+    far = idx.copy(); fv = vals.copy()
+    worst = int(np.argmin(s[2])); far[2, 0] = worst; fv[2, 0] = s[2, worst]
+    assert not parity.compare_topk(far, fv, s, q, norms, k).ok()
+    off = vals.copy(); off[0, 2] += 1.0
+    assert not parity.compare_topk(idx, off, s, q, norms, k).ok()
