@@ -164,6 +164,26 @@ TQ_API int tq_logits(tq_handle h, const float* queries, int64_t groups, int64_t 
               const float* rnorms, int64_t n, float* scores, void* workspace,
               size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace tq_logits_topk needs for `groups` x `nq`
+ * queries against n keys per group, k best keys per query. */
+TQ_API size_t tq_logits_topk_workspace_size(tq_handle h, int64_t groups, int64_t nq, int64_t n, int32_t k);
+
+/* Search ("TurboQuant digest", section 3: brute-force scores compared by
+ * recall): the k best keys per query by the asymmetric score of tq_logits,
+ * without materialising the score matrix.  queries, packed arrays, groups,
+ * nq and n as for tq_logits; 1 <= k <= 64.  top_idx: device int64
+ * [groups][nq][k], key index within the group; top_scores: device float
+ * [groups][nq][k], best first, equal scores in ascending key index.  When
+ * k > n the entries past n hold index -1 and score -inf.  workspace: device,
+ * at least tq_logits_topk_workspace_size(h, groups, nq, n, k) bytes,
+ * 256-byte aligned; its contents are scratch.  Scores are computed exactly
+ * as tq_logits computes them, a chunk of keys at a time.  Asynchronous on
+ * `stream`. */
+TQ_API int tq_logits_topk(tq_handle h, const float* queries, int64_t groups, int64_t nq,
+                          const uint32_t* codes, const uint32_t* signs, const float* norms,
+                          const float* rnorms, int64_t n, int32_t k, int64_t* top_idx,
+                          float* top_scores, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Stage-1 reconstruction k_hat = n * Pi^T c[idx] of n packed keys.
  * codes, norms: device as in the packed layout; khat: device float [n][d].
  * Asynchronous on `stream`. */

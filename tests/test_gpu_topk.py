@@ -1,0 +1,121 @@
+"""Search entry point (tq_logits_topk): the k best keys per query against the
+oracle's top-k of its own scores on the same packed keys (rule in
+``oracle.parity.compare_topk``), including many score chunks, k past n,
+partial query quads, several groups and equal scores; recall against exact
+inner products on the search workload's generator.  Expected values come
+only from ``oracle``."""
+import os
+
+import numpy as np
+import pytest
+
+from oracle import parity
+from oracle import tq
+from tests.test_gpu_parity import _announce, _cpu, _dev, _packed_to_dev, _params
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import vector_quantization_quantize_amd as tqm
+    from vector_quantization_quantize_amd import workloads as wl
+    return torch, tqm, wl
+
+
+def _check_topk(env, d, bits, keys, queries, k, chunk=None):
+    """Quantize on the oracle, score and select on the GPU from the oracle's
+    packed keys; returns (gpu indices, oracle top-k indices) per group."""
+    torch, tqm, _ = env
+    pr = _params(d, bits)
+    h = tqm.tq_init(d, bits, 0)
+    groups, nq, _ = queries.shape
+    n = keys.shape[0] // groups
+    qz = tq.quantize(pr, keys.astype(np.float64))
+    packed = tq.pack(pr, qz)
+    pdev = _packed_to_dev(torch, packed)
+    old = os.environ.get("TQ_TOPK_CHUNK")
+    if chunk is not None:
+        os.environ["TQ_TOPK_CHUNK"] = str(chunk)
+    try:
+        idx, sc = tqm.tq_logits_topk(h, _dev(torch, queries.astype(np.float32)), *pdev, k=k, n=n)
+        torch.cuda.synchronize()
+    finally:
+        if chunk is not None:
+            if old is None:
+                del os.environ["TQ_TOPK_CHUNK"]
+            else:
+                os.environ["TQ_TOPK_CHUNK"] = old
+    idx, sc = _cpu(idx), _cpu(sc)
+    found, ref = [], []
+    for g in range(groups):
+        sl = slice(g * n, (g + 1) * n)
+        s_ref = tq.scores(pr, queries[g], qz.idx[sl], qz.beta[sl], packed[2][sl].astype(np.float64),
+                          packed[3][sl].astype(np.float64))
+        kk = min(k, n)
+        rep = parity.compare_topk(idx[g][:, :kk], sc[g][:, :kk], s_ref, queries[g], packed[2][sl], k)
+        assert rep.ok(), (g, rep.bad[:5])
+        if k > n:  # entries past n are empty
+            assert np.all(idx[g][:, n:] == -1) and np.all(np.isneginf(sc[g][:, n:]))
+        found.append(idx[g][:, :kk])
+        ref.append(tq.topk(s_ref, kk)[0])
+        print("group", g, "near-k swaps", rep.swapped)
+    return found, ref
+
+
+@pytest.mark.parametrize("d,bits,groups,nq,n,k,chunk", [
+    (128, 3, 1, 4, 3000, 10, 256),     # table scorer, 12 chunks, ragged last
+    (128, 2, 2, 5, 1000, 16, None),    # two groups, partial query quad, one chunk
+    (100, 4, 1, 1, 777, 1, 64),        # top-1, d < 128 on the table scorer
+    (200, 2, 1, 6, 2050, 10, 512),     # general scorer (d = 200), several chunks
+    (64, 5, 3, 2, 7, 10, None),        # k > n
+    (256, 3, 1, 3, 640, 64, 128),      # k at its maximum, general scorer
+])
+def test_topk_matches_oracle(env, d, bits, groups, nq, n, k, chunk):
+    _announce(f"topk d={d} bits={bits} groups={groups} nq={nq} n={n} k={k} chunk={chunk}")
+    rs = np.random.default_rng(d + bits + n)
+    keys = rs.standard_normal((groups * n, d))
+    queries = rs.standard_normal((groups, nq, d)).astype(np.float32)
+    _check_topk(env, d, bits, keys, queries, k, chunk)
+
+
+def test_topk_equal_scores_in_index_order(env):
+    """Every key appears three times: equal packed keys get equal scores, and
+    the three copies must come out in ascending index order."""
+    _announce("topk equal scores")
+    rs = np.random.default_rng(9)
+    base = rs.standard_normal((200, 128))
+    keys = np.concatenate([base, base, base])
+    queries = rs.standard_normal((1, 4, 128)).astype(np.float32)
+    found, _ = _check_topk(env, 128, 3, keys, queries, 12, chunk=128)
+    for row in found[0]:
+        copies = {}
+        for pos, i in enumerate(row.tolist()):
+            copies.setdefault(i % 200, []).append(i)
+        for lst in copies.values():
+            assert lst == sorted(lst)
+
+
+@pytest.mark.parametrize("name", ["search_b2", "search_b4"])
+def test_topk_search_recall(env, name):
+    """The search workload's generator at 60 000 keys and 32 queries: parity
+    of the top-10 with the oracle, and recall against exact inner products
+    of the unquantized vectors equal to the oracle's own (the sets may differ
+    only at the 10th score)."""
+    torch, tqm, wl = env
+    w = wl.WORKLOADS[name].scaled(n=60000, nq=32)
+    _announce(f"topk recall {w.name} n={w.n} nq={w.nq} bits={w.bits}")
+    keys = wl.keys(w)
+    queries = wl.queries(w)
+    found, ref = _check_topk(env, w.d, w.bits, keys, queries, 10, chunk=8192)
+    exact = tq.exact_inner_products(queries[0], keys)
+    exact_idx, _ = tq.topk(exact, 10)
+    r_gpu = tq.recall_at_k(found[0], exact_idx)
+    r_ref = tq.recall_at_k(ref[0], exact_idx)
+    r1_gpu = tq.recall_1_at_k(found[0], exact_idx[:, 0])
+    r1_ref = tq.recall_1_at_k(ref[0], exact_idx[:, 0])
+    print(f"{w.name}: recall@10 gpu {r_gpu:.3f} oracle {r_ref:.3f}; Recall@1@10 gpu {r1_gpu:.3f} oracle {r1_ref:.3f}")
+    assert abs(r_gpu - r_ref) <= 0.05 and abs(r1_gpu - r1_ref) <= 0.1

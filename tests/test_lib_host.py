@@ -70,6 +70,9 @@ def test_bad_arguments_are_rejected(tqm):
     assert lib.tq_quantize(None, None, 0, 1, 128, None, None, None, None, None) == tqm.TQ_EINVAL
     assert lib.tq_logits(None, None, 1, 1, None, None, None, None, 1, None, None, 0, None) == tqm.TQ_EINVAL
     assert lib.tq_dequant_mse(None, None, None, 1, None, None) == tqm.TQ_EINVAL
+    assert lib.tq_logits_topk(None, None, 1, 1, None, None, None, None, 1, 10, None, None, None, 0,
+                              None) == tqm.TQ_EINVAL
+    assert lib.tq_logits_topk_workspace_size(None, 1, 1, 1, 10) == 0
     assert lib.tq_destroy(None) == tqm.TQ_OK
     assert lib.tq_params_hash(None) == 0
     assert lib.tq_logits_workspace_size(None, 1, 1) == 0

@@ -26,7 +26,7 @@ TQ_FORMAT_VERSION = 1
 # every symbol include/tq.h declares
 EXPORTS = ("tq_init", "tq_init_explicit", "tq_destroy", "tq_get_layout", "tq_host_params",
            "tq_params_hash", "tq_quantize", "tq_logits_workspace_size", "tq_logits",
-           "tq_dequant_mse", "tq_strerror")
+           "tq_logits_topk_workspace_size", "tq_logits_topk", "tq_dequant_mse", "tq_strerror")
 
 
 class TqError(RuntimeError):
@@ -65,6 +65,8 @@ def _lib():
         "tq_logits_workspace_size": (sz, [vp, i64, i64]),
         "tq_logits": (ctypes.c_int, [vp, vp, i64, i64, vp, vp, vp, vp, i64, vp, vp, sz, vp]),
         "tq_dequant_mse": (ctypes.c_int, [vp, vp, vp, i64, vp, vp]),
+        "tq_logits_topk_workspace_size": (sz, [vp, i64, i64, i64, i32]),
+        "tq_logits_topk": (ctypes.c_int, [vp, vp, i64, i64, vp, vp, vp, vp, i64, i32, vp, vp, vp, sz, vp]),
         "tq_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -227,6 +229,41 @@ def tq_logits(h, queries, codes, signs, norms, rnorms, n=None, scores=None, work
                                          _ptr(norms), _ptr(rnorms), n, _ptr(scores), _ptr(workspace),
                                          workspace.numel() * workspace.element_size(), _stream(stream)))
     return scores
+
+
+def tq_logits_topk_workspace_size(h, groups, nq, n, k):
+    return int(_lib().tq_logits_topk_workspace_size(h.ptr, int(groups), int(nq), int(n), int(k)))
+
+
+def tq_logits_topk(h, queries, codes, signs, norms, rnorms, k, n=None, out=None, workspace=None, stream=None):
+    """The k best keys per query by the score tq_logits computes.
+
+    queries: cuda float32 (groups, nq, d); packed arrays hold groups*n keys.
+    Returns (indices int64 (groups, nq, k), scores float32 (groups, nq, k)),
+    best first; index -1 / score -inf past n keys."""
+    import torch
+    if queries.dim() == 2:
+        queries = queries.unsqueeze(0)
+    groups, nq, d = queries.shape
+    if d != h.d or not queries.is_contiguous() or queries.dtype != torch.float32:
+        raise ValueError("queries must be contiguous float32 (groups, nq, d)")
+    total = norms.shape[0]
+    if n is None:
+        n = total // groups
+    if groups * n > total:
+        raise ValueError("packed arrays hold fewer than groups * n keys")
+    if out is None:
+        out = (torch.empty((groups, nq, k), dtype=torch.int64, device=queries.device),
+               torch.empty((groups, nq, k), dtype=torch.float32, device=queries.device))
+    idx, sc = out
+    ws_bytes = tq_logits_topk_workspace_size(h, groups, nq, n, k)
+    if workspace is None:
+        workspace = torch.empty((max(ws_bytes, 256) + 255) // 4, dtype=torch.float32, device=queries.device)
+    _check("tq_logits_topk", _lib().tq_logits_topk(h.ptr, _ptr(queries), groups, nq, _ptr(codes), _ptr(signs),
+                                                   _ptr(norms), _ptr(rnorms), n, int(k), _ptr(idx), _ptr(sc),
+                                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                                   _stream(stream)))
+    return idx, sc
 
 
 def tq_dequant_mse(h, codes, norms, khat=None, stream=None):

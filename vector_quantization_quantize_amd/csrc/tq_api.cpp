@@ -403,6 +403,92 @@ int tq_logits(tq_handle h, const float* queries, int64_t groups, int64_t nq, con
   return e == hipSuccess ? TQ_OK : TQ_EHIP;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Keys scored per chunk by the search entry point: scores of one chunk for
+// all nq queries stay within 64 Mi floats (about the size of the MALL).
+// TQ_TOPK_CHUNK=<keys> overrides it (tests use it to force many chunks).
+int64_t topk_chunk(int64_t nq, int64_t n) {
+  int64_t c = (int64_t(64) << 20) / (nq > 0 ? nq : 1);
+  if (const char* v = std::getenv("TQ_TOPK_CHUNK")) c = std::atoll(v);
+  c = c / 64 * 64;
+  if (c < 64) c = 64;
+  return c < n ? c : n;
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+struct TopkWorkspace {
+  size_t chunk, list_s, list_i, vw, total;
+};
+
+TopkWorkspace topk_layout(const tq_ctx* h, int64_t nq, int64_t n, int32_t k) {
+  TopkWorkspace w{};
+  const int64_t c = topk_chunk(nq, n);
+  w.chunk = 0;
+  w.list_s = align256(size_t(nq) * size_t(c) * sizeof(float));
+  w.list_i = w.list_s + align256(size_t(nq) * size_t(k) * sizeof(float));
+  w.vw = w.list_i + align256(size_t(nq) * size_t(k) * sizeof(int64_t));
+  w.total = w.vw + align256(size_t(nq) * size_t(tqdev::vw_stride(h->d)) * sizeof(float));
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tq_logits_topk_workspace_size(tq_handle h, int64_t groups, int64_t nq, int64_t n, int32_t k) {
+  if (!h || groups < 0 || nq < 0 || n < 0 || k < 1 || k > tqdev::kTopkMax) return 0;
+  return topk_layout(h, nq, n, k).total;
+}
+
+int tq_logits_topk(tq_handle h, const float* queries, int64_t groups, int64_t nq, const uint32_t* codes,
+                   const uint32_t* signs, const float* norms, const float* rnorms, int64_t n, int32_t k,
+                   int64_t* top_idx, float* top_scores, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!h || groups < 0 || nq < 0 || n < 0) return TQ_EINVAL;
+  if (k < 1 || k > tqdev::kTopkMax) return TQ_EINVAL;
+  if (groups == 0 || nq == 0) return TQ_OK;
+  if (!queries || !top_idx || !top_scores || !workspace) return TQ_EINVAL;
+  if (n > 0 && (!codes || !signs || !norms || !rnorms)) return TQ_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return TQ_EINVAL;
+  const TopkWorkspace lay = topk_layout(h, nq, n, k);
+  if (workspace_bytes < lay.total) return TQ_EINVAL;
+  if (check_device(h) != TQ_OK) return TQ_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  float* chunk = reinterpret_cast<float*>(ws + lay.chunk);
+  float* list_s = reinterpret_cast<float*>(ws + lay.list_s);
+  int64_t* list_i = reinterpret_cast<int64_t*>(ws + lay.list_i);
+  float* vw = reinterpret_cast<float*>(ws + lay.vw);
+  const bool lut = !tqdev::force_reference_kernels() && tqdev::logits_lut128_supported(h);
+  const int64_t c = topk_chunk(nq, n);
+  const int64_t cw = int64_t(h->code_bits) * h->words;  // code words per key
+  hipError_t e = hipSuccess;
+  for (int64_t g = 0; g < groups && e == hipSuccess; ++g) {
+    const float* qg = queries + g * nq * h->d;
+    float* og = top_scores + g * nq * k;
+    int64_t* oi = top_idx + g * nq * k;
+    if (n == 0) {  // no keys: every entry is empty
+      e = tqdev::launch_topk_merge(chunk, nq, 0, 0, k, list_s, list_i, true, og, oi, s);
+      continue;
+    }
+    if (!lut && (e = tqdev::launch_query_prep(h, qg, nq, vw, s)) != hipSuccess) break;
+    for (int64_t c0 = 0; c0 < n && e == hipSuccess; c0 += c) {
+      const int64_t ce = n - c0 < c ? n - c0 : c;
+      const int64_t key0 = g * n + c0;
+      e = lut ? tqdev::launch_logits_lut128(h, qg, 1, nq, codes + key0 * cw, signs + key0 * h->words,
+                                            norms + key0, rnorms + key0, ce, chunk, s)
+              : tqdev::launch_logits_v1(h, vw, 1, nq, codes + key0 * cw, signs + key0 * h->words, norms + key0,
+                                        rnorms + key0, ce, chunk, s);
+      if (e != hipSuccess) break;
+      e = tqdev::launch_topk_merge(chunk, nq, ce, c0, k, list_s, list_i, c0 + ce >= n, og, oi, s);
+    }
+  }
+  return e == hipSuccess ? TQ_OK : TQ_EHIP;
+}
+
 int tq_dequant_mse(tq_handle h, const uint32_t* codes, const float* norms, int64_t n, float* khat,
                    void* stream) {
   if (!h || n < 0) return TQ_EINVAL;

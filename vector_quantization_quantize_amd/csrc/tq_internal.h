@@ -106,6 +106,13 @@ hipError_t launch_dequant_mfma128(const tq_ctx* h, const uint32_t* codes, const 
 // TQ_KERNELS=ref selects the straightforward kernels everywhere (A/B checks)
 bool force_reference_kernels();
 
+// search: merge one chunk of scores ([nq][csize], keys c0 ..) into the running
+// lists of the k best keys per query ([nq][k]); the last chunk writes the
+// outputs instead (index -1, score -inf past the keys seen)
+constexpr int kTopkMax = 64;
+hipError_t launch_topk_merge(const float* chunk, int64_t nq, int64_t csize, int64_t c0, int k, float* list_s,
+                             int64_t* list_i, bool last, float* out_s, int64_t* out_i, hipStream_t stream);
+
 hipError_t launch_dequant_v1(const tq_ctx* h, const uint32_t* codes, const float* norms, int64_t n,
                              float* khat, hipStream_t stream);
 
