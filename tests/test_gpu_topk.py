@@ -119,3 +119,36 @@ def test_topk_search_recall(env, name):
     r1_ref = tq.recall_1_at_k(ref[0], exact_idx[:, 0])
     print(f"{w.name}: recall@10 gpu {r_gpu:.3f} oracle {r_ref:.3f}; Recall@1@10 gpu {r1_gpu:.3f} oracle {r1_ref:.3f}")
     assert abs(r_gpu - r_ref) <= 0.05 and abs(r1_gpu - r1_ref) <= 0.1
+
+
+@pytest.mark.parametrize("d,bits,groups,nq,n", [
+    (128, 3, 1, 16, 1000),   # fewest queries that take the matrix-core scorer
+    (200, 2, 1, 130, 777),   # two query tiles, the second nearly empty; ragged key tile
+    (256, 5, 2, 33, 65),     # d at its maximum, two groups
+    (33, 4, 1, 20, 500),     # d not a multiple of 16
+    (2, 2, 1, 16, 40),       # smallest d
+    (100, 3, 3, 17, 300),
+])
+def test_matrix_core_scorer_every_score(env, d, bits, groups, nq, n):
+    """Many queries per group go to the matrix-core scorer: every score of
+    the oracle's packed keys against the oracle's estimator."""
+    torch, tqm, _ = env
+    _announce(f"matrix-core scorer d={d} bits={bits} groups={groups} nq={nq} n={n}")
+    pr = _params(d, bits)
+    h = tqm.tq_init(d, bits, 0)
+    rs = np.random.default_rng(d * 7 + nq + n)
+    keys = rs.standard_normal((groups * n, d)) * np.exp(0.5 * rs.standard_normal((groups * n, 1)))
+    queries = rs.standard_normal((groups, nq, d)).astype(np.float32) * 3.0
+    qz = tq.quantize(pr, keys)
+    packed = tq.pack(pr, qz)
+    pdev = _packed_to_dev(torch, packed)
+    s = _cpu(tqm.tq_logits(h, _dev(torch, queries), *pdev, n=n))
+    worst = 0.0
+    for g in range(groups):
+        sl = slice(g * n, (g + 1) * n)
+        ref = tq.scores(pr, queries[g], qz.idx[sl], qz.beta[sl], packed[2][sl].astype(np.float64),
+                        packed[3][sl].astype(np.float64))
+        bad, ratio = parity.score_violations(s[g], ref, queries[g], packed[2][sl])
+        assert bad == 0, (g, ratio)
+        worst = max(worst, ratio)
+    print(f"worst |error| / tolerance {worst:.3f}")

@@ -233,10 +233,32 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 }  // namespace
 
+namespace {
+
+// Which scorer serves nq queries per group: the matrix-core kernel for many
+// queries (d <= 256), the lookup-table kernel for a few (d in (96, 128]),
+// else the general kernel (also for TQ_KERNELS=ref).
+enum class Scorer { kGeneral, kLut, kMfma };
+
+Scorer pick_scorer(const tq_ctx* h, int64_t nq);
+
+}  // namespace
+
 bool tqdev::force_reference_kernels() {
   const char* v = std::getenv("TQ_KERNELS");
   return v && std::strcmp(v, "ref") == 0;
 }
+
+namespace {
+
+Scorer pick_scorer(const tq_ctx* h, int64_t nq) {
+  if (tqdev::force_reference_kernels()) return Scorer::kGeneral;
+  if (nq >= tqdev::kScoreMfmaMinQueries && tqdev::score_mfma_supported(h)) return Scorer::kMfma;
+  if (tqdev::logits_lut128_supported(h)) return Scorer::kLut;
+  return Scorer::kGeneral;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -391,14 +413,16 @@ int tq_logits(tq_handle h, const float* queries, int64_t groups, int64_t nq, con
   if (check_device(h) != TQ_OK) return TQ_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (!tqdev::force_reference_kernels() && tqdev::logits_lut128_supported(h)) {
+  const Scorer sc = pick_scorer(h, nq);
+  if (sc == Scorer::kLut) {
     // query transform fused into the scoring kernel; workspace unused
     e = tqdev::launch_logits_lut128(h, queries, groups, nq, codes, signs, norms, rnorms, n, scores, s);
   } else {
     float* vw = static_cast<float*>(workspace);
     e = tqdev::launch_query_prep(h, queries, groups * nq, vw, s);
     if (e != hipSuccess) return TQ_EHIP;
-    e = tqdev::launch_logits_v1(h, vw, groups, nq, codes, signs, norms, rnorms, n, scores, s);
+    e = sc == Scorer::kMfma ? tqdev::launch_score_mfma(h, vw, groups, nq, codes, signs, norms, rnorms, n, scores, s)
+                            : tqdev::launch_logits_v1(h, vw, groups, nq, codes, signs, norms, rnorms, n, scores, s);
   }
   return e == hipSuccess ? TQ_OK : TQ_EHIP;
 }
@@ -408,10 +432,13 @@ int tq_logits(tq_handle h, const float* queries, int64_t groups, int64_t nq, con
 namespace {
 
 // Keys scored per chunk by the search entry point: scores of one chunk for
-// all nq queries stay within 64 Mi floats (about the size of the MALL).
-// TQ_TOPK_CHUNK=<keys> overrides it (tests use it to force many chunks).
-int64_t topk_chunk(int64_t nq, int64_t n) {
+// all nq queries stay within 64 Mi floats (about the size of the MALL); the
+// general scorer, which spreads only over keys, gets at least 65536 keys
+// per chunk to fill the GPU.  TQ_TOPK_CHUNK=<keys> overrides it (tests use
+// it to force many chunks).
+int64_t topk_chunk(const tq_ctx* h, int64_t nq, int64_t n) {
   int64_t c = (int64_t(64) << 20) / (nq > 0 ? nq : 1);
+  if (pick_scorer(h, nq) == Scorer::kGeneral && c < 65536) c = 65536;
   if (const char* v = std::getenv("TQ_TOPK_CHUNK")) c = std::atoll(v);
   c = c / 64 * 64;
   if (c < 64) c = 64;
@@ -426,7 +453,7 @@ struct TopkWorkspace {
 
 TopkWorkspace topk_layout(const tq_ctx* h, int64_t nq, int64_t n, int32_t k) {
   TopkWorkspace w{};
-  const int64_t c = topk_chunk(nq, n);
+  const int64_t c = topk_chunk(h, nq, n);
   w.chunk = 0;
   w.list_s = align256(size_t(nq) * size_t(c) * sizeof(float));
   w.list_i = w.list_s + align256(size_t(nq) * size_t(k) * sizeof(float));
@@ -462,8 +489,8 @@ int tq_logits_topk(tq_handle h, const float* queries, int64_t groups, int64_t nq
   float* list_s = reinterpret_cast<float*>(ws + lay.list_s);
   int64_t* list_i = reinterpret_cast<int64_t*>(ws + lay.list_i);
   float* vw = reinterpret_cast<float*>(ws + lay.vw);
-  const bool lut = !tqdev::force_reference_kernels() && tqdev::logits_lut128_supported(h);
-  const int64_t c = topk_chunk(nq, n);
+  const Scorer sc = pick_scorer(h, nq);
+  const int64_t c = topk_chunk(h, nq, n);
   const int64_t cw = int64_t(h->code_bits) * h->words;  // code words per key
   hipError_t e = hipSuccess;
   for (int64_t g = 0; g < groups && e == hipSuccess; ++g) {
@@ -474,14 +501,22 @@ int tq_logits_topk(tq_handle h, const float* queries, int64_t groups, int64_t nq
       e = tqdev::launch_topk_merge(chunk, nq, 0, 0, k, list_s, list_i, true, og, oi, s);
       continue;
     }
-    if (!lut && (e = tqdev::launch_query_prep(h, qg, nq, vw, s)) != hipSuccess) break;
+    if (sc != Scorer::kLut && (e = tqdev::launch_query_prep(h, qg, nq, vw, s)) != hipSuccess) break;
     for (int64_t c0 = 0; c0 < n && e == hipSuccess; c0 += c) {
       const int64_t ce = n - c0 < c ? n - c0 : c;
       const int64_t key0 = g * n + c0;
-      e = lut ? tqdev::launch_logits_lut128(h, qg, 1, nq, codes + key0 * cw, signs + key0 * h->words,
-                                            norms + key0, rnorms + key0, ce, chunk, s)
-              : tqdev::launch_logits_v1(h, vw, 1, nq, codes + key0 * cw, signs + key0 * h->words, norms + key0,
-                                        rnorms + key0, ce, chunk, s);
+      const uint32_t* cg = codes + key0 * cw;
+      const uint32_t* sg = signs + key0 * h->words;
+      switch (sc) {
+        case Scorer::kLut:
+          e = tqdev::launch_logits_lut128(h, qg, 1, nq, cg, sg, norms + key0, rnorms + key0, ce, chunk, s);
+          break;
+        case Scorer::kMfma:
+          e = tqdev::launch_score_mfma(h, vw, 1, nq, cg, sg, norms + key0, rnorms + key0, ce, chunk, s);
+          break;
+        default:
+          e = tqdev::launch_logits_v1(h, vw, 1, nq, cg, sg, norms + key0, rnorms + key0, ce, chunk, s);
+      }
       if (e != hipSuccess) break;
       e = tqdev::launch_topk_merge(chunk, nq, ce, c0, k, list_s, list_i, c0 + ce >= n, og, oi, s);
     }

@@ -94,6 +94,13 @@ hipError_t launch_logits_lut128(const tq_ctx* h, const float* queries, int64_t g
 
 // also requires 16-byte aligned keys and outputs (outputs are written as
 // whole 16-byte rows)
+// matrix-core scorer for many queries (d <= 256); vw from launch_query_prep
+bool score_mfma_supported(const tq_ctx* h);
+constexpr int64_t kScoreMfmaMinQueries = 16;  // below this the lookup-table scorer is used
+hipError_t launch_score_mfma(const tq_ctx* h, const float* vw, int64_t groups, int64_t nq, const uint32_t* codes,
+                             const uint32_t* signs, const float* norms, const float* rnorms, int64_t n,
+                             float* scores, hipStream_t stream);
+
 bool quantize_mfma128_supported(const tq_ctx* h, const void* keys, int key_dtype, int64_t ldk,
                                 const void* codes, const void* signs, const void* norms, const void* rnorms);
 hipError_t launch_quantize_mfma128(const tq_ctx* h, const void* keys, int64_t n, int64_t ldk, uint32_t* codes,
