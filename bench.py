@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--cold-reps", type=int, default=10, help="flushed-cache reps per kernel")
     ap.add_argument("--cpu-groups", type=int, default=24, help="key groups timed on the CPU oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-search", action="store_true", help="skip the search (top-k) measurement")
+    ap.add_argument("--search-workload", default="search_b2")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -94,6 +96,61 @@ def measured_profile(workload):
             if "mfma_busy_pct" in fields:
                 mfma_busy[entry] = float(fields["mfma_busy_pct"])
     return traffic, mfma_busy
+
+
+def search_topk(name, seed, k=10, reps=3, recall_queries=64):
+    """Top-k search over a full search workload (every query against every
+    key, best k per query, no score matrix): time per call and recall of
+    the returned keys against the exact inner products of the unquantized
+    vectors on a sample of queries (plain numpy brute force)."""
+    import numpy as np
+    import torch
+
+    import vector_quantization_quantize_amd as tqm
+    from vector_quantization_quantize_amd import workloads as wl
+    w = wl.WORKLOADS[name]
+    keys_np = wl.keys(w, seed)
+    queries_np = wl.queries(w, seed)
+    h = tqm.tq_init(w.d, w.bits, 0)
+    keys = torch.from_numpy(keys_np).cuda()
+    queries = torch.from_numpy(queries_np).cuda()
+    packed = tqm.tq_quantize(h, keys)
+    del keys
+    ws = torch.empty(tqm.tq_logits_topk_workspace_size(h, w.groups, w.nq, w.n, k) // 4 + 64, dtype=torch.float32,
+                     device="cuda")
+    out = (torch.empty((w.groups, w.nq, k), dtype=torch.int64, device="cuda"),
+           torch.empty((w.groups, w.nq, k), dtype=torch.float32, device="cuda"))
+    fn = lambda: tqm.tq_logits_topk(h, queries, *packed, k=k, n=w.n, out=out, workspace=ws)
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    found = out[0][0, :recall_queries].cpu().numpy()
+    sample = queries_np[0, :recall_queries].astype(np.float64)
+    exact = sample @ keys_np.astype(np.float64).T
+    top = np.argsort(-exact, axis=1, kind="stable")[:, :k]
+    recall = float(np.mean([len(set(f) & set(t)) / k for f, t in zip(found.tolist(), top.tolist())]))
+    recall1 = float(np.mean([t[0] in set(f) for f, t in zip(found.tolist(), top.tolist())]))
+    scores = w.groups * w.nq * w.n
+    kp = (w.d + 15) // 16 * 16
+    # algorithmic work per score: d level products and d signed adds (4d
+    # flops); the matrix-core scorer runs three f16 passes over K = d
+    # rounded up to 16
+    useful = 4.0 * w.d * scores / (ms * 1e-3) / 1e12
+    raw = 3 * 2.0 * kp * scores / (ms * 1e-3) / 1e12
+    tqm.tq_destroy(h)
+    return {"workload": f"{w.name}: {w.description}", "keys": w.n * w.groups, "queries": w.nq * w.groups, "d": w.d,
+            "bits": w.bits, "k": k, "ms": round(ms, 3), "scores_per_s": scores / (ms * 1e-3),
+            "recall_at_10": round(recall, 4), "recall_1_at_10": round(recall1, 4),
+            "recall_sample_queries": recall_queries,
+            "roofline": {"bound": "mfma", "achieved": round(useful, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(useful / BF16_MFMA_PEAK_TFLOPS, 4),
+                         "raw_mfma_TFLOPs": round(raw, 2)}}
 
 
 def cpu_baseline(w, keys_np, queries_np, groups, seed):
@@ -267,6 +324,10 @@ def main():
         "roofline_logits": roofline("tq_logits"),
         "roofline_by_kernel": {n: roofline(n) for n in names},
     }
+    if not args.no_search:
+        del keys, queries, packed, scores, ws, khat
+        torch.cuda.empty_cache()
+        line["search_topk"] = search_topk(args.search_workload, args.seed)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, keys_np, queries_np, min(args.cpu_groups, w.groups), args.seed)
     print(json.dumps(line), flush=True)
