@@ -2,8 +2,11 @@
 oracle's top-k of its own scores on the same packed keys (rule in
 ``oracle.parity.compare_topk``), including many score chunks, k past n,
 partial query quads, several groups and equal scores; recall against exact
-inner products on the search workload's generator.  Expected values come
-only from ``oracle``."""
+inner products on the search workload's generator.  Both forms: chunked
+(score chunks, then merge; forced by TQ_TOPK_CHUNK) and fused (the
+matrix-core scorer keeps per-block lists; taken for 16 or more queries with
+d <= 256 when no chunk size is forced).  Expected values come only from
+``oracle``."""
 import os
 
 import numpy as np
@@ -82,15 +85,34 @@ def test_topk_matches_oracle(env, d, bits, groups, nq, n, k, chunk):
     _check_topk(env, d, bits, keys, queries, k, chunk)
 
 
-def test_topk_equal_scores_in_index_order(env):
+@pytest.mark.parametrize("d,bits,groups,nq,n,k", [
+    (128, 3, 1, 16, 3000, 10),    # fewest queries of the fused form
+    (200, 2, 1, 130, 2050, 10),   # one index bit (sign form), two query tiles, ragged key tile
+    (256, 5, 2, 33, 700, 64),     # k at its maximum, four index bits, two groups
+    (33, 4, 1, 20, 7, 10),        # k > n, one partial key tile
+    (100, 2, 3, 17, 300, 1),      # top-1, sign form, three groups
+    (64, 2, 1, 40, 40000, 5),     # many blocks per query tile
+    (48, 4, 1, 300, 5000, 32),    # three query tiles, three index bits
+])
+def test_topk_fused_matches_oracle(env, d, bits, groups, nq, n, k):
+    _announce(f"topk fused d={d} bits={bits} groups={groups} nq={nq} n={n} k={k}")
+    rs = np.random.default_rng(d * 3 + bits + n + k)
+    keys = rs.standard_normal((groups * n, d))
+    queries = rs.standard_normal((groups, nq, d)).astype(np.float32)
+    _check_topk(env, d, bits, keys, queries, k)
+
+
+@pytest.mark.parametrize("nq,chunk", [(4, 128), (20, None)])
+def test_topk_equal_scores_in_index_order(env, nq, chunk):
     """Every key appears three times: equal packed keys get equal scores, and
-    the three copies must come out in ascending index order."""
-    _announce("topk equal scores")
+    the three copies must come out in ascending index order (chunked form,
+    and the fused form, where copies fall in different key tiles)."""
+    _announce(f"topk equal scores nq={nq} chunk={chunk}")
     rs = np.random.default_rng(9)
     base = rs.standard_normal((200, 128))
     keys = np.concatenate([base, base, base])
-    queries = rs.standard_normal((1, 4, 128)).astype(np.float32)
-    found, _ = _check_topk(env, 128, 3, keys, queries, 12, chunk=128)
+    queries = rs.standard_normal((1, nq, 128)).astype(np.float32)
+    found, _ = _check_topk(env, 128, 3, keys, queries, 12, chunk=chunk)
     for row in found[0]:
         copies = {}
         for pos, i in enumerate(row.tolist()):
@@ -99,18 +121,19 @@ def test_topk_equal_scores_in_index_order(env):
             assert lst == sorted(lst)
 
 
-@pytest.mark.parametrize("name", ["search_b2", "search_b4"])
-def test_topk_search_recall(env, name):
+@pytest.mark.parametrize("name,chunk", [("search_b2", 8192), ("search_b4", 8192), ("search_b2", None),
+                                        ("search_b4", None)])
+def test_topk_search_recall(env, name, chunk):
     """The search workload's generator at 60 000 keys and 32 queries: parity
     of the top-10 with the oracle, and recall against exact inner products
     of the unquantized vectors equal to the oracle's own (the sets may differ
     only at the 10th score)."""
     torch, tqm, wl = env
     w = wl.WORKLOADS[name].scaled(n=60000, nq=32)
-    _announce(f"topk recall {w.name} n={w.n} nq={w.nq} bits={w.bits}")
+    _announce(f"topk recall {w.name} n={w.n} nq={w.nq} bits={w.bits} chunk={chunk}")
     keys = wl.keys(w)
     queries = wl.queries(w)
-    found, ref = _check_topk(env, w.d, w.bits, keys, queries, 10, chunk=8192)
+    found, ref = _check_topk(env, w.d, w.bits, keys, queries, 10, chunk=chunk)
     exact = tq.exact_inner_products(queries[0], keys)
     exact_idx, _ = tq.topk(exact, 10)
     r_gpu = tq.recall_at_k(found[0], exact_idx)

@@ -1,0 +1,10 @@
+// Matrix-core scorer instantiations: four index bits, two float16 pieces per level, every K-step count.
+#include "score_mfma.h"
+
+namespace tqdev {
+
+hipError_t score_launch_two4(const ScoreArgs& a) { return score::launch_form<4, kTwoPiece>(a); }
+
+size_t score_lds_two4(int d) { return score::static_lds_form<4, kTwoPiece>(d); }
+
+}  // namespace tqdev

@@ -1,6 +1,8 @@
 // Running top-k of the search entry point ("TurboQuant digest", section 3:
 // brute-force scores, compared by recall): merges one chunk of scores per
-// query into that query's list of the k best keys so far.
+// query into that query's list of the k best keys so far.  The chunk holds
+// either consecutive keys (scores only) or (score, key) pairs, such as the
+// per-block lists of the matrix-core search kernel.
 //
 // One wave per query.  Lane j holds entry j of the list (best first: larger
 // score, then smaller key index).  The wave reads the chunk 64 scores at a
@@ -47,8 +49,9 @@ __device__ __forceinline__ int64_t from_prev(int64_t x) {
 }
 
 __global__ void __launch_bounds__(64 * kWavesPerBlock)
-topk_merge_kernel(const float* __restrict__ chunk, int64_t nq, int64_t csize, int64_t c0, int k,
-                  float* __restrict__ list_s, int64_t* __restrict__ list_i, int last,
+topk_merge_kernel(const float* __restrict__ chunk, const int64_t* __restrict__ chunk_i, int64_t nq,
+                  int64_t csize, int64_t c0, int k, float* __restrict__ list_s, int64_t* __restrict__ list_i,
+                  int last,
                   float* __restrict__ out_s, int64_t* __restrict__ out_i) {
   const int lane = threadIdx.x & 63;
   const int64_t q = int64_t(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
@@ -69,11 +72,12 @@ topk_merge_kernel(const float* __restrict__ chunk, int64_t nq, int64_t csize, in
     ti = read_lane(li, k - 1);
   }
   const float* row = chunk + q * csize;
+  const int64_t* row_i = chunk_i ? chunk_i + q * csize : nullptr;
   for (int64_t b = 0; b < csize; b += 64) {
     const int64_t t = b + lane;
     const bool in = t < csize;
     const float s = in ? row[t] : -INFINITY;
-    const int64_t idx = in ? c0 + t : kNoIndex;
+    const int64_t idx = !in ? kNoIndex : row_i ? row_i[t] : c0 + t;
     uint64_t mask = __ballot(better(s, idx, ts, ti));
     while (mask) {
       const int j = __ffsll(static_cast<unsigned long long>(mask)) - 1;
@@ -114,15 +118,29 @@ topk_merge_kernel(const float* __restrict__ chunk, int64_t nq, int64_t csize, in
   }
 }
 
+__global__ void fill_u32_kernel(unsigned int* __restrict__ p, int64_t n, unsigned int v) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
 }  // namespace
 
-hipError_t launch_topk_merge(const float* chunk, int64_t nq, int64_t csize, int64_t c0, int k, float* list_s,
-                             int64_t* list_i, bool last, float* out_s, int64_t* out_i, hipStream_t stream) {
+hipError_t launch_fill_u32(unsigned int* p, int64_t n, unsigned int v, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_merge(const float* chunk, const int64_t* chunk_i, int64_t nq, int64_t csize, int64_t c0,
+                             int k, float* list_s, int64_t* list_i, bool last, float* out_s, int64_t* out_i,
+                             hipStream_t stream) {
   if (k < 1 || k > kTopkMax) return hipErrorInvalidValue;
   const int64_t blocks = (nq + kWavesPerBlock - 1) / kWavesPerBlock;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(topk_merge_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(64 * kWavesPerBlock), 0, stream,
-                     chunk, nq, csize, c0, k, list_s, list_i, last ? 1 : 0, out_s, out_i);
+                     chunk, chunk_i, nq, csize, c0, k, list_s, list_i, last ? 1 : 0, out_s, out_i);
   return hipGetLastError();
 }
 

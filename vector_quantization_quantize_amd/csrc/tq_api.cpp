@@ -184,6 +184,8 @@ int finish_init(tq_ctx* h) {
   if (hipDeviceGetAttribute(&h->cus, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess ||
       h->cus <= 0)
     return TQ_EHIP;
+  if (hipDeviceGetAttribute(&h->lds_per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, h->device) != hipSuccess)
+    return TQ_EHIP;
   for (int i = 0; i < tqdev::kMaxLevels; ++i) {
     h->cb.c[i] = i < h->levels ? h->centroids[i] : 0.0f;
     h->cb.t[i] = i + 1 < h->levels ? h->thresholds[i] : INFINITY;
@@ -431,11 +433,27 @@ int tq_logits(tq_handle h, const float* queries, int64_t groups, int64_t nq, con
 
 namespace {
 
-// Keys scored per chunk by the search entry point: scores of one chunk for
-// all nq queries stay within 64 Mi floats (about the size of the MALL); the
-// general scorer, which spreads only over keys, gets at least 65536 keys
-// per chunk to fill the GPU.  TQ_TOPK_CHUNK=<keys> overrides it (tests use
-// it to force many chunks).
+// Search entry point, two forms:
+//  * fused: the matrix-core scorer keeps each query's k best keys per block
+//    (no score matrix is written), then one merge pass combines the blocks'
+//    lists.  Used whenever the matrix-core scorer is (many queries, d <= 256)
+//    and the lists fit in LDS.  The blocks that walk one query's keys share
+//    the best k-th score any of them has found (a lower bound of the k-th
+//    best overall), so that far fewer keys enter a list only to be pushed
+//    out again.
+//  * chunked: score a chunk of keys for all queries into the workspace, merge
+//    it into running lists, repeat.
+// TQ_TOPK_CHUNK=<keys> forces the chunked form with that chunk size (tests
+// use it to cover many chunks).
+bool topk_fused(const tq_ctx* h, int64_t groups, int64_t nq, int64_t n, int32_t k) {
+  if (std::getenv("TQ_TOPK_CHUNK")) return false;
+  return n > 0 && groups <= 65535 && pick_scorer(h, nq) == Scorer::kMfma && tqdev::score_topk_mfma_supported(h, n, k);
+}
+
+// Keys scored per chunk by the chunked form: scores of one chunk for all nq
+// queries stay within 64 Mi floats (about the size of the MALL); the general
+// scorer, which spreads only over keys, gets at least 65536 keys per chunk
+// to fill the GPU.
 int64_t topk_chunk(const tq_ctx* h, int64_t nq, int64_t n) {
   int64_t c = (int64_t(64) << 20) / (nq > 0 ? nq : 1);
   if (pick_scorer(h, nq) == Scorer::kGeneral && c < 65536) c = 65536;
@@ -447,18 +465,36 @@ int64_t topk_chunk(const tq_ctx* h, int64_t nq, int64_t n) {
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// chunked: chunk [nq][c] scores, running lists [nq][k], vw of one group;
+// fused: block lists [groups][nq][splits][k] (part_s, part_i), vw of all
+// groups, shared bounds [groups][nq] (bound)
 struct TopkWorkspace {
-  size_t chunk, list_s, list_i, vw, total;
+  bool fused;
+  int64_t splits;
+  size_t chunk, list_s, list_i, vw, bound, total;
 };
 
-TopkWorkspace topk_layout(const tq_ctx* h, int64_t nq, int64_t n, int32_t k) {
+TopkWorkspace topk_layout(const tq_ctx* h, int64_t groups, int64_t nq, int64_t n, int32_t k) {
   TopkWorkspace w{};
+  const size_t vw_row = size_t(tqdev::vw_stride(h->d)) * sizeof(float);
+  w.fused = topk_fused(h, groups, nq, n, k);
+  if (w.fused) {
+    w.splits = tqdev::score_topk_mfma_splits(h, groups, nq, n);
+    const size_t entries = size_t(groups) * size_t(nq) * size_t(w.splits) * size_t(k);
+    w.chunk = 0;
+    w.list_s = 0;
+    w.list_i = align256(entries * sizeof(float));
+    w.vw = w.list_i + align256(entries * sizeof(int64_t));
+    w.bound = w.vw + align256(size_t(groups) * size_t(nq) * vw_row);
+    w.total = w.bound + align256(size_t(groups) * size_t(nq) * sizeof(unsigned int));
+    return w;
+  }
   const int64_t c = topk_chunk(h, nq, n);
   w.chunk = 0;
   w.list_s = align256(size_t(nq) * size_t(c) * sizeof(float));
   w.list_i = w.list_s + align256(size_t(nq) * size_t(k) * sizeof(float));
   w.vw = w.list_i + align256(size_t(nq) * size_t(k) * sizeof(int64_t));
-  w.total = w.vw + align256(size_t(nq) * size_t(tqdev::vw_stride(h->d)) * sizeof(float));
+  w.total = w.vw + align256(size_t(nq) * vw_row);
   return w;
 }
 
@@ -468,7 +504,7 @@ extern "C" {
 
 size_t tq_logits_topk_workspace_size(tq_handle h, int64_t groups, int64_t nq, int64_t n, int32_t k) {
   if (!h || groups < 0 || nq < 0 || n < 0 || k < 1 || k > tqdev::kTopkMax) return 0;
-  return topk_layout(h, nq, n, k).total;
+  return topk_layout(h, groups, nq, n, k).total;
 }
 
 int tq_logits_topk(tq_handle h, const float* queries, int64_t groups, int64_t nq, const uint32_t* codes,
@@ -480,25 +516,38 @@ int tq_logits_topk(tq_handle h, const float* queries, int64_t groups, int64_t nq
   if (!queries || !top_idx || !top_scores || !workspace) return TQ_EINVAL;
   if (n > 0 && (!codes || !signs || !norms || !rnorms)) return TQ_EINVAL;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return TQ_EINVAL;
-  const TopkWorkspace lay = topk_layout(h, nq, n, k);
+  const TopkWorkspace lay = topk_layout(h, groups, nq, n, k);
   if (workspace_bytes < lay.total) return TQ_EINVAL;
   if (check_device(h) != TQ_OK) return TQ_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
-  float* chunk = reinterpret_cast<float*>(ws + lay.chunk);
   float* list_s = reinterpret_cast<float*>(ws + lay.list_s);
   int64_t* list_i = reinterpret_cast<int64_t*>(ws + lay.list_i);
   float* vw = reinterpret_cast<float*>(ws + lay.vw);
+  hipError_t e = hipSuccess;
+  if (lay.fused) {
+    // every group at once: query transform, bounds to -inf, per-block lists,
+    // one merge
+    unsigned int* bound = reinterpret_cast<unsigned int*>(ws + lay.bound);
+    if ((e = tqdev::launch_query_prep(h, queries, groups * nq, vw, s)) != hipSuccess) return TQ_EHIP;
+    if ((e = tqdev::launch_fill_u32(bound, groups * nq, tqdev::kBoundEmpty, s)) != hipSuccess) return TQ_EHIP;
+    e = tqdev::launch_score_topk_mfma(h, vw, groups, nq, codes, signs, norms, rnorms, n, n, k, bound, list_s, list_i,
+                                      s);
+    if (e != hipSuccess) return TQ_EHIP;
+    e = tqdev::launch_topk_merge(list_s, list_i, groups * nq, lay.splits * k, 0, k, nullptr, nullptr, true,
+                                 top_scores, top_idx, s);
+    return e == hipSuccess ? TQ_OK : TQ_EHIP;
+  }
+  float* chunk = reinterpret_cast<float*>(ws + lay.chunk);
   const Scorer sc = pick_scorer(h, nq);
   const int64_t c = topk_chunk(h, nq, n);
   const int64_t cw = int64_t(h->code_bits) * h->words;  // code words per key
-  hipError_t e = hipSuccess;
   for (int64_t g = 0; g < groups && e == hipSuccess; ++g) {
     const float* qg = queries + g * nq * h->d;
     float* og = top_scores + g * nq * k;
     int64_t* oi = top_idx + g * nq * k;
     if (n == 0) {  // no keys: every entry is empty
-      e = tqdev::launch_topk_merge(chunk, nq, 0, 0, k, list_s, list_i, true, og, oi, s);
+      e = tqdev::launch_topk_merge(chunk, nullptr, nq, 0, 0, k, list_s, list_i, true, og, oi, s);
       continue;
     }
     if (sc != Scorer::kLut && (e = tqdev::launch_query_prep(h, qg, nq, vw, s)) != hipSuccess) break;
@@ -518,7 +567,7 @@ int tq_logits_topk(tq_handle h, const float* queries, int64_t groups, int64_t nq
           e = tqdev::launch_logits_v1(h, vw, 1, nq, cg, sg, norms + key0, rnorms + key0, ce, chunk, s);
       }
       if (e != hipSuccess) break;
-      e = tqdev::launch_topk_merge(chunk, nq, ce, c0, k, list_s, list_i, c0 + ce >= n, og, oi, s);
+      e = tqdev::launch_topk_merge(chunk, nullptr, nq, ce, c0, k, list_s, list_i, c0 + ce >= n, og, oi, s);
     }
   }
   return e == hipSuccess ? TQ_OK : TQ_EHIP;

@@ -53,6 +53,7 @@ struct tq_ctx {
   int d = 0, bits = 0, code_bits = 0, levels = 0, words = 0;
   int device = -1;
   int cus = 0;  // compute units of the device
+  int lds_per_block = 0;  // bytes of LDS one workgroup may use
   // host copies (float32), row-major d x d
   std::vector<float> pi, g, centroids, thresholds;
   // device tables
@@ -94,7 +95,8 @@ hipError_t launch_logits_lut128(const tq_ctx* h, const float* queries, int64_t g
 
 // also requires 16-byte aligned keys and outputs (outputs are written as
 // whole 16-byte rows)
-// matrix-core scorer for many queries (d <= 256); vw from launch_query_prep
+// matrix-core scorer for many queries (d <= 256; one index bit needs a
+// symmetric level set); vw from launch_query_prep
 bool score_mfma_supported(const tq_ctx* h);
 constexpr int64_t kScoreMfmaMinQueries = 16;  // below this the lookup-table scorer is used
 hipError_t launch_score_mfma(const tq_ctx* h, const float* vw, int64_t groups, int64_t nq, const uint32_t* codes,
@@ -113,12 +115,74 @@ hipError_t launch_dequant_mfma128(const tq_ctx* h, const uint32_t* codes, const 
 // TQ_KERNELS=ref selects the straightforward kernels everywhere (A/B checks)
 bool force_reference_kernels();
 
-// search: merge one chunk of scores ([nq][csize], keys c0 ..) into the running
-// lists of the k best keys per query ([nq][k]); the last chunk writes the
-// outputs instead (index -1, score -inf past the keys seen)
+// search: merge one chunk of scores ([nq][csize], keys c0 .. or, with
+// chunk_i, the keys chunk_i holds; INT64_MAX marks an empty entry) into the
+// running lists of the k best keys per query ([nq][k]); the last chunk writes
+// the outputs instead (index -1, score -inf past the keys seen)
 constexpr int kTopkMax = 64;
-hipError_t launch_topk_merge(const float* chunk, int64_t nq, int64_t csize, int64_t c0, int k, float* list_s,
-                             int64_t* list_i, bool last, float* out_s, int64_t* out_i, hipStream_t stream);
+hipError_t launch_topk_merge(const float* chunk, const int64_t* chunk_i, int64_t nq, int64_t csize, int64_t c0,
+                             int k, float* list_s, int64_t* list_i, bool last, float* out_s, int64_t* out_i,
+                             hipStream_t stream);
+
+// Forms of the level values in the matrix-core scorer: sign (one index bit,
+// symmetric levels: c[1] times +-1), one float16 piece (sigma c[level], at
+// most two magnitudes), two float16 pieces (2^10 c[level], hi and lo).
+enum { kSignForm = 0, kOnePiece = 1, kTwoPiece = 2 };
+struct ScoreForm {
+  float val[kMaxLevels];  // one piece: sigma c[level]; two pieces: 2^10 c[level]
+  float lambda;           // w rows are scaled lambda times the v rows
+  float gamma;            // score = gamma / s_R * u for the row scale s_R
+};
+// one launch of the matrix-core scorer (scores form, or search form with topk)
+struct ScoreArgs {
+  const tq_ctx* h;
+  const float* vw;
+  int64_t groups, nq;
+  const uint32_t* codes;
+  const uint32_t* signs;
+  const float* norms;
+  const float* rnorms;
+  int64_t n;           // keys scored per group
+  int64_t key_stride;  // keys between groups in the packed arrays
+  float* scores;       // scores form: [groups][nq][n]
+  bool topk;         // search form
+  float* part_s;     // search form: [groups][nq][splits][k]
+  int64_t* part_i;
+  int k;
+  unsigned int* bound;  // search form, optional: [groups][nq] shared bounds, set to kBoundEmpty first
+  ScoreForm form;
+  int64_t qtiles, splits, tiles_per_block;  // grid (qtiles, splits, groups)
+  hipStream_t stream;
+};
+inline size_t score_list_bytes(int k) { return size_t(128) * size_t(k) * (sizeof(float) + sizeof(int)); }
+// per form (one translation unit each): launch, and the search kernel's
+// static LDS bytes for dimension d
+hipError_t score_launch_sign(const ScoreArgs& a);
+hipError_t score_launch_one2(const ScoreArgs& a);
+hipError_t score_launch_two2(const ScoreArgs& a);
+hipError_t score_launch_two3(const ScoreArgs& a);
+hipError_t score_launch_two4(const ScoreArgs& a);
+size_t score_lds_sign(int d);
+size_t score_lds_one2(int d);
+size_t score_lds_two2(int d);
+size_t score_lds_two3(int d);
+size_t score_lds_two4(int d);
+
+// search form of the matrix-core scorer: per block, the k best keys of each
+// of its rows ([groups][nq][splits][k] scores and keys); merged afterwards
+// with launch_topk_merge (csize = splits * k)
+// Keys n of each group are scored (groups key_stride apart).  bound, when
+// given ([groups][nq], each set to kBoundEmpty beforehand), lets the blocks
+// that walk one row's keys share the best k-th score found so far.
+constexpr unsigned int kBoundEmpty = 0x007FFFFFu;  // -inf in the order-preserving encoding
+bool score_topk_mfma_supported(const tq_ctx* h, int64_t n, int k);
+int64_t score_topk_mfma_splits(const tq_ctx* h, int64_t groups, int64_t nq, int64_t n);
+hipError_t launch_score_topk_mfma(const tq_ctx* h, const float* vw, int64_t groups, int64_t nq,
+                                  const uint32_t* codes, const uint32_t* signs, const float* norms,
+                                  const float* rnorms, int64_t n, int64_t key_stride, int k, unsigned int* bound,
+                                  float* part_s, int64_t* part_i, hipStream_t stream);
+// fill n words with a value (stream-ordered; no memset node in graphs)
+hipError_t launch_fill_u32(unsigned int* p, int64_t n, unsigned int v, hipStream_t stream);
 
 hipError_t launch_dequant_v1(const tq_ctx* h, const uint32_t* codes, const float* norms, int64_t n,
                              float* khat, hipStream_t stream);
