@@ -139,10 +139,12 @@ def search_topk(name, seed, k=10, reps=3, recall_queries=64):
     scores = w.groups * w.nq * w.n
     kp = (w.d + 15) // 16 * 16
     # algorithmic work per score: d level products and d signed adds (4d
-    # flops); the matrix-core scorer runs three f16 passes over K = d
-    # rounded up to 16
+    # flops); the matrix-core scorer runs f16 passes over K = d rounded up
+    # to 16: one for the signs plus one for the level values when they fit
+    # one float16 piece (one or two index bits), two otherwise
+    passes = 2 if w.bits <= 3 else 3
     useful = 4.0 * w.d * scores / (ms * 1e-3) / 1e12
-    raw = 3 * 2.0 * kp * scores / (ms * 1e-3) / 1e12
+    raw = passes * 2.0 * kp * scores / (ms * 1e-3) / 1e12
     tqm.tq_destroy(h)
     return {"workload": f"{w.name}: {w.description}", "keys": w.n * w.groups, "queries": w.nq * w.groups, "d": w.d,
             "bits": w.bits, "k": k, "ms": round(ms, 3), "scores_per_s": scores / (ms * 1e-3),

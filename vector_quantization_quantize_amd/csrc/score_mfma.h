@@ -416,8 +416,9 @@ score_mfma_kernel(const float* __restrict__ vw, int64_t vw_stride, int64_t vw_ha
           // entries ahead of the candidate: u at least as high (placeholders
           // hold -inf, below any candidate)
           const int pos = __popcll(__ballot(in && ls >= s));
-          const float ps = __shfl_up(ls, 1);
-          const int pi = __shfl_up(li, 1);
+          // each entry from the lane before (a whole-wave shift by one lane)
+          const float ps = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, ls), 0x138, 0xF, 0xF, false));
+          const int pi = __builtin_amdgcn_update_dpp(0, li, 0x138, 0xF, 0xF, false);
           const float ns = lane == pos ? s : lane > pos ? ps : ls;
           const int ni = lane == pos ? key_base + (j & 31) : lane > pos ? pi : li;
           if (in && lane >= pos) {
@@ -432,7 +433,7 @@ score_mfma_kernel(const float* __restrict__ vw, int64_t vw_stride, int64_t vw_ha
     }
     if constexpr (kTopk) {
       const int64_t done = tile - t0 + 1;
-      if (bound && (done & (done < 64 ? done - 1 : 63)) == 0) sync_bounds();
+      if (bound && (done & (done < 16 ? done - 1 : 15)) == 0) sync_bounds();
     }
     if constexpr (Fm::kBufs == 1) {
       __syncthreads();  // the tile's rows are no longer read
