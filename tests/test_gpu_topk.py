@@ -93,6 +93,9 @@ def test_topk_matches_oracle(env, d, bits, groups, nq, n, k, chunk):
     (100, 2, 3, 17, 300, 1),      # top-1, sign form, three groups
     (64, 2, 1, 40, 40000, 5),     # many blocks per query tile
     (48, 4, 1, 300, 5000, 32),    # three query tiles, three index bits
+    (1536, 4, 1, 40, 3000, 10),   # tiled form (d > 256), three index bits
+    (300, 2, 2, 20, 1000, 16),    # tiled form, sign form, two groups
+    (257, 3, 1, 130, 700, 64),    # tiled form at its smallest d, k at its maximum, two query tiles
 ])
 def test_topk_fused_matches_oracle(env, d, bits, groups, nq, n, k):
     _announce(f"topk fused d={d} bits={bits} groups={groups} nq={nq} n={n} k={k}")
@@ -151,6 +154,10 @@ def test_topk_search_recall(env, name, chunk):
     (33, 4, 1, 20, 500),     # d not a multiple of 16
     (2, 2, 1, 16, 40),       # smallest d
     (100, 3, 3, 17, 300),
+    (300, 2, 1, 20, 300),    # tiled form (d > 256): sign form, ragged key tile
+    (1536, 4, 1, 130, 200),  # tiled form, two query tiles
+    (257, 5, 2, 17, 150),    # tiled form at its smallest d, four index bits, two groups
+    (1024, 3, 1, 16, 129),   # tiled form, one float16 piece per level
 ])
 def test_matrix_core_scorer_every_score(env, d, bits, groups, nq, n):
     """Many queries per group go to the matrix-core scorer: every score of

@@ -1,5 +1,6 @@
 // Matrix-core scorer: choice of form, grid shape and per-form dispatch (the
-// kernels are in score_mfma.h, instantiated by score_mfma_<form>.hip).
+// kernels are in score_mfma.h, d <= 256, and score_gemm.h, d > 256,
+// instantiated by score_mfma_<form>.hip).
 #include <cstdint>
 
 #include "tq_internal.h"
@@ -37,6 +38,9 @@ int64_t pick_splits(int cus, int64_t qtiles, int64_t groups, int64_t ntiles) {
   return (ntiles + tpb - 1) / tpb;
 }
 
+// keys per tile: 32 in the register form, 128 in the tiled form
+int64_t tile_keys(const tq_ctx* h) { return h->d >= kScoreGemmMinD ? 128 : kTileKeys; }
+
 int form_of(const tq_ctx* h) {
   if (h->code_bits == 1) return kSignForm;  // symmetric: checked by score_mfma_supported
   if (h->code_bits == 2 && h->dqt.two_pass) return kOnePiece;
@@ -70,6 +74,15 @@ ScoreForm form_params(const tq_ctx* h) {
 }
 
 hipError_t dispatch(const ScoreArgs& a) {
+  if (a.h->d >= kScoreGemmMinD) {
+    switch (a.h->code_bits) {
+      case 1: return score_gemm_launch_sign(a);
+      case 2: return form_of(a.h) == kOnePiece ? score_gemm_launch_one2(a) : score_gemm_launch_two2(a);
+      case 3: return score_gemm_launch_two3(a);
+      case 4: return score_gemm_launch_two4(a);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (a.h->code_bits) {
     case 1: return score_launch_sign(a);
     case 2: return form_of(a.h) == kOnePiece ? score_launch_one2(a) : score_launch_two2(a);
@@ -80,6 +93,15 @@ hipError_t dispatch(const ScoreArgs& a) {
 }
 
 size_t static_lds(const tq_ctx* h) {
+  if (h->d >= kScoreGemmMinD) {
+    switch (h->code_bits) {
+      case 1: return score_gemm_lds_sign();
+      case 2: return form_of(h) == kOnePiece ? score_gemm_lds_one2() : score_gemm_lds_two2();
+      case 3: return score_gemm_lds_two3();
+      case 4: return score_gemm_lds_two4();
+      default: return SIZE_MAX;
+    }
+  }
   switch (h->code_bits) {
     case 1: return score_lds_sign(h->d);
     case 2: return form_of(h) == kOnePiece ? score_lds_one2(h->d) : score_lds_two2(h->d);
@@ -104,17 +126,25 @@ ScoreArgs make_args(const tq_ctx* h, const float* vw, int64_t groups, int64_t nq
   a.key_stride = n;
   a.form = form_params(h);
   a.qtiles = (nq + 127) / 128;
-  const int64_t ntiles = (n + kTileKeys - 1) / kTileKeys;
+  const int64_t tk = tile_keys(h);
+  const int64_t ntiles = (n + tk - 1) / tk;
   a.splits = pick_splits(h->cus, a.qtiles, groups, ntiles);
   a.tiles_per_block = (ntiles + a.splits - 1) / a.splits;
   a.stream = stream;
+  if (h->d >= kScoreGemmMinD) {
+    // float16 query rows and row factors follow the vw rows
+    const int64_t rows = groups * nq;
+    char* base = reinterpret_cast<char*>(const_cast<float*>(vw)) + score_vw_bytes(h->d, rows);
+    a.qa = base;
+    a.row_f = reinterpret_cast<float*>(base + score_qa_bytes(h->d, groups, nq));
+  }
   return a;
 }
 
 }  // namespace
 
 bool score_mfma_supported(const tq_ctx* h) {
-  if (h->d > 256 || h->code_bits < 1 || h->code_bits > 4) return false;
+  if (h->code_bits < 1 || h->code_bits > 4) return false;
   return h->code_bits > 1 || h->symmetric;
 }
 
@@ -137,7 +167,8 @@ bool score_topk_mfma_supported(const tq_ctx* h, int64_t n, int k) {
 
 int64_t score_topk_mfma_splits(const tq_ctx* h, int64_t groups, int64_t nq, int64_t n) {
   const int64_t qtiles = (nq + 127) / 128;
-  const int64_t ntiles = (n + kTileKeys - 1) / kTileKeys;
+  const int64_t tk = tile_keys(h);
+  const int64_t ntiles = (n + tk - 1) / tk;
   return pick_splits(h->cus, qtiles, groups, ntiles);
 }
 

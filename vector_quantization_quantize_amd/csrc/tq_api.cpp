@@ -400,7 +400,7 @@ int tq_quantize(tq_handle h, const void* keys, int32_t key_dtype, int64_t n, int
 
 size_t tq_logits_workspace_size(tq_handle h, int64_t groups, int64_t nq) {
   if (!h || groups < 0 || nq < 0) return 0;
-  return size_t(groups) * size_t(nq) * size_t(tqdev::vw_stride(h->d)) * sizeof(float);
+  return tqdev::score_prep_bytes(h->d, groups, nq);
 }
 
 int tq_logits(tq_handle h, const float* queries, int64_t groups, int64_t nq, const uint32_t* codes,
@@ -476,7 +476,6 @@ struct TopkWorkspace {
 
 TopkWorkspace topk_layout(const tq_ctx* h, int64_t groups, int64_t nq, int64_t n, int32_t k) {
   TopkWorkspace w{};
-  const size_t vw_row = size_t(tqdev::vw_stride(h->d)) * sizeof(float);
   w.fused = topk_fused(h, groups, nq, n, k);
   if (w.fused) {
     w.splits = tqdev::score_topk_mfma_splits(h, groups, nq, n);
@@ -485,7 +484,7 @@ TopkWorkspace topk_layout(const tq_ctx* h, int64_t groups, int64_t nq, int64_t n
     w.list_s = 0;
     w.list_i = align256(entries * sizeof(float));
     w.vw = w.list_i + align256(entries * sizeof(int64_t));
-    w.bound = w.vw + align256(size_t(groups) * size_t(nq) * vw_row);
+    w.bound = w.vw + tqdev::score_prep_bytes(h->d, groups, nq);
     w.total = w.bound + align256(size_t(groups) * size_t(nq) * sizeof(unsigned int));
     return w;
   }
@@ -494,7 +493,7 @@ TopkWorkspace topk_layout(const tq_ctx* h, int64_t groups, int64_t nq, int64_t n
   w.list_s = align256(size_t(nq) * size_t(c) * sizeof(float));
   w.list_i = w.list_s + align256(size_t(nq) * size_t(k) * sizeof(float));
   w.vw = w.list_i + align256(size_t(nq) * size_t(k) * sizeof(int64_t));
-  w.total = w.vw + align256(size_t(nq) * vw_row);
+  w.total = w.vw + tqdev::score_prep_bytes(h->d, 1, nq);
   return w;
 }
 

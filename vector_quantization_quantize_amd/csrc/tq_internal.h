@@ -150,6 +150,8 @@ struct ScoreArgs {
   int64_t* part_i;
   int k;
   unsigned int* bound;  // search form, optional: [groups][nq] shared bounds, set to kBoundEmpty first
+  void* qa;             // d > 256: float16 query rows [groups * nq][2 kp] (kp = d rounded up to 16)
+  float* row_f;         // d > 256: score factor per query row
   ScoreForm form;
   int64_t qtiles, splits, tiles_per_block;  // grid (qtiles, splits, groups)
   hipStream_t stream;
@@ -167,6 +169,18 @@ size_t score_lds_one2(int d);
 size_t score_lds_two2(int d);
 size_t score_lds_two3(int d);
 size_t score_lds_two4(int d);
+// d > 256: the tiled form (both operands through LDS), same forms
+hipError_t score_gemm_launch_sign(const ScoreArgs& a);
+hipError_t score_gemm_launch_one2(const ScoreArgs& a);
+hipError_t score_gemm_launch_two2(const ScoreArgs& a);
+hipError_t score_gemm_launch_two3(const ScoreArgs& a);
+hipError_t score_gemm_launch_two4(const ScoreArgs& a);
+size_t score_gemm_lds_sign();
+size_t score_gemm_lds_one2();
+size_t score_gemm_lds_two2();
+size_t score_gemm_lds_two3();
+size_t score_gemm_lds_two4();
+constexpr int kScoreGemmMinD = 257;  // from this d on the tiled form runs
 
 // search form of the matrix-core scorer: per block, the k best keys of each
 // of its rows ([groups][nq][splits][k] scores and keys); merged afterwards
@@ -191,5 +205,20 @@ hipError_t launch_dequant_v1(const tq_ctx* h, const uint32_t* codes, const float
 // stride between queries: v at q*vw_stride, w at q*vw_stride + vw_half
 inline int64_t vw_half(int d) { return (int64_t(d) + 63) / 64 * 64; }
 inline int64_t vw_stride(int d) { return 2 * vw_half(d); }
+
+// Workspace of the query transform for `rows` query rows: the vw rows, then
+// (d > 256, for the tiled matrix-core scorer) float16 query rows and one
+// score factor per row.
+inline size_t ws_align(size_t x) { return (x + 255) / 256 * 256; }
+inline size_t score_vw_bytes(int d, int64_t rows) { return ws_align(size_t(rows) * size_t(vw_stride(d)) * 4); }
+// float16 rows for `groups` groups of nq queries, padded to 128-row tiles
+inline size_t score_qa_bytes(int d, int64_t groups, int64_t nq) {
+  return ws_align(size_t(groups) * size_t((nq + 127) / 128 * 128) * size_t(2 * ((d + 15) / 16 * 16)) * 2);
+}
+inline size_t score_prep_bytes(int d, int64_t groups, int64_t nq) {
+  const int64_t rows = groups * nq;
+  return score_vw_bytes(d, rows) +
+         (d >= kScoreGemmMinD ? score_qa_bytes(d, groups, nq) + ws_align(size_t(rows) * 4) : 0);
+}
 
 }  // namespace tqdev
