@@ -9,15 +9,15 @@ namespace tqdev {
 namespace {
 
 constexpr int kTileKeys = 32;
-constexpr int kBlocksPerCu = 2;
+// resident blocks per CU: the register form runs 2 of 4 waves, the tiled
+// form 1 of 8
+int blocks_per_cu(const tq_ctx* h) { return h->d >= kScoreGemmMinD ? 1 : 2; }
 constexpr float kCScale = 1024.0f;
 
 // Blocks of key tiles per query tile: enough blocks to fill the resident
-// slots (kBlocksPerCu per CU), with the total a close fit to a whole number
-// of rounds of slots (a last round that holds a few blocks costs as much as
-// a full one).
-int64_t pick_splits(int cus, int64_t qtiles, int64_t groups, int64_t ntiles) {
-  const int64_t slots = int64_t(kBlocksPerCu) * cus;
+// slots, with the total a close fit to a whole number of rounds of slots (a
+// last round that holds a few blocks costs as much as a full one).
+int64_t pick_splits(int64_t slots, int64_t qtiles, int64_t groups, int64_t ntiles) {
   const int64_t per = qtiles * groups;
   int64_t lo = (slots + per - 1) / per;
   lo = lo < ntiles ? lo : ntiles;
@@ -128,7 +128,7 @@ ScoreArgs make_args(const tq_ctx* h, const float* vw, int64_t groups, int64_t nq
   a.qtiles = (nq + 127) / 128;
   const int64_t tk = tile_keys(h);
   const int64_t ntiles = (n + tk - 1) / tk;
-  a.splits = pick_splits(h->cus, a.qtiles, groups, ntiles);
+  a.splits = pick_splits(int64_t(blocks_per_cu(h)) * h->cus, a.qtiles, groups, ntiles);
   a.tiles_per_block = (ntiles + a.splits - 1) / a.splits;
   a.stream = stream;
   if (h->d >= kScoreGemmMinD) {
@@ -169,7 +169,7 @@ int64_t score_topk_mfma_splits(const tq_ctx* h, int64_t groups, int64_t nq, int6
   const int64_t qtiles = (nq + 127) / 128;
   const int64_t tk = tile_keys(h);
   const int64_t ntiles = (n + tk - 1) / tk;
-  return pick_splits(h->cus, qtiles, groups, ntiles);
+  return pick_splits(int64_t(blocks_per_cu(h)) * h->cus, qtiles, groups, ntiles);
 }
 
 hipError_t launch_score_topk_mfma(const tq_ctx* h, const float* vw, int64_t groups, int64_t nq,
