@@ -4,8 +4,8 @@ oracle's top-k of its own scores on the same packed keys (rule in
 partial query quads, several groups and equal scores; recall against exact
 inner products on the search workload's generator.  Both forms: chunked
 (score chunks, then merge; forced by TQ_TOPK_CHUNK) and fused (the
-matrix-core scorer keeps per-block lists; taken for 16 or more queries with
-d <= 256 when no chunk size is forced).  Expected values come only from
+matrix-core scorer keeps per-block lists; taken for 16 or more queries when
+no chunk size is forced: register form for d <= 256, tiled form above).  Expected values come only from
 ``oracle``."""
 import os
 
@@ -124,15 +124,17 @@ def test_topk_equal_scores_in_index_order(env, nq, chunk):
             assert lst == sorted(lst)
 
 
-@pytest.mark.parametrize("name,chunk", [("search_b2", 8192), ("search_b4", 8192), ("search_b2", None),
-                                        ("search_b4", None)])
-def test_topk_search_recall(env, name, chunk):
-    """The search workload's generator at 60 000 keys and 32 queries: parity
-    of the top-10 with the oracle, and recall against exact inner products
-    of the unquantized vectors equal to the oracle's own (the sets may differ
-    only at the 10th score)."""
+@pytest.mark.parametrize("name,chunk,n", [("search_b2", 8192, 60000), ("search_b4", 8192, 60000),
+                                          ("search_b2", None, 60000), ("search_b4", None, 60000),
+                                          ("cone", None, 20000)])
+def test_topk_search_recall(env, name, chunk, n):
+    """The search workloads' generators (d = 200 anisotropic; d = 1536 cone,
+    which takes the tiled scorer) at n keys and 32 queries: parity of the
+    top-10 with the oracle, and recall against exact inner products of the
+    unquantized vectors equal to the oracle's own (the sets may differ only
+    at the 10th score)."""
     torch, tqm, wl = env
-    w = wl.WORKLOADS[name].scaled(n=60000, nq=32)
+    w = wl.WORKLOADS[name].scaled(n=n, nq=32)
     _announce(f"topk recall {w.name} n={w.n} nq={w.nq} bits={w.bits} chunk={chunk}")
     keys = wl.keys(w)
     queries = wl.queries(w)

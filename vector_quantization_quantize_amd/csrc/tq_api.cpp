@@ -238,7 +238,8 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 namespace {
 
 // Which scorer serves nq queries per group: the matrix-core kernel for many
-// queries (d <= 256), the lookup-table kernel for a few (d in (96, 128]),
+// queries (register form for d <= 256, tiled form above), the lookup-table
+// kernel for a few (d in (96, 128]),
 // else the general kernel (also for TQ_KERNELS=ref).
 enum class Scorer { kGeneral, kLut, kMfma };
 
@@ -436,7 +437,7 @@ namespace {
 // Search entry point, two forms:
 //  * fused: the matrix-core scorer keeps each query's k best keys per block
 //    (no score matrix is written), then one merge pass combines the blocks'
-//    lists.  Used whenever the matrix-core scorer is (many queries, d <= 256)
+//    lists.  Used whenever the matrix-core scorer is (many queries, any d)
 //    and the lists fit in LDS.  The blocks that walk one query's keys share
 //    the best k-th score any of them has found (a lower bound of the k-th
 //    best overall), so that far fewer keys enter a list only to be pushed
