@@ -39,9 +39,31 @@ Stages (page, section):
    unquantized vectors: recall@k is the shared fraction, and Recall@1@k the
    share of queries whose exact best key is among the k found.
 
+9. reconstruction with the correction: the score is linear in q
+   (<w, 2 beta - 1> = <G Pi q, 2 beta - 1> = <q, Pi^T G^T (2 beta - 1)>), so
+   one vector per key reproduces it for every query,
+       k_tilde = n * Pi^T ( c[idx] + rho * sqrt(pi/2) / d * G^T (2 beta - 1) )
+   ("TurboQuant deep review", error compensation section: the corrected
+   estimate is unbiased, and this is the vector it is the inner product
+   with).
+10. decode attention over a compressed cache: the cache holds key-value
+   pairs ("Why KV-cache compression works", section 2: the method quantizes
+   the KV cache; "TurboQuant tutorial", glossary: q asks, k identifies, v
+   carries the content).  Keys are scored with the stage-6 estimate;
+   values are stored with stage 1 only and read back by the stage-7
+   reconstruction (the QJL bit serves inner products with a query, which
+   a value never takes part in).  For each query
+       o = sum_t softmax_t(scale * s_t) * v_hat_t,
+   with the caller's scale (1/sqrt(d) in the usual attention) and every
+   stored token visible; also lse = log sum_t exp(scale * s_t).  With no
+   tokens o = 0 and lse = -inf.
+
 Packed layout (bit planes): ``codes[n][B][W]`` and ``signs[n][W]`` as
 uint32 with W = ceil(d / 32); bit p of the index of coordinate j is bit
 (j mod 32) of word (j div 32) of plane p (LSB first); padding bits are 0.
+Stored values use token blocks instead: ``vcodes[ceil(n/32)][B][32 W]``,
+where bit i of word (b, p, j) is bit p of the index of coordinate j of
+token 32 b + i; tokens past n and coordinates past d are 0.
 """
 from dataclasses import dataclass
 
@@ -133,6 +155,32 @@ def dequant_mse(params: Params, idx, norms):
     return np.asarray(norms, dtype=np.float64)[:, None] * (chat @ params.pi)
 
 
+def dequant_prod(params: Params, idx, beta, norms, rnorms):
+    """Stage 9: k_tilde = n Pi^T (c[idx] + rho sqrt(pi/2)/d G^T (2 beta - 1))
+    for each key (rows of the result)."""
+    chat = params.centroids[np.asarray(idx)]                  # (n, d)
+    signs = np.where(np.asarray(beta), 1.0, -1.0)             # (n, d)
+    scale = np.asarray(rnorms, dtype=np.float64) * QJL_CONST / params.d
+    corr = scale[:, None] * (signs @ params.g)                # row b: (G^T s_b)^T
+    return np.asarray(norms, dtype=np.float64)[:, None] * ((chat + corr) @ params.pi)
+
+
+def attention(key_params: Params, value_params: Params, queries, k_idx, k_beta, k_norms, k_rnorms, v_idx,
+              v_norms, scale):
+    """Stage 10: (o (m, d), lse (m,)) of m queries over n stored tokens."""
+    q = np.asarray(queries, dtype=np.float64)
+    m, n = q.shape[0], np.asarray(v_norms).shape[0]
+    if n == 0:
+        return np.zeros((m, value_params.d)), np.full(m, -np.inf)
+    s = float(scale) * scores(key_params, q, k_idx, k_beta, k_norms, k_rnorms)   # (m, n)
+    top = s.max(axis=1, keepdims=True)
+    e = np.exp(s - top)
+    total = e.sum(axis=1)
+    probs = e / total[:, None]
+    vhat = dequant_mse(value_params, v_idx, v_norms)          # (n, d)
+    return probs @ vhat, top[:, 0] + np.log(total)
+
+
 def topk(scores, k):
     """Stage 8: (indices, scores) of the k largest entries of each row of an
     (m, n) score matrix, best first; equal scores in ascending column order.
@@ -213,3 +261,32 @@ def pack(params: Params, qz: Quantized):
     """Packed buffers (codes, signs, norms fp32, rnorms fp32) of a batch."""
     return (pack_codes(qz.idx, params.code_bits), pack_bits(qz.beta),
             qz.norms.astype(np.float32), qz.rnorms.astype(np.float32))
+
+
+def pack_values(idx, code_bits):
+    """(n, d) value indices -> (ceil(n/32), B, 32 W) uint32 token blocks:
+    word (b, p, j) holds bit p of the indices of coordinate j for tokens
+    32 b .. 32 b + 31, token 32 b + i at bit i."""
+    idx = np.asarray(idx, dtype=np.int64)
+    n, d = idx.shape
+    nb = (n + 31) // 32
+    dp = 32 * words_per_plane(d)
+    padded = np.zeros((nb * 32, dp), dtype=np.int64)
+    padded[:n, :d] = idx
+    out = np.zeros((nb, code_bits, dp), dtype=np.uint32)
+    for b in range(nb):
+        block = padded[32 * b:32 * b + 32]                    # (32 tokens, dp)
+        for p in range(code_bits):
+            out[b, p, :] = pack_bits(((block >> p) & 1).T.astype(bool))[:, 0]
+    return out
+
+
+def unpack_values(vcodes, n, d):
+    """Inverse of pack_values: (n, d) indices."""
+    vcodes = np.asarray(vcodes, dtype=np.uint32)
+    nb, code_bits, dp = vcodes.shape
+    idx = np.zeros((nb * 32, dp), dtype=np.int64)
+    for p in range(code_bits):
+        bits = unpack_bits(vcodes[:, p, :].reshape(nb * dp, 1), 32)   # (nb*dp, 32 tokens)
+        idx |= bits.reshape(nb, dp, 32).transpose(0, 2, 1).reshape(nb * 32, dp).astype(np.int64) << p
+    return idx[:n, :d]

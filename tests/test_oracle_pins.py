@@ -469,3 +469,106 @@ def test_compare_topk_flags_planted_mistakes():
     assert not parity.compare_topk(far, fv, s, q, norms, k).ok()
     off = vals.copy(); off[0, 2] += 1.0
     assert not parity.compare_topk(idx, off, s, q, norms, k).ok()
+
+
+# ---------------------------------------------------------------------------
+# reconstruction with the correction, decode attention, value blocks
+# ---------------------------------------------------------------------------
+
+def test_dequant_prod_reproduces_every_score():
+    """Stage 9 is the vector whose inner product with any query is the
+    (separately pinned) stage-6 estimate: linearity of the score in q."""
+    pr = P.init(40, 4, 3)
+    rs = np.random.default_rng(21)
+    keys = rs.standard_normal((12, 40)) * 3.0
+    qs = rs.standard_normal((7, 40))
+    qz = tq.quantize(pr, keys)
+    kt = tq.dequant_prod(pr, qz.idx, qz.beta, qz.norms, qz.rnorms)
+    s = tq.scores(pr, qs, qz.idx, qz.beta, qz.norms, qz.rnorms)
+    assert np.allclose(qs @ kt.T, s, rtol=1e-12, atol=1e-12)
+
+
+def test_dequant_prod_unbiased_over_seeds():
+    """Averaged over seeds of (Pi, G), k_tilde estimates the key itself (the
+    zero-bias property, per coordinate within 4 standard errors)."""
+    d = 16
+    rs = np.random.default_rng(22)
+    key = rs.standard_normal((1, d))
+    est = []
+    for seed in range(1200):
+        pr = P.init(d, 2, seed)
+        qz = tq.quantize(pr, key)
+        est.append(tq.dequant_prod(pr, qz.idx, qz.beta, qz.norms, qz.rnorms)[0])
+    est = np.array(est)
+    sem = est.std(axis=0) / math.sqrt(len(est))
+    assert np.all(np.abs(est.mean(axis=0) - key[0]) < 4 * sem + 1e-12)
+
+
+def _attention_case(d=24, n=50, m=5, kbits=3, vbits=4, seed=23):
+    prk, prv = P.init(d, kbits, seed), P.init(d, vbits, seed + 1)
+    rs = np.random.default_rng(seed)
+    keys = rs.standard_normal((n, d)) * np.exp(0.5 * rs.standard_normal((n, 1)))
+    vals = rs.standard_normal((n, d))
+    qs = rs.standard_normal((m, d))
+    kz, vz = tq.quantize(prk, keys), tq.quantize(prv, vals)
+    return prk, prv, qs, kz, vz
+
+
+def test_attention_equals_library_sdpa():
+    """Stage 10 against torch's scaled_dot_product_attention (float64, CPU)
+    over the explicit reconstructions: keys k_tilde (stage 9), values v_hat
+    (stage 7); lse against scipy's logsumexp."""
+    import torch
+    from scipy.special import logsumexp
+    prk, prv, qs, kz, vz = _attention_case()
+    scale = 0.37
+    o, lse = tq.attention(prk, prv, qs, kz.idx, kz.beta, kz.norms, kz.rnorms, vz.idx, vz.norms, scale)
+    kt = tq.dequant_prod(prk, kz.idx, kz.beta, kz.norms, kz.rnorms)
+    vh = tq.dequant_mse(prv, vz.idx, vz.norms)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(qs)[None], torch.from_numpy(kt)[None], torch.from_numpy(vh)[None], scale=scale)[0].numpy()
+    assert np.allclose(o, ref, rtol=1e-10, atol=1e-12)
+    assert np.allclose(lse, logsumexp(scale * (qs @ kt.T), axis=1), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_special_cases():
+    """Closed forms: a zero query weighs every token alike (o = mean of the
+    reconstructed values, lse = log n); one token gives its value; a large
+    scale picks the best-scoring token; no tokens give o = 0, lse = -inf;
+    the order of the tokens does not matter."""
+    prk, prv, qs, kz, vz = _attention_case()
+    args = lambda sl: (kz.idx[sl], kz.beta[sl], kz.norms[sl], kz.rnorms[sl], vz.idx[sl], vz.norms[sl])
+    every = slice(None)
+    vh = tq.dequant_mse(prv, vz.idx, vz.norms)
+    o, lse = tq.attention(prk, prv, np.zeros((1, prk.d)), *args(every), 0.5)
+    assert np.allclose(o[0], vh.mean(axis=0), rtol=1e-12, atol=1e-12)
+    assert abs(lse[0] - math.log(len(vh))) < 1e-12
+    o, lse = tq.attention(prk, prv, qs, *args(slice(3, 4)), 0.5)
+    assert np.allclose(o, vh[3][None, :].repeat(len(qs), 0), rtol=1e-12, atol=1e-12)
+    s = tq.scores(prk, qs, kz.idx, kz.beta, kz.norms, kz.rnorms)
+    o, _ = tq.attention(prk, prv, qs, *args(every), 1e4)
+    assert np.allclose(o, vh[np.argmax(s, axis=1)], rtol=1e-9, atol=1e-9)
+    o, lse = tq.attention(prk, prv, qs, *args(slice(0, 0)), 0.5)
+    assert np.all(o == 0.0) and np.all(np.isneginf(lse))
+    perm = np.random.default_rng(5).permutation(len(vh))
+    o1, l1 = tq.attention(prk, prv, qs, *args(every), 0.5)
+    o2, l2 = tq.attention(prk, prv, qs, *args(perm), 0.5)
+    assert np.allclose(o1, o2, rtol=1e-12, atol=1e-12) and np.allclose(l1, l2, rtol=1e-12, atol=1e-12)
+
+
+def test_pack_values_bit_positions():
+    """Token-blocked value planes: token 33, coordinate 37, index 0b10 sets
+    bit 1 (33 mod 32) of word (block 1, plane 1, coordinate 37) and nothing
+    else; coordinates past d and tokens past n stay 0."""
+    idx = np.zeros((40, 50), dtype=np.int64)
+    idx[33, 37] = 2
+    v = tq.pack_values(idx, 2)
+    assert v.shape == (2, 2, 64)
+    assert v[1, 1, 37] == 2 and np.count_nonzero(v) == 1
+    full = np.full((40, 50), 3, dtype=np.int64)
+    v = tq.pack_values(full, 2)
+    assert np.all(v[0, :, :50] == 0xFFFFFFFF) and np.all(v[:, :, 50:] == 0)
+    assert np.all(v[1, :, :50] == 0xFF)               # tokens 32..39 only
+    rs = np.random.default_rng(3)
+    idx = rs.integers(0, 8, (77, 45))
+    assert np.array_equal(tq.unpack_values(tq.pack_values(idx, 3), 77, 45), idx)
