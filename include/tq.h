@@ -190,6 +190,46 @@ TQ_API int tq_logits_topk(tq_handle h, const float* queries, int64_t groups, int
 TQ_API int tq_dequant_mse(tq_handle h, const uint32_t* codes, const float* norms, int64_t n,
                    float* khat, void* stream);
 
+/* Value cache layout for tq_attention.  Values are quantized like keys
+ * (tq_quantize with the value handle; only codes and norms are kept: the
+ * attention reads values back through the stage-1 reconstruction) and their
+ * codes are regrouped into token blocks:
+ *   vcodes [groups][ceil(n/32)][B][32 W] uint32, bit i of word (b, p, j) =
+ *   bit p of the index of coordinate j of token 32 b + i
+ * (tokens past n and coordinates past d are 0).  One word then carries one
+ * coordinate of 32 tokens, which is what a weighted sum over tokens reads.
+ * codes: device, groups * n packed keys' codes [groups][n][B][W]; vcodes:
+ * device, as above.  Asynchronous on `stream`. */
+TQ_API int tq_pack_values(tq_handle h, const uint32_t* codes, int64_t groups, int64_t n, uint32_t* vcodes,
+                          void* stream);
+
+/* Bytes of device workspace tq_attention needs. */
+TQ_API size_t tq_attention_workspace_size(tq_handle hk, tq_handle hv, int64_t groups, int64_t nq, int64_t n);
+
+/* Decode attention over a compressed KV cache ("Why KV-cache compression
+ * works", section 2: the method compresses the key-value cache; "TurboQuant
+ * tutorial", glossary: queries, keys and values).  For each query of group
+ * g against the group's n stored tokens:
+ *   o   = sum_t softmax_t(scale * s_t) * v_hat_t,
+ *   lse = log sum_t exp(scale * s_t),
+ * s_t the asymmetric score of the query against key t (exactly as
+ * tq_logits computes it, with handle hk) and v_hat_t = n_t Pi^T c[idx_t] the
+ * stage-1 reconstruction of value t (handle hv: its rotation and levels;
+ * same d as hk, any bit width).  Every stored token is visible; `scale` is
+ * the caller's (1/sqrt(d) in the usual attention), any finite value.
+ * queries: device float [groups][nq][d]; kcodes, ksigns, knorms, krnorms:
+ * groups * n packed keys as for tq_logits; vcodes: token blocks from
+ * tq_pack_values; vnorms: device float [groups][n].  out: device float
+ * [groups][nq][d]; lse: device float [groups][nq] or NULL.  n = 0 gives
+ * o = 0 and lse = -inf.  workspace: device, at least
+ * tq_attention_workspace_size(hk, hv, groups, nq, n) bytes (it holds the
+ * score matrix), 256-byte aligned.  Asynchronous on `stream`. */
+TQ_API int tq_attention(tq_handle hk, tq_handle hv, const float* queries, int64_t groups, int64_t nq,
+                        const uint32_t* kcodes, const uint32_t* ksigns, const float* knorms,
+                        const float* krnorms, const uint32_t* vcodes, const float* vnorms, int64_t n,
+                        float scale, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
 /* Static string naming an error code. */
 TQ_API const char* tq_strerror(int code);
 

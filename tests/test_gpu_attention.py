@@ -1,0 +1,179 @@
+"""Decode attention over a compressed cache (tq_attention) and the value
+token blocks (tq_pack_values) against the oracle.
+
+Decode parity: keys and values are quantized by the oracle, and both sides
+read the same packed arrays.  Value blocks must match ``oracle.tq.pack_values``
+bit for bit.
+
+Attention tolerance (derived from the logit bar, since the pages fix no
+bar for attention):
+* every score may be off by e_t = 1e-3 ||q|| n_t; in softmax units that is
+  delta = |scale| max_t e_t;
+* each probability ratio then moves by at most exp(+-2 delta), so the sum of
+  |dp_t| is at most exp(2 delta) - 1;
+* hence |do_i| <= (exp(2 delta) - 1) max_t |v_hat_t,i| + eps;
+* eps = 2e-5 max_t ||v_hat_t|| covers the value pass's own rounding (22-bit
+  weights, level pieces, float32 sums and rotation);
+* lse moves by at most delta plus float32 rounding.
+
+Two cases make delta = 0 and so check the value pass tightly: zero queries
+(every score is exactly 0, uniform weights) and a single token.  Expected
+values come only from ``oracle``."""
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import tq
+from tests.test_gpu_parity import _announce, _cpu, _dev, _params
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import vector_quantization_quantize_amd as tqm
+    return torch, tqm
+
+
+class _Split:
+    """TQ_ATTN_SPLIT for the duration of a call."""
+
+    def __init__(self, tokens):
+        self.tokens = tokens
+
+    def __enter__(self):
+        self.old = os.environ.get("TQ_ATTN_SPLIT")
+        if self.tokens is not None:
+            os.environ["TQ_ATTN_SPLIT"] = str(self.tokens)
+
+    def __exit__(self, *exc):
+        if self.tokens is not None:
+            if self.old is None:
+                del os.environ["TQ_ATTN_SPLIT"]
+            else:
+                os.environ["TQ_ATTN_SPLIT"] = self.old
+
+
+def _run(env, d, kbits, vbits, groups, nq, n, seed, queries=None, scale=None, split=None):
+    """Oracle quantization of seeded keys and values; GPU value blocks
+    (checked bit for bit) and attention; returns (gpu out, gpu lse, oracle
+    out, oracle lse, per-row tolerances (out, lse))."""
+    torch, tqm = env
+    prk, prv = _params(d, kbits, 0), _params(d, vbits, 1)
+    hk, hv = tqm.tq_init(d, kbits, 0), tqm.tq_init(d, vbits, 1)
+    rs = np.random.default_rng(seed)
+    keys = rs.standard_normal((groups * n, d)) * np.exp(0.5 * rs.standard_normal((groups * n, 1)))
+    vals = rs.standard_normal((groups * n, d)) * np.exp(0.3 * rs.standard_normal((groups * n, 1)))
+    if queries is None:
+        queries = rs.standard_normal((groups, nq, d)).astype(np.float32)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    kz, vz = tq.quantize(prk, keys), tq.quantize(prv, vals)
+    kc, ks, kn, kr = tq.pack(prk, kz)
+    vc = tq.pack_codes(vz.idx, prv.code_bits)
+    vn = vz.norms.astype(np.float32)
+
+    blocks = tqm.tq_pack_values(hv, _dev(torch, vc.view(np.int32)), groups=groups, n=n)
+    torch.cuda.synchronize()
+    got = _cpu(blocks).view(np.uint32)
+    for g in range(groups):
+        want = tq.pack_values(vz.idx[g * n:(g + 1) * n], prv.code_bits)
+        assert np.array_equal(got[g], want), f"value blocks of group {g} differ"
+
+    with _Split(split):
+        out, lse = tqm.tq_attention(hk, hv, _dev(torch, queries), _dev(torch, kc.view(np.int32)),
+                                    _dev(torch, ks.view(np.int32)), _dev(torch, kn), _dev(torch, kr), blocks,
+                                    _dev(torch, vn), scale=scale, n=n)
+        torch.cuda.synchronize()
+    out, lse = _cpu(out), _cpu(lse)
+    ref_o = np.zeros((groups, nq, d))
+    ref_l = np.zeros((groups, nq))
+    tol_o = np.zeros((groups, nq, d))
+    tol_l = np.zeros((groups, nq))
+    for g in range(groups):
+        sl = slice(g * n, (g + 1) * n)
+        o, l = tq.attention(prk, prv, queries[g], kz.idx[sl], kz.beta[sl], kn[sl].astype(np.float64),
+                            kr[sl].astype(np.float64), vz.idx[sl], vn[sl].astype(np.float64), scale)
+        ref_o[g], ref_l[g] = o, l
+        vh = tq.dequant_mse(prv, vz.idx[sl], vn[sl].astype(np.float64))
+        vmax = np.abs(vh).max(axis=0) if n else np.zeros(d)
+        vnorm = np.sqrt((vh * vh).sum(axis=1)).max() if n else 0.0
+        qn = np.sqrt((queries[g].astype(np.float64) ** 2).sum(axis=1))
+        delta = abs(scale) * 1e-3 * qn * (kn[sl].max() if n else 0.0)
+        tol_o[g] = np.expm1(2 * delta)[:, None] * vmax[None, :] + 2e-5 * vnorm
+        tol_l[g] = delta + 1e-5 * np.maximum(1.0, np.abs(l))
+    return out, lse, ref_o, ref_l, tol_o, tol_l
+
+
+def _assert_close(out, lse, ref_o, ref_l, tol_o, tol_l):
+    err = np.abs(out - ref_o)
+    assert np.all(err <= tol_o), (float((err / np.maximum(tol_o, 1e-30)).max()), np.argwhere(err > tol_o)[:5])
+    finite = np.isfinite(ref_l)
+    assert np.array_equal(np.isfinite(lse), finite)
+    assert np.all(np.abs(lse[finite] - ref_l[finite]) <= tol_l[finite])
+    print(f"worst |error| / tolerance: out {float((err / np.maximum(tol_o, 1e-30)).max()):.3g}")
+
+
+@pytest.mark.parametrize("d,kbits,vbits,groups,nq,n,split", [
+    (128, 3, 3, 2, 4, 1000, None),    # lookup-table scorer, one float16 piece per value level
+    (128, 4, 4, 3, 4, 777, None),     # three value index bits (two pieces), ragged last tile
+    (200, 3, 2, 1, 20, 500, None),    # matrix-core scorer; sign-form values; 7 words (two word groups)
+    (64, 2, 5, 2, 17, 300, None),     # four value index bits; 17 queries (two row chunks)
+    (33, 3, 3, 1, 1, 65, None),       # d not a multiple of 32, one query, general scorer
+    (300, 3, 3, 1, 4, 100, None),     # general scorer, d > 256
+    (1536, 4, 4, 1, 16, 200, None),   # tiled scorer, 48 words (12 word groups)
+    (128, 3, 3, 2, 4, 1000, 64),      # 16 splits per group merged
+    (128, 4, 2, 1, 8, 4097, 96),      # 43 splits, the last with one token
+])
+def test_attention_matches_oracle(env, d, kbits, vbits, groups, nq, n, split):
+    _announce(f"attention d={d} kbits={kbits} vbits={vbits} groups={groups} nq={nq} n={n} split={split}")
+    _assert_close(*_run(env, d, kbits, vbits, groups, nq, n, seed=d + n + nq, split=split))
+
+
+@pytest.mark.parametrize("vbits,split", [(3, None), (3, 256), (2, 96), (5, 128)])
+def test_attention_zero_queries_average_values(env, vbits, split):
+    """Zero queries score every key exactly 0: o is the plain mean of the
+    value reconstructions, lse = log n (delta = 0: the value pass alone)."""
+    d, groups, nq, n = 128, 2, 4, 2000
+    _announce(f"attention zero queries vbits={vbits} split={split}")
+    q = np.zeros((groups, nq, d), dtype=np.float32)
+    out, lse, ref_o, ref_l, tol_o, tol_l = _run(env, d, 3, vbits, groups, nq, n, seed=7, queries=q, split=split)
+    assert np.allclose(ref_l, math.log(n))
+    _assert_close(out, lse, ref_o, ref_l, tol_o, tol_l)
+
+
+def test_attention_single_token_and_empty(env):
+    """One token: o is its value reconstruction exactly (weight 1); no
+    tokens: o = 0, lse = -inf."""
+    torch, tqm = env
+    _announce("attention one token / no tokens")
+    out, lse, ref_o, ref_l, tol_o, tol_l = _run(env, 128, 3, 4, 2, 4, 1, seed=3)
+    assert np.all(np.abs(out - ref_o) <= 2e-5 * np.abs(ref_o).max())
+    _assert_close(out, lse, ref_o, ref_l, tol_o, tol_l)
+    hk, hv = tqm.tq_init(128, 3, 0), tqm.tq_init(128, 3, 1)
+    dummy = torch.zeros(64, dtype=torch.int32, device="cuda")
+    o, l = tqm.tq_attention(hk, hv, torch.ones((2, 4, 128), device="cuda"), dummy, dummy, dummy.float(),
+                            dummy.float(), dummy, dummy.float(), n=0)
+    torch.cuda.synchronize()
+    assert np.all(_cpu(o) == 0.0) and np.all(np.isneginf(_cpu(l)))
+
+
+@pytest.mark.parametrize("d,bits,groups,n", [(128, 3, 3, 1), (128, 4, 2, 31), (200, 2, 1, 33), (33, 5, 2, 100),
+                                             (1536, 4, 1, 64), (2, 3, 2, 70)])
+def test_pack_values_matches_oracle(env, d, bits, groups, n):
+    """Token blocks bit for bit, including ragged token blocks and padding
+    coordinates."""
+    torch, tqm = env
+    _announce(f"pack values d={d} bits={bits} groups={groups} n={n}")
+    pr = _params(d, bits, 0)
+    h = tqm.tq_init(d, bits, 0)
+    rs = np.random.default_rng(d + n)
+    idx = rs.integers(0, 1 << pr.code_bits, (groups * n, d))
+    codes = tq.pack_codes(idx, pr.code_bits)
+    got = _cpu(tqm.tq_pack_values(h, _dev(torch, codes.view(np.int32)), groups=groups, n=n)).view(np.uint32)
+    for g in range(groups):
+        assert np.array_equal(got[g], tq.pack_values(idx[g * n:(g + 1) * n], pr.code_bits))

@@ -73,6 +73,10 @@ def test_bad_arguments_are_rejected(tqm):
     assert lib.tq_logits_topk(None, None, 1, 1, None, None, None, None, 1, 10, None, None, None, 0,
                               None) == tqm.TQ_EINVAL
     assert lib.tq_logits_topk_workspace_size(None, 1, 1, 1, 10) == 0
+    assert lib.tq_pack_values(None, None, 1, 1, None, None) == tqm.TQ_EINVAL
+    assert lib.tq_attention_workspace_size(None, None, 1, 1, 1) == 0
+    assert lib.tq_attention(None, None, None, 1, 1, None, None, None, None, None, None, 1, 0.1, None, None, None,
+                            0, None) == tqm.TQ_EINVAL
     assert lib.tq_destroy(None) == tqm.TQ_OK
     assert lib.tq_params_hash(None) == 0
     assert lib.tq_logits_workspace_size(None, 1, 1) == 0

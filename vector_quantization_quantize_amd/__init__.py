@@ -26,7 +26,8 @@ TQ_FORMAT_VERSION = 1
 # every symbol include/tq.h declares
 EXPORTS = ("tq_init", "tq_init_explicit", "tq_destroy", "tq_get_layout", "tq_host_params",
            "tq_params_hash", "tq_quantize", "tq_logits_workspace_size", "tq_logits",
-           "tq_logits_topk_workspace_size", "tq_logits_topk", "tq_dequant_mse", "tq_strerror")
+           "tq_logits_topk_workspace_size", "tq_logits_topk", "tq_dequant_mse", "tq_pack_values",
+           "tq_attention_workspace_size", "tq_attention", "tq_strerror")
 
 
 class TqError(RuntimeError):
@@ -67,6 +68,10 @@ def _lib():
         "tq_dequant_mse": (ctypes.c_int, [vp, vp, vp, i64, vp, vp]),
         "tq_logits_topk_workspace_size": (sz, [vp, i64, i64, i64, i32]),
         "tq_logits_topk": (ctypes.c_int, [vp, vp, i64, i64, vp, vp, vp, vp, i64, i32, vp, vp, vp, sz, vp]),
+        "tq_pack_values": (ctypes.c_int, [vp, vp, i64, i64, vp, vp]),
+        "tq_attention_workspace_size": (sz, [vp, vp, i64, i64, i64]),
+        "tq_attention": (ctypes.c_int, [vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, i64, ctypes.c_float, vp, vp,
+                                        vp, sz, vp]),
         "tq_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -275,6 +280,61 @@ def tq_dequant_mse(h, codes, norms, khat=None, stream=None):
     _check("tq_dequant_mse", _lib().tq_dequant_mse(h.ptr, _ptr(codes), _ptr(norms), n, _ptr(khat),
                                                    _stream(stream)))
     return khat
+
+
+def tq_pack_values(h, codes, groups=1, n=None, vcodes=None, stream=None):
+    """Token blocks (groups, ceil(n/32), B, 32 W) uint32 of value codes
+    (groups * n, B, W) from tq_quantize."""
+    import torch
+    if n is None:
+        n = codes.shape[0] // groups
+    if groups * n > codes.shape[0]:
+        raise ValueError("codes hold fewer than groups * n values")
+    nb = (n + 31) // 32
+    if vcodes is None:
+        vcodes = torch.empty((groups, nb, h.code_bits, 32 * h.words), dtype=torch.int32, device=codes.device)
+    _check("tq_pack_values", _lib().tq_pack_values(h.ptr, _ptr(codes), int(groups), int(n), _ptr(vcodes),
+                                                   _stream(stream)))
+    return vcodes
+
+
+def tq_attention_workspace_size(hk, hv, groups, nq, n):
+    return int(_lib().tq_attention_workspace_size(hk.ptr, hv.ptr, int(groups), int(nq), int(n)))
+
+
+def tq_attention(hk, hv, queries, kcodes, ksigns, knorms, krnorms, vcodes, vnorms, scale=None, n=None, out=None,
+                 lse=None, workspace=None, stream=None):
+    """Decode attention over a compressed cache.
+
+    queries: cuda float32 (groups, nq, d); keys packed by tq_quantize(hk)
+    (groups * n of them); values: token blocks from tq_pack_values(hv) and
+    their norms (groups * n).  scale defaults to 1/sqrt(d).  Returns
+    (out float32 (groups, nq, d), lse float32 (groups, nq))."""
+    import torch
+    if queries.dim() == 2:
+        queries = queries.unsqueeze(0)
+    groups, nq, d = queries.shape
+    if d != hk.d or d != hv.d or not queries.is_contiguous() or queries.dtype != torch.float32:
+        raise ValueError("queries must be contiguous float32 (groups, nq, d)")
+    if n is None:
+        n = knorms.shape[0] // groups
+    if groups * n > knorms.shape[0] or groups * n > vnorms.shape[0]:
+        raise ValueError("packed arrays hold fewer than groups * n tokens")
+    if scale is None:
+        scale = 1.0 / d ** 0.5
+    if out is None:
+        out = torch.empty((groups, nq, d), dtype=torch.float32, device=queries.device)
+    if lse is None:
+        lse = torch.empty((groups, nq), dtype=torch.float32, device=queries.device)
+    ws_bytes = tq_attention_workspace_size(hk, hv, groups, nq, n)
+    if workspace is None:
+        workspace = torch.empty((max(ws_bytes, 256) + 255) // 4, dtype=torch.float32, device=queries.device)
+    _check("tq_attention", _lib().tq_attention(hk.ptr, hv.ptr, _ptr(queries), groups, nq, _ptr(kcodes),
+                                               _ptr(ksigns), _ptr(knorms), _ptr(krnorms), _ptr(vcodes),
+                                               _ptr(vnorms), int(n), float(scale), _ptr(out), _ptr(lse),
+                                               _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                               _stream(stream)))
+    return out, lse
 
 
 _lib()

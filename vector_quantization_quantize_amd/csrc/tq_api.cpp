@@ -404,17 +404,15 @@ size_t tq_logits_workspace_size(tq_handle h, int64_t groups, int64_t nq) {
   return tqdev::score_prep_bytes(h->d, groups, nq);
 }
 
-int tq_logits(tq_handle h, const float* queries, int64_t groups, int64_t nq, const uint32_t* codes,
-              const uint32_t* signs, const float* norms, const float* rnorms, int64_t n, float* scores,
-              void* workspace, size_t workspace_bytes, void* stream) {
-  if (!h || groups < 0 || nq < 0 || n < 0) return TQ_EINVAL;
-  if (groups == 0 || nq == 0 || n == 0) return TQ_OK;
-  if (!queries || !codes || !signs || !norms || !rnorms || !scores || !workspace) return TQ_EINVAL;
-  if (workspace_bytes < tq_logits_workspace_size(h, groups, nq)) return TQ_EINVAL;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return TQ_EINVAL;
-  if (groups > 65535) return TQ_EUNSUPPORTED;
-  if (check_device(h) != TQ_OK) return TQ_EINVAL;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+}  // extern "C"
+
+namespace {
+
+// scores [groups][nq][n] by the scorer pick_scorer chooses; workspace of
+// tq_logits_workspace_size bytes (arguments already checked)
+int run_logits(const tq_ctx* h, const float* queries, int64_t groups, int64_t nq, const uint32_t* codes,
+               const uint32_t* signs, const float* norms, const float* rnorms, int64_t n, float* scores,
+               void* workspace, hipStream_t s) {
   hipError_t e;
   const Scorer sc = pick_scorer(h, nq);
   if (sc == Scorer::kLut) {
@@ -427,6 +425,85 @@ int tq_logits(tq_handle h, const float* queries, int64_t groups, int64_t nq, con
     e = sc == Scorer::kMfma ? tqdev::launch_score_mfma(h, vw, groups, nq, codes, signs, norms, rnorms, n, scores, s)
                             : tqdev::launch_logits_v1(h, vw, groups, nq, codes, signs, norms, rnorms, n, scores, s);
   }
+  return e == hipSuccess ? TQ_OK : TQ_EHIP;
+}
+
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+// workspace of tq_attention: scores, the query transform, the value pass's
+// partial sums
+struct AttnWorkspace {
+  size_t scores, prep, partials, total;
+};
+
+AttnWorkspace attn_workspace(const tq_ctx* hk, const tq_ctx* hv, int64_t groups, int64_t nq, int64_t n) {
+  AttnWorkspace w{};
+  w.scores = tqdev::ws_align(size_t(groups) * size_t(nq) * size_t(n) * sizeof(float));
+  w.prep = tqdev::ws_align(tqdev::score_prep_bytes(hk->d, groups, nq));
+  w.partials = tqdev::attn_partial_bytes(hv, groups, nq, n);
+  w.total = w.scores + w.prep + w.partials;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tq_logits(tq_handle h, const float* queries, int64_t groups, int64_t nq, const uint32_t* codes,
+              const uint32_t* signs, const float* norms, const float* rnorms, int64_t n, float* scores,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!h || groups < 0 || nq < 0 || n < 0) return TQ_EINVAL;
+  if (groups == 0 || nq == 0 || n == 0) return TQ_OK;
+  if (!queries || !codes || !signs || !norms || !rnorms || !scores || !workspace) return TQ_EINVAL;
+  if (workspace_bytes < tq_logits_workspace_size(h, groups, nq)) return TQ_EINVAL;
+  if (!aligned256(workspace)) return TQ_EINVAL;
+  if (groups > 65535) return TQ_EUNSUPPORTED;
+  if (check_device(h) != TQ_OK) return TQ_EINVAL;
+  return run_logits(h, queries, groups, nq, codes, signs, norms, rnorms, n, scores, workspace,
+                    static_cast<hipStream_t>(stream));
+}
+
+int tq_pack_values(tq_handle h, const uint32_t* codes, int64_t groups, int64_t n, uint32_t* vcodes, void* stream) {
+  if (!h || groups < 0 || n < 0) return TQ_EINVAL;
+  if (groups == 0 || n == 0) return TQ_OK;
+  if (!codes || !vcodes || !aligned4(codes) || !aligned4(vcodes)) return TQ_EINVAL;
+  if (groups > 65535 || (n + 31) / 32 > 0x7FFFFFFF) return TQ_EUNSUPPORTED;
+  if (check_device(h) != TQ_OK) return TQ_EINVAL;
+  const hipError_t e = tqdev::launch_pack_values(h, codes, groups, n, vcodes, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : TQ_EHIP;
+}
+
+size_t tq_attention_workspace_size(tq_handle hk, tq_handle hv, int64_t groups, int64_t nq, int64_t n) {
+  if (!hk || !hv || groups < 0 || nq < 0 || n < 0) return 0;
+  return attn_workspace(hk, hv, groups, nq, n).total;
+}
+
+int tq_attention(tq_handle hk, tq_handle hv, const float* queries, int64_t groups, int64_t nq,
+                 const uint32_t* kcodes, const uint32_t* ksigns, const float* knorms, const float* krnorms,
+                 const uint32_t* vcodes, const float* vnorms, int64_t n, float scale, float* out, float* lse,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (!hk || !hv || groups < 0 || nq < 0 || n < 0) return TQ_EINVAL;
+  if (hk->d != hv->d || hk->device != hv->device || !std::isfinite(scale)) return TQ_EINVAL;
+  if (groups == 0 || nq == 0) return TQ_OK;
+  if (!out || !aligned4(out) || (lse && !aligned4(lse))) return TQ_EINVAL;
+  if (groups * ((nq + 15) / 16) > 65535) return TQ_EUNSUPPORTED;
+  if (check_device(hk) != TQ_OK) return TQ_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (n == 0) {  // no tokens: o = 0, lse = -inf
+    hipError_t e = tqdev::launch_fill_u32(reinterpret_cast<unsigned int*>(out), groups * nq * hk->d, 0u, s);
+    if (e == hipSuccess && lse) e = tqdev::launch_fill_u32(reinterpret_cast<unsigned int*>(lse), groups * nq, 0xFF800000u, s);
+    return e == hipSuccess ? TQ_OK : TQ_EHIP;
+  }
+  if (!queries || !kcodes || !ksigns || !knorms || !krnorms || !vcodes || !vnorms || !workspace) return TQ_EINVAL;
+  if (!aligned4(vcodes) || !aligned4(vnorms) || !aligned256(workspace)) return TQ_EINVAL;
+  const AttnWorkspace w = attn_workspace(hk, hv, groups, nq, n);
+  if (workspace_bytes < w.total) return TQ_EINVAL;
+  char* base = static_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(base);
+  const int rc = run_logits(hk, queries, groups, nq, kcodes, ksigns, knorms, krnorms, n, scores, base + w.scores, s);
+  if (rc != TQ_OK) return rc;
+  const hipError_t e = tqdev::launch_attention_values(hv, scores, groups, nq, n, vcodes, vnorms, scale,
+                                                      base + w.scores + w.prep, out, lse, s);
   return e == hipSuccess ? TQ_OK : TQ_EHIP;
 }
 

@@ -221,4 +221,19 @@ inline size_t score_prep_bytes(int d, int64_t groups, int64_t nq) {
          (d >= kScoreGemmMinD ? score_qa_bytes(d, groups, nq) + ws_align(size_t(rows) * 4) : 0);
 }
 
+// Decode attention (attention.hip).  Values in token blocks:
+// vcodes[group][ceil(n/32)][B][32 W], bit i of word (b, p, j) = bit p of the
+// index of coordinate j of token 32 b + i.
+hipError_t launch_pack_values(const tq_ctx* h, const uint32_t* codes, int64_t groups, int64_t n, uint32_t* vcodes,
+                              hipStream_t stream);
+// tokens per key split of the value pass, and the bytes of its partial sums
+int64_t attn_split_tokens(const tq_ctx* hv, int64_t groups, int64_t nq, int64_t n);
+size_t attn_partial_bytes(const tq_ctx* hv, int64_t groups, int64_t nq, int64_t n);
+// from scores [groups][nq][n]: softmax(scale s) over each row, weighted sum
+// of the value reconstructions into out [groups][nq][d] and, if lse is not
+// null, log sum exp(scale s) into lse [groups][nq]; n >= 1
+hipError_t launch_attention_values(const tq_ctx* hv, const float* scores, int64_t groups, int64_t nq, int64_t n,
+                                   const uint32_t* vcodes, const float* vnorms, float scale, void* partials,
+                                   float* out, float* lse, hipStream_t stream);
+
 }  // namespace tqdev
