@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-search", action="store_true", help="skip the search (top-k) measurement")
     ap.add_argument("--search-workload", default="search_b2")
+    ap.add_argument("--no-attention", action="store_true",
+                    help="skip the decode-attention and uncompressed-logits measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -153,6 +155,76 @@ def search_topk(name, seed, k=10, reps=3, recall_queries=64):
             "roofline": {"bound": "mfma", "achieved": round(useful, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(useful / BF16_MFMA_PEAK_TFLOPS, 4),
                          "raw_mfma_TFLOPs": round(raw, 2)}}
+
+
+def attention_leg(w, h, keys, queries, packed, seed, stream, reps=10):
+    """Decode attention over the compressed cache of the step's workload and
+    the uncompressed comparison.  Values: seeded N(0,1) bfloat16 vectors
+    quantized with their own handle (same bits, seed 1) and regrouped into
+    token blocks; every query head attends over its KV head's n tokens with
+    scale 1/sqrt(d).  Comparison: inner products of the same queries with
+    the unquantized keys, as float32 and as bfloat16.  Times: HIP events on
+    the library's stream, mean of `reps` calls after one warm-up."""
+    import torch
+
+    import vector_quantization_quantize_amd as tqm
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1000 + seed)
+    values = torch.randn((w.total_keys, w.d), generator=gen, device="cuda").to(torch.bfloat16)
+    hv = tqm.tq_init(w.d, w.bits, 1)
+    vc, vs, vn, vr = tqm.tq_quantize(hv, values, stream=stream)
+    del values, vs, vr
+    vblocks = tqm.tq_pack_values(hv, vc, groups=w.groups, n=w.n, stream=stream)
+    del vc
+    out = torch.empty((w.groups, w.nq, w.d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.groups, w.nq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tqm.tq_attention_workspace_size(h, hv, w.groups, w.nq, w.n) // 4 + 64, dtype=torch.float32,
+                     device="cuda")
+    scores = torch.empty((w.groups, w.nq, w.n), dtype=torch.float32, device="cuda")
+    lws = torch.empty(tqm.tq_logits_workspace_size(h, w.groups, w.nq) // 4 + 64, dtype=torch.float32,
+                      device="cuda")
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    t_attn = timed(lambda: tqm.tq_attention(h, hv, queries, *packed, vblocks, vn, n=w.n, out=out, lse=lse,
+                                            workspace=ws, stream=stream))
+    t_logits = timed(lambda: tqm.tq_logits(h, queries, *packed, n=w.n, scores=scores, workspace=lws,
+                                           stream=stream))
+    kb = keys.to(torch.bfloat16) if keys.dtype != torch.bfloat16 else keys
+    kf = keys.float()
+    t_f32 = timed(lambda: tqm.tq_dense_logits(queries, kf, n=w.n, scores=scores, stream=stream))
+    del kf
+    t_bf16 = timed(lambda: tqm.tq_dense_logits(queries, kb, n=w.n, scores=scores, stream=stream))
+    tokens = w.total_keys
+    words = (w.d + 31) // 32
+    key_bytes = 4 * (w.bits - 1) * words + 4 * words + 8
+    value_bytes = 4 * (w.bits - 1) * words + 4
+    # algorithmic bytes: the packed keys and values once (scores, in the
+    # ideal, never leave the chip) plus the outputs
+    alg = (key_bytes + value_bytes) * tokens + 4 * w.groups * w.nq * (w.d + 1)
+    gbs = alg / (t_attn * 1e-3) / 1e9
+    dense_b = {"f32": 4 * w.d, "bf16": 2 * w.d}
+    res = {"ms": round(t_attn, 4), "ms_scores": round(t_logits, 4), "ms_values": round(t_attn - t_logits, 4),
+           "tokens_per_s": tokens / (t_attn * 1e-3), "bytes_per_token": key_bytes + value_bytes,
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4)},
+           "value_bits": w.bits - 1, "scale": "1/sqrt(d)",
+           "dense_logits": {}}
+    for name, t in (("f32", t_f32), ("bf16", t_bf16)):
+        b = (dense_b[name] + 4 * w.nq) * tokens
+        res["dense_logits"][name] = {"ms": round(t, 4), "GBps": round(b / (t * 1e-3) / 1e9, 1),
+                                     "tq_logits_speedup": round(t / t_logits, 2)}
+    tqm.tq_destroy(hv)
+    return res
 
 
 def cpu_baseline(w, keys_np, queries_np, groups, seed):
@@ -326,6 +398,8 @@ def main():
         "roofline_logits": roofline("tq_logits"),
         "roofline_by_kernel": {n: roofline(n) for n in names},
     }
+    if not args.no_attention:
+        line["attention"] = attention_leg(w, h, keys, queries, packed, args.seed, stream)
     if not args.no_search:
         del keys, queries, packed, scores, ws, khat
         torch.cuda.empty_cache()

@@ -190,16 +190,34 @@ TQ_API int tq_logits_topk(tq_handle h, const float* queries, int64_t groups, int
 TQ_API int tq_dequant_mse(tq_handle h, const uint32_t* codes, const float* norms, int64_t n,
                    float* khat, void* stream);
 
+/* The uncompressed comparison: raw inner products of float32 queries with
+ * unquantized keys, the operation whose time the pages compare 4-bit keys
+ * against ("TurboQuant digest", section 3: attention logits against 32-bit
+ * keys).  No handle.  queries: device float [groups][nq][d]; keys: device,
+ * groups * n rows of d elements of key_dtype (TQ_F32 or TQ_BF16), row i at
+ * keys + i*ldk elements (ldk >= d), group g's keys are rows g*n ..
+ * g*n + n - 1; scores: device float [groups][nq][n].  1 <= d <= 4096.
+ * Summation in float32 (order unspecified).  Asynchronous on `stream`. */
+TQ_API int tq_dense_logits(const float* queries, int64_t groups, int64_t nq, const void* keys,
+                           int32_t key_dtype, int64_t n, int32_t d, int64_t ldk, float* scores,
+                           void* stream);
+
 /* Value cache layout for tq_attention.  Values are quantized like keys
  * (tq_quantize with the value handle; only codes and norms are kept: the
  * attention reads values back through the stage-1 reconstruction) and their
  * codes are regrouped into token blocks:
- *   vcodes [groups][ceil(n/32)][B][32 W] uint32, bit i of word (b, p, j) =
- *   bit p of the index of coordinate j of token 32 b + i
- * (tokens past n and coordinates past d are 0).  One word then carries one
- * coordinate of 32 tokens, which is what a weighted sum over tokens reads.
+ *   vcodes [groups][ceil(n/32)][B][32 W] uint32 (4 W * 32 bytes per plane).
+ *   For plane p of block b let T_c be the 32-bit word whose bit i is bit p
+ *   of the index of coordinate c of token 32 b + i (tokens past n and
+ *   coordinates past d give 0).  Coordinates come in groups of 128 (the
+ *   last group holds G = W mod 4 of the key layout's words when that is
+ *   not 0, else G = 4); group g's 128 G bytes start at byte 512 g of the
+ *   plane, and byte k of T_{128 g + r} sits at byte
+ *   ((r mod 16) + 16 k) * 2 G + (r div 16) of the group.
+ * One T_c carries one coordinate of 32 tokens, which is what a weighted sum
+ * over tokens reads, and the bytes one lane of that sum needs are adjacent.
  * codes: device, groups * n packed keys' codes [groups][n][B][W]; vcodes:
- * device, as above.  Asynchronous on `stream`. */
+ * device, 16-byte aligned, as above.  Asynchronous on `stream`. */
 TQ_API int tq_pack_values(tq_handle h, const uint32_t* codes, int64_t groups, int64_t n, uint32_t* vcodes,
                           void* stream);
 

@@ -61,9 +61,14 @@ Stages (page, section):
 Packed layout (bit planes): ``codes[n][B][W]`` and ``signs[n][W]`` as
 uint32 with W = ceil(d / 32); bit p of the index of coordinate j is bit
 (j mod 32) of word (j div 32) of plane p (LSB first); padding bits are 0.
-Stored values use token blocks instead: ``vcodes[ceil(n/32)][B][32 W]``,
-where bit i of word (b, p, j) is bit p of the index of coordinate j of
-token 32 b + i; tokens past n and coordinates past d are 0.
+Stored values use token blocks instead: ``vcodes[ceil(n/32)][B][32 W]``
+(uint32 words, read here as little-endian bytes).  For plane p of block b,
+let T_j be the 32-bit word whose bit i is bit p of the index of coordinate
+j of token 32 b + i (tokens past n and coordinates past d give 0 bits).
+Coordinates come in groups of 128 (4 words of the key layout; the last
+group holds G = W mod 4 words when that is not 0) and a group's 128 G bytes
+start at byte 512 g of the plane; byte k of T_{128 g + r} (r < 32 G) sits
+at byte ((r mod 16) + 16 k) * 2 G + (r div 16) of the group.
 """
 from dataclasses import dataclass
 
@@ -263,30 +268,52 @@ def pack(params: Params, qz: Quantized):
             qz.norms.astype(np.float32), qz.rnorms.astype(np.float32))
 
 
+def value_byte_position(d):
+    """(32 W, 4) int: the byte of a value plane that holds byte k of the
+    token word T_j of coordinate j (see the module docstring)."""
+    w = words_per_plane(d)
+    pos = np.empty((32 * w, 4), dtype=np.int64)
+    for j in range(32 * w):
+        g, r = divmod(j, 128)
+        gw = min(4, w - 4 * g)                      # words in this group
+        for k in range(4):
+            pos[j, k] = 512 * g + ((r % 16) + 16 * k) * 2 * gw + r // 16
+    return pos
+
+
 def pack_values(idx, code_bits):
     """(n, d) value indices -> (ceil(n/32), B, 32 W) uint32 token blocks:
-    word (b, p, j) holds bit p of the indices of coordinate j for tokens
-    32 b .. 32 b + 31, token 32 b + i at bit i."""
+    the token words T_j (bit i = bit p of the index of coordinate j of
+    token 32 b + i) of each plane, their bytes placed by
+    value_byte_position."""
     idx = np.asarray(idx, dtype=np.int64)
     n, d = idx.shape
     nb = (n + 31) // 32
     dp = 32 * words_per_plane(d)
+    pos = value_byte_position(d)
     padded = np.zeros((nb * 32, dp), dtype=np.int64)
     padded[:n, :d] = idx
-    out = np.zeros((nb, code_bits, dp), dtype=np.uint32)
+    out = np.zeros((nb, code_bits, 4 * dp), dtype=np.uint8)
     for b in range(nb):
         block = padded[32 * b:32 * b + 32]                    # (32 tokens, dp)
         for p in range(code_bits):
-            out[b, p, :] = pack_bits(((block >> p) & 1).T.astype(bool))[:, 0]
-    return out
+            words = pack_bits(((block >> p) & 1).T.astype(bool))[:, 0]   # T_j, j < dp
+            for k in range(4):
+                out[b, p, pos[:, k]] = (words >> np.uint32(8 * k)) & np.uint32(0xFF)
+    return out.view("<u4")
 
 
 def unpack_values(vcodes, n, d):
     """Inverse of pack_values: (n, d) indices."""
-    vcodes = np.asarray(vcodes, dtype=np.uint32)
+    vcodes = np.ascontiguousarray(np.asarray(vcodes, dtype=np.uint32))
     nb, code_bits, dp = vcodes.shape
+    raw = vcodes.view("<u1").reshape(nb, code_bits, 4 * dp).astype(np.uint32)
+    pos = value_byte_position(d)
+    by_coord = np.zeros((nb, code_bits, dp), dtype=np.uint32)   # T_j at j
+    for k in range(4):
+        by_coord |= raw[:, :, pos[:, k]] << np.uint32(8 * k)
     idx = np.zeros((nb * 32, dp), dtype=np.int64)
     for p in range(code_bits):
-        bits = unpack_bits(vcodes[:, p, :].reshape(nb * dp, 1), 32)   # (nb*dp, 32 tokens)
+        bits = unpack_bits(by_coord[:, p, :].reshape(nb * dp, 1), 32)   # (nb*dp, 32 tokens)
         idx |= bits.reshape(nb, dp, 32).transpose(0, 2, 1).reshape(nb * 32, dp).astype(np.int64) << p
     return idx[:n, :d]

@@ -177,3 +177,33 @@ def test_pack_values_matches_oracle(env, d, bits, groups, n):
     got = _cpu(tqm.tq_pack_values(h, _dev(torch, codes.view(np.int32)), groups=groups, n=n)).view(np.uint32)
     for g in range(groups):
         assert np.array_equal(got[g], tq.pack_values(idx[g * n:(g + 1) * n], pr.code_bits))
+
+
+@pytest.mark.parametrize("d,nq,groups,n,dtype,ldk", [
+    (128, 4, 2, 1000, "f32", 128),   # the fast kernel, GQA 4
+    (128, 4, 3, 777, "bf16", 136),   # bfloat16 keys, strided rows, ragged last block
+    (128, 1, 1, 300, "f32", 128),
+    (128, 3, 2, 257, "bf16", 128),   # padded query slot
+    (128, 8, 1, 513, "f32", 160),
+    (200, 12, 2, 100, "f32", 200),   # general kernel
+    (33, 5, 1, 70, "bf16", 40),
+])
+def test_dense_logits_match_exact_inner_products(env, d, nq, groups, n, dtype, ldk):
+    """The uncompressed comparison: inner products with the unquantized keys
+    (the oracle's exact_inner_products in float64) within the float32
+    summation bound d 2^-24 sum_i |q_i k_i|."""
+    torch, tqm = env
+    _announce(f"dense logits d={d} nq={nq} groups={groups} n={n} {dtype} ldk={ldk}")
+    rs = np.random.default_rng(d + nq + n)
+    rows = rs.standard_normal((groups * n, ldk)).astype(np.float32)
+    q = rs.standard_normal((groups, nq, d)).astype(np.float32)
+    kt = _dev(torch, rows)
+    if dtype == "bf16":
+        kt = kt.to(torch.bfloat16)
+    rows_used = _cpu(kt.float())[:, :d].astype(np.float64)   # the values the kernel reads
+    s = _cpu(tqm.tq_dense_logits(_dev(torch, q), kt[:, :d], n=n))
+    for g in range(groups):
+        kg = rows_used[g * n:(g + 1) * n]
+        ref = tq.exact_inner_products(q[g], kg)
+        bound = d * 2.0 ** -24 * (np.abs(q[g]).astype(np.float64) @ np.abs(kg).T) + 1e-30
+        assert np.all(np.abs(s[g] - ref) <= bound), float((np.abs(s[g] - ref) / bound).max())

@@ -557,18 +557,34 @@ def test_attention_special_cases():
 
 
 def test_pack_values_bit_positions():
-    """Token-blocked value planes: token 33, coordinate 37, index 0b10 sets
-    bit 1 (33 mod 32) of word (block 1, plane 1, coordinate 37) and nothing
-    else; coordinates past d and tokens past n stay 0."""
+    """Token-blocked value planes, worked by hand.  d = 50 has W = 2 words:
+    one group of G = 2.  Token 33 with index 0b10 at coordinate 37 sets bit 1
+    (33 mod 32) of T_37 in plane 1 of block 1: byte k = 0 of T_37, with
+    r = 37, sits at byte ((37 mod 16) + 0) * 4 + 37 div 16 = 22; nothing
+    else is set.  Token 9 (byte k = 1, bit 1) at coordinate 3 sits at byte
+    (3 + 16) * 4 + 0 = 76."""
     idx = np.zeros((40, 50), dtype=np.int64)
     idx[33, 37] = 2
     v = tq.pack_values(idx, 2)
     assert v.shape == (2, 2, 64)
-    assert v[1, 1, 37] == 2 and np.count_nonzero(v) == 1
+    raw = v.view(np.uint8).reshape(2, 2, 256)
+    assert raw[1, 1, 22] == 2 and np.count_nonzero(raw) == 1
+    idx = np.zeros((40, 50), dtype=np.int64)
+    idx[9, 3] = 1
+    raw = tq.pack_values(idx, 2).view(np.uint8).reshape(2, 2, 256)
+    assert raw[0, 0, 76] == 2 and np.count_nonzero(raw) == 1
+    # d = 200: W = 7, a full group (G = 4) then G = 3 from byte 512; byte 2
+    # of T_130 (r = 2 of group 1): 512 + (2 + 32) * 6 + 0 = 716; byte 3 of
+    # T_127: (15 + 48) * 8 + 7 = 511; byte 0 of T_16: 0 * 8 + 1 = 1
+    pos = tq.value_byte_position(200)
+    assert pos[130, 2] == 716 and pos[127, 3] == 511 and pos[16, 0] == 1
+    assert sorted(pos.ravel().tolist()) == list(range(4 * 224))
     full = np.full((40, 50), 3, dtype=np.int64)
-    v = tq.pack_values(full, 2)
-    assert np.all(v[0, :, :50] == 0xFFFFFFFF) and np.all(v[:, :, 50:] == 0)
-    assert np.all(v[1, :, :50] == 0xFF)               # tokens 32..39 only
+    raw = tq.pack_values(full, 2).view(np.uint8).reshape(2, 2, 256)
+    pos = tq.value_byte_position(50)
+    assert np.all(raw[0][:, pos[:50].ravel()] == 0xFF) and np.all(raw[:, :, pos[50:].ravel()] == 0)
+    assert np.all(raw[1][:, pos[:50, 0]] == 0xFF) and np.all(raw[1][:, pos[:50, 1:].ravel()] == 0)
     rs = np.random.default_rng(3)
-    idx = rs.integers(0, 8, (77, 45))
-    assert np.array_equal(tq.unpack_values(tq.pack_values(idx, 3), 77, 45), idx)
+    for n, d in ((77, 45), (40, 200), (33, 128), (70, 64)):
+        idx = rs.integers(0, 8, (n, d))
+        assert np.array_equal(tq.unpack_values(tq.pack_values(idx, 3), n, d), idx)

@@ -26,7 +26,7 @@ TQ_FORMAT_VERSION = 1
 # every symbol include/tq.h declares
 EXPORTS = ("tq_init", "tq_init_explicit", "tq_destroy", "tq_get_layout", "tq_host_params",
            "tq_params_hash", "tq_quantize", "tq_logits_workspace_size", "tq_logits",
-           "tq_logits_topk_workspace_size", "tq_logits_topk", "tq_dequant_mse", "tq_pack_values",
+           "tq_logits_topk_workspace_size", "tq_logits_topk", "tq_dequant_mse", "tq_dense_logits", "tq_pack_values",
            "tq_attention_workspace_size", "tq_attention", "tq_strerror")
 
 
@@ -68,6 +68,7 @@ def _lib():
         "tq_dequant_mse": (ctypes.c_int, [vp, vp, vp, i64, vp, vp]),
         "tq_logits_topk_workspace_size": (sz, [vp, i64, i64, i64, i32]),
         "tq_logits_topk": (ctypes.c_int, [vp, vp, i64, i64, vp, vp, vp, vp, i64, i32, vp, vp, vp, sz, vp]),
+        "tq_dense_logits": (ctypes.c_int, [vp, i64, i64, vp, i32, i64, i32, i64, vp, vp]),
         "tq_pack_values": (ctypes.c_int, [vp, vp, i64, i64, vp, vp]),
         "tq_attention_workspace_size": (sz, [vp, vp, i64, i64, i64]),
         "tq_attention": (ctypes.c_int, [vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, i64, ctypes.c_float, vp, vp,
@@ -280,6 +281,33 @@ def tq_dequant_mse(h, codes, norms, khat=None, stream=None):
     _check("tq_dequant_mse", _lib().tq_dequant_mse(h.ptr, _ptr(codes), _ptr(norms), n, _ptr(khat),
                                                    _stream(stream)))
     return khat
+
+
+def tq_dense_logits(queries, keys, n=None, scores=None, stream=None):
+    """Raw inner products with unquantized keys (the uncompressed
+    comparison).  queries: cuda float32 (groups, nq, d); keys: cuda float32
+    or bfloat16 (groups * n, d), rows may be strided.  Returns float32
+    (groups, nq, n)."""
+    import torch
+    if queries.dim() == 2:
+        queries = queries.unsqueeze(0)
+    groups, nq, d = queries.shape
+    if not queries.is_contiguous() or queries.dtype != torch.float32:
+        raise ValueError("queries must be contiguous float32 (groups, nq, d)")
+    if keys.dim() != 2 or keys.shape[1] != d or keys.stride(1) != 1:
+        raise ValueError("keys must be (rows, d) with unit column stride")
+    kdt = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}.get(keys.dtype)
+    if kdt is None:
+        raise ValueError("keys must be float32 or bfloat16")
+    if n is None:
+        n = keys.shape[0] // groups
+    if groups * n > keys.shape[0]:
+        raise ValueError("keys hold fewer than groups * n rows")
+    if scores is None:
+        scores = torch.empty((groups, nq, n), dtype=torch.float32, device=queries.device)
+    _check("tq_dense_logits", _lib().tq_dense_logits(_ptr(queries), groups, nq, _ptr(keys), kdt, int(n), d,
+                                                     keys.stride(0), _ptr(scores), _stream(stream)))
+    return scores
 
 
 def tq_pack_values(h, codes, groups=1, n=None, vcodes=None, stream=None):

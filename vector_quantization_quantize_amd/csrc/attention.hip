@@ -9,23 +9,32 @@
 // so the weighted sum runs in the rotated domain, over the stored levels,
 // and the rotation back is one d x d product per query at the end.
 //
-// Value layout (token blocks): vcodes[group][ceil(n/32)][B][32 W] uint32,
-// bit i of word (block b, plane p, coordinate j) = bit p of the index of
-// coordinate j of token 32 b + i.  One word then holds one coordinate of 32
-// tokens: the contraction over tokens is the matrix-core K dimension, and a
-// lane expands its operand from one byte without a bit transpose.
+// Value layout (token blocks): vcodes[group][ceil(n/32)][B][32 W] uint32.
+// For plane p of block b, the token word T_c of coordinate c has bit i =
+// bit p of the index of coordinate c of token 32 b + i: the contraction
+// over tokens is the matrix-core K dimension, and one byte of T_c is the
+// operand of 8 tokens for one coordinate, expanded without a bit transpose.
+// The bytes are stored in the order the value pass's lanes read them:
+// within each group of 128 coordinates, lane L finds byte L / 16 of the
+// words of coordinates L mod 16 + 16 j (j < 8) as 8 contiguous bytes, so a
+// tile costs one 8-byte load per lane and plane, no byte loaded twice.
 //
 // Kernels:
 //  * pack_values_kernel: key-layout codes -> token blocks (a 32 x 32 bit
 //    transpose per word by wave ballots).
-//  * attn_pv_kernel: per (key split, 4-word coordinate group, group, 16
-//    query rows): pass 1 finds each row's max of scale s over the split and
-//    the split's largest norm; pass 2 walks 32-token tiles: weights
-//    p = exp(scale s - max) n / 2^e go to LDS as two float16 pieces (22
-//    bits), each wave expands its word's levels (the scorer's level forms)
-//    and runs v_mfma_f32_16x16x32_f16: 16 query rows x 32 tokens x 16
-//    coordinates per pass.  Writes the split's (max, sum of exp) per row and
-//    its partial sums per coordinate.
+//  * attn_pv_kernel: one wave per (key split, group of 4 words = 128
+//    coordinates, group, up to 16 query rows), with no block-wide barrier
+//    after the level table.  A first pass over the split's norms finds the
+//    largest (weights are scaled by a power of two so that they fit
+//    float16); then the wave walks 32-token tiles with the next two tiles'
+//    scores, norms and value words already loading, keeping running row
+//    maxima (online softmax: sums so far are rescaled when a maximum
+//    grows).  Weights p = exp(scale s - max) n / 2^e go through the wave's
+//    own LDS slice as two float16 pieces (22 bits), and per word the wave
+//    expands its levels (the scorer's level forms) and runs
+//    v_mfma_f32_16x16x32_f16: 16 query rows x 32 tokens x 16 coordinates
+//    per pass.  Writes the split's (max, sum of exp) per row and its
+//    partial sums per coordinate.
 //  * attn_merge_kernel: per (group, query): combines the splits (rescaled to
 //    the overall max), divides by the sum, and applies Pi^T.
 #include <hip/hip_runtime.h>
@@ -45,13 +54,28 @@ using score::f16x8;
 
 constexpr int kRows = 16;   // query rows per block (matrix-core M)
 constexpr int kTile = 32;   // tokens per tile (matrix-core K; one word of a value plane)
-constexpr int kWaves = 4;   // waves per block: one 32-coordinate word each
+constexpr int kWaves = 4;   // waves per block, each on its own key split
+constexpr int kWordsPerWave = 4;  // 32-coordinate words per wave (128 coordinates)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxSplits = 1024;
+constexpr float kSlack = 8.0f;  // weights relative to a row's reference maximum stay <= 2^kSlack
 
 // ---------------------------------------------------------------------------
 // value packing
 // ---------------------------------------------------------------------------
+
+// Byte of a value plane that holds byte k of the token word of coordinate
+// c: coordinates come in groups of 128 (4 key-layout words; the last group
+// has G = W mod 4 words when that is not 0), a group's 128 G bytes start at
+// byte 512 g, and byte k of coordinate 128 g + r sits at byte
+// ((r mod 16) + 16 k) 2 G + r div 16 of the group.  Lane L of the value
+// pass (L mod 16 = r mod 16, L div 16 = k) then finds its 2 G bytes
+// contiguous at 2 G L.
+__device__ __forceinline__ int value_byte(int c, int k, int W) {
+  const int g = c >> 7, r = c & 127;
+  const int gw = W - 4 * g < 4 ? W - 4 * g : 4;
+  return 512 * g + ((r & 15) + 16 * k) * 2 * gw + (r >> 4);
+}
 
 // block (token block, group); wave pairs of key-layout words: lanes 0-31
 // hold word `pw` of tokens 0-31, lanes 32-63 word `pw + 1`; ballot j
@@ -76,8 +100,10 @@ pack_values_kernel(const uint32_t* __restrict__ codes, int64_t n, int B, int W, 
       out = (lane & 31) == j ? part : out;
     }
     if (mine < pws) {
-      const int p = mine / W, w = mine % W;
-      vcodes[int64_t(p) * 32 * W + 32 * w + (lane & 31)] = out;
+      const int p = mine / W, w = mine % W, c = 32 * w + (lane & 31);
+      uint8_t* plane = reinterpret_cast<uint8_t*>(vcodes + int64_t(p) * 32 * W);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) plane[value_byte(c, k, W)] = uint8_t(out >> (8 * k));
     }
   }
 }
@@ -92,26 +118,41 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
-template <int B, int F>
+// one 32-token tile of a wave's inputs: its share of the scores (pairs
+// lane + 64 k: row (lane + 64 k) / 32, token lane % 32), the token's norm,
+// and per plane the lane's 2 G value bytes (byte j: tokens 8 (lane / 16) ..
+// + 7 of coordinate 16 j + lane % 16 of its group); passed by value so that
+// the prefetch stays in registers
+template <int B, int RQ, int G>
+struct TileIn {
+  float s[RQ * kTile / 64];
+  float nv;
+  uint32_t w[B][(2 * G + 3) / 4];
+};
+
+// RQ: query rows per wave (4 or 16; the matrix-core M is 16 either way,
+// rows past RQ stay 0).  G: words in the wave's coordinate group (4, or
+// W mod 4 for the last group); the group starts at word word_base + 4
+// blockIdx.y.  Blocks with blockIdx.y = 0 of the launch that has write_ml
+// set write the (max, sum) of each row.
+template <int B, int F, int RQ, int G>
 __global__ void __launch_bounds__(kThreads)
 attn_pv_kernel(const float* __restrict__ scores, int64_t nq, int64_t n, const uint32_t* __restrict__ vcodes,
-               const float* __restrict__ vnorms, int W, float scale, int64_t tps, int qchunks, ScoreForm fp,
-               float* __restrict__ part_y, float2* __restrict__ part_ml, int64_t splits) {
+               const float* __restrict__ vnorms, int W, int word_base, bool write_ml, float scale, int64_t tps,
+               int qchunks, ScoreForm fp, float* __restrict__ part_y, float2* __restrict__ part_ml,
+               int64_t splits) {
   using Fm = score::Form<B, F>;
   constexpr int E = Fm::E;
+  constexpr int kPairs = RQ * kTile / 64;  // (row, token) weights per lane per tile
   __shared__ _Float16 vtab[F == kSignForm ? 8 : Fm::kEntries * Fm::kHalves];
-  __shared__ __align__(16) _Float16 pa[2][2][kRows][kTile];  // [buf][hi, lo][row][token]
-  __shared__ float red[kWaves][kRows + 1];
-  __shared__ float row_m[kRows];
+  __shared__ __align__(16) _Float16 pa[kWaves][2][kRows][kTile];  // per wave: [hi, lo][row][token]
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int64_t split = blockIdx.x;
-  const int word = kWaves * blockIdx.y + wave;
+  const int64_t split = int64_t(blockIdx.x) * kWaves + wave;
+  const int word0 = word_base + kWordsPerWave * blockIdx.y;
   const int64_t grp = blockIdx.z / qchunks;
-  const int64_t q0 = int64_t(blockIdx.z % qchunks) * kRows;
-  const int rows = nq - q0 < kRows ? int(nq - q0) : kRows;
-  const int64_t t0 = split * tps;
-  const int64_t t1 = t0 + tps < n ? t0 + tps : n;
+  const int64_t q0 = int64_t(blockIdx.z % qchunks) * RQ;
+  const int rows = nq - q0 < RQ ? int(nq - q0) : RQ;
   const int64_t nb = (n + kTile - 1) / kTile;
   const int dp = 32 * W;
   scores += (grp * nq + q0) * n;
@@ -132,124 +173,212 @@ attn_pv_kernel(const float* __restrict__ scores, int64_t nq, int64_t n, const ui
       }
     }
   }
+  // rows past nq keep weight 0 for the whole kernel
+  for (int i = lane; i < 2 * kRows * kTile; i += 64) (&pa[wave][0][0][0])[i] = static_cast<_Float16>(0.0f);
+  __syncthreads();  // the table; the only block-wide barrier
+  if (split >= splits) return;
+  // the split's token range is the same in every lane: scalar registers
+  const int64_t t0 = (int64_t(__builtin_amdgcn_readfirstlane(int(split))) * tps);
+  const int64_t t1r = t0 + tps < n ? t0 + tps : n;
+  const int64_t t1 = int64_t(__builtin_amdgcn_readfirstlane(int(t1r >> 32))) << 32 |
+                     uint32_t(__builtin_amdgcn_readfirstlane(int(t1r & 0xFFFFFFFF)));
 
-  // ---- pass 1: row maxima of scale * s and the largest norm over the split
-  float lm[kRows];
-#pragma unroll
-  for (int r = 0; r < kRows; ++r) lm[r] = -INFINITY;
+  // ---- the split's largest norm (weights carry n / 2^e <= 1 times at most
+  // 2^kSlack, so their float16 pieces cannot overflow); eight loads in
+  // flight per lane
+  const float a = scale * 1.4426950408889634f;  // weights are 2^(a s - max)
   float nmax = 0.0f;
-  for (int64_t t = t0 + tid; t < t1; t += kThreads) {
-    nmax = fmaxf(nmax, vnorms[t]);
+  for (int64_t tb = t0; tb < t1; tb += 8 * 64) {
+    float nv[8];
 #pragma unroll
-    for (int r = 0; r < kRows; ++r)
-      if (r < rows) lm[r] = fmaxf(lm[r], scale * scores[r * n + t]);
-  }
+    for (int u = 0; u < 8; ++u) {
+      const int64_t t = tb + 64 * u + lane;
+      nv[u] = vnorms[t < t1 ? t : t1 - 1];
+    }
 #pragma unroll
-  for (int r = 0; r < kRows; ++r) {
-    const float m = wave_max(lm[r]);
-    if (lane == 0) red[wave][r] = m;
+    for (int u = 0; u < 8; ++u) nmax = fmaxf(nmax, nv[u]);
   }
-  {
-    const float m = wave_max(nmax);
-    if (lane == 0) red[wave][kRows] = m;
-  }
-  __syncthreads();
-  if (tid < kRows) row_m[tid] = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
-  const float nm = fmaxf(fmaxf(red[0][kRows], red[1][kRows]), fmaxf(red[2][kRows], red[3][kRows]));
-  // weights carry n / 2^e <= 1, so their float16 pieces cannot overflow
+  nmax = wave_max(nmax);
   int ne = 0;
-  if (nm > 0.0f && nm < INFINITY) (void)frexpf(nm, &ne);
+  if (nmax > 0.0f && nmax < INFINITY) (void)frexpf(nmax, &ne);
   const float nscale = ldexpf(1.0f, -ne);
-  __syncthreads();
+  // reference row maxima of a s (the same in every lane)
+  float lm[RQ];
+#pragma unroll
+  for (int r = 0; r < RQ; ++r) lm[r] = -INFINITY;
 
-  // ---- pass 2: 32-token tiles.  Thread tid computes the weights of
-  // (row tid / 32 and 8 + tid / 32, token tid % 32).
-  const int wr = tid >> 5, wt = tid & 31;
-  float lsum[2] = {0.0f, 0.0f};
-  const int n16 = lane & 15, g16 = lane >> 4;
+  // ---- 32-token tiles, inputs loaded two tiles ahead
+  const int n16 = lane & 15, g16 = lane >> 4, tl = lane & 31;
+  // every load is unconditional from a clamped, valid address (a tile past
+  // the split reloads the first, rows and tokens past the end repeat the
+  // last); the arithmetic gives such entries weight 0, so no load waits
+  // behind a branch
+  auto load = [&](int64_t tb) __attribute__((always_inline)) {
+    TileIn<B, RQ, G> x;
+    const int64_t tbc = tb < t1 ? tb : t0;
+    const int64_t tok = tbc + tl < t1 ? tbc + tl : t1 - 1;
+#pragma unroll
+    for (int k = 0; k < kPairs; ++k) {
+      const int r = 2 * k + (lane >> 5);
+      x.s[k] = scores[(r < rows ? r : rows - 1) * n + tok];
+    }
+    x.nv = vnorms[tok];
+    const uint8_t* vb = reinterpret_cast<const uint8_t*>(vcodes + (tbc / kTile) * B * dp) + 128 * word0 + 2 * G * lane;
+#pragma unroll
+    for (int p = 0; p < B; ++p) {
+      const uint8_t* q = vb + 4 * p * dp;
+      if constexpr (G == 4) {
+        const uint2 u = *reinterpret_cast<const uint2*>(q);
+        x.w[p][0] = u.x, x.w[p][1] = u.y;
+      } else if constexpr (G == 2) {
+        x.w[p][0] = *reinterpret_cast<const uint32_t*>(q);
+      } else if constexpr (G == 1) {
+        x.w[p][0] = *reinterpret_cast<const uint16_t*>(q);
+      } else {
+        const uint32_t a0 = *reinterpret_cast<const uint16_t*>(q), a1 = *reinterpret_cast<const uint16_t*>(q + 2),
+                       a2 = *reinterpret_cast<const uint16_t*>(q + 4);
+        x.w[p][0] = a0 | (a1 << 16), x.w[p][1] = a2;
+      }
+    }
+    return x;
+  };
+  float lsum[kPairs];
+#pragma unroll
+  for (int k = 0; k < kPairs; ++k) lsum[k] = 0.0f;
   uint32_t sgn_mask = 0x80008000u, sgn_one = 0x3C003C00u;
   asm volatile("" : "+v"(sgn_mask), "+v"(sgn_one));
-  f32x4 acc[2] = {f32x4{}, f32x4{}};
-  const bool active = word < W;
-  int buf = 0;
-  for (int64_t tb = t0; tb < t1; tb += kTile, buf ^= 1) {
-    const int64_t tok = tb + wt;
-    const bool tin = tok < t1;
-    const float nv = tin ? vnorms[tok] * nscale : 0.0f;
+  f32x4 acc[2 * G];  // coordinate 32 word0 + 16 j + n16
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int r = wr + 8 * k;
-      float p = 0.0f;
-      if (tin && r < rows) {
-        const float w = expf(scale * scores[r * n + tok] - row_m[r]);
-        lsum[k] += w;
-        p = w * nv;
-      }
-      const _Float16 hi = static_cast<_Float16>(p);
-      pa[buf][0][r][wt] = hi;
-      pa[buf][1][r][wt] = static_cast<_Float16>(p - float(hi));
+  for (int j = 0; j < 2 * G; ++j) acc[j] = f32x4{};
+  // three tiles in flight in a ring of named slots: a slot is refilled with
+  // the tile three ahead right after its own tile is used (rotating the
+  // slots would move registers whose loads are still landing, which waits
+  // for every load in flight)
+  TileIn<B, RQ, G> s0 = load(t0), s1 = load(t0 + kTile), s2 = load(t0 + 2 * kTile);
+  auto step = [&](int64_t tb, const TileIn<B, RQ, G> in) __attribute__((always_inline)) {
+    // weights of (row 2k + lane / 32, token lane % 32) into this wave's slice;
+    // LDS is in order within a wave, so the reads below see these writes
+    const float nv = in.nv * nscale;
+    const bool tin = tb + tl < t1;
+    // online softmax with a reference maximum per row: weights are
+    // 2^(a s - ref) <= 2^kSlack, so the reference moves (and what was summed
+    // so far is rescaled) only when a score passes it by more than kSlack;
+    // one ballot per tile tests that
+    float x[kPairs];
+    bool over = false;
+#pragma unroll
+    for (int k = 0; k < kPairs; ++k) {
+      const int r = 2 * k + (lane >> 5);
+      x[k] = tin && r < rows ? a * in.s[k] : -INFINITY;
+      over |= x[k] > ((lane >> 5) ? lm[2 * k + 1] : lm[2 * k]) + kSlack;
     }
-    __syncthreads();
-    if (active) {
-      // A: row n16, tokens 8 g16 .. 8 g16 + 7 (both pieces); B: coordinate
-      // 32 word + 16 h + n16, the same tokens, from byte g16 of its words
-      const f16x8 ah = *reinterpret_cast<const f16x8*>(&pa[buf][0][n16][8 * g16]);
-      const f16x8 al = *reinterpret_cast<const f16x8*>(&pa[buf][1][n16][8 * g16]);
-      const uint32_t* vw = vcodes + (tb / kTile) * B * dp + 32 * word + n16;
+    if (__builtin_amdgcn_ballot_w64(over) != 0) {
+      float f[RQ];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uint32_t pw[B];
+      for (int k = 0; k < kPairs; ++k) {
+        float m = x[k];
 #pragma unroll
-        for (int p = 0; p < B; ++p) pw[p] = __builtin_amdgcn_ubfe(vw[p * dp + 16 * h], 8 * g16, 8);
-        f16x8 bv, bl;
-        if constexpr (F == kSignForm) {
-          const uint4 s = score::expand_signs(pw[0], sgn_mask, sgn_one);
-          bv = *reinterpret_cast<const f16x8*>(&s);
-        } else {
+        for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+        const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 0));
+        const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 32));
 #pragma unroll
-          for (int k = 0; k < 8 / E; ++k) {
-            uint32_t idx = 0;
+        for (int e = 0; e < 2; ++e) {
+          const int rr = 2 * k + e;
+          const float nm = fmaxf(lm[rr], e ? hi : lo);
+          f[rr] = nm > lm[rr] ? exp2f(lm[rr] - nm) : 1.0f;
+          lm[rr] = nm;
+        }
+      }
 #pragma unroll
-            for (int p = 0; p < B; ++p) idx |= __builtin_amdgcn_ubfe(pw[p], k * E, E) << (p * E);
+      for (int k = 0; k < kPairs; ++k) lsum[k] *= (lane >> 5) ? f[2 * k + 1] : f[2 * k];
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-              bv[k * E + e] = vtab[idx * Fm::kHalves + e];
-              if constexpr (F == kTwoPiece) bl[k * E + e] = vtab[idx * Fm::kHalves + E + e];
-            }
+      for (int j = 0; j < 2 * G; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float fr = f[i];
+          if constexpr (RQ > 4) {
+            fr = g16 == 1 ? f[4 + i] : fr;
+            fr = g16 == 2 ? f[8 + i] : fr;
+            fr = g16 == 3 ? f[12 + i] : fr;
+          }
+          acc[j][i] *= fr;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kPairs; ++k) {
+      const int r = 2 * k + (lane >> 5);
+      const float w = exp2f(x[k] - ((lane >> 5) ? lm[2 * k + 1] : lm[2 * k]));
+      const bool use = tin && r < rows;
+      lsum[k] += use ? w : 0.0f;
+      const float p = use ? w * nv : 0.0f;
+      const _Float16 hi = static_cast<_Float16>(p);
+      pa[wave][0][r][tl] = hi;
+      pa[wave][1][r][tl] = static_cast<_Float16>(p - float(hi));
+    }
+    // A: row n16, tokens 8 g16 .. 8 g16 + 7 (both pieces); B: coordinate
+    // 32 word0 + 16 j + n16, the same tokens, from the lane's byte j
+    const f16x8 ah = *reinterpret_cast<const f16x8*>(&pa[wave][0][n16][8 * g16]);
+    const f16x8 al = *reinterpret_cast<const f16x8*>(&pa[wave][1][n16][8 * g16]);
+#pragma unroll
+    for (int j = 0; j < 2 * G; ++j) {
+      uint32_t pw[B];
+#pragma unroll
+      for (int p = 0; p < B; ++p) pw[p] = __builtin_amdgcn_ubfe(in.w[p][j >> 2], 8 * (j & 3), 8);
+      f16x8 bv, bl;
+      if constexpr (F == kSignForm) {
+        const uint4 sg = score::expand_signs(pw[0], sgn_mask, sgn_one);
+        bv = *reinterpret_cast<const f16x8*>(&sg);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8 / E; ++k) {
+          uint32_t idx = 0;
+#pragma unroll
+          for (int p = 0; p < B; ++p) idx |= __builtin_amdgcn_ubfe(pw[p], k * E, E) << (p * E);
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            bv[k * E + e] = vtab[idx * Fm::kHalves + e];
+            if constexpr (F == kTwoPiece) bl[k * E + e] = vtab[idx * Fm::kHalves + E + e];
           }
         }
-        acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bv, acc[h], 0, 0, 0);
-        acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bv, acc[h], 0, 0, 0);
-        if constexpr (F == kTwoPiece) acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl, acc[h], 0, 0, 0);
       }
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bv, acc[j], 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bv, acc[j], 0, 0, 0);
+      if constexpr (F == kTwoPiece) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl, acc[j], 0, 0, 0);
     }
+  };
+  // whole rounds of three tiles: tiles past the split's end carry weight 0
+  // (a branch per step would leave the loop head unable to count the loads
+  // in flight, and it would wait for all of them)
+  for (int64_t tb = t0; tb < t1; tb += 3 * kTile) {
+    step(tb, s0);
+    s0 = load(tb + 3 * kTile);
+    step(tb + kTile, s1);
+    s1 = load(tb + 4 * kTile);
+    step(tb + 2 * kTile, s2);
+    s2 = load(tb + 5 * kTile);
   }
 
-  // ---- partial results of the split
+  // ---- partial results of the split (rows 2k + lane / 32 summed over the
+  // 32 lanes of each half)
+  const int64_t rowbase = grp * nq + q0;
+  const float ln2 = 0.6931471805599453f;
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < kPairs; ++k) {
 #pragma unroll
     for (int o = 16; o > 0; o >>= 1) lsum[k] += __shfl_xor(lsum[k], o);
+    const int r = 2 * k + (lane >> 5);
+    if (write_ml && blockIdx.y == 0 && tl == 0 && r < rows)
+      part_ml[(rowbase + r) * splits + split] = make_float2(((lane >> 5) ? lm[2 * k + 1] : lm[2 * k]) * ln2, lsum[k]);
   }
-  const int64_t rowbase = grp * nq + q0;
-  if (blockIdx.y == 0 && wt == 0) {
+  // element i of acc[j]: row 4 g16 + i, coordinate 32 word0 + 16 j + n16
+  const float f = fp.gamma * ldexpf(1.0f, ne);
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int r = wr + 8 * k;
-      if (r < rows) part_ml[(rowbase + r) * splits + split] = make_float2(row_m[r], lsum[k]);
+  for (int j = 0; j < 2 * G; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g16 + i;
+      if (r < rows) part_y[((rowbase + r) * splits + split) * dp + 32 * word0 + 16 * j + n16] = acc[j][i] * f;
     }
-  }
-  if (active) {
-    // element i of acc[h]: row 4 g16 + i, coordinate 32 word + 16 h + n16
-    const float f = fp.gamma * ldexpf(1.0f, ne);
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * g16 + i;
-        if (r < rows) part_y[((rowbase + r) * splits + split) * dp + 32 * word + 16 * h + n16] = acc[h][i] * f;
-      }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -271,11 +400,18 @@ __device__ __forceinline__ float block_reduce(float x, float* sh, bool is_max) {
   return r;
 }
 
-// block per (group, query) row; dynamic LDS: d floats of the normalised sum
+// block per (group, query) row; dynamic LDS: the normalised sum (d floats)
+// and the partition partials (kThreads floats).  Thread t works on
+// coordinate t mod d' and partition t div d' (d' = min(d, kThreads), P =
+// kThreads / d' partitions): each partition sums every P-th split (or
+// coordinate, for Pi^T) with 8 loads in flight, and the partitions meet in
+// LDS.
 __global__ void __launch_bounds__(kThreads)
 attn_merge_kernel(const float* __restrict__ part_y, const float2* __restrict__ part_ml, int64_t splits, int dp,
                   int d, const float* __restrict__ pi, float* __restrict__ out, float* __restrict__ lse) {
-  extern __shared__ float yh[];
+  extern __shared__ float dyn[];
+  float* yh = dyn;          // [d]
+  float* parts = dyn + d;   // [kThreads]
   __shared__ float wts[kMaxSplits];
   __shared__ float sh[kWaves];
   const int tid = threadIdx.x;
@@ -294,16 +430,56 @@ attn_merge_kernel(const float* __restrict__ part_y, const float2* __restrict__ p
   }
   const float L = block_reduce(l, sh, false);  // (its barriers also publish wts)
   const float inv = 1.0f / L;
-  for (int c = tid; c < d; c += kThreads) {
+  const int dd = d < kThreads ? d : kThreads;
+  const int P = kThreads / dd;
+  const int part = tid / dd, cl = tid % dd;
+  // combine the splits: coordinate c, splits part, part + P, ...
+  for (int c0 = 0; c0 < d; c0 += dd) {
+    const int c = c0 + cl;
     float a = 0.0f;
-    for (int64_t s = 0; s < splits; ++s) a = fmaf(part_y[s * dp + c], wts[s], a);
-    yh[c] = a * inv;
+    if (part < P && c < d) {
+      int64_t s = part;
+      for (; s + 7 * P < splits; s += 8 * P) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = part_y[(s + u * P) * dp + c];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) a = fmaf(v[u], wts[s + u * P], a);
+      }
+      for (; s < splits; s += P) a = fmaf(part_y[s * dp + c], wts[s], a);
+    }
+    parts[tid] = a;
+    __syncthreads();
+    if (part == 0 && c < d) {
+      float t = 0.0f;
+      for (int q = 0; q < P; ++q) t += parts[q * dd + cl];
+      yh[c] = t * inv;
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  for (int i = tid; i < d; i += kThreads) {
+  // out_i = sum_c Pi[c][i] yh[c]: coordinate i, rows c = part, part + P, ...
+  for (int i0 = 0; i0 < d; i0 += dd) {
+    const int i = i0 + cl;
     float o = 0.0f;
-    for (int c = 0; c < d; ++c) o = fmaf(pi[int64_t(c) * d + i], yh[c], o);
-    out[row * d + i] = o;
+    if (part < P && i < d) {
+      int c = part;
+      for (; c + 7 * P < d; c += 8 * P) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = pi[int64_t(c + u * P) * d + i];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) o = fmaf(v[u], yh[c + u * P], o);
+      }
+      for (; c < d; c += P) o = fmaf(pi[int64_t(c) * d + i], yh[c], o);
+    }
+    parts[tid] = o;
+    __syncthreads();
+    if (part == 0 && i < d) {
+      float t = 0.0f;
+      for (int q = 0; q < P; ++q) t += parts[q * dd + cl];
+      out[row * d + i] = t;
+    }
+    __syncthreads();
   }
   if (tid == 0 && lse) lse[row] = M + logf(L);
 }
@@ -339,6 +515,8 @@ struct PvArgs {
   const uint32_t* vcodes;
   const float* vnorms;
   int W;
+  int word_base;
+  bool write_ml;
   float scale;
   int64_t tps;
   int qchunks;
@@ -348,10 +526,42 @@ struct PvArgs {
   int64_t splits;
 };
 
+template <int B, int F, int RQ, int G>
+void launch_pv_g(const PvArgs& a, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((attn_pv_kernel<B, F, RQ, G>), grid, dim3(kThreads), 0, s, a.scores, a.nq, a.n, a.vcodes,
+                     a.vnorms, a.W, a.word_base, a.write_ml, a.scale, a.tps, a.qchunks, a.fp, a.part_y, a.part_ml,
+                     a.splits);
+}
+
+template <int B, int F, int RQ>
+void launch_pv_rq(const PvArgs& a, dim3 grid, int g, hipStream_t s) {
+  switch (g) {
+    case 1: launch_pv_g<B, F, RQ, 1>(a, grid, s); break;
+    case 2: launch_pv_g<B, F, RQ, 2>(a, grid, s); break;
+    case 3: launch_pv_g<B, F, RQ, 3>(a, grid, s); break;
+    default: launch_pv_g<B, F, RQ, 4>(a, grid, s);
+  }
+}
+
+// full coordinate groups (4 words) in one launch, the last partial group
+// (W mod 4 words) in another
 template <int B, int F>
-hipError_t launch_pv(const PvArgs& a, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((attn_pv_kernel<B, F>), grid, dim3(kThreads), 0, s, a.scores, a.nq, a.n, a.vcodes, a.vnorms,
-                     a.W, a.scale, a.tps, a.qchunks, a.fp, a.part_y, a.part_ml, a.splits);
+hipError_t launch_pv(PvArgs a, dim3 grid, hipStream_t s) {
+  const int full = a.W / kWordsPerWave, rest = a.W % kWordsPerWave;
+  if (full > 0) {
+    grid.y = unsigned(full);
+    a.word_base = 0;
+    a.write_ml = true;
+    if (a.nq <= 4) launch_pv_rq<B, F, 4>(a, grid, 4, s);
+    else launch_pv_rq<B, F, kRows>(a, grid, 4, s);
+  }
+  if (rest > 0) {
+    grid.y = 1;
+    a.word_base = kWordsPerWave * full;
+    a.write_ml = full == 0;
+    if (a.nq <= 4) launch_pv_rq<B, F, 4>(a, grid, rest, s);
+    else launch_pv_rq<B, F, kRows>(a, grid, rest, s);
+  }
   return hipGetLastError();
 }
 
@@ -374,8 +584,8 @@ int64_t attn_split_tokens(const tq_ctx* hv, int64_t groups, int64_t nq, int64_t 
   if (const char* v = std::getenv("TQ_ATTN_SPLIT")) {
     tps = std::atoll(v);
   } else {
-    const int64_t per = int64_t((hv->words + kWaves - 1) / kWaves) * groups * ((nq + kRows - 1) / kRows);
-    const int64_t target = 4 * int64_t(hv->cus > 0 ? hv->cus : 256);
+    const int64_t per = int64_t((hv->words + kWordsPerWave - 1) / kWordsPerWave) * groups * ((nq + kRows - 1) / kRows);
+    const int64_t target = 8 * int64_t(hv->cus > 0 ? hv->cus : 256);  // waves: 2 per SIMD, one round
     int64_t splits = (target + per - 1) / per;
     const int64_t tiles = (n + kTile - 1) / kTile;
     splits = splits < tiles ? splits : tiles;
@@ -415,7 +625,8 @@ hipError_t launch_attention_values(const tq_ctx* hv, const float* scores, int64_
   const size_t ybytes = size_t(groups) * nq * a.splits * 32 * hv->words * sizeof(float);
   a.part_y = static_cast<float*>(partials);
   a.part_ml = reinterpret_cast<float2*>(static_cast<char*>(partials) + ws_align(ybytes));
-  const dim3 grid(unsigned(a.splits), unsigned((hv->words + kWaves - 1) / kWaves), unsigned(groups * a.qchunks));
+  const dim3 grid(unsigned((a.splits + kWaves - 1) / kWaves), unsigned((hv->words + kWordsPerWave - 1) / kWordsPerWave),
+                  unsigned(groups * a.qchunks));
   hipError_t e;
   switch (hv->code_bits) {
     case 1:
@@ -429,7 +640,8 @@ hipError_t launch_attention_values(const tq_ctx* hv, const float* scores, int64_
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(unsigned(groups * nq)), dim3(kThreads), size_t(hv->d) * sizeof(float),
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(unsigned(groups * nq)), dim3(kThreads),
+                     size_t(hv->d + kThreads) * sizeof(float),
                      stream, a.part_y, a.part_ml, a.splits, 32 * hv->words, hv->d, hv->d_pi, out, lse);
   return hipGetLastError();
 }

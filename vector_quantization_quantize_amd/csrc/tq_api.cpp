@@ -463,10 +463,23 @@ int tq_logits(tq_handle h, const float* queries, int64_t groups, int64_t nq, con
                     static_cast<hipStream_t>(stream));
 }
 
+int tq_dense_logits(const float* queries, int64_t groups, int64_t nq, const void* keys, int32_t key_dtype,
+                    int64_t n, int32_t d, int64_t ldk, float* scores, void* stream) {
+  if (groups < 0 || nq < 0 || n < 0 || d < 1 || d > 4096 || ldk < d) return TQ_EINVAL;
+  if (key_dtype != TQ_F32 && key_dtype != TQ_BF16) return TQ_EINVAL;
+  if (groups == 0 || nq == 0 || n == 0) return TQ_OK;
+  if (!queries || !keys || !scores || !aligned4(queries) || !aligned4(scores)) return TQ_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(keys) & (key_dtype == TQ_BF16 ? 1u : 3u)) != 0) return TQ_EINVAL;
+  if (groups > 65535 || (n + 3) / 4 > 0x7FFFFFFF) return TQ_EUNSUPPORTED;
+  const hipError_t e = tqdev::launch_dense_logits(queries, groups, nq, keys, key_dtype, n, d, ldk, scores,
+                                                  static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : TQ_EHIP;
+}
+
 int tq_pack_values(tq_handle h, const uint32_t* codes, int64_t groups, int64_t n, uint32_t* vcodes, void* stream) {
   if (!h || groups < 0 || n < 0) return TQ_EINVAL;
   if (groups == 0 || n == 0) return TQ_OK;
-  if (!codes || !vcodes || !aligned4(codes) || !aligned4(vcodes)) return TQ_EINVAL;
+  if (!codes || !vcodes || !aligned4(codes) || (reinterpret_cast<uintptr_t>(vcodes) & 15u) != 0) return TQ_EINVAL;
   if (groups > 65535 || (n + 31) / 32 > 0x7FFFFFFF) return TQ_EUNSUPPORTED;
   if (check_device(h) != TQ_OK) return TQ_EINVAL;
   const hipError_t e = tqdev::launch_pack_values(h, codes, groups, n, vcodes, static_cast<hipStream_t>(stream));
@@ -495,7 +508,8 @@ int tq_attention(tq_handle hk, tq_handle hv, const float* queries, int64_t group
     return e == hipSuccess ? TQ_OK : TQ_EHIP;
   }
   if (!queries || !kcodes || !ksigns || !knorms || !krnorms || !vcodes || !vnorms || !workspace) return TQ_EINVAL;
-  if (!aligned4(vcodes) || !aligned4(vnorms) || !aligned256(workspace)) return TQ_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(vcodes) & 15u) != 0 || !aligned4(vnorms) || !aligned256(workspace))
+    return TQ_EINVAL;
   const AttnWorkspace w = attn_workspace(hk, hv, groups, nq, n);
   if (workspace_bytes < w.total) return TQ_EINVAL;
   char* base = static_cast<char*>(workspace);

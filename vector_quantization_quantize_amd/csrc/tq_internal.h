@@ -221,6 +221,11 @@ inline size_t score_prep_bytes(int d, int64_t groups, int64_t nq) {
          (d >= kScoreGemmMinD ? score_qa_bytes(d, groups, nq) + ws_align(size_t(rows) * 4) : 0);
 }
 
+// Inner products with unquantized float32 (key_dtype 0) or bfloat16 (1)
+// keys (dense_logits.hip)
+hipError_t launch_dense_logits(const float* queries, int64_t groups, int64_t nq, const void* keys, int key_dtype,
+                               int64_t n, int d, int64_t ldk, float* scores, hipStream_t stream);
+
 // Decode attention (attention.hip).  Values in token blocks:
 // vcodes[group][ceil(n/32)][B][32 W], bit i of word (b, p, j) = bit p of the
 // index of coordinate j of token 32 b + i.
