@@ -190,6 +190,16 @@ TQ_API int tq_logits_topk(tq_handle h, const float* queries, int64_t groups, int
 TQ_API int tq_dequant_mse(tq_handle h, const uint32_t* codes, const float* norms, int64_t n,
                    float* khat, void* stream);
 
+/* Reconstruction with the QJL correction ("TurboQuant deep review", error
+ * compensation section: the corrected estimate is unbiased):
+ *   k_tilde = n * Pi^T ( c[idx] + rho * sqrt(pi/2) / d * G^T (2 beta - 1) ),
+ * the vector whose inner product with any query q equals the asymmetric
+ * score tq_logits estimates (the score is linear in q).  codes, signs,
+ * norms, rnorms: device, n packed keys; ktilde: device float [n][d].
+ * Float32 arithmetic.  Asynchronous on `stream`. */
+TQ_API int tq_dequant_prod(tq_handle h, const uint32_t* codes, const uint32_t* signs, const float* norms,
+                           const float* rnorms, int64_t n, float* ktilde, void* stream);
+
 /* The uncompressed comparison: raw inner products of float32 queries with
  * unquantized keys, the operation whose time the pages compare 4-bit keys
  * against ("TurboQuant digest", section 3: attention logits against 32-bit

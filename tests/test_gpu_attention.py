@@ -207,3 +207,30 @@ def test_dense_logits_match_exact_inner_products(env, d, nq, groups, n, dtype, l
         ref = tq.exact_inner_products(q[g], kg)
         bound = d * 2.0 ** -24 * (np.abs(q[g]).astype(np.float64) @ np.abs(kg).T) + 1e-30
         assert np.all(np.abs(s[g] - ref) <= bound), float((np.abs(s[g] - ref) / bound).max())
+
+
+@pytest.mark.parametrize("d,bits,n", [(128, 3, 300), (200, 4, 77), (33, 2, 65), (1536, 4, 40), (2, 3, 9),
+                                      (128, 5, 129)])
+def test_dequant_prod_matches_oracle(env, d, bits, n):
+    """Reconstruction with the QJL correction on the oracle's packed keys:
+    per key ||k_gpu - k_oracle|| <= 1e-5 ||k_oracle|| (the reconstruction
+    bar); inner products with it reproduce the oracle's scores within the
+    logit bar."""
+    torch, tqm = env
+    _announce(f"dequant_prod d={d} bits={bits} n={n}")
+    pr = _params(d, bits)
+    h = tqm.tq_init(d, bits, 0)
+    rs = np.random.default_rng(d + bits + n)
+    keys = rs.standard_normal((n, d)) * np.exp(0.5 * rs.standard_normal((n, 1)))
+    qz = tq.quantize(pr, keys)
+    codes, signs, norms, rnorms = tq.pack(pr, qz)
+    got = _cpu(tqm.tq_dequant_prod(h, _dev(torch, codes.view(np.int32)), _dev(torch, signs.view(np.int32)),
+                                   _dev(torch, norms), _dev(torch, rnorms))).astype(np.float64)
+    ref = tq.dequant_prod(pr, qz.idx, qz.beta, norms.astype(np.float64), rnorms.astype(np.float64))
+    err = np.sqrt(((got - ref) ** 2).sum(axis=1))
+    size = np.sqrt((ref ** 2).sum(axis=1))
+    assert np.all(err <= 1e-5 * size + 1e-30), float((err / np.maximum(size, 1e-30)).max())
+    q = rs.standard_normal((5, d))
+    s_ref = tq.scores(pr, q, qz.idx, qz.beta, norms.astype(np.float64), rnorms.astype(np.float64))
+    bar = 1e-3 * np.sqrt((q * q).sum(axis=1))[:, None] * norms.astype(np.float64)[None, :]
+    assert np.all(np.abs(q @ got.T - s_ref) <= bar)

@@ -74,6 +74,7 @@ def test_bad_arguments_are_rejected(tqm):
                               None) == tqm.TQ_EINVAL
     assert lib.tq_logits_topk_workspace_size(None, 1, 1, 1, 10) == 0
     assert lib.tq_pack_values(None, None, 1, 1, None, None) == tqm.TQ_EINVAL
+    assert lib.tq_dequant_prod(None, None, None, None, None, 1, None, None) == tqm.TQ_EINVAL
     assert lib.tq_dense_logits(None, 1, 1, None, 0, 1, 128, 128, None, None) == tqm.TQ_EINVAL
     assert lib.tq_dense_logits(None, 1, 1, None, 2, 1, 128, 128, None, None) == tqm.TQ_EINVAL
     assert lib.tq_attention_workspace_size(None, None, 1, 1, 1) == 0

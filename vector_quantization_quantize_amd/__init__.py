@@ -26,7 +26,7 @@ TQ_FORMAT_VERSION = 1
 # every symbol include/tq.h declares
 EXPORTS = ("tq_init", "tq_init_explicit", "tq_destroy", "tq_get_layout", "tq_host_params",
            "tq_params_hash", "tq_quantize", "tq_logits_workspace_size", "tq_logits",
-           "tq_logits_topk_workspace_size", "tq_logits_topk", "tq_dequant_mse", "tq_dense_logits", "tq_pack_values",
+           "tq_logits_topk_workspace_size", "tq_logits_topk", "tq_dequant_mse", "tq_dequant_prod", "tq_dense_logits", "tq_pack_values",
            "tq_attention_workspace_size", "tq_attention", "tq_strerror")
 
 
@@ -68,6 +68,7 @@ def _lib():
         "tq_dequant_mse": (ctypes.c_int, [vp, vp, vp, i64, vp, vp]),
         "tq_logits_topk_workspace_size": (sz, [vp, i64, i64, i64, i32]),
         "tq_logits_topk": (ctypes.c_int, [vp, vp, i64, i64, vp, vp, vp, vp, i64, i32, vp, vp, vp, sz, vp]),
+        "tq_dequant_prod": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, vp, vp]),
         "tq_dense_logits": (ctypes.c_int, [vp, i64, i64, vp, i32, i64, i32, i64, vp, vp]),
         "tq_pack_values": (ctypes.c_int, [vp, vp, i64, i64, vp, vp]),
         "tq_attention_workspace_size": (sz, [vp, vp, i64, i64, i64]),
@@ -281,6 +282,18 @@ def tq_dequant_mse(h, codes, norms, khat=None, stream=None):
     _check("tq_dequant_mse", _lib().tq_dequant_mse(h.ptr, _ptr(codes), _ptr(norms), n, _ptr(khat),
                                                    _stream(stream)))
     return khat
+
+
+def tq_dequant_prod(h, codes, signs, norms, rnorms, ktilde=None, stream=None):
+    """Reconstruction with the QJL correction (n, d) float32: inner products
+    with it equal tq_logits' scores."""
+    import torch
+    n = norms.shape[0]
+    if ktilde is None:
+        ktilde = torch.empty((n, h.d), dtype=torch.float32, device=norms.device)
+    _check("tq_dequant_prod", _lib().tq_dequant_prod(h.ptr, _ptr(codes), _ptr(signs), _ptr(norms), _ptr(rnorms),
+                                                     n, _ptr(ktilde), _stream(stream)))
+    return ktilde
 
 
 def tq_dense_logits(queries, keys, n=None, scores=None, stream=None):

@@ -283,6 +283,85 @@ dequant_ref_kernel(const uint32_t* __restrict__ codes, const float* __restrict__
   }
 }
 
+// ---------------------------------------------------------------------------
+// reconstruction with the correction: k_tilde = n Pi^T (c[idx] + rho kappa
+// G^T (2 beta - 1)), kappa = sqrt(pi/2) / d (the vector whose inner product
+// with any query is the asymmetric score).  Block per tile of tk keys:
+// t = c[idx] and the signs go to LDS; t += rho kappa G^T s; then Pi^T t.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads)
+dequant_prod_ref_kernel(const uint32_t* __restrict__ codes, const uint32_t* __restrict__ signs,
+                        const float* __restrict__ norms, const float* __restrict__ rnorms, int64_t n, int d,
+                        int code_bits, int words, int tk, const float* __restrict__ pi,
+                        const float* __restrict__ g, Codebook cb, float kappa, float* __restrict__ out) {
+  extern __shared__ float smem[];
+  const int ds = d + 1;
+  float* t = smem;                       // [tk][ds] c[idx], then c + rho kappa G^T s
+  float* sg = smem + size_t(tk) * ds;    // [tk][ds] 2 beta - 1
+  float* lvl = sg + size_t(tk) * ds;
+  const int tid = threadIdx.x;
+  const int64_t base = int64_t(blockIdx.x) * tk;
+  if (tid < kMaxLevels) lvl[tid] = cb.c[tid];
+  __syncthreads();
+  for (int p = tid; p < tk * words; p += kThreads) {
+    const int k = p / words, w = p - k * words;
+    const int64_t key = base + k;
+    uint32_t plane[4] = {0u, 0u, 0u, 0u};
+    uint32_t sw = 0u;
+    if (key < n) {
+      for (int q = 0; q < code_bits; ++q) plane[q] = codes[(key * code_bits + q) * words + w];
+      sw = signs[key * words + w];
+    }
+    for (int b = 0; b < 32; ++b) {
+      const int j = 32 * w + b;
+      if (j >= d) break;
+      int idx = 0;
+      for (int q = 0; q < code_bits; ++q) idx |= int((plane[q] >> b) & 1u) << q;
+      t[k * ds + j] = lvl[idx];
+      sg[k * ds + j] = (sw >> b) & 1u ? 1.0f : -1.0f;
+    }
+  }
+  __syncthreads();
+  const int groups = tk / 4;
+  // (G^T s)_i = sum_j G[j][i] s_j; each (key, i) of t is written by one thread
+  for (int p = tid; p < groups * d; p += kThreads) {
+    const int kg = p / d, i = p - kg * d;
+    const float* s0 = sg + (4 * kg) * ds;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int j = 0; j < d; ++j) {
+      const float w = g[size_t(j) * d + i];
+      a0 = fmaf(w, s0[j], a0);
+      a1 = fmaf(w, s0[ds + j], a1);
+      a2 = fmaf(w, s0[2 * ds + j], a2);
+      a3 = fmaf(w, s0[3 * ds + j], a3);
+    }
+    const float acc[4] = {a0, a1, a2, a3};
+    for (int r = 0; r < 4; ++r) {
+      const int64_t key = base + 4 * kg + r;
+      const float rho = key < n ? rnorms[key] : 0.0f;
+      t[(4 * kg + r) * ds + i] = fmaf(rho * kappa, acc[r], t[(4 * kg + r) * ds + i]);
+    }
+  }
+  __syncthreads();
+  for (int p = tid; p < groups * d; p += kThreads) {
+    const int kg = p / d, j = p - kg * d;
+    const float* c0 = t + (4 * kg) * ds;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int i = 0; i < d; ++i) {
+      const float w = pi[size_t(i) * d + j];  // (Pi^T t)_j = sum_i Pi[i][j] t_i
+      a0 = fmaf(w, c0[i], a0);
+      a1 = fmaf(w, c0[ds + i], a1);
+      a2 = fmaf(w, c0[2 * ds + i], a2);
+      a3 = fmaf(w, c0[3 * ds + i], a3);
+    }
+    const float acc[4] = {a0, a1, a2, a3};
+    for (int r = 0; r < 4; ++r) {
+      const int64_t key = base + 4 * kg + r;
+      if (key < n) out[key * d + j] = norms[key] * acc[r];
+    }
+  }
+}
+
 // keys per tile so that `buffers` LDS arrays of tk x (d+1) floats fit in
 // `budget` bytes; a multiple of 4, at least 4
 int tile_keys(int d, int buffers, size_t budget, int cap) {
@@ -350,6 +429,21 @@ hipError_t launch_dequant_v1(const tq_ctx* h, const uint32_t* codes, const float
   const int64_t blocks = (n + tk - 1) / tk;
   hipLaunchKernelGGL(dequant_ref_kernel, dim3(unsigned(blocks)), dim3(kThreads), lds, stream, codes, norms,
                      n, d, h->code_bits, h->words, tk, h->d_pi, h->cb, khat);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_prod_v1(const tq_ctx* h, const uint32_t* codes, const uint32_t* signs,
+                                  const float* norms, const float* rnorms, int64_t n, float* out,
+                                  hipStream_t stream) {
+  const int d = h->d;
+  const int tk = tile_keys(d, 2, 64 * 1024, 64);
+  const size_t lds = (size_t(2) * tk * (d + 1) + kMaxLevels) * sizeof(float);
+  hipError_t e = allow_lds(dequant_prod_ref_kernel, lds);
+  if (e != hipSuccess) return e;
+  const int64_t blocks = (n + tk - 1) / tk;
+  const float kappa = float(1.2533141373155002512 / double(d));  // sqrt(pi/2) / d
+  hipLaunchKernelGGL(dequant_prod_ref_kernel, dim3(unsigned(blocks)), dim3(kThreads), lds, stream, codes, signs,
+                     norms, rnorms, n, d, h->code_bits, h->words, tk, h->d_pi, h->d_g, h->cb, kappa, out);
   return hipGetLastError();
 }
 

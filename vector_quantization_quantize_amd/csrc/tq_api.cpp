@@ -463,6 +463,18 @@ int tq_logits(tq_handle h, const float* queries, int64_t groups, int64_t nq, con
                     static_cast<hipStream_t>(stream));
 }
 
+int tq_dequant_prod(tq_handle h, const uint32_t* codes, const uint32_t* signs, const float* norms,
+                    const float* rnorms, int64_t n, float* ktilde, void* stream) {
+  if (!h || n < 0) return TQ_EINVAL;
+  if (n == 0) return TQ_OK;
+  if (!codes || !signs || !norms || !rnorms || !ktilde) return TQ_EINVAL;
+  if (n > int64_t(0x7FFFFFFF) * 4) return TQ_EUNSUPPORTED;
+  if (check_device(h) != TQ_OK) return TQ_EINVAL;
+  const hipError_t e = tqdev::launch_dequant_prod_v1(h, codes, signs, norms, rnorms, n, ktilde,
+                                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : TQ_EHIP;
+}
+
 int tq_dense_logits(const float* queries, int64_t groups, int64_t nq, const void* keys, int32_t key_dtype,
                     int64_t n, int32_t d, int64_t ldk, float* scores, void* stream) {
   if (groups < 0 || nq < 0 || n < 0 || d < 1 || d > 4096 || ldk < d) return TQ_EINVAL;

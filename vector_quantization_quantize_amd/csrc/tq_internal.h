@@ -200,6 +200,10 @@ hipError_t launch_fill_u32(unsigned int* p, int64_t n, unsigned int v, hipStream
 
 hipError_t launch_dequant_v1(const tq_ctx* h, const uint32_t* codes, const float* norms, int64_t n,
                              float* khat, hipStream_t stream);
+// k_tilde = n Pi^T (c[idx] + rho sqrt(pi/2)/d G^T (2 beta - 1)), float32
+hipError_t launch_dequant_prod_v1(const tq_ctx* h, const uint32_t* codes, const uint32_t* signs,
+                                  const float* norms, const float* rnorms, int64_t n, float* out,
+                                  hipStream_t stream);
 
 // float offset between a query's v and w vectors in the workspace, and the
 // stride between queries: v at q*vw_stride, w at q*vw_stride + vw_half
