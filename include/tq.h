@@ -118,6 +118,20 @@ TQ_API int tq_init(int32_t d, int32_t bits, uint64_t seed, tq_handle* out);
  * tutorial page's 4-D example.  Orthogonality of `pi` is not checked. */
 TQ_API int tq_init_explicit(int32_t d, int32_t bits, const float* pi, const float* g, tq_handle* out);
 
+/* As tq_init with a randomized Hadamard rotation in place of the Haar one
+ * ("TurboQuant tutorial", PolarQuant section: its 4-D example rotates with
+ * a +-1/2 matrix, the Hadamard matrix of order 4 over 2):
+ *   Pi = H diag(sigma) / sqrt(d),  H[i][j] = (-1)^popcount(i & j)
+ * (Sylvester order), sigma_j = -1 when bit 63 of counter j of stream 2 of
+ * the seed is set, else +1; entries rounded to float32.  G and the codebook
+ * are tq_init's.  d a power of two in [2, 4096]; every entry point then
+ * works as for a tq_init handle (the rotation is applied as a dense matrix). */
+TQ_API int tq_init_hadamard(int32_t d, int32_t bits, uint64_t seed, tq_handle* out);
+
+/* Host only, no HIP call: the rotation tq_init_hadamard(d, ., seed) uses,
+ * float[d*d] row-major into pi. */
+TQ_API int tq_hadamard_rotation(int32_t d, uint64_t seed, float* pi);
+
 /* Release the handle and its device tables.  NULL is accepted. */
 TQ_API int tq_destroy(tq_handle h);
 

@@ -232,6 +232,32 @@ def init(d, bits, seed):
     return Params(d, bits, int(seed), pi, g, c32, thresholds_from_centroids(c32))
 
 
+def hadamard_rotation(d, seed):
+    """Randomized Hadamard rotation H diag(sigma) / sqrt(d) (float64 of the
+    float32 entries): H the Sylvester Hadamard matrix (scipy), sigma the
+    stream-2 signs.  The tutorial page's 4-D example rotates with H_4 / 2.
+    d must be a power of two."""
+    if d < 2 or d > 4096 or d & (d - 1):
+        raise ValueError("d must be a power of two in [2, 4096]")
+    from scipy.linalg import hadamard
+    sigma = rng.signs(seed, 2, d)
+    scale = np.float32(1.0 / np.sqrt(d))
+    return (hadamard(d).astype(np.float64) * sigma[None, :] * np.float64(scale)).astype(np.float32).astype(np.float64)
+
+
+def init_hadamard(d, bits, seed):
+    """Parameters with the randomized Hadamard rotation; G and the codebook
+    as in ``init``."""
+    if not (2 <= bits <= 5):
+        raise ValueError("bits must lie in [2, 5]")
+    levels = 1 << (bits - 1)
+    pi = hadamard_rotation(d, seed)
+    g = gaussian_projection(d, seed).astype(np.float32).astype(np.float64)
+    c64, _ = sphere_codebook_fp64(d, levels)
+    c32 = c64.astype(np.float32).astype(np.float64)
+    return Params(d, bits, int(seed), pi, g, c32, thresholds_from_centroids(c32))
+
+
 def explicit(d, bits, pi, g):
     """Parameters with given matrices (codebook still from ``d`` and ``bits``)."""
     levels = 1 << (bits - 1)

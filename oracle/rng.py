@@ -20,6 +20,8 @@ published generator independently, from this definition:
   [0, 1), ``R = sqrt(-2 ln u1)``; element ``2i`` is ``R cos(2 pi u2)`` and
   element ``2i+1`` is ``R sin(2 pi u2)`` (Box & Muller 1958).  An odd count
   drops the last sine.
+* Random signs (stream 2, the randomized Hadamard rotation): sign ``j`` is
+  -1 when bit 63 of counter ``j`` is set, else +1.
 """
 import numpy as np
 
@@ -70,3 +72,9 @@ def normals(seed, stream, count):
     out[0::2] = radius * np.cos(theta)
     out[1::2] = radius * np.sin(theta)
     return out[:count]
+
+
+def signs(seed, stream, count):
+    """``count`` random signs (float64 +-1) of the given stream."""
+    bits = uniform_bits(seed, stream, count)
+    return np.where((bits >> np.uint64(63)) != 0, -1.0, 1.0)

@@ -227,3 +227,25 @@ def test_search_full_keys(env, name):
 def test_cone_subset(env):
     w = env[2].WORKLOADS["cone"].scaled(n=20000, nq=16)
     _sampled_check(env, w, sample=1024)
+
+
+@pytest.mark.parametrize("d,bits,key_dtype,groups,n,nq", [
+    (128, 3, "bf16", 2, 1000, 4),   # the matrix-core quantize path (bf16, d = 128) and the lookup-table scorer
+    (128, 4, "f32", 1, 300, 20),    # general quantize, matrix-core scorer
+    (64, 2, "f32", 3, 200, 5),
+    (256, 5, "f32", 1, 100, 3),
+    (4, 3, "f32", 1, 50, 2),
+])
+def test_hadamard_rotation_full(env, d, bits, key_dtype, groups, n, nq):
+    """A randomized Hadamard handle through every entry point against the
+    oracle built with the same rotation (oracle.params.init_hadamard)."""
+    torch, tqm, _ = env
+    _announce(f"hadamard d={d} bits={bits} {key_dtype} groups={groups} n={n} nq={nq}")
+    pr = P.init_hadamard(d, bits, 7)
+    h = tqm.tq_init_hadamard(d, bits, 7)
+    rs = np.random.default_rng(d + bits)
+    keys = rs.standard_normal((groups * n, d)) * np.exp(0.5 * rs.standard_normal((groups * n, 1)))
+    if key_dtype == "bf16":
+        keys = np.asarray(torch.tensor(keys).bfloat16().float().numpy(), dtype=np.float64)
+    check_full(env, d, bits, keys, rs.standard_normal((groups, nq, d)).astype(np.float32), key_dtype=key_dtype,
+               h=h, pr=pr)

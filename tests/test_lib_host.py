@@ -52,6 +52,23 @@ def test_host_params_match_oracle(tqm, d, bits, seed):
     assert _ulps(t, pr.thresholds).max() <= 1
 
 
+@pytest.mark.parametrize("d", [2, 4, 64, 128, 1024])
+def test_hadamard_rotation_matches_oracle(tqm, d):
+    """The C++ and oracle randomized Hadamard rotations agree bit for bit
+    (both round +-1/sqrt(d) once to float32 and draw the same signs)."""
+    pi = tqm.tq_hadamard_rotation(d, 7)
+    assert np.array_equal(pi.astype(np.float64), P.hadamard_rotation(d, 7))
+
+
+def test_hadamard_rejects_other_d(tqm):
+    lib = tqm._lib()
+    out = ctypes.c_void_p()
+    buf = np.empty(100 * 100, dtype=np.float32)
+    for d in (1, 3, 100, 8192):
+        assert lib.tq_init_hadamard(d, 3, 0, ctypes.byref(out)) == tqm.TQ_EINVAL
+        assert lib.tq_hadamard_rotation(d, 0, buf.ctypes.data) == tqm.TQ_EINVAL
+
+
 def test_host_params_d1536(tqm):
     pi, g, c, t = tqm.tq_host_params(1536, 4, 0)
     pr = P.init(1536, 4, 0)

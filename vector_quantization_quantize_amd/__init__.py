@@ -24,7 +24,7 @@ TQ_BF16 = 1
 TQ_FORMAT_VERSION = 1
 
 # every symbol include/tq.h declares
-EXPORTS = ("tq_init", "tq_init_explicit", "tq_destroy", "tq_get_layout", "tq_host_params",
+EXPORTS = ("tq_init", "tq_init_explicit", "tq_init_hadamard", "tq_hadamard_rotation", "tq_destroy", "tq_get_layout", "tq_host_params",
            "tq_params_hash", "tq_quantize", "tq_logits_workspace_size", "tq_logits",
            "tq_logits_topk_workspace_size", "tq_logits_topk", "tq_dequant_mse", "tq_dequant_prod", "tq_dense_logits", "tq_pack_values",
            "tq_attention_workspace_size", "tq_attention", "tq_strerror")
@@ -58,6 +58,8 @@ def _lib():
     sig = {
         "tq_init": (ctypes.c_int, [i32, i32, u64, ctypes.POINTER(vp)]),
         "tq_init_explicit": (ctypes.c_int, [i32, i32, fp, fp, ctypes.POINTER(vp)]),
+        "tq_init_hadamard": (ctypes.c_int, [i32, i32, u64, ctypes.POINTER(vp)]),
+        "tq_hadamard_rotation": (ctypes.c_int, [i32, u64, vp]),
         "tq_destroy": (ctypes.c_int, [vp]),
         "tq_get_layout": (ctypes.c_int, [vp, ctypes.POINTER(Layout)]),
         "tq_host_params": (ctypes.c_int, [i32, i32, u64, vp, vp, vp, vp]),
@@ -134,6 +136,23 @@ def tq_init(d, bits, seed):
     _check("tq_init", _lib().tq_init(int(d), int(bits), ctypes.c_uint64(int(seed) & (2 ** 64 - 1)),
                                      ctypes.byref(out)))
     return Handle(out)
+
+
+def tq_init_hadamard(d, bits, seed):
+    """Handle with the randomized Hadamard rotation (d a power of two)."""
+    out = ctypes.c_void_p()
+    _check("tq_init_hadamard", _lib().tq_init_hadamard(int(d), int(bits), ctypes.c_uint64(int(seed) & (2 ** 64 - 1)),
+                                                       ctypes.byref(out)))
+    return Handle(out)
+
+
+def tq_hadamard_rotation(d, seed):
+    """Host-only: the rotation tq_init_hadamard uses (numpy float32 (d, d))."""
+    import numpy as np
+    pi = np.empty((d, d), dtype=np.float32)
+    _check("tq_hadamard_rotation", _lib().tq_hadamard_rotation(int(d), ctypes.c_uint64(int(seed) & (2 ** 64 - 1)),
+                                                               pi.ctypes.data))
+    return pi
 
 
 def tq_init_explicit(d, bits, pi, g):

@@ -312,6 +312,22 @@ int lloyd_max_sphere(int d, int levels, double* c) {
 }
 
 // ---------------------------------------------------------------------------
+// Randomized Hadamard rotation: Pi = H diag(sigma) / sqrt(d), H the Sylvester
+// Hadamard matrix (H[i][j] = (-1)^popcount(i & j)), sigma_j = -1 when the top
+// bit of counter j of stream 2 is set, else +1.
+// ---------------------------------------------------------------------------
+int hadamard_rotation(int d, uint64_t seed, float* pi) {
+  if (d < 2 || d > 4096 || (d & (d - 1)) != 0) return -1;
+  const uint64_t state = stream_state(seed, 2);
+  const float a = float(1.0 / std::sqrt(double(d)));
+  std::vector<float> sigma(d);
+  for (int j = 0; j < d; ++j) sigma[j] = (counter_bits(state, uint64_t(j)) >> 63) ? -a : a;
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j) pi[size_t(i) * d + j] = (__builtin_popcount(unsigned(i & j)) & 1) ? -sigma[j] : sigma[j];
+  return 0;
+}
+
+// ---------------------------------------------------------------------------
 // Public assembly
 // ---------------------------------------------------------------------------
 int build_params(int d, int bits, uint64_t seed, float* pi, float* g, float* centroids, float* thresholds) {

@@ -19,6 +19,12 @@ void haar_from_gaussian(int d, const double* a, double* q);
 // uniform unit vector in R^d.  Returns 0 on convergence.
 int lloyd_max_sphere(int d, int levels, double* c);
 
+// Randomized Hadamard rotation H diag(sigma) / sqrt(d) (float[d*d] row-major):
+// H[i][j] = (-1)^popcount(i & j) (Sylvester), sigma_j = -1 when bit 63 of
+// counter j of stream 2 is set, else +1.  d a power of two in [2, 4096];
+// returns 0, or -1 for another d.
+int hadamard_rotation(int d, uint64_t seed, float* pi);
+
 // Fill any of pi, g (float[d*d]), centroids (float[L]), thresholds
 // (float[L-1]); NULL outputs are skipped.  Returns 0, or < 0 on bad
 // arguments / non-convergence.

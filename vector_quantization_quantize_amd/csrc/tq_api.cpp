@@ -289,8 +289,12 @@ int tq_host_params(int32_t d, int32_t bits, uint64_t seed, float* pi, float* g, 
   }
 }
 
+// rotation: kRotHaar (from the seed), kRotExplicit (pi_in, g_in given),
+// kRotHadamard (randomized Hadamard from the seed, G from the seed)
+enum { kRotHaar = 0, kRotExplicit = 1, kRotHadamard = 2 };
+
 static int init_common(int32_t d, int32_t bits, const float* pi_in, const float* g_in, uint64_t seed,
-                       tq_handle* out) {
+                       tq_handle* out, int rotation = kRotHaar) {
   if (!out) return TQ_EINVAL;
   *out = nullptr;
   if (d < 2 || d > 4096 || bits < 2 || bits > 5) return TQ_EINVAL;
@@ -306,10 +310,14 @@ static int init_common(int32_t d, int32_t bits, const float* pi_in, const float*
     h->centroids.resize(levels);
     h->thresholds.resize(levels - 1 > 0 ? levels - 1 : 1);
     int rc;
-    if (pi_in) {
+    if (rotation == kRotExplicit) {
       std::memcpy(h->pi.data(), pi_in, dd * sizeof(float));
       std::memcpy(h->g.data(), g_in, dd * sizeof(float));
       rc = tqhost::build_params(d, bits, 0, nullptr, nullptr, h->centroids.data(), h->thresholds.data());
+    } else if (rotation == kRotHadamard) {
+      rc = tqhost::hadamard_rotation(d, seed, h->pi.data());
+      if (rc == 0)
+        rc = tqhost::build_params(d, bits, seed, nullptr, h->g.data(), h->centroids.data(), h->thresholds.data());
     } else {
       rc = tqhost::build_params(d, bits, seed, h->pi.data(), h->g.data(), h->centroids.data(),
                                 h->thresholds.data());
@@ -343,7 +351,20 @@ int tq_init(int32_t d, int32_t bits, uint64_t seed, tq_handle* out) {
 
 int tq_init_explicit(int32_t d, int32_t bits, const float* pi, const float* g, tq_handle* out) {
   if (!pi || !g) return TQ_EINVAL;
-  return init_common(d, bits, pi, g, 0, out);
+  return init_common(d, bits, pi, g, 0, out, kRotExplicit);
+}
+
+int tq_init_hadamard(int32_t d, int32_t bits, uint64_t seed, tq_handle* out) {
+  if (d < 2 || d > 4096 || (d & (d - 1)) != 0) {
+    if (out) *out = nullptr;
+    return TQ_EINVAL;
+  }
+  return init_common(d, bits, nullptr, nullptr, seed, out, kRotHadamard);
+}
+
+int tq_hadamard_rotation(int32_t d, uint64_t seed, float* pi) {
+  if (!pi || d < 2 || d > 4096 || (d & (d - 1)) != 0) return TQ_EINVAL;
+  return tqhost::hadamard_rotation(d, seed, pi) == 0 ? TQ_OK : TQ_EINVAL;
 }
 
 int tq_destroy(tq_handle h) {
