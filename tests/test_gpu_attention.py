@@ -234,3 +234,51 @@ def test_dequant_prod_matches_oracle(env, d, bits, n):
     s_ref = tq.scores(pr, q, qz.idx, qz.beta, norms.astype(np.float64), rnorms.astype(np.float64))
     bar = 1e-3 * np.sqrt((q * q).sum(axis=1))[:, None] * norms.astype(np.float64)[None, :]
     assert np.all(np.abs(q @ got.T - s_ref) <= bar)
+
+
+def test_attention_long_context_full_size(env):
+    """The long-context shape in the launch configuration the bench times
+    (32 key heads x 131072 tokens, 4 queries per head, d = 128, 3 bits, the
+    default splits): every head quantized by the library, then two sampled
+    heads' packed keys and values replaced by the oracle's own (decode
+    parity: the oracle's output is computed from its own packing) and
+    compared with the oracle's attention under the derived tolerance."""
+    torch, tqm = env
+    from vector_quantization_quantize_amd import workloads as wl
+    w = wl.WORKLOADS["long_context"]
+    _announce(f"attention full size {w.name} groups={w.groups} n={w.n} nq={w.nq}")
+    keys = wl.keys(w)
+    vals = wl.keys(w, 1)
+    queries = wl.queries(w)
+    prk, prv = _params(w.d, w.bits, 0), _params(w.d, w.bits, 1)
+    hk, hv = tqm.tq_init(w.d, w.bits, 0), tqm.tq_init(w.d, w.bits, 1)
+    kp = tqm.tq_quantize(hk, _dev(torch, keys, torch.bfloat16))
+    vc, _, vn, _ = tqm.tq_quantize(hv, _dev(torch, vals, torch.bfloat16))
+    sampled = (3, 29)
+    oracle = {}
+    for g in sampled:
+        sl = slice(g * w.n, (g + 1) * w.n)
+        kz, vz = tq.quantize(prk, keys[sl].astype(np.float64)), tq.quantize(prv, vals[sl].astype(np.float64))
+        packed = tq.pack(prk, kz)
+        for dst, src in zip(kp, packed):
+            dst[sl] = _dev(torch, src.view(np.int32) if src.dtype == np.uint32 else src)
+        vc[sl] = _dev(torch, tq.pack_codes(vz.idx, prv.code_bits).view(np.int32))
+        vn[sl] = _dev(torch, vz.norms.astype(np.float32))
+        oracle[g] = (kz, vz, packed[2].astype(np.float64), packed[3].astype(np.float64),
+                     vz.norms.astype(np.float32).astype(np.float64))
+    blocks = tqm.tq_pack_values(hv, vc, groups=w.groups, n=w.n)
+    out, lse = tqm.tq_attention(hk, hv, _dev(torch, queries), *kp, blocks, vn, n=w.n)
+    torch.cuda.synchronize()
+    out, lse = _cpu(out), _cpu(lse)
+    scale = 1.0 / math.sqrt(w.d)
+    for g in sampled:
+        kz, vz, kn, kr, vnn = oracle[g]
+        o, l = tq.attention(prk, prv, queries[g], kz.idx, kz.beta, kn, kr, vz.idx, vnn, scale)
+        vh = tq.dequant_mse(prv, vz.idx, vnn)
+        qn = np.sqrt((queries[g].astype(np.float64) ** 2).sum(axis=1))
+        delta = scale * 1e-3 * qn * kn.max()
+        tol = np.expm1(2 * delta)[:, None] * np.abs(vh).max(axis=0)[None, :] + 2e-5 * np.sqrt((vh * vh).sum(axis=1)).max()
+        err = np.abs(out[g] - o)
+        assert np.all(err <= tol), (g, float((err / tol).max()))
+        assert np.all(np.abs(lse[g] - l) <= delta + 1e-5 * np.maximum(1.0, np.abs(l)))
+        print(f"head {g}: worst |error| / tolerance {float((err / tol).max()):.3g}")
