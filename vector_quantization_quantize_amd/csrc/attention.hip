@@ -130,7 +130,7 @@ struct TileIn {
   uint32_t w[B][(2 * G + 3) / 4];
 };
 
-// RQ: query rows per wave (4 or 16; the matrix-core M is 16 either way,
+// RQ: query rows per wave (4, 8 or 16; the matrix-core M is 16 either way,
 // rows past RQ stay 0).  G: words in the wave's coordinate group (4, or
 // W mod 4 for the last group); the group starts at word word_base + 4
 // blockIdx.y.  Blocks with blockIdx.y = 0 of the launch that has write_ml
@@ -296,8 +296,8 @@ attn_pv_kernel(const float* __restrict__ scores, int64_t nq, int64_t n, const ui
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float fr = f[i];
-          if constexpr (RQ > 4) {
-            fr = g16 == 1 ? f[4 + i] : fr;
+          if constexpr (RQ > 4) fr = g16 == 1 ? f[4 + i] : fr;
+          if constexpr (RQ > 8) {
             fr = g16 == 2 ? f[8 + i] : fr;
             fr = g16 == 3 ? f[12 + i] : fr;
           }
@@ -548,19 +548,22 @@ void launch_pv_rq(const PvArgs& a, dim3 grid, int g, hipStream_t s) {
 template <int B, int F>
 hipError_t launch_pv(PvArgs a, dim3 grid, hipStream_t s) {
   const int full = a.W / kWordsPerWave, rest = a.W % kWordsPerWave;
+  auto go = [&](int g) {
+    if (a.nq <= 4) launch_pv_rq<B, F, 4>(a, grid, g, s);
+    else if (a.nq <= 8) launch_pv_rq<B, F, 8>(a, grid, g, s);
+    else launch_pv_rq<B, F, kRows>(a, grid, g, s);
+  };
   if (full > 0) {
     grid.y = unsigned(full);
     a.word_base = 0;
     a.write_ml = true;
-    if (a.nq <= 4) launch_pv_rq<B, F, 4>(a, grid, 4, s);
-    else launch_pv_rq<B, F, kRows>(a, grid, 4, s);
+    go(4);
   }
   if (rest > 0) {
     grid.y = 1;
     a.word_base = kWordsPerWave * full;
     a.write_ml = full == 0;
-    if (a.nq <= 4) launch_pv_rq<B, F, 4>(a, grid, rest, s);
-    else launch_pv_rq<B, F, kRows>(a, grid, rest, s);
+    go(rest);
   }
   return hipGetLastError();
 }
