@@ -183,30 +183,6 @@ attn_pv_kernel(const float* __restrict__ scores, int64_t nq, int64_t n, const ui
   const int64_t t1 = int64_t(__builtin_amdgcn_readfirstlane(int(t1r >> 32))) << 32 |
                      uint32_t(__builtin_amdgcn_readfirstlane(int(t1r & 0xFFFFFFFF)));
 
-  // ---- the split's largest norm (weights carry n / 2^e <= 1 times at most
-  // 2^kSlack, so their float16 pieces cannot overflow); eight loads in
-  // flight per lane
-  const float a = scale * 1.4426950408889634f;  // weights are 2^(a s - max)
-  float nmax = 0.0f;
-  for (int64_t tb = t0; tb < t1; tb += 8 * 64) {
-    float nv[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t t = tb + 64 * u + lane;
-      nv[u] = vnorms[t < t1 ? t : t1 - 1];
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) nmax = fmaxf(nmax, nv[u]);
-  }
-  nmax = wave_max(nmax);
-  int ne = 0;
-  if (nmax > 0.0f && nmax < INFINITY) (void)frexpf(nmax, &ne);
-  const float nscale = ldexpf(1.0f, -ne);
-  // reference row maxima of a s (the same in every lane)
-  float lm[RQ];
-#pragma unroll
-  for (int r = 0; r < RQ; ++r) lm[r] = -INFINITY;
-
   // ---- 32-token tiles, inputs loaded two tiles ahead
   const int n16 = lane & 15, g16 = lane >> 4, tl = lane & 31;
   // every load is unconditional from a clamped, valid address (a tile past
@@ -255,6 +231,36 @@ attn_pv_kernel(const float* __restrict__ scores, int64_t nq, int64_t n, const ui
   // slots would move registers whose loads are still landing, which waits
   // for every load in flight)
   TileIn<B, RQ, G> s0 = load(t0), s1 = load(t0 + kTile), s2 = load(t0 + 2 * kTile);
+  // (the first tiles' loads are in flight while the norm pass runs)
+  // ---- the split's largest norm (weights carry n / 2^e <= 1 times at most
+  // 2^kSlack, so their float16 pieces cannot overflow); eight loads in
+  // flight per lane
+  const float a = scale * 1.4426950408889634f;  // weights are 2^(a s - max)
+  float nmax = 0.0f;
+  for (int64_t tb = t0; tb < t1; tb += 8 * 64) {
+    float nv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t t = tb + 64 * u + lane;
+      nv[u] = vnorms[t < t1 ? t : t1 - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) nmax = fmaxf(nmax, nv[u]);
+  }
+  nmax = wave_max(nmax);
+  int ne = 0;
+  if (nmax > 0.0f && nmax < INFINITY) (void)frexpf(nmax, &ne);
+  const float nscale = ldexpf(1.0f, -ne);
+  // reference row maxima of a s (the same in every lane).  A vector value,
+  // not an array: a per-lane choice between two of its elements must stay
+  // a select of two registers (an array indexed that way was moved to
+  // per-work-item LDS, whose address every wave then computed from the
+  // dispatch packet, and that cost more than the tiles of a decode call)
+  typedef float rowvec __attribute__((ext_vector_type(RQ)));
+  rowvec lm;
+#pragma unroll
+  for (int r = 0; r < RQ; ++r) lm[r] = -INFINITY;
+
   auto step = [&](int64_t tb, const TileIn<B, RQ, G> in) __attribute__((always_inline)) {
     // weights of (row 2k + lane / 32, token lane % 32) into this wave's slice;
     // LDS is in order within a wave, so the reads below see these writes
@@ -401,17 +407,19 @@ __device__ __forceinline__ float block_reduce(float x, float* sh, bool is_max) {
 }
 
 // block per (group, query) row; dynamic LDS: the normalised sum (d floats)
-// and the partition partials (kThreads floats).  Thread t works on
-// coordinate t mod d' and partition t div d' (d' = min(d, kThreads), P =
-// kThreads / d' partitions): each partition sums every P-th split (or
-// coordinate, for Pi^T) with 8 loads in flight, and the partitions meet in
-// LDS.
+// and the partials (kThreads float4).  With d a multiple of 4 (dp, the
+// padded width, always is), thread t takes coordinates 4 (t mod Q) .. + 3
+// (Q = min(dp, 4 kThreads) / 4 quads per pass) and partition t div Q of the
+// P = kThreads / Q partitions: each partition sums every P-th split (then
+// every P-th row of Pi^T) with float4 loads, 8 in flight, and the
+// partitions meet in LDS.  A decode-sized call has few rows, so the
+// latency of these load rounds, not their bytes, sets its time.
 __global__ void __launch_bounds__(kThreads)
 attn_merge_kernel(const float* __restrict__ part_y, const float2* __restrict__ part_ml, int64_t splits, int dp,
                   int d, const float* __restrict__ pi, float* __restrict__ out, float* __restrict__ lse) {
   extern __shared__ float dyn[];
-  float* yh = dyn;          // [d]
-  float* parts = dyn + d;   // [kThreads]
+  float* yh = dyn;                                   // [dp]
+  float4* parts = reinterpret_cast<float4*>(dyn + dp);  // [kThreads]
   __shared__ float wts[kMaxSplits];
   __shared__ float sh[kWaves];
   const int tid = threadIdx.x;
@@ -430,54 +438,100 @@ attn_merge_kernel(const float* __restrict__ part_y, const float2* __restrict__ p
   }
   const float L = block_reduce(l, sh, false);  // (its barriers also publish wts)
   const float inv = 1.0f / L;
-  const int dd = d < kThreads ? d : kThreads;
-  const int P = kThreads / dd;
-  const int part = tid / dd, cl = tid % dd;
-  // combine the splits: coordinate c, splits part, part + P, ...
-  for (int c0 = 0; c0 < d; c0 += dd) {
-    const int c = c0 + cl;
-    float a = 0.0f;
-    if (part < P && c < d) {
+  const int quads = dp / 4;
+  const int Q = quads < kThreads ? quads : kThreads;
+  const int P = kThreads / Q;
+  const int part = tid / Q, ql = tid % Q;
+  // combine the splits: coordinates 4 c4 .. 4 c4 + 3, splits part, part + P, ...
+  for (int q0 = 0; q0 < quads; q0 += Q) {
+    const int c4 = q0 + ql;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (part < P && c4 < quads) {
+      const float4* py = reinterpret_cast<const float4*>(part_y) + c4;
       int64_t s = part;
       for (; s + 7 * P < splits; s += 8 * P) {
-        float v[8];
+        float4 v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = part_y[(s + u * P) * dp + c];
+        for (int u = 0; u < 8; ++u) v[u] = py[(s + u * P) * quads];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) a = fmaf(v[u], wts[s + u * P], a);
+        for (int u = 0; u < 8; ++u) {
+          const float wv = wts[s + u * P];
+          a.x = fmaf(v[u].x, wv, a.x), a.y = fmaf(v[u].y, wv, a.y);
+          a.z = fmaf(v[u].z, wv, a.z), a.w = fmaf(v[u].w, wv, a.w);
+        }
       }
-      for (; s < splits; s += P) a = fmaf(part_y[s * dp + c], wts[s], a);
+      for (; s < splits; s += P) {
+        const float4 v = py[s * quads];
+        const float wv = wts[s];
+        a.x = fmaf(v.x, wv, a.x), a.y = fmaf(v.y, wv, a.y), a.z = fmaf(v.z, wv, a.z), a.w = fmaf(v.w, wv, a.w);
+      }
     }
     parts[tid] = a;
     __syncthreads();
-    if (part == 0 && c < d) {
-      float t = 0.0f;
-      for (int q = 0; q < P; ++q) t += parts[q * dd + cl];
-      yh[c] = t * inv;
+    if (part == 0 && c4 < quads) {
+      float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int q = 0; q < P; ++q) {
+        const float4 v = parts[q * Q + ql];
+        t.x += v.x, t.y += v.y, t.z += v.z, t.w += v.w;
+      }
+      yh[4 * c4] = t.x * inv, yh[4 * c4 + 1] = t.y * inv, yh[4 * c4 + 2] = t.z * inv, yh[4 * c4 + 3] = t.w * inv;
     }
     __syncthreads();
   }
-  // out_i = sum_c Pi[c][i] yh[c]: coordinate i, rows c = part, part + P, ...
-  for (int i0 = 0; i0 < d; i0 += dd) {
-    const int i = i0 + cl;
-    float o = 0.0f;
-    if (part < P && i < d) {
-      int c = part;
-      for (; c + 7 * P < d; c += 8 * P) {
-        float v[8];
+  // out_i = sum_c Pi[c][i] yh[c] (c < d): outputs 4 i4 .. + 3, rows part, part + P, ...
+  // (Pi rows are d floats; d % 4 == 0 takes float4 loads)
+  const int oq = (d + 3) / 4;
+  const int Qo = oq < kThreads ? oq : kThreads;
+  const int Po = kThreads / Qo;
+  const int parto = tid / Qo, qo = tid % Qo;
+  const bool vec = (d & 3) == 0;
+  for (int i0 = 0; i0 < oq; i0 += Qo) {
+    const int i4 = i0 + qo;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (parto < Po && i4 < oq) {
+      if (vec) {
+        const float4* pr = reinterpret_cast<const float4*>(pi) + i4;
+        int c = parto;
+        for (; c + 7 * Po < d; c += 8 * Po) {
+          float4 v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = pi[int64_t(c + u * P) * d + i];
+          for (int u = 0; u < 8; ++u) v[u] = pr[int64_t(c + u * Po) * oq];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) o = fmaf(v[u], yh[c + u * P], o);
+          for (int u = 0; u < 8; ++u) {
+            const float y = yh[c + u * Po];
+            o.x = fmaf(v[u].x, y, o.x), o.y = fmaf(v[u].y, y, o.y);
+            o.z = fmaf(v[u].z, y, o.z), o.w = fmaf(v[u].w, y, o.w);
+          }
+        }
+        for (; c < d; c += Po) {
+          const float4 v = pr[int64_t(c) * oq];
+          const float y = yh[c];
+          o.x = fmaf(v.x, y, o.x), o.y = fmaf(v.y, y, o.y), o.z = fmaf(v.z, y, o.z), o.w = fmaf(v.w, y, o.w);
+        }
+      } else {
+        for (int c = parto; c < d; c += Po) {
+          const float y = yh[c];
+          const float* pr = pi + int64_t(c) * d + 4 * i4;
+          o.x = fmaf(pr[0], y, o.x);
+          if (4 * i4 + 1 < d) o.y = fmaf(pr[1], y, o.y);
+          if (4 * i4 + 2 < d) o.z = fmaf(pr[2], y, o.z);
+          if (4 * i4 + 3 < d) o.w = fmaf(pr[3], y, o.w);
+        }
       }
-      for (; c < d; c += P) o = fmaf(pi[int64_t(c) * d + i], yh[c], o);
     }
     parts[tid] = o;
     __syncthreads();
-    if (part == 0 && i < d) {
-      float t = 0.0f;
-      for (int q = 0; q < P; ++q) t += parts[q * dd + cl];
-      out[row * d + i] = t;
+    if (parto == 0 && i4 < oq) {
+      float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int q = 0; q < Po; ++q) {
+        const float4 v = parts[q * Qo + qo];
+        t.x += v.x, t.y += v.y, t.z += v.z, t.w += v.w;
+      }
+      float* dst = out + row * d + 4 * i4;
+      dst[0] = t.x;
+      if (4 * i4 + 1 < d) dst[1] = t.y;
+      if (4 * i4 + 2 < d) dst[2] = t.z;
+      if (4 * i4 + 3 < d) dst[3] = t.w;
     }
     __syncthreads();
   }
@@ -644,7 +698,7 @@ hipError_t launch_attention_values(const tq_ctx* hv, const float* scores, int64_
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_merge_kernel, dim3(unsigned(groups * nq)), dim3(kThreads),
-                     size_t(hv->d + kThreads) * sizeof(float),
+                     size_t(32 * hv->words) * sizeof(float) + size_t(kThreads) * sizeof(float4),
                      stream, a.part_y, a.part_ml, a.splits, 32 * hv->words, hv->d, hv->d_pi, out, lse);
   return hipGetLastError();
 }
