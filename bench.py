@@ -227,6 +227,58 @@ def attention_leg(w, h, keys, queries, packed, seed, stream, reps=10):
     return res
 
 
+def decode_leg(seed, reps=50):
+    """One decode step at the llama_decode shape (8 key heads x 32768 bf16
+    tokens, 4 query heads per key head, d = 128, 4 bits): latency of
+    tq_logits, tq_attention (values quantized with their own handle, scale
+    1/sqrt(d)) and the uncompressed comparison on the same keys (float32
+    and bfloat16).  Mean of `reps` back-to-back calls after a warm-up."""
+    import torch
+
+    import vector_quantization_quantize_amd as tqm
+    from vector_quantization_quantize_amd import workloads as wl
+    w = wl.WORKLOADS["llama_decode"]
+    keys = torch.from_numpy(wl.keys(w, seed)).to(torch.bfloat16).cuda()
+    values = torch.from_numpy(wl.keys(w, seed + 1)).to(torch.bfloat16).cuda()
+    queries = torch.from_numpy(wl.queries(w, seed)).cuda()
+    h, hv = tqm.tq_init(w.d, w.bits, 0), tqm.tq_init(w.d, w.bits, 1)
+    packed = tqm.tq_quantize(h, keys)
+    vc, _, vn, _ = tqm.tq_quantize(hv, values)
+    vblocks = tqm.tq_pack_values(hv, vc, groups=w.groups, n=w.n)
+    scores = torch.empty((w.groups, w.nq, w.n), dtype=torch.float32, device="cuda")
+    lws = torch.empty(tqm.tq_logits_workspace_size(h, w.groups, w.nq) // 4 + 64, dtype=torch.float32, device="cuda")
+    out = torch.empty((w.groups, w.nq, w.d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.groups, w.nq), dtype=torch.float32, device="cuda")
+    aws = torch.empty(tqm.tq_attention_workspace_size(h, hv, w.groups, w.nq, w.n) // 4 + 64, dtype=torch.float32,
+                      device="cuda")
+    kf = keys.float()
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e3
+
+    res = {"workload": f"{w.name}: {w.description}",
+           "tq_logits_us": timed(lambda: tqm.tq_logits(h, queries, *packed, n=w.n, scores=scores, workspace=lws)),
+           "tq_attention_us": timed(lambda: tqm.tq_attention(h, hv, queries, *packed, vblocks, vn, n=w.n, out=out,
+                                                             lse=lse, workspace=aws)),
+           "dense_logits_f32_us": timed(lambda: tqm.tq_dense_logits(queries, kf, n=w.n, scores=scores)),
+           "dense_logits_bf16_us": timed(lambda: tqm.tq_dense_logits(queries, keys, n=w.n, scores=scores))}
+    for k in list(res):
+        if k.endswith("_us"):
+            res[k] = round(res[k], 2)
+    tqm.tq_destroy(h)
+    tqm.tq_destroy(hv)
+    return res
+
+
 def cpu_baseline(w, keys_np, queries_np, groups, seed):
     """Oracle (numpy float64) on the first `groups` key groups."""
     import numpy as np
@@ -400,6 +452,7 @@ def main():
     }
     if not args.no_attention:
         line["attention"] = attention_leg(w, h, keys, queries, packed, args.seed, stream)
+        line["decode_step"] = decode_leg(args.seed)
     if not args.no_search:
         del keys, queries, packed, scores, ws, khat
         torch.cuda.empty_cache()
