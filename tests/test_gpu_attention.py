@@ -282,3 +282,32 @@ def test_attention_long_context_full_size(env):
         assert np.all(err <= tol), (g, float((err / tol).max()))
         assert np.all(np.abs(lse[g] - l) <= delta + 1e-5 * np.maximum(1.0, np.abs(l)))
         print(f"head {g}: worst |error| / tolerance {float((err / tol).max()):.3g}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_dense_logits_long_context_full_size(env, dtype):
+    """The uncompressed comparison at the long-context shape in the bench's
+    launch configuration (32 key heads x 131072 keys, 4 queries per head):
+    4096 sampled scores against the oracle's exact inner products of the
+    same (bfloat16-valued) keys, within the float32 summation bound."""
+    torch, tqm = env
+    from vector_quantization_quantize_amd import workloads as wl
+    w = wl.WORKLOADS["long_context"]
+    _announce(f"dense logits full size {w.name} {dtype}")
+    keys = wl.keys(w)
+    queries = wl.queries(w)
+    kt = _dev(torch, keys, torch.bfloat16)
+    if dtype == "f32":
+        kt = kt.float()
+    s = tqm.tq_dense_logits(_dev(torch, queries), kt, n=w.n)
+    torch.cuda.synchronize()
+    rs = np.random.default_rng(5)
+    g = rs.integers(0, w.groups, 4096)
+    q = rs.integers(0, w.nq, 4096)
+    t = rs.integers(0, w.n, 4096)
+    got = _cpu(s[torch.from_numpy(g).cuda(), torch.from_numpy(q).cuda(), torch.from_numpy(t).cuda()])
+    kv = keys[g * w.n + t].astype(np.float64)
+    qv = queries[g, q].astype(np.float64)
+    ref = np.array([tq.exact_inner_products(qv[i:i + 1], kv[i:i + 1])[0, 0] for i in range(len(g))])
+    bound = w.d * 2.0 ** -24 * (np.abs(qv) * np.abs(kv)).sum(axis=1)
+    assert np.all(np.abs(got - ref) <= bound), float((np.abs(got - ref) / bound).max())
