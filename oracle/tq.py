@@ -62,13 +62,16 @@ Packed layout (bit planes): ``codes[n][B][W]`` and ``signs[n][W]`` as
 uint32 with W = ceil(d / 32); bit p of the index of coordinate j is bit
 (j mod 32) of word (j div 32) of plane p (LSB first); padding bits are 0.
 Stored values use token blocks instead: ``vcodes[ceil(n/32)][B][32 W]``
-(uint32 words, read here as little-endian bytes).  For plane p of block b,
-let T_j be the 32-bit word whose bit i is bit p of the index of coordinate
-j of token 32 b + i (tokens past n and coordinates past d give 0 bits).
+(uint32 words, read here as little-endian bytes: 128 B W bytes per block
+of 32 tokens; tokens past n and coordinates past d give index 0).
 Coordinates come in groups of 128 (4 words of the key layout; the last
-group holds G = W mod 4 words when that is not 0) and a group's 128 G bytes
-start at byte 512 g of the plane; byte k of T_{128 g + r} (r < 32 G) sits
-at byte ((r mod 16) + 16 k) * 2 G + (r div 16) of the group.
+group holds G = W mod 4 words when that is not 0); group g's 512 B G bytes
+start at byte 512 B g of the block.  For coordinate 128 g + r (r < 32 G)
+and token octet o (tokens 32 b + 8 o .. + 7), the B-byte little-endian
+integer X at byte ((r mod 16) + 16 o) * 2 G B + (r div 16) * B of the
+group holds, for token 8 o + t and plane p, bit p of the token's index at
+bit (t div E) * B E + p E + (t mod E), with E = 8, 4, 2, 2 for B = 1, 2,
+3, 4: each run of B E bits is the index bits of E consecutive tokens.
 """
 from dataclasses import dataclass
 
@@ -268,52 +271,64 @@ def pack(params: Params, qz: Quantized):
             qz.norms.astype(np.float32), qz.rnorms.astype(np.float32))
 
 
-def value_byte_position(d):
-    """(32 W, 4) int: the byte of a value plane that holds byte k of the
-    token word T_j of coordinate j (see the module docstring)."""
+def value_group_of_e(code_bits):
+    """Tokens per index run in the value layout: 8, 4, 2, 2 for B = 1..4."""
+    return {1: 8, 2: 4, 3: 2, 4: 2}[code_bits]
+
+
+def value_slot(d, code_bits):
+    """(32 W, 4) int: byte offset, within a block, of the B-byte integer X
+    for coordinate j and token octet o (see the module docstring)."""
     w = words_per_plane(d)
     pos = np.empty((32 * w, 4), dtype=np.int64)
     for j in range(32 * w):
         g, r = divmod(j, 128)
         gw = min(4, w - 4 * g)                      # words in this group
-        for k in range(4):
-            pos[j, k] = 512 * g + ((r % 16) + 16 * k) * 2 * gw + r // 16
+        for o in range(4):
+            pos[j, o] = 512 * code_bits * g + ((r % 16) + 16 * o) * 2 * gw * code_bits + (r // 16) * code_bits
     return pos
 
 
 def pack_values(idx, code_bits):
-    """(n, d) value indices -> (ceil(n/32), B, 32 W) uint32 token blocks:
-    the token words T_j (bit i = bit p of the index of coordinate j of
-    token 32 b + i) of each plane, their bytes placed by
-    value_byte_position."""
+    """(n, d) value indices -> (ceil(n/32), B, 32 W) uint32 token blocks in
+    the value layout (module docstring)."""
     idx = np.asarray(idx, dtype=np.int64)
     n, d = idx.shape
     nb = (n + 31) // 32
     dp = 32 * words_per_plane(d)
-    pos = value_byte_position(d)
+    e = value_group_of_e(code_bits)
+    slot = value_slot(d, code_bits)
     padded = np.zeros((nb * 32, dp), dtype=np.int64)
     padded[:n, :d] = idx
-    out = np.zeros((nb, code_bits, 4 * dp), dtype=np.uint8)
+    out = np.zeros((nb, 4 * code_bits * dp), dtype=np.uint8)
     for b in range(nb):
-        block = padded[32 * b:32 * b + 32]                    # (32 tokens, dp)
-        for p in range(code_bits):
-            words = pack_bits(((block >> p) & 1).T.astype(bool))[:, 0]   # T_j, j < dp
-            for k in range(4):
-                out[b, p, pos[:, k]] = (words >> np.uint32(8 * k)) & np.uint32(0xFF)
-    return out.view("<u4")
+        for o in range(4):
+            toks = padded[32 * b + 8 * o:32 * b + 8 * o + 8]          # (8 tokens, dp)
+            x = np.zeros(dp, dtype=np.uint64)
+            for t in range(8):
+                for p in range(code_bits):
+                    bit = (toks[t] >> p) & 1
+                    x |= bit.astype(np.uint64) << np.uint64((t // e) * code_bits * e + p * e + t % e)
+            for k in range(code_bits):
+                out[b, slot[:, o] + k] = (x >> np.uint64(8 * k)) & np.uint64(0xFF)
+    return out.view("<u4").reshape(nb, code_bits, dp)
 
 
 def unpack_values(vcodes, n, d):
     """Inverse of pack_values: (n, d) indices."""
     vcodes = np.ascontiguousarray(np.asarray(vcodes, dtype=np.uint32))
     nb, code_bits, dp = vcodes.shape
-    raw = vcodes.view("<u1").reshape(nb, code_bits, 4 * dp).astype(np.uint32)
-    pos = value_byte_position(d)
-    by_coord = np.zeros((nb, code_bits, dp), dtype=np.uint32)   # T_j at j
-    for k in range(4):
-        by_coord |= raw[:, :, pos[:, k]] << np.uint32(8 * k)
+    raw = vcodes.reshape(nb, code_bits * dp).view("<u1").astype(np.uint64)
+    e = value_group_of_e(code_bits)
+    slot = value_slot(d, code_bits)
     idx = np.zeros((nb * 32, dp), dtype=np.int64)
-    for p in range(code_bits):
-        bits = unpack_bits(by_coord[:, p, :].reshape(nb * dp, 1), 32)   # (nb*dp, 32 tokens)
-        idx |= bits.reshape(nb, dp, 32).transpose(0, 2, 1).reshape(nb * 32, dp).astype(np.int64) << p
+    for b in range(nb):
+        for o in range(4):
+            x = np.zeros(dp, dtype=np.uint64)
+            for k in range(code_bits):
+                x |= raw[b, slot[:, o] + k] << np.uint64(8 * k)
+            for t in range(8):
+                for p in range(code_bits):
+                    bit = (x >> np.uint64((t // e) * code_bits * e + p * e + t % e)) & np.uint64(1)
+                    idx[32 * b + 8 * o + t] |= bit.astype(np.int64) << p
     return idx[:n, :d]

@@ -557,37 +557,40 @@ def test_attention_special_cases():
 
 
 def test_pack_values_bit_positions():
-    """Token-blocked value planes, worked by hand.  d = 50 has W = 2 words:
-    one group of G = 2.  Token 33 with index 0b10 at coordinate 37 sets bit 1
-    (33 mod 32) of T_37 in plane 1 of block 1: byte k = 0 of T_37, with
-    r = 37, sits at byte ((37 mod 16) + 0) * 4 + 37 div 16 = 22; nothing
-    else is set.  Token 9 (byte k = 1, bit 1) at coordinate 3 sits at byte
-    (3 + 16) * 4 + 0 = 76."""
+    """Token-blocked value layout, worked by hand.  d = 50: W = 2 words, one
+    group of G = 2.  B = 2 (E = 4): token 33 (block 1, octet 0, t = 1) with
+    index 0b10 at coordinate 37 (r = 37) sets plane-1 bit (1 div 4) * 8 +
+    1 * 4 + 1 = 5 of X at byte ((37 mod 16) + 0) * 8 + (37 div 16) * 2 = 44
+    of block 1: byte 44 = 0x20, nothing else.  Token 14 (block 0, octet 1,
+    t = 6) with index 0b01 at coordinate 3: plane-0 bit (6 div 4) * 8 + 0 +
+    2 = 10 of X at byte (3 + 16) * 8 + 0 = 152: byte 153 = 0x04."""
     idx = np.zeros((40, 50), dtype=np.int64)
     idx[33, 37] = 2
-    v = tq.pack_values(idx, 2)
-    assert v.shape == (2, 2, 64)
-    raw = v.view(np.uint8).reshape(2, 2, 256)
-    assert raw[1, 1, 22] == 2 and np.count_nonzero(raw) == 1
+    raw = tq.pack_values(idx, 2).view(np.uint8).reshape(2, 512)
+    assert raw[1, 44] == 0x20 and np.count_nonzero(raw) == 1
     idx = np.zeros((40, 50), dtype=np.int64)
-    idx[9, 3] = 1
-    raw = tq.pack_values(idx, 2).view(np.uint8).reshape(2, 2, 256)
-    assert raw[0, 0, 76] == 2 and np.count_nonzero(raw) == 1
-    # d = 200: W = 7, a full group (G = 4) then G = 3 from byte 512; byte 2
-    # of T_130 (r = 2 of group 1): 512 + (2 + 32) * 6 + 0 = 716; byte 3 of
-    # T_127: (15 + 48) * 8 + 7 = 511; byte 0 of T_16: 0 * 8 + 1 = 1
-    pos = tq.value_byte_position(200)
-    assert pos[130, 2] == 716 and pos[127, 3] == 511 and pos[16, 0] == 1
-    assert sorted(pos.ravel().tolist()) == list(range(4 * 224))
-    full = np.full((40, 50), 3, dtype=np.int64)
-    raw = tq.pack_values(full, 2).view(np.uint8).reshape(2, 2, 256)
-    pos = tq.value_byte_position(50)
-    assert np.all(raw[0][:, pos[:50].ravel()] == 0xFF) and np.all(raw[:, :, pos[50:].ravel()] == 0)
-    assert np.all(raw[1][:, pos[:50, 0]] == 0xFF) and np.all(raw[1][:, pos[:50, 1:].ravel()] == 0)
+    idx[14, 3] = 1
+    raw = tq.pack_values(idx, 2).view(np.uint8).reshape(2, 512)
+    assert raw[0, 153] == 0x04 and np.count_nonzero(raw) == 1
+    # B = 3 (E = 2), d = 200: W = 7, a full group then G = 3 from byte
+    # 512 * 3 = 1536; coordinate 130 is r = 2 of group 1, octet 2: X at
+    # 1536 + (2 + 32) * 18 + 0 = 2148; token 8*2 + 5 (t = 5) plane 2 ->
+    # bit 2 * 6 + 2 * 2 + 1 = 17 -> byte 2150 bit 1
+    slot = tq.value_slot(200, 3)
+    assert slot[130, 2] == 2148
+    idx = np.zeros((32, 200), dtype=np.int64)
+    idx[21, 130] = 4
+    raw = tq.pack_values(idx, 3).view(np.uint8).reshape(-1)
+    assert raw[2150] == 0x02 and np.count_nonzero(raw) == 1
+    # slots tile the block without overlap, B bytes each
+    for d, b in ((200, 3), (50, 2), (128, 4), (33, 1)):
+        s = tq.value_slot(d, b)
+        cover = sorted((s[:, :, None] + np.arange(b)[None, None, :]).ravel().tolist())
+        assert cover == list(range(4 * b * 32 * tq.words_per_plane(d)))
     rs = np.random.default_rng(3)
-    for n, d in ((77, 45), (40, 200), (33, 128), (70, 64)):
-        idx = rs.integers(0, 8, (n, d))
-        assert np.array_equal(tq.unpack_values(tq.pack_values(idx, 3), n, d), idx)
+    for n, d, b in ((77, 45, 3), (40, 200, 2), (33, 128, 4), (70, 64, 1), (65, 33, 2)):
+        idx = rs.integers(0, 1 << b, (n, d))
+        assert np.array_equal(tq.unpack_values(tq.pack_values(idx, b), n, d), idx)
 
 
 # ---------------------------------------------------------------------------

@@ -14,14 +14,17 @@
 // bit p of the index of coordinate c of token 32 b + i: the contraction
 // over tokens is the matrix-core K dimension, and one byte of T_c is the
 // operand of 8 tokens for one coordinate, expanded without a bit transpose.
-// The bytes are stored in the order the value pass's lanes read them:
-// within each group of 128 coordinates, lane L finds byte L / 16 of the
-// words of coordinates L mod 16 + 16 j (j < 8) as 8 contiguous bytes, so a
-// tile costs one 8-byte load per lane and plane, no byte loaded twice.
+// The bits are stored in the order the value pass's lanes read them: the
+// planes of one coordinate and token octet are interleaved so that each
+// run of B E bits is a level-table index for E tokens, and within each
+// group of 128 coordinates lane L finds its octet's integers for
+// coordinates L mod 16 + 16 j (j < 8) contiguous, so a tile costs one
+// 8 B-byte read per lane, no byte read twice, and one bit-field extract
+// per table lookup.
 //
 // Kernels:
 //  * pack_values_kernel: key-layout codes -> token blocks (a 32 x 32 bit
-//    transpose per word by wave ballots).
+//    transpose per word by wave ballots, then the planes interleaved).
 //  * attn_pv_kernel: one wave per (key split, group of 4 words = 128
 //    coordinates, group, up to 16 query rows), with no block-wide barrier
 //    after the level table.  A first pass over the split's norms finds the
@@ -64,47 +67,66 @@ constexpr float kSlack = 8.0f;  // weights relative to a row's reference maximum
 // value packing
 // ---------------------------------------------------------------------------
 
-// Byte of a value plane that holds byte k of the token word of coordinate
-// c: coordinates come in groups of 128 (4 key-layout words; the last group
-// has G = W mod 4 words when that is not 0), a group's 128 G bytes start at
-// byte 512 g, and byte k of coordinate 128 g + r sits at byte
-// ((r mod 16) + 16 k) 2 G + r div 16 of the group.  Lane L of the value
-// pass (L mod 16 = r mod 16, L div 16 = k) then finds its 2 G bytes
-// contiguous at 2 G L.
-__device__ __forceinline__ int value_byte(int c, int k, int W) {
+// Tokens per index run in the value layout (the level forms' table width)
+__host__ __device__ constexpr int value_e(int B) { return B == 1 ? 8 : B == 2 ? 4 : 2; }
+
+// Byte offset, within a block, of the B-byte integer X of coordinate c and
+// token octet o: coordinates come in groups of 128 (4 key-layout words; the
+// last group has G = W mod 4 words when that is not 0), group g starts at
+// byte 512 B g, and (r = c mod 128) X sits at ((r mod 16) + 16 o) 2 G B +
+// (r div 16) B.  Lane L of the value pass (L mod 16 = r mod 16, L div 16 =
+// o) then finds its 2 G integers contiguous at 2 G B L.  X holds, for token
+// 8 o + t and plane p, bit p of the index at bit (t div E) B E + p E +
+// (t mod E): each run of B E bits indexes the level table for E tokens.
+__device__ __forceinline__ int value_slot(int c, int o, int W, int B) {
   const int g = c >> 7, r = c & 127;
   const int gw = W - 4 * g < 4 ? W - 4 * g : 4;
-  return 512 * g + ((r & 15) + 16 * k) * 2 * gw + (r >> 4);
+  return 512 * B * g + ((r & 15) + 16 * o) * 2 * gw * B + (r >> 4) * B;
 }
 
-// block (token block, group); wave pairs of key-layout words: lanes 0-31
-// hold word `pw` of tokens 0-31, lanes 32-63 word `pw + 1`; ballot j
-// collects bit j (coordinate 32 w + j) of the 32 tokens of each half.
+// block (token block, group).  Phase 1: the token words T of every plane
+// and coordinate (bit i = bit p of the index of coordinate c of token
+// 32 b + i) into LDS, by wave ballots over key-layout words: lanes 0-31
+// hold word `pw` of tokens 0-31, lanes 32-63 word `pw + 1`, ballot j
+// collects bit j of each half.  Phase 2: thread per (coordinate, token
+// octet) interleaves the planes' bytes into X and writes its B bytes.
+// Dynamic LDS: B * 32 W words.
 __global__ void __launch_bounds__(kThreads)
 pack_values_kernel(const uint32_t* __restrict__ codes, int64_t n, int B, int W, int64_t nb,
                    uint32_t* __restrict__ vcodes) {
+  extern __shared__ uint32_t tw[];  // [B][32 W]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t blk = blockIdx.x, grp = blockIdx.y;
   const int pws = B * W;  // words per token in the key layout
   codes += grp * n * pws;
-  vcodes += (grp * nb + blk) * int64_t(pws) * 32;
+  uint8_t* out = reinterpret_cast<uint8_t*>(vcodes + (grp * nb + blk) * int64_t(pws) * 32);
   const int64_t tok = blk * 32 + (lane & 31);
   for (int pw = 2 * wave; pw < pws; pw += 2 * kWaves) {
     const int mine = pw + (lane >> 5);
     const uint32_t x = (mine < pws && tok < n) ? codes[tok * pws + mine] : 0u;
-    uint32_t out = 0;
+    uint32_t t = 0;
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
       const uint64_t m = __ballot((x >> j) & 1u);
       const uint32_t part = lane < 32 ? uint32_t(m) : uint32_t(m >> 32);
-      out = (lane & 31) == j ? part : out;
+      t = (lane & 31) == j ? part : t;
     }
     if (mine < pws) {
-      const int p = mine / W, w = mine % W, c = 32 * w + (lane & 31);
-      uint8_t* plane = reinterpret_cast<uint8_t*>(vcodes + int64_t(p) * 32 * W);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) plane[value_byte(c, k, W)] = uint8_t(out >> (8 * k));
+      const int p = mine / W, w = mine % W;
+      tw[p * 32 * W + 32 * w + (lane & 31)] = t;
     }
+  }
+  __syncthreads();
+  const int E = value_e(B);
+  for (int i = threadIdx.x; i < 4 * 32 * W; i += kThreads) {
+    const int c = i >> 2, o = i & 3;
+    uint32_t x = 0;
+    for (int p = 0; p < B; ++p) {
+      const uint32_t byte = (tw[p * 32 * W + c] >> (8 * o)) & 0xFFu;
+      for (int t = 0; t < 8; ++t) x |= ((byte >> t) & 1u) << ((t / E) * B * E + p * E + (t % E));
+    }
+    uint8_t* dst = out + value_slot(c, o, W, B);
+    for (int k = 0; k < B; ++k) dst[k] = uint8_t(x >> (8 * k));
   }
 }
 
@@ -127,8 +149,16 @@ template <int B, int RQ, int G>
 struct TileIn {
   float s[RQ * kTile / 64];
   float nv;
-  uint32_t w[B][(2 * G + 3) / 4];
+  uint32_t w[(2 * G * B + 3) / 4];  // the lane's 2 G integers X (B bytes each)
 };
+
+// bits [pos, pos + width) of a little-endian multi-word value
+template <int N>
+__device__ __forceinline__ uint32_t bit_field(const uint32_t (&w)[N], int pos, int width) {
+  const int i = pos >> 5, sh = pos & 31;
+  if (sh + width <= 32) return __builtin_amdgcn_ubfe(w[i], sh, width);
+  return __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(w[i + 1], w[i], sh), 0, width);
+}
 
 // RQ: query rows per wave (4, 8 or 16; the matrix-core M is 16 either way,
 // rows past RQ stay 0).  G: words in the wave's coordinate group (4, or
@@ -199,21 +229,27 @@ attn_pv_kernel(const float* __restrict__ scores, int64_t nq, int64_t n, const ui
       x.s[k] = scores[(r < rows ? r : rows - 1) * n + tok];
     }
     x.nv = vnorms[tok];
-    const uint8_t* vb = reinterpret_cast<const uint8_t*>(vcodes + (tbc / kTile) * B * dp) + 128 * word0 + 2 * G * lane;
+    // the lane's 2 G B bytes at 2 G B lane of its group (group word0 / 4
+    // starts at byte 512 B (word0 / 4) = 128 B word0), loaded in the widest
+    // chunks their alignment allows
+    constexpr int kBytes = 2 * G * B;
+    constexpr int kChunk = kBytes % 16 == 0 ? 16 : kBytes % 8 == 0 ? 8 : kBytes % 4 == 0 ? 4 : 2;
+    const uint8_t* q = reinterpret_cast<const uint8_t*>(vcodes + (tbc / kTile) * B * dp) + 128 * B * word0 +
+                       kBytes * lane;
 #pragma unroll
-    for (int p = 0; p < B; ++p) {
-      const uint8_t* q = vb + 4 * p * dp;
-      if constexpr (G == 4) {
-        const uint2 u = *reinterpret_cast<const uint2*>(q);
-        x.w[p][0] = u.x, x.w[p][1] = u.y;
-      } else if constexpr (G == 2) {
-        x.w[p][0] = *reinterpret_cast<const uint32_t*>(q);
-      } else if constexpr (G == 1) {
-        x.w[p][0] = *reinterpret_cast<const uint16_t*>(q);
+    for (int c = 0; c < kBytes / kChunk; ++c) {
+      if constexpr (kChunk == 16) {
+        const uint4 u = *reinterpret_cast<const uint4*>(q + 16 * c);
+        x.w[4 * c] = u.x, x.w[4 * c + 1] = u.y, x.w[4 * c + 2] = u.z, x.w[4 * c + 3] = u.w;
+      } else if constexpr (kChunk == 8) {
+        const uint2 u = *reinterpret_cast<const uint2*>(q + 8 * c);
+        x.w[2 * c] = u.x, x.w[2 * c + 1] = u.y;
+      } else if constexpr (kChunk == 4) {
+        x.w[c] = *reinterpret_cast<const uint32_t*>(q + 4 * c);
       } else {
-        const uint32_t a0 = *reinterpret_cast<const uint16_t*>(q), a1 = *reinterpret_cast<const uint16_t*>(q + 2),
-                       a2 = *reinterpret_cast<const uint16_t*>(q + 4);
-        x.w[p][0] = a0 | (a1 << 16), x.w[p][1] = a2;
+        const uint32_t h = *reinterpret_cast<const uint16_t*>(q + 2 * c);
+        if (c % 2 == 0) x.w[c / 2] = h;
+        else x.w[c / 2] |= h << 16;
       }
     }
     return x;
@@ -322,24 +358,20 @@ attn_pv_kernel(const float* __restrict__ scores, int64_t nq, int64_t n, const ui
       pa[wave][1][r][tl] = static_cast<_Float16>(p - float(hi));
     }
     // A: row n16, tokens 8 g16 .. 8 g16 + 7 (both pieces); B: coordinate
-    // 32 word0 + 16 j + n16, the same tokens, from the lane's byte j
+    // 32 word0 + 16 j + n16, the same tokens, from the lane's integer j
     const f16x8 ah = *reinterpret_cast<const f16x8*>(&pa[wave][0][n16][8 * g16]);
     const f16x8 al = *reinterpret_cast<const f16x8*>(&pa[wave][1][n16][8 * g16]);
 #pragma unroll
     for (int j = 0; j < 2 * G; ++j) {
-      uint32_t pw[B];
-#pragma unroll
-      for (int p = 0; p < B; ++p) pw[p] = __builtin_amdgcn_ubfe(in.w[p][j >> 2], 8 * (j & 3), 8);
       f16x8 bv, bl;
       if constexpr (F == kSignForm) {
-        const uint4 sg = score::expand_signs(pw[0], sgn_mask, sgn_one);
+        const uint4 sg = score::expand_signs(bit_field(in.w, 8 * B * j, 8), sgn_mask, sgn_one);
         bv = *reinterpret_cast<const f16x8*>(&sg);
       } else {
 #pragma unroll
         for (int k = 0; k < 8 / E; ++k) {
-          uint32_t idx = 0;
-#pragma unroll
-          for (int p = 0; p < B; ++p) idx |= __builtin_amdgcn_ubfe(pw[p], k * E, E) << (p * E);
+          // tokens k E .. k E + E - 1: one run of B E bits is the table index
+          const uint32_t idx = bit_field(in.w, 8 * B * j + k * B * E, B * E);
 #pragma unroll
           for (int e = 0; e < E; ++e) {
             bv[k * E + e] = vtab[idx * Fm::kHalves + e];
@@ -628,7 +660,13 @@ hipError_t launch_pack_values(const tq_ctx* h, const uint32_t* codes, int64_t gr
                               hipStream_t stream) {
   const int64_t nb = (n + kTile - 1) / kTile;
   if (nb == 0 || groups == 0) return hipSuccess;
-  hipLaunchKernelGGL(pack_values_kernel, dim3(unsigned(nb), unsigned(groups)), dim3(kThreads), 0, stream, codes, n,
+  const size_t lds = size_t(h->code_bits) * 32 * h->words * sizeof(uint32_t);
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(pack_values_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(pack_values_kernel, dim3(unsigned(nb), unsigned(groups)), dim3(kThreads), lds, stream, codes, n,
                      h->code_bits, h->words, nb, vcodes);
   return hipGetLastError();
 }
