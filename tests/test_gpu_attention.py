@@ -311,3 +311,30 @@ def test_dense_logits_long_context_full_size(env, dtype):
     ref = np.array([tq.exact_inner_products(qv[i:i + 1], kv[i:i + 1])[0, 0] for i in range(len(g))])
     bound = w.d * 2.0 ** -24 * (np.abs(qv) * np.abs(kv)).sum(axis=1)
     assert np.all(np.abs(got - ref) <= bound), float((np.abs(got - ref) / bound).max())
+
+
+def test_attention_rejects_bad_arguments(env):
+    """Error paths of the new entry points return TQ_EINVAL and launch
+    nothing: key and value handles of different d, value blocks not 16-byte
+    aligned, a non-finite scale, a workspace too small, an unknown key type."""
+    import ctypes
+    torch, tqm = env
+    _announce("attention argument checks")
+    lib = tqm._lib()
+    hk, hv, hv2 = tqm.tq_init(128, 3, 0), tqm.tq_init(128, 3, 1), tqm.tq_init(64, 3, 1)
+    q = torch.zeros((1, 4, 128), device="cuda")
+    buf = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    out = torch.zeros((1, 4, 128), device="cuda")
+    ws_bytes = tqm.tq_attention_workspace_size(hk, hv, 1, 4, 64)
+    ws = torch.zeros(ws_bytes // 4 + 64, device="cuda")
+    p = lambda t, off=0: ctypes.c_void_p(t.data_ptr() + off)
+    args = lambda h2, vc_off, scale, wsb: (hk.ptr, h2.ptr, p(q), 1, 4, p(buf), p(buf), p(buf), p(buf), p(buf, vc_off),
+                                           p(buf), 64, ctypes.c_float(scale), p(out), None, p(ws), wsb, None)
+    assert lib.tq_attention(*args(hv2, 0, 0.1, ws_bytes)) == tqm.TQ_EINVAL
+    assert lib.tq_attention(*args(hv, 4, 0.1, ws_bytes)) == tqm.TQ_EINVAL
+    assert lib.tq_attention(*args(hv, 0, float("nan"), ws_bytes)) == tqm.TQ_EINVAL
+    assert lib.tq_attention(*args(hv, 0, 0.1, ws_bytes - 256)) == tqm.TQ_EINVAL
+    assert lib.tq_pack_values(hv.ptr, p(buf), 1, 64, p(buf, 4), None) == tqm.TQ_EINVAL
+    assert lib.tq_dense_logits(p(q), 1, 4, p(buf), 7, 64, 128, 128, p(out), None) == tqm.TQ_EINVAL
+    assert lib.tq_dense_logits(p(q), 1, 4, p(buf), 0, 64, 128, 64, p(out), None) == tqm.TQ_EINVAL
+    torch.cuda.synchronize()
