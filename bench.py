@@ -227,6 +227,34 @@ def attention_leg(w, h, keys, queries, packed, seed, stream, reps=10):
     return res
 
 
+def dequant_prod_leg(w, h, packed, out, stream, reps=10):
+    """The reconstruction with the QJL correction (tq_dequant_prod) over the
+    step's packed cache into the step's reconstruction buffer: time per call
+    (mean of `reps` after a warm-up) against HBM, algorithmic bytes per key =
+    packed codes + sign bits + norm + residual norm read, 4 d float32
+    written; the 4 d^2 flops per key (G^T s, then Pi^T t) are reported
+    beside it."""
+    import torch
+
+    import vector_quantization_quantize_amd as tqm
+    fn = lambda: tqm.tq_dequant_prod(h, *packed, ktilde=out, stream=stream)
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    tfl = 4.0 * w.d * w.d * w.total_keys / (ms * 1e-3) / 1e12
+    nbytes = sum(t.numel() * t.element_size() for t in packed) + 4 * w.d * w.total_keys
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 3), "keys": w.total_keys, "TFLOPs": round(tfl, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_key": nbytes / w.total_keys}}
+
+
 def decode_leg(seed, reps=50):
     """One decode step at the llama_decode shape (8 key heads x 32768 bf16
     tokens, 4 query heads per key head, d = 128, 4 bits): latency of
@@ -453,6 +481,7 @@ def main():
     if not args.no_attention:
         line["attention"] = attention_leg(w, h, keys, queries, packed, args.seed, stream)
         line["decode_step"] = decode_leg(args.seed)
+        line["dequant_prod"] = dequant_prod_leg(w, h, packed, khat, stream)
     if not args.no_search:
         del keys, queries, packed, scores, ws, khat
         torch.cuda.empty_cache()

@@ -210,7 +210,7 @@ def test_dense_logits_match_exact_inner_products(env, d, nq, groups, n, dtype, l
 
 
 @pytest.mark.parametrize("d,bits,n", [(128, 3, 300), (200, 4, 77), (33, 2, 65), (1536, 4, 40), (2, 3, 9),
-                                      (128, 5, 129)])
+                                      (128, 5, 129), (128, 2, 31), (128, 4, 1057), (128, 2, 4096)])
 def test_dequant_prod_matches_oracle(env, d, bits, n):
     """Reconstruction with the QJL correction on the oracle's packed keys:
     per key ||k_gpu - k_oracle|| <= 1e-5 ||k_oracle|| (the reconstruction

@@ -38,6 +38,7 @@
 
 #include <cstdint>
 
+#include "score_mfma.h"
 #include "tq_internal.h"
 
 namespace tqdev {
@@ -134,14 +135,22 @@ __device__ __forceinline__ void load_a(const uint32_t* tab, const uint32_t (&wp)
   alo = __builtin_bit_cast(f16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
 }
 
-template <int B, bool kTwo>
+// kProd: the corrected reconstruction k_tilde = n (Pi^T c[idx] + rho kappa
+// S^T (2 beta - 1)), S = G Pi: per step two more passes, the key's sign
+// bits expanded to +-1 (exact in float16; a set bit stages as -1) against
+// two float16 pieces of 2^10 S, into a second accumulator scaled per key by
+// -n rho kappa 2^-10.
+template <int B, bool kTwo, bool kProd>
 __global__ void __launch_bounds__(kDqThreads, 2)
 dequant_mfma128_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ norms, int64_t n,
                        const uint4* __restrict__ pi_frag, Codebook cb, DequantTable dqt, float* __restrict__ khat,
-                       int64_t tiles, int64_t stride, int64_t bound1, int64_t bound2) {
+                       int64_t tiles, int64_t stride, int64_t bound1, int64_t bound2,
+                       const uint32_t* __restrict__ signs, const float* __restrict__ rnorms,
+                       const uint4* __restrict__ s_frag, float kappa) {
   using L = Lookup<B, kTwo>;
   __shared__ uint4 tab4[L::kEntries * L::kDwords / 4];
   __shared__ float4 nrow[4][8];  // per wave: the tile's 32 norms
+  __shared__ float4 crow[4][kProd ? 8 : 1];  // per wave: the tile's correction factors
   uint32_t* tab = reinterpret_cast<uint32_t*>(tab4);
   build_table<B, kTwo>(tab, cb, dqt);
   const float out_scale = kTwo ? dqt.out_scale : kOutScale;
@@ -156,15 +165,29 @@ dequant_mfma128_kernel(const uint32_t* __restrict__ codes, const float* __restri
   for (int s = 0; s < kSteps; ++s)
 #pragma unroll
     for (int q = 0; q < 2; ++q) bpi[s][q] = __builtin_bit_cast(f16x8, pi_frag[((w * kSteps + s) * 2 + q) * 64 + lane]);
+  f16x8 bs[kProd ? kSteps : 1][2];
+  if constexpr (kProd) {
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) bs[s][q] = __builtin_bit_cast(f16x8, s_frag[((w * kSteps + s) * 2 + q) * 64 + lane]);
+  }
+  uint32_t sgn_mask = 0x80008000u, sgn_one = 0x3C003C00u;
+  asm volatile("" : "+v"(sgn_mask), "+v"(sgn_one));
 
-  // packed codes and norm of this lane's key (clamped to n - 1), one tile
-  // ahead; a fetch past the last tile also reads key n - 1 and is unused
-  auto fetch = [&](int64_t tile, uint4 (&v)[B], float& nv) {
+  // packed codes and norm (and, for kProd, signs and rho) of this lane's key
+  // (clamped to n - 1), one tile ahead; a fetch past the last tile also
+  // reads key n - 1 and is unused
+  auto fetch = [&](int64_t tile, uint4 (&v)[B], float& nv, uint4& sv, float& rv) {
     int64_t key = tile * 32 + kl;
     key = key < n ? key : n - 1;
 #pragma unroll
     for (int p = 0; p < B; ++p) v[p] = *reinterpret_cast<const uint4*>(codes + (key * B + p) * 4);
     nv = norms[key];
+    if constexpr (kProd) {
+      sv = *reinterpret_cast<const uint4*>(signs + key * 4);
+      rv = rnorms[key];
+    }
   };
   // This block's tiles: tier t = blockIdx.x / stride walks the range
   // [bound_t, bound_t+1) (bound_0 = 0, bound_3 = tiles) from its offset
@@ -173,9 +196,9 @@ dequant_mfma128_kernel(const uint32_t* __restrict__ codes, const float* __restri
   const int64_t tier = bid / stride;
   const int64_t tbeg = tier == 0 ? 0 : tier == 1 ? bound1 : bound2;
   const int64_t tend = tier == 0 ? bound1 : tier == 1 ? bound2 : tiles;
-  uint4 nxt[B];
-  float nxt_n;
-  fetch(tbeg + bid % stride, nxt, nxt_n);
+  uint4 nxt[B], nxt_s = make_uint4(0u, 0u, 0u, 0u);
+  float nxt_n, nxt_r = 0.0f;
+  fetch(tbeg + bid % stride, nxt, nxt_n, nxt_s, nxt_r);
   for (int64_t tile = tbeg + bid % stride; tile < tend; tile += stride) {
     uint32_t pl[B][4];
 #pragma unroll
@@ -185,9 +208,10 @@ dequant_mfma128_kernel(const uint32_t* __restrict__ codes, const float* __restri
       pl[p][2] = nxt[p].z;
       pl[p][3] = nxt[p].w;
     }
-    const float nk = nxt_n;
-    fetch(tile + stride, nxt, nxt_n);
-    f32x16 acc = {};
+    const uint32_t sw[4] = {nxt_s.x, nxt_s.y, nxt_s.z, nxt_s.w};
+    const float nk = nxt_n, rk = nxt_r;
+    fetch(tile + stride, nxt, nxt_n, nxt_s, nxt_r);
+    f32x16 acc = {}, acc2 = {};
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
       uint32_t wp[B];
@@ -198,9 +222,18 @@ dequant_mfma128_kernel(const uint32_t* __restrict__ codes, const float* __restri
       acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, bpi[s][0], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, bpi[s][1], acc, 0, 0, 0);
       if constexpr (!kTwo) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, bpi[s][0], acc, 0, 0, 0);
+      if constexpr (kProd) {
+        // signs of coordinates 16 s + 8 g .. + 7: byte 2 (s % 2) + g of word s / 2
+        const uint4 sg = score::expand_signs(__builtin_amdgcn_ubfe(sw[s >> 1], 8 * (2 * (s & 1) + g), 8), sgn_mask,
+                                             sgn_one);
+        const f16x8 as = __builtin_bit_cast(f16x8, sg);
+        acc2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(as, bs[s][0], acc2, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(as, bs[s][1], acc2, 0, 0, 0);
+      }
     }
     // lane holds coordinate 32w + kl of keys 8(r/4) + 4g + r%4
     reinterpret_cast<float*>(nrow[w])[kl] = nk * out_scale;  // both lane groups hold key kl
+    if constexpr (kProd) reinterpret_cast<float*>(crow[w])[kl] = -nk * rk * kappa * (1.0f / 1024.0f);
     float o[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -209,6 +242,13 @@ dequant_mfma128_kernel(const uint32_t* __restrict__ codes, const float* __restri
       o[4 * q + 1] = v.y * acc[4 * q + 1];
       o[4 * q + 2] = v.z * acc[4 * q + 2];
       o[4 * q + 3] = v.w * acc[4 * q + 3];
+      if constexpr (kProd) {
+        const float4 c = crow[w][2 * q + g];
+        o[4 * q] = fmaf(c.x, acc2[4 * q], o[4 * q]);
+        o[4 * q + 1] = fmaf(c.y, acc2[4 * q + 1], o[4 * q + 1]);
+        o[4 * q + 2] = fmaf(c.z, acc2[4 * q + 2], o[4 * q + 2]);
+        o[4 * q + 3] = fmaf(c.w, acc2[4 * q + 3], o[4 * q + 3]);
+      }
     }
     float* out = khat + tile * 32 * 128 + 32 * w + kl;
     if (tile * 32 + 32 <= n) {
@@ -229,9 +269,9 @@ dequant_mfma128_kernel(const uint32_t* __restrict__ codes, const float* __restri
 constexpr double kTierShare[4][3] = {
     {0.385, 0.33, 0.285}, {0.385, 0.33, 0.285}, {0.55, 0.45, 0.0}, {0.42, 0.33, 0.25}};
 
-template <int B, bool kTwo>
+template <int B, bool kTwo, bool kProd = false>
 hipError_t launch_b(const tq_ctx* h, const uint32_t* codes, const float* norms, int64_t n, float* khat,
-                    hipStream_t stream) {
+                    hipStream_t stream, const uint32_t* signs = nullptr, const float* rnorms = nullptr) {
   const int64_t tiles = (n + 31) / 32;
   // One resident wave of blocks: R per CU (3 when registers and the table
   // allow, else 2).  The CU's wave arbiter favours older waves, so the
@@ -240,7 +280,7 @@ hipError_t launch_b(const tq_ctx* h, const uint32_t* codes, const float* norms, 
   // tile range sized by kTierShare, so that the tiers finish together.  The
   // split only moves work between blocks; any dispatch order gives the same
   // results.
-  constexpr int R = B == 3 ? 2 : 3;
+  constexpr int R = (B == 3 || kProd) ? 2 : 3;
   const int64_t cus = h->cus;
   int64_t blocks, stride, bound1, bound2;
   if (tiles >= 4 * R * cus) {
@@ -258,10 +298,11 @@ hipError_t launch_b(const tq_ctx* h, const uint32_t* codes, const float* norms, 
     stride = blocks;
     bound1 = bound2 = tiles;
   }
-  const auto kernel = dequant_mfma128_kernel<B, kTwo>;
+  const auto kernel = dequant_mfma128_kernel<B, kTwo, kProd>;
+  const float kappa = float(1.2533141373155002512 / 128.0);  // sqrt(pi/2) / d
   hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kDqThreads), 0, stream, codes, norms, n,
                      reinterpret_cast<const uint4*>(h->d_dq_frag), h->cb, h->dqt, khat, tiles, stride, bound1,
-                     bound2);
+                     bound2, signs, rnorms, reinterpret_cast<const uint4*>(h->d_ds_frag), kappa);
   return hipGetLastError();
 }
 
@@ -283,6 +324,23 @@ hipError_t launch_dequant_mfma128(const tq_ctx* h, const uint32_t* codes, const 
                  : launch_b<2, false>(h, codes, norms, n, khat, stream);
     case 3: return launch_b<3, false>(h, codes, norms, n, khat, stream);
     case 4: return launch_b<4, false>(h, codes, norms, n, khat, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_dequant_prod_mfma128(const tq_ctx* h, const uint32_t* codes, const uint32_t* signs,
+                                       const float* norms, const float* rnorms, int64_t n, float* out,
+                                       hipStream_t stream) {
+  const bool two = h->dqt.two_pass != 0;
+  switch (h->code_bits) {
+    case 1:
+      return two ? launch_b<1, true, true>(h, codes, norms, n, out, stream, signs, rnorms)
+                 : launch_b<1, false, true>(h, codes, norms, n, out, stream, signs, rnorms);
+    case 2:
+      return two ? launch_b<2, true, true>(h, codes, norms, n, out, stream, signs, rnorms)
+                 : launch_b<2, false, true>(h, codes, norms, n, out, stream, signs, rnorms);
+    case 3: return launch_b<3, false, true>(h, codes, norms, n, out, stream, signs, rnorms);
+    case 4: return launch_b<4, false, true>(h, codes, norms, n, out, stream, signs, rnorms);
     default: return hipErrorInvalidValue;
   }
 }

@@ -28,7 +28,7 @@ void free_device(tq_ctx* h) {
     if (*p) (void)hipFree(*p);
     *p = nullptr;
   }
-  uint16_t** frags[] = {&h->d_pi_frag, &h->d_g_frag, &h->d_dq_frag};
+  uint16_t** frags[] = {&h->d_pi_frag, &h->d_g_frag, &h->d_dq_frag, &h->d_ds_frag};
   for (uint16_t** p : frags) {
     if (*p) (void)hipFree(*p);
     *p = nullptr;
@@ -98,9 +98,29 @@ int build_fragments(tq_ctx* h) {
           df[(((size_t(w) * 8 + s) * 2 + 0) * 64 + l) * 8 + e] = hi;
           df[(((size_t(w) * 8 + s) * 2 + 1) * 64 + l) * 8 + e] = f16_bits(x - f16_value(hi));
         }
+  // corrected reconstruction: the same layout for 2^10 S, S = G Pi (computed
+  // in float64 from the float32 matrices): lane l of word w, step s holds
+  // 2^10 S[16s + 8(l/32) + e][32w + l%32]
+  std::vector<double> sm(size_t(d) * d, 0.0);
+  for (int i = 0; i < d; ++i)
+    for (int k = 0; k < d; ++k) {
+      const double gik = h->g[size_t(i) * d + k];
+      for (int j = 0; j < d; ++j) sm[size_t(i) * d + j] += gik * double(h->pi[size_t(k) * d + j]);
+    }
+  std::vector<uint16_t> sf(size_t(4) * 8 * 2 * 64 * 8);
+  for (int w = 0; w < 4; ++w)
+    for (int s = 0; s < 8; ++s)
+      for (int l = 0; l < 64; ++l)
+        for (int e = 0; e < 8; ++e) {
+          const float x = float(sm[size_t(16 * s + 8 * (l >> 5) + e) * d + 32 * w + (l & 31)] * 1024.0);
+          const uint16_t hi = f16_bits(x);
+          sf[(((size_t(w) * 8 + s) * 2 + 0) * 64 + l) * 8 + e] = hi;
+          sf[(((size_t(w) * 8 + s) * 2 + 1) * 64 + l) * 8 + e] = f16_bits(x - f16_value(hi));
+        }
   int rc = upload_u16(&h->d_pi_frag, pf);
   if (rc != TQ_OK) return rc;
   if ((rc = upload_u16(&h->d_g_frag, gf)) != TQ_OK) return rc;
+  if ((rc = upload_u16(&h->d_ds_frag, sf)) != TQ_OK) return rc;
   return upload_u16(&h->d_dq_frag, df);
 }
 
@@ -491,8 +511,10 @@ int tq_dequant_prod(tq_handle h, const uint32_t* codes, const uint32_t* signs, c
   if (!codes || !signs || !norms || !rnorms || !ktilde) return TQ_EINVAL;
   if (n > int64_t(0x7FFFFFFF) * 4) return TQ_EUNSUPPORTED;
   if (check_device(h) != TQ_OK) return TQ_EINVAL;
-  const hipError_t e = tqdev::launch_dequant_prod_v1(h, codes, signs, norms, rnorms, n, ktilde,
-                                                     static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = (!tqdev::force_reference_kernels() && tqdev::dequant_mfma128_supported(h) && h->d_ds_frag)
+                           ? tqdev::launch_dequant_prod_mfma128(h, codes, signs, norms, rnorms, n, ktilde, s)
+                           : tqdev::launch_dequant_prod_v1(h, codes, signs, norms, rnorms, n, ktilde, s);
   return e == hipSuccess ? TQ_OK : TQ_EHIP;
 }
 

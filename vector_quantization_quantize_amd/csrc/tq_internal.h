@@ -67,6 +67,7 @@ struct tq_ctx {
   uint16_t* d_pi_frag = nullptr;  // [word 4][step 8][piece 2][lane 64][8] f16 pieces of 2^12 Pi
   uint16_t* d_g_frag = nullptr;   // [word 4][step 8][piece 2][lane 64][8] f16 pieces of 2^10 G
   uint16_t* d_dq_frag = nullptr;  // [word 4][step 8][piece 2][lane 64][8] f16 pieces of 2^12 Pi (B operand)
+  uint16_t* d_ds_frag = nullptr;  // the same for 2^10 S, S = G Pi (corrected reconstruction)
   tqdev::Codebook cb{};
   tqdev::PlaneExpansion planes{};
   bool symmetric = false;  // level set exactly symmetric in float32
@@ -200,7 +201,11 @@ hipError_t launch_fill_u32(unsigned int* p, int64_t n, unsigned int v, hipStream
 
 hipError_t launch_dequant_v1(const tq_ctx* h, const uint32_t* codes, const float* norms, int64_t n,
                              float* khat, hipStream_t stream);
-// k_tilde = n Pi^T (c[idx] + rho sqrt(pi/2)/d G^T (2 beta - 1)), float32
+// k_tilde = n Pi^T (c[idx] + rho sqrt(pi/2)/d G^T (2 beta - 1)); d = 128 on
+// the matrix cores (dequant_mfma.hip), float32 otherwise (kernels_ref.hip)
+hipError_t launch_dequant_prod_mfma128(const tq_ctx* h, const uint32_t* codes, const uint32_t* signs,
+                                       const float* norms, const float* rnorms, int64_t n, float* out,
+                                       hipStream_t stream);
 hipError_t launch_dequant_prod_v1(const tq_ctx* h, const uint32_t* codes, const uint32_t* signs,
                                   const float* norms, const float* rnorms, int64_t n, float* out,
                                   hipStream_t stream);
