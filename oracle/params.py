@@ -202,6 +202,11 @@ class Params:
     g: np.ndarray
     centroids: np.ndarray
     thresholds: np.ndarray
+    # fractional widths: rotated coordinates 0 .. hi-1 use the finer level
+    # set below (one more index bit); hi = 0 for a plain handle
+    hi: int = 0
+    centroids_hi: np.ndarray = None
+    thresholds_hi: np.ndarray = None
 
     @property
     def code_bits(self):
@@ -230,6 +235,28 @@ def init(d, bits, seed):
     c64, _ = sphere_codebook_fp64(d, levels)
     c32 = c64.astype(np.float32).astype(np.float64)
     return Params(d, bits, int(seed), pi, g, c32, thresholds_from_centroids(c32))
+
+
+def init_split(d, bits, hi, seed):
+    """Fractional widths: ``init(d, bits, seed)`` plus a second Lloyd-Max
+    level set with twice the levels (one more index bit) for the rotated
+    coordinates 0 .. hi-1.  The stage-1 budget is then (bits - 1) + hi / d
+    bits per coordinate, bits + hi / d with the QJL sign bit; e.g. d = 128,
+    hi = 64 gives 2.5 bits from bits = 2 and 3.5 from bits = 3.  Every
+    rotated coordinate has the same law, so which coordinates get the finer
+    set does not change the expected error; the first hi keeps the layout
+    simple.  bits in [2, 4] (the finer set stays within 16 levels)."""
+    if not (2 <= bits <= 4):
+        raise ValueError("bits must lie in [2, 4] for fractional widths")
+    if not (0 <= hi <= d):
+        raise ValueError("hi must lie in [0, d]")
+    pr = init(d, bits, seed)
+    c64, _ = sphere_codebook_fp64(d, 1 << bits)
+    c32 = c64.astype(np.float32).astype(np.float64)
+    pr.hi = int(hi)
+    pr.centroids_hi = c32
+    pr.thresholds_hi = thresholds_from_centroids(c32)
+    return pr
 
 
 def hadamard_rotation(d, seed):

@@ -58,6 +58,16 @@ Stages (page, section):
    stored token visible; also lse = log sum_t exp(scale * s_t).  With no
    tokens o = 0 and lse = -inf.
 
+11. fractional widths (2.5 or 3.5 bits per coordinate): the rotated
+   coordinates are split in two groups, the first hi with one more index
+   bit (a Lloyd-Max set with twice the levels for the same coordinate law)
+   and the rest with bits - 1; stages 3, 4, 6, 7 and 9 take each
+   coordinate's level from its own set.  The pages quote these operating
+   points ("TurboQuant digest", section 4: 3.5 bits per channel with no
+   loss of quality, 2.5 bits with a marginal one) without the mechanism;
+   this split of the rotated coordinates into two widths is the reading
+   taken.
+
 Packed layout (bit planes): ``codes[n][B][W]`` and ``signs[n][W]`` as
 uint32 with W = ceil(d / 32); bit p of the index of coordinate j is bit
 (j mod 32) of word (j div 32) of plane p (LSB first); padding bits are 0.
@@ -108,14 +118,30 @@ def rotate(params: Params, u):
 
 
 def bucketize(params: Params, z):
-    """Stage 3: index = #{i : t_i <= fp32(z)} (upper cell on a tie)."""
+    """Stage 3: index = #{i : t_i <= fp32(z)} (upper cell on a tie), with
+    the finer thresholds for coordinates below ``params.hi``."""
     z32 = np.asarray(z, dtype=np.float64).astype(np.float32).astype(np.float64)
-    return np.searchsorted(params.thresholds, z32, side="right").astype(np.int64)
+    h = params.hi
+    if h == 0:
+        return np.searchsorted(params.thresholds, z32, side="right").astype(np.int64)
+    fine = np.searchsorted(params.thresholds_hi, z32[:, :h], side="right")
+    base = np.searchsorted(params.thresholds, z32[:, h:], side="right")
+    return np.concatenate([fine, base], axis=1).astype(np.int64)
+
+
+def levels_of(params: Params, idx):
+    """c[idx] for an (n, d) index array, each coordinate from its own level
+    set (the finer one below ``params.hi``)."""
+    idx = np.asarray(idx)
+    h = params.hi
+    if h == 0:
+        return params.centroids[idx]
+    return np.concatenate([params.centroids_hi[idx[:, :h]], params.centroids[idx[:, h:]]], axis=1)
 
 
 def residual(params: Params, z, idx):
     """Stage 4: r = z - c[idx] and its norm."""
-    r = z - params.centroids[idx]
+    r = z - levels_of(params, idx)
     return r, np.sqrt(np.sum(r * r, axis=1))
 
 
@@ -149,7 +175,7 @@ def query_transform(params: Params, queries):
 def scores(params: Params, queries, idx, beta, norms, rnorms):
     """Stage 6: (m, n) matrix of estimates <q_a, k_hat_b>."""
     v, w = query_transform(params, queries)
-    chat = params.centroids[np.asarray(idx)]                  # (n, d)
+    chat = levels_of(params, idx)                             # (n, d)
     signs = np.where(np.asarray(beta), 1.0, -1.0)             # (n, d)
     stage1 = v @ chat.T                                       # (m, n)
     qjl = w @ signs.T                                         # (m, n)
@@ -159,14 +185,14 @@ def scores(params: Params, queries, idx, beta, norms, rnorms):
 
 def dequant_mse(params: Params, idx, norms):
     """Stage 7: k_hat = n * Pi^T c[idx] for each key."""
-    chat = params.centroids[np.asarray(idx)]
+    chat = levels_of(params, idx)
     return np.asarray(norms, dtype=np.float64)[:, None] * (chat @ params.pi)
 
 
 def dequant_prod(params: Params, idx, beta, norms, rnorms):
     """Stage 9: k_tilde = n Pi^T (c[idx] + rho sqrt(pi/2)/d G^T (2 beta - 1))
     for each key (rows of the result)."""
-    chat = params.centroids[np.asarray(idx)]                  # (n, d)
+    chat = levels_of(params, idx)                             # (n, d)
     signs = np.where(np.asarray(beta), 1.0, -1.0)             # (n, d)
     scale = np.asarray(rnorms, dtype=np.float64) * QJL_CONST / params.d
     corr = scale[:, None] * (signs @ params.g)                # row b: (G^T s_b)^T
@@ -265,10 +291,37 @@ def unpack_codes(codes, d):
     return idx
 
 
+def pack_codes_split(idx, code_bits, hi):
+    """Fractional widths: (n, d) indices (coordinates below hi may use one
+    more bit) -> (n, B W + ceil(hi / 32)) uint32: planes 0 .. B-1 over all
+    coordinates as in pack_codes, one after another, then plane B over the
+    coordinates 0 .. hi-1 only."""
+    idx = np.asarray(idx, dtype=np.int64)
+    n = idx.shape[0]
+    base = pack_codes(idx & ((1 << code_bits) - 1), code_bits).reshape(n, -1)
+    if hi == 0:
+        return base
+    top = pack_bits(((idx[:, :hi] >> code_bits) & 1).astype(bool))
+    return np.concatenate([base, top], axis=1)
+
+
+def unpack_codes_split(codes, d, code_bits, hi):
+    """Inverse of pack_codes_split."""
+    codes = np.asarray(codes, dtype=np.uint32)
+    n = codes.shape[0]
+    w = words_per_plane(d)
+    idx = unpack_codes(codes[:, :code_bits * w].reshape(n, code_bits, w), d)
+    if hi:
+        idx[:, :hi] |= unpack_bits(codes[:, code_bits * w:], hi).astype(np.int64) << code_bits
+    return idx
+
+
 def pack(params: Params, qz: Quantized):
-    """Packed buffers (codes, signs, norms fp32, rnorms fp32) of a batch."""
-    return (pack_codes(qz.idx, params.code_bits), pack_bits(qz.beta),
-            qz.norms.astype(np.float32), qz.rnorms.astype(np.float32))
+    """Packed buffers (codes, signs, norms fp32, rnorms fp32) of a batch;
+    codes as pack_codes_split when the parameters have fractional widths."""
+    codes = (pack_codes_split(qz.idx, params.code_bits, params.hi) if params.hi
+             else pack_codes(qz.idx, params.code_bits))
+    return (codes, pack_bits(qz.beta), qz.norms.astype(np.float32), qz.rnorms.astype(np.float32))
 
 
 def value_group_of_e(code_bits):

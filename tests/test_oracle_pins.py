@@ -641,3 +641,95 @@ def test_hadamard_quantizer_mse_close_to_haar():
     qz = tq.quantize(pr, x)
     mse = float(np.mean(qz.rnorms ** 2))
     assert abs(mse / 0.0340 - 1.0) < 0.1, mse
+
+
+# ---------------------------------------------------------------------------
+# fractional widths (stage 11)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,bits,hi", [(40, 2, 16), (128, 3, 64), (33, 2, 33), (50, 4, 7)])
+def test_split_indices_are_the_two_plain_quantizers(d, bits, hi):
+    """Stage 11 against two independently pinned quantizers of the same
+    seed: coordinates below hi carry the (bits + 1)-bit handle's index, the
+    rest the bits-bit handle's, and the residual / scores / reconstructions
+    use the matching levels (the finer set's levels are the bits + 1
+    handle's, the coarse set's the bits handle's)."""
+    seed = 5
+    pr = P.init_split(d, bits, hi, seed)
+    fine, base = P.init(d, bits + 1, seed), P.init(d, bits, seed)
+    assert np.array_equal(pr.centroids_hi, fine.centroids) and np.array_equal(pr.centroids, base.centroids)
+    rs = np.random.default_rng(d + hi)
+    keys = rs.standard_normal((60, d)) * 2.0
+    qz = tq.quantize(pr, keys)
+    qf, qb = tq.quantize(fine, keys), tq.quantize(base, keys)
+    assert np.array_equal(qz.idx[:, :hi], qf.idx[:, :hi])
+    assert np.array_equal(qz.idx[:, hi:], qb.idx[:, hi:])
+    # the residual takes each coordinate's own level
+    r = np.concatenate([qf.z[:, :hi] - fine.centroids[qf.idx[:, :hi]],
+                        qb.z[:, hi:] - base.centroids[qb.idx[:, hi:]]], axis=1)
+    assert np.allclose(qz.rnorms, np.sqrt((r * r).sum(axis=1)), rtol=1e-13)
+    # stage-1 reconstruction: Pi^T of the same level vector
+    khat = tq.dequant_mse(pr, qz.idx, qz.norms)
+    want = qz.norms[:, None] * (np.concatenate([fine.centroids[qz.idx[:, :hi]], base.centroids[qz.idx[:, hi:]]],
+                                               axis=1) @ pr.pi)
+    assert np.allclose(khat, want, rtol=1e-12, atol=1e-12)
+    # the corrected reconstruction reproduces every score (linearity in q)
+    qs = rs.standard_normal((4, d))
+    kt = tq.dequant_prod(pr, qz.idx, qz.beta, qz.norms, qz.rnorms)
+    s = tq.scores(pr, qs, qz.idx, qz.beta, qz.norms, qz.rnorms)
+    assert np.allclose(qs @ kt.T, s, rtol=1e-11, atol=1e-11)
+
+
+def test_split_mse_interpolates_the_closed_forms():
+    """Empirical ||z - c[idx]||^2 over many rotated keys equals
+    hi * m(2L) + (d - hi) * m(L), m the per-coordinate closed form of each
+    level set: 2.5 bits lands between the 2- and 3-bit errors."""
+    d, bits, hi = 64, 2, 32
+    pr = P.init_split(d, bits, hi, 4)
+    keys = np.random.default_rng(2).standard_normal((20000, d))
+    qz = tq.quantize(pr, keys)
+    emp = np.mean(qz.rnorms ** 2)
+    m_fine, m_base = P.codebook_mse(pr.centroids_hi, d), P.codebook_mse(pr.centroids, d)
+    want = hi * m_fine + (d - hi) * m_base
+    assert abs(emp - want) / want < 0.015
+    assert d * m_fine < emp < d * m_base
+
+
+def test_split_estimator_unbiased_over_seeds():
+    """The score with fractional widths still estimates <q, k> without bias
+    (averaged over seeds of (Pi, G))."""
+    d = 24
+    rs = np.random.default_rng(19)
+    key = rs.standard_normal((1, d))
+    q = rs.standard_normal((1, d))
+    est = []
+    for seed in range(1500):
+        pr = P.init_split(d, 2, 12, seed)
+        z = tq.quantize(pr, key)
+        est.append(tq.scores(pr, q, z.idx, z.beta, z.norms, z.rnorms)[0, 0])
+    est = np.array(est)
+    sem = est.std() / math.sqrt(len(est))
+    assert abs(est.mean() - float(q[0] @ key[0])) < 4 * sem
+
+
+def test_split_pack_bit_positions():
+    """Hand-worked packing: d = 40 (W = 2), B = 1, hi = 8: plane 0 over all
+    40 coordinates in words 0-1, then plane 1 over coordinates 0-7 in word
+    2; the storage is B d + hi index bits per key."""
+    idx = np.zeros((1, 40), dtype=np.int64)
+    idx[0, 0] = 3      # plane 0 word 0 bit 0, plane 1 bit 0
+    idx[0, 7] = 2      # plane 1 bit 7 only
+    idx[0, 33] = 1     # plane 0 word 1 bit 1
+    codes = tq.pack_codes_split(idx, 1, 8)
+    assert codes.shape == (1, 3)
+    assert codes[0].tolist() == [1, 1 << 1, 1 | (1 << 7)]
+    assert np.array_equal(tq.unpack_codes_split(codes, 40, 1, 8), idx)
+    rs = np.random.default_rng(3)
+    big = rs.integers(0, 4, (9, 77))
+    big[:, 45:] &= 1
+    c = tq.pack_codes_split(big, 1, 45)
+    assert c.shape == (9, 3 + 2)
+    assert np.array_equal(tq.unpack_codes_split(c, 77, 1, 45), big)
+    # hi = 0 is the plain layout, flattened
+    plain = rs.integers(0, 8, (4, 70))
+    assert np.array_equal(tq.pack_codes_split(plain, 3, 0), tq.pack_codes(plain, 3).reshape(4, -1))
