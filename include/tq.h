@@ -102,15 +102,34 @@ typedef struct {
   int32_t levels;         /* L = 2^B                                          */
   int32_t words;          /* W = ceil(d / 32)                                 */
   int32_t format_version; /* TQ_FORMAT_VERSION                                */
-  int64_t code_bytes;     /* bytes of codes per key  = 4 B W                  */
+  int64_t code_bytes;     /* bytes of codes per key  = 4 (B W + hi_words)     */
   int64_t sign_bytes;     /* bytes of signs per key  = 4 W                    */
   int64_t key_bytes;      /* code_bytes + sign_bytes + 8 (norm and rnorm)     */
+  int32_t hi;             /* coordinates with one more index bit (0: plain)   */
+  int32_t hi_words;       /* ceil(hi / 32): words of the extra plane          */
 } tq_layout;
 
 /* Build the method for (d, bits, seed) on the current HIP device: rotation,
  * projection and codebook as described above.  2 <= d <= 4096,
  * 2 <= bits <= 5.  Synchronous.  *out receives the handle. */
 TQ_API int tq_init(int32_t d, int32_t bits, uint64_t seed, tq_handle* out);
+
+/* Fractional widths ("TurboQuant digest", section 4 quotes 2.5 and 3.5
+ * bits per channel as operating points; the pages give no mechanism, so
+ * this is a reading): tq_init(d, bits, seed) whose rotated coordinates
+ * 0 .. hi-1 are quantized with the Lloyd-Max set of 2^bits levels (one more
+ * index bit, the codebook tq_init(d, bits + 1, .) uses) and the rest with the
+ * 2^(bits-1) levels of tq_init(d, bits, .).  Budget: bits + hi / d bits per
+ * coordinate with the sign bit (d = 128, hi = 64: 2.5 from bits = 2, 3.5
+ * from bits = 3).  Codes per key: the B = bits - 1 planes of W words as
+ * usual, then one plane of hi_words = ceil(hi / 32) words holding bit B of
+ * the indices of coordinates 0 .. hi-1 (bit j mod 32 of word j div 32,
+ * padding 0); tq_layout gives code_bytes.  2 <= bits <= 4, 0 <= hi <= d
+ * (hi = 0 is tq_init).  tq_quantize, tq_logits, tq_logits_topk,
+ * tq_dequant_mse, tq_dequant_prod and the key side of tq_attention take such
+ * handles (general kernels); tq_pack_values and the value side of
+ * tq_attention return TQ_EUNSUPPORTED. */
+TQ_API int tq_init_split(int32_t d, int32_t bits, int32_t hi, uint64_t seed, tq_handle* out);
 
 /* As tq_init but with caller-given float32 matrices (host, row-major d x d):
  * `pi` is used as the rotation, `g` as the projection; the codebook still

@@ -83,12 +83,24 @@ def compare_quantize(params, qz, codes, signs, norms, rnorms):
     norms = np.asarray(norms, dtype=np.float64)
     rnorms = np.asarray(rnorms, dtype=np.float64)
     rep = QuantizeReport(elements=2 * qz.idx.size)
-    rep.padding_bad = _padding_zero(codes, d) + _padding_zero(signs, d)
-
-    idx = tq.unpack_codes(codes, d)
+    if params.hi:
+        # fractional widths: B full planes, then the plane of the first hi
+        # coordinates; the decision window is each coordinate's own set
+        n, b, w = codes.shape[0], params.code_bits, tq.words_per_plane(d)
+        codes = codes.reshape(n, -1)
+        rep.padding_bad = (_padding_zero(codes[:, :b * w].reshape(n, b, w), d) + _padding_zero(codes[:, b * w:], params.hi)
+                           + _padding_zero(signs, d))
+        idx = tq.unpack_codes_split(codes, d, b, params.hi)
+        h = params.hi
+        dist = np.concatenate(
+            [np.min(np.abs(qz.z[:, :h, None] - params.thresholds_hi[None, None, :]), axis=2),
+             np.min(np.abs(qz.z[:, h:, None] - params.thresholds[None, None, :]), axis=2)], axis=1)
+    else:
+        rep.padding_bad = _padding_zero(codes, d) + _padding_zero(signs, d)
+        idx = tq.unpack_codes(codes, d)
+        dist = np.min(np.abs(qz.z[:, :, None] - params.thresholds[None, None, :]), axis=2) \
+            if len(params.thresholds) else np.full(qz.z.shape, np.inf)
     cmis = idx != qz.idx
-    dist = np.min(np.abs(qz.z[:, :, None] - params.thresholds[None, None, :]), axis=2) \
-        if len(params.thresholds) else np.full(qz.z.shape, np.inf)
     rep.code_mismatch = int(cmis.sum())
     rep.code_bad = int((cmis & (dist >= CODE_WINDOW)).sum())
     flipped = cmis.any(axis=1)

@@ -83,6 +83,10 @@ def test_bad_arguments_are_rejected(tqm):
     for d, bits in [(1, 3), (4097, 3), (128, 1), (128, 6)]:
         assert lib.tq_init(d, bits, 0, ctypes.byref(out)) == tqm.TQ_EINVAL
     assert lib.tq_init(128, 3, 0, None) == tqm.TQ_EINVAL
+    # fractional widths: hi in [0, d], bits <= 4 when hi > 0
+    for d, bits, hi in [(128, 3, -1), (128, 3, 129), (128, 5, 1), (1, 3, 0), (40, 1, 3)]:
+        assert lib.tq_init_split(d, bits, hi, 0, ctypes.byref(out)) == tqm.TQ_EINVAL
+    assert lib.tq_init_split(128, 3, 64, 0, None) == tqm.TQ_EINVAL
     assert lib.tq_host_params(0, 3, 0, None, None, None, None) == tqm.TQ_EINVAL
     assert lib.tq_quantize(None, None, 0, 1, 128, None, None, None, None, None) == tqm.TQ_EINVAL
     assert lib.tq_logits(None, None, 1, 1, None, None, None, None, 1, None, None, 0, None) == tqm.TQ_EINVAL

@@ -24,7 +24,7 @@ TQ_BF16 = 1
 TQ_FORMAT_VERSION = 1
 
 # every symbol include/tq.h declares
-EXPORTS = ("tq_init", "tq_init_explicit", "tq_init_hadamard", "tq_hadamard_rotation", "tq_destroy", "tq_get_layout", "tq_host_params",
+EXPORTS = ("tq_init", "tq_init_explicit", "tq_init_hadamard", "tq_init_split", "tq_hadamard_rotation", "tq_destroy", "tq_get_layout", "tq_host_params",
            "tq_params_hash", "tq_quantize", "tq_logits_workspace_size", "tq_logits",
            "tq_logits_topk_workspace_size", "tq_logits_topk", "tq_dequant_mse", "tq_dequant_prod", "tq_dense_logits", "tq_pack_values",
            "tq_attention_workspace_size", "tq_attention", "tq_strerror")
@@ -40,7 +40,8 @@ class Layout(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("bits", ctypes.c_int32), ("code_bits", ctypes.c_int32),
                 ("levels", ctypes.c_int32), ("words", ctypes.c_int32),
                 ("format_version", ctypes.c_int32), ("code_bytes", ctypes.c_int64),
-                ("sign_bytes", ctypes.c_int64), ("key_bytes", ctypes.c_int64)]
+                ("sign_bytes", ctypes.c_int64), ("key_bytes", ctypes.c_int64),
+                ("hi", ctypes.c_int32), ("hi_words", ctypes.c_int32)]
 
 
 _LIB = None
@@ -59,6 +60,7 @@ def _lib():
         "tq_init": (ctypes.c_int, [i32, i32, u64, ctypes.POINTER(vp)]),
         "tq_init_explicit": (ctypes.c_int, [i32, i32, fp, fp, ctypes.POINTER(vp)]),
         "tq_init_hadamard": (ctypes.c_int, [i32, i32, u64, ctypes.POINTER(vp)]),
+        "tq_init_split": (ctypes.c_int, [i32, i32, i32, u64, ctypes.POINTER(vp)]),
         "tq_hadamard_rotation": (ctypes.c_int, [i32, u64, vp]),
         "tq_destroy": (ctypes.c_int, [vp]),
         "tq_get_layout": (ctypes.c_int, [vp, ctypes.POINTER(Layout)]),
@@ -114,6 +116,12 @@ class Handle:
         self.bits = lay.bits
         self.code_bits = lay.code_bits
         self.words = lay.words
+        self.hi = lay.hi
+        self.hi_words = lay.hi_words
+        # per-key shape of the codes: (B, W) planes, or flat B W + hi_words
+        # words with fractional widths
+        self.code_shape = ((lay.code_bits * lay.words + lay.hi_words,) if lay.hi
+                           else (lay.code_bits, lay.words))
 
     @property
     def ptr(self):
@@ -135,6 +143,15 @@ def tq_init(d, bits, seed):
     out = ctypes.c_void_p()
     _check("tq_init", _lib().tq_init(int(d), int(bits), ctypes.c_uint64(int(seed) & (2 ** 64 - 1)),
                                      ctypes.byref(out)))
+    return Handle(out)
+
+
+def tq_init_split(d, bits, hi, seed):
+    """Handle with fractional widths: rotated coordinates 0 .. hi-1 get one
+    more index bit (bits + hi / d bits per coordinate)."""
+    out = ctypes.c_void_p()
+    _check("tq_init_split", _lib().tq_init_split(int(d), int(bits), int(hi), ctypes.c_uint64(int(seed) & (2 ** 64 - 1)),
+                                                 ctypes.byref(out)))
     return Handle(out)
 
 
@@ -196,7 +213,7 @@ def tq_host_params(d, bits, seed):
 def empty_packed(h, n, device="cuda"):
     """Allocate (codes, signs, norms, rnorms) device tensors for n keys."""
     import torch
-    codes = torch.empty((n, h.code_bits, h.words), dtype=torch.int32, device=device)
+    codes = torch.empty((n,) + h.code_shape, dtype=torch.int32, device=device)
     signs = torch.empty((n, h.words), dtype=torch.int32, device=device)
     norms = torch.empty((n,), dtype=torch.float32, device=device)
     rnorms = torch.empty((n,), dtype=torch.float32, device=device)
@@ -206,7 +223,7 @@ def empty_packed(h, n, device="cuda"):
 def tq_quantize(h, keys, out=None, stream=None):
     """keys: cuda tensor (n, d) float32 or bfloat16 with unit column stride.
 
-    Returns (codes int32 (n, B, W), signs int32 (n, W), norms, rnorms); the
+    Returns (codes int32 (n,) + h.code_shape, signs int32 (n, W), norms, rnorms); the
     int32 tensors hold the uint32 words bit for bit."""
     import torch
     if keys.dim() != 2 or keys.shape[1] != h.d or keys.stride(1) != 1:

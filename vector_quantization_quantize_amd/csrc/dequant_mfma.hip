@@ -309,7 +309,7 @@ hipError_t launch_b(const tq_ctx* h, const uint32_t* codes, const float* norms, 
 }  // namespace
 
 bool dequant_mfma128_supported(const tq_ctx* h) {
-  return h->d == 128 && h->d_dq_frag && h->code_bits >= 1 && h->code_bits <= 4;
+  return h->d == 128 && h->hi == 0 && h->d_dq_frag && h->code_bits >= 1 && h->code_bits <= 4;
 }
 
 hipError_t launch_dequant_mfma128(const tq_ctx* h, const uint32_t* codes, const float* norms, int64_t n,

@@ -1,6 +1,11 @@
 // Straightforward gfx950 kernels for every stage of the path (fp32 VALU,
 // any d in [2, 4096], any bits in [2, 5]).  They are the general fallback
-// and the baseline the tuned kernels are checked against.
+// and the baseline the tuned kernels are checked against, and the kernels
+// of fractional widths: the first `hi` rotated coordinates take their level
+// from a second set `cbh` with one more index bit, stored as one extra
+// plane of hi_words = ceil(hi / 32) words after the code_bits full planes
+// (per-key code stride code_bits * words + hi_words; hi = 0 for a plain
+// handle).
 //
 // Stages (web pages about TurboQuant, by title and section):
 //   quantize  - "TurboQuant tutorial" (gitcode.csdn.net), PolarQuant and QJL
@@ -44,7 +49,7 @@ quantize_ref_kernel(const void* __restrict__ keys, int key_dtype, int64_t n, int
                     int code_bits, int words, int tk, const float* __restrict__ piT,
                     const float* __restrict__ gT, Codebook cb, uint32_t* __restrict__ codes,
                     uint32_t* __restrict__ signs, float* __restrict__ norms,
-                    float* __restrict__ rnorms) {
+                    float* __restrict__ rnorms, int hi, int hi_words, Codebook cbh) {
   extern __shared__ float smem[];
   const int ds = d + 1;  // padded row stride
   float* buf0 = smem;
@@ -52,12 +57,16 @@ quantize_ref_kernel(const void* __restrict__ keys, int key_dtype, int64_t n, int
   float* nrm = buf1 + size_t(tk) * ds;
   float* lvl = nrm + tk;           // levels
   float* thr = lvl + kMaxLevels;   // thresholds
+  float* lvlh = thr + kMaxLevels;  // the finer set (coordinates below hi)
+  float* thrh = lvlh + kMaxLevels;
   const int tid = threadIdx.x;
   const int64_t base = int64_t(blockIdx.x) * tk;
-  const int levels = cb.levels;
+  const int64_t cw = int64_t(code_bits) * words + hi_words;  // code words per key
   if (tid < kMaxLevels) {
     lvl[tid] = cb.c[tid];
     thr[tid] = cb.t[tid];
+    lvlh[tid] = cbh.c[tid];
+    thrh[tid] = cbh.t[tid];
   }
   // keys -> buf0 (fp32)
   for (int p = tid; p < tk * d; p += kThreads) {
@@ -98,18 +107,21 @@ quantize_ref_kernel(const void* __restrict__ keys, int key_dtype, int64_t n, int
   // bucketize, residual in place, code planes
   for (int p = tid; p < tk * words; p += kThreads) {
     const int k = p / words, w = p - k * words;
-    uint32_t plane[4] = {0u, 0u, 0u, 0u};
+    uint32_t plane[5] = {0u, 0u, 0u, 0u, 0u};
     for (int b = 0; b < 32; ++b) {
       const int j = 32 * w + b;
       if (j >= d) break;
       const float z = buf1[k * ds + j];
-      const int idx = bucket(z, thr, levels);
-      buf1[k * ds + j] = z - lvl[idx];
-      for (int q = 0; q < code_bits; ++q) plane[q] |= uint32_t((idx >> q) & 1) << b;
+      const bool fine = j < hi;
+      const int idx = bucket(z, fine ? thrh : thr, fine ? cbh.levels : cb.levels);
+      buf1[k * ds + j] = z - (fine ? lvlh[idx] : lvl[idx]);
+      for (int q = 0; q <= code_bits; ++q) plane[q] |= uint32_t((idx >> q) & 1) << b;
     }
     const int64_t key = base + k;
-    if (key < n)
-      for (int q = 0; q < code_bits; ++q) codes[(key * code_bits + q) * words + w] = plane[q];
+    if (key < n) {
+      for (int q = 0; q < code_bits; ++q) codes[key * cw + int64_t(q) * words + w] = plane[q];
+      if (w < hi_words) codes[key * cw + int64_t(code_bits) * words + w] = plane[code_bits];
+    }
   }
   __syncthreads();
   for (int k = tid; k < tk; k += kThreads) {
@@ -184,14 +196,20 @@ __global__ void __launch_bounds__(kThreads)
 logits_ref_kernel(const float* __restrict__ vw, int64_t nq, int d, int code_bits, int words,
                   int64_t n, int64_t stride, int64_t half, const uint32_t* __restrict__ codes,
                   const uint32_t* __restrict__ signs, const float* __restrict__ norms,
-                  const float* __restrict__ rnorms, float* __restrict__ scores, Codebook cb) {
+                  const float* __restrict__ rnorms, float* __restrict__ scores, Codebook cb, int hi,
+                  int hi_words, Codebook cbh) {
   extern __shared__ float smem[];
   float* lvl = smem;
-  float* qv = smem + kMaxLevels;  // [4][d] v then [4][d] w
+  float* lvlh = smem + kMaxLevels;    // the finer set (coordinates below hi)
+  float* qv = smem + 2 * kMaxLevels;  // [4][d] v then [4][d] w
   const int64_t g = blockIdx.y;
   const int64_t t = int64_t(blockIdx.x) * kThreads + threadIdx.x;
   const int64_t key = g * n + t;
-  if (threadIdx.x < kMaxLevels) lvl[threadIdx.x] = cb.c[threadIdx.x];
+  if (threadIdx.x < kMaxLevels) {
+    lvl[threadIdx.x] = cb.c[threadIdx.x];
+    lvlh[threadIdx.x] = cbh.c[threadIdx.x];
+  }
+  const int64_t cw = int64_t(code_bits) * words + hi_words;  // code words per key
   const float kappa = 1.2533141373155002512f / float(d);  // sqrt(pi/2) / d
   float nk = 0.f, rho = 0.f;
   if (t < n) {
@@ -211,15 +229,16 @@ logits_ref_kernel(const float* __restrict__ vw, int64_t nq, int d, int code_bits
     if (t >= n) continue;
     float a1[4] = {0.f, 0.f, 0.f, 0.f}, a2[4] = {0.f, 0.f, 0.f, 0.f};
     for (int w = 0; w < words; ++w) {
-      uint32_t plane[4] = {0u, 0u, 0u, 0u};
-      for (int q = 0; q < code_bits; ++q) plane[q] = codes[(key * code_bits + q) * words + w];
+      uint32_t plane[5] = {0u, 0u, 0u, 0u, 0u};
+      for (int q = 0; q < code_bits; ++q) plane[q] = codes[key * cw + int64_t(q) * words + w];
+      if (w < hi_words) plane[code_bits] = codes[key * cw + int64_t(code_bits) * words + w];
       const uint32_t sw = signs[key * words + w];
       for (int b = 0; b < 32; ++b) {
         const int j = 32 * w + b;
         if (j >= d) break;
         int idx = 0;
-        for (int q = 0; q < code_bits; ++q) idx |= int((plane[q] >> b) & 1u) << q;
-        const float cv = lvl[idx];
+        for (int q = 0; q <= code_bits; ++q) idx |= int((plane[q] >> b) & 1u) << q;
+        const float cv = j < hi ? lvlh[idx] : lvl[idx];
         const float sg = ((sw >> b) & 1u) ? 1.0f : -1.0f;
         for (int q = 0; q < 4; ++q) {
           a1[q] = fmaf(qv[q * d + j], cv, a1[q]);
@@ -239,27 +258,34 @@ logits_ref_kernel(const float* __restrict__ vw, int64_t nq, int d, int code_bits
 __global__ void __launch_bounds__(kThreads)
 dequant_ref_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ norms, int64_t n, int d,
                    int code_bits, int words, int tk, const float* __restrict__ pi, Codebook cb,
-                   float* __restrict__ khat) {
+                   float* __restrict__ khat, int hi, int hi_words, Codebook cbh) {
   extern __shared__ float smem[];
   const int ds = d + 1;
   float* ch = smem;                    // [tk][ds] c[idx]
   float* lvl = smem + size_t(tk) * ds;
+  float* lvlh = lvl + kMaxLevels;      // the finer set (coordinates below hi)
   const int tid = threadIdx.x;
   const int64_t base = int64_t(blockIdx.x) * tk;
-  if (tid < kMaxLevels) lvl[tid] = cb.c[tid];
+  const int64_t cw = int64_t(code_bits) * words + hi_words;  // code words per key
+  if (tid < kMaxLevels) {
+    lvl[tid] = cb.c[tid];
+    lvlh[tid] = cbh.c[tid];
+  }
   __syncthreads();
   for (int p = tid; p < tk * words; p += kThreads) {
     const int k = p / words, w = p - k * words;
     const int64_t key = base + k;
-    uint32_t plane[4] = {0u, 0u, 0u, 0u};
-    if (key < n)
-      for (int q = 0; q < code_bits; ++q) plane[q] = codes[(key * code_bits + q) * words + w];
+    uint32_t plane[5] = {0u, 0u, 0u, 0u, 0u};
+    if (key < n) {
+      for (int q = 0; q < code_bits; ++q) plane[q] = codes[key * cw + int64_t(q) * words + w];
+      if (w < hi_words) plane[code_bits] = codes[key * cw + int64_t(code_bits) * words + w];
+    }
     for (int b = 0; b < 32; ++b) {
       const int j = 32 * w + b;
       if (j >= d) break;
       int idx = 0;
-      for (int q = 0; q < code_bits; ++q) idx |= int((plane[q] >> b) & 1u) << q;
-      ch[k * ds + j] = lvl[idx];
+      for (int q = 0; q <= code_bits; ++q) idx |= int((plane[q] >> b) & 1u) << q;
+      ch[k * ds + j] = j < hi ? lvlh[idx] : lvl[idx];
     }
   }
   __syncthreads();
@@ -293,31 +319,38 @@ __global__ void __launch_bounds__(kThreads)
 dequant_prod_ref_kernel(const uint32_t* __restrict__ codes, const uint32_t* __restrict__ signs,
                         const float* __restrict__ norms, const float* __restrict__ rnorms, int64_t n, int d,
                         int code_bits, int words, int tk, const float* __restrict__ pi,
-                        const float* __restrict__ g, Codebook cb, float kappa, float* __restrict__ out) {
+                        const float* __restrict__ g, Codebook cb, float kappa, float* __restrict__ out, int hi,
+                        int hi_words, Codebook cbh) {
   extern __shared__ float smem[];
   const int ds = d + 1;
   float* t = smem;                       // [tk][ds] c[idx], then c + rho kappa G^T s
   float* sg = smem + size_t(tk) * ds;    // [tk][ds] 2 beta - 1
   float* lvl = sg + size_t(tk) * ds;
+  float* lvlh = lvl + kMaxLevels;        // the finer set (coordinates below hi)
   const int tid = threadIdx.x;
   const int64_t base = int64_t(blockIdx.x) * tk;
-  if (tid < kMaxLevels) lvl[tid] = cb.c[tid];
+  const int64_t cw = int64_t(code_bits) * words + hi_words;  // code words per key
+  if (tid < kMaxLevels) {
+    lvl[tid] = cb.c[tid];
+    lvlh[tid] = cbh.c[tid];
+  }
   __syncthreads();
   for (int p = tid; p < tk * words; p += kThreads) {
     const int k = p / words, w = p - k * words;
     const int64_t key = base + k;
-    uint32_t plane[4] = {0u, 0u, 0u, 0u};
+    uint32_t plane[5] = {0u, 0u, 0u, 0u, 0u};
     uint32_t sw = 0u;
     if (key < n) {
-      for (int q = 0; q < code_bits; ++q) plane[q] = codes[(key * code_bits + q) * words + w];
+      for (int q = 0; q < code_bits; ++q) plane[q] = codes[key * cw + int64_t(q) * words + w];
+      if (w < hi_words) plane[code_bits] = codes[key * cw + int64_t(code_bits) * words + w];
       sw = signs[key * words + w];
     }
     for (int b = 0; b < 32; ++b) {
       const int j = 32 * w + b;
       if (j >= d) break;
       int idx = 0;
-      for (int q = 0; q < code_bits; ++q) idx |= int((plane[q] >> b) & 1u) << q;
-      t[k * ds + j] = lvl[idx];
+      for (int q = 0; q <= code_bits; ++q) idx |= int((plane[q] >> b) & 1u) << q;
+      t[k * ds + j] = j < hi ? lvlh[idx] : lvl[idx];
       sg[k * ds + j] = (sw >> b) & 1u ? 1.0f : -1.0f;
     }
   }
@@ -387,13 +420,13 @@ hipError_t launch_quantize_v1(const tq_ctx* h, const void* keys, int key_dtype, 
                               hipStream_t stream) {
   const int d = h->d;
   const int tk = tile_keys(d, 2, 64 * 1024, 64);
-  const size_t lds = (size_t(2) * tk * (d + 1) + tk + 2 * kMaxLevels) * sizeof(float);
+  const size_t lds = (size_t(2) * tk * (d + 1) + tk + 4 * kMaxLevels) * sizeof(float);
   hipError_t e = allow_lds(quantize_ref_kernel, lds);
   if (e != hipSuccess) return e;
   const int64_t blocks = (n + tk - 1) / tk;
   hipLaunchKernelGGL(quantize_ref_kernel, dim3(unsigned(blocks)), dim3(kThreads), lds, stream, keys,
                      key_dtype, n, ldk, d, h->code_bits, h->words, tk, h->d_piT, h->d_gT, h->cb, codes,
-                     signs, norms, rnorms);
+                     signs, norms, rnorms, h->hi, h->hi_words, h->cbh);
   return hipGetLastError();
 }
 
@@ -410,12 +443,13 @@ hipError_t launch_logits_v1(const tq_ctx* h, const float* vw, int64_t groups, in
                             const uint32_t* codes, const uint32_t* signs, const float* norms,
                             const float* rnorms, int64_t n, float* scores, hipStream_t stream) {
   const int d = h->d;
-  const size_t lds = (kMaxLevels + size_t(8) * d) * sizeof(float);
+  const size_t lds = (2 * kMaxLevels + size_t(8) * d) * sizeof(float);
   hipError_t e = allow_lds(logits_ref_kernel, lds);
   if (e != hipSuccess) return e;
   const dim3 grid(static_cast<uint32_t>((n + kThreads - 1) / kThreads), static_cast<uint32_t>(groups));
   hipLaunchKernelGGL(logits_ref_kernel, grid, dim3(kThreads), lds, stream, vw, nq, d, h->code_bits,
-                     h->words, n, vw_stride(d), vw_half(d), codes, signs, norms, rnorms, scores, h->cb);
+                     h->words, n, vw_stride(d), vw_half(d), codes, signs, norms, rnorms, scores, h->cb, h->hi,
+                     h->hi_words, h->cbh);
   return hipGetLastError();
 }
 
@@ -423,12 +457,12 @@ hipError_t launch_dequant_v1(const tq_ctx* h, const uint32_t* codes, const float
                              float* khat, hipStream_t stream) {
   const int d = h->d;
   const int tk = tile_keys(d, 1, 64 * 1024, 64);
-  const size_t lds = (size_t(tk) * (d + 1) + kMaxLevels) * sizeof(float);
+  const size_t lds = (size_t(tk) * (d + 1) + 2 * kMaxLevels) * sizeof(float);
   hipError_t e = allow_lds(dequant_ref_kernel, lds);
   if (e != hipSuccess) return e;
   const int64_t blocks = (n + tk - 1) / tk;
   hipLaunchKernelGGL(dequant_ref_kernel, dim3(unsigned(blocks)), dim3(kThreads), lds, stream, codes, norms,
-                     n, d, h->code_bits, h->words, tk, h->d_pi, h->cb, khat);
+                     n, d, h->code_bits, h->words, tk, h->d_pi, h->cb, khat, h->hi, h->hi_words, h->cbh);
   return hipGetLastError();
 }
 
@@ -437,13 +471,14 @@ hipError_t launch_dequant_prod_v1(const tq_ctx* h, const uint32_t* codes, const 
                                   hipStream_t stream) {
   const int d = h->d;
   const int tk = tile_keys(d, 2, 64 * 1024, 64);
-  const size_t lds = (size_t(2) * tk * (d + 1) + kMaxLevels) * sizeof(float);
+  const size_t lds = (size_t(2) * tk * (d + 1) + 2 * kMaxLevels) * sizeof(float);
   hipError_t e = allow_lds(dequant_prod_ref_kernel, lds);
   if (e != hipSuccess) return e;
   const int64_t blocks = (n + tk - 1) / tk;
   const float kappa = float(1.2533141373155002512 / double(d));  // sqrt(pi/2) / d
   hipLaunchKernelGGL(dequant_prod_ref_kernel, dim3(unsigned(blocks)), dim3(kThreads), lds, stream, codes, signs,
-                     norms, rnorms, n, d, h->code_bits, h->words, tk, h->d_pi, h->d_g, h->cb, kappa, out);
+                     norms, rnorms, n, d, h->code_bits, h->words, tk, h->d_pi, h->d_g, h->cb, kappa, out, h->hi,
+                     h->hi_words, h->cbh);
   return hipGetLastError();
 }
 

@@ -426,7 +426,7 @@ hipError_t launch_b(const tq_ctx* h, const float* queries, int64_t groups, int64
 }  // namespace
 
 bool logits_lut128_supported(const tq_ctx* h) {
-  return h->words == 4 && h->d <= kDim && h->d_piT128 && h->d_sT128 && h->code_bits >= 1 && h->code_bits <= 4;
+  return h->hi == 0 && h->words == 4 && h->d <= kDim && h->d_piT128 && h->d_sT128 && h->code_bits >= 1 && h->code_bits <= 4;
 }
 
 hipError_t launch_logits_lut128(const tq_ctx* h, const float* queries, int64_t groups, int64_t nq,

@@ -621,7 +621,7 @@ hipError_t launch_b(const tq_ctx* h, const void* keys, int64_t n, int64_t ldk, u
 bool quantize_mfma128_supported(const tq_ctx* h, const void* keys, int key_dtype, int64_t ldk,
                                 const void* codes, const void* signs, const void* norms, const void* rnorms) {
   auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-  return h->d == 128 && key_dtype == TQ_BF16 && h->d_pi_frag && h->d_g_frag && h->symmetric && ldk >= 128 &&
+  return h->d == 128 && h->hi == 0 && key_dtype == TQ_BF16 && h->d_pi_frag && h->d_g_frag && h->symmetric && ldk >= 128 &&
          (ldk % 8) == 0 && a16(keys) && a16(codes) && a16(signs) && a16(norms) && a16(rnorms) &&
          h->code_bits >= 1 && h->code_bits <= 4;
 }

@@ -144,7 +144,7 @@ ScoreArgs make_args(const tq_ctx* h, const float* vw, int64_t groups, int64_t nq
 }  // namespace
 
 bool score_mfma_supported(const tq_ctx* h) {
-  if (h->code_bits < 1 || h->code_bits > 4) return false;
+  if (h->hi != 0 || h->code_bits < 1 || h->code_bits > 4) return false;
   return h->code_bits > 1 || h->symmetric;
 }
 

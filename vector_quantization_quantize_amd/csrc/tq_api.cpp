@@ -211,6 +211,15 @@ int finish_init(tq_ctx* h) {
     h->cb.t[i] = i + 1 < h->levels ? h->thresholds[i] : INFINITY;
   }
   h->cb.levels = h->levels;
+  if (h->hi > 0) {
+    const int lh = 2 * h->levels;
+    for (int i = 0; i < tqdev::kMaxLevels; ++i) {
+      h->cbh.c[i] = i < lh ? h->centroids_hi[i] : 0.0f;
+      h->cbh.t[i] = i + 1 < lh ? h->thresholds_hi[i] : INFINITY;
+    }
+    h->cbh.levels = lh;
+    h->hi_words = (h->hi + 31) / 32;
+  }
   plane_expansion(h->centroids, h->code_bits, &h->planes);
   dequant_table(h->centroids, &h->dqt);
   {
@@ -314,10 +323,11 @@ int tq_host_params(int32_t d, int32_t bits, uint64_t seed, float* pi, float* g, 
 enum { kRotHaar = 0, kRotExplicit = 1, kRotHadamard = 2 };
 
 static int init_common(int32_t d, int32_t bits, const float* pi_in, const float* g_in, uint64_t seed,
-                       tq_handle* out, int rotation = kRotHaar) {
+                       tq_handle* out, int rotation = kRotHaar, int32_t hi = 0) {
   if (!out) return TQ_EINVAL;
   *out = nullptr;
   if (d < 2 || d > 4096 || bits < 2 || bits > 5) return TQ_EINVAL;
+  if (hi < 0 || hi > d || (hi > 0 && bits > 4)) return TQ_EINVAL;
   tq_ctx* h = nullptr;
   try {
     h = new tq_ctx();
@@ -341,6 +351,14 @@ static int init_common(int32_t d, int32_t bits, const float* pi_in, const float*
     } else {
       rc = tqhost::build_params(d, bits, seed, h->pi.data(), h->g.data(), h->centroids.data(),
                                 h->thresholds.data());
+    }
+    if (rc == 0 && hi > 0) {
+      // the finer level set: the codebook of one more bit for the same d
+      h->hi = hi;
+      h->centroids_hi.resize(size_t(2) * levels);
+      h->thresholds_hi.resize(size_t(2) * levels - 1);
+      rc = tqhost::build_params(d, bits + 1, seed, nullptr, nullptr, h->centroids_hi.data(),
+                                h->thresholds_hi.data());
     }
     if (rc != 0) {
       delete h;
@@ -367,6 +385,10 @@ static int init_common(int32_t d, int32_t bits, const float* pi_in, const float*
 
 int tq_init(int32_t d, int32_t bits, uint64_t seed, tq_handle* out) {
   return init_common(d, bits, nullptr, nullptr, seed, out);
+}
+
+int tq_init_split(int32_t d, int32_t bits, int32_t hi, uint64_t seed, tq_handle* out) {
+  return init_common(d, bits, nullptr, nullptr, seed, out, kRotHaar, hi);
 }
 
 int tq_init_explicit(int32_t d, int32_t bits, const float* pi, const float* g, tq_handle* out) {
@@ -402,9 +424,11 @@ int tq_get_layout(tq_handle h, tq_layout* out) {
   out->levels = h->levels;
   out->words = h->words;
   out->format_version = TQ_FORMAT_VERSION;
-  out->code_bytes = int64_t(4) * h->code_bits * h->words;
+  out->code_bytes = int64_t(4) * (int64_t(h->code_bits) * h->words + h->hi_words);
   out->sign_bytes = int64_t(4) * h->words;
   out->key_bytes = out->code_bytes + out->sign_bytes + 8;
+  out->hi = h->hi;
+  out->hi_words = h->hi_words;
   return TQ_OK;
 }
 
@@ -421,6 +445,11 @@ uint64_t tq_params_hash(tq_handle h) {
   eat(h->pi);
   eat(h->g);
   eat(h->centroids);
+  eat(h->centroids_hi);
+  for (int i = 0; i < 4; ++i) {
+    x ^= uint64_t(h->hi >> (8 * i)) & 0xFFu;
+    x *= 0x100000001b3ull;
+  }
   return x;
 }
 
@@ -533,6 +562,7 @@ int tq_dense_logits(const float* queries, int64_t groups, int64_t nq, const void
 
 int tq_pack_values(tq_handle h, const uint32_t* codes, int64_t groups, int64_t n, uint32_t* vcodes, void* stream) {
   if (!h || groups < 0 || n < 0) return TQ_EINVAL;
+  if (h->hi != 0) return TQ_EUNSUPPORTED;  // stored values use one width
   if (groups == 0 || n == 0) return TQ_OK;
   if (!codes || !vcodes || !aligned4(codes) || (reinterpret_cast<uintptr_t>(vcodes) & 15u) != 0) return TQ_EINVAL;
   if (groups > 65535 || (n + 31) / 32 > 0x7FFFFFFF) return TQ_EUNSUPPORTED;
@@ -552,6 +582,7 @@ int tq_attention(tq_handle hk, tq_handle hv, const float* queries, int64_t group
                  void* workspace, size_t workspace_bytes, void* stream) {
   if (!hk || !hv || groups < 0 || nq < 0 || n < 0) return TQ_EINVAL;
   if (hk->d != hv->d || hk->device != hv->device || !std::isfinite(scale)) return TQ_EINVAL;
+  if (hv->hi != 0) return TQ_EUNSUPPORTED;  // stored values use one width
   if (groups == 0 || nq == 0) return TQ_OK;
   if (!out || !aligned4(out) || (lse && !aligned4(lse))) return TQ_EINVAL;
   if (groups * ((nq + 15) / 16) > 65535) return TQ_EUNSUPPORTED;
@@ -687,7 +718,7 @@ int tq_logits_topk(tq_handle h, const float* queries, int64_t groups, int64_t nq
   float* chunk = reinterpret_cast<float*>(ws + lay.chunk);
   const Scorer sc = pick_scorer(h, nq);
   const int64_t c = topk_chunk(h, nq, n);
-  const int64_t cw = int64_t(h->code_bits) * h->words;  // code words per key
+  const int64_t cw = int64_t(h->code_bits) * h->words + h->hi_words;  // code words per key
   for (int64_t g = 0; g < groups && e == hipSuccess; ++g) {
     const float* qg = queries + g * nq * h->d;
     float* og = top_scores + g * nq * k;

@@ -69,6 +69,12 @@ struct tq_ctx {
   uint16_t* d_dq_frag = nullptr;  // [word 4][step 8][piece 2][lane 64][8] f16 pieces of 2^12 Pi (B operand)
   uint16_t* d_ds_frag = nullptr;  // the same for 2^10 S, S = G Pi (corrected reconstruction)
   tqdev::Codebook cb{};
+  // fractional widths: rotated coordinates 0 .. hi-1 use cbh (2^(B+1)
+  // levels); their extra index bit is one more plane of hi_words words
+  // after the B full planes.  hi = hi_words = 0 for a plain handle.
+  int hi = 0, hi_words = 0;
+  std::vector<float> centroids_hi, thresholds_hi;
+  tqdev::Codebook cbh{};
   tqdev::PlaneExpansion planes{};
   bool symmetric = false;  // level set exactly symmetric in float32
   tqdev::HalfCodebook half{};
