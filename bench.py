@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-search", action="store_true", help="skip the search (top-k) measurement")
     ap.add_argument("--search-workload", default="search_b2")
+    ap.add_argument("--no-split", action="store_true",
+                    help="skip the fractional-width line (2.5 and 3.5 bits, general kernels)")
     ap.add_argument("--no-attention", action="store_true",
                     help="skip the decode-attention and uncompressed-logits measurement")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -253,6 +255,49 @@ def dequant_prod_leg(w, h, packed, out, stream, reps=10):
     return {"ms": round(ms, 3), "keys": w.total_keys, "TFLOPs": round(tfl, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_key": nbytes / w.total_keys}}
+
+
+def split_leg(w, keys, queries, scores, khat, seed, stream, reps=3):
+    """Fractional widths (tq_init_split) on the step's keys and queries: the
+    first d/2 rotated coordinates with one more index bit, 2.5 and 3.5 bits
+    per coordinate with the sign bit.  Per width: tq_quantize, tq_logits and
+    tq_dequant_mse (general float32 kernels: the matrix-core paths take one
+    width only), mean of `reps` calls after a warm-up, and the packed bytes
+    per key against the plain handles'."""
+    import torch
+
+    import vector_quantization_quantize_amd as tqm
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    res = {}
+    hi = w.d // 2
+    for bits in (2, 3):
+        h = tqm.tq_init_split(w.d, bits, hi, seed)
+        packed = tqm.empty_packed(h, w.total_keys)
+        lws = torch.empty(tqm.tq_logits_workspace_size(h, w.groups, w.nq) // 4 + 64, dtype=torch.float32,
+                          device="cuda")
+        t_q = timed(lambda: tqm.tq_quantize(h, keys, out=packed, stream=stream))
+        t_l = timed(lambda: tqm.tq_logits(h, queries, *packed, n=w.n, scores=scores, workspace=lws, stream=stream))
+        t_d = timed(lambda: tqm.tq_dequant_mse(h, packed[0], packed[2], khat=khat, stream=stream))
+        kb = h.layout.key_bytes
+        res[f"{bits + hi / w.d:g}_bits"] = {
+            "bits": bits, "hi": hi, "key_bytes": kb, "tq_quantize_ms": round(t_q, 3), "tq_logits_ms": round(t_l, 4),
+            "tq_dequant_mse_ms": round(t_d, 3),
+            "logits_GBps": round((kb * w.total_keys) / (t_l * 1e-3) / 1e9, 1),
+            "keys_scored_per_s": w.groups * w.nq * w.n / (t_l * 1e-3)}
+        del packed, lws
+        tqm.tq_destroy(h)
+    return res
 
 
 def decode_leg(seed, reps=50):
@@ -482,6 +527,8 @@ def main():
         line["attention"] = attention_leg(w, h, keys, queries, packed, args.seed, stream)
         line["decode_step"] = decode_leg(args.seed)
         line["dequant_prod"] = dequant_prod_leg(w, h, packed, khat, stream)
+    if not args.no_split:
+        line["fractional_widths"] = split_leg(w, keys, queries, scores, khat, args.seed, stream)
     if not args.no_search:
         del keys, queries, packed, scores, ws, khat
         torch.cuda.empty_cache()
