@@ -338,3 +338,34 @@ def test_attention_rejects_bad_arguments(env):
     assert lib.tq_dense_logits(p(q), 1, 4, p(buf), 7, 64, 128, 128, p(out), None) == tqm.TQ_EINVAL
     assert lib.tq_dense_logits(p(q), 1, 4, p(buf), 0, 64, 128, 64, p(out), None) == tqm.TQ_EINVAL
     torch.cuda.synchronize()
+
+
+def test_dequant_prod_long_context_full_size(env):
+    """The corrected reconstruction over the whole long-context cache (32 x
+    131072 bf16 keys, d = 128, 3 bits) in the configuration the bench times,
+    quantized by the library; 4096 sampled keys plus the last one against
+    the oracle's reconstruction of the library's own packed keys (decode
+    parity), to the reconstruction bar."""
+    torch, tqm = env
+    from vector_quantization_quantize_amd import workloads as wl
+    w = wl.WORKLOADS["long_context"]
+    _announce(f"dequant_prod full size {w.name} keys={w.total_keys}")
+    pr = _params(w.d, w.bits, 0)
+    h = tqm.tq_init(w.d, w.bits, 0)
+    kd = _dev(torch, wl.keys(w), torch.bfloat16)
+    codes, signs, norms, rnorms = tqm.tq_quantize(h, kd)
+    del kd
+    out = tqm.tq_dequant_prod(h, codes, signs, norms, rnorms)
+    torch.cuda.synchronize()
+    rs = np.random.default_rng(77)
+    pick = np.unique(np.concatenate([rs.integers(0, w.total_keys, 4096), [w.total_keys - 1]]))
+    sel = torch.from_numpy(pick).cuda()
+    c = _cpu(codes[sel]).view(np.uint32)
+    sg = _cpu(signs[sel]).view(np.uint32)
+    nk = _cpu(norms[sel]).astype(np.float64)
+    rk = _cpu(rnorms[sel]).astype(np.float64)
+    got = _cpu(out[sel]).astype(np.float64)
+    ref = tq.dequant_prod(pr, tq.unpack_codes(c, w.d), tq.unpack_bits(sg, w.d), nk, rk)
+    err = np.sqrt(((got - ref) ** 2).sum(axis=1))
+    size = np.sqrt((ref ** 2).sum(axis=1))
+    assert np.all(err <= 1e-5 * size + 1e-30), float((err / np.maximum(size, 1e-30)).max())

@@ -201,7 +201,10 @@ logits_ref_kernel(const float* __restrict__ vw, int64_t nq, int d, int code_bits
   extern __shared__ float smem[];
   float* lvl = smem;
   float* lvlh = smem + kMaxLevels;    // the finer set (coordinates below hi)
-  float* qv = smem + 2 * kMaxLevels;  // [4][d] v then [4][d] w
+  // [d][8]: coordinate j's v for the 4 queries, then its w for them, so
+  // that two 16-byte reads (the same address in every lane) serve all 8
+  // products of one coordinate
+  float* qv = smem + 2 * kMaxLevels;
   const int64_t g = blockIdx.y;
   const int64_t t = int64_t(blockIdx.x) * kThreads + threadIdx.x;
   const int64_t key = g * n + t;
@@ -222,28 +225,46 @@ logits_ref_kernel(const float* __restrict__ vw, int64_t nq, int d, int code_bits
     for (int p = threadIdx.x; p < 4 * d; p += kThreads) {
       const int q = p / d, j = p - q * d;
       const float* src = vw + (g * nq + q0 + (q < qc ? q : 0)) * stride;
-      qv[q * d + j] = q < qc ? src[j] : 0.f;
-      qv[4 * d + q * d + j] = q < qc ? src[half + j] : 0.f;
+      qv[8 * j + q] = q < qc ? src[j] : 0.f;
+      qv[8 * j + 4 + q] = q < qc ? src[half + j] : 0.f;
     }
     __syncthreads();
     if (t >= n) continue;
     float a1[4] = {0.f, 0.f, 0.f, 0.f}, a2[4] = {0.f, 0.f, 0.f, 0.f};
     for (int w = 0; w < words; ++w) {
+      // planes past the key's own (at most 5) stay 0 and add nothing to the
+      // index, so every plane loop below has a fixed trip count
       uint32_t plane[5] = {0u, 0u, 0u, 0u, 0u};
-      for (int q = 0; q < code_bits; ++q) plane[q] = codes[key * cw + int64_t(q) * words + w];
-      if (w < hi_words) plane[code_bits] = codes[key * cw + int64_t(code_bits) * words + w];
+#pragma unroll
+      for (int q = 0; q < 5; ++q)
+        if (q < code_bits) plane[q] = codes[key * cw + int64_t(q) * words + w];
+#pragma unroll
+      for (int q = 1; q < 5; ++q)
+        if (q == code_bits && w < hi_words) plane[q] = codes[key * cw + int64_t(q) * words + w];
       const uint32_t sw = signs[key * words + w];
-      for (int b = 0; b < 32; ++b) {
+      auto step = [&](int b) {
         const int j = 32 * w + b;
-        if (j >= d) break;
         int idx = 0;
-        for (int q = 0; q <= code_bits; ++q) idx |= int((plane[q] >> b) & 1u) << q;
+#pragma unroll
+        for (int q = 0; q < 5; ++q) idx |= int((plane[q] >> b) & 1u) << q;
         const float cv = j < hi ? lvlh[idx] : lvl[idx];
         const float sg = ((sw >> b) & 1u) ? 1.0f : -1.0f;
-        for (int q = 0; q < 4; ++q) {
-          a1[q] = fmaf(qv[q * d + j], cv, a1[q]);
-          a2[q] = fmaf(qv[4 * d + q * d + j], sg, a2[q]);
-        }
+        const float4 vv = *reinterpret_cast<const float4*>(qv + 8 * j);
+        const float4 ww = *reinterpret_cast<const float4*>(qv + 8 * j + 4);
+        a1[0] = fmaf(vv.x, cv, a1[0]);
+        a1[1] = fmaf(vv.y, cv, a1[1]);
+        a1[2] = fmaf(vv.z, cv, a1[2]);
+        a1[3] = fmaf(vv.w, cv, a1[3]);
+        a2[0] = fmaf(ww.x, sg, a2[0]);
+        a2[1] = fmaf(ww.y, sg, a2[1]);
+        a2[2] = fmaf(ww.z, sg, a2[2]);
+        a2[3] = fmaf(ww.w, sg, a2[3]);
+      };
+      if (32 * w + 32 <= d) {
+#pragma unroll
+        for (int b = 0; b < 32; ++b) step(b);
+      } else {
+        for (int b = 0; b < d - 32 * w; ++b) step(b);
       }
     }
     const float corr = rho * kappa;
