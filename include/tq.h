@@ -127,7 +127,8 @@ TQ_API int tq_init(int32_t d, int32_t bits, uint64_t seed, tq_handle* out);
  * padding 0); tq_layout gives code_bytes.  2 <= bits <= 4, 0 <= hi <= d
  * (hi = 0 is tq_init).  tq_quantize, tq_logits, tq_logits_topk,
  * tq_dequant_mse, tq_dequant_prod and the key side of tq_attention take such
- * handles (general kernels); tq_pack_values and the value side of
+ * handles (general kernels; the two reconstructions run on the matrix cores
+ * when d = 128 and hi = 64); tq_pack_values and the value side of
  * tq_attention return TQ_EUNSUPPORTED. */
 TQ_API int tq_init_split(int32_t d, int32_t bits, int32_t hi, uint64_t seed, tq_handle* out);
 

@@ -49,8 +49,11 @@ def _keys(rs, n, d):
 
 # (d, bits, hi, groups, n, nq): 2.5 and 3.5 bits at d = 128, ragged hi
 # (one partial extra word, several words, hi = d), tiny and wide d
-CASES = [(128, 2, 64, 1, 300, 4), (128, 3, 64, 2, 257, 3), (40, 2, 16, 1, 77, 5), (33, 3, 33, 2, 65, 2),
-         (200, 4, 100, 1, 50, 6), (128, 4, 1, 1, 129, 2), (2, 2, 1, 1, 9, 1), (300, 2, 257, 1, 40, 3)]
+# d = 128 with hi = 64 also takes the matrix-core reconstruction (ragged
+# tile counts: 300, 257, 4097 keys)
+CASES = [(128, 2, 64, 1, 300, 4), (128, 3, 64, 2, 257, 3), (128, 4, 64, 1, 4097, 2), (40, 2, 16, 1, 77, 5),
+         (33, 3, 33, 2, 65, 2), (200, 4, 100, 1, 50, 6), (128, 4, 1, 1, 129, 2), (2, 2, 1, 1, 9, 1),
+         (300, 2, 257, 1, 40, 3)]
 
 
 @pytest.mark.parametrize("d,bits,hi,groups,n,nq", CASES)

@@ -140,19 +140,33 @@ __device__ __forceinline__ void load_a(const uint32_t* tab, const uint32_t (&wp)
 // bits expanded to +-1 (exact in float16; a set bit stages as -1) against
 // two float16 pieces of 2^10 S, into a second accumulator scaled per key by
 // -n rho kappa 2^-10.
-template <int B, bool kTwo, bool kProd>
+//
+// kSplit (fractional widths, the first 64 of the 128 rotated coordinates one
+// bit wider): a key's codes are the B planes (4 words each) and then one
+// plane of 2 words for coordinates 0..63, 8-byte aligned per key.  Steps
+// 0..3 (coordinates 0..63) look their values up in a second table of B + 1
+// bits built from the finer level set; both tables hold the three-pass
+// pieces of 2^12 c, so one accumulator and one output scale serve both.
+template <int B, bool kTwo, bool kProd, bool kSplit = false>
 __global__ void __launch_bounds__(kDqThreads, 2)
 dequant_mfma128_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ norms, int64_t n,
                        const uint4* __restrict__ pi_frag, Codebook cb, DequantTable dqt, float* __restrict__ khat,
                        int64_t tiles, int64_t stride, int64_t bound1, int64_t bound2,
                        const uint32_t* __restrict__ signs, const float* __restrict__ rnorms,
-                       const uint4* __restrict__ s_frag, float kappa) {
+                       const uint4* __restrict__ s_frag, float kappa, Codebook cbh) {
+  static_assert(!kSplit || (!kTwo && B <= 3), "fractional widths use the three-pass tables, B + 1 <= 4");
   using L = Lookup<B, kTwo>;
+  using LH = Lookup<kSplit ? B + 1 : B, false>;
+  constexpr int kFineSteps = kSplit ? 4 : 0;         // steps of coordinates 0..63
+  constexpr int64_t kCw = 4 * B + (kSplit ? 2 : 0);  // code words per key
   __shared__ uint4 tab4[L::kEntries * L::kDwords / 4];
+  __shared__ uint4 tabh4[kSplit ? LH::kEntries * LH::kDwords / 4 : 1];
   __shared__ float4 nrow[4][8];  // per wave: the tile's 32 norms
   __shared__ float4 crow[4][kProd ? 8 : 1];  // per wave: the tile's correction factors
   uint32_t* tab = reinterpret_cast<uint32_t*>(tab4);
+  uint32_t* tabh = reinterpret_cast<uint32_t*>(tabh4);
   build_table<B, kTwo>(tab, cb, dqt);
+  if constexpr (kSplit) build_table<B + 1, false>(tabh, cbh, dqt);
   const float out_scale = kTwo ? dqt.out_scale : kOutScale;
   __syncthreads();
 
@@ -178,11 +192,22 @@ dequant_mfma128_kernel(const uint32_t* __restrict__ codes, const float* __restri
   // packed codes and norm (and, for kProd, signs and rho) of this lane's key
   // (clamped to n - 1), one tile ahead; a fetch past the last tile also
   // reads key n - 1 and is unused
-  auto fetch = [&](int64_t tile, uint4 (&v)[B], float& nv, uint4& sv, float& rv) {
+  auto fetch = [&](int64_t tile, uint4 (&v)[B], float& nv, uint4& sv, float& rv, uint2& xv) {
     int64_t key = tile * 32 + kl;
     key = key < n ? key : n - 1;
+    if constexpr (kSplit) {
+      // 8-byte aligned rows: two 8-byte loads per plane, then the extra plane
 #pragma unroll
-    for (int p = 0; p < B; ++p) v[p] = *reinterpret_cast<const uint4*>(codes + (key * B + p) * 4);
+      for (int p = 0; p < B; ++p) {
+        const uint2 a = *reinterpret_cast<const uint2*>(codes + key * kCw + 4 * p);
+        const uint2 b = *reinterpret_cast<const uint2*>(codes + key * kCw + 4 * p + 2);
+        v[p] = make_uint4(a.x, a.y, b.x, b.y);
+      }
+      xv = *reinterpret_cast<const uint2*>(codes + key * kCw + 4 * B);
+    } else {
+#pragma unroll
+      for (int p = 0; p < B; ++p) v[p] = *reinterpret_cast<const uint4*>(codes + (key * B + p) * 4);
+    }
     nv = norms[key];
     if constexpr (kProd) {
       sv = *reinterpret_cast<const uint4*>(signs + key * 4);
@@ -197,8 +222,9 @@ dequant_mfma128_kernel(const uint32_t* __restrict__ codes, const float* __restri
   const int64_t tbeg = tier == 0 ? 0 : tier == 1 ? bound1 : bound2;
   const int64_t tend = tier == 0 ? bound1 : tier == 1 ? bound2 : tiles;
   uint4 nxt[B], nxt_s = make_uint4(0u, 0u, 0u, 0u);
+  uint2 nxt_x = make_uint2(0u, 0u);
   float nxt_n, nxt_r = 0.0f;
-  fetch(tbeg + bid % stride, nxt, nxt_n, nxt_s, nxt_r);
+  fetch(tbeg + bid % stride, nxt, nxt_n, nxt_s, nxt_r, nxt_x);
   for (int64_t tile = tbeg + bid % stride; tile < tend; tile += stride) {
     uint32_t pl[B][4];
 #pragma unroll
@@ -209,16 +235,28 @@ dequant_mfma128_kernel(const uint32_t* __restrict__ codes, const float* __restri
       pl[p][3] = nxt[p].w;
     }
     const uint32_t sw[4] = {nxt_s.x, nxt_s.y, nxt_s.z, nxt_s.w};
+    const uint32_t xw[2] = {nxt_x.x, nxt_x.y};
     const float nk = nxt_n, rk = nxt_r;
-    fetch(tile + stride, nxt, nxt_n, nxt_s, nxt_r);
+    fetch(tile + stride, nxt, nxt_n, nxt_s, nxt_r, nxt_x);
     f32x16 acc = {}, acc2 = {};
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      uint32_t wp[B];
-#pragma unroll
-      for (int p = 0; p < B; ++p) wp[p] = pl[p][s >> 1];
       f16x8 ahi, alo;
-      load_a<B, kTwo>(tab, wp, 8 * (2 * (s & 1) + g), ahi, alo);
+      if (s < kFineSteps) {
+        // coordinates 16 s .. 16 s + 15 < 64: B planes plus the extra one
+        uint32_t wp[kSplit ? B + 1 : B];
+#pragma unroll
+        for (int p = 0; p < B; ++p) wp[p] = pl[p][s >> 1];
+        if constexpr (kSplit) {
+          wp[B] = xw[(s >> 1) & 1];
+          load_a<kSplit ? B + 1 : B, false>(tabh, wp, 8 * (2 * (s & 1) + g), ahi, alo);
+        }
+      } else {
+        uint32_t wp[B];
+#pragma unroll
+        for (int p = 0; p < B; ++p) wp[p] = pl[p][s >> 1];
+        load_a<B, kTwo>(tab, wp, 8 * (2 * (s & 1) + g), ahi, alo);
+      }
       acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, bpi[s][0], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, bpi[s][1], acc, 0, 0, 0);
       if constexpr (!kTwo) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, bpi[s][0], acc, 0, 0, 0);
@@ -269,7 +307,7 @@ dequant_mfma128_kernel(const uint32_t* __restrict__ codes, const float* __restri
 constexpr double kTierShare[4][3] = {
     {0.385, 0.33, 0.285}, {0.385, 0.33, 0.285}, {0.55, 0.45, 0.0}, {0.42, 0.33, 0.25}};
 
-template <int B, bool kTwo, bool kProd = false>
+template <int B, bool kTwo, bool kProd = false, bool kSplit = false>
 hipError_t launch_b(const tq_ctx* h, const uint32_t* codes, const float* norms, int64_t n, float* khat,
                     hipStream_t stream, const uint32_t* signs = nullptr, const float* rnorms = nullptr) {
   const int64_t tiles = (n + 31) / 32;
@@ -280,7 +318,7 @@ hipError_t launch_b(const tq_ctx* h, const uint32_t* codes, const float* norms, 
   // tile range sized by kTierShare, so that the tiers finish together.  The
   // split only moves work between blocks; any dispatch order gives the same
   // results.
-  constexpr int R = (B == 3 || kProd) ? 2 : 3;
+  constexpr int R = (B == 3 || kProd || kSplit) ? 2 : 3;
   const int64_t cus = h->cus;
   int64_t blocks, stride, bound1, bound2;
   if (tiles >= 4 * R * cus) {
@@ -298,22 +336,37 @@ hipError_t launch_b(const tq_ctx* h, const uint32_t* codes, const float* norms, 
     stride = blocks;
     bound1 = bound2 = tiles;
   }
-  const auto kernel = dequant_mfma128_kernel<B, kTwo, kProd>;
+  const auto kernel = dequant_mfma128_kernel<B, kTwo, kProd, kSplit>;
   const float kappa = float(1.2533141373155002512 / 128.0);  // sqrt(pi/2) / d
   hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kDqThreads), 0, stream, codes, norms, n,
                      reinterpret_cast<const uint4*>(h->d_dq_frag), h->cb, h->dqt, khat, tiles, stride, bound1,
-                     bound2, signs, rnorms, reinterpret_cast<const uint4*>(h->d_ds_frag), kappa);
+                     bound2, signs, rnorms, reinterpret_cast<const uint4*>(h->d_ds_frag), kappa, h->cbh);
   return hipGetLastError();
+}
+
+// fractional widths with the first 64 coordinates one bit wider (B <= 3)
+template <bool kProd>
+hipError_t launch_split(const tq_ctx* h, const uint32_t* codes, const float* norms, int64_t n, float* out,
+                        hipStream_t stream, const uint32_t* signs, const float* rnorms) {
+  switch (h->code_bits) {
+    case 1: return launch_b<1, false, kProd, true>(h, codes, norms, n, out, stream, signs, rnorms);
+    case 2: return launch_b<2, false, kProd, true>(h, codes, norms, n, out, stream, signs, rnorms);
+    case 3: return launch_b<3, false, kProd, true>(h, codes, norms, n, out, stream, signs, rnorms);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
 bool dequant_mfma128_supported(const tq_ctx* h) {
-  return h->d == 128 && h->hi == 0 && h->d_dq_frag && h->code_bits >= 1 && h->code_bits <= 4;
+  if (h->d != 128 || !h->d_dq_frag || h->code_bits < 1) return false;
+  return h->hi == 0 ? h->code_bits <= 4 : (h->hi == 64 && h->code_bits <= 3);
 }
 
 hipError_t launch_dequant_mfma128(const tq_ctx* h, const uint32_t* codes, const float* norms, int64_t n,
                                   float* khat, hipStream_t stream) {
+  if (h->hi == 64) return launch_split<false>(h, codes, norms, n, khat, stream, nullptr, nullptr);
+  if (h->hi != 0) return hipErrorInvalidValue;
   const bool two = h->dqt.two_pass != 0;
   switch (h->code_bits) {
     case 1:
@@ -331,6 +384,8 @@ hipError_t launch_dequant_mfma128(const tq_ctx* h, const uint32_t* codes, const 
 hipError_t launch_dequant_prod_mfma128(const tq_ctx* h, const uint32_t* codes, const uint32_t* signs,
                                        const float* norms, const float* rnorms, int64_t n, float* out,
                                        hipStream_t stream) {
+  if (h->hi == 64) return launch_split<true>(h, codes, norms, n, out, stream, signs, rnorms);
+  if (h->hi != 0) return hipErrorInvalidValue;
   const bool two = h->dqt.two_pass != 0;
   switch (h->code_bits) {
     case 1:
