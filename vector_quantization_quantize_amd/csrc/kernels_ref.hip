@@ -26,19 +26,59 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ float load_key(const void* keys, int key_dtype, int64_t off) {
-  if (key_dtype == TQ_BF16) {
-    const uint16_t b = static_cast<const uint16_t*>(keys)[off];
-    return __uint_as_float(uint32_t(b) << 16);
-  }
-  return static_cast<const float*>(keys)[off];
-}
-
 // idx = #{ i : t_i <= z }  (a tie goes to the upper cell)
 __device__ __forceinline__ int bucket(float z, const float* t, int levels) {
   int idx = 0;
   for (int i = 0; i + 1 < levels; ++i) idx += (t[i] <= z) ? 1 : 0;
   return idx;
+}
+
+// Register block of a matrix product over an LDS tile: for the 4 rows
+// x_r = x + r ds (r < 4) and the output columns j0 .. j0+3 (those below d),
+//   a[r][c] = sum_i m[i d + j0 + c] x_r[i],  i ascending, one fma per term.
+// Four columns per thread cut the loads per fma from 5/4 to 1/2 (1/4 with
+// 16-byte loads when d is a multiple of 4).
+// The loop is unrolled by 8 with no branch in its body, so that the matrix
+// loads of 8 rows (L2 hits, but hundreds of cycles each) are in flight
+// together; columns past d read column d - 1 and are never stored.
+template <bool kVec>
+__device__ __forceinline__ void product4x4_body(const float* __restrict__ m, int d, const float* x, int ds, int j0,
+                                                float (&a)[4][4]) {
+  int jc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) jc[c] = j0 + c < d ? j0 + c : d - 1;
+#pragma unroll 8
+  for (int i = 0; i < d; ++i) {
+    const float* row = m + size_t(i) * d;
+    float w[4];
+    if constexpr (kVec) {
+      const float4 v = *reinterpret_cast<const float4*>(row + j0);
+      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) w[c] = row[jc[c]];
+    }
+    const float x0 = x[i], x1 = x[ds + i], x2 = x[2 * ds + i], x3 = x[3 * ds + i];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      a[0][c] = fmaf(w[c], x0, a[0][c]);
+      a[1][c] = fmaf(w[c], x1, a[1][c]);
+      a[2][c] = fmaf(w[c], x2, a[2][c]);
+      a[3][c] = fmaf(w[c], x3, a[3][c]);
+    }
+  }
+}
+
+__device__ __forceinline__ void product4x4(const float* __restrict__ m, int d, const float* x, int ds, int j0,
+                                           float (&a)[4][4]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) a[r][c] = 0.0f;
+  if ((d & 3) == 0)
+    product4x4_body<true>(m, d, x, ds, j0, a);
+  else
+    product4x4_body<false>(m, d, x, ds, j0, a);
 }
 
 // ---------------------------------------------------------------------------
@@ -68,12 +108,21 @@ quantize_ref_kernel(const void* __restrict__ keys, int key_dtype, int64_t n, int
     lvlh[tid] = cbh.c[tid];
     thrh[tid] = cbh.t[tid];
   }
-  // keys -> buf0 (fp32)
-  for (int p = tid; p < tk * d; p += kThreads) {
-    const int k = p / d, i = p - k * d;
-    const int64_t key = base + k;
-    buf0[k * ds + i] = key < n ? load_key(keys, key_dtype, key * ldk + i) : 0.0f;
-  }
+  // keys -> buf0 (fp32): one loop per key type, loads from clamped rows and
+  // no branch in the body, so the unrolled loads are all in flight at once
+  auto stage = [&](auto load) {
+#pragma unroll 8
+    for (int p = tid; p < tk * d; p += kThreads) {
+      const int k = p / d, i = p - k * d;
+      const int64_t key = base + k;
+      const float v = load((key < n ? key : n - 1) * ldk + i);
+      buf0[k * ds + i] = key < n ? v : 0.0f;
+    }
+  };
+  if (key_dtype == TQ_BF16)
+    stage([&](int64_t off) { return __uint_as_float(uint32_t(static_cast<const uint16_t*>(keys)[off]) << 16); });
+  else
+    stage([&](int64_t off) { return static_cast<const float*>(keys)[off]; });
   __syncthreads();
   // norms
   for (int k = tid; k < tk; k += kThreads) {
@@ -84,23 +133,17 @@ quantize_ref_kernel(const void* __restrict__ keys, int key_dtype, int64_t n, int
     if (base + k < n) norms[base + k] = nk;
   }
   __syncthreads();
-  // z = (Pi k) / n, four keys per thread per output coordinate
-  const int groups = tk / 4;
-  for (int p = tid; p < groups * d; p += kThreads) {
-    const int kg = p / d, j = p - kg * d;
-    const float* k0 = buf0 + (4 * kg) * ds;
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    for (int i = 0; i < d; ++i) {
-      const float w = piT[size_t(i) * d + j];
-      a0 = fmaf(w, k0[i], a0);
-      a1 = fmaf(w, k0[ds + i], a1);
-      a2 = fmaf(w, k0[2 * ds + i], a2);
-      a3 = fmaf(w, k0[3 * ds + i], a3);
-    }
-    const float acc[4] = {a0, a1, a2, a3};
+  // z = (Pi k) / n, four keys x four output coordinates per thread
+  const int groups = tk / 4, quads = (d + 3) / 4;
+  for (int p = tid; p < groups * quads; p += kThreads) {
+    const int kg = p / quads, j0 = 4 * (p - kg * quads);
+    float a[4][4];
+    product4x4(piT, d, buf0 + (4 * kg) * ds, ds, j0, a);
     for (int r = 0; r < 4; ++r) {
       const float nk = nrm[4 * kg + r];
-      buf1[(4 * kg + r) * ds + j] = nk > 0.0f ? acc[r] / nk : 0.0f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (j0 + c < d) buf1[(4 * kg + r) * ds + j0 + c] = nk > 0.0f ? a[r][c] / nk : 0.0f;
     }
   }
   __syncthreads();
@@ -130,21 +173,14 @@ quantize_ref_kernel(const void* __restrict__ keys, int key_dtype, int64_t n, int
     if (base + k < n) rnorms[base + k] = sqrtf(s);
   }
   // p = G r -> buf0
-  for (int p = tid; p < groups * d; p += kThreads) {
-    const int kg = p / d, j = p - kg * d;
-    const float* r0 = buf1 + (4 * kg) * ds;
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    for (int i = 0; i < d; ++i) {
-      const float w = gT[size_t(i) * d + j];
-      a0 = fmaf(w, r0[i], a0);
-      a1 = fmaf(w, r0[ds + i], a1);
-      a2 = fmaf(w, r0[2 * ds + i], a2);
-      a3 = fmaf(w, r0[3 * ds + i], a3);
-    }
-    buf0[(4 * kg) * ds + j] = a0;
-    buf0[(4 * kg + 1) * ds + j] = a1;
-    buf0[(4 * kg + 2) * ds + j] = a2;
-    buf0[(4 * kg + 3) * ds + j] = a3;
+  for (int p = tid; p < groups * quads; p += kThreads) {
+    const int kg = p / quads, j0 = 4 * (p - kg * quads);
+    float a[4][4];
+    product4x4(gT, d, buf1 + (4 * kg) * ds, ds, j0, a);
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (j0 + c < d) buf0[(4 * kg + r) * ds + j0 + c] = a[r][c];
   }
   __syncthreads();
   for (int p = tid; p < tk * words; p += kThreads) {
@@ -310,22 +346,19 @@ dequant_ref_kernel(const uint32_t* __restrict__ codes, const float* __restrict__
     }
   }
   __syncthreads();
-  const int groups = tk / 4;
-  for (int p = tid; p < groups * d; p += kThreads) {
-    const int kg = p / d, j = p - kg * d;
-    const float* c0 = ch + (4 * kg) * ds;
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    for (int i = 0; i < d; ++i) {
-      const float w = pi[size_t(i) * d + j];  // (Pi^T c)_j = sum_i Pi[i][j] c_i
-      a0 = fmaf(w, c0[i], a0);
-      a1 = fmaf(w, c0[ds + i], a1);
-      a2 = fmaf(w, c0[2 * ds + i], a2);
-      a3 = fmaf(w, c0[3 * ds + i], a3);
-    }
-    const float acc[4] = {a0, a1, a2, a3};
+  // (Pi^T c)_j = sum_i Pi[i][j] c_i
+  const int groups = tk / 4, quads = (d + 3) / 4;
+  for (int p = tid; p < groups * quads; p += kThreads) {
+    const int kg = p / quads, j0 = 4 * (p - kg * quads);
+    float a[4][4];
+    product4x4(pi, d, ch + (4 * kg) * ds, ds, j0, a);
     for (int r = 0; r < 4; ++r) {
       const int64_t key = base + 4 * kg + r;
-      if (key < n) khat[key * d + j] = norms[key] * acc[r];
+      if (key >= n) continue;
+      const float nk = norms[key];
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (j0 + c < d) khat[key * d + j0 + c] = nk * a[r][c];
     }
   }
 }
@@ -376,42 +409,33 @@ dequant_prod_ref_kernel(const uint32_t* __restrict__ codes, const uint32_t* __re
     }
   }
   __syncthreads();
-  const int groups = tk / 4;
+  const int groups = tk / 4, quads = (d + 3) / 4;
   // (G^T s)_i = sum_j G[j][i] s_j; each (key, i) of t is written by one thread
-  for (int p = tid; p < groups * d; p += kThreads) {
-    const int kg = p / d, i = p - kg * d;
-    const float* s0 = sg + (4 * kg) * ds;
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    for (int j = 0; j < d; ++j) {
-      const float w = g[size_t(j) * d + i];
-      a0 = fmaf(w, s0[j], a0);
-      a1 = fmaf(w, s0[ds + j], a1);
-      a2 = fmaf(w, s0[2 * ds + j], a2);
-      a3 = fmaf(w, s0[3 * ds + j], a3);
-    }
-    const float acc[4] = {a0, a1, a2, a3};
+  for (int p = tid; p < groups * quads; p += kThreads) {
+    const int kg = p / quads, i0 = 4 * (p - kg * quads);
+    float a[4][4];
+    product4x4(g, d, sg + (4 * kg) * ds, ds, i0, a);
     for (int r = 0; r < 4; ++r) {
       const int64_t key = base + 4 * kg + r;
-      const float rho = key < n ? rnorms[key] : 0.0f;
-      t[(4 * kg + r) * ds + i] = fmaf(rho * kappa, acc[r], t[(4 * kg + r) * ds + i]);
+      const float rk = (key < n ? rnorms[key] : 0.0f) * kappa;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (i0 + c < d) t[(4 * kg + r) * ds + i0 + c] = fmaf(rk, a[r][c], t[(4 * kg + r) * ds + i0 + c]);
     }
   }
   __syncthreads();
-  for (int p = tid; p < groups * d; p += kThreads) {
-    const int kg = p / d, j = p - kg * d;
-    const float* c0 = t + (4 * kg) * ds;
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    for (int i = 0; i < d; ++i) {
-      const float w = pi[size_t(i) * d + j];  // (Pi^T t)_j = sum_i Pi[i][j] t_i
-      a0 = fmaf(w, c0[i], a0);
-      a1 = fmaf(w, c0[ds + i], a1);
-      a2 = fmaf(w, c0[2 * ds + i], a2);
-      a3 = fmaf(w, c0[3 * ds + i], a3);
-    }
-    const float acc[4] = {a0, a1, a2, a3};
+  // (Pi^T t)_j = sum_i Pi[i][j] t_i
+  for (int p = tid; p < groups * quads; p += kThreads) {
+    const int kg = p / quads, j0 = 4 * (p - kg * quads);
+    float a[4][4];
+    product4x4(pi, d, t + (4 * kg) * ds, ds, j0, a);
     for (int r = 0; r < 4; ++r) {
       const int64_t key = base + 4 * kg + r;
-      if (key < n) out[key * d + j] = norms[key] * acc[r];
+      if (key >= n) continue;
+      const float nk = norms[key];
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (j0 + c < d) out[key * d + j0 + c] = nk * a[r][c];
     }
   }
 }

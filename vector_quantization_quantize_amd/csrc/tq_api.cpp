@@ -262,6 +262,13 @@ int check_device(const tq_ctx* h) {
 
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
+// The matrix-core reconstruction reads a key's code row with 16-byte loads
+// (8-byte loads for fractional widths); other addresses take the general
+// kernel.
+bool dequant_rows_aligned(const tq_ctx* h, const void* codes) {
+  return (reinterpret_cast<uintptr_t>(codes) & (h->hi ? 7u : 15u)) == 0;
+}
+
 }  // namespace
 
 namespace {
@@ -541,7 +548,8 @@ int tq_dequant_prod(tq_handle h, const uint32_t* codes, const uint32_t* signs, c
   if (n > int64_t(0x7FFFFFFF) * 4) return TQ_EUNSUPPORTED;
   if (check_device(h) != TQ_OK) return TQ_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = (!tqdev::force_reference_kernels() && tqdev::dequant_mfma128_supported(h) && h->d_ds_frag)
+  const hipError_t e = (!tqdev::force_reference_kernels() && tqdev::dequant_mfma128_supported(h) && h->d_ds_frag &&
+                        dequant_rows_aligned(h, codes) && (reinterpret_cast<uintptr_t>(signs) & 15u) == 0)
                            ? tqdev::launch_dequant_prod_mfma128(h, codes, signs, norms, rnorms, n, ktilde, s)
                            : tqdev::launch_dequant_prod_v1(h, codes, signs, norms, rnorms, n, ktilde, s);
   return e == hipSuccess ? TQ_OK : TQ_EHIP;
@@ -757,7 +765,8 @@ int tq_dequant_mse(tq_handle h, const uint32_t* codes, const float* norms, int64
   if (!codes || !norms || !khat) return TQ_EINVAL;
   if (check_device(h) != TQ_OK) return TQ_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = (!tqdev::force_reference_kernels() && tqdev::dequant_mfma128_supported(h))
+  const hipError_t e = (!tqdev::force_reference_kernels() && tqdev::dequant_mfma128_supported(h) &&
+                        dequant_rows_aligned(h, codes))
                            ? tqdev::launch_dequant_mfma128(h, codes, norms, n, khat, s)
                            : tqdev::launch_dequant_v1(h, codes, norms, n, khat, s);
   return e == hipSuccess ? TQ_OK : TQ_EHIP;
