@@ -91,15 +91,20 @@ __device__ __forceinline__ int value_slot(int c, int o, int W, int B) {
 // collects bit j of each half.  Phase 2: thread per (coordinate, token
 // octet) interleaves the planes' bytes into X and writes its B bytes.
 // Dynamic LDS: B * 32 W words.
+// B is a template argument so that the interleave below unrolls with
+// constant shifts; the block's 128 B W output bytes are assembled in LDS and
+// leave with 16-byte stores (the block is 16-byte aligned: the caller's
+// buffer is, and 128 B W is a multiple of 16).
+template <int B>
 __global__ void __launch_bounds__(kThreads)
-pack_values_kernel(const uint32_t* __restrict__ codes, int64_t n, int B, int W, int64_t nb,
-                   uint32_t* __restrict__ vcodes) {
-  extern __shared__ uint32_t tw[];  // [B][32 W]
+pack_values_kernel(const uint32_t* __restrict__ codes, int64_t n, int W, int64_t nb, uint32_t* __restrict__ vcodes) {
+  extern __shared__ uint32_t tw[];  // [B][32 W] transposed planes, then [B][32 W] output staging
+  uint8_t* stage = reinterpret_cast<uint8_t*>(tw + B * 32 * W);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t blk = blockIdx.x, grp = blockIdx.y;
   const int pws = B * W;  // words per token in the key layout
   codes += grp * n * pws;
-  uint8_t* out = reinterpret_cast<uint8_t*>(vcodes + (grp * nb + blk) * int64_t(pws) * 32);
+  uint4* out = reinterpret_cast<uint4*>(vcodes + (grp * nb + blk) * int64_t(pws) * 32);
   const int64_t tok = blk * 32 + (lane & 31);
   for (int pw = 2 * wave; pw < pws; pw += 2 * kWaves) {
     const int mine = pw + (lane >> 5);
@@ -117,17 +122,23 @@ pack_values_kernel(const uint32_t* __restrict__ codes, int64_t n, int B, int W, 
     }
   }
   __syncthreads();
-  const int E = value_e(B);
+  constexpr int E = value_e(B);
   for (int i = threadIdx.x; i < 4 * 32 * W; i += kThreads) {
     const int c = i >> 2, o = i & 3;
     uint32_t x = 0;
+#pragma unroll
     for (int p = 0; p < B; ++p) {
       const uint32_t byte = (tw[p * 32 * W + c] >> (8 * o)) & 0xFFu;
+#pragma unroll
       for (int t = 0; t < 8; ++t) x |= ((byte >> t) & 1u) << ((t / E) * B * E + p * E + (t % E));
     }
-    uint8_t* dst = out + value_slot(c, o, W, B);
+    uint8_t* dst = stage + value_slot(c, o, W, B);
+#pragma unroll
     for (int k = 0; k < B; ++k) dst[k] = uint8_t(x >> (8 * k));
   }
+  __syncthreads();
+  const uint4* st4 = reinterpret_cast<const uint4*>(stage);
+  for (int i = threadIdx.x; i < 8 * B * W; i += kThreads) out[i] = st4[i];
 }
 
 // ---------------------------------------------------------------------------
@@ -660,15 +671,25 @@ hipError_t launch_pack_values(const tq_ctx* h, const uint32_t* codes, int64_t gr
                               hipStream_t stream) {
   const int64_t nb = (n + kTile - 1) / kTile;
   if (nb == 0 || groups == 0) return hipSuccess;
-  const size_t lds = size_t(h->code_bits) * 32 * h->words * sizeof(uint32_t);
-  if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(pack_values_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (e != hipSuccess) return e;
+  // transposed planes and the output staging, B x 32 W words each
+  const size_t lds = size_t(2) * h->code_bits * 32 * h->words * sizeof(uint32_t);
+  auto launch = [&](auto kernel) {
+    if (lds > 65536) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kernel, dim3(unsigned(nb), unsigned(groups)), dim3(kThreads), lds, stream, codes, n, h->words,
+                       nb, vcodes);
+    return hipGetLastError();
+  };
+  switch (h->code_bits) {
+    case 1: return launch(pack_values_kernel<1>);
+    case 2: return launch(pack_values_kernel<2>);
+    case 3: return launch(pack_values_kernel<3>);
+    case 4: return launch(pack_values_kernel<4>);
+    default: return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL(pack_values_kernel, dim3(unsigned(nb), unsigned(groups)), dim3(kThreads), lds, stream, codes, n,
-                     h->code_bits, h->words, nb, vcodes);
-  return hipGetLastError();
 }
 
 // tokens per split: enough blocks to fill the GPU a few times over, at
