@@ -177,3 +177,18 @@ def test_split_rejections(env):
         tqm.tq_attention(hk, hs, torch.ones((1, 4, 128), device="cuda"), dummy, dummy, dummy.float(), dummy.float(),
                          dummy, dummy.float(), n=32)
     assert e.value.code == tqm.TQ_EUNSUPPORTED
+
+
+def test_split_hi_zero_is_the_plain_handle(env):
+    """hi = 0 builds exactly tq_init's parameters and packed format: same
+    parameter hash, layout and bit-identical quantizer output."""
+    torch, tqm = env
+    _announce("split hi=0 equals plain")
+    a, b = tqm.tq_init_split(128, 3, 0, 9), tqm.tq_init(128, 3, 9)
+    assert tqm.tq_params_hash(a) == tqm.tq_params_hash(b)
+    assert a.code_shape == b.code_shape == (2, 4) and a.layout.code_bytes == b.layout.code_bytes
+    keys = _dev(torch, _keys(np.random.default_rng(3), 500, 128), torch.bfloat16)
+    pa, pb = tqm.tq_quantize(a, keys), tqm.tq_quantize(b, keys)
+    torch.cuda.synchronize()
+    for x, y in zip(pa, pb):
+        assert torch.equal(x, y)
