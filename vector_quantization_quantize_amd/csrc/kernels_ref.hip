@@ -228,6 +228,9 @@ query_prep_kernel(const float* __restrict__ queries, int d, const float* __restr
 // ---------------------------------------------------------------------------
 // scores: one thread per key, queries of the group in chunks of 4
 // ---------------------------------------------------------------------------
+// NP = planes per coordinate at most (code_bits, plus one with fractional
+// widths): a compile-time bound for the index loops.
+template <int NP>
 __global__ void __launch_bounds__(kThreads)
 logits_ref_kernel(const float* __restrict__ vw, int64_t nq, int d, int code_bits, int words,
                   int64_t n, int64_t stride, int64_t half, const uint32_t* __restrict__ codes,
@@ -268,21 +271,23 @@ logits_ref_kernel(const float* __restrict__ vw, int64_t nq, int d, int code_bits
     if (t >= n) continue;
     float a1[4] = {0.f, 0.f, 0.f, 0.f}, a2[4] = {0.f, 0.f, 0.f, 0.f};
     for (int w = 0; w < words; ++w) {
-      // planes past the key's own (at most 5) stay 0 and add nothing to the
-      // index, so every plane loop below has a fixed trip count
-      uint32_t plane[5] = {0u, 0u, 0u, 0u, 0u};
+      // planes past the key's own stay 0 and add nothing to the index, so
+      // every plane loop below has the fixed trip count NP
+      uint32_t plane[NP];
 #pragma unroll
-      for (int q = 0; q < 5; ++q)
+      for (int q = 0; q < NP; ++q) plane[q] = 0u;
+#pragma unroll
+      for (int q = 0; q < NP; ++q)
         if (q < code_bits) plane[q] = codes[key * cw + int64_t(q) * words + w];
 #pragma unroll
-      for (int q = 1; q < 5; ++q)
+      for (int q = 1; q < NP; ++q)
         if (q == code_bits && w < hi_words) plane[q] = codes[key * cw + int64_t(q) * words + w];
       const uint32_t sw = signs[key * words + w];
       auto step = [&](int b) {
         const int j = 32 * w + b;
         int idx = 0;
 #pragma unroll
-        for (int q = 0; q < 5; ++q) idx |= int((plane[q] >> b) & 1u) << q;
+        for (int q = 0; q < NP; ++q) idx |= int((plane[q] >> b) & 1u) << q;
         const float cv = j < hi ? lvlh[idx] : lvl[idx];
         const float sg = ((sw >> b) & 1u) ? 1.0f : -1.0f;
         const float4 vv = *reinterpret_cast<const float4*>(qv + 8 * j);
@@ -489,13 +494,23 @@ hipError_t launch_logits_v1(const tq_ctx* h, const float* vw, int64_t groups, in
                             const float* rnorms, int64_t n, float* scores, hipStream_t stream) {
   const int d = h->d;
   const size_t lds = (2 * kMaxLevels + size_t(8) * d) * sizeof(float);
-  hipError_t e = allow_lds(logits_ref_kernel, lds);
-  if (e != hipSuccess) return e;
   const dim3 grid(static_cast<uint32_t>((n + kThreads - 1) / kThreads), static_cast<uint32_t>(groups));
-  hipLaunchKernelGGL(logits_ref_kernel, grid, dim3(kThreads), lds, stream, vw, nq, d, h->code_bits,
-                     h->words, n, vw_stride(d), vw_half(d), codes, signs, norms, rnorms, scores, h->cb, h->hi,
-                     h->hi_words, h->cbh);
-  return hipGetLastError();
+  auto launch = [&](auto kernel) {
+    hipError_t e = allow_lds(kernel, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), lds, stream, vw, nq, d, h->code_bits, h->words, n,
+                       vw_stride(d), vw_half(d), codes, signs, norms, rnorms, scores, h->cb, h->hi, h->hi_words,
+                       h->cbh);
+    return hipGetLastError();
+  };
+  switch (h->code_bits + (h->hi > 0 ? 1 : 0)) {
+    case 1: return launch(logits_ref_kernel<1>);
+    case 2: return launch(logits_ref_kernel<2>);
+    case 3: return launch(logits_ref_kernel<3>);
+    case 4: return launch(logits_ref_kernel<4>);
+    case 5: return launch(logits_ref_kernel<5>);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_dequant_v1(const tq_ctx* h, const uint32_t* codes, const float* norms, int64_t n,
