@@ -92,53 +92,67 @@ __device__ __forceinline__ int value_slot(int c, int o, int W, int B) {
 // octet) interleaves the planes' bytes into X and writes its B bytes.
 // Dynamic LDS: B * 32 W words.
 // B is a template argument so that the interleave below unrolls with
-// constant shifts; the block's 128 B W output bytes are assembled in LDS and
-// leave with 16-byte stores (the block is 16-byte aligned: the caller's
-// buffer is, and 128 B W is a multiple of 16).
-template <int B>
+// constant shifts; each token block's 128 B W output bytes are assembled in
+// LDS and leave with 16-byte stores (a block is 16-byte aligned: the
+// caller's buffer is, and 128 B W is a multiple of 16).  A workgroup takes
+// TB consecutive token blocks and issues their loads together, so that the
+// load latency is paid once per TB blocks.
+template <int B, int TB>
 __global__ void __launch_bounds__(kThreads)
 pack_values_kernel(const uint32_t* __restrict__ codes, int64_t n, int W, int64_t nb, uint32_t* __restrict__ vcodes) {
-  extern __shared__ uint32_t tw[];  // [B][32 W] transposed planes, then [B][32 W] output staging
-  uint8_t* stage = reinterpret_cast<uint8_t*>(tw + B * 32 * W);
+  extern __shared__ uint32_t tw[];  // [TB][B][32 W] transposed planes, then [TB][B][32 W] output staging
+  const int bw = B * 32 * W;        // words per token block
+  uint8_t* stage = reinterpret_cast<uint8_t*>(tw + TB * bw);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t blk = blockIdx.x, grp = blockIdx.y;
+  const int64_t blk0 = int64_t(blockIdx.x) * TB, grp = blockIdx.y;
   const int pws = B * W;  // words per token in the key layout
   codes += grp * n * pws;
-  uint4* out = reinterpret_cast<uint4*>(vcodes + (grp * nb + blk) * int64_t(pws) * 32);
-  const int64_t tok = blk * 32 + (lane & 31);
   for (int pw = 2 * wave; pw < pws; pw += 2 * kWaves) {
     const int mine = pw + (lane >> 5);
-    const uint32_t x = (mine < pws && tok < n) ? codes[tok * pws + mine] : 0u;
-    uint32_t t = 0;
+    uint32_t x[TB];
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const uint64_t m = __ballot((x >> j) & 1u);
-      const uint32_t part = lane < 32 ? uint32_t(m) : uint32_t(m >> 32);
-      t = (lane & 31) == j ? part : t;
+    for (int tb = 0; tb < TB; ++tb) {
+      const int64_t tok = (blk0 + tb) * 32 + (lane & 31);  // past n (and past the last block): zero
+      x[tb] = (mine < pws && tok < n) ? codes[tok * pws + mine] : 0u;
     }
-    if (mine < pws) {
-      const int p = mine / W, w = mine % W;
-      tw[p * 32 * W + 32 * w + (lane & 31)] = t;
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      uint32_t t = 0;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const uint64_t m = __ballot((x[tb] >> j) & 1u);
+        const uint32_t part = lane < 32 ? uint32_t(m) : uint32_t(m >> 32);
+        t = (lane & 31) == j ? part : t;
+      }
+      if (mine < pws) {
+        const int p = mine / W, w = mine % W;
+        tw[tb * bw + p * 32 * W + 32 * w + (lane & 31)] = t;
+      }
     }
   }
   __syncthreads();
   constexpr int E = value_e(B);
-  for (int i = threadIdx.x; i < 4 * 32 * W; i += kThreads) {
-    const int c = i >> 2, o = i & 3;
+  for (int i = threadIdx.x; i < TB * 4 * 32 * W; i += kThreads) {
+    const int tb = i / (128 * W), ii = i - tb * 128 * W;
+    const int c = ii >> 2, o = ii & 3;
+    const uint32_t* src = tw + tb * bw;
     uint32_t x = 0;
 #pragma unroll
     for (int p = 0; p < B; ++p) {
-      const uint32_t byte = (tw[p * 32 * W + c] >> (8 * o)) & 0xFFu;
+      const uint32_t byte = (src[p * 32 * W + c] >> (8 * o)) & 0xFFu;
 #pragma unroll
       for (int t = 0; t < 8; ++t) x |= ((byte >> t) & 1u) << ((t / E) * B * E + p * E + (t % E));
     }
-    uint8_t* dst = stage + value_slot(c, o, W, B);
+    uint8_t* dst = stage + size_t(tb) * 4 * bw + value_slot(c, o, W, B);
 #pragma unroll
     for (int k = 0; k < B; ++k) dst[k] = uint8_t(x >> (8 * k));
   }
   __syncthreads();
+  // the blocks that exist, as one contiguous run of 16-byte words
+  const int64_t blocks = nb - blk0 < TB ? nb - blk0 : TB;
+  uint4* out = reinterpret_cast<uint4*>(vcodes + (grp * nb + blk0) * int64_t(bw));
   const uint4* st4 = reinterpret_cast<const uint4*>(stage);
-  for (int i = threadIdx.x; i < 8 * B * W; i += kThreads) out[i] = st4[i];
+  for (int64_t i = threadIdx.x; i < blocks * 8 * B * W; i += kThreads) out[i] = st4[i];
 }
 
 // ---------------------------------------------------------------------------
@@ -671,23 +685,31 @@ hipError_t launch_pack_values(const tq_ctx* h, const uint32_t* codes, int64_t gr
                               hipStream_t stream) {
   const int64_t nb = (n + kTile - 1) / kTile;
   if (nb == 0 || groups == 0) return hipSuccess;
-  // transposed planes and the output staging, B x 32 W words each
-  const size_t lds = size_t(2) * h->code_bits * 32 * h->words * sizeof(uint32_t);
+  // transposed planes and the output staging, B x 32 W words each per token
+  // block; 4 token blocks per workgroup while that fits 64 KiB, else 1
+  const size_t per = size_t(2) * h->code_bits * 32 * h->words * sizeof(uint32_t);
+  const bool four = 4 * per <= 65536;
+  const size_t lds = four ? 4 * per : per;
+  const int64_t wgs = four ? (nb + 3) / 4 : nb;
   auto launch = [&](auto kernel) {
     if (lds > 65536) {
       const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kernel, dim3(unsigned(nb), unsigned(groups)), dim3(kThreads), lds, stream, codes, n, h->words,
-                       nb, vcodes);
+    hipLaunchKernelGGL(kernel, dim3(unsigned(wgs), unsigned(groups)), dim3(kThreads), lds, stream, codes, n,
+                       h->words, nb, vcodes);
     return hipGetLastError();
   };
-  switch (h->code_bits) {
-    case 1: return launch(pack_values_kernel<1>);
-    case 2: return launch(pack_values_kernel<2>);
-    case 3: return launch(pack_values_kernel<3>);
-    case 4: return launch(pack_values_kernel<4>);
+  switch (h->code_bits * 2 + (four ? 1 : 0)) {
+    case 2: return launch(pack_values_kernel<1, 1>);
+    case 3: return launch(pack_values_kernel<1, 4>);
+    case 4: return launch(pack_values_kernel<2, 1>);
+    case 5: return launch(pack_values_kernel<2, 4>);
+    case 6: return launch(pack_values_kernel<3, 1>);
+    case 7: return launch(pack_values_kernel<3, 4>);
+    case 8: return launch(pack_values_kernel<4, 1>);
+    case 9: return launch(pack_values_kernel<4, 4>);
     default: return hipErrorInvalidValue;
   }
 }
