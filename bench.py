@@ -8,11 +8,15 @@ batch entry, 4 per KV head):
   tq_dequant_mse  stage-1 reconstruction of the full cache
 All inputs are synthetic (seeded), resident in HBM before timing starts.
 
-Prints one JSON line.  ``value`` = (query, key) scores produced per second of
-step time.  Per-kernel times come from HIP events recorded on the stream the
-library launches on; ``roofline`` is for the kernel with the largest share of
-the step.  ``cpu_baseline`` times the CPU oracle on a bounded sample of the
-same workload on the host cores.
+Prints one JSON line.  ``value`` = tq_logits (query, key) scores per second,
+the kernel timed with the caches flushed before each launch (the metric's
+"keys scored/s"); the step's own rate is under ``step``.  Per-kernel times
+come from HIP events recorded on the stream the library launches on;
+``roofline`` is for the kernel with the largest share of the step, priced
+against the roof its arithmetic intensity puts it under.  ``cpu_baseline``
+times the CPU oracle on a bounded sample of the same workload on the host
+cores, and ``parity`` compares every key of that sample with the GPU's
+output from the timed step.
 """
 import argparse
 import json
@@ -352,30 +356,91 @@ def decode_leg(seed, reps=50):
     return res
 
 
-def cpu_baseline(w, keys_np, queries_np, groups, seed):
-    """Oracle (numpy float64) on the first `groups` key groups."""
-    import numpy as np
-    from oracle import params as P
-    from oracle import tq
+def _host_cores():
+    """Cores this process may run on (its CPU affinity)."""
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(w, keys_np, queries_np, groups, seed, gpu_out):
+    """Oracle (numpy float64) on the first `groups` key groups, timed on the
+    host cores with BLAS limited to the process's CPU affinity; then (not
+    timed) every key of those groups compared with the GPU's packed output,
+    scores and reconstruction from the timed step (``gpu_out``: codes,
+    signs, norms, rnorms, scores, khat as device tensors)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import params as P
+    from oracle import parity
+    from oracle import tq
+    cores = _host_cores()
     pr = P.init(w.d, w.bits, seed)
-    t0 = time.perf_counter()
+    fields = ("elements", "code_mismatch", "code_bad", "sign_mismatch", "sign_bad", "sign_bad_normalized",
+              "cascade_keys", "decision_keys", "norm_bad", "rnorm_bad", "padding_bad")
+    total = {f: 0 for f in fields}
+    bad_scores = bad_khat = 0
+    worst_score = worst_khat = 0.0
+    codes, signs, norms, rnorms, scores, khat = gpu_out
+    dt = 0.0
     scored = 0
-    for g in range(groups):
-        k = keys_np[g * w.n:(g + 1) * w.n].astype(np.float64)
-        qz = tq.quantize(pr, k)
-        s = tq.scores(pr, queries_np[g], qz.idx, qz.beta, qz.norms, qz.rnorms)
-        tq.dequant_mse(pr, qz.idx, qz.norms)
-        scored += s.size
-    dt = time.perf_counter() - t0
-    return {"value": scored / dt, "unit": "keys scored/s", "cores": int(threads), "kind": "oracle",
+    with threadpool_limits(limits=cores):
+        for g in range(groups):
+            sl = slice(g * w.n, (g + 1) * w.n)
+            k = keys_np[sl].astype(np.float64)
+            t0 = time.perf_counter()
+            qz = tq.quantize(pr, k)
+            s = tq.scores(pr, queries_np[g], qz.idx, qz.beta, qz.norms, qz.rnorms)
+            kh = tq.dequant_mse(pr, qz.idx, qz.norms)
+            dt += time.perf_counter() - t0
+            scored += s.size
+            # parity of this group (outside the timed region)
+            nn = norms[sl].cpu().numpy()
+            rep = parity.compare_quantize(pr, qz, codes[sl].cpu().numpy(), signs[sl].cpu().numpy(), nn,
+                                          rnorms[sl].cpu().numpy())
+            for f in fields:
+                total[f] += getattr(rep, f)
+            ref = rep.reference
+            if rep.decision_keys:
+                s = parity.e2e_scores(pr, rep, queries_np[g], qz.norms)
+            b, wr = parity.score_violations(scores[g].cpu().numpy(), s, queries_np[g], qz.norms)
+            bad_scores += b
+            worst_score = max(worst_score, wr)
+            kh = tq.dequant_mse(pr, ref.idx, nn.astype(np.float64))
+            b, wr = parity.dequant_violations(khat[sl].cpu().numpy(), kh)
+            bad_khat += b
+            worst_khat = max(worst_khat, wr)
+        # the toy workload on one thread: the oracle's single-core rate
+        toy = wl_toy()
+        tk, tqq = toy
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            prt = P.init(128, 3, seed)
+            qt = tq.quantize(prt, tk.astype(np.float64))
+            st = tq.scores(prt, tqq[0], qt.idx, qt.beta, qt.norms, qt.rnorms)
+            tq.dequant_mse(prt, qt.idx, qt.norms)
+            dt1 = time.perf_counter() - t0
+    rate = (total["code_mismatch"] + total["sign_mismatch"]) / max(total["elements"], 1)
+    parity_line = dict(total, mismatch_rate=rate, score_violations=bad_scores, worst_score_error_of_tol=worst_score,
+                       reconstruction_violations=bad_khat, worst_reconstruction_error_of_tol=worst_khat,
+                       keys_compared=groups * w.n,
+                       rule="codes and signs bit-exact outside |z - t| < 1e-6 and |p| < 1e-6, mismatches "
+                            "< 1e-5 of all decisions; scores within 1e-3 ||q|| n; reconstruction within 1e-5")
+    base = {"value": scored / dt, "unit": "keys scored/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{groups} of {w.groups} key groups ({groups * w.n} keys x {w.nq} queries): quantize + "
-                      f"score + stage-1 reconstruction in numpy float64, {dt:.1f} s; cores = BLAS threads "
-                      f"(elementwise numpy runs on one)"}
+                      f"score + stage-1 reconstruction in numpy float64, {dt:.1f} s; BLAS limited to the "
+                      f"{cores} cores of the process's CPU affinity (elementwise numpy runs on one)",
+            "one_thread_toy": {"value": st.size / dt1, "unit": "keys scored/s", "cores": 1,
+                               "sample": f"toy workload (4096 fp32 keys x 16 queries, d = 128, 3 bits), {dt1:.2f} s"}}
+    return base, parity_line
+
+
+def wl_toy():
+    from vector_quantization_quantize_amd import workloads as wl
+    w = wl.WORKLOADS["toy"]
+    return wl.keys(w), wl.queries(w)
 
 
 def main():
@@ -474,36 +539,37 @@ def main():
     kern["tq_logits"]["keys_scored_per_s"] = scored / (per["tq_logits"] * 1e-3)
     kern["tq_logits"]["keys_scored_per_s_cold"] = scored / (cold["tq_logits"] * 1e-3)
 
-    # which resource bounds each kernel as built at d = 128: logits streams
-    # bytes; quantize runs its two projections on the matrix cores (2 f16
-    # passes for Pi k on power-of-two scaled keys + 3 for G r, each 2 d^2, for
-    # 4 d^2 useful flops per key); the reconstruction (3 passes of 2 d^2)
-    # writes 512 B per key and is bound by HBM writes
-    bound = {"tq_quantize": ("mfma", BF16_MFMA_PEAK_TFLOPS), "tq_logits": ("hbm", HBM_PEAK_GBS),
-             "tq_dequant_mse": ("hbm", HBM_PEAK_GBS)}
-    # reconstruction: 2 passes when the level set has at most two magnitudes
-    # (B <= 2 at d = 128), else 3
+    # which roof bounds each kernel, by its arithmetic intensity against the
+    # ridge of HBM and bf16 matrix cores (2500 TFLOP/s / 8 TB/s = 312 flop/B):
+    # quantize does 4 d^2 useful flops on 2 d + 56 bytes per key at d = 128
+    # (210 flop/B), logits streams 72 bytes per key for 4 queries, and the
+    # reconstruction writes 4 d bytes per key; all three are HBM-bound.  The
+    # matrix-core work each one really runs is reported beside it: quantize
+    # runs 2 f16 passes for Pi k on power-of-two scaled keys + 3 for G r,
+    # each 2 d^2 flops; the reconstruction 2 passes when the level set has
+    # at most two magnitudes (B <= 2 at d = 128), else 3.
+    bound = {n: ("hbm", HBM_PEAK_GBS) for n in names}
     raw_passes = {"tq_quantize": 10 * w.d * w.d, "tq_dequant_mse": (4 if w.bits <= 3 else 6) * w.d * w.d}
     for n, f in raw_passes.items():
         kern[n]["raw_mfma_TFLOPs"] = round(f * total / (per[n] * 1e-3) / 1e12, 2)
+        kern[n]["mfma_useful_frac"] = round(kern[n]["TFLOPs"] / BF16_MFMA_PEAK_TFLOPS, 4)
+        kern[n]["mfma_raw_frac"] = round(kern[n]["raw_mfma_TFLOPs"] / BF16_MFMA_PEAK_TFLOPS, 4)
 
     def roofline(n):
         kind, peak = bound[n]
-        if kind == "hbm":
-            ach, ach_cold, unit = kern[n]["GBps"], kern[n]["GBps_cold"], "GB/s"
-        else:
-            ach, unit = kern[n]["TFLOPs"], "TFLOP/s"
-            ach_cold = round(models[n]["flops"] * total / (cold[n] * 1e-3) / 1e12, 2)
-        return {"kernel": n, "bound": kind, "achieved": ach, "peak": peak, "unit": unit,
-                "frac": round(ach / peak, 4), "traffic": traffic.get(n),
-                "achieved_cold": ach_cold, "frac_cold": round(ach_cold / peak, 4),
+        ach, ach_cold, unit = kern[n]["GBps"], kern[n]["GBps_cold"], "GB/s"
+        return {"kernel": n, "bound": kind, "achieved": ach_cold, "peak": peak, "unit": unit,
+                "frac": round(ach_cold / peak, 4), "traffic": traffic.get(n),
+                "timing": "flushed caches (1 GiB read before each launch), median of the cold reps",
+                "achieved_in_step": ach, "frac_in_step": round(ach / peak, 4),
+                "bytes_per_key": models[n]["bytes"], "keys_per_launch": total,
                 "mfma_busy_pct": mfma_busy.get(n)}
 
     traffic, mfma_busy = measured_profile(args.workload)
     dominant = max(names, key=lambda n: per[n])
     line = {
         "metric": METRIC,
-        "value": scored / (step_ms * 1e-3),
+        "value": scored / (cold["tq_logits"] * 1e-3),
         "unit": "keys scored/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -516,13 +582,20 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.description}", "keys": total, "d": w.d, "bits": w.bits,
                    "queries": w.groups * w.nq, "key_dtype": w.key_dtype,
-                   "step": "tq_quantize + tq_logits + tq_dequant_mse over the full cache"},
+                   "step": "tq_quantize + tq_logits + tq_dequant_mse over the full cache",
+                   "value": "tq_logits (query, key) scores per second with the caches flushed before the launch"},
+        "step": {"ms": round(step_ms, 4), "keys_scored_per_s": scored / (step_ms * 1e-3),
+                 "tq_quantize_Mkeys_per_s": kern["tq_quantize"]["Mkeys_per_s"]},
         "wall_s": round(wall, 3),
         "kernels": kern,
         "roofline": roofline(dominant),
         "roofline_logits": roofline("tq_logits"),
         "roofline_by_kernel": {n: roofline(n) for n in names},
     }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"], line["parity"] = cpu_baseline(
+            w, keys_np, queries_np, min(args.cpu_groups, w.groups), args.seed,
+            (packed[0], packed[1], packed[2], packed[3], scores, khat))
     if not args.no_attention:
         line["attention"] = attention_leg(w, h, keys, queries, packed, args.seed, stream)
         line["decode_step"] = decode_leg(args.seed)
@@ -533,8 +606,6 @@ def main():
         del keys, queries, packed, scores, ws, khat
         torch.cuda.empty_cache()
         line["search_topk"] = search_topk(args.search_workload, args.seed)
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, keys_np, queries_np, min(args.cpu_groups, w.groups), args.seed)
     print(json.dumps(line), flush=True)
 
 

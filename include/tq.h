@@ -249,17 +249,23 @@ TQ_API int tq_dense_logits(const float* queries, int64_t groups, int64_t nq, con
 /* Value cache layout for tq_attention.  Values are quantized like keys
  * (tq_quantize with the value handle; only codes and norms are kept: the
  * attention reads values back through the stage-1 reconstruction) and their
- * codes are regrouped into token blocks:
- *   vcodes [groups][ceil(n/32)][B][32 W] uint32 (4 W * 32 bytes per plane).
- *   For plane p of block b let T_c be the 32-bit word whose bit i is bit p
- *   of the index of coordinate c of token 32 b + i (tokens past n and
- *   coordinates past d give 0).  Coordinates come in groups of 128 (the
- *   last group holds G = W mod 4 of the key layout's words when that is
- *   not 0, else G = 4); group g's 128 G bytes start at byte 512 g of the
- *   plane, and byte k of T_{128 g + r} sits at byte
- *   ((r mod 16) + 16 k) * 2 G + (r div 16) of the group.
- * One T_c carries one coordinate of 32 tokens, which is what a weighted sum
- * over tokens reads, and the bytes one lane of that sum needs are adjacent.
+ * codes are regrouped into token blocks of 32 tokens:
+ *   vcodes [groups][ceil(n/32)][B][32 W] uint32, i.e. 128 B W bytes per
+ *   block, read as little-endian bytes (tokens past n and coordinates past
+ *   d give index 0).
+ * Within a block the 32 tokens form 4 octets o (tokens 32 b + 8 o .. + 7).
+ * For coordinate c and octet o, one B-byte little-endian integer X holds
+ * the B index bits of the octet's 8 tokens: bit p of the index of token
+ * 8 o + t sits at bit (t div E) B E + p E + (t mod E) of X, with E = 8, 4,
+ * 2, 2 tokens for B = 1, 2, 3, 4.  So each run of B E bits of X is the
+ * packed index of E consecutive tokens, which the attention's value pass
+ * looks up in one table read.  Coordinates come in groups of 128 (the last
+ * group holds G = W mod 4 words of the key layout when that is not 0, else
+ * G = 4); group g's 512 B G bytes start at byte 512 B g of the block, and
+ * for coordinate c = 128 g + r (r < 32 G) the integer X of octet o starts at
+ * byte ((r mod 16) + 16 o) * 2 G B + (r div 16) * B of the group.  That puts
+ * the integers one lane of the value pass reads (one octet, coordinates
+ * r mod 16 + 16 j) side by side.
  * codes: device, groups * n packed keys' codes [groups][n][B][W]; vcodes:
  * device, 16-byte aligned, as above.  Asynchronous on `stream`. */
 TQ_API int tq_pack_values(tq_handle h, const uint32_t* codes, int64_t groups, int64_t n, uint32_t* vcodes,

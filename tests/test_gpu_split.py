@@ -85,15 +85,14 @@ def test_split_matches_oracle(env, d, bits, hi, groups, n, nq):
     qd = _dev(torch, queries)
     s_dec = _cpu(tqm.tq_logits(h, qd, *pdev, n=n))
     s_e2e = _cpu(tqm.tq_logits(h, qd, codes, signs, norms, rnorms, n=n))
-    idx_gpu = tq.unpack_codes_split(_cpu(codes).view(np.uint32), d, bits - 1, hi)
-    keep = ~(idx_gpu != qz.idx).any(axis=1)
     for g in range(groups):
         sl = slice(g * n, (g + 1) * n)
         ref = tq.scores(pr, queries[g], qz.idx[sl], qz.beta[sl], packed[2][sl].astype(np.float64),
                         packed[3][sl].astype(np.float64))
         bad, worst = parity.score_violations(s_dec[g], ref, queries[g], packed[2][sl])
         assert bad == 0, (g, worst)
-        bad, worst = parity.score_violations(s_e2e[g], ref, queries[g], packed[2][sl], keep=keep[sl])
+        ref = parity.e2e_scores(pr, rep, queries[g], qz.norms[sl], sl)
+        bad, worst = parity.score_violations(s_e2e[g], ref, queries[g], qz.norms[sl])
         assert bad == 0, (g, worst)
 
     kh = _cpu(tqm.tq_dequant_mse(h, pdev[0], pdev[2]))

@@ -733,3 +733,232 @@ def test_split_pack_bit_positions():
     # hi = 0 is the plain layout, flattened
     plain = rs.integers(0, 8, (4, 70))
     assert np.array_equal(tq.pack_codes_split(plain, 3, 0), tq.pack_codes(plain, 3).reshape(4, -1))
+
+
+# ---------------------------------------------------------------------------
+# the parity rules themselves (oracle.parity), with mistakes planted on the CPU
+# ---------------------------------------------------------------------------
+
+def _bisect(f, lo, hi, iters=200):
+    """Root of a monotone scalar function between lo and hi (float64)."""
+    flo = f(lo)
+    for _ in range(iters):
+        mid = 0.5 * (lo + hi)
+        fm = f(mid)
+        if (fm > 0) == (flo > 0):
+            lo, flo = mid, fm
+        else:
+            hi = mid
+    return 0.5 * (lo + hi)
+
+
+def _plant_z(pr, key, j, target):
+    """key + a Pi_j so that the oracle's z_j equals target (found by
+    bisection through the oracle's own normalize + rotate)."""
+    row = pr.pi[j]
+    zj = lambda a: tq.rotate(pr, tq.normalize((key + a * row)[None, :])[1])[0, j] - target
+    a = _bisect(zj, -0.3 * np.linalg.norm(key), 0.3 * np.linalg.norm(key))
+    return key + a * row
+
+
+def _plant_p(pr, key, target):
+    """key moved along Pi^T G_j, for the j of its smallest |p_j|, so that the
+    oracle's p_j equals target; None when a code changes on the way."""
+    base = tq.quantize(pr, key[None, :])
+    j = int(np.argmin(np.abs(base.p[0])))
+    direction = pr.pi.T @ pr.g[j]
+    direction /= np.linalg.norm(direction)
+    pj = lambda a: tq.quantize(pr, (key + a * direction)[None, :]).p[0, j] - target
+    span = 0.05 * np.linalg.norm(key)
+    if (pj(-span) > 0) == (pj(span) > 0):
+        return None, j
+    moved = key + _bisect(pj, -span, span) * direction
+    if not np.array_equal(tq.quantize(pr, moved[None, :]).idx, base.idx):
+        return None, j
+    return moved, j
+
+
+def _packed(pr, qz):
+    codes, signs, norms, rnorms = tq.pack(pr, qz)
+    return codes.copy(), signs.copy(), norms.astype(np.float32), rnorms.astype(np.float32)
+
+
+def _planted_case():
+    """2000 keys at d = 32, 3 bits (128 000 decisions, so one mismatch is a
+    rate of 7.8e-6): key 0 has z_3 3e-7 above threshold 1; key a has one
+    p_j = 3e-6 (outside |p| < 1e-6, inside |p| / sqrt(d) < 1e-6) and key b
+    one p_j = 4e-7 (inside both windows).  Returns the keys' positions."""
+    pr = P.init(32, 3, 5)
+    rs = np.random.default_rng(55)
+    keys = rs.standard_normal((2000, 32))
+    t = pr.thresholds[1]
+    keys[0] = _plant_z(pr, keys[0], 3, t + 3e-7)
+    planted = []
+    for target in (3e-6, 4e-7):
+        for i in range(1 + len(planted) * 100, 2000):
+            moved, j = _plant_p(pr, keys[i], target)
+            if moved is not None:
+                keys[i] = moved
+                planted.append((i, j))
+                break
+    qz = tq.quantize(pr, keys)
+    assert 0 < qz.z[0, 3] - t < 1e-6
+    (a, ja), (b, jb) = planted
+    assert abs(qz.p[a, ja] - 3e-6) < 1e-10 and abs(qz.p[b, jb] - 4e-7) < 1e-10
+    return pr, keys, qz, planted
+
+
+def test_compare_quantize_accepts_the_oracle_and_in_window_flips():
+    """The oracle's own packed output passes with no mismatch.  A code
+    flipped inside the window passes when the key's signs and rho are the
+    oracle's for the flipped code (the cascade), and is counted; a sign
+    flipped inside |p| < 1e-6 passes and is counted."""
+    from oracle import parity
+    pr, keys, qz, ((a, ja), (b, jb)) = _planted_case()
+    rep = parity.compare_quantize(pr, qz, *_packed(pr, qz))
+    assert rep.ok() and rep.code_mismatch == rep.sign_mismatch == rep.cascade_keys == 0
+    assert rep.elements == 2 * 2000 * 32
+
+    idx = qz.idx.copy()
+    idx[0, 3] -= 1                                 # the lower cell, 3e-7 away
+    ref = parity.reference_for_codes(pr, qz, idx)
+    assert not np.array_equal(ref.beta[0], qz.beta[0]) and ref.rnorms[0] != qz.rnorms[0]
+    assert np.array_equal(ref.beta[1:], qz.beta[1:])
+    rep = parity.compare_quantize(pr, qz, *_packed(pr, ref))
+    assert rep.ok(), rep
+    assert rep.code_mismatch == 1 and rep.code_bad == 0 and rep.cascade_keys == 1 and rep.sign_mismatch == 0
+
+    beta = qz.beta.copy()
+    beta[b, jb] = ~beta[b, jb]
+    rep = parity.compare_quantize(pr, qz, *_packed(pr, tq.Quantized(qz.idx, beta, qz.norms, qz.rnorms, qz.z, qz.p)))
+    assert rep.ok() and rep.sign_mismatch == 1 and rep.sign_bad == 0 and rep.decision_keys == 1
+    # that one in-window sign moves the key's scores by more than the score
+    # bound for some queries; the end-to-end reference is the estimator on
+    # the library's decisions, which the scores computed from them meet
+    q = np.random.default_rng(9).standard_normal((64, 32))
+    lib = tq.scores(pr, q, qz.idx[b:b + 1], beta[b:b + 1], qz.norms[b:b + 1], qz.rnorms[b:b + 1])
+    own = tq.scores(pr, q, qz.idx[b:b + 1], qz.beta[b:b + 1], qz.norms[b:b + 1], qz.rnorms[b:b + 1])
+    assert parity.score_violations(lib, own, q, qz.norms[b:b + 1])[0] > 0
+    ref = parity.e2e_scores(pr, rep, q, qz.norms[b:b + 1], slice(b, b + 1))
+    assert parity.score_violations(lib, ref, q, qz.norms[b:b + 1]) == (0, 0.0)
+
+
+def test_compare_quantize_rejects_planted_mistakes():
+    """Each of these makes the comparison fail: a flipped code whose key
+    keeps the unflipped code's signs (the cascade not followed), a code
+    flipped outside the window, a sign flipped outside |p| < 1e-6 (also when
+    it is inside the wider |p| / sqrt(d) window, which is only reported), a
+    NaN / infinite / off norm or rho, a set padding bit, and in-window
+    mismatches above 1e-5 of the decisions."""
+    from oracle import parity
+    pr, keys, qz, ((a, ja), (b, jb)) = _planted_case()
+
+    def run(codes=None, signs=None, norms=None, rnorms=None, params=pr, q=qz):
+        c, s, n, r = _packed(params, q)
+        return parity.compare_quantize(params, q, *(x if x is not None else y
+                                                   for x, y in zip((codes, signs, norms, rnorms), (c, s, n, r))))
+
+    idx = qz.idx.copy()
+    idx[0, 3] -= 1
+    stale = tq.pack(pr, tq.Quantized(idx, qz.beta, qz.norms, qz.rnorms, qz.z, qz.p))
+    rep = run(codes=stale[0])
+    assert not rep.ok() and rep.sign_bad > 0 and rep.cascade_keys == 1
+
+    far = int(np.argmax(np.min(np.abs(qz.z[5, :, None] - pr.thresholds[None, :]), axis=1)))
+    idx = qz.idx.copy()
+    idx[5, far] = (idx[5, far] + 1) % 4
+    ref = parity.reference_for_codes(pr, qz, idx)
+    rep = run(codes=_packed(pr, ref)[0], signs=_packed(pr, ref)[1], rnorms=_packed(pr, ref)[3])
+    assert not rep.ok() and rep.code_bad == 1 and "code" in rep.worst
+
+    beta = qz.beta.copy()
+    beta[a, ja] = ~beta[a, ja]                     # |p| = 3e-6: outside 1e-6, inside 1e-6 sqrt(32)
+    rep = run(signs=tq.pack_bits(beta))
+    assert not rep.ok() and rep.sign_bad == 1 and rep.sign_bad_normalized == 0
+    beta = qz.beta.copy()
+    far = int(np.argmax(np.abs(qz.p[9])))
+    beta[9, far] = ~beta[9, far]
+    rep = run(signs=tq.pack_bits(beta))
+    assert not rep.ok() and rep.sign_bad == 1 and rep.sign_bad_normalized == 1
+
+    for bad in (np.nan, np.inf):
+        n = qz.norms.astype(np.float32)
+        n[11] = bad
+        rep = run(norms=n)
+        assert not rep.ok() and rep.norm_bad == 1 and rep.nonfinite == 1
+        r = qz.rnorms.astype(np.float32)
+        r[12] = bad
+        rep = run(rnorms=r)
+        assert not rep.ok() and rep.rnorm_bad == 1
+    n = qz.norms.astype(np.float32)
+    n[13] = qz.norms[13] * (1 + 2 * 32 * 2.0 ** -24)
+    assert run(norms=n).norm_bad == 1
+    r = qz.rnorms.astype(np.float32)
+    r[14] = qz.rnorms[14] + 3 * (np.sqrt(32) * 1e-6 + 32 * 2.0 ** -24 * qz.rnorms[14])
+    assert run(rnorms=r).rnorm_bad == 1
+    # all-NaN outputs, as from a kernel that never wrote them
+    rep = run(norms=np.full(2000, np.nan, np.float32), rnorms=np.full(2000, np.nan, np.float32))
+    assert not rep.ok() and rep.norm_bad == 2000 and rep.rnorm_bad == 2000
+
+    # a padding bit past d (d = 30: the top two bits of the last word)
+    pr30 = P.init(30, 3, 5)
+    q30 = tq.quantize(pr30, keys[:, :30])
+    c, s, n, r = _packed(pr30, q30)
+    s[4, 0] |= np.uint32(1 << 31)
+    assert parity.compare_quantize(pr30, q30, c, s, n, r).padding_bad == 1
+    c[6, 1, 0] |= np.uint32(1 << 30)
+    assert not parity.compare_quantize(pr30, q30, c, *_packed(pr30, q30)[1:]).ok()
+
+    # the rate: the in-window flip of key 0 is 1 of 2 * 10 * 32 decisions
+    sub = tq.quantize(pr, keys[:10])
+    idx = sub.idx.copy()
+    idx[0, 3] -= 1
+    ref = parity.reference_for_codes(pr, sub, idx)
+    rep = parity.compare_quantize(pr, sub, *_packed(pr, ref))
+    assert rep.code_bad == 0 and rep.sign_bad == 0 and rep.mismatch_rate > 1e-5 and not rep.ok()
+
+
+def test_score_and_reconstruction_rules_reject_planted_mistakes():
+    """score_violations and dequant_violations count an error of twice the
+    tolerance, a NaN and an infinity as violations (worst ratio inf for the
+    non-finite ones), and pass the oracle's own values and an error of half
+    the tolerance."""
+    from oracle import parity
+    pr = P.init(24, 3, 2)
+    rs = np.random.default_rng(8)
+    keys = rs.standard_normal((40, 24)) * 2.0
+    q = rs.standard_normal((3, 24))
+    qz = tq.quantize(pr, keys)
+    s = tq.scores(pr, q, qz.idx, qz.beta, qz.norms, qz.rnorms)
+    tol = 1e-3 * np.linalg.norm(q, axis=1)[:, None] * qz.norms[None, :]
+    assert parity.score_violations(s, s, q, qz.norms) == (0, 0.0)
+    half = s + 0.5 * tol
+    bad, worst = parity.score_violations(half, s, q, qz.norms)
+    assert bad == 0 and worst == pytest.approx(0.5)
+    for planted, ratio in ((s[1, 7] + 2 * tol[1, 7], 2.0), (np.nan, np.inf), (np.inf, np.inf), (-np.inf, np.inf)):
+        x = s.copy()
+        x[1, 7] = planted
+        bad, worst = parity.score_violations(x, s, q, qz.norms)
+        assert bad == 1 and worst == pytest.approx(ratio)
+        keep = np.ones(40, dtype=bool)
+        keep[7] = False
+        assert parity.score_violations(x, s, q, qz.norms, keep=keep)[0] == 0
+    assert parity.score_violations(np.full_like(s, np.nan), s, q, qz.norms)[0] == s.size
+
+    kh = tq.dequant_mse(pr, qz.idx, qz.norms)
+    assert parity.dequant_violations(kh, kh) == (0, 0.0)
+    e = np.zeros(24)
+    e[0] = 1.0
+    x = kh.copy()
+    x[3] += 2e-5 * np.linalg.norm(kh[3]) * e
+    bad, worst = parity.dequant_violations(x, kh)
+    assert bad == 1 and worst == pytest.approx(2.0)
+    x = kh.copy()
+    x[4] += 0.5e-5 * np.linalg.norm(kh[4]) * e
+    assert parity.dequant_violations(x, kh)[0] == 0
+    for planted in (np.nan, np.inf):
+        x = kh.copy()
+        x[5, 2] = planted
+        bad, worst = parity.dequant_violations(x, kh)
+        assert bad == 1 and worst == np.inf
+    assert parity.dequant_violations(np.full_like(kh, np.nan), kh)[0] == 40

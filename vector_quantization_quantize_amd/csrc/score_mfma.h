@@ -17,10 +17,14 @@
 // puts max(||v||, lambda ||w||) in [2^9, 2^10), lambda being the form's
 // ratio that lets both products share one output scale:
 //     u = n (acc_v + rho acc_w),   score = (gamma / s_R) u.
-// Rounding the rows to float16 (11 bits, all elements normal) moves <v, c>
-// by at most 2^-12 ||v|| ||c|| (Cauchy-Schwarz, ||c[idx]|| about 1) and the
-// sign term by at most 2^-12 ||w||_1 sqrt(pi/2) rho / d: together about half
-// of the 1e-3 ||q|| n bound in the worst case, far less for random data.
+// Rounding the rows to float16 (11 significant bits, all elements normal,
+// round to nearest: relative error at most 2^-11 per element) moves <v, c>
+// by at most 2^-11 ||v|| ||c|| (Cauchy-Schwarz, ||c[idx]|| below 1) and the
+// sign term by at most 2^-11 ||w||_1 sqrt(pi/2) rho / d, which is about
+// 2^-11 rho ||q|| for a Gaussian G (||w||_1 near sqrt(2/pi) d ||q||):
+// together at most about 0.7 of the 1e-3 ||q|| n bound when every rounding
+// error lines up with the key; for data not built against the rounding the
+// errors add incoherently and stay near 2^-11 / sqrt(d) of the score scale.
 //
 // The number of K steps (d / 16, rounded up) is a template parameter, so the
 // step loop is straight-line code the compiler can pipeline; one translation
