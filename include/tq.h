@@ -86,6 +86,7 @@ extern "C" {
 #define TQ_EUNSUPPORTED (-2) /* valid but not implemented                  */
 #define TQ_EHIP (-3)         /* a HIP runtime call or kernel launch failed */
 #define TQ_ENOMEM (-4)       /* host or device allocation failed           */
+#define TQ_ESCRATCH (-5)     /* request larger than the static scratch     */
 
 #define TQ_FORMAT_VERSION 1
 
@@ -197,6 +198,25 @@ TQ_API int tq_logits(tq_handle h, const float* queries, int64_t groups, int64_t 
               const uint32_t* codes, const uint32_t* signs, const float* norms,
               const float* rnorms, int64_t n, float* scores, void* workspace,
               size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): tq_logits
+ * with the workspace taken from a static scratch array of the library
+ * instead of an argument.  Same arguments otherwise, same kernels, and the
+ * same scores bit for bit.  No allocation happens in the call (nor any
+ * hipMalloc / hipFree); the caller still provides queries, packed keys and
+ * scores.  Returns TQ_ESCRATCH when tq_logits_workspace_size(h, groups, nq)
+ * exceeds tq_noalloc_scratch_bytes() (16 MiB: query rows of d = 128 up to
+ * 16384 per call).  The array is one per GPU, held until the process ends
+ * and shared by every call on that GPU: calls that overlap in time on one
+ * GPU (other streams or host threads) race on it and must be serialised by
+ * the caller. */
+TQ_API int tq_logits_noalloc(tq_handle h, const float* queries, int64_t groups, int64_t nq,
+                             const uint32_t* codes, const uint32_t* signs, const float* norms,
+                             const float* rnorms, int64_t n, float* scores, void* stream);
+
+/* Bytes of the static scratch array tq_logits_noalloc uses (per GPU). */
+TQ_API size_t tq_noalloc_scratch_bytes(void);
 
 /* Bytes of device workspace tq_logits_topk needs for `groups` x `nq`
  * queries against n keys per group, k best keys per query. */

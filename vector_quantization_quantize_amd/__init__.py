@@ -19,6 +19,7 @@ TQ_EINVAL = -1
 TQ_EUNSUPPORTED = -2
 TQ_EHIP = -3
 TQ_ENOMEM = -4
+TQ_ESCRATCH = -5
 TQ_F32 = 0
 TQ_BF16 = 1
 TQ_FORMAT_VERSION = 1
@@ -27,7 +28,8 @@ TQ_FORMAT_VERSION = 1
 EXPORTS = ("tq_init", "tq_init_explicit", "tq_init_hadamard", "tq_init_split", "tq_hadamard_rotation", "tq_destroy", "tq_get_layout", "tq_host_params",
            "tq_params_hash", "tq_quantize", "tq_logits_workspace_size", "tq_logits",
            "tq_logits_topk_workspace_size", "tq_logits_topk", "tq_dequant_mse", "tq_dequant_prod", "tq_dense_logits", "tq_pack_values",
-           "tq_attention_workspace_size", "tq_attention", "tq_strerror")
+           "tq_attention_workspace_size", "tq_attention", "tq_logits_noalloc", "tq_noalloc_scratch_bytes",
+           "tq_strerror")
 
 
 class TqError(RuntimeError):
@@ -78,6 +80,8 @@ def _lib():
         "tq_attention_workspace_size": (sz, [vp, vp, i64, i64, i64]),
         "tq_attention": (ctypes.c_int, [vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, i64, ctypes.c_float, vp, vp,
                                         vp, sz, vp]),
+        "tq_logits_noalloc": (ctypes.c_int, [vp, vp, i64, i64, vp, vp, vp, vp, i64, vp, vp]),
+        "tq_noalloc_scratch_bytes": (sz, []),
         "tq_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -271,6 +275,35 @@ def tq_logits(h, queries, codes, signs, norms, rnorms, n=None, scores=None, work
     _check("tq_logits", _lib().tq_logits(h.ptr, _ptr(queries), groups, nq, _ptr(codes), _ptr(signs),
                                          _ptr(norms), _ptr(rnorms), n, _ptr(scores), _ptr(workspace),
                                          workspace.numel() * workspace.element_size(), _stream(stream)))
+    return scores
+
+
+def tq_noalloc_scratch_bytes():
+    return int(_lib().tq_noalloc_scratch_bytes())
+
+
+def tq_logits_noalloc(h, queries, codes, signs, norms, rnorms, n=None, scores=None, stream=None):
+    """tq_logits with the library's static scratch as workspace (the C entry
+    point allocates nothing; pass `scores` to allocate nothing here either).
+
+    queries: cuda float32 (groups, nq, d); packed arrays hold groups*n keys.
+    Returns scores float32 (groups, nq, n)."""
+    import torch
+    if queries.dim() == 2:
+        queries = queries.unsqueeze(0)
+    groups, nq, d = queries.shape
+    if d != h.d or not queries.is_contiguous() or queries.dtype != torch.float32:
+        raise ValueError("queries must be contiguous float32 (groups, nq, d)")
+    total = norms.shape[0]
+    if n is None:
+        n = total // groups
+    if groups * n > total:
+        raise ValueError("packed arrays hold fewer than groups * n keys")
+    if scores is None:
+        scores = torch.empty((groups, nq, n), dtype=torch.float32, device=queries.device)
+    _check("tq_logits_noalloc", _lib().tq_logits_noalloc(h.ptr, _ptr(queries), groups, nq, _ptr(codes), _ptr(signs),
+                                                         _ptr(norms), _ptr(rnorms), n, _ptr(scores),
+                                                         _stream(stream)))
     return scores
 
 

@@ -308,6 +308,7 @@ const char* tq_strerror(int code) {
     case TQ_EUNSUPPORTED: return "unsupported configuration";
     case TQ_EHIP: return "HIP runtime error";
     case TQ_ENOMEM: return "out of memory";
+    case TQ_ESCRATCH: return "request needs more than the library's static scratch buffer";
     default: return "unknown error";
   }
 }
@@ -384,6 +385,10 @@ static int init_common(int32_t d, int32_t bits, const float* pi_in, const float*
     delete h;
     return rc;
   }
+  // the static scratch of the allocation-free entry points: its address on
+  // this device, looked up once (a failure here is reported by those entry
+  // points, not by init)
+  (void)tqdev::noalloc_prepare(h->device);
   if (trace_enabled())
     std::fprintf(stderr, "[tq] init d=%d bits=%d device=%d\n", h->d, h->bits, h->device);
   *out = h;
@@ -483,7 +488,7 @@ size_t tq_logits_workspace_size(tq_handle h, int64_t groups, int64_t nq) {
 
 }  // extern "C"
 
-namespace {
+namespace tqdev {
 
 // scores [groups][nq][n] by the scorer pick_scorer chooses; workspace of
 // tq_logits_workspace_size bytes (arguments already checked)
@@ -504,6 +509,21 @@ int run_logits(const tq_ctx* h, const float* queries, int64_t groups, int64_t nq
   }
   return e == hipSuccess ? TQ_OK : TQ_EHIP;
 }
+
+// the checks tq_logits makes on everything but the workspace
+int check_logits_args(const tq_ctx* h, const float* queries, int64_t groups, int64_t nq, const uint32_t* codes,
+                      const uint32_t* signs, const float* norms, const float* rnorms, int64_t n, float* scores) {
+  if (!h || groups < 0 || nq < 0 || n < 0) return TQ_EINVAL;
+  if (groups == 0 || nq == 0 || n == 0) return TQ_OK;
+  if (!queries || !codes || !signs || !norms || !rnorms || !scores) return TQ_EINVAL;
+  if (groups > 65535) return TQ_EUNSUPPORTED;
+  if (check_device(h) != TQ_OK) return TQ_EINVAL;
+  return TQ_OK;
+}
+
+}  // namespace tqdev
+
+namespace {
 
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
@@ -529,15 +549,12 @@ extern "C" {
 int tq_logits(tq_handle h, const float* queries, int64_t groups, int64_t nq, const uint32_t* codes,
               const uint32_t* signs, const float* norms, const float* rnorms, int64_t n, float* scores,
               void* workspace, size_t workspace_bytes, void* stream) {
-  if (!h || groups < 0 || nq < 0 || n < 0) return TQ_EINVAL;
-  if (groups == 0 || nq == 0 || n == 0) return TQ_OK;
-  if (!queries || !codes || !signs || !norms || !rnorms || !scores || !workspace) return TQ_EINVAL;
-  if (workspace_bytes < tq_logits_workspace_size(h, groups, nq)) return TQ_EINVAL;
+  const int rc = tqdev::check_logits_args(h, queries, groups, nq, codes, signs, norms, rnorms, n, scores);
+  if (rc != TQ_OK || groups == 0 || nq == 0 || n == 0) return rc;
+  if (!workspace || workspace_bytes < tq_logits_workspace_size(h, groups, nq)) return TQ_EINVAL;
   if (!aligned256(workspace)) return TQ_EINVAL;
-  if (groups > 65535) return TQ_EUNSUPPORTED;
-  if (check_device(h) != TQ_OK) return TQ_EINVAL;
-  return run_logits(h, queries, groups, nq, codes, signs, norms, rnorms, n, scores, workspace,
-                    static_cast<hipStream_t>(stream));
+  return tqdev::run_logits(h, queries, groups, nq, codes, signs, norms, rnorms, n, scores, workspace,
+                           static_cast<hipStream_t>(stream));
 }
 
 int tq_dequant_prod(tq_handle h, const uint32_t* codes, const uint32_t* signs, const float* norms,
@@ -608,7 +625,7 @@ int tq_attention(tq_handle hk, tq_handle hv, const float* queries, int64_t group
   if (workspace_bytes < w.total) return TQ_EINVAL;
   char* base = static_cast<char*>(workspace);
   float* scores = reinterpret_cast<float*>(base);
-  const int rc = run_logits(hk, queries, groups, nq, kcodes, ksigns, knorms, krnorms, n, scores, base + w.scores, s);
+  const int rc = tqdev::run_logits(hk, queries, groups, nq, kcodes, ksigns, knorms, krnorms, n, scores, base + w.scores, s);
   if (rc != TQ_OK) return rc;
   const hipError_t e = tqdev::launch_attention_values(hv, scores, groups, nq, n, vcodes, vnorms, scale,
                                                       base + w.scores + w.prep, out, lse, s);

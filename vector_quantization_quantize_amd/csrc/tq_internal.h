@@ -122,6 +122,19 @@ hipError_t launch_dequant_mfma128(const tq_ctx* h, const uint32_t* codes, const 
 // TQ_KERNELS=ref selects the straightforward kernels everywhere (A/B checks)
 bool force_reference_kernels();
 
+// tq_logits after its argument checks (tq_api.cpp): check_logits_args
+// returns TQ_OK for valid arguments (also for an empty request);
+// run_logits launches with a workspace of tq_logits_workspace_size bytes
+int check_logits_args(const tq_ctx* h, const float* queries, int64_t groups, int64_t nq, const uint32_t* codes,
+                      const uint32_t* signs, const float* norms, const float* rnorms, int64_t n, float* scores);
+int run_logits(const tq_ctx* h, const float* queries, int64_t groups, int64_t nq, const uint32_t* codes,
+               const uint32_t* signs, const float* norms, const float* rnorms, int64_t n, float* scores,
+               void* workspace, hipStream_t s);
+// the static scratch of the allocation-free entry points (noalloc.hip):
+// looks up its address on `device` (which must be current) once; TQ_OK or
+// TQ_EHIP
+int noalloc_prepare(int device);
+
 // search: merge one chunk of scores ([nq][csize], keys c0 .. or, with
 // chunk_i, the keys chunk_i holds; INT64_MAX marks an empty entry) into the
 // running lists of the k best keys per query ([nq][k]); the last chunk writes
