@@ -126,7 +126,4 @@ def test_search_every_key(env, name):
 
 @pytest.mark.timeout(900)
 def test_cone_every_key(env):
-    # the general float32 quantizer sums d = 1536 products in float32, which
-    # moves p by up to about 1e-6: 172 of 1.5e9 signs fall outside |p| < 1e-6
-    # (all inside |p| / sqrt(d) < 1e-6); that count is printed
-    full_check(env, "cone", score_queries=256, chunk=16384, strict_signs=False)
+    full_check(env, "cone", score_queries=256, chunk=16384)

@@ -33,6 +33,7 @@ void free_device(tq_ctx* h) {
     if (*p) (void)hipFree(*p);
     *p = nullptr;
   }
+  tqdev::free_quantize_gemm(h);
 }
 
 uint16_t f16_bits(float x) {
@@ -251,6 +252,7 @@ int finish_init(tq_ctx* h) {
     if ((rc = upload(&h->d_piT128, pt)) != TQ_OK) return rc;
     if ((rc = upload(&h->d_sT128, st)) != TQ_OK) return rc;
   }
+  if ((rc = tqdev::build_quantize_gemm_tiles(h)) != TQ_OK) return rc;
   return build_fragments(h);
 }
 
@@ -474,10 +476,17 @@ int tq_quantize(tq_handle h, const void* keys, int32_t key_dtype, int64_t n, int
   if (!aligned4(codes) || !aligned4(signs) || !aligned4(norms) || !aligned4(rnorms)) return TQ_EINVAL;
   if (check_device(h) != TQ_OK) return TQ_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e =
-      (!tqdev::force_reference_kernels() && tqdev::quantize_mfma128_supported(h, keys, key_dtype, ldk, codes, signs, norms, rnorms))
-          ? tqdev::launch_quantize_mfma128(h, keys, n, ldk, codes, signs, norms, rnorms, s)
-          : tqdev::launch_quantize_v1(h, keys, key_dtype, n, ldk, codes, signs, norms, rnorms, s);
+  // d = 128 with bf16 keys: the register-resident matrix-core kernel; other
+  // d >= 16: the tiled matrix-core kernels; smaller d: float32 kernels
+  hipError_t e;
+  if (tqdev::force_reference_kernels())
+    e = tqdev::launch_quantize_v1(h, keys, key_dtype, n, ldk, codes, signs, norms, rnorms, s);
+  else if (tqdev::quantize_mfma128_supported(h, keys, key_dtype, ldk, codes, signs, norms, rnorms))
+    e = tqdev::launch_quantize_mfma128(h, keys, n, ldk, codes, signs, norms, rnorms, s);
+  else if (tqdev::quantize_gemm_supported(h))
+    e = tqdev::launch_quantize_gemm(h, keys, key_dtype, n, ldk, codes, signs, norms, rnorms, s);
+  else
+    e = tqdev::launch_quantize_v1(h, keys, key_dtype, n, ldk, codes, signs, norms, rnorms, s);
   return e == hipSuccess ? TQ_OK : TQ_EHIP;
 }
 

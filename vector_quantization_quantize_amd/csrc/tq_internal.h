@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 #include <vector>
 
 #include "../../include/tq.h"
@@ -79,6 +80,20 @@ struct tq_ctx {
   bool symmetric = false;  // level set exactly symmetric in float32
   tqdev::HalfCodebook half{};
   tqdev::DequantTable dqt{};
+  // general matrix-core quantizer (quantize_gemm.hip), d >= 16: operand
+  // tiles of 2^12 Pi and 2^10 G as two float16 pieces,
+  // [coord tile][K step][row 128][piece 2][16 halves]
+  uint16_t* d_qpi_tiles = nullptr;
+  uint16_t* d_qg_tiles = nullptr;
+  // its scratch (residual pieces and rho^2 partials of one chunk of keys),
+  // allocated at first use; a call on another stream waits for the event of
+  // the last call that used it
+  void* qscratch = nullptr;
+  size_t qscratch_bytes = 0;
+  hipEvent_t qscratch_done = nullptr;
+  hipStream_t qscratch_stream = nullptr;
+  bool qscratch_used = false;
+  std::mutex qscratch_mu;
 };
 
 namespace tqdev {
@@ -109,6 +124,16 @@ constexpr int64_t kScoreMfmaMinQueries = 16;  // below this the lookup-table sco
 hipError_t launch_score_mfma(const tq_ctx* h, const float* vw, int64_t groups, int64_t nq, const uint32_t* codes,
                              const uint32_t* signs, const float* norms, const float* rnorms, int64_t n,
                              float* scores, hipStream_t stream);
+
+// General matrix-core quantizer (quantize_gemm.hip): any d >= kQGemmMinD,
+// float32 or bfloat16 keys, plain or fractional-width handles.
+constexpr int kQGemmMinD = 16;
+bool quantize_gemm_supported(const tq_ctx* h);
+// the operand tiles for tq_init (host, float64 products where needed)
+int build_quantize_gemm_tiles(tq_ctx* h);
+hipError_t launch_quantize_gemm(tq_ctx* h, const void* keys, int key_dtype, int64_t n, int64_t ldk, uint32_t* codes,
+                                uint32_t* signs, float* norms, float* rnorms, hipStream_t stream);
+void free_quantize_gemm(tq_ctx* h);
 
 bool quantize_mfma128_supported(const tq_ctx* h, const void* keys, int key_dtype, int64_t ldk,
                                 const void* codes, const void* signs, const void* norms, const void* rnorms);
