@@ -198,6 +198,84 @@ def e2e_scores(params, rep, queries, norms, rows=slice(None)):
     return tq.scores(params, queries, rep.idx[rows], rep.beta[rows], norms, rep.reference.rnorms[rows])
 
 
+def polar_angle_distance(pp, angles):
+    """(n, d) distance of every angle (slot order) to its level's nearest
+    decision boundary; level 1 also counts the cut of the circle at 0 = 2 pi
+    (an angle just below 2 pi and one at 0 lie in different cells); the
+    unused slot d - 1 gets inf."""
+    from . import polar
+    out = []
+    for lvl, a in enumerate(angles):
+        t = np.asarray(pp.thresholds[lvl], dtype=np.float64)
+        if lvl == 0:
+            t = np.concatenate(([0.0], t, [polar.TWO_PI]))
+        out.append(_threshold_distance(np.asarray(a, dtype=np.float64), t))
+    n = out[0].shape[0]
+    return np.concatenate(out + [np.full((n, 1), np.inf)], axis=1)
+
+
+def compare_quantize_polar(pp, pq, codes, signs, norms, rnorms):
+    """The quantize rules for a polar handle (``oracle.polar``): angle codes
+    (slot order in the bit planes) bit-exact except where the angle lies
+    within 1e-6 of a decision boundary of its level; signs, norms and rho as
+    in ``compare_quantize``, keys with a changed code compared with the
+    oracle recomputed from the library's codes (z_hat, r, rho, p).
+    ``report.reference`` holds that reference (codes, beta, p, rnorms)."""
+    from . import polar
+    d = pp.d
+    codes = np.asarray(codes).view(np.uint32)
+    signs = np.asarray(signs).view(np.uint32)
+    norms = np.asarray(norms, dtype=np.float64)
+    rnorms = np.asarray(rnorms, dtype=np.float64)
+    rep = QuantizeReport(elements=2 * pq.z.size)
+    slots = tq.unpack_codes(codes, d)
+    rep.padding_bad = _padding_zero(codes, d) + _padding_zero(signs, d) + int(np.count_nonzero(slots[:, d - 1]))
+    ref_slots = polar.slots(pq.codes)
+    dist = polar_angle_distance(pp, pq.angles)
+    cmis = slots != ref_slots
+    rep.code_mismatch = int(cmis.sum())
+    rep.code_bad = int((cmis & (dist >= CODE_WINDOW)).sum())
+    changed = cmis.any(axis=1)
+    rep.cascade_keys = int(changed.sum())
+    beta, p, rn = pq.beta.copy(), pq.p.copy(), pq.rnorms.copy()
+    lib_codes = polar.unslot(slots, d)
+    if changed.any():
+        zh = polar.reconstruct(pp, [c[changed] for c in lib_codes])
+        r = pq.z[changed] - zh
+        rn[changed] = np.sqrt(np.sum(r * r, axis=1))
+        p[changed] = r @ pp.g.T
+        beta[changed] = p[changed].astype(np.float32) > 0
+    ref = dict(codes=lib_codes, beta=beta, p=p, rnorms=rn)
+    rep.reference = ref
+    lib_beta = tq.unpack_bits(signs, d)
+    smis = lib_beta != beta
+    pa = np.abs(p)
+    rep.sign_mismatch = int(smis.sum())
+    rep.sign_bad = int((smis & (pa >= SIGN_WINDOW)).sum())
+    rep.sign_bad_normalized = int((smis & (pa / np.sqrt(d) >= SIGN_WINDOW)).sum())
+    rep.decision_keys = int((cmis.any(axis=1) | smis.any(axis=1)).sum())
+    rep.idx, rep.beta = slots, lib_beta
+    rep.nonfinite = int((~np.isfinite(norms)).sum() + (~np.isfinite(rnorms)).sum())
+    rep.norm_bad = int((~_within(np.abs(norms - pq.norms), d * 2.0 ** -24 * pq.norms)).sum())
+    rep.rnorm_bad = int((~_within(np.abs(rnorms - rn), np.sqrt(d) * 1e-6 + d * 2.0 ** -24 * rn)).sum())
+    if rep.code_bad:
+        i = np.argwhere(cmis & (dist >= CODE_WINDOW))[0]
+        rep.worst["code"] = (tuple(int(x) for x in i), float(dist[tuple(i)]))
+    if rep.sign_bad:
+        i = np.argwhere(smis & (pa >= SIGN_WINDOW))[0]
+        rep.worst["sign"] = (tuple(int(x) for x in i), float(pa[tuple(i)]))
+    return rep
+
+
+def e2e_scores_polar(pp, rep, queries, norms, rows=slice(None)):
+    """End-to-end score reference for polar keys ``rows``: the oracle's
+    estimator on the library's codes and signs, the oracle's norms and the
+    reference rho."""
+    from . import polar
+    codes = [c[rows] for c in rep.reference["codes"]]
+    return polar.scores(pp, queries, codes, rep.beta[rows], norms, rep.reference["rnorms"][rows])
+
+
 def _ratio(err, tol):
     """err / tol with NaN and infinities mapped to inf."""
     r = np.asarray(err, dtype=np.float64) / np.maximum(tol, 1e-300)

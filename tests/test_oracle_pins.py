@@ -962,3 +962,175 @@ def test_score_and_reconstruction_rules_reject_planted_mistakes():
         bad, worst = parity.dequant_violations(x, kh)
         assert bad == 1 and worst == np.inf
     assert parity.dequant_violations(np.full_like(kh, np.nan), kh)[0] == 40
+
+
+# ---------------------------------------------------------------------------
+# the recursive polar-angle variant of stage 1 (oracle.polar)
+# ---------------------------------------------------------------------------
+
+def test_polar_decompose_hand_examples_and_round_trip():
+    """Hand-worked decompositions (level-1 angle of the pair (0, 1) is pi/2,
+    of (1, 0) is 0, of (0, -1) is 3 pi/2; the top angle compares the two
+    halves' lengths), d - 1 angles, top radius = ||z||, and compose inverts
+    decompose."""
+    from oracle import polar as PL
+    z = np.array([[1.0, 0.0, 0.0, 0.0], [0.0, 0.0, 0.0, 1.0], [0.0, -1.0, 0.0, 0.0], [0.6, 0.0, 0.0, 0.8]])
+    ang, r = PL.decompose(z)
+    assert [a.shape[1] for a in ang] == [2, 1]
+    assert np.allclose(ang[0], [[0.0, 0.0], [0.0, np.pi / 2], [3 * np.pi / 2, 0.0], [0.0, np.pi / 2]])
+    assert np.allclose(ang[1][:, 0], [0.0, np.pi / 2, 0.0, np.arctan2(0.8, 0.6)])
+    assert np.allclose(r, 1.0)
+    rs = np.random.default_rng(31)
+    for d in (2, 8, 64, 256):
+        x = rs.standard_normal((20, d)) * 3.0
+        ang, r = PL.decompose(x)
+        assert sum(a.shape[1] for a in ang) == d - 1
+        assert np.allclose(r, np.linalg.norm(x, axis=1), rtol=1e-14)
+        assert np.allclose(PL.compose(ang, r), x, atol=1e-12)
+        assert np.all((ang[0] >= 0) & (ang[0] < 2 * np.pi))
+        assert all(np.all((a >= 0) & (a <= np.pi / 2)) for a in ang[1:])
+
+
+def test_polar_angle_laws():
+    """For uniformly random unit vectors (d = 64), level-1 angles are uniform
+    on [0, 2 pi) and a level-l angle has the law sin^2 psi ~ Beta(m/2, m/2),
+    m = 2^(l-1) (Kolmogorov-Smirnov; the CDF is checked against direct
+    quadrature of the density)."""
+    from oracle import polar as PL
+    rs = np.random.default_rng(32)
+    x = rs.standard_normal((4000, 64))
+    ang, _ = PL.decompose(x / np.linalg.norm(x, axis=1, keepdims=True))
+    assert stats.kstest(ang[0].ravel(), stats.uniform(0, 2 * np.pi).cdf).pvalue > 1e-3
+    for lvl in range(2, 7):
+        m = 1 << (lvl - 1)
+        assert stats.kstest(ang[lvl - 1].ravel(), lambda p: PL.angle_cdf(p, m)).pvalue > 1e-3
+        for p in (0.3, np.pi / 4, 1.2):
+            assert PL.angle_cdf(p, m) == pytest.approx(integrate.quad(lambda s: PL.angle_pdf(s, m), 0, p)[0],
+                                                       rel=1e-9, abs=1e-12)
+
+
+def test_polar_codebooks_closed_forms_and_fixed_point():
+    """m = 2 (density sin 2 psi on [0, pi/2]) with 2 levels: the threshold
+    is pi/4 and the levels are 1/2 and pi/2 - 1/2 (closed form of the
+    conditional means).  Other laws: every level is the conditional mean of
+    its cell, with the mass from the Beta CDF of sin^2 psi (a second route to
+    the mass) and the moment by quadrature; levels are symmetric about pi/4.
+    Level 1 of a handle is the uniform quantizer of the circle."""
+    from oracle import polar as PL
+    c = PL.level_codebook_fp64(2, 2)
+    assert c == pytest.approx([0.5, np.pi / 2 - 0.5], abs=1e-12)
+    for m, levels in ((2, 4), (8, 4), (64, 8), (512, 2)):
+        c = PL.level_codebook_fp64(m, levels)
+        assert np.allclose(c + c[::-1], np.pi / 2, atol=1e-13)
+        t = np.concatenate(([0.0], 0.5 * (c[:-1] + c[1:]), [np.pi / 2]))
+        for i in range(levels):
+            mass = PL.angle_cdf(t[i + 1], m) - PL.angle_cdf(t[i], m)
+            mom = integrate.quad(lambda s: s * PL.angle_pdf(s, m), t[i], t[i + 1], epsrel=1e-13, limit=200)[0]
+            assert mom / mass == pytest.approx(c[i], rel=1e-9)
+    pp = PL.init_polar(16, 3, 0)
+    assert np.allclose(pp.centroids[0], (np.arange(4) + 0.5) * np.pi / 2, rtol=1e-7)
+    assert np.allclose(pp.thresholds[0], np.arange(1, 4) * np.pi / 2, rtol=1e-7)
+    assert len(pp.centroids) == 4 and all(len(x) == 4 for x in pp.centroids)
+
+
+def test_polar_d2_mse_closed_form():
+    """d = 2: one uniform angle, L levels on the circle; the squared error of
+    the unit vector is 2 - 2 cos(e) with e uniform on [-pi/L, pi/L], so its
+    mean is 2 - 2 sin(pi/L) / (pi/L)."""
+    from oracle import polar as PL
+    for bits in (2, 3, 4):
+        pp = PL.init_polar(2, bits, 1)
+        L = 1 << (bits - 1)
+        th = (np.arange(400000) + 0.5) * (2 * np.pi / 400000)   # midpoint rule over the circle
+        z = np.stack([np.cos(th), np.sin(th)], axis=1)
+        ang, _ = PL.decompose(z)
+        zh = PL.reconstruct(pp, PL.quantize_angles(pp, ang))
+        mse = np.mean(np.sum((z - zh) ** 2, axis=1))
+        h = np.pi / L
+        assert mse == pytest.approx(2 - 2 * np.sin(h) / h, rel=1e-6)
+
+
+def test_polar_scores_equal_dense_formula_and_qjl_unbiased():
+    """The polar score equals <q, n Pi^T (z_hat + rho sqrt(pi/2)/d G^T s)>
+    with explicit matrices (catches a transposed operand), the slot packing
+    round-trips, and the QJL term averaged over 6000 Gaussian G estimates
+    <q, Pi^T r> (zero bias) within 4 standard errors."""
+    from oracle import polar as PL
+    pp = PL.init_polar(16, 3, 4)
+    rs = np.random.default_rng(34)
+    keys = rs.standard_normal((9, 16)) * 2.0
+    q = rs.standard_normal((5, 16))
+    pq = PL.quantize(pp, keys)
+    s = PL.scores(pp, q, pq.codes, pq.beta, pq.norms, pq.rnorms)
+    sg = np.where(pq.beta, 1.0, -1.0)
+    kt = pq.norms[:, None] * ((pq.zhat + (pq.rnorms * tq.QJL_CONST / 16)[:, None] * (sg @ pp.g)) @ pp.pi)
+    assert np.allclose(s, q @ kt.T, rtol=1e-12, atol=1e-12)
+    sl = PL.slots(pq.codes)
+    assert sl.shape == (9, 16) and np.all(sl[:, 15] == 0)
+    assert all(np.array_equal(a, b) for a, b in zip(PL.unslot(sl, 16), pq.codes))
+    # zero bias of the QJL term over projections
+    u = keys[0] / np.linalg.norm(keys[0])
+    z = pp.pi @ u
+    ang, _ = PL.decompose(z[None, :])
+    r = z - PL.reconstruct(pp, PL.quantize_angles(pp, ang))[0]
+    v = pp.pi @ q[0]
+    est = []
+    for _ in range(6000):
+        g = rs.standard_normal((16, 16))
+        est.append(np.linalg.norm(r) * tq.QJL_CONST / 16 * (g @ v) @ np.where(g @ r > 0, 1.0, -1.0))
+    est = np.array(est)
+    assert abs(est.mean() - v @ r) < 4 * est.std() / np.sqrt(len(est))
+
+
+def test_compare_quantize_polar_rules():
+    """The polar rule passes the oracle's own packed output and rejects a
+    code changed far from its boundary, a flipped sign far from 0, a NaN
+    norm and a set unused slot; a code changed at an angle within 1e-6 of a
+    boundary passes when the key's signs and rho follow the changed code."""
+    from oracle import parity
+    from oracle import polar as PL
+    pp = PL.init_polar(32, 3, 6)
+    rs = np.random.default_rng(35)
+    keys = rs.standard_normal((3000, 32))
+    pq = PL.quantize(pp, keys)
+    codes = tq.pack_codes(PL.slots(pq.codes), 2)
+    signs = tq.pack_bits(pq.beta)
+    n32, r32 = pq.norms.astype(np.float32), pq.rnorms.astype(np.float32)
+    rep = parity.compare_quantize_polar(pp, pq, codes, signs, n32, r32)
+    assert rep.ok() and rep.code_mismatch == rep.sign_mismatch == 0, rep
+    dist = parity.polar_angle_distance(pp, pq.angles)
+    k, j = np.unravel_index(np.argmax(np.where(np.isfinite(dist), dist, -1)), dist.shape)
+    sl = PL.slots(pq.codes)
+    sl[k, j] = (sl[k, j] + 1) % 4
+    assert parity.compare_quantize_polar(pp, pq, tq.pack_codes(sl, 2), signs, n32, r32).code_bad == 1
+    beta = pq.beta.copy()
+    far = int(np.argmax(np.abs(pq.p[7])))
+    beta[7, far] = ~beta[7, far]
+    assert parity.compare_quantize_polar(pp, pq, codes, tq.pack_bits(beta), n32, r32).sign_bad == 1
+    bad = n32.copy()
+    bad[3] = np.nan
+    assert not parity.compare_quantize_polar(pp, pq, codes, signs, bad, r32).ok()
+    sl = PL.slots(pq.codes)
+    sl[5, 31] = 1
+    assert parity.compare_quantize_polar(pp, pq, tq.pack_codes(sl, 2), signs, n32, r32).padding_bad == 1
+    # an in-window change: plant an angle 3e-7 above a level-2 threshold
+    # through the inverse transform, flip its code to the lower cell and give
+    # the key the signs and rho of the changed code
+    z = pq.z[0].copy()
+    ang, r = PL.decompose(z[None, :])
+    t = pp.thresholds[1][1]
+    ang[1][0, 3] = t + 3e-7
+    key = PL.compose(ang, r)[0] @ pp.pi   # Pi^T z (Pi is orthogonal to 1e-7)
+    pq1 = PL.quantize(pp, key[None, :])
+    d1 = parity.polar_angle_distance(pp, pq1.angles)[0, 16 + 3]
+    assert d1 < 1e-6, d1
+    sl = PL.slots(pq1.codes)
+    sl[0, 16 + 3] -= 1
+    changed = PL.unslot(sl, 32)
+    zh = PL.reconstruct(pp, changed)
+    rr = pq1.z - zh
+    pv = rr @ pp.g.T
+    rep = parity.compare_quantize_polar(pp, pq1, tq.pack_codes(sl, 2), tq.pack_bits(pv.astype(np.float32) > 0),
+                                        pq1.norms.astype(np.float32),
+                                        np.sqrt(np.sum(rr * rr, axis=1)).astype(np.float32))
+    assert rep.code_mismatch == 1 and rep.code_bad == 0 and rep.sign_mismatch == 0 and rep.cascade_keys == 1
