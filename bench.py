@@ -50,6 +50,8 @@ def parse():
                     help="skip the fractional-width line (2.5 and 3.5 bits, general kernels)")
     ap.add_argument("--no-attention", action="store_true",
                     help="skip the decode-attention and uncompressed-logits measurement")
+    ap.add_argument("--no-general", action="store_true",
+                    help="skip the float32-key quantize line (cone, search, toy)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -264,10 +266,11 @@ def dequant_prod_leg(w, h, packed, out, stream, reps=10):
 def split_leg(w, keys, queries, scores, khat, seed, stream, reps=3):
     """Fractional widths (tq_init_split) on the step's keys and queries: the
     first d/2 rotated coordinates with one more index bit, 2.5 and 3.5 bits
-    per coordinate with the sign bit.  Per width: tq_quantize, tq_logits and
-    tq_dequant_mse (general float32 kernels: the matrix-core paths take one
-    width only), mean of `reps` calls after a warm-up, and the packed bytes
-    per key against the plain handles'."""
+    per coordinate with the sign bit.  Per width: tq_quantize (the general
+    matrix-core quantizer), tq_logits (the general float32 scorer: the
+    lookup-table scorer takes one width only) and tq_dequant_mse (matrix
+    cores), mean of `reps` calls after a warm-up, and the packed bytes per
+    key against the plain handles'."""
     import torch
 
     import vector_quantization_quantize_amd as tqm
@@ -362,6 +365,79 @@ def _host_cores():
         return len(os.sched_getaffinity(0))
     except AttributeError:
         return os.cpu_count() or 1
+
+
+def quantize_general_leg(seed, reps=5):
+    """tq_quantize on the float32-key workloads (the general matrix-core
+    quantizer: norms and key pieces, then Z = Pi K and P = G R as tiled
+    f16 matrix-core products with operands split into two pieces): cone
+    (1e6 x 1536, 4 bits), search_b2 / search_b4 (1e6 x 200) and toy.  Keys
+    are drawn on the device with the workload's law (the search and toy
+    generators' exact streams are not needed for timing).  Per workload:
+    ms per call (mean of `reps` after a warm-up), Mkeys/s, HBM GB/s of keys
+    in + packed out, useful matrix flops (4 d^2 per key) and raw matrix
+    flops (3 passes of 2 x 128-row tiles x K per product) against the bf16
+    matrix-core peak."""
+    import numpy as np
+    import torch
+
+    import vector_quantization_quantize_amd as tqm
+    from vector_quantization_quantize_amd import workloads as wl
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(2000 + seed)
+    res = {}
+    for name in ("cone", "search_b2", "search_b4", "toy"):
+        w = wl.WORKLOADS[name]
+        n, d = w.total_keys, w.d
+        if name == "cone":
+            mu, basis = wl._cone_frame(w, seed)
+            mu_t = torch.from_numpy(mu).float().cuda()
+            b_t = torch.from_numpy(basis).float().cuda()
+            keys = torch.empty((n, d), dtype=torch.float32, device="cuda")
+            for c0 in range(0, n, 1 << 16):
+                m = min(1 << 16, n - c0)
+                z = torch.randn((m, 64), generator=gen, device="cuda")
+                eps = 0.01 * torch.randn((m, d), generator=gen, device="cuda")
+                x = 0.87 * mu_t[None, :] + 0.49 * (z @ b_t.T / 8.0 + eps)
+                keys[c0:c0 + m] = x / x.norm(dim=1, keepdim=True)
+        elif name.startswith("search"):
+            scale = torch.arange(1, d + 1, device="cuda", dtype=torch.float32) ** -0.5
+            keys = torch.randn((n, d), generator=gen, device="cuda") * scale[None, :]
+            keys /= keys.norm(dim=1, keepdim=True)
+        else:
+            keys = torch.from_numpy(wl.keys(w, seed)).cuda()
+        h = tqm.tq_init(d, w.bits, 0)
+        out = tqm.empty_packed(h, n)
+        fn = lambda: tqm.tq_quantize(h, keys, out=out)
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        words = (d + 31) // 32
+        dpm = 32 * words
+        kp = (d + 15) // 16 * 16
+        nct = (dpm + 127) // 128
+        packed = 4 * (w.bits - 1) * words + 4 * words + 8
+        useful = 4.0 * d * d * n / (ms * 1e-3) / 1e12
+        raw = 3 * 2.0 * 128 * nct * (kp + dpm) * n / (ms * 1e-3) / 1e12
+        gbs = (4 * d + packed) * n / (ms * 1e-3) / 1e9
+        res[name] = {"keys": n, "d": d, "bits": w.bits, "ms": round(ms, 3), "Mkeys_per_s": round(n / ms / 1e3, 1),
+                     "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "useful_TFLOPs": round(useful, 1), "useful_mfma_frac": round(useful / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "raw_TFLOPs": round(raw, 1), "raw_mfma_frac": round(raw / BF16_MFMA_PEAK_TFLOPS, 4)}
+        tqm.tq_destroy(h)
+        del keys, out
+        torch.cuda.empty_cache()
+    c = res["cone"]
+    res["roofline_cone"] = {"bound": "mfma", "achieved": c["useful_TFLOPs"], "peak": BF16_MFMA_PEAK_TFLOPS,
+                            "unit": "TFLOP/s", "frac": c["useful_mfma_frac"], "raw_frac": c["raw_mfma_frac"],
+                            "note": "useful = 4 d^2 flops per key (the two projections); raw = the f16 passes run"}
+    return res
 
 
 def cpu_baseline(w, keys_np, queries_np, groups, seed, gpu_out):
@@ -606,6 +682,9 @@ def main():
         del keys, queries, packed, scores, ws, khat
         torch.cuda.empty_cache()
         line["search_topk"] = search_topk(args.search_workload, args.seed)
+    if not args.no_general:
+        torch.cuda.empty_cache()
+        line["quantize_general"] = quantize_general_leg(args.seed)
     print(json.dumps(line), flush=True)
 
 

@@ -7,7 +7,8 @@
 //   rho = ||r||, beta = [G r > 0], packed into bit planes.
 // Both projections are dense contractions over all keys, so they run as
 // tiled matrix products on the matrix cores:
-//   1. norms: n = ||k|| in float32, one wave per key (tree sum of squares).
+//   1. prep: n = ||k|| in float32 and the keys as float16 pieces of 2^s k
+//      (below), in the operand layout of step 2.
 //   2. rotate: Z = (2^12 Pi) (2^s K) for tiles of 128 output coordinates x
 //      128 keys, then per element: bucketize, the code bits, r = z - c[idx]
 //      and rho^2 (partial sums per coordinate tile).  r goes to a scratch
@@ -31,16 +32,17 @@
 //     z by about 2^-24 sqrt(d / 16) |z|, and G amplifies an error in r by
 //     about sqrt(d) in p, more than the 1e-6 decision window on p.
 //
-// Work split of a block (8 waves, one tile of 128 coordinates x 128 keys):
+// Work split of a block (8 waves, tiles of 128 coordinates x 128 keys):
 // waves 0-3 multiply (wave (wm, wn): 64 x 64, 2 x 2 tiles of 32 x 32),
-// waves 4-7 load and stage the next K step into LDS (double-buffered, loads
-// issued six steps ahead in six named register slots).  The operand tiles
+// waves 4-7 load and stage K steps into a ring of three LDS buffers (loads
+// issued eight steps ahead in six named register slots); one block per CU
+// walks a run of tiles.  The operand tiles
 // of Pi and G are built once by tq_init with their rows permuted inside each
 // 32-row tile so that accumulator element e of lane l is output coordinate
 // 16 (l / 32) + e of the tile: a lane's 16 decisions of one bit word are
 // contiguous, and one exchange with lane l ^ 32 completes the word.
-// Keys are processed in chunks whose residual pieces fit the handle's
-// scratch (at most 256 MB).
+// Keys are processed in chunks whose key and residual pieces fit the
+// handle's scratch (at most 256 MB): prep, rotate, project per chunk.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -54,42 +56,26 @@ namespace tqdev {
 namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 128;          // output coordinates per block tile
 constexpr int kBN = 128;          // keys per block tile
-constexpr int kRow = 24;          // staged row: 16 halves + 8 pad (conflict-free 16-byte reads)
+// Staged operand of one K step: two planes (hi, lo pieces) of 128 rows x 16
+// halves; a row's two 16-byte units are swapped in rows 4-7 of every 8
+// (XOR with bit 2 of the row), and plane 1 starts 64 bytes past a multiple
+// of 128 bytes.  Then the 8 lanes that share an LDS cycle hit 8 distinct
+// 16-byte bank groups both when the multiplying waves read 8 consecutive
+// rows of one unit and when the staging waves write 2 rows x 2 units x 2
+// planes (2-way conflicts with the padded layout this replaced).
+constexpr int kPlaneH = kBM * 16 + 32;  // halves per plane (4096 + 64 bytes)
 constexpr int kThreads = 512;     // 4 multiplying + 4 staging waves
 constexpr int kChunkSteps = 8;    // K steps per fresh accumulator (rotation)
 constexpr int kStepHalves = kBM * 2 * 16;  // one K step of an operand tile: [row][piece][16]
 constexpr size_t kScratchBudget = size_t(256) << 20;
+constexpr int kMaxCoordTiles = 4096 / kBM;  // d <= 4096
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t u) { return __uint_as_float(uint32_t(u) << 16); }
-
-// ---------------------------------------------------------------------------
-// 1. norms
-// ---------------------------------------------------------------------------
-template <int KT>
-__global__ void __launch_bounds__(256)
-qg_norm_kernel(const void* __restrict__ keys, int64_t n, int64_t ldk, int d, float* __restrict__ norms) {
-  const int64_t key = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (key >= n) return;
-  float ss = 0.0f;
-  if constexpr (KT == TQ_F32) {
-    const float* row = static_cast<const float*>(keys) + key * ldk;
-    for (int i = lane; i < d; i += 64) ss = fmaf(row[i], row[i], ss);
-  } else {
-    const uint16_t* row = static_cast<const uint16_t*>(keys) + key * ldk;
-    for (int i = lane; i < d; i += 64) {
-      const float x = bf16_to_f32(row[i]);
-      ss = fmaf(x, x, ss);
-    }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-  if (lane == 0) norms[key] = sqrtf(ss);
-}
 
 // the power of two 2^s with 2^s n in [2^13, 2^14) (1 for n = 0)
 __device__ __forceinline__ float key_scale(float nk) {
@@ -98,6 +84,112 @@ __device__ __forceinline__ float key_scale(float nk) {
   (void)frexpf(nk, &e);
   return ldexpf(1.0f, 14 - e);
 }
+
+// ---------------------------------------------------------------------------
+// 1. prep: per tile of 128 keys, the norms (float32, a fixed order: each
+// thread's elements in sequence, then a tree over the 4 (float32) or 2
+// (bfloat16) threads of a key) and the keys scaled by 2^s and split into two
+// float16 pieces, written in the rotation's operand layout
+// [key tile][K step][key 128][piece 2][16].  Float32 keys: chunk c in
+// {t, t + 256} is elements 4 (c % 4) .. + 3 of each K step of key c / 4;
+// bfloat16 keys: thread t takes elements 8 (t % 2) .. + 7 of key t / 2.
+// Either way 4 (2) lanes read 64 (32) contiguous bytes of a row.
+// ---------------------------------------------------------------------------
+template <int KT>
+__global__ void __launch_bounds__(256)
+qg_prep_kernel(const void* __restrict__ keys, int64_t nkeys, int64_t ldk, int d, int ks, int vec_ok,
+               float* __restrict__ norms, uint16_t* __restrict__ kpc) {
+  constexpr int kPer = KT == TQ_F32 ? 2 : 1;  // chunks per thread
+  constexpr int kElems = KT == TQ_F32 ? 4 : 8;  // elements per chunk
+  constexpr int kParts = 16 / kElems;  // chunks per key and K step
+  const int t = threadIdx.x;
+  const int64_t kt = blockIdx.x;
+  int64_t key[kPer];
+  int part[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int c = t + 256 * i;
+    int64_t k = kt * kBN + c / kParts;
+    key[i] = k < nkeys ? k : nkeys - 1;
+    part[i] = c % kParts;
+  }
+  auto load = [&](int i, int s, float (&x)[kElems]) __attribute__((always_inline)) {
+    const int k0 = 16 * s + kElems * part[i];
+    if constexpr (KT == TQ_F32) {
+      const float* row = static_cast<const float*>(keys) + key[i] * ldk;
+      if (vec_ok && k0 + 4 <= d) {
+        const float4 v = *reinterpret_cast<const float4*>(row + k0);
+        x[0] = v.x;
+        x[1] = v.y;
+        x[2] = v.z;
+        x[3] = v.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = k0 + e < d ? row[k0 + e] : 0.0f;
+      }
+    } else {
+      const uint16_t* row = static_cast<const uint16_t*>(keys) + key[i] * ldk;
+      if (vec_ok && k0 + 8 <= d) {
+        const uint4 v = *reinterpret_cast<const uint4*>(row + k0);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[2 * e] = bf16_to_f32(uint16_t(w[e] & 0xFFFFu));
+          x[2 * e + 1] = bf16_to_f32(uint16_t(w[e] >> 16));
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = k0 + e < d ? bf16_to_f32(row[k0 + e]) : 0.0f;
+      }
+    }
+  };
+  float ss[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) ss[i] = 0.0f;
+  for (int s = 0; s < ks; ++s) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      float x[kElems];
+      load(i, s, x);
+#pragma unroll
+      for (int e = 0; e < kElems; ++e) ss[i] = fmaf(x[e], x[e], ss[i]);
+    }
+  }
+  float scale[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+#pragma unroll
+    for (int o = 1; o < kParts; o <<= 1) ss[i] += __shfl_xor(ss[i], o);
+    const float nk = sqrtf(ss[i]);
+    const int64_t k = kt * kBN + (t + 256 * i) / kParts;
+    if (part[i] == 0 && k < nkeys) norms[k] = nk;
+    scale[i] = key_scale(nk);
+  }
+  for (int s = 0; s < ks; ++s) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      float x[kElems];
+      load(i, s, x);
+      _Float16 hi[kElems], lo[kElems];
+#pragma unroll
+      for (int e = 0; e < kElems; ++e) {
+        const float v = x[e] * scale[i];
+        hi[e] = static_cast<_Float16>(v);
+        lo[e] = static_cast<_Float16>(v - static_cast<float>(hi[e]));
+      }
+      _Float16* dst = reinterpret_cast<_Float16*>(kpc) + ((kt * ks + s) * kBN + (t + 256 * i) / kParts) * 32 +
+                      kElems * part[i];
+      if constexpr (KT == TQ_F32) {
+        *reinterpret_cast<f16x4*>(dst) = f16x4{hi[0], hi[1], hi[2], hi[3]};
+        *reinterpret_cast<f16x4*>(dst + 16) = f16x4{lo[0], lo[1], lo[2], lo[3]};
+      } else {
+        *reinterpret_cast<f16x8*>(dst) = f16x8{hi[0], hi[1], hi[2], hi[3], hi[4], hi[5], hi[6], hi[7]};
+        *reinterpret_cast<f16x8*>(dst + 16) = f16x8{lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]};
+      }
+    }
+  }
+}
+
 
 // two float16 pieces of 8 floats: hi = f16(x), lo = f16(x - hi)
 __device__ __forceinline__ void split8(const float (&x)[8], f16x8& hi, f16x8& lo) {
@@ -116,6 +208,9 @@ struct Slot {
   uint4 a0, a1, b0, b1;
 };
 
+// halves offset of 16-byte unit u (0, 1) of row r within a plane
+__device__ __forceinline__ int unit_off(int r, int u) { return 16 * r + 8 * (u ^ ((r >> 2) & 1)); }
+
 struct Levels {
   float t[kMaxLevels];   // thresholds, ascending (L - 1 used)
   float c[kMaxLevels];   // levels, ascending
@@ -123,20 +218,19 @@ struct Levels {
 };
 
 // ---------------------------------------------------------------------------
-// 2. / 3. the tiled products.  MODE 0: rotate + bucketize; MODE 1: project +
-// signs.  KT: key type (rotation only).
+// 2. / 3. the tiled products.  MODE 0: rotate + bucketize (B operand: the
+// key pieces); MODE 1: project + signs (B operand: the residual pieces).
 // ---------------------------------------------------------------------------
 struct QArgs {
   const uint16_t* atiles;  // operand tiles of this matrix
   int ks;                  // K steps of this product
-  const void* keys;        // rotation: the chunk's keys
-  int64_t ldk;
-  int vec_ok;              // rotation: rows 16-byte aligned (whole 8-element loads allowed)
+  const uint16_t* bsrc;    // B operand pieces [key tile][K step][key 128][piece 2][16]
   int d, dpm, nct, ks2;    // dimension, coordinates padded to 32, coordinate tiles, residual K steps
   const float* norms;      // the chunk's norms
   int64_t nkeys;           // keys in the chunk
   uint16_t* rp;            // residual pieces [key tile][step ks2][key 128][piece 2][16]
-  float* part;             // rho^2 partials [key][nct]
+  float* part;             // rho^2 partials [key][nct][row half]
+  int64_t items, tiles;    // (key tile, coordinate tile) items of the launch; key tiles
   uint32_t* codes;         // the chunk's code rows
   int code_row, B, W, hi, hi_words;
   uint32_t* signs;         // the chunk's sign rows
@@ -144,279 +238,268 @@ struct QArgs {
   Levels base, fine;       // level sets (fine: coordinates below hi)
 };
 
-template <int MODE, int KT>
+// Work items are (key tile, coordinate tile) pairs, key tile fastest, and
+// block b takes items b, b + B, b + 2B, ... (B blocks): at any time every
+// block works on the same coordinate tile, whose operand rows (128 x d x 4
+// bytes) then stay in each XCD's L2 instead of all coordinate tiles
+// streaming from the MALL.  A step is one K step of one item; the block's steps run back to back, so the staging
+// waves load the next item's operands while the multiplying waves finish
+// the current one.  LDS holds three staged steps: at iteration it the
+// multiplying waves read step it + 1's fragments from LDS while the matrix
+// cores work on step it, and the staging waves fill step it + 2; one barrier
+// per step.
+// NB: code bits of the handle (rotation; 0 for the projection)
+template <int MODE, int NB>
 __global__ void __launch_bounds__(kThreads, 1) qgemm_kernel(QArgs a) {
-  __shared__ __align__(16) _Float16 sA[2][2 * kBM * kRow];  // [buf][piece][row][kRow]
-  __shared__ __align__(16) _Float16 sB[2][2 * kBN * kRow];  // [buf][piece][key][kRow]
-  __shared__ float red[2][kBN];                               // rho^2 of each multiplying row half
-  __shared__ float lv_t[2][kMaxLevels], lv_c[2][kMaxLevels];
+  __shared__ __align__(16) _Float16 sA[3][2 * kPlaneH];  // [buf][piece plane][row][16], swizzled
+  __shared__ __align__(16) _Float16 sB[3][2 * kPlaneH];  // [buf][piece plane][key][16], swizzled
+  __shared__ float lv_c[2][kMaxLevels];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, kl = lane & 31, g = lane >> 5;
   const bool producer = w >= 4;
   const int wm = w & 1, wn = (w >> 1) & 1, pt = tid - 256;
-  const int64_t kt = blockIdx.x;
-  const int ct = blockIdx.y;
   const int ks = a.ks;
+  // this block's items: blockIdx.x + j * gridDim.x, j < my_items
+  const int64_t nb = gridDim.x;
+  const int64_t my_items = a.items > blockIdx.x ? (a.items - blockIdx.x + nb - 1) / nb : 0;
+  const int64_t steps = my_items * ks;
   if (tid < kMaxLevels) {
-    lv_t[0][tid] = a.base.t[tid];
     lv_c[0][tid] = a.base.c[tid];
-    lv_t[1][tid] = a.fine.t[tid];
     lv_c[1][tid] = a.fine.c[tid];
   }
 
-  const uint16_t* atile = a.atiles + int64_t(ct) * ks * kStepHalves;
-  const uint16_t* btile = a.rp + kt * int64_t(a.ks2) * kStepHalves;  // projection's B operand
-
-  // ---- staging role ----
-  // A (and the projection's B): chunk c in {pt, pt + 256} of a step's 512
-  // 16-byte chunks is (row c / 4, piece (c / 2) % 2, half c % 2).
-  // The rotation's B: thread pt takes key pt % 128, elements 8 (pt / 128)
-  // .. + 7 of the step.
-  const int skey = pt & (kBN - 1), sh8 = pt >> 7;
-  int64_t gkey = kt * kBN + skey;
-  gkey = gkey < a.nkeys ? gkey : a.nkeys - 1;
-  float kscale = 1.0f;
-  if (MODE == 0 && producer) kscale = key_scale(a.norms[gkey]);
-  int f_s = 0;  // next step to fetch
-  auto fetch = [&]() __attribute__((always_inline)) {
-    const int s = f_s < ks ? f_s : ks - 1;  // past the last step: a valid address, unused data
-    ++f_s;
-    Slot sl;
-    const uint4* ap = reinterpret_cast<const uint4*>(atile + int64_t(s) * kStepHalves);
-    sl.a0 = ap[pt];
-    sl.a1 = ap[pt + 256];
-    if constexpr (MODE == 1) {
-      const uint4* bp = reinterpret_cast<const uint4*>(btile + int64_t(s) * kStepHalves);
+  if (producer) {
+    // chunk c in {pt, pt + 256} of a step's 512 16-byte chunks (of either
+    // operand) is (row c / 4, piece (c / 2) % 2, half c % 2)
+    int64_t f_j = 0;  // item (as its j) and step of the next step to fetch
+    int f_s = 0;
+    auto fetch = [&]() __attribute__((always_inline)) {
+      // past the block's last step: the last step again (valid addresses, unused data)
+      const int64_t j = f_j < my_items ? f_j : my_items - 1;
+      const int s = f_j < my_items ? f_s : ks - 1;
+      if (++f_s == ks) {
+        f_s = 0;
+        ++f_j;
+      }
+      const int64_t it = blockIdx.x + j * nb;
+      const int ct = int(it / a.tiles);
+      const int64_t kt = it - int64_t(ct) * a.tiles;
+      Slot sl;
+      const uint4* ap = reinterpret_cast<const uint4*>(a.atiles + (int64_t(ct) * ks + s) * kStepHalves);
+      sl.a0 = ap[pt];
+      sl.a1 = ap[pt + 256];
+      const uint4* bp = reinterpret_cast<const uint4*>(a.bsrc + (kt * ks + s) * kStepHalves);
       sl.b0 = bp[pt];
       sl.b1 = bp[pt + 256];
-    } else {
-      const int k0 = 16 * s + 8 * sh8;
-      if constexpr (KT == TQ_F32) {
-        const float* row = static_cast<const float*>(a.keys) + gkey * a.ldk;
-        if (a.vec_ok && k0 + 8 <= a.d) {
-          sl.b0 = *reinterpret_cast<const uint4*>(row + k0);
-          sl.b1 = *reinterpret_cast<const uint4*>(row + k0 + 4);
-        } else {
-          uint32_t v[8];
+      return sl;
+    };
+    auto stage = [&](int buf, const Slot& sl) __attribute__((always_inline)) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = k0 + e < a.d ? __float_as_uint(row[k0 + e]) : 0u;
-          sl.b0 = uint4{v[0], v[1], v[2], v[3]};
-          sl.b1 = uint4{v[4], v[5], v[6], v[7]};
-        }
-      } else {
-        const uint16_t* row = static_cast<const uint16_t*>(a.keys) + gkey * a.ldk;
-        if (a.vec_ok && k0 + 8 <= a.d) {
-          sl.b0 = *reinterpret_cast<const uint4*>(row + k0);
-        } else {
-          uint32_t v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t lo = k0 + 2 * e < a.d ? row[k0 + 2 * e] : 0u;
-            const uint32_t hi = k0 + 2 * e + 1 < a.d ? row[k0 + 2 * e + 1] : 0u;
-            v[e] = lo | (hi << 16);
-          }
-          sl.b0 = uint4{v[0], v[1], v[2], v[3]};
-        }
-        sl.b1 = uint4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < 2; ++i) {
+        const int c = pt + 256 * i, row = c >> 2, piece = (c >> 1) & 1, half = c & 1;
+        const int off = piece * kPlaneH + unit_off(row, half);
+        *reinterpret_cast<uint4*>(&sA[buf][off]) = i == 0 ? sl.a0 : sl.a1;
+        *reinterpret_cast<uint4*>(&sB[buf][off]) = i == 0 ? sl.b0 : sl.b1;
       }
+    };
+    Slot pa0 = fetch(), pa1 = fetch(), pa2 = fetch(), pa3 = fetch(), pa4 = fetch(), pa5 = fetch();
+    if (steps > 0) {
+      stage(0, pa0);
+      pa0 = fetch();  // step 6
+      stage(1, pa1);
+      pa1 = fetch();  // step 7
     }
-    return sl;
-  };
-  auto stage = [&](int buf, const Slot& sl) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = pt + 256 * i, row = c >> 2, piece = (c >> 1) & 1, half = c & 1;
-      const int off = piece * kBM * kRow + row * kRow + 8 * half;
-      *reinterpret_cast<uint4*>(&sA[buf][off]) = i == 0 ? sl.a0 : sl.a1;
-      if constexpr (MODE == 1) *reinterpret_cast<uint4*>(&sB[buf][off]) = i == 0 ? sl.b0 : sl.b1;
+    __syncthreads();
+    // iteration it stages step it + 2 (slot (it + 2) % 6) into buffer
+    // (it + 2) % 3, then fetches step it + 8 into that slot
+#define TQ_QG_STEP(D, SLOT)                        \
+  if (it0 + (D) < steps) {                         \
+    stage(int((it0 + (D) + 2) % 3), SLOT);         \
+    SLOT = fetch();                                \
+    __syncthreads();                               \
+  }
+    for (int64_t it0 = 0; it0 < steps; it0 += 6) {
+      TQ_QG_STEP(0, pa2)
+      TQ_QG_STEP(1, pa3)
+      TQ_QG_STEP(2, pa4)
+      TQ_QG_STEP(3, pa5)
+      TQ_QG_STEP(4, pa0)
+      TQ_QG_STEP(5, pa1)
     }
-    if constexpr (MODE == 0) {
-      float x[8];
-      if constexpr (KT == TQ_F32) {
-        const uint32_t v[8] = {sl.b0.x, sl.b0.y, sl.b0.z, sl.b0.w, sl.b1.x, sl.b1.y, sl.b1.z, sl.b1.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = __uint_as_float(v[e]) * kscale;
-      } else {
-        const uint32_t v[4] = {sl.b0.x, sl.b0.y, sl.b0.z, sl.b0.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[2 * e] = bf16_to_f32(uint16_t(v[e] & 0xFFFFu)) * kscale;
-          x[2 * e + 1] = bf16_to_f32(uint16_t(v[e] >> 16)) * kscale;
-        }
-      }
-      f16x8 hi, lo;
-      split8(x, hi, lo);
-      const int off = skey * kRow + 8 * sh8;
-      *reinterpret_cast<f16x8*>(&sB[buf][off]) = hi;
-      *reinterpret_cast<f16x8*>(&sB[buf][kBN * kRow + off]) = lo;
-    }
-  };
+#undef TQ_QG_STEP
+    return;
+  }
 
-  // ---- multiplying role ----
+  // ---- multiplying waves ----
   f32x16 acc[2][2], run[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = run[i][j] = f32x16{};
-
-  if (producer) {
-    Slot pa0 = fetch(), pa1 = fetch(), pa2 = fetch(), pa3 = fetch(), pa4 = fetch(), pa5 = fetch();
-    stage(0, pa0);
-    pa0 = fetch();
-    __syncthreads();
-    // iteration it stages step it + 1 (slot (it + 1) % 6) into buffer
-    // (it + 1) % 2, then fetches step it + 7 into that slot
-#define TQ_QG_STEP(D, PAR, SLOT) \
-  if (it0 + (D) < ks) {          \
-    stage(PAR, SLOT);            \
-    SLOT = fetch();              \
-    __syncthreads();             \
-  }
-    for (int it0 = 0; it0 < ks; it0 += 6) {
-      TQ_QG_STEP(0, 1, pa1)
-      TQ_QG_STEP(1, 0, pa2)
-      TQ_QG_STEP(2, 1, pa3)
-      TQ_QG_STEP(3, 0, pa4)
-      TQ_QG_STEP(4, 1, pa5)
-      TQ_QG_STEP(5, 0, pa0)
-    }
-#undef TQ_QG_STEP
-  } else {
-    __syncthreads();
-    for (int it = 0; it < ks; ++it) {
-      const _Float16* sa = sA[it & 1];
-      const _Float16* sb = sB[it & 1];
-      f16x8 ah[2], al[2], bh[2], bl[2];
+  struct Frags {
+    f16x8 ah[2], al[2], bh[2], bl[2];
+  };
+  auto read_frags = [&](int buf) __attribute__((always_inline)) {
+    Frags f;
+    const _Float16* sa = sA[buf];
+    const _Float16* sb = sB[buf];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int off = (64 * wm + 32 * i + kl) * kRow + 8 * g;
-        ah[i] = *reinterpret_cast<const f16x8*>(sa + off);
-        al[i] = *reinterpret_cast<const f16x8*>(sa + kBM * kRow + off);
-      }
+    for (int i = 0; i < 2; ++i) {
+      const int off = unit_off(64 * wm + 32 * i + kl, g);
+      f.ah[i] = *reinterpret_cast<const f16x8*>(sa + off);
+      f.al[i] = *reinterpret_cast<const f16x8*>(sa + kPlaneH + off);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int off = unit_off(64 * wn + 32 * j + kl, g);
+      f.bh[j] = *reinterpret_cast<const f16x8*>(sb + off);
+      f.bl[j] = *reinterpret_cast<const f16x8*>(sb + kPlaneH + off);
+    }
+    return f;
+  };
+  __syncthreads();
+  Frags cur = read_frags(0);
+  int64_t m_item = blockIdx.x;
+  int m_s = 0;
+  for (int64_t it = 0; it < steps; ++it) {
+    Frags nxt = cur;
+    if (it + 1 < steps) nxt = read_frags(int((it + 1) % 3));
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int off = (64 * wn + 32 * j + kl) * kRow + 8 * g;
-        bh[j] = *reinterpret_cast<const f16x8*>(sb + off);
-        bl[j] = *reinterpret_cast<const f16x8*>(sb + kBN * kRow + off);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.ah[i], cur.bh[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.ah[i], cur.bl[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.al[i], cur.bh[j], acc[i][j], 0, 0, 0);
+      }
+    ++m_s;
+    if constexpr (MODE == 0) {
+      if (m_s % kChunkSteps == 0 || m_s == ks) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            run[i][j] += acc[i][j];
+            acc[i][j] = f32x16{};
+          }
+      }
+    }
+    if (m_s == ks) {
+      // the item's epilogue: element e of tile (i, j) is coordinate
+      // c0(i) + 16 g + e, key 64 wn + 32 j + kl of the key tile
+      const int ct = int(m_item / a.tiles);
+      const int64_t kt = m_item - int64_t(ct) * a.tiles;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int tkey = 64 * wn + 32 * j + kl;
+        int64_t key = kt * kBN + tkey;
+        const bool kin = key < a.nkeys;
+        key = kin ? key : a.nkeys - 1;
+        float rho2 = 0.0f;
+        float inv = 0.0f;
+        if constexpr (MODE == 0) {
+          const float nk = a.norms[key];
+          inv = nk > 0.0f ? 1.0f / (4096.0f * key_scale(nk) * nk) : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int c0 = ct * kBM + 64 * wm + 32 * i;
+          if (c0 >= a.dpm) continue;  // padding rows of the last coordinate tile (wave-uniform)
+          const int word = c0 >> 5;
+          uint32_t hw[6] = {0u, 0u, 0u, 0u, 0u, 0u};  // bit planes 0..B of the index (B + 1 <= 5), or the signs
+          if constexpr (MODE == 0) {
+            const f32x16 tot = run[i][j];
+            const bool fine_here = c0 < a.hi;
+            f16x8 rh[2], rl[2];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int coord = c0 + 16 * g + e;
+              const bool valid = coord < a.d;
+              const float z = tot[e] * inv;
+              // idx = #{t_i <= z}: compares against the thresholds (kernel
+              // arguments, uniform), no dependent lookups
+              int idx = 0;
+#pragma unroll
+              for (int q = 0; q + 1 < (1 << NB); ++q) idx += z >= a.base.t[q] ? 1 : 0;
+              int set = 0;
+              if constexpr (NB < 4) {  // fractional widths take B <= 3
+                if (fine_here) {       // the word has coordinates below hi (wave-uniform)
+                  int idf = 0;
+#pragma unroll
+                  for (int q = 0; q + 1 < (2 << NB); ++q) idf += z >= a.fine.t[q] ? 1 : 0;
+                  set = coord < a.hi ? 1 : 0;
+                  idx = set ? idf : idx;
+                }
+              }
+              const float r = valid ? z - lv_c[set][idx] : 0.0f;
+              idx = valid ? idx : 0;
+#pragma unroll
+              for (int p = 0; p < 6; ++p) hw[p] |= uint32_t((idx >> p) & 1) << e;
+              rho2 = fmaf(r, r, rho2);
+              const float r2 = r * 4096.0f;
+              const _Float16 h = static_cast<_Float16>(r2);
+              rh[e >> 3][e & 7] = h;
+              rl[e >> 3][e & 7] = static_cast<_Float16>(r2 - static_cast<float>(h));
+            }
+            // residual pieces: step (c0 + 16 g) / 16 of the projection's K
+            const int s2 = (c0 + 16 * g) >> 4;
+            _Float16* dst = reinterpret_cast<_Float16*>(a.rp) + ((kt * a.ks2 + s2) * kBN + tkey) * 32;
+            *reinterpret_cast<f16x8*>(dst) = rh[0];
+            *reinterpret_cast<f16x8*>(dst + 8) = rh[1];
+            *reinterpret_cast<f16x8*>(dst + 16) = rl[0];
+            *reinterpret_cast<f16x8*>(dst + 24) = rl[1];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int coord = c0 + 16 * g + e;
+              hw[0] |= uint32_t(coord < a.d && acc[i][j][e] > 0.0f) << e;
+            }
+          }
+          // the other 16 decisions of the word are in lane l ^ 32
+          uint32_t full[6];
+#pragma unroll
+          for (int p = 0; p < 6; ++p) {
+            const uint32_t other = __shfl_xor(hw[p], 32);
+            full[p] = g == 0 ? (hw[p] | (other << 16)) : 0u;
+          }
+          if (g == 0 && kin && word < a.W) {
+            if constexpr (MODE == 0) {
+              uint32_t* crow = a.codes + key * a.code_row;
+              for (int p = 0; p < a.B; ++p) crow[p * a.W + word] = full[p];
+              if (a.hi > 0 && word < a.hi_words) crow[a.B * a.W + word] = full[a.B];
+            } else {
+              a.signs[key * a.W + word] = full[0];
+            }
+          }
+        }
+        if constexpr (MODE == 0) {
+          rho2 += __shfl_xor(rho2, 32);
+          // this wave's half of the item's rows
+          if (g == 0 && kin) a.part[(key * a.nct + ct) * 2 + wm] = rho2;
+        } else {
+          // rho from the partials (fixed order), once per key
+          if (ct == 0 && wm == 0 && g == 0 && kin) {
+            // all loads first (one round trip), then the sum in order
+            const float* pp = a.part + key * 2 * a.nct;
+            float v[2 * kMaxCoordTiles];
+#pragma unroll
+            for (int c = 0; c < 2 * kMaxCoordTiles; ++c) v[c] = c < 2 * a.nct ? pp[c] : 0.0f;
+            float s2 = 0.0f;
+#pragma unroll
+            for (int c = 0; c < 2 * kMaxCoordTiles; ++c) s2 += v[c];
+            a.rnorms[key] = sqrtf(s2);
+          }
+        }
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[i], bh[j], acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[i], bl[j], acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[i], bh[j], acc[i][j], 0, 0, 0);
-        }
-      if constexpr (MODE == 0) {
-        if ((it + 1) % kChunkSteps == 0) {
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              run[i][j] += acc[i][j];
-              acc[i][j] = f32x16{};
-            }
-        }
-      }
-      __syncthreads();
+        for (int j = 0; j < 2; ++j) acc[i][j] = run[i][j] = f32x16{};
+      m_s = 0;
+      m_item += nb;
     }
-  }
-
-  // ---- epilogue (multiplying waves; every thread meets the barriers) ----
-  // element e of tile (i, j): coordinate c0(i) + 16 g + e, key 64 wn + 32 j + kl
-  if (!producer) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int tkey = 64 * wn + 32 * j + kl;
-      int64_t key = kt * kBN + tkey;
-      const bool kin = key < a.nkeys;
-      key = kin ? key : a.nkeys - 1;
-      float rho2 = 0.0f;
-      float inv = 0.0f;
-      if constexpr (MODE == 0) {
-        const float nk = a.norms[key];
-        inv = nk > 0.0f ? 1.0f / (4096.0f * key_scale(nk) * nk) : 0.0f;
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int c0 = ct * kBM + 64 * wm + 32 * i;
-        if (c0 >= a.dpm) continue;  // padding rows of the last coordinate tile (wave-uniform)
-        const int word = c0 >> 5;
-        uint32_t hw[6] = {0u, 0u, 0u, 0u, 0u, 0u};  // bit planes 0..B of the index (B + 1 <= 5), or the signs
-        if constexpr (MODE == 0) {
-          const f32x16 tot = run[i][j] + acc[i][j];
-          f16x8 rh[2], rl[2];
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int coord = c0 + 16 * g + e;
-            const bool valid = coord < a.d;
-            const int set = coord < a.hi ? 1 : 0;
-            const int bits = set ? a.fine.bits : a.base.bits;
-            const float z = tot[e] * inv;
-            int idx = 0;
-            for (int st = (1 << bits) >> 1; st > 0; st >>= 1) idx += z >= lv_t[set][idx + st - 1] ? st : 0;
-            const float r = valid ? z - lv_c[set][idx] : 0.0f;
-            idx = valid ? idx : 0;
-#pragma unroll
-            for (int p = 0; p < 6; ++p) hw[p] |= uint32_t((idx >> p) & 1) << e;
-            rho2 = fmaf(r, r, rho2);
-            const float r2 = r * 4096.0f;
-            const _Float16 h = static_cast<_Float16>(r2);
-            rh[e >> 3][e & 7] = h;
-            rl[e >> 3][e & 7] = static_cast<_Float16>(r2 - static_cast<float>(h));
-          }
-          // residual pieces: step (c0 + 16 g) / 16 of the projection's K
-          const int s2 = (c0 + 16 * g) >> 4;
-          _Float16* dst = reinterpret_cast<_Float16*>(a.rp) + ((kt * a.ks2 + s2) * kBN + tkey) * 32;
-          *reinterpret_cast<f16x8*>(dst) = rh[0];
-          *reinterpret_cast<f16x8*>(dst + 8) = rh[1];
-          *reinterpret_cast<f16x8*>(dst + 16) = rl[0];
-          *reinterpret_cast<f16x8*>(dst + 24) = rl[1];
-        } else {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int coord = c0 + 16 * g + e;
-            hw[0] |= uint32_t(coord < a.d && acc[i][j][e] > 0.0f) << e;
-          }
-        }
-        // the other 16 decisions of the word are in lane l ^ 32
-        uint32_t full[6];
-#pragma unroll
-        for (int p = 0; p < 6; ++p) {
-          const uint32_t other = __shfl_xor(hw[p], 32);
-          full[p] = g == 0 ? (hw[p] | (other << 16)) : 0u;
-        }
-        if (g == 0 && kin && word < a.W) {
-          if constexpr (MODE == 0) {
-            uint32_t* crow = a.codes + key * a.code_row;
-            for (int p = 0; p < a.B; ++p) crow[p * a.W + word] = full[p];
-            if (a.hi > 0 && word < a.hi_words) crow[a.B * a.W + word] = full[a.B];
-          } else {
-            a.signs[key * a.W + word] = full[0];
-          }
-        }
-      }
-      if constexpr (MODE == 0) {
-        rho2 += __shfl_xor(rho2, 32);
-        if (g == 0) red[wm][tkey] = rho2;
-      }
-    }
-  }
-  if constexpr (MODE == 0) {
+    cur = nxt;
     __syncthreads();
-    if (tid < kBN) {
-      const int64_t key = kt * kBN + tid;
-      if (key < a.nkeys) a.part[key * a.nct + ct] = red[0][tid] + red[1][tid];
-    }
-  } else {
-    if (ct == 0 && tid < kBN) {
-      const int64_t key = kt * kBN + tid;
-      if (key < a.nkeys) {
-        float s = 0.0f;
-        for (int c = 0; c < a.nct; ++c) s += a.part[key * a.nct + c];
-        a.rnorms[key] = sqrtf(s);
-      }
-    }
   }
 }
 
@@ -526,24 +609,15 @@ hipError_t launch_quantize_gemm(tq_ctx* h, const void* keys, int key_dtype, int6
                                 uint32_t* signs, float* norms, float* rnorms, hipStream_t stream) {
   const Shape s = shape_of(h);
   const int d = h->d;
-  // norms of every key
-  {
-    const int64_t blocks = (n + 3) / 4;
-    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    if (key_dtype == TQ_F32)
-      hipLaunchKernelGGL(qg_norm_kernel<TQ_F32>, dim3(uint32_t(blocks)), dim3(256), 0, stream, keys, n, ldk, d, norms);
-    else
-      hipLaunchKernelGGL(qg_norm_kernel<TQ_BF16>, dim3(uint32_t(blocks)), dim3(256), 0, stream, keys, n, ldk, d, norms);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  // the chunk of keys whose residual pieces and partials fit the scratch
-  const size_t per_key = size_t(s.dpm) * 4 + size_t(s.nct) * 4;
+  // the chunk of keys whose key pieces, residual pieces and rho^2 partials
+  // fit the scratch
+  const size_t per_key = size_t(s.kp) * 4 + size_t(s.dpm) * 4 + size_t(s.nct) * 8;
   int64_t max_chunk = int64_t(kScratchBudget / per_key) / kBN * kBN;
   max_chunk = std::max<int64_t>(max_chunk, kBN);
   const int64_t chunk = std::min<int64_t>(max_chunk, (n + kBN - 1) / kBN * kBN);
+  const size_t kp_bytes = (size_t(chunk) * s.kp * 4 + 255) / 256 * 256;
   const size_t rp_bytes = (size_t(chunk) * s.dpm * 4 + 255) / 256 * 256;
-  const size_t need = rp_bytes + size_t(chunk) * s.nct * 4;
+  const size_t need = kp_bytes + rp_bytes + size_t(chunk) * s.nct * 8;
 
   std::lock_guard<std::mutex> lock(h->qscratch_mu);
   if (!h->qscratch_done && hipEventCreateWithFlags(&h->qscratch_done, hipEventDisableTiming) != hipSuccess) {
@@ -568,15 +642,14 @@ hipError_t launch_quantize_gemm(tq_ctx* h, const void* keys, int key_dtype, int6
     const hipError_t e = hipStreamWaitEvent(stream, h->qscratch_done, 0);
     if (e != hipSuccess) return e;
   }
-  uint16_t* rp = static_cast<uint16_t*>(h->qscratch);
-  float* part = reinterpret_cast<float*>(static_cast<char*>(h->qscratch) + rp_bytes);
+  uint16_t* kpc = static_cast<uint16_t*>(h->qscratch);
+  uint16_t* rp = reinterpret_cast<uint16_t*>(static_cast<char*>(h->qscratch) + kp_bytes);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(h->qscratch) + kp_bytes + rp_bytes);
 
   const int elem = key_dtype == TQ_F32 ? 4 : 2;
   const bool vec_ok = (reinterpret_cast<uintptr_t>(keys) & 15u) == 0 && (ldk * elem) % 16 == 0;
   const int code_row = h->code_bits * h->words + (h->hi ? h->hi_words : 0);
   QArgs base{};
-  base.ldk = ldk;
-  base.vec_ok = vec_ok ? 1 : 0;
   base.d = d;
   base.dpm = s.dpm;
   base.nct = s.nct;
@@ -594,24 +667,42 @@ hipError_t launch_quantize_gemm(tq_ctx* h, const void* keys, int key_dtype, int6
   for (int64_t c0 = 0; c0 < n && e == hipSuccess; c0 += chunk) {
     const int64_t nc = std::min<int64_t>(chunk, n - c0);
     const int64_t tiles = (nc + kBN - 1) / kBN;
+    // norms and key pieces of the chunk
+    const void* ck = static_cast<const char*>(keys) + size_t(c0) * size_t(ldk) * elem;
+    if (key_dtype == TQ_F32)
+      hipLaunchKernelGGL(qg_prep_kernel<TQ_F32>, dim3(uint32_t(tiles)), dim3(256), 0, stream, ck, nc, ldk, d, s.ks,
+                         vec_ok ? 1 : 0, norms + c0, kpc);
+    else
+      hipLaunchKernelGGL(qg_prep_kernel<TQ_BF16>, dim3(uint32_t(tiles)), dim3(256), 0, stream, ck, nc, ldk, d, s.ks,
+                         vec_ok ? 1 : 0, norms + c0, kpc);
+    e = hipGetLastError();
+    if (e != hipSuccess) break;
     QArgs rot = base, pro = base;
     rot.atiles = h->d_qpi_tiles;
+    rot.bsrc = kpc;
     rot.ks = s.ks;
-    rot.keys = static_cast<const char*>(keys) + size_t(c0) * size_t(ldk) * elem;
     rot.norms = norms + c0;
     rot.nkeys = nc;
     rot.codes = codes + c0 * code_row;
     pro.atiles = h->d_qg_tiles;
+    pro.bsrc = rp;
     pro.ks = s.ks2;
     pro.norms = norms + c0;
     pro.nkeys = nc;
     pro.signs = signs + c0 * h->words;
     pro.rnorms = rnorms + c0;
-    const dim3 grid(uint32_t(tiles), uint32_t(s.nct));
-    if (key_dtype == TQ_F32)
-      e = launch_pair(rot, qgemm_kernel<0, TQ_F32>, pro, qgemm_kernel<1, TQ_F32>, grid, stream);
-    else
-      e = launch_pair(rot, qgemm_kernel<0, TQ_BF16>, pro, qgemm_kernel<1, TQ_F32>, grid, stream);
+    // persistent blocks, one per CU, on strided items
+    const int64_t items = tiles * s.nct;
+    const int64_t blocks = std::min<int64_t>(items, h->cus);
+    rot.items = pro.items = items;
+    rot.tiles = pro.tiles = tiles;
+    const dim3 grid{static_cast<uint32_t>(blocks)};
+    switch (h->code_bits) {
+      case 1: e = launch_pair(rot, qgemm_kernel<0, 1>, pro, qgemm_kernel<1, 0>, grid, stream); break;
+      case 2: e = launch_pair(rot, qgemm_kernel<0, 2>, pro, qgemm_kernel<1, 0>, grid, stream); break;
+      case 3: e = launch_pair(rot, qgemm_kernel<0, 3>, pro, qgemm_kernel<1, 0>, grid, stream); break;
+      default: e = launch_pair(rot, qgemm_kernel<0, 4>, pro, qgemm_kernel<1, 0>, grid, stream); break;
+    }
   }
   if (e != hipSuccess) return e;
   e = hipEventRecord(h->qscratch_done, stream);
