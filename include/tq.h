@@ -108,6 +108,7 @@ typedef struct {
   int64_t key_bytes;      /* code_bytes + sign_bytes + 8 (norm and rnorm)     */
   int32_t hi;             /* coordinates with one more index bit (0: plain)   */
   int32_t hi_words;       /* ceil(hi / 32): words of the extra plane          */
+  int32_t polar;          /* 1 for a tq_init_polar handle                     */
 } tq_layout;
 
 /* Build the method for (d, bits, seed) on the current HIP device: rotation,
@@ -148,6 +149,38 @@ TQ_API int tq_init_explicit(int32_t d, int32_t bits, const float* pi, const floa
  * are tq_init's.  d a power of two in [2, 4096]; every entry point then
  * works as for a tq_init handle (the rotation is applied as a dense matrix). */
 TQ_API int tq_init_hadamard(int32_t d, int32_t bits, uint64_t seed, tq_handle* out);
+
+/* Recursive polar-angle stage 1 in place of the scalar codebook ("TurboQuant
+ * tutorial", section on turning Cartesian into polar coordinates: one length
+ * kept at high precision and d - 1 angles of 2 or 3 bits; "TurboQuant deep
+ * review", breakthrough section: a recursive polar transform after the random
+ * rotation, angles with a concentrated law of analytic form; the pages leave
+ * the recursion open, this is a reading).  With z = Pi u (u = k / ||k||) and
+ * d a power of two: level 1 takes the pairs (z_2i, z_2i+1) to a radius and an
+ * angle atan2(z_2i+1, z_2i) in [0, 2 pi); level l >= 2 takes pairs of level
+ * l-1 radii (a, b) to sqrt(a^2 + b^2) and atan2(b, a) in [0, pi/2]; after
+ * log2 d levels one radius (1) and d - 1 angles remain.  Each angle gets
+ * bits - 1 index bits: level 1 the uniform quantizer of the circle (level
+ * (k + 1/2) 2 pi / L), level l the Lloyd-Max quantizer of the law of
+ * atan2(|b|, |a|) for two independent 2^(l-1)-dimensional Gaussian blocks
+ * (density proportional to sin^(m-1) psi cos^(m-1) psi); tq_polar_codebook
+ * gives them.  z_hat composes the level values back from radius 1, and the
+ * QJL stage, the score and the stage-1 reconstruction use z_hat where a
+ * plain handle uses c[idx]: r = z - z_hat, rho = ||r||, beta = [G r > 0],
+ * score = n (<Pi q, z_hat> + rho sqrt(pi/2)/d <G Pi q, 2 beta - 1>),
+ * k_hat = n Pi^T z_hat.  Codes: the d - 1 angle indices in level order
+ * (level 1's d/2 angles, then level 2's d/4, ..., the top angle) in slots
+ * 0 .. d-2 of the usual bit planes, slot d-1 zero; tq_layout reports
+ * polar = 1.  Pi and G are tq_init's for the seed.  d a power of two in
+ * [2, 4096], 2 <= bits <= 5.  tq_quantize, tq_logits and tq_dequant_mse take
+ * such handles (float32 kernels); tq_logits_topk, tq_dequant_prod,
+ * tq_pack_values and tq_attention return TQ_EUNSUPPORTED. */
+TQ_API int tq_init_polar(int32_t d, int32_t bits, uint64_t seed, tq_handle* out);
+
+/* Host only, no HIP call: the angle codebook of recursion level `level`
+ * (1 .. log2 d) of tq_init_polar(d, bits, .): levels float[2^(bits-1)]
+ * ascending, thresholds float[2^(bits-1) - 1] (either may be NULL). */
+TQ_API int tq_polar_codebook(int32_t d, int32_t bits, int32_t level, float* levels, float* thresholds);
 
 /* Host only, no HIP call: the rotation tq_init_hadamard(d, ., seed) uses,
  * float[d*d] row-major into pi. */

@@ -113,3 +113,36 @@ def test_host_params_null_outputs_skip(tqm):
     c = np.empty(4, dtype=np.float32)
     assert lib.tq_host_params(16, 3, 0, None, None, c.ctypes.data, None) == 0
     assert np.array_equal(c, P.init(16, 3, 0).centroids.astype(np.float32))
+
+
+@pytest.mark.parametrize("d,bits", [(2, 2), (16, 3), (128, 3), (128, 4), (1024, 2), (4096, 5)])
+def test_polar_codebooks_match_oracle(tqm, d, bits):
+    """Polar angle codebooks: the C++ builder (Lloyd-Max in theta = 2 psi -
+    pi/2 by Gauss-Legendre panels) and the oracle (Lloyd-Max in phi = psi -
+    pi/4 with incomplete-beta masses and adaptive quadrature moments) agree
+    to <= 1 float32 ulp on every level; thresholds are the same midpoints."""
+    from oracle import polar as PL
+    L = 1 << (bits - 1)
+    nl = d.bit_length() - 1
+    levels = list(range(1, nl + 1)) if nl <= 4 else [1, 2, 3, nl - 1, nl]
+    for lvl in levels:
+        c, t = tqm.tq_polar_codebook(d, bits, lvl)
+        if lvl == 1:
+            c_or = ((np.arange(L) + 0.5) * PL.TWO_PI / L).astype(np.float32)
+            t_or = (np.arange(1, L) * PL.TWO_PI / L).astype(np.float32)
+        else:
+            c_or = PL.level_codebook_fp64(1 << (lvl - 1), L).astype(np.float32)
+            t_or = P.thresholds_from_centroids(c_or).astype(np.float32)
+        assert _ulps(c, c_or).max() <= 1, (lvl, c, c_or)
+        assert _ulps(t, t_or).max() <= 1, (lvl, t, t_or)
+
+
+def test_polar_init_rejects_bad_arguments(tqm):
+    """d not a power of two, or bits out of range: TQ_EINVAL without a GPU
+    call; the host codebook refuses a level past log2 d."""
+    out = ctypes.c_void_p()
+    lib = tqm._lib()
+    assert lib.tq_init_polar(200, 3, 0, ctypes.byref(out)) == tqm.TQ_EINVAL
+    assert lib.tq_init_polar(1, 3, 0, ctypes.byref(out)) == tqm.TQ_EINVAL
+    assert lib.tq_polar_codebook(128, 3, 8, None, None) == tqm.TQ_EINVAL
+    assert lib.tq_polar_codebook(128, 6, 1, None, None) == tqm.TQ_EINVAL

@@ -25,7 +25,8 @@ TQ_BF16 = 1
 TQ_FORMAT_VERSION = 1
 
 # every symbol include/tq.h declares
-EXPORTS = ("tq_init", "tq_init_explicit", "tq_init_hadamard", "tq_init_split", "tq_hadamard_rotation", "tq_destroy", "tq_get_layout", "tq_host_params",
+EXPORTS = ("tq_init", "tq_init_explicit", "tq_init_hadamard", "tq_init_split", "tq_init_polar", "tq_polar_codebook",
+           "tq_hadamard_rotation", "tq_destroy", "tq_get_layout", "tq_host_params",
            "tq_params_hash", "tq_quantize", "tq_logits_workspace_size", "tq_logits",
            "tq_logits_topk_workspace_size", "tq_logits_topk", "tq_dequant_mse", "tq_dequant_prod", "tq_dense_logits", "tq_pack_values",
            "tq_attention_workspace_size", "tq_attention", "tq_logits_noalloc", "tq_noalloc_scratch_bytes",
@@ -43,7 +44,7 @@ class Layout(ctypes.Structure):
                 ("levels", ctypes.c_int32), ("words", ctypes.c_int32),
                 ("format_version", ctypes.c_int32), ("code_bytes", ctypes.c_int64),
                 ("sign_bytes", ctypes.c_int64), ("key_bytes", ctypes.c_int64),
-                ("hi", ctypes.c_int32), ("hi_words", ctypes.c_int32)]
+                ("hi", ctypes.c_int32), ("hi_words", ctypes.c_int32), ("polar", ctypes.c_int32)]
 
 
 _LIB = None
@@ -63,6 +64,8 @@ def _lib():
         "tq_init_explicit": (ctypes.c_int, [i32, i32, fp, fp, ctypes.POINTER(vp)]),
         "tq_init_hadamard": (ctypes.c_int, [i32, i32, u64, ctypes.POINTER(vp)]),
         "tq_init_split": (ctypes.c_int, [i32, i32, i32, u64, ctypes.POINTER(vp)]),
+        "tq_init_polar": (ctypes.c_int, [i32, i32, u64, ctypes.POINTER(vp)]),
+        "tq_polar_codebook": (ctypes.c_int, [i32, i32, i32, vp, vp]),
         "tq_hadamard_rotation": (ctypes.c_int, [i32, u64, vp]),
         "tq_destroy": (ctypes.c_int, [vp]),
         "tq_get_layout": (ctypes.c_int, [vp, ctypes.POINTER(Layout)]),
@@ -122,6 +125,7 @@ class Handle:
         self.words = lay.words
         self.hi = lay.hi
         self.hi_words = lay.hi_words
+        self.polar = lay.polar
         # per-key shape of the codes: (B, W) planes, or flat B W + hi_words
         # words with fractional widths
         self.code_shape = ((lay.code_bits * lay.words + lay.hi_words,) if lay.hi
@@ -165,6 +169,25 @@ def tq_init_hadamard(d, bits, seed):
     _check("tq_init_hadamard", _lib().tq_init_hadamard(int(d), int(bits), ctypes.c_uint64(int(seed) & (2 ** 64 - 1)),
                                                        ctypes.byref(out)))
     return Handle(out)
+
+
+def tq_init_polar(d, bits, seed):
+    """Handle with the recursive polar-angle stage 1 (d a power of two)."""
+    out = ctypes.c_void_p()
+    _check("tq_init_polar", _lib().tq_init_polar(int(d), int(bits), ctypes.c_uint64(int(seed) & (2 ** 64 - 1)),
+                                                 ctypes.byref(out)))
+    return Handle(out)
+
+
+def tq_polar_codebook(d, bits, level):
+    """Host-only: (levels, thresholds) float32 of recursion level `level`."""
+    import numpy as np
+    L = 1 << (int(bits) - 1)
+    lv = np.empty(L, dtype=np.float32)
+    th = np.empty(max(L - 1, 1), dtype=np.float32)
+    _check("tq_polar_codebook", _lib().tq_polar_codebook(int(d), int(bits), int(level), lv.ctypes.data_as(ctypes.c_void_p),
+                                                         th.ctypes.data_as(ctypes.c_void_p)))
+    return lv, th[:L - 1]
 
 
 def tq_hadamard_rotation(d, seed):

@@ -240,6 +240,38 @@ void cell_integrals(int d, double za, double zb, double* m0, double* m1) {
   *m1 = s1;
 }
 
+// mass and first moment in theta of the cell [ta, tb] of (-pi/2, pi/2)
+// under the weight cos(theta)^e (the polar angle laws), up to a common factor
+void cell_integrals_theta(double e, double ta, double tb, double* m0, double* m1) {
+  const double width_scale = 1.0 / std::sqrt(std::max(e, 1.0));
+  const double cut = 40.0 * width_scale;
+  ta = std::max(ta, -cut);
+  tb = std::min(tb, cut);
+  *m0 = 0.0;
+  *m1 = 0.0;
+  if (!(tb > ta)) return;
+  const double panel = 0.25 * width_scale;
+  int panels = int(std::ceil((tb - ta) / panel));
+  panels = std::max(panels, 8);
+  const double h = (tb - ta) / panels;
+  const GaussLegendre& rule = gl();
+  double s0 = 0.0, s1 = 0.0;
+  for (int p = 0; p < panels; ++p) {
+    const double mid = ta + (p + 0.5) * h;
+    double q0 = 0.0, q1 = 0.0;
+    for (int i = 0; i < kGL; ++i) {
+      const double th = mid + 0.5 * h * rule.x[i];
+      const double wgt = rule.w[i] * (e == 0.0 ? 1.0 : std::exp(e * std::log(std::cos(th))));
+      q0 += wgt;
+      q1 += wgt * th;
+    }
+    s0 += 0.5 * h * q0;
+    s1 += 0.5 * h * q1;
+  }
+  *m0 = s0;
+  *m1 = s1;
+}
+
 // inverse standard normal CDF (Acklam's rational approximation, refined by
 // one Halley step) - only used for the starting levels
 double norm_ppf(double p) {
@@ -309,6 +341,75 @@ int lloyd_max_sphere(int d, int levels, double* c) {
     }
   }
   return -1;
+}
+
+// ---------------------------------------------------------------------------
+// Polar angle codebooks.  A level-l angle psi (l >= 2) compares the lengths of
+// two m = 2^(l-1)-dimensional Gaussian blocks: its density is proportional to
+// sin^(m-1) psi cos^(m-1) psi on [0, pi/2].  With theta = 2 psi - pi/2 that is
+// cos(theta)^(m-1) on (-pi/2, pi/2); Lloyd-Max commutes with the linear map,
+// so the levels are computed in theta and mapped back.
+// ---------------------------------------------------------------------------
+int lloyd_max_polar_level(int m, int levels, double* psi) {
+  const double half_pi = 1.5707963267948966192313216916398;
+  const double e = double(m) - 1.0;
+  std::vector<double> cur(levels), nxt(levels), t(levels + 1);
+  for (int i = 0; i < levels; ++i) {
+    const double v = norm_ppf((i + 0.5) / levels) / std::sqrt(double(m));
+    cur[i] = std::max(-0.999 * half_pi, std::min(0.999 * half_pi, v));
+  }
+  int settle = -1, near = 0;
+  for (int it = 0; it < 200000; ++it) {
+    t[0] = -half_pi;
+    t[levels] = half_pi;
+    for (int i = 1; i < levels; ++i) t[i] = 0.5 * (cur[i - 1] + cur[i]);
+    for (int i = 0; i < levels; ++i) {
+      double m0, m1;
+      cell_integrals_theta(e, t[i], t[i + 1], &m0, &m1);
+      nxt[i] = m1 / m0;
+    }
+    double delta = 0.0, big = 0.0;
+    for (int i = 0; i < levels; ++i) {
+      const double sym = 0.5 * (nxt[i] - nxt[levels - 1 - i]);
+      delta = std::max(delta, std::fabs(sym - cur[i]));
+      big = std::max(big, std::fabs(sym));
+      t[i] = sym;
+    }
+    for (int i = 0; i < levels; ++i) cur[i] = t[i];
+    const double rel = delta / big;
+    if (settle < 0 && rel <= 1.4210854715202004e-14 /* 2^-46 */) settle = 20;
+    near = rel <= 1e-11 ? near + 1 : 0;
+    if (near >= 300 || (settle >= 0 && --settle <= 0)) {
+      for (int i = 0; i < levels; ++i) psi[i] = 0.5 * cur[i] + 0.5 * half_pi;
+      return 0;
+    }
+  }
+  return -1;
+}
+
+int polar_level_codebook(int d, int bits, int level, float* levels, float* thresholds) {
+  if (d < 2 || d > 4096 || (d & (d - 1)) != 0 || bits < 2 || bits > 5) return -1;
+  int nl = 0;
+  while ((1 << nl) < d) ++nl;
+  if (level < 1 || level > nl) return -1;
+  const int L = 1 << (bits - 1);
+  std::vector<float> c32(L);
+  if (level == 1) {
+    // uniform quantizer of the circle: cells [k, k+1) 2 pi / L, levels at the centres
+    const double two_pi = 6.283185307179586476925286766559;
+    for (int i = 0; i < L; ++i) c32[i] = float((i + 0.5) * two_pi / L);
+    if (levels) std::memcpy(levels, c32.data(), sizeof(float) * L);
+    if (thresholds)
+      for (int i = 0; i + 1 < L; ++i) thresholds[i] = float((i + 1) * two_pi / L);
+    return 0;
+  }
+  std::vector<double> c(L);
+  if (lloyd_max_polar_level(1 << (level - 1), L, c.data()) != 0) return -2;
+  for (int i = 0; i < L; ++i) c32[i] = float(c[i]);
+  if (levels) std::memcpy(levels, c32.data(), sizeof(float) * L);
+  if (thresholds)
+    for (int i = 0; i + 1 < L; ++i) thresholds[i] = float(0.5 * (double(c32[i]) + double(c32[i + 1])));
+  return 0;
 }
 
 // ---------------------------------------------------------------------------

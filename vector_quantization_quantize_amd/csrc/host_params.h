@@ -19,6 +19,14 @@ void haar_from_gaussian(int d, const double* a, double* q);
 // uniform unit vector in R^d.  Returns 0 on convergence.
 int lloyd_max_sphere(int d, int levels, double* c);
 
+// Angle codebook of recursion level `level` (1 .. log2 d) of the polar
+// stage: level 1 the uniform quantizer of [0, 2 pi), higher levels Lloyd-Max
+// for the angle law of two 2^(level-1)-dimensional Gaussian blocks.
+// levels: float[2^(bits-1)] ascending; thresholds: float[2^(bits-1) - 1]
+// (float32 midpoints; level 1: the cell edges).  d a power of two.
+// Returns 0, or < 0 on bad arguments / non-convergence.
+int polar_level_codebook(int d, int bits, int level, float* levels, float* thresholds);
+
 // Randomized Hadamard rotation H diag(sigma) / sqrt(d) (float[d*d] row-major):
 // H[i][j] = (-1)^popcount(i & j) (Sylvester), sigma_j = -1 when bit 63 of
 // counter j of stream 2 is set, else +1.  d a power of two in [2, 4096];

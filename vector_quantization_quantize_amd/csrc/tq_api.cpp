@@ -34,6 +34,8 @@ void free_device(tq_ctx* h) {
     *p = nullptr;
   }
   tqdev::free_quantize_gemm(h);
+  if (h->d_polar_tab) (void)hipFree(h->d_polar_tab);
+  h->d_polar_tab = nullptr;
 }
 
 uint16_t f16_bits(float x) {
@@ -279,7 +281,7 @@ namespace {
 // queries (register form for d <= 256, tiled form above), the lookup-table
 // kernel for a few (d in (96, 128]),
 // else the general kernel (also for TQ_KERNELS=ref).
-enum class Scorer { kGeneral, kLut, kMfma };
+enum class Scorer { kGeneral, kLut, kMfma, kPolar };
 
 Scorer pick_scorer(const tq_ctx* h, int64_t nq);
 
@@ -293,6 +295,7 @@ bool tqdev::force_reference_kernels() {
 namespace {
 
 Scorer pick_scorer(const tq_ctx* h, int64_t nq) {
+  if (h->polar) return Scorer::kPolar;
   if (tqdev::force_reference_kernels()) return Scorer::kGeneral;
   if (nq >= tqdev::kScoreMfmaMinQueries && tqdev::score_mfma_supported(h)) return Scorer::kMfma;
   if (tqdev::logits_lut128_supported(h)) return Scorer::kLut;
@@ -333,7 +336,7 @@ int tq_host_params(int32_t d, int32_t bits, uint64_t seed, float* pi, float* g, 
 enum { kRotHaar = 0, kRotExplicit = 1, kRotHadamard = 2 };
 
 static int init_common(int32_t d, int32_t bits, const float* pi_in, const float* g_in, uint64_t seed,
-                       tq_handle* out, int rotation = kRotHaar, int32_t hi = 0) {
+                       tq_handle* out, int rotation = kRotHaar, int32_t hi = 0, bool polar = false) {
   if (!out) return TQ_EINVAL;
   *out = nullptr;
   if (d < 2 || d > 4096 || bits < 2 || bits > 5) return TQ_EINVAL;
@@ -370,6 +373,26 @@ static int init_common(int32_t d, int32_t bits, const float* pi_in, const float*
       rc = tqhost::build_params(d, bits + 1, seed, nullptr, nullptr, h->centroids_hi.data(),
                                 h->thresholds_hi.data());
     }
+    if (rc == 0 && polar) {
+      // per-level angle codebooks; thresholds padded with +inf, cos and sin
+      // of each level in float64 rounded once
+      int nl = 0;
+      while ((1 << nl) < d) ++nl;
+      h->polar = 1;
+      h->polar_levels = nl;
+      h->polar_tab.assign(size_t(nl) * tqdev::kPolarTab, 0.0f);
+      const int L = 1 << (bits - 1);
+      std::vector<float> lv(L), th(L);
+      for (int l = 1; l <= nl && rc == 0; ++l) {
+        rc = tqhost::polar_level_codebook(d, bits, l, lv.data(), th.data());
+        float* tab = &h->polar_tab[size_t(l - 1) * tqdev::kPolarTab];
+        for (int i = 0; i < 16; ++i) {
+          tab[i] = i + 1 < L ? th[i] : INFINITY;
+          tab[16 + i] = i < L ? float(std::cos(double(lv[i]))) : 1.0f;
+          tab[32 + i] = i < L ? float(std::sin(double(lv[i]))) : 0.0f;
+        }
+      }
+    }
     if (rc != 0) {
       delete h;
       return TQ_EUNSUPPORTED;
@@ -381,7 +404,16 @@ static int init_common(int32_t d, int32_t bits, const float* pi_in, const float*
     delete h;
     return TQ_EUNSUPPORTED;
   }
-  const int rc = finish_init(h);
+  int rc = finish_init(h);
+  if (rc == TQ_OK && h->polar) {
+    const size_t bytes = h->polar_tab.size() * sizeof(float);
+    if (hipMalloc(reinterpret_cast<void**>(&h->d_polar_tab), bytes) != hipSuccess) {
+      h->d_polar_tab = nullptr;
+      rc = TQ_ENOMEM;
+    } else if (hipMemcpy(h->d_polar_tab, h->polar_tab.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
+      rc = TQ_EHIP;
+    }
+  }
   if (rc != TQ_OK) {
     free_device(h);
     delete h;
@@ -418,6 +450,23 @@ int tq_init_hadamard(int32_t d, int32_t bits, uint64_t seed, tq_handle* out) {
   return init_common(d, bits, nullptr, nullptr, seed, out, kRotHadamard);
 }
 
+int tq_init_polar(int32_t d, int32_t bits, uint64_t seed, tq_handle* out) {
+  if (d < 2 || d > 4096 || (d & (d - 1)) != 0) {
+    if (out) *out = nullptr;
+    return TQ_EINVAL;
+  }
+  return init_common(d, bits, nullptr, nullptr, seed, out, kRotHaar, 0, true);
+}
+
+int tq_polar_codebook(int32_t d, int32_t bits, int32_t level, float* levels, float* thresholds) {
+  try {
+    const int rc = tqhost::polar_level_codebook(d, bits, level, levels, thresholds);
+    return rc == 0 ? TQ_OK : rc == -1 ? TQ_EINVAL : TQ_EUNSUPPORTED;
+  } catch (...) {
+    return TQ_ENOMEM;
+  }
+}
+
 int tq_hadamard_rotation(int32_t d, uint64_t seed, float* pi) {
   if (!pi || d < 2 || d > 4096 || (d & (d - 1)) != 0) return TQ_EINVAL;
   return tqhost::hadamard_rotation(d, seed, pi) == 0 ? TQ_OK : TQ_EINVAL;
@@ -443,6 +492,7 @@ int tq_get_layout(tq_handle h, tq_layout* out) {
   out->key_bytes = out->code_bytes + out->sign_bytes + 8;
   out->hi = h->hi;
   out->hi_words = h->hi_words;
+  out->polar = h->polar;
   return TQ_OK;
 }
 
@@ -464,6 +514,7 @@ uint64_t tq_params_hash(tq_handle h) {
     x ^= uint64_t(h->hi >> (8 * i)) & 0xFFu;
     x *= 0x100000001b3ull;
   }
+  eat(h->polar_tab);
   return x;
 }
 
@@ -479,7 +530,9 @@ int tq_quantize(tq_handle h, const void* keys, int32_t key_dtype, int64_t n, int
   // d = 128 with bf16 keys: the register-resident matrix-core kernel; other
   // d >= 16: the tiled matrix-core kernels; smaller d: float32 kernels
   hipError_t e;
-  if (tqdev::force_reference_kernels())
+  if (h->polar)
+    e = tqdev::launch_quantize_polar(h, keys, key_dtype, n, ldk, codes, signs, norms, rnorms, s);
+  else if (tqdev::force_reference_kernels())
     e = tqdev::launch_quantize_v1(h, keys, key_dtype, n, ldk, codes, signs, norms, rnorms, s);
   else if (tqdev::quantize_mfma128_supported(h, keys, key_dtype, ldk, codes, signs, norms, rnorms))
     e = tqdev::launch_quantize_mfma128(h, keys, n, ldk, codes, signs, norms, rnorms, s);
@@ -513,8 +566,9 @@ int run_logits(const tq_ctx* h, const float* queries, int64_t groups, int64_t nq
     float* vw = static_cast<float*>(workspace);
     e = tqdev::launch_query_prep(h, queries, groups * nq, vw, s);
     if (e != hipSuccess) return TQ_EHIP;
-    e = sc == Scorer::kMfma ? tqdev::launch_score_mfma(h, vw, groups, nq, codes, signs, norms, rnorms, n, scores, s)
-                            : tqdev::launch_logits_v1(h, vw, groups, nq, codes, signs, norms, rnorms, n, scores, s);
+    e = sc == Scorer::kMfma    ? tqdev::launch_score_mfma(h, vw, groups, nq, codes, signs, norms, rnorms, n, scores, s)
+        : sc == Scorer::kPolar ? tqdev::launch_logits_polar(h, vw, groups, nq, codes, signs, norms, rnorms, n, scores, s)
+                               : tqdev::launch_logits_v1(h, vw, groups, nq, codes, signs, norms, rnorms, n, scores, s);
   }
   return e == hipSuccess ? TQ_OK : TQ_EHIP;
 }
@@ -569,6 +623,7 @@ int tq_logits(tq_handle h, const float* queries, int64_t groups, int64_t nq, con
 int tq_dequant_prod(tq_handle h, const uint32_t* codes, const uint32_t* signs, const float* norms,
                     const float* rnorms, int64_t n, float* ktilde, void* stream) {
   if (!h || n < 0) return TQ_EINVAL;
+  if (h->polar) return TQ_EUNSUPPORTED;
   if (n == 0) return TQ_OK;
   if (!codes || !signs || !norms || !rnorms || !ktilde) return TQ_EINVAL;
   if (n > int64_t(0x7FFFFFFF) * 4) return TQ_EUNSUPPORTED;
@@ -596,7 +651,7 @@ int tq_dense_logits(const float* queries, int64_t groups, int64_t nq, const void
 
 int tq_pack_values(tq_handle h, const uint32_t* codes, int64_t groups, int64_t n, uint32_t* vcodes, void* stream) {
   if (!h || groups < 0 || n < 0) return TQ_EINVAL;
-  if (h->hi != 0) return TQ_EUNSUPPORTED;  // stored values use one width
+  if (h->hi != 0 || h->polar) return TQ_EUNSUPPORTED;  // stored values use one width of scalar codes
   if (groups == 0 || n == 0) return TQ_OK;
   if (!codes || !vcodes || !aligned4(codes) || (reinterpret_cast<uintptr_t>(vcodes) & 15u) != 0) return TQ_EINVAL;
   if (groups > 65535 || (n + 31) / 32 > 0x7FFFFFFF) return TQ_EUNSUPPORTED;
@@ -616,7 +671,7 @@ int tq_attention(tq_handle hk, tq_handle hv, const float* queries, int64_t group
                  void* workspace, size_t workspace_bytes, void* stream) {
   if (!hk || !hv || groups < 0 || nq < 0 || n < 0) return TQ_EINVAL;
   if (hk->d != hv->d || hk->device != hv->device || !std::isfinite(scale)) return TQ_EINVAL;
-  if (hv->hi != 0) return TQ_EUNSUPPORTED;  // stored values use one width
+  if (hv->hi != 0 || hv->polar || hk->polar) return TQ_EUNSUPPORTED;  // scalar codes, one width
   if (groups == 0 || nq == 0) return TQ_OK;
   if (!out || !aligned4(out) || (lse && !aligned4(lse))) return TQ_EINVAL;
   if (groups * ((nq + 15) / 16) > 65535) return TQ_EUNSUPPORTED;
@@ -722,6 +777,7 @@ int tq_logits_topk(tq_handle h, const float* queries, int64_t groups, int64_t nq
                    const uint32_t* signs, const float* norms, const float* rnorms, int64_t n, int32_t k,
                    int64_t* top_idx, float* top_scores, void* workspace, size_t workspace_bytes, void* stream) {
   if (!h || groups < 0 || nq < 0 || n < 0) return TQ_EINVAL;
+  if (h->polar) return TQ_EUNSUPPORTED;
   if (k < 1 || k > tqdev::kTopkMax) return TQ_EINVAL;
   if (groups == 0 || nq == 0) return TQ_OK;
   if (!queries || !top_idx || !top_scores || !workspace) return TQ_EINVAL;
@@ -791,8 +847,9 @@ int tq_dequant_mse(tq_handle h, const uint32_t* codes, const float* norms, int64
   if (!codes || !norms || !khat) return TQ_EINVAL;
   if (check_device(h) != TQ_OK) return TQ_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = (!tqdev::force_reference_kernels() && tqdev::dequant_mfma128_supported(h) &&
-                        dequant_rows_aligned(h, codes))
+  const hipError_t e = h->polar ? tqdev::launch_dequant_polar(h, codes, norms, n, khat, s)
+                       : (!tqdev::force_reference_kernels() && tqdev::dequant_mfma128_supported(h) &&
+                          dequant_rows_aligned(h, codes))
                            ? tqdev::launch_dequant_mfma128(h, codes, norms, n, khat, s)
                            : tqdev::launch_dequant_v1(h, codes, norms, n, khat, s);
   return e == hipSuccess ? TQ_OK : TQ_EHIP;

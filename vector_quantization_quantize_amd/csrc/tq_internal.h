@@ -80,6 +80,12 @@ struct tq_ctx {
   bool symmetric = false;  // level set exactly symmetric in float32
   tqdev::HalfCodebook half{};
   tqdev::DequantTable dqt{};
+  // polar stage 1 (tq_init_polar): log2 d recursion levels; per level
+  // (0-based) 48 floats: thresholds (+inf past L - 1), cos and sin of the
+  // levels (float32 of the float64 values of the float32 levels)
+  int polar = 0, polar_levels = 0;
+  std::vector<float> polar_tab;
+  float* d_polar_tab = nullptr;
   // general matrix-core quantizer (quantize_gemm.hip), d >= 16: operand
   // tiles of 2^12 Pi and 2^10 G as two float16 pieces,
   // [coord tile][K step][row 128][piece 2][16 halves]
@@ -245,6 +251,18 @@ hipError_t launch_fill_u32(unsigned int* p, int64_t n, unsigned int v, hipStream
 
 hipError_t launch_dequant_v1(const tq_ctx* h, const uint32_t* codes, const float* norms, int64_t n,
                              float* khat, hipStream_t stream);
+
+// polar handles (kernels_ref.hip): quantize, scores (vw from
+// launch_query_prep) and the stage-1 reconstruction with the composed
+// z_hat in place of c[idx]
+constexpr int kPolarTab = 48;  // floats per level: thresholds, cos, sin (16 each)
+hipError_t launch_quantize_polar(const tq_ctx* h, const void* keys, int key_dtype, int64_t n, int64_t ldk,
+                                 uint32_t* codes, uint32_t* signs, float* norms, float* rnorms, hipStream_t stream);
+hipError_t launch_logits_polar(const tq_ctx* h, const float* vw, int64_t groups, int64_t nq, const uint32_t* codes,
+                               const uint32_t* signs, const float* norms, const float* rnorms, int64_t n,
+                               float* scores, hipStream_t stream);
+hipError_t launch_dequant_polar(const tq_ctx* h, const uint32_t* codes, const float* norms, int64_t n, float* khat,
+                                hipStream_t stream);
 // k_tilde = n Pi^T (c[idx] + rho sqrt(pi/2)/d G^T (2 beta - 1)); d = 128 on
 // the matrix cores (dequant_mfma.hip), float32 otherwise (kernels_ref.hip)
 hipError_t launch_dequant_prod_mfma128(const tq_ctx* h, const uint32_t* codes, const uint32_t* signs,
