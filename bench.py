@@ -433,6 +433,32 @@ def quantize_general_leg(seed, reps=5):
         tqm.tq_destroy(h)
         del keys, out
         torch.cuda.empty_cache()
+    # a randomized Hadamard handle against a Haar handle on the same 1e6
+    # unit keys of a power-of-two d: fast transform + projection versus the
+    # two dense products
+    n, d = 1000000, 1024
+    keys = torch.randn((n, d), generator=gen, device="cuda")
+    keys /= keys.norm(dim=1, keepdim=True)
+    had = {"keys": n, "d": d, "bits": 4}
+    for kind, init in (("haar", tqm.tq_init), ("hadamard", tqm.tq_init_hadamard)):
+        h = init(d, 4, 0)
+        out = tqm.empty_packed(h, n)
+        tqm.tq_quantize(h, keys, out=out)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            tqm.tq_quantize(h, keys, out=out)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        had[kind + "_ms"] = round(ms, 3)
+        had[kind + "_GBps"] = round((4 * d + 4 * 4 * (d // 32) + 8) * n / (ms * 1e-3) / 1e9, 1)
+        tqm.tq_destroy(h)
+        del out
+    res["hadamard_d1024"] = had
+    del keys
+    torch.cuda.empty_cache()
     c = res["cone"]
     res["roofline_cone"] = {"bound": "mfma", "achieved": c["useful_TFLOPs"], "peak": BF16_MFMA_PEAK_TFLOPS,
                             "unit": "TFLOP/s", "frac": c["useful_mfma_frac"], "raw_frac": c["raw_mfma_frac"],

@@ -179,20 +179,28 @@ def test_pages_4d_example_on_gpu(env):
 
 @pytest.mark.parametrize("d,bits,key_dtype,groups,n,nq", [
     (128, 3, "bf16", 2, 1000, 4),   # the matrix-core quantize path (bf16, d = 128) and the lookup-table scorer
-    (128, 4, "f32", 1, 300, 20),    # general quantize, matrix-core scorer
+    (128, 4, "f32", 1, 300, 20),    # fast transform + projection, matrix-core scorer
     (64, 2, "f32", 3, 200, 5),
     (256, 5, "f32", 1, 100, 3),
-    (4, 3, "f32", 1, 50, 2),
+    (4, 3, "f32", 1, 50, 2),        # below the matrix-core quantizer: the dense rotation
+    (16, 3, "f32", 2, 300, 3),      # one coordinate per lane, half a code word
+    (32, 2, "bf16", 1, 129, 2),
+    (512, 3, "bf16", 1, 300, 3),
+    (1024, 4, "f32", 1, 400, 4),    # 16 coordinates per lane
+    (4096, 3, "f32", 1, 130, 2),    # 64 per lane, two code words per lane
 ])
 def test_hadamard_rotation_full(env, d, bits, key_dtype, groups, n, nq):
     """A randomized Hadamard handle through every entry point against the
-    oracle built with the same rotation (oracle.params.init_hadamard)."""
+    oracle built with the same rotation (oracle.params.init_hadamard).  For
+    d >= 16 the library rotates by the fast Walsh-Hadamard transform, not
+    by the dense matrix the oracle multiplies with."""
     torch, tqm, _ = env
     _announce(f"hadamard d={d} bits={bits} {key_dtype} groups={groups} n={n} nq={nq}")
     pr = P.init_hadamard(d, bits, 7)
     h = tqm.tq_init_hadamard(d, bits, 7)
     rs = np.random.default_rng(d + bits)
     keys = rs.standard_normal((groups * n, d)) * np.exp(0.5 * rs.standard_normal((groups * n, 1)))
+    keys[min(5, groups * n - 1)] = 0.0
     if key_dtype == "bf16":
         keys = np.asarray(torch.tensor(keys).bfloat16().float().numpy(), dtype=np.float64)
     check_full(env, d, bits, keys, rs.standard_normal((groups, nq, d)).astype(np.float32), key_dtype=key_dtype,

@@ -218,6 +218,198 @@ struct Levels {
 };
 
 // ---------------------------------------------------------------------------
+// Randomized Hadamard rotation (tq_init_hadamard handles, d a power of two):
+// Pi = H diag(sigma) c with H the Sylvester matrix and c = float32(1/sqrt(d)),
+// so z = c H (sigma * k) / n, a fast Walsh-Hadamard transform: d log2 d
+// additions instead of the d^2 products of the dense rotation.  A block
+// takes 4 consecutive keys, one wave each; lane l holds elements
+// l M .. l M + M - 1 (M = d / 64, or one element per lane below d = 64):
+// log2 M butterfly stages inside the lane, the rest across lanes by
+// exchanges with lane l ^ 2^b.  Then, per element, the rotation's
+// epilogue: bucketize, code bits, r = z - c[idx] as residual pieces for the
+// projection, and rho^2.  The pieces go through LDS so that the block writes
+// each K step of its 4 keys as one contiguous 256-byte run of the
+// projection's operand layout (a wave writing its own key directly would
+// scatter 64-byte pieces d / 16 steps apart).
+// ---------------------------------------------------------------------------
+template <int KT, int LGD>
+__global__ void __launch_bounds__(256)
+qg_wht_kernel(const void* __restrict__ keys, int64_t nkeys, int64_t ldk, int vec_ok,
+              const float* __restrict__ sigma, float c, Levels lv, int B, int W, int code_row,
+              uint32_t* __restrict__ codes, float* __restrict__ norms, uint16_t* __restrict__ rp,
+              float* __restrict__ part, int nct) {
+  constexpr int D = 1 << LGD;
+  constexpr int LGM = LGD > 6 ? LGD - 6 : 0;
+  constexpr int M = 1 << LGM;
+  constexpr int DPM = D < 32 ? 32 : D;  // coordinates padded to whole code words
+  constexpr int KS2 = DPM / 16;         // K steps of the projection
+  constexpr int ROWH = 4 * 32 + 8;      // halves per staged K step (4 keys x 2 pieces x 16) + 16 bytes
+  __shared__ __align__(16) _Float16 stage[KS2 * ROWH];
+  __shared__ float lc[kMaxLevels];
+  if (threadIdx.x < kMaxLevels) lc[threadIdx.x] = lv.c[threadIdx.x];
+
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t key0 = int64_t(blockIdx.x) * 4, key = key0 + w;
+  const bool kin = key < nkeys;
+  const int j0 = lane * M;
+  const bool active = kin && j0 < D;
+  float x[M];
+  if constexpr (KT == TQ_F32) {
+    const float* row = static_cast<const float*>(keys) + (kin ? key : 0) * ldk;
+    if (M >= 4 && vec_ok) {
+#pragma unroll
+      for (int q = 0; q < M / 4; ++q) {
+        const float4 v = active ? *reinterpret_cast<const float4*>(row + j0 + 4 * q) : float4{0.f, 0.f, 0.f, 0.f};
+        x[4 * q] = v.x;
+        x[4 * q + 1] = v.y;
+        x[4 * q + 2] = v.z;
+        x[4 * q + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < M; ++e) x[e] = active ? row[j0 + e] : 0.0f;
+    }
+  } else {
+    const uint16_t* row = static_cast<const uint16_t*>(keys) + (kin ? key : 0) * ldk;
+    if (M >= 8 && vec_ok) {
+#pragma unroll
+      for (int q = 0; q < M / 8; ++q) {
+        const uint4 v = active ? *reinterpret_cast<const uint4*>(row + j0 + 8 * q) : uint4{0u, 0u, 0u, 0u};
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          x[8 * q + 2 * t] = bf16_to_f32(uint16_t(u[t] & 0xFFFFu));
+          x[8 * q + 2 * t + 1] = bf16_to_f32(uint16_t(u[t] >> 16));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < M; ++e) x[e] = active ? bf16_to_f32(row[j0 + e]) : 0.0f;
+    }
+  }
+  float ss = 0.0f;
+#pragma unroll
+  for (int e = 0; e < M; ++e) ss = fmaf(x[e], x[e], ss);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  const float nk = sqrtf(ss);
+  if (M >= 4) {
+#pragma unroll
+    for (int q = 0; q < M / 4; ++q) {
+      const float4 sg = active ? *reinterpret_cast<const float4*>(sigma + j0 + 4 * q) : float4{0.f, 0.f, 0.f, 0.f};
+      x[4 * q] *= sg.x;
+      x[4 * q + 1] *= sg.y;
+      x[4 * q + 2] *= sg.z;
+      x[4 * q + 3] *= sg.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < M; ++e) x[e] *= active ? sigma[j0 + e] : 0.0f;
+  }
+  // butterflies (a, b) -> (a + b, a - b) over each index bit: inside the
+  // lane for the low log2 M bits, then across lanes
+#pragma unroll
+  for (int b = 0; b < LGM; ++b)
+#pragma unroll
+    for (int e = 0; e < M; ++e)
+      if (!(e & (1 << b))) {
+        const float a0 = x[e], a1 = x[e | (1 << b)];
+        x[e] = a0 + a1;
+        x[e | (1 << b)] = a0 - a1;
+      }
+#pragma unroll
+  for (int b = 0; b < LGD - LGM; ++b) {
+    const bool upper = (lane >> b) & 1;
+#pragma unroll
+    for (int e = 0; e < M; ++e) {
+      const float y = __shfl_xor(x[e], 1 << b);
+      x[e] = upper ? y - x[e] : x[e] + y;
+    }
+  }
+  __syncthreads();  // lc
+  const float zs = nk > 0.0f ? c / nk : 0.0f;
+  float rho2 = 0.0f;
+  uint32_t bits[4] = {0u, 0u, 0u, 0u};  // code bits per plane of this lane's (part of a) word
+  constexpr int G = M < 8 ? M : 8;        // elements per LDS store
+#pragma unroll
+  for (int q = 0; q < M / G; ++q) {
+    _Float16 ph[G], pl[G];
+#pragma unroll
+    for (int t = 0; t < G; ++t) {
+      const int e = q * G + t;
+      const float z = x[e] * zs;
+      // idx = #{thresholds <= z}; unused thresholds are +inf
+      int idx = 0;
+#pragma unroll
+      for (int u = 0; u + 1 < kMaxLevels; ++u) idx += z >= lv.t[u] ? 1 : 0;
+      const float r = active ? z - lc[idx] : 0.0f;
+      idx = active ? idx : 0;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) bits[p] |= uint32_t((idx >> p) & 1) << ((j0 + e) & 31);
+      rho2 = fmaf(r, r, rho2);
+      const float r2 = r * 4096.0f;
+      ph[t] = static_cast<_Float16>(r2);
+      pl[t] = static_cast<_Float16>(r2 - static_cast<float>(ph[t]));
+    }
+    const int j = j0 + q * G;
+    if (j < DPM) {
+      _Float16* at = stage + (j >> 4) * ROWH + w * 32 + (j & 15);
+      if constexpr (G == 8) {
+        f16x8 vh, vl;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          vh[t] = ph[t];
+          vl[t] = pl[t];
+        }
+        *reinterpret_cast<f16x8*>(at) = vh;
+        *reinterpret_cast<f16x8*>(at + 16) = vl;
+      } else {
+#pragma unroll
+        for (int t = 0; t < G; ++t) {
+          at[t] = ph[t];
+          at[16 + t] = pl[t];
+        }
+      }
+    }
+    if constexpr (M >= 32) {
+      if (((q + 1) * G) % 32 == 0) {  // a whole word of this lane is done
+        const int word = (j0 + q * G) >> 5;
+        if (kin)
+          for (int p = 0; p < B; ++p) codes[key * code_row + p * W + word] = bits[p];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) bits[p] = 0u;
+      }
+    }
+  }
+  if constexpr (M < 32) {
+    // a word spans 32 / M lanes: OR their bits together
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int o = 1; o < 32 / M; o <<= 1) bits[p] |= __shfl_xor(bits[p], o);
+    if (kin && (j0 & 31) == 0 && j0 < D) {
+      const int word = j0 >> 5;
+      for (int p = 0; p < B; ++p) codes[key * code_row + p * W + word] = bits[p];
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) rho2 += __shfl_xor(rho2, o);
+  if (kin) {
+    if (lane == 0) norms[key] = nk;
+    if (lane < 2 * nct) part[key * 2 * nct + lane] = lane == 0 ? rho2 : 0.0f;
+  }
+  __syncthreads();
+  // K step s of the 4 keys: 256 contiguous bytes at key tile kt, step s,
+  // keys tkey0 .. tkey0 + 3 (keys past the chunk get zero pieces)
+  const int64_t kt = key0 / kBN, tkey0 = key0 - kt * kBN;
+  for (int i = threadIdx.x; i < KS2 * 16; i += 256) {
+    const int st = i >> 4, u = i & 15;
+    const uint4 v = *reinterpret_cast<const uint4*>(stage + st * ROWH + 8 * u);
+    *reinterpret_cast<uint4*>(rp + ((kt * KS2 + st) * kBN + tkey0) * 32 + 8 * u) = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 2. / 3. the tiled products.  MODE 0: rotate + bucketize (B operand: the
 // key pieces); MODE 1: project + signs (B operand: the residual pieces).
 // ---------------------------------------------------------------------------
@@ -558,6 +750,36 @@ Levels levels_of(const Codebook& cb) {
   return l;
 }
 
+hipError_t launch_wht(const tq_ctx* h, const void* keys, int key_dtype, int64_t nc, int64_t ldk, bool vec_ok,
+                      uint32_t* codes, float* norms, uint16_t* rp, float* part, const Shape& s, hipStream_t stream) {
+  int lgd = 0;
+  while ((1 << lgd) < h->d) ++lgd;
+  const int code_row = h->code_bits * h->words;
+  const Levels lv = levels_of(h->cb);
+  const dim3 grid{static_cast<uint32_t>((nc + 3) / 4)};
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, keys, nc, ldk, vec_ok ? 1 : 0, h->d_hsigma, h->hscale,
+                       lv, h->code_bits, h->words, code_row, codes, norms, rp, part, s.nct);
+    return hipGetLastError();
+  };
+#define TQ_WHT_CASE(L) \
+  case L:              \
+    return key_dtype == TQ_F32 ? go(qg_wht_kernel<TQ_F32, L>) : go(qg_wht_kernel<TQ_BF16, L>);
+  switch (lgd) {
+    TQ_WHT_CASE(4)
+    TQ_WHT_CASE(5)
+    TQ_WHT_CASE(6)
+    TQ_WHT_CASE(7)
+    TQ_WHT_CASE(8)
+    TQ_WHT_CASE(9)
+    TQ_WHT_CASE(10)
+    TQ_WHT_CASE(11)
+    TQ_WHT_CASE(12)
+    default: return hipErrorInvalidValue;
+  }
+#undef TQ_WHT_CASE
+}
+
 template <typename K>
 hipError_t launch_pair(const QArgs& a0, K k0, const QArgs& a1, K k1, dim3 grid, hipStream_t stream) {
   hipLaunchKernelGGL(k0, grid, dim3(kThreads), 0, stream, a0);
@@ -667,8 +889,28 @@ hipError_t launch_quantize_gemm(tq_ctx* h, const void* keys, int key_dtype, int6
   for (int64_t c0 = 0; c0 < n && e == hipSuccess; c0 += chunk) {
     const int64_t nc = std::min<int64_t>(chunk, n - c0);
     const int64_t tiles = (nc + kBN - 1) / kBN;
-    // norms and key pieces of the chunk
     const void* ck = static_cast<const char*>(keys) + size_t(c0) * size_t(ldk) * elem;
+    if (h->hadamard && !h->hi) {
+      // rotation by the fast transform, straight into the residual pieces
+      e = launch_wht(h, ck, key_dtype, nc, ldk, vec_ok, codes + c0 * code_row, norms + c0, rp, part, s, stream);
+      if (e != hipSuccess) break;
+      QArgs pro = base;
+      pro.atiles = h->d_qg_tiles;
+      pro.bsrc = rp;
+      pro.ks = s.ks2;
+      pro.norms = norms + c0;
+      pro.nkeys = nc;
+      pro.signs = signs + c0 * h->words;
+      pro.rnorms = rnorms + c0;
+      const int64_t items = tiles * s.nct;
+      pro.items = items;
+      pro.tiles = tiles;
+      const dim3 grid{static_cast<uint32_t>(std::min<int64_t>(items, h->cus))};
+      hipLaunchKernelGGL((qgemm_kernel<1, 0>), grid, dim3(kThreads), 0, stream, pro);
+      e = hipGetLastError();
+      continue;
+    }
+    // norms and key pieces of the chunk
     if (key_dtype == TQ_F32)
       hipLaunchKernelGGL(qg_prep_kernel<TQ_F32>, dim3(uint32_t(tiles)), dim3(256), 0, stream, ck, nc, ldk, d, s.ks,
                          vec_ok ? 1 : 0, norms + c0, kpc);

@@ -36,6 +36,8 @@ void free_device(tq_ctx* h) {
   tqdev::free_quantize_gemm(h);
   if (h->d_polar_tab) (void)hipFree(h->d_polar_tab);
   h->d_polar_tab = nullptr;
+  if (h->d_hsigma) (void)hipFree(h->d_hsigma);
+  h->d_hsigma = nullptr;
 }
 
 uint16_t f16_bits(float x) {
@@ -359,6 +361,7 @@ static int init_common(int32_t d, int32_t bits, const float* pi_in, const float*
       rc = tqhost::build_params(d, bits, 0, nullptr, nullptr, h->centroids.data(), h->thresholds.data());
     } else if (rotation == kRotHadamard) {
       rc = tqhost::hadamard_rotation(d, seed, h->pi.data());
+      h->hadamard = 1;
       if (rc == 0)
         rc = tqhost::build_params(d, bits, seed, nullptr, h->g.data(), h->centroids.data(), h->thresholds.data());
     } else {
@@ -405,6 +408,18 @@ static int init_common(int32_t d, int32_t bits, const float* pi_in, const float*
     return TQ_EUNSUPPORTED;
   }
   int rc = finish_init(h);
+  if (rc == TQ_OK && h->hadamard) {
+    // row 0 of H is all +1: Pi[0][j] = sigma_j c
+    std::vector<float> sig(d);
+    h->hscale = std::fabs(h->pi[0]);
+    for (int j = 0; j < d; ++j) sig[j] = h->pi[j] < 0.0f ? -1.0f : 1.0f;
+    if (hipMalloc(reinterpret_cast<void**>(&h->d_hsigma), sizeof(float) * d) != hipSuccess) {
+      h->d_hsigma = nullptr;
+      rc = TQ_ENOMEM;
+    } else if (hipMemcpy(h->d_hsigma, sig.data(), sizeof(float) * d, hipMemcpyHostToDevice) != hipSuccess) {
+      rc = TQ_EHIP;
+    }
+  }
   if (rc == TQ_OK && h->polar) {
     const size_t bytes = h->polar_tab.size() * sizeof(float);
     if (hipMalloc(reinterpret_cast<void**>(&h->d_polar_tab), bytes) != hipSuccess) {

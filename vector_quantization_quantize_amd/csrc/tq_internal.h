@@ -80,6 +80,11 @@ struct tq_ctx {
   bool symmetric = false;  // level set exactly symmetric in float32
   tqdev::HalfCodebook half{};
   tqdev::DequantTable dqt{};
+  // randomized Hadamard rotation (tq_init_hadamard): Pi = H diag(sigma) c
+  // with c = float32(1 / sqrt(d)); d_hsigma holds sigma (float +-1)
+  int hadamard = 0;
+  float hscale = 0.0f;
+  float* d_hsigma = nullptr;
   // polar stage 1 (tq_init_polar): log2 d recursion levels; per level
   // (0-based) 48 floats: thresholds (+inf past L - 1), cos and sin of the
   // levels (float32 of the float64 values of the float32 levels)
