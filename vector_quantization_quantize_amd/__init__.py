@@ -12,7 +12,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libtq.so")
+# TQ_LIBRARY names another build of the same library (the host-sanitizer
+# build the CPU tests use); by default the in-tree libtq.so
+LIB_PATH = os.environ.get("TQ_LIBRARY") or os.path.join(HERE, "libtq.so")
 
 TQ_OK = 0
 TQ_EINVAL = -1
