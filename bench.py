@@ -9,8 +9,10 @@ batch entry, 4 per KV head):
 All inputs are synthetic (seeded), resident in HBM before timing starts.
 
 Prints one JSON line.  ``value`` = tq_logits (query, key) scores per second,
-the kernel timed with the caches flushed before each launch (the metric's
-"keys scored/s"); the step's own rate is under ``step``.  Per-kernel times
+the kernel timed with cold caches (back-to-back launches rotating over
+copies of its inputs that span at least 1 GiB, so every launch reads its
+inputs from HBM; the metric's "keys scored/s"); the step's own rate is under
+``step``.  Per-kernel times
 come from HIP events recorded on the stream the library launches on;
 ``roofline`` is for the kernel with the largest share of the step, priced
 against the roof its arithmetic intensity puts it under.  ``cpu_baseline``
@@ -41,7 +43,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long_context")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cold-reps", type=int, default=10, help="flushed-cache reps per kernel")
+    ap.add_argument("--cold-reps", type=int, default=10, help="rounds over the cold-cache input copies per kernel")
     ap.add_argument("--cpu-groups", type=int, default=24, help="key groups timed on the CPU oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-search", action="store_true", help="skip the search (top-k) measurement")
@@ -605,26 +607,44 @@ def main():
     per = {n: float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]))
            for i, n in enumerate(names)}
 
-    # each kernel again with the caches flushed before every launch: reading
-    # 1 GiB (> L2 + MALL) leaves only clean lines behind.  A write-based flush
-    # would leave up to the MALL's size of dirty lines whose write-back lands
-    # inside the timed kernel and roughly halves its apparent read rate.
-    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-    sink = torch.zeros((), dtype=torch.float32, device="cuda")
-    cold = {}
+    # each kernel again with cold caches: launches run back to back over R
+    # copies of the kernel's inputs and outputs, R chosen so that the copies
+    # of the inputs span at least 1 GiB (> L2 + MALL); a launch's inputs were
+    # last touched R - 1 launches (>= 1 GiB of traffic) earlier, so they
+    # come from HBM.  HIP events bracket the whole run of R x cold_reps
+    # launches on the launch stream; the cold time is that span over the
+    # launch count (a single launch bracketed by events would also count
+    # the event and dispatch latency around it).
+    in_bytes = {"tq_quantize": keys.numel() * keys.element_size(),
+                "tq_logits": sum(t.numel() * t.element_size() for t in packed),
+                "tq_dequant_mse": packed[0].numel() * 4 + packed[2].numel() * 4}
+    cold, cold_copies = {}, {}
     for i, n in enumerate(names):
-        times = []
+        r = max(2, -(-(1 << 30) // in_bytes[n]))
+        cold_copies[n] = r
+        if n == "tq_quantize":
+            sets = [(keys.clone(), tqm.empty_packed(h, total)) for _ in range(r)]
+            run = [lambda k=k, o=o: tqm.tq_quantize(h, k, out=o, stream=stream) for k, o in sets]
+        elif n == "tq_logits":
+            sets = [(tuple(t.clone() for t in packed), torch.empty_like(scores)) for _ in range(r)]
+            run = [lambda p=p, o=o: tqm.tq_logits(h, queries, *p, n=w.n, scores=o, workspace=ws, stream=stream)
+                   for p, o in sets]
+        else:
+            sets = [((packed[0].clone(), packed[2].clone()), torch.empty_like(khat)) for _ in range(r)]
+            run = [lambda p=p, o=o: tqm.tq_dequant_mse(h, p[0], p[1], khat=o, stream=stream) for p, o in sets]
+        for f in run:  # warm-up round
+            f()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
         for _ in range(args.cold_reps):
-            torch.sum(flush, dim=0, out=sink)
-            torch.cuda.synchronize()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            fns[i]()
-            b.record(stream)
-            torch.cuda.synchronize()
-            times.append(a.elapsed_time(b))
-        cold[n] = float(np.median(times))
-    del flush, sink
+            for f in run:
+                f()
+        b.record(stream)
+        torch.cuda.synchronize()
+        cold[n] = a.elapsed_time(b) / (args.cold_reps * r)
+        del sets, run
+        torch.cuda.empty_cache()
 
     models = kernel_models(w)
     scored = w.groups * w.nq * w.n
@@ -662,7 +682,8 @@ def main():
         ach, ach_cold, unit = kern[n]["GBps"], kern[n]["GBps_cold"], "GB/s"
         return {"kernel": n, "bound": kind, "achieved": ach_cold, "peak": peak, "unit": unit,
                 "frac": round(ach_cold / peak, 4), "traffic": traffic.get(n),
-                "timing": "flushed caches (1 GiB read before each launch), median of the cold reps",
+                "timing": f"cold caches: back-to-back launches over {cold_copies[n]} copies of the inputs "
+                          f"(>= 1 GiB apart), HIP events around all {cold_copies[n] * args.cold_reps} launches",
                 "achieved_in_step": ach, "frac_in_step": round(ach / peak, 4),
                 "bytes_per_key": models[n]["bytes"], "keys_per_launch": total,
                 "mfma_busy_pct": mfma_busy.get(n)}
@@ -685,7 +706,7 @@ def main():
         "config": {"workload": f"{w.name}: {w.description}", "keys": total, "d": w.d, "bits": w.bits,
                    "queries": w.groups * w.nq, "key_dtype": w.key_dtype,
                    "step": "tq_quantize + tq_logits + tq_dequant_mse over the full cache",
-                   "value": "tq_logits (query, key) scores per second with the caches flushed before the launch"},
+                   "value": "tq_logits (query, key) scores per second, inputs read from HBM (cold caches)"},
         "step": {"ms": round(step_ms, 4), "keys_scored_per_s": scored / (step_ms * 1e-3),
                  "tq_quantize_Mkeys_per_s": kern["tq_quantize"]["Mkeys_per_s"]},
         "wall_s": round(wall, 3),
