@@ -378,7 +378,8 @@ def quantize_general_leg(seed, reps=5):
     generators' exact streams are not needed for timing).  Per workload:
     ms per call (mean of `reps` after a warm-up), Mkeys/s, HBM GB/s of keys
     in + packed out, useful matrix flops (4 d^2 per key) and raw matrix
-    flops (3 passes of 2 x 128-row tiles x K per product) against the bf16
+    flops (3 passes of 2 x 128-row tiles x K for Z = Pi K, 2 for P = G R
+    with the seeded float16-exact G) against the bf16
     matrix-core peak."""
     import numpy as np
     import torch
@@ -426,7 +427,7 @@ def quantize_general_leg(seed, reps=5):
         nct = (dpm + 127) // 128
         packed = 4 * (w.bits - 1) * words + 4 * words + 8
         useful = 4.0 * d * d * n / (ms * 1e-3) / 1e12
-        raw = 3 * 2.0 * 128 * nct * (kp + dpm) * n / (ms * 1e-3) / 1e12
+        raw = 2.0 * 128 * nct * (3 * kp + 2 * dpm) * n / (ms * 1e-3) / 1e12
         gbs = (4 * d + packed) * n / (ms * 1e-3) / 1e9
         res[name] = {"keys": n, "d": d, "bits": w.bits, "ms": round(ms, 3), "Mkeys_per_s": round(n / ms / 1e3, 1),
                      "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -667,11 +668,12 @@ def main():
     # (210 flop/B), logits streams 72 bytes per key for 4 queries, and the
     # reconstruction writes 4 d bytes per key; all three are HBM-bound.  The
     # matrix-core work each one really runs is reported beside it: quantize
-    # runs 2 f16 passes for Pi k on power-of-two scaled keys + 3 for G r,
+    # runs 2 f16 passes for Pi k on power-of-two scaled keys + 2 for G r
+    # (G's entries are float16-exact),
     # each 2 d^2 flops; the reconstruction 2 passes when the level set has
     # at most two magnitudes (B <= 2 at d = 128), else 3.
     bound = {n: ("hbm", HBM_PEAK_GBS) for n in names}
-    raw_passes = {"tq_quantize": 10 * w.d * w.d, "tq_dequant_mse": (4 if w.bits <= 3 else 6) * w.d * w.d}
+    raw_passes = {"tq_quantize": 8 * w.d * w.d, "tq_dequant_mse": (4 if w.bits <= 3 else 6) * w.d * w.d}
     for n, f in raw_passes.items():
         kern[n]["raw_mfma_TFLOPs"] = round(f * total / (per[n] * 1e-3) / 1e12, 2)
         kern[n]["mfma_useful_frac"] = round(kern[n]["TFLOPs"] / BF16_MFMA_PEAK_TFLOPS, 4)

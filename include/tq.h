@@ -40,7 +40,8 @@
  * 2i = R cos(2 pi u2), 2i+1 = R sin(2 pi u2)), filling a d x d matrix in row
  * order.  Pi = Q diag(sign(diag R)) from the Householder QR of the stream-0
  * matrix, in float64, then rounded to float32; G is the stream-1 matrix
- * rounded to float32.
+ * rounded to float16 precision (11 significant bits, round to nearest even,
+ * held as float32), so that the matrix cores multiply by it exactly.
  *
  * Packed layout (format version 1), all arrays dense and 4-byte aligned:
  *   codes [n][B][W] uint32   bit p of idx_j at plane p, word j/32, bit j%32

@@ -61,6 +61,16 @@ def gaussian_projection(d, seed):
     return rng.normals(seed, STREAM_PROJECTION, d * d).reshape(d, d)
 
 
+def projection_matrix(d, seed):
+    """The QJL matrix G of a seeded handle: the projection stream's N(0, 1)
+    draws rounded once to float16 precision (11 significant bits, nearest
+    even), as float64.  The pages ask for iid standard normal entries and
+    fix no storage precision; entries with 11 significant bits are exact
+    operands for float16 matrix arithmetic, and the rounding moves each
+    entry by at most 2^-11 of itself."""
+    return gaussian_projection(d, seed).astype(np.float16).astype(np.float64)
+
+
 # ----------------------------------------------------------------------------
 # Lloyd-Max on a density given by its cell mass and cell first moment.
 # ----------------------------------------------------------------------------
@@ -231,7 +241,7 @@ def init(d, bits, seed):
         raise ValueError("bits must lie in [2, 5]")
     levels = 1 << (bits - 1)
     pi = haar_rotation(d, seed).astype(np.float32).astype(np.float64)
-    g = gaussian_projection(d, seed).astype(np.float32).astype(np.float64)
+    g = projection_matrix(d, seed)
     c64, _ = sphere_codebook_fp64(d, levels)
     c32 = c64.astype(np.float32).astype(np.float64)
     return Params(d, bits, int(seed), pi, g, c32, thresholds_from_centroids(c32))
@@ -279,7 +289,7 @@ def init_hadamard(d, bits, seed):
         raise ValueError("bits must lie in [2, 5]")
     levels = 1 << (bits - 1)
     pi = hadamard_rotation(d, seed)
-    g = gaussian_projection(d, seed).astype(np.float32).astype(np.float64)
+    g = projection_matrix(d, seed)
     c64, _ = sphere_codebook_fp64(d, levels)
     c32 = c64.astype(np.float32).astype(np.float64)
     return Params(d, bits, int(seed), pi, g, c32, thresholds_from_centroids(c32))

@@ -48,6 +48,7 @@ def test_host_params_match_oracle(tqm, d, bits, seed):
     assert _ulps(pi, pr.pi).max() <= 1
     assert (_ulps(pi, pr.pi) > 0).mean() < 1e-4
     assert np.array_equal(g, pr.g.astype(np.float32))
+    assert np.array_equal(g.astype(np.float16).astype(np.float32), g)  # float16-exact G
     assert _ulps(c, pr.centroids).max() <= 1
     assert _ulps(t, pr.thresholds).max() <= 1
 

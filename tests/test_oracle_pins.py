@@ -619,6 +619,27 @@ def test_hadamard_rotation_definition_and_pages_example():
     assert np.array_equal(z, np.array(g["expected"]))
 
 
+def test_projection_matrix_is_the_nearest_float16_of_each_draw():
+    """G keeps the projection stream's N(0, 1) draws to float16 precision:
+    every entry is a float16 value and no float16 value lies closer to the
+    draw (ties at exactly half a spacing allowed); the rounding leaves the
+    law standard normal (KS), and in the float16 normal range keeps every
+    draw's sign and moves it by at most 2^-11 of itself."""
+    for d, seed in ((64, 3), (200, 0)):
+        raw = P.gaussian_projection(d, seed)
+        g = P.projection_matrix(d, seed)
+        h = g.astype(np.float16)
+        assert np.array_equal(h.astype(np.float64), g)
+        up = np.nextafter(h, np.float16(np.inf)).astype(np.float64)
+        dn = np.nextafter(h, np.float16(-np.inf)).astype(np.float64)
+        err = np.abs(g - raw)
+        assert np.all(err <= np.abs(up - raw)) and np.all(err <= np.abs(dn - raw))
+        normal = np.abs(raw) >= 2.0 ** -14  # float16 normal range
+        assert np.all(np.sign(g[normal]) == np.sign(raw[normal]))
+        assert np.max(err[normal] / np.abs(raw[normal])) <= 2.0 ** -11
+        assert stats.kstest(g.ravel(), "norm").pvalue > 1e-3
+
+
 def test_hadamard_signs_balanced_and_seeded():
     """Stream-2 signs: +-1 with mean within 4 standard errors of 0; distinct
     seeds give distinct sign vectors, the same seed the same one."""

@@ -442,8 +442,10 @@ int build_params(int d, int bits, uint64_t seed, float* pi, float* g, float* cen
     for (size_t i = 0; i < dd; ++i) pi[i] = float(q[i]);
   }
   if (g) {
+    // float16 precision (one rounding from float64): exact as a matrix-core
+    // operand, so the projection needs no second piece of G
     normal_draws(seed, 1, dd, buf.data());
-    for (size_t i = 0; i < dd; ++i) g[i] = float(buf[i]);
+    for (size_t i = 0; i < dd; ++i) g[i] = float(static_cast<_Float16>(buf[i]));
   }
   if (centroids || thresholds) {
     const int levels = 1 << (bits - 1);

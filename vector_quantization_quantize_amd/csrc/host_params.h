@@ -34,7 +34,8 @@ int polar_level_codebook(int d, int bits, int level, float* levels, float* thres
 int hadamard_rotation(int d, uint64_t seed, float* pi);
 
 // Fill any of pi, g (float[d*d]), centroids (float[L]), thresholds
-// (float[L-1]); NULL outputs are skipped.  Returns 0, or < 0 on bad
+// (float[L-1]); NULL outputs are skipped.  g holds the stream-1 draws
+// rounded to float16 precision.  Returns 0, or < 0 on bad
 // arguments / non-convergence.
 int build_params(int d, int bits, uint64_t seed, float* pi, float* g, float* centroids,
                  float* thresholds);

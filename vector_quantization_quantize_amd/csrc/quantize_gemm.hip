@@ -25,7 +25,8 @@
 //   * 2^12 Pi, 2^10 G and 2^12 r are split the same way; hi*hi + hi*lo +
 //     lo*hi (3 passes of 32 x 32 x 16 f16 MFMA) leave a representation error
 //     near 2^-22 of the terms' magnitudes, and the power-of-two scales keep
-//     every decision's sign and threshold;
+//     every decision's sign and threshold; a seeded G has float16-exact
+//     entries, whose lo piece is zero: its projection runs 2 passes;
 //   * the rotation accumulates each run of 8 K steps (128 input coordinates)
 //     in fresh matrix-core accumulators and adds it into float32 running
 //     sums: float32 accumulation over d = 1536 terms in one chain would move
@@ -411,7 +412,9 @@ qg_wht_kernel(const void* __restrict__ keys, int64_t nkeys, int64_t ldk, int vec
 
 // ---------------------------------------------------------------------------
 // 2. / 3. the tiled products.  MODE 0: rotate + bucketize (B operand: the
-// key pieces); MODE 1: project + signs (B operand: the residual pieces).
+// key pieces); MODE 1: project + signs (B operand: the residual pieces);
+// MODE 2: MODE 1 for a G whose entries are exact in float16 (its lo piece
+// is zero, so the lo x hi pass is skipped).
 // ---------------------------------------------------------------------------
 struct QArgs {
   const uint16_t* atiles;  // operand tiles of this matrix
@@ -562,7 +565,8 @@ __global__ void __launch_bounds__(kThreads, 1) qgemm_kernel(QArgs a) {
       for (int j = 0; j < 2; ++j) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.ah[i], cur.bh[j], acc[i][j], 0, 0, 0);
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.ah[i], cur.bl[j], acc[i][j], 0, 0, 0);
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.al[i], cur.bh[j], acc[i][j], 0, 0, 0);
+        if constexpr (MODE != 2)  // MODE 2: A exact in one float16 piece
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.al[i], cur.bh[j], acc[i][j], 0, 0, 0);
       }
     ++m_s;
     if constexpr (MODE == 0) {
@@ -906,7 +910,10 @@ hipError_t launch_quantize_gemm(tq_ctx* h, const void* keys, int key_dtype, int6
       pro.items = items;
       pro.tiles = tiles;
       const dim3 grid{static_cast<uint32_t>(std::min<int64_t>(items, h->cus))};
-      hipLaunchKernelGGL((qgemm_kernel<1, 0>), grid, dim3(kThreads), 0, stream, pro);
+      if (h->g_f16)
+        hipLaunchKernelGGL((qgemm_kernel<2, 0>), grid, dim3(kThreads), 0, stream, pro);
+      else
+        hipLaunchKernelGGL((qgemm_kernel<1, 0>), grid, dim3(kThreads), 0, stream, pro);
       e = hipGetLastError();
       continue;
     }
@@ -939,11 +946,12 @@ hipError_t launch_quantize_gemm(tq_ctx* h, const void* keys, int key_dtype, int6
     rot.items = pro.items = items;
     rot.tiles = pro.tiles = tiles;
     const dim3 grid{static_cast<uint32_t>(blocks)};
+    auto project = h->g_f16 ? qgemm_kernel<2, 0> : qgemm_kernel<1, 0>;
     switch (h->code_bits) {
-      case 1: e = launch_pair(rot, qgemm_kernel<0, 1>, pro, qgemm_kernel<1, 0>, grid, stream); break;
-      case 2: e = launch_pair(rot, qgemm_kernel<0, 2>, pro, qgemm_kernel<1, 0>, grid, stream); break;
-      case 3: e = launch_pair(rot, qgemm_kernel<0, 3>, pro, qgemm_kernel<1, 0>, grid, stream); break;
-      default: e = launch_pair(rot, qgemm_kernel<0, 4>, pro, qgemm_kernel<1, 0>, grid, stream); break;
+      case 1: e = launch_pair(rot, qgemm_kernel<0, 1>, pro, project, grid, stream); break;
+      case 2: e = launch_pair(rot, qgemm_kernel<0, 2>, pro, project, grid, stream); break;
+      case 3: e = launch_pair(rot, qgemm_kernel<0, 3>, pro, project, grid, stream); break;
+      default: e = launch_pair(rot, qgemm_kernel<0, 4>, pro, project, grid, stream); break;
     }
   }
   if (e != hipSuccess) return e;

@@ -16,10 +16,12 @@
 //     significant bits, 2 MFMA passes), every product is exact and only the
 //     float32 accumulation rounds; the representation error is at most
 //     2^-22 ||Pi_i|| ||k||, i.e. 2^-22 in units of z.
-//   * p = G r: G * 2^10 and r * 2^12 are each split into two float16 pieces
-//     (22 bits); hi*hi + hi*lo + lo*hi (3 passes) leaves an error near
-//     2^-21 sum_j |G_mj r_j|, far under 1e-6 of the JL-normalised value
-//     p/sqrt(d).  The power-of-two scales do not change signs.
+//   * p = G r: r * 2^12 is split into two float16 pieces (22 bits).  A
+//     seeded G has float16-exact entries, so G * 2^10 is one exact piece and
+//     G r_hi + G r_lo (2 passes) rounds only in the accumulation; a G given
+//     by the caller is split too and hi*hi + hi*lo + lo*hi (3 passes) leaves
+//     an error near 2^-21 sum_j |G_mj r_j|.  The power-of-two scales do not
+//     change signs.
 //   * n = ||k|| in float32 from the bf16 key: sixteen-term partial sums in
 //     eight lanes, then a three-level tree.
 //
@@ -174,7 +176,9 @@ struct Quantizer {
   }
 };
 
-template <int B>
+// G3: G needs two float16 pieces (three passes for p = G r); without it
+// (G exact in float16) the G lo pass is skipped
+template <int B, bool G3>
 __global__ void __launch_bounds__(kQThreads, 2)
 quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ldk,
                         const uint4* __restrict__ pi_frag, const uint4* __restrict__ g_frag, HalfCodebook hc,
@@ -206,7 +210,8 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       api[s][q] = __builtin_bit_cast(f16x8, pi_frag[((w * kSteps + s) * 2 + q) * 64 + lane]);
-      ag[s][q] = __builtin_bit_cast(f16x8, g_frag[((w * kSteps + s) * 2 + q) * 64 + lane]);
+      ag[s][q] = G3 || q == 0 ? __builtin_bit_cast(f16x8, g_frag[((w * kSteps + s) * 2 + q) * 64 + lane])
+                              : f16x8{};
     }
   Q quant;
 #pragma unroll
@@ -404,7 +409,7 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
       const int r1 = 15 - 2 * s, r0 = r1 - 1;  // pair s
       f16x8 nrh = rh, nrl = rl;
       if (s + 1 < kSteps) nrh = __builtin_bit_cast(f16x8, xb[ob][0][s + 1][g][kl]);
-      acc2 = mfma16(ag[s][1], rh, acc2);
+      if constexpr (G3) acc2 = mfma16(ag[s][1], rh, acc2);
       if (s + 1 < kSteps) {
         e[r1 - 2] = quant(zt[r1 - 2], inv, us, sgn, jw);
         TQ_PIN(e[r1 - 2]);
@@ -549,7 +554,7 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
     for (int s = 0; s < kSteps; ++s) {
       const f16x8 rh = __builtin_bit_cast(f16x8, xb[buf][0][s][g][kl]);
       const f16x8 rl = __builtin_bit_cast(f16x8, xb[buf][1][s][g][kl]);
-      acc2 = mfma16(ag[s][1], rh, acc2);
+      if constexpr (G3) acc2 = mfma16(ag[s][1], rh, acc2);
       acc2 = mfma16(ag[s][0], rl, acc2);
       acc2 = mfma16(ag[s][0], rh, acc2);
     }
@@ -609,7 +614,8 @@ hipError_t launch_b(const tq_ctx* h, const void* keys, int64_t n, int64_t ldk, u
     half = blocks;
     lead = tiles;
   }
-  hipLaunchKernelGGL(quantize_mfma128_kernel<B>, dim3(static_cast<uint32_t>(blocks)), dim3(kQThreads), 0, stream,
+  auto kernel = h->g_f16 ? quantize_mfma128_kernel<B, false> : quantize_mfma128_kernel<B, true>;
+  hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kQThreads), 0, stream,
                      static_cast<const uint16_t*>(keys), n, ldk, reinterpret_cast<const uint4*>(h->d_pi_frag),
                      reinterpret_cast<const uint4*>(h->d_g_frag), h->half, codes, signs, norms, rnorms, tiles, half,
                      lead);

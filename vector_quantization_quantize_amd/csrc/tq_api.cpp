@@ -228,6 +228,13 @@ int finish_init(tq_ctx* h) {
   plane_expansion(h->centroids, h->code_bits, &h->planes);
   dequant_table(h->centroids, &h->dqt);
   {
+    // G with float16-exact entries (every seeded handle) takes one matrix-core
+    // piece in the projection instead of two
+    bool f16 = true;
+    for (const float x : h->g) f16 = f16 && float(static_cast<_Float16>(x)) == x;
+    h->g_f16 = f16;
+  }
+  {
     const int L = h->levels, M = L / 2;
     bool sym = h->thresholds[M - 1] == 0.0f;
     for (int i = 0; i < L; ++i) sym = sym && h->centroids[L - 1 - i] == -h->centroids[i];

@@ -82,6 +82,7 @@ struct tq_ctx {
   tqdev::DequantTable dqt{};
   // randomized Hadamard rotation (tq_init_hadamard): Pi = H diag(sigma) c
   // with c = float32(1 / sqrt(d)); d_hsigma holds sigma (float +-1)
+  bool g_f16 = false;  // every entry of G is exact in float16
   int hadamard = 0;
   float hscale = 0.0f;
   float* d_hsigma = nullptr;
