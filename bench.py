@@ -309,6 +309,39 @@ def split_leg(w, keys, queries, scores, khat, seed, stream, reps=3):
     return res
 
 
+def toy_leg(seed, reps=50):
+    """The toy workload (4096 float32 keys, d = 128, 3 bits, 16 queries):
+    latency of tq_quantize and tq_logits, mean of `reps` back-to-back calls
+    after a warm-up (inputs stay in cache at this size)."""
+    import torch
+
+    import vector_quantization_quantize_amd as tqm
+    from vector_quantization_quantize_amd import workloads as wl
+    w = wl.WORKLOADS["toy"]
+    keys = torch.from_numpy(wl.keys(w, seed)).cuda()
+    queries = torch.from_numpy(wl.queries(w, seed)).cuda()
+    h = tqm.tq_init(w.d, w.bits, 0)
+    packed = tqm.tq_quantize(h, keys)
+    scores = torch.empty((w.groups, w.nq, w.n), dtype=torch.float32, device="cuda")
+    lws = torch.empty(tqm.tq_logits_workspace_size(h, w.groups, w.nq) // 4 + 64, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return round(a.elapsed_time(b) / reps * 1e3, 2)
+
+    return {"workload": f"{w.name}: {w.description}",
+            "tq_quantize_us": timed(lambda: tqm.tq_quantize(h, keys, out=packed)),
+            "tq_logits_us": timed(lambda: tqm.tq_logits(h, queries, *packed, n=w.n, scores=scores, workspace=lws))}
+
+
 def decode_leg(seed, reps=50):
     """One decode step at the llama_decode shape (8 key heads x 32768 bf16
     tokens, 4 query heads per key head, d = 128, 4 bits): latency of
@@ -348,6 +381,7 @@ def decode_leg(seed, reps=50):
         return a.elapsed_time(b) / reps * 1e3
 
     res = {"workload": f"{w.name}: {w.description}",
+           "tq_quantize_us": timed(lambda: tqm.tq_quantize(h, keys, out=packed)),
            "tq_logits_us": timed(lambda: tqm.tq_logits(h, queries, *packed, n=w.n, scores=scores, workspace=lws)),
            "tq_attention_us": timed(lambda: tqm.tq_attention(h, hv, queries, *packed, vblocks, vn, n=w.n, out=out,
                                                              lse=lse, workspace=aws)),
@@ -724,6 +758,7 @@ def main():
     if not args.no_attention:
         line["attention"] = attention_leg(w, h, keys, queries, packed, args.seed, stream)
         line["decode_step"] = decode_leg(args.seed)
+        line["toy"] = toy_leg(args.seed)
         line["dequant_prod"] = dequant_prod_leg(w, h, packed, khat, stream)
     if not args.no_split:
         line["fractional_widths"] = split_leg(w, keys, queries, scores, khat, args.seed, stream)

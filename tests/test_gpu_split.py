@@ -51,18 +51,23 @@ def _keys(rs, n, d):
 # (one partial extra word, several words, hi = d), tiny and wide d
 # d = 128 with hi = 64 also takes the matrix-core reconstruction (ragged
 # tile counts: 300, 257, 4097 keys)
-CASES = [(128, 2, 64, 1, 300, 4), (128, 3, 64, 2, 257, 3), (128, 4, 64, 1, 4097, 2), (40, 2, 16, 1, 77, 5),
-         (33, 3, 33, 2, 65, 2), (200, 4, 100, 1, 50, 6), (128, 4, 1, 1, 129, 2), (2, 2, 1, 1, 9, 1),
-         (300, 2, 257, 1, 40, 3)]
+# bf16 keys at d = 128, hi = 64 take the matrix-core quantizer (two waves
+# with the finer set; 300, 257 and 4097 keys leave ragged last tiles whose
+# code rows end inside a 16-byte row)
+CASES = [(128, 2, 64, 1, 300, 4, "f32"), (128, 3, 64, 2, 257, 3, "f32"), (128, 4, 64, 1, 4097, 2, "f32"),
+         (40, 2, 16, 1, 77, 5, "f32"), (33, 3, 33, 2, 65, 2, "f32"), (200, 4, 100, 1, 50, 6, "f32"),
+         (128, 4, 1, 1, 129, 2, "f32"), (2, 2, 1, 1, 9, 1, "f32"), (300, 2, 257, 1, 40, 3, "f32"),
+         (128, 2, 64, 1, 300, 4, "bf16"), (128, 3, 64, 2, 257, 3, "bf16"), (128, 4, 64, 1, 4097, 2, "bf16"),
+         (128, 3, 64, 1, 70001, 2, "bf16")]
 
 
-@pytest.mark.parametrize("d,bits,hi,groups,n,nq", CASES)
-def test_split_matches_oracle(env, d, bits, hi, groups, n, nq):
+@pytest.mark.parametrize("d,bits,hi,groups,n,nq,key_dtype", CASES)
+def test_split_matches_oracle(env, d, bits, hi, groups, n, nq, key_dtype):
     """Quantize (codes, signs, norms bit for bit outside the decision
     windows), scores of the oracle's packed keys and of the library's own,
     both reconstructions, and the layout's sizes."""
     torch, tqm = env
-    _announce(f"split d={d} bits={bits} hi={hi} groups={groups} n={n} nq={nq}")
+    _announce(f"split d={d} bits={bits} hi={hi} groups={groups} n={n} nq={nq} {key_dtype}")
     pr = P.init_split(d, bits, hi, 11)
     h = tqm.tq_init_split(d, bits, hi, 11)
     w = tq.words_per_plane(d)
@@ -70,8 +75,14 @@ def test_split_matches_oracle(env, d, bits, hi, groups, n, nq):
     assert h.layout.code_bytes == 4 * ((bits - 1) * w + (hi + 31) // 32)
     rs = np.random.default_rng(d * 7 + hi)
     keys = _keys(rs, groups * n, d).astype(np.float32)
+    keys[min(2, groups * n - 1)] = 0.0  # a zero key
     queries = rs.standard_normal((groups, nq, d)).astype(np.float32)
-    codes, signs, norms, rnorms = tqm.tq_quantize(h, _dev(torch, keys))
+    if key_dtype == "bf16":
+        kd = _dev(torch, keys).to(torch.bfloat16)
+        keys = kd.float().cpu().numpy()
+    else:
+        kd = _dev(torch, keys)
+    codes, signs, norms, rnorms = tqm.tq_quantize(h, kd)
     torch.cuda.synchronize()
     assert tuple(codes.shape) == (groups * n, (bits - 1) * w + (hi + 31) // 32)
     qz = tq.quantize(pr, keys.astype(np.float64))

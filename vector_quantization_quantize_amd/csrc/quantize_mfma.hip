@@ -33,6 +33,13 @@
 // j, flipped for z < 0.  A sign bit of p = +0 (only possible when G r
 // cancels exactly) is stored as 1, also inside the tie window.
 //
+// Fractional widths (a finer level set with one more index bit on the first
+// hi = 64 coordinates): the two waves that own those coordinates bucketize
+// with the finer set (same symmetric form, B + 1 bits) and write the extra
+// index plane to the words after the B full planes of each code row; the
+// other two waves run the ordinary passes.  Both kinds of wave go through
+// the same passes and barriers.
+//
 // Work split: a block of 4 waves takes 32 keys at a time (one 32 x 32 x 16
 // MFMA tile in N); wave w owns output coordinates [32w, 32w + 32), i.e. bit
 // word w of every plane, and keeps its slices of Pi and G (two float16
@@ -177,12 +184,17 @@ struct Quantizer {
 };
 
 // G3: G needs two float16 pieces (three passes for p = G r); without it
-// (G exact in float16) the G lo pass is skipped
-template <int B, bool G3>
-__global__ void __launch_bounds__(kQThreads, 2)
+// (G exact in float16) the G lo pass is skipped.  HW: words of the extra
+// index plane of fractional widths (hi = 32 HW coordinates with the finer
+// level set hch and one more index bit; waves w < HW own exactly those
+// coordinates), 0 for one level set.
+// Two waves per SIMD (two blocks per CU) and no more: the slices of Pi and
+// G stay in registers, so the register budget is that of two waves.
+template <int B, bool G3, int HW>
+__global__ void __launch_bounds__(kQThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ldk,
                         const uint4* __restrict__ pi_frag, const uint4* __restrict__ g_frag, HalfCodebook hc,
-                        uint32_t* __restrict__ codes, uint32_t* __restrict__ signs, float* __restrict__ norms,
+                        HalfCodebook hch, uint32_t* __restrict__ codes, uint32_t* __restrict__ signs, float* __restrict__ norms,
                         float* __restrict__ rnorms, int64_t tiles, int64_t half, int64_t lead_tiles) {
   using Q = Quantizer<B>;
   // scaled float16 keys, double buffered: 32 rows of 128 halves, row stride
@@ -192,11 +204,13 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
   // residual exchange [buf][piece][step][lane group][key] (8 halves each)
   __shared__ uint4 xb[2][2][kSteps][2][32];
   __shared__ float rsq[2][4][32];
-  // output staging, by tile parity: the tile's 32 B code rows, the previous
-  // tile's 32 sign rows, 8 rows of this tile's norms, 8 rows of the previous
-  // tile's rnorms (16 bytes each, the order they have in memory)
-  constexpr int kOutRows = 32 * B + 48;
-  constexpr int kRowS = 32 * B, kRowN = kRowS + 32, kRowR = kRowN + 8;
+  // output staging, by tile parity: the tile's code block (32 code rows of
+  // CR words), the previous tile's 32 sign rows, 8 rows of this tile's
+  // norms, 8 rows of the previous tile's rnorms (16 bytes each, the order
+  // they have in memory)
+  constexpr int CR = 4 * B + HW;  // words of a key's code row
+  constexpr int kOutRows = 8 * CR + 48;
+  constexpr int kRowS = 8 * CR, kRowN = kRowS + 32, kRowR = kRowN + 8;
   __shared__ uint4 ost[2][kOutRows];
 
   const int w = threadIdx.x >> 6;
@@ -213,11 +227,8 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
       ag[s][q] = G3 || q == 0 ? __builtin_bit_cast(f16x8, g_frag[((w * kSteps + s) * 2 + q) * 64 + lane])
                               : f16x8{};
     }
-  Q quant;
-#pragma unroll
-  for (int k = 0; k < Q::M; ++k) quant.m[k] = hc.m[k];
-#pragma unroll
-  for (int k = 0; k + 1 < Q::M; ++k) quant.u[k] = hc.u[k];
+  // the finer level set (one more index bit) of the waves below HW
+  using QF = Quantizer<(HW > 0 ? B + 1 : B)>;
 
   // staging: thread t owns bf16 elements [16 (t % 8), +16) of key t / 8.
   // Rows are fetched in tile order, one call per tile.  Rows past the end
@@ -341,12 +352,12 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
   // of the code rows
   auto out_ptr = [&](int r, int64_t c) -> uint4* {
     const int64_t pc = c - tstride;
-    if (r < kRowS) return codes4 + c * (32 * B) + r;
+    if (r < kRowS) return codes4 + c * (8 * CR) + r;
     if (r < kRowN) return signs4 + pc * 32 + (r - kRowS);
     if (r < kRowR) return norms4 + c * 8 + (r - kRowN);
     return rnorms4 + pc * 8 + (r - kRowR);
   };
-  const int64_t ostep = (orow < kRowS ? 32 * B : orow < kRowN ? 32 : 8) * tstride;
+  const int64_t ostep = (orow < kRowS ? 8 * CR : orow < kRowN ? 32 : 8) * tstride;
   uint4* optr = nullptr;  // this lane's destination in the next copy-out (from the third pass on)
 
   // Lanes l and l ^ 32 hold the low and high 16 bits of a word; every lane
@@ -371,9 +382,19 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
   // (staged sign rows and rnorms belong to no tile: those lanes repeat a code
   // or norm row instead), 2 after.  Every tile but the last of the block is
   // full, so copy-outs need no bounds.
-  auto pass = [&](int64_t i, auto bufc, auto phasec) {
+  auto pass = [&](int64_t i, auto bufc, auto phasec, auto finec) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
     constexpr int phase = decltype(phasec)::value;
+    constexpr bool fine = decltype(finec)::value;  // this wave's coordinates take the finer set
+    using QP = std::conditional_t<fine, QF, Q>;
+    // the wave's level set, from the kernel arguments (uniform values)
+    const HalfCodebook& hq = fine ? hch : hc;
+    QP qz;
+#pragma unroll
+    for (int k = 0; k < QP::M; ++k) qz.m[k] = hq.m[k];
+#pragma unroll
+    for (int k = 0; k + 1 < QP::M; ++k) qz.u[k] = hq.u[k];
+    constexpr int NP = fine ? B + 1 : B;  // index planes of this wave's coordinates
     constexpr bool first = phase == 0;
     constexpr int ob = buf ^ 1;
     uint4 ov;       // staged row of this lane
@@ -386,15 +407,15 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
     f16x8 rl = __builtin_bit_cast(f16x8, xb[ob][1][0][g][kl]);
     const f32x16 zt = acc1;
     const float inv = info.x, nrm = info.y;
-    float us[Q::NU];
+    float us[QP::NU];
 #pragma unroll
-    for (int k = 0; k + 1 < Q::M; ++k) us[k] = quant.u[k] * info.z;
-    uint32_t sgn = 0u, jw[Q::NJ];
+    for (int k = 0; k + 1 < QP::M; ++k) us[k] = qz.u[k] * info.z;
+    uint32_t sgn = 0u, jw[QP::NJ];
 #pragma unroll
-    for (int p = 0; p < Q::NJ; ++p) jw[p] = 0u;
+    for (int p = 0; p < QP::NJ; ++p) jw[p] = 0u;
     float e[16];  // scaled residuals, coordinates processed from 15 down
-    e[15] = quant(zt[15], inv, us, sgn, jw);
-    e[14] = quant(zt[14], inv, us, sgn, jw);
+    e[15] = qz(zt[15], inv, us, sgn, jw);
+    e[14] = qz(zt[14], inv, us, sgn, jw);
     TQ_PIN(e[15]);
     TQ_PIN(e[14]);
     TQ_SLOT_END();
@@ -411,7 +432,7 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
       if (s + 1 < kSteps) nrh = __builtin_bit_cast(f16x8, xb[ob][0][s + 1][g][kl]);
       if constexpr (G3) acc2 = mfma16(ag[s][1], rh, acc2);
       if (s + 1 < kSteps) {
-        e[r1 - 2] = quant(zt[r1 - 2], inv, us, sgn, jw);
+        e[r1 - 2] = qz(zt[r1 - 2], inv, us, sgn, jw);
         TQ_PIN(e[r1 - 2]);
       }
       if constexpr (phase == 1) {
@@ -435,7 +456,7 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
       if (s + 1 < kSteps) nrl = __builtin_bit_cast(f16x8, xb[ob][1][s + 1][g][kl]);
       acc2 = mfma16(ag[s][0], rl, acc2);
       if (s + 1 < kSteps) {
-        e[r0 - 2] = quant(zt[r0 - 2], inv, us, sgn, jw);
+        e[r0 - 2] = qz(zt[r0 - 2], inv, us, sgn, jw);
         TQ_PIN(e[r0 - 2]);
       }
       TQ_SLOT_END();
@@ -459,7 +480,7 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
     f32x16 a1 = {};
     Stage st;
     uint32_t sw = 0u;
-    uint32_t word[B + 1];  // planes 0..B-1, then the sign word of tile i-1
+    uint32_t word[NP + 1];  // index planes 0..NP-1, then the sign word of tile i-1
     float prn = 0.0f;      // rho of tile i-1
     f16x8 nkf = kf;        // next step's keys, read one step ahead
 #pragma unroll
@@ -486,31 +507,33 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
           // 16-bit halves: plane B-1 = [z >= 0], plane p = j_p ^ [z < 0],
           // signs = [p > 0]
 #pragma unroll
-          for (int p = 0; p + 1 < B; ++p) word[p] = jw[p] ^ sgn;
-          word[B - 1] = sgn ^ 0xFFFFu;
-          word[B] = sw ^ 0xFFFFu;
+          for (int p = 0; p + 1 < NP; ++p) word[p] = jw[p] ^ sgn;
+          word[NP - 1] = sgn ^ 0xFFFFu;
+          word[NP] = sw ^ 0xFFFFu;
           if (!first) prn = rnorm_of(ob);
           break;
         case 7: stage_reduce(st, 1); break;
         case 8:
 #pragma unroll
-          for (int p = 0; p <= B; ++p) word[p] = whole(word[p]);
+          for (int p = 0; p <= NP; ++p) word[p] = whole(word[p]);
           break;
         case 9: stage_reduce(st, 2); break;
         case 10: rsq[buf][w][kl] = both_sum(rr); break;
         case 11: stage_norm(st); break;
         case 12: {
-          // word w of this tile's code rows and of the previous tile's sign
-          // rows (lane group g takes every other word; with B even the last
-          // word goes twice), this tile's norm (g = 0) and the previous
-          // tile's rho (g = 1)
+          // word w of this tile's code rows (planes 0..B-1 at 4 p + w, the
+          // extra plane of the finer coordinates at 4 B + w) and of the
+          // previous tile's sign rows (lane group g takes every other word;
+          // with an even count the last word goes twice), this tile's norm
+          // (g = 0) and the previous tile's rho (g = 1)
           uint32_t* o32 = reinterpret_cast<uint32_t*>(ost[buf]);
+          auto addr = [&](int p) {
+            return p < B ? kl * CR + 4 * p + w : p < NP ? kl * CR + 4 * B + w : (kRowS + kl) * 4 + w;
+          };
 #pragma unroll
-          for (int q = 0; 2 * q <= B; ++q) {
-            const int p0 = 2 * q, p1 = 2 * q + 1 <= B ? 2 * q + 1 : B;
-            const int a0 = (p0 < B ? kl * B + p0 : kRowS + kl) * 4 + w;
-            const int a1 = (p1 < B ? kl * B + p1 : kRowS + kl) * 4 + w;
-            o32[g ? a1 : a0] = g ? word[p1] : word[p0];
+          for (int q = 0; 2 * q <= NP; ++q) {
+            const int p0 = 2 * q, p1 = 2 * q + 1 <= NP ? 2 * q + 1 : NP;
+            o32[g ? addr(p1) : addr(p0)] = g ? word[p1] : word[p0];
           }
           reinterpret_cast<float*>(&ost[buf][kRowN])[32 * g + kl] = g ? prn : nrm;
           break;
@@ -529,14 +552,24 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
   // After the last pass (tile i): the rows it staged, bounded by n since its
   // tile may be the ragged last one, then p of tile i and its sign words and
   // rho, written directly (rows past the end go to key n - 1, same value).
-  auto finish = [&](int64_t i, auto bufc) {
+  auto finish = [&](int64_t i, auto bufc) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
     const int64_t c = tstart + i * tstride;
     const int64_t left = n - c * 32;
     const int vk = left < 32 ? static_cast<int>(left) : 32;  // keys of tile c
     const uint4 v = ost[buf][orow];
     if (orow < kRowS) {
-      if (orow < vk * B) *out_ptr(orow, c) = v;
+      // the code words of the tile's vk keys (a row may end inside one)
+      const int vw = vk * CR;
+      if (4 * orow + 4 <= vw) {
+        *out_ptr(orow, c) = v;
+      } else if (4 * orow < vw) {
+        uint32_t* d32 = reinterpret_cast<uint32_t*>(out_ptr(orow, c));
+        const int left = vw - 4 * orow;  // 1 .. 3
+        d32[0] = v.x;
+        if (left > 1) d32[1] = v.y;
+        if (left > 2) d32[2] = v.z;
+      }
     } else if (orow < kRowN || orow >= kRowR) {
       if (i > 0) *out_ptr(orow, c) = v;  // the tile before c, if any
     } else {
@@ -569,22 +602,34 @@ quantize_mfma128_kernel(const uint16_t* __restrict__ keys, int64_t n, int64_t ld
   constexpr std::integral_constant<int, 0> kFirst{};
   constexpr std::integral_constant<int, 1> kSecond{};
   constexpr std::integral_constant<int, 2> kLater{};
-  pass(0, kBuf0, kFirst);
-  if (ntile == 1) {
-    finish(0, kBuf0);
-    return;
-  }
-  pass(1, kBuf1, kSecond);
-  int64_t i = 2;
-  for (; i + 1 < ntile; i += 2) {
-    pass(i, kBuf0, kLater);
-    pass(i + 1, kBuf1, kLater);
-  }
-  if (i < ntile) {
-    pass(i, kBuf0, kLater);
-    finish(i, kBuf0);
+  // the same sequence of passes and barriers for every wave; waves whose
+  // coordinates take the finer level set run the passes built for it
+  auto run = [&](auto finec) __attribute__((always_inline)) {
+    pass(0, kBuf0, kFirst, finec);
+    if (ntile == 1) {
+      finish(0, kBuf0);
+      return;
+    }
+    pass(1, kBuf1, kSecond, finec);
+    int64_t i = 2;
+    for (; i + 1 < ntile; i += 2) {
+      pass(i, kBuf0, kLater, finec);
+      pass(i + 1, kBuf1, kLater, finec);
+    }
+    if (i < ntile) {
+      pass(i, kBuf0, kLater, finec);
+      finish(i, kBuf0);
+    } else {
+      finish(i - 1, kBuf1);
+    }
+  };
+  if constexpr (HW > 0) {
+    if (__builtin_amdgcn_readfirstlane(w) < HW)
+      run(std::true_type{});
+    else
+      run(std::false_type{});
   } else {
-    finish(i - 1, kBuf1);
+    run(std::false_type{});
   }
 }
 
@@ -614,11 +659,18 @@ hipError_t launch_b(const tq_ctx* h, const void* keys, int64_t n, int64_t ldk, u
     half = blocks;
     lead = tiles;
   }
-  auto kernel = h->g_f16 ? quantize_mfma128_kernel<B, false> : quantize_mfma128_kernel<B, true>;
+  auto kernel = h->g_f16 ? quantize_mfma128_kernel<B, false, 0> : quantize_mfma128_kernel<B, true, 0>;
+  if (h->hi > 0) {
+    // fractional widths: hi = 64, seeded G (checked by the caller)
+    if constexpr (B <= 3)
+      kernel = quantize_mfma128_kernel<B, false, 2>;
+    else
+      return hipErrorInvalidValue;
+  }
   hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kQThreads), 0, stream,
                      static_cast<const uint16_t*>(keys), n, ldk, reinterpret_cast<const uint4*>(h->d_pi_frag),
-                     reinterpret_cast<const uint4*>(h->d_g_frag), h->half, codes, signs, norms, rnorms, tiles, half,
-                     lead);
+                     reinterpret_cast<const uint4*>(h->d_g_frag), h->half, h->half_hi, codes, signs, norms, rnorms,
+                     tiles, half, lead);
   return hipGetLastError();
 }
 
@@ -627,7 +679,10 @@ hipError_t launch_b(const tq_ctx* h, const void* keys, int64_t n, int64_t ldk, u
 bool quantize_mfma128_supported(const tq_ctx* h, const void* keys, int key_dtype, int64_t ldk,
                                 const void* codes, const void* signs, const void* norms, const void* rnorms) {
   auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-  return h->d == 128 && h->hi == 0 && key_dtype == TQ_BF16 && h->d_pi_frag && h->d_g_frag && h->symmetric && ldk >= 128 &&
+  // fractional widths: the finer set on the first 64 coordinates (two waves'
+  // words), symmetric too, B + 1 <= 4 index bits there, seeded G
+  const bool widths = h->hi == 0 || (h->hi == 64 && h->symmetric_hi && h->g_f16 && h->code_bits <= 3);
+  return h->d == 128 && widths && key_dtype == TQ_BF16 && h->d_pi_frag && h->d_g_frag && h->symmetric && ldk >= 128 &&
          (ldk % 8) == 0 && a16(keys) && a16(codes) && a16(signs) && a16(norms) && a16(rnorms) &&
          h->code_bits >= 1 && h->code_bits <= 4;
 }

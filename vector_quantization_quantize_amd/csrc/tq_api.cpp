@@ -243,6 +243,16 @@ int finish_init(tq_ctx* h) {
     for (int j = 0; j < M; ++j) h->half.m[j] = h->centroids[M + j] * 4096.0f;
     for (int k = 0; k + 1 < M; ++k) h->half.u[k] = h->thresholds[M + k] * 4096.0f;
   }
+  if (h->hi > 0) {
+    // the finer level set of the first hi coordinates, the same way
+    const int L = 2 * h->levels, M = L / 2;
+    bool sym = h->thresholds_hi[M - 1] == 0.0f;
+    for (int i = 0; i < L; ++i) sym = sym && h->centroids_hi[L - 1 - i] == -h->centroids_hi[i];
+    for (int i = 0; i + 1 < L; ++i) sym = sym && h->thresholds_hi[L - 2 - i] == -h->thresholds_hi[i];
+    h->symmetric_hi = sym;
+    for (int j = 0; j < M; ++j) h->half_hi.m[j] = h->centroids_hi[M + j] * 4096.0f;
+    for (int k = 0; k + 1 < M; ++k) h->half_hi.u[k] = h->thresholds_hi[M + k] * 4096.0f;
+  }
   int rc;
   if ((rc = upload(&h->d_pi, h->pi)) != TQ_OK) return rc;
   if ((rc = upload(&h->d_piT, transpose(h->pi, d))) != TQ_OK) return rc;

@@ -79,6 +79,8 @@ struct tq_ctx {
   tqdev::PlaneExpansion planes{};
   bool symmetric = false;  // level set exactly symmetric in float32
   tqdev::HalfCodebook half{};
+  tqdev::HalfCodebook half_hi{};  // the finer set of coordinates below hi
+  bool symmetric_hi = false;
   tqdev::DequantTable dqt{};
   // randomized Hadamard rotation (tq_init_hadamard): Pi = H diag(sigma) c
   // with c = float32(1 / sqrt(d)); d_hsigma holds sigma (float +-1)
