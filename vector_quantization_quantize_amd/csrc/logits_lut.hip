@@ -91,6 +91,46 @@ __device__ __forceinline__ Packed<B> load_key(const uint32_t* __restrict__ codes
   return k;
 }
 
+// Fractional widths (code rows of 4B + 2 words: B full planes, then plane B
+// of coordinates 0..63): rows are 8-byte aligned, so each plane is two
+// 8-byte loads; the extra plane is returned as a plane whose bytes 8..15
+// are zero.
+template <int B>
+__device__ __forceinline__ Packed<B + 1> load_key_hi(const uint32_t* __restrict__ codes,
+                                                     const uint32_t* __restrict__ signs,
+                                                     const float* __restrict__ norms,
+                                                     const float* __restrict__ rnorms, int64_t key) {
+  Packed<B + 1> k;
+  const uint2* row = reinterpret_cast<const uint2*>(codes + key * (4 * B + 2));
+#pragma unroll
+  for (int p = 0; p < B; ++p) {
+    const uint2 a = row[2 * p], b = row[2 * p + 1];
+    k.plane[p] = make_uint4(a.x, a.y, b.x, b.y);
+  }
+  const uint2 x = row[2 * B];
+  k.plane[B] = make_uint4(x.x, x.y, 0u, 0u);
+  k.sign = *reinterpret_cast<const uint4*>(signs + key * 4);
+  k.n = norms[key];
+  k.rho = rnorms[key];
+  return k;
+}
+
+// Byte order of a fractional-width lane: the 8 bytes of each half rotated
+// by r (0..7), and the halves swapped when sw is set, so that out words 0-1
+// are one half and words 2-3 the other.
+__device__ __forceinline__ Words rotate_halves(const uint4& in, bool w1, uint32_t bs, bool sw) {
+  const uint32_t a0 = w1 ? in.y : in.x, a1 = w1 ? in.x : in.y;  // half 0
+  const uint32_t c0 = w1 ? in.w : in.z, c1 = w1 ? in.z : in.w;  // half 1
+  const uint32_t h0 = __builtin_amdgcn_alignbyte(a1, a0, bs), h1 = __builtin_amdgcn_alignbyte(a0, a1, bs);
+  const uint32_t h2 = __builtin_amdgcn_alignbyte(c1, c0, bs), h3 = __builtin_amdgcn_alignbyte(c0, c1, bs);
+  Words out;
+  out.w[0] = sw ? h2 : h0;
+  out.w[1] = sw ? h3 : h1;
+  out.w[2] = sw ? h0 : h2;
+  out.w[3] = sw ? h1 : h3;
+  return out;
+}
+
 // rotate the 16-byte plane right by r bytes: out.byte[k] = in.byte[(k + r) & 15]
 __device__ __forceinline__ Words rotate(const uint4& in, bool w1, bool w2, uint32_t bs) {
   const uint32_t a0 = w1 ? in.y : in.x;
@@ -150,16 +190,25 @@ struct Shape {
   static constexpr int kWalk = 256 * 2 * 16 * 4 / kThreads;  // table entries per thread
 };
 
-template <int B>
-__global__ void __launch_bounds__(Shape<B>::kThreads, 1)
+// HI: fractional widths with hi = 64: coordinates 0..63 (bytes 0..7 of
+// each plane) carry B + 1 index bits and the finer level set, whose plane
+// expansion is peh; 64..127 carry B bits and pe.  A lane scores one half in
+// byte steps 0..7 and the other in steps 8..15 (lanes 8..15 of every 16 the
+// other way round), so the 16 lanes of an LDS pass still read 16 distinct
+// byte positions; each step looks up the finer set's term count, and a
+// lane in its coarse half leaves the surplus terms' sums out.
+template <int B, bool HI>
+__global__ void __launch_bounds__(Shape<HI ? B + 1 : B>::kThreads, 1)
 logits_lut128_kernel(const float* __restrict__ queries, int quads, int64_t nq, int64_t n, int d,
                      const float* __restrict__ piT, const float* __restrict__ sT,  // 128 x 128, zero-padded
                      const uint32_t* __restrict__ codes, const uint32_t* __restrict__ signs,
                      const float* __restrict__ norms, const float* __restrict__ rnorms,
-                     float* __restrict__ scores, PlaneExpansion pe, float kappa, int chunks,
+                     float* __restrict__ scores, PlaneExpansion pe, PlaneExpansion peh, float kappa, int chunks,
                      int64_t keys_per_block) {
-  using TT = Terms<B>;
-  using SH = Shape<B>;
+  constexpr int NPL = HI ? B + 1 : B;  // planes loaded per key
+  using TT = Terms<NPL>;               // terms of the (finer) level set
+  using TB = Terms<B>;                 // terms of the coarse set
+  using SH = Shape<NPL>;
   constexpr int NT = TT::count;
   constexpr int kThreads = SH::kThreads, kWaves = kThreads / 64;
   __shared__ __align__(16) unsigned char tabs[kTableBytes];
@@ -216,7 +265,13 @@ logits_lut128_kernel(const float* __restrict__ queries, int quads, int64_t nq, i
   if (tid < 4 * kDim) reinterpret_cast<float*>(qs)[qi * 4 + qq] = qok ? qraw : 0.0f;
   if (tid == 0) next_batch = kWaves;
   __syncthreads();
-  Packed<B> cur = load_key<B>(codes, signs, norms, rnorms, grp * n + key_of(wave));
+  auto load = [&](int64_t key) {
+    if constexpr (HI)
+      return load_key_hi<B>(codes, signs, norms, rnorms, key);
+    else
+      return load_key<B>(codes, signs, norms, rnorms, key);
+  };
+  Packed<NPL> cur = load(grp * n + key_of(wave));
   {
     float av[4] = {0.0f, 0.0f, 0.0f, 0.0f}, aw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     auto accumulate = [&](int i0, const float (&pv)[16], const float (&pw)[16]) {
@@ -311,13 +366,31 @@ logits_lut128_kernel(const float* __restrict__ queries, int quads, int64_t nq, i
   const bool w1 = (r >> 2) & 1u, w2 = (r >> 3) & 1u;
   const uint32_t bs = r & 3u;
   uint32_t lb[8];
+  // byte position of step t: (t + r) mod 16, or for fractional widths
+  // ((t + r) mod 8) in the half that step t covers
+  auto pos = [&](uint32_t t) -> uint32_t {
+    if constexpr (HI)
+      return ((((t >> 3) & 1u) ^ (w2 ? 1u : 0u)) << 3) | ((t + r) & 7u);
+    else
+      return (t + r) & 15u;
+  };
 #pragma unroll
-  for (int k = 0; k < 8; ++k) lb[k] = (((2u * k + r) & 15u) * 8u) | ((((2u * k + 1u + r) & 15u) * 8u) << 8);
+  for (int k = 0; k < 8; ++k) lb[k] = (pos(2u * k) * 8u) | ((pos(2u * k + 1u) * 8u) << 8);
   float inv_v[4], inv_w[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     inv_v[q] = 1.0f / scale[0][q];
     inv_w[q] = kappa / scale[1][q];
+  }
+  // HI: coefficients of the term sums of the lane's first and second half
+  // (finer set peh, coarse set pe with no terms past its count)
+  float al_a[NT], al_b[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const float af = HI ? peh.alpha[j] : pe.alpha[j];
+    const float ac = j < TB::count ? pe.alpha[j] : 0.0f;
+    al_a[j] = w2 ? ac : af;
+    al_b[j] = w2 ? af : ac;
   }
   const half2_t pick_lo = {(_Float16)1.0f, (_Float16)0.0f};
   const half2_t pick_hi = {(_Float16)0.0f, (_Float16)1.0f};
@@ -332,11 +405,11 @@ logits_lut128_kernel(const float* __restrict__ queries, int quads, int64_t nq, i
   int64_t bn = claim();     // the one after it
   while (b < nbatch) {
     const int64_t bnn = claim();
-    const Packed<B> nxt = load_key<B>(codes, signs, norms, rnorms, grp * n + key_of(bn));  // unused past the end
-    Words pl[B];
+    const Packed<NPL> nxt = load(grp * n + key_of(bn));  // unused past the end
+    Words pl[NPL];
 #pragma unroll
-    for (int p = 0; p < B; ++p) pl[p] = rotate(cur.plane[p], w1, w2, bs);
-    const Words sg = rotate(cur.sign, w1, w2, bs);
+    for (int p = 0; p < NPL; ++p) pl[p] = HI ? rotate_halves(cur.plane[p], w1, bs, w2) : rotate(cur.plane[p], w1, w2, bs);
+    const Words sg = HI ? rotate_halves(cur.sign, w1, bs, w2) : rotate(cur.sign, w1, w2, bs);
     Words term[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
@@ -344,14 +417,26 @@ logits_lut128_kernel(const float* __restrict__ queries, int quads, int64_t nq, i
       for (int i = 0; i < 4; ++i) {
         uint32_t x = 0;
 #pragma unroll
-        for (int p = 0; p < B; ++p)
+        for (int p = 0; p < NPL; ++p)
           if (TT::mask[j] & (1u << p)) x ^= pl[p].w[i];
+        if constexpr (HI) {
+          // words 0-1 are this lane's first half: the finer one unless the
+          // halves are swapped (w2)
+          uint32_t y = 0;
+          if (j < TB::count) {
+#pragma unroll
+            for (int p = 0; p < B; ++p)
+              if (TB::mask[j] & (1u << p)) y ^= pl[p].w[i];
+          }
+          x = ((i < 2) != w2) ? x : y;
+        }
         term[j].w[i] = x;
       }
     }
     float acc[NT + 1][4];
 #pragma unroll
     for (int j = 0; j <= NT; ++j) acc[j][0] = acc[j][1] = acc[j][2] = acc[j][3] = 0.0f;
+    float s1h[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // HI: level-set sums of the first half
 #pragma unroll
     for (int i = 0; i < 4; ++i) {  // one 32-bit word (4 byte steps) at a time
       half2_t part[NT + 1][2];
@@ -382,6 +467,19 @@ logits_lut128_kernel(const float* __restrict__ queries, int quads, int64_t nq, i
         acc[j][2] = __builtin_amdgcn_fdot2(part[j][1], pick_lo, acc[j][2], false);
         acc[j][3] = __builtin_amdgcn_fdot2(part[j][1], pick_hi, acc[j][3], false);
       }
+      if constexpr (HI) {
+        if (i == 1) {
+          // end of the first half: its level set's coefficients, then the
+          // term sums start again for the second half
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j) s1h[q] = fmaf(al_a[j], acc[j][q], s1h[q]);
+          }
+#pragma unroll
+          for (int j = 0; j < NT; ++j) acc[j][0] = acc[j][1] = acc[j][2] = acc[j][3] = 0.0f;
+        }
+      }
     }
     // lanes past the end scored key kend - 1 again and store the same value
     // there: no branch around the stores
@@ -389,9 +487,9 @@ logits_lut128_kernel(const float* __restrict__ queries, int quads, int64_t nq, i
     const float corr = cur.rho;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      float s1 = 0.0f;
+      float s1 = s1h[q];
 #pragma unroll
-      for (int j = 0; j < NT; ++j) s1 = fmaf(pe.alpha[j], acc[j][q], s1);
+      for (int j = 0; j < NT; ++j) s1 = fmaf(HI ? al_b[j] : pe.alpha[j], acc[j][q], s1);
       const float sw = acc[NT][q] * inv_w[q];
       if (q < qc) scores[(grp * nq + q0 + q) * n + key] = cur.n * fmaf(corr, sw, s1 * inv_v[q]);
     }
@@ -401,7 +499,7 @@ logits_lut128_kernel(const float* __restrict__ queries, int quads, int64_t nq, i
   }
 }
 
-template <int B>
+template <int B, bool HI>
 hipError_t launch_b(const tq_ctx* h, const float* queries, int64_t groups, int64_t nq, const uint32_t* codes,
                     const uint32_t* signs, const float* norms, const float* rnorms, int64_t n, float* scores,
                     hipStream_t stream) {
@@ -417,26 +515,39 @@ hipError_t launch_b(const tq_ctx* h, const float* queries, int64_t groups, int64
   const int64_t blocks = chunks * pairs;
   if (blocks > 0x7FFFFFFF || chunks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const float kappa = 1.2533141373155002512f / float(h->d);
-  hipLaunchKernelGGL(logits_lut128_kernel<B>, dim3(static_cast<uint32_t>(blocks)), dim3(Shape<B>::kThreads), 0,
-                     stream, queries, int(quads), nq, n, h->d, h->d_piT128, h->d_sT128, codes, signs, norms,
-                     rnorms, scores, h->planes, kappa, static_cast<int>(chunks), kpb);
+  hipLaunchKernelGGL((logits_lut128_kernel<B, HI>), dim3(static_cast<uint32_t>(blocks)),
+                     dim3(Shape<HI ? B + 1 : B>::kThreads), 0, stream, queries, int(quads), nq, n, h->d, h->d_piT128,
+                     h->d_sT128, codes, signs, norms, rnorms, scores, h->planes, h->planes_hi, kappa,
+                     static_cast<int>(chunks), kpb);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool logits_lut128_supported(const tq_ctx* h) {
-  return h->hi == 0 && h->words == 4 && h->d <= kDim && h->d_piT128 && h->d_sT128 && h->code_bits >= 1 && h->code_bits <= 4;
+  // fractional widths: the finer set on bytes 0..7 (hi = 64), at most 4
+  // index bits there
+  const bool widths = h->hi == 0 || (h->hi == 64 && h->code_bits <= 3);
+  return widths && h->words == 4 && h->d <= kDim && h->d_piT128 && h->d_sT128 && h->code_bits >= 1 &&
+         h->code_bits <= 4;
 }
 
 hipError_t launch_logits_lut128(const tq_ctx* h, const float* queries, int64_t groups, int64_t nq,
                                 const uint32_t* codes, const uint32_t* signs, const float* norms,
                                 const float* rnorms, int64_t n, float* scores, hipStream_t stream) {
+  if (h->hi > 0) {
+    switch (h->code_bits) {
+      case 1: return launch_b<1, true>(h, queries, groups, nq, codes, signs, norms, rnorms, n, scores, stream);
+      case 2: return launch_b<2, true>(h, queries, groups, nq, codes, signs, norms, rnorms, n, scores, stream);
+      case 3: return launch_b<3, true>(h, queries, groups, nq, codes, signs, norms, rnorms, n, scores, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (h->code_bits) {
-    case 1: return launch_b<1>(h, queries, groups, nq, codes, signs, norms, rnorms, n, scores, stream);
-    case 2: return launch_b<2>(h, queries, groups, nq, codes, signs, norms, rnorms, n, scores, stream);
-    case 3: return launch_b<3>(h, queries, groups, nq, codes, signs, norms, rnorms, n, scores, stream);
-    case 4: return launch_b<4>(h, queries, groups, nq, codes, signs, norms, rnorms, n, scores, stream);
+    case 1: return launch_b<1, false>(h, queries, groups, nq, codes, signs, norms, rnorms, n, scores, stream);
+    case 2: return launch_b<2, false>(h, queries, groups, nq, codes, signs, norms, rnorms, n, scores, stream);
+    case 3: return launch_b<3, false>(h, queries, groups, nq, codes, signs, norms, rnorms, n, scores, stream);
+    case 4: return launch_b<4, false>(h, queries, groups, nq, codes, signs, norms, rnorms, n, scores, stream);
     default: return hipErrorInvalidValue;
   }
 }

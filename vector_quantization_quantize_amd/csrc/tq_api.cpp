@@ -250,6 +250,7 @@ int finish_init(tq_ctx* h) {
     for (int i = 0; i < L; ++i) sym = sym && h->centroids_hi[L - 1 - i] == -h->centroids_hi[i];
     for (int i = 0; i + 1 < L; ++i) sym = sym && h->thresholds_hi[L - 2 - i] == -h->thresholds_hi[i];
     h->symmetric_hi = sym;
+    plane_expansion(h->centroids_hi, h->code_bits + 1, &h->planes_hi);
     for (int j = 0; j < M; ++j) h->half_hi.m[j] = h->centroids_hi[M + j] * 4096.0f;
     for (int k = 0; k + 1 < M; ++k) h->half_hi.u[k] = h->thresholds_hi[M + k] * 4096.0f;
   }

@@ -80,6 +80,7 @@ struct tq_ctx {
   bool symmetric = false;  // level set exactly symmetric in float32
   tqdev::HalfCodebook half{};
   tqdev::HalfCodebook half_hi{};  // the finer set of coordinates below hi
+  tqdev::PlaneExpansion planes_hi{};
   bool symmetric_hi = false;
   tqdev::DequantTable dqt{};
   // randomized Hadamard rotation (tq_init_hadamard): Pi = H diag(sigma) c
