@@ -41,22 +41,27 @@ def env():
 
 
 class _Split:
-    """TQ_ATTN_SPLIT for the duration of a call."""
+    """The two-kernel form (scores, then the value pass) for the duration of
+    a call, with TQ_ATTN_SPLIT tokens per split ("two": its default
+    splits); None leaves the library's choice (the one-kernel form where it
+    applies)."""
 
     def __init__(self, tokens):
         self.tokens = tokens
+        self.env = {} if tokens is None else {"TQ_ATTN_FUSED": "0"}
+        if tokens is not None and tokens != "two":
+            self.env["TQ_ATTN_SPLIT"] = str(tokens)
 
     def __enter__(self):
-        self.old = os.environ.get("TQ_ATTN_SPLIT")
-        if self.tokens is not None:
-            os.environ["TQ_ATTN_SPLIT"] = str(self.tokens)
+        self.old = {k: os.environ.get(k) for k in self.env}
+        os.environ.update(self.env)
 
     def __exit__(self, *exc):
-        if self.tokens is not None:
-            if self.old is None:
-                del os.environ["TQ_ATTN_SPLIT"]
+        for k, v in self.old.items():
+            if v is None:
+                del os.environ[k]
             else:
-                os.environ["TQ_ATTN_SPLIT"] = self.old
+                os.environ[k] = v
 
 
 def _run(env, d, kbits, vbits, groups, nq, n, seed, queries=None, scale=None, split=None):
@@ -119,8 +124,13 @@ def _assert_close(out, lse, ref_o, ref_l, tol_o, tol_l):
 
 
 @pytest.mark.parametrize("d,kbits,vbits,groups,nq,n,split", [
-    (128, 3, 3, 2, 4, 1000, None),    # lookup-table scorer, one float16 piece per value level
-    (128, 4, 4, 3, 4, 777, None),     # three value index bits (two pieces), ragged last tile
+    (128, 3, 3, 2, 4, 1000, None),    # one kernel: byte-table scores, one float16 piece per value level
+    (128, 3, 3, 2, 4, 1000, "two"),   # the same through the two-kernel form
+    (128, 4, 4, 3, 4, 777, None),     # one kernel, three value index bits (two pieces), ragged last batch
+    (128, 4, 4, 3, 4, 777, "two"),
+    (128, 2, 2, 3, 7, 333, None),     # one kernel, sign-form values, a partial query quad
+    (128, 3, 2, 2, 4, 70000, None),   # one kernel, several chunks per pair, sign-form values
+    (128, 3, 3, 1, 4, 1, None),       # one kernel, one token
     (200, 3, 2, 1, 20, 500, None),    # matrix-core scorer; sign-form values; 7 words (two word groups)
     (64, 2, 5, 2, 17, 300, None),     # four value index bits; 17 queries (two row chunks)
     (33, 3, 3, 1, 1, 65, None),       # d not a multiple of 32, one query, general scorer
@@ -134,7 +144,7 @@ def test_attention_matches_oracle(env, d, kbits, vbits, groups, nq, n, split):
     _assert_close(*_run(env, d, kbits, vbits, groups, nq, n, seed=d + n + nq, split=split))
 
 
-@pytest.mark.parametrize("vbits,split", [(3, None), (3, 256), (2, 96), (5, 128)])
+@pytest.mark.parametrize("vbits,split", [(3, None), (2, None), (4, None), (3, 256), (2, 96), (5, 128)])
 def test_attention_zero_queries_average_values(env, vbits, split):
     """Zero queries score every key exactly 0: o is the plain mean of the
     value reconstructions, lse = log n (delta = 0: the value pass alone)."""

@@ -45,7 +45,10 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <cstring>
+#include <type_traits>
 
+#include "lut_tables.h"
 #include "score_mfma.h"
 #include "tq_internal.h"
 
@@ -445,6 +448,424 @@ attn_pv_kernel(const float* __restrict__ scores, int64_t nq, int64_t n, const ui
 }
 
 // ---------------------------------------------------------------------------
+// fused form: key scores by the byte tables and the value pass in one kernel
+// ---------------------------------------------------------------------------
+// For d = 128 and a key handle the byte-table scorer takes: a workgroup of 8
+// waves takes every token of a chunk of one (group, query quad), builds the
+// scorer's tables for its 4 queries (the scorer's prologue), and then each
+// wave walks batches of 64 tokens claimed from a counter in LDS: the keys'
+// scores (one token per lane, the scorer's lookups), the online softmax
+// with a reference maximum per row (as in the value pass), the weights
+// p = 2^(a s - ref) n_v / 2^e through the wave's LDS slice as two float16
+// pieces, and the value levels of the batch's two 32-token blocks against
+// them on v_mfma_f32_16x16x32_f16 (rows 4..15 of the A operand are zero).
+// The score matrix never leaves the chip.  The waves' (max, sum, partial
+// sums) are combined in LDS into one split per workgroup, in the layout the
+// merge kernel reads.
+constexpr int kFThreads = 512;
+constexpr int kFWaves = kFThreads / 64;
+
+// a wave's inputs for one batch: the lane's key, and per 32-token block the
+// lane's 8 VB value bytes (octet lane / 16, coordinates lane % 16 + 16 j)
+// and its token's value norm
+template <int KB, int VB>
+struct FusedIn {
+  ltab::Packed<KB> key;
+  uint32_t vw[2][2 * VB];
+  float vn;
+};
+
+template <int KB, int VB, int VF>
+__global__ void __launch_bounds__(kFThreads, 1)
+attn_fused_kernel(const float* __restrict__ queries, int quads, int64_t nq, int64_t n, int d,
+                  const float* __restrict__ piT, const float* __restrict__ sT, const uint32_t* __restrict__ codes,
+                  const uint32_t* __restrict__ signs, const float* __restrict__ norms,
+                  const float* __restrict__ rnorms, PlaneExpansion pe, float kappa,
+                  const uint32_t* __restrict__ vcodes, const float* __restrict__ vnorms, ScoreForm fp, float scale,
+                  int chunks, int64_t keys_per_block, float* __restrict__ part_y, float2* __restrict__ part_ml) {
+  using namespace ltab;
+  using TT = Terms<KB>;
+  constexpr int NT = TT::count;
+  using Fm = score::Form<VB, VF>;
+  constexpr int E = Fm::E;
+  constexpr int kParts = kFThreads / kDim;  // row slices of the query transform
+  constexpr int kPRows = kDim / kParts;     // 32 rows per slice
+  constexpr int kWalk = 256 * 2 * 16 * 4 / kFThreads;
+  constexpr int dp = 128;                   // value coordinates per token block row
+  __shared__ __align__(16) unsigned char tabs[kTableBytes];
+  // the prologue's queries and vectors, then the waves' weight slices
+  __shared__ __align__(16) union {
+    struct {
+      float4 qs[kDim];
+      float vec[2][4][kDim];
+    } pro;
+    _Float16 pa[kFWaves][2][4][64];  // [wave][hi, lo][row][token of the batch]
+  } sh;
+  __shared__ _Float16 vtab[VF == kSignForm ? 8 : Fm::kEntries * Fm::kHalves];
+  __shared__ float scale_t[2][4];
+  __shared__ float wmax[kFWaves][4], wsum[kFWaves][4], nred[kFWaves];
+  __shared__ uint32_t next_batch;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t pair = blockIdx.x / chunks, c = blockIdx.x % chunks;
+  const int64_t grp = pair / quads, q0 = (pair % quads) * 4;
+  const int qc = int(nq - q0 < 4 ? nq - q0 : 4);
+  const int64_t kbeg = c * keys_per_block;  // a multiple of 64: whole value blocks
+  const int64_t kend = kbeg + keys_per_block < n ? kbeg + keys_per_block : n;  // the launch leaves no block empty
+  const int64_t nbatch = (kend - kbeg + 63) / 64;
+  const int64_t nbv = (n + kTile - 1) / kTile;  // value blocks of the group
+  vcodes += grp * nbv * VB * dp;
+  vnorms += grp * n;
+  auto key_of = [&](int64_t batch) {
+    const int64_t k = kbeg + batch * 64 + lane;
+    return k < kend ? k : kend - 1;
+  };
+  auto load_in = [&](int64_t batch) __attribute__((always_inline)) {
+    FusedIn<KB, VB> x;
+    const int64_t k = key_of(batch);
+    x.key = load_key<KB>(codes, signs, norms, rnorms, grp * n + k);
+    x.vn = vnorms[k];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      int64_t tb = (kbeg + batch * 64) / kTile + kk;
+      tb = tb < nbv ? tb : nbv - 1;
+      const uint2* q = reinterpret_cast<const uint2*>(vcodes + tb * VB * dp) + VB * lane;
+#pragma unroll
+      for (int u = 0; u < VB; ++u) {
+        const uint2 v = q[u];
+        x.vw[kk][2 * u] = v.x;
+        x.vw[kk][2 * u + 1] = v.y;
+      }
+    }
+    return x;
+  };
+
+  // ---- prologue: v = Pi q, w = S q, power-of-two scales, byte tables (the
+  // scorer's), the value level table, and the chunk's largest value norm
+  const int mj = tid & (kDim - 1), part = tid / kDim;
+  const float* pcol = piT + kPRows * part * kDim + mj;
+  const float* scol = sT + kPRows * part * kDim + mj;
+  const int qi = tid & (kDim - 1), qq = (tid >> 7) & 3;
+  const bool qok = q0 + qq < nq && qi < d;
+  const float qraw = queries[(grp * nq + (q0 + qq < nq ? q0 + qq : nq - 1)) * d + (qi < d ? qi : d - 1)];
+  float pv[kPRows], pw[kPRows];
+#pragma unroll
+  for (int k = 0; k < kPRows; ++k) {
+    pv[k] = pcol[k * kDim];
+    pw[k] = scol[k * kDim];
+  }
+  FusedIn<KB, VB> cur = load_in(wave);
+  reinterpret_cast<float*>(sh.pro.qs)[qi * 4 + qq] = qok ? qraw : 0.0f;  // 512 threads: every (q, i) once
+  if (tid == 0) next_batch = kFWaves;
+  float nmax = 0.0f;
+  for (int64_t t = kbeg + tid; t < kend; t += kFThreads) nmax = fmaxf(nmax, vnorms[t]);
+  nmax = wave_max(nmax);
+  if (lane == 0) nred[wave] = nmax;
+  __syncthreads();
+  {
+    float av[4] = {0.0f, 0.0f, 0.0f, 0.0f}, aw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < kPRows; ++k) {
+      const float4 x = sh.pro.qs[kPRows * part + k];
+      av[0] = fmaf(pv[k], x.x, av[0]);
+      av[1] = fmaf(pv[k], x.y, av[1]);
+      av[2] = fmaf(pv[k], x.z, av[2]);
+      av[3] = fmaf(pv[k], x.w, av[3]);
+      aw[0] = fmaf(pw[k], x.x, aw[0]);
+      aw[1] = fmaf(pw[k], x.y, aw[1]);
+      aw[2] = fmaf(pw[k], x.z, aw[2]);
+      aw[3] = fmaf(pw[k], x.w, aw[3]);
+    }
+    float* red = reinterpret_cast<float*>(tabs);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      red[((part * 2 + 0) * 4 + q) * kDim + mj] = av[q];
+      red[((part * 2 + 1) * 4 + q) * kDim + mj] = aw[q];
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < 2 * 4 * kDim; e += kFThreads) {  // e = (tab * 4 + q) * kDim + j
+    const float* red = reinterpret_cast<const float*>(tabs);
+    float sum = 0.0f;
+#pragma unroll
+    for (int pp = 0; pp < kParts; ++pp) sum += red[pp * 1024 + e];
+    sh.pro.vec[e >> 9][(e >> 7) & 3][e & (kDim - 1)] = sum;
+  }
+  if constexpr (VF != kSignForm) {
+    for (int idx = tid; idx < Fm::kEntries; idx += kFThreads) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        int level = 0;
+#pragma unroll
+        for (int p = 0; p < VB; ++p) level |= ((idx >> (p * E + e)) & 1) << p;
+        const float x = fp.val[level];
+        const _Float16 hi = static_cast<_Float16>(x);
+        vtab[idx * Fm::kHalves + e] = hi;
+        if constexpr (VF == kTwoPiece) vtab[idx * Fm::kHalves + E + e] = static_cast<_Float16>(x - float(hi));
+      }
+    }
+  }
+  __syncthreads();
+  {
+    const int tab = wave >> 2, q = wave & 3;  // 8 waves: one (table, query) vector each
+    const float x0 = sh.pro.vec[tab][q][lane], x1 = sh.pro.vec[tab][q][lane + 64];
+    float ss = fmaf(x0, x0, x1 * x1);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+    if (lane == 0) {
+      int e = 0;
+      (void)frexpf(sqrtf(ss), &e);
+      scale_t[tab][q] = ss > 0.0f ? ldexpf(1.0f, 1 - e) : 1.0f;
+    }
+  }
+  __syncthreads();
+  {
+    constexpr int kSegs = 256 / kWalk, kHi = kWalk / 2;
+    const int q = tid & 3, gg = (tid >> 2) & 15, seg = (tid >> 6) & (kSegs - 1), tab = tid / (64 * kSegs);
+    const float sc = scale_t[tab][q];
+    float xs[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xs[i] = sc * sh.pro.vec[tab][q][8 * gg + i];
+    unsigned char* col = tabs + tab * 128 + gg * 8 + q * 2;
+    const int rank0 = kWalk * seg, gb = rank0 ^ (rank0 >> 1);
+    unsigned char* base0 = col + 256 * gb;
+    unsigned char* base1 = col + 256 * (gb ^ kHi);
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc += ((gb >> i) & 1) ? xs[i] : -xs[i];
+    *reinterpret_cast<_Float16*>(base0) = static_cast<_Float16>(acc);
+#pragma unroll
+    for (int m = 1; m < kWalk; ++m) {
+      const int gm = m ^ (m >> 1), b = __builtin_ctz(m);
+      const bool up = (1 << b) == kHi ? (((gb ^ gm) >> b) & 1) != 0 : ((gm >> b) & 1) != 0;
+      acc += up ? 2.0f * xs[b] : -2.0f * xs[b];
+      *reinterpret_cast<_Float16*>(((gm & kHi) ? base1 : base0) + 256 * (gm & (kHi - 1))) =
+          static_cast<_Float16>(acc);
+    }
+  }
+  float nm_all = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kFWaves; ++w) nm_all = fmaxf(nm_all, nred[w]);
+  int ne = 0;
+  if (nm_all > 0.0f && nm_all < INFINITY) (void)frexpf(nm_all, &ne);
+  const float nscale = ldexpf(1.0f, -ne);
+  __syncthreads();  // tables; the prologue's LDS becomes the weight slices
+
+  // ---- per-lane scorer setup (the scorer's rotation and address bases)
+  const uint32_t r = uint32_t(tid) & 15u;
+  const bool w1 = (r >> 2) & 1u, w2 = (r >> 3) & 1u;
+  const uint32_t bs = r & 3u;
+  uint32_t lb[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) lb[k] = (((2u * k + r) & 15u) * 8u) | ((((2u * k + 1u + r) & 15u) * 8u) << 8);
+  float inv_v[4], inv_w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    inv_v[q] = 1.0f / scale_t[0][q];
+    inv_w[q] = kappa / scale_t[1][q];
+  }
+  const half2_t pick_lo = {(_Float16)1.0f, (_Float16)0.0f};
+  const half2_t pick_hi = {(_Float16)0.0f, (_Float16)1.0f};
+  auto claim = [&]() -> int64_t {
+    uint32_t v = 0;
+    if (lane == 0) v = atomicAdd(&next_batch, 1u);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  const int n16 = lane & 15, g16 = lane >> 4;
+  uint32_t sgn_mask = 0x80008000u, sgn_one = 0x3C003C00u;
+  asm volatile("" : "+v"(sgn_mask), "+v"(sgn_one));
+  const float a = scale * 1.4426950408889634f;  // weights are 2^(a s - ref)
+  float lm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};  // reference maxima (log2), the same in every lane
+  float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  f32x4 acc2[8];  // row 4 g16 + i, coordinate 16 j + n16
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc2[j] = f32x4{};
+
+  int64_t b = wave;
+  int64_t bn = claim();
+  while (b < nbatch) {
+    const int64_t bnn = claim();
+    const FusedIn<KB, VB> nxt = load_in(bn);  // unused past the end
+    // scores of the batch's tokens (the scorer's inner loop)
+    float sc[4];
+    {
+      Words pl[KB];
+#pragma unroll
+      for (int p = 0; p < KB; ++p) pl[p] = rotate(cur.key.plane[p], w1, w2, bs);
+      const Words sg = rotate(cur.key.sign, w1, w2, bs);
+      Words term[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t x = 0;
+#pragma unroll
+          for (int p = 0; p < KB; ++p)
+            if (TT::mask[j] & (1u << p)) x ^= pl[p].w[i];
+          term[j].w[i] = x;
+        }
+      }
+      float acc[NT + 1][4];
+#pragma unroll
+      for (int j = 0; j <= NT; ++j) acc[j][0] = acc[j][1] = acc[j][2] = acc[j][3] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        half2_t part[NT + 1][2];
+#pragma unroll
+        for (int j = 0; j <= NT; ++j) part[j][0] = part[j][1] = half2_t{(_Float16)0.0f, (_Float16)0.0f};
+#define TQ_FSTEP(T)                                                                                    \
+  {                                                                                                    \
+    _Pragma("unroll") for (int j = 0; j < NT; ++j) {                                                   \
+      const Entry e = lut<0>(tabs, __builtin_amdgcn_perm(term[j].w[i], lb[(T) >> 1], perm_sel<(T)>())); \
+      part[j][0] += e.q01;                                                                             \
+      part[j][1] += e.q23;                                                                             \
+    }                                                                                                  \
+    const Entry e = lut<1>(tabs, __builtin_amdgcn_perm(sg.w[i], lb[(T) >> 1], perm_sel<(T)>()));       \
+    part[NT][0] += e.q01;                                                                              \
+    part[NT][1] += e.q23;                                                                              \
+    if ((T) & 1) pin<NT + 1>(part);                                                                    \
+  }
+        if (i == 0) { TQ_FSTEP(0) TQ_FSTEP(1) TQ_FSTEP(2) TQ_FSTEP(3) }
+        if (i == 1) { TQ_FSTEP(4) TQ_FSTEP(5) TQ_FSTEP(6) TQ_FSTEP(7) }
+        if (i == 2) { TQ_FSTEP(8) TQ_FSTEP(9) TQ_FSTEP(10) TQ_FSTEP(11) }
+        if (i == 3) { TQ_FSTEP(12) TQ_FSTEP(13) TQ_FSTEP(14) TQ_FSTEP(15) }
+#undef TQ_FSTEP
+#pragma unroll
+        for (int j = 0; j <= NT; ++j) {
+          acc[j][0] = __builtin_amdgcn_fdot2(part[j][0], pick_lo, acc[j][0], false);
+          acc[j][1] = __builtin_amdgcn_fdot2(part[j][0], pick_hi, acc[j][1], false);
+          acc[j][2] = __builtin_amdgcn_fdot2(part[j][1], pick_lo, acc[j][2], false);
+          acc[j][3] = __builtin_amdgcn_fdot2(part[j][1], pick_hi, acc[j][3], false);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float s1 = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) s1 = fmaf(pe.alpha[j], acc[j][q], s1);
+        const float sw = acc[NT][q] * inv_w[q];
+        sc[q] = cur.key.n * fmaf(cur.key.rho, sw, s1 * inv_v[q]);
+      }
+    }
+    // online softmax: the reference maximum of a row moves (and what was
+    // summed so far is rescaled) only when a score passes it by kSlack
+    const bool tin = kbeg + b * 64 + lane < kend;
+    float x[4];
+    bool over = false;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      x[q] = tin && q < qc ? a * sc[q] : -INFINITY;
+      over |= x[q] > lm[q] + kSlack;
+    }
+    if (__builtin_amdgcn_ballot_w64(over) != 0) {
+      float f[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float nm = fmaxf(lm[q], wave_max(x[q]));
+        f[q] = nm > lm[q] ? exp2f(lm[q] - nm) : 1.0f;
+        lm[q] = nm;
+        lsum[q] *= f[q];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc2[j][i] *= f[i];  // rows 4..15 (g16 > 0) hold zeros
+    }
+    const float nv = cur.vn * nscale;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool use = tin && q < qc;
+      const float w = use ? exp2f(x[q] - lm[q]) : 0.0f;
+      lsum[q] += w;
+      const float p = w * nv;
+      const _Float16 hi = static_cast<_Float16>(p);
+      sh.pa[wave][0][q][lane] = hi;
+      sh.pa[wave][1][q][lane] = static_cast<_Float16>(p - float(hi));
+    }
+    // the value levels of the batch's two token blocks against the weights
+    // (LDS is in order within a wave: the reads see the writes above)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      f16x8 ah = {}, al = {};
+      if (n16 < 4) {
+        ah = *reinterpret_cast<const f16x8*>(&sh.pa[wave][0][n16][32 * kk + 8 * g16]);
+        al = *reinterpret_cast<const f16x8*>(&sh.pa[wave][1][n16][32 * kk + 8 * g16]);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        f16x8 bv, bl;
+        if constexpr (VF == kSignForm) {
+          const uint4 sg = score::expand_signs(bit_field(cur.vw[kk], 8 * VB * j, 8), sgn_mask, sgn_one);
+          bv = *reinterpret_cast<const f16x8*>(&sg);
+        } else {
+#pragma unroll
+          for (int k = 0; k < 8 / E; ++k) {
+            const uint32_t idx = bit_field(cur.vw[kk], 8 * VB * j + k * VB * E, VB * E);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              bv[k * E + e] = vtab[idx * Fm::kHalves + e];
+              if constexpr (VF == kTwoPiece) bl[k * E + e] = vtab[idx * Fm::kHalves + E + e];
+            }
+          }
+        }
+        acc2[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bv, acc2[j], 0, 0, 0);
+        acc2[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bv, acc2[j], 0, 0, 0);
+        if constexpr (VF == kTwoPiece) acc2[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl, acc2[j], 0, 0, 0);
+      }
+    }
+    cur = nxt;
+    b = bn;
+    bn = bnn;
+  }
+
+  // ---- the waves' partials combined into the workgroup's split
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) lsum[q] += __shfl_xor(lsum[q], o);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      wmax[wave][q] = lm[q];
+      wsum[wave][q] = lsum[q];
+    }
+  }
+  __syncthreads();  // every wave is past its last lookup: the tables' space is free
+  float mq[4], fw[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kFWaves; ++w) m = fmaxf(m, wmax[w][q]);
+    mq[q] = m;
+    fw[q] = lm[q] > -INFINITY ? exp2f(lm[q] - m) : 0.0f;
+  }
+  float* red = reinterpret_cast<float*>(tabs);  // [wave][row][coordinate]
+  if (g16 == 0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[(wave * 4 + i) * dp + 16 * j + n16] = acc2[j][i] * fw[i];
+  }
+  __syncthreads();
+  {
+    const int row = tid >> 7, coord = tid & 127;  // 512 threads: 4 rows x 128 coordinates
+    float y = 0.0f, l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kFWaves; ++w) {
+      y += red[(w * 4 + row) * dp + coord];
+      if (coord == 0) l += wmax[w][row] > -INFINITY ? wsum[w][row] * exp2f(wmax[w][row] - mq[row]) : 0.0f;
+    }
+    if (row < qc) {
+      const int64_t rr = (grp * nq + q0 + row) * chunks + c;
+      part_y[rr * dp + coord] = y * (fp.gamma * ldexpf(1.0f, ne));
+      if (coord == 0) part_ml[rr] = make_float2(mq[row] * 0.6931471805599453f, l);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // merge of the splits and the rotation back
 // ---------------------------------------------------------------------------
 
@@ -743,6 +1164,63 @@ size_t attn_partial_bytes(const tq_ctx* hv, int64_t groups, int64_t nq, int64_t 
   const size_t y = size_t(groups) * nq * splits * 32 * hv->words * sizeof(float);
   const size_t ml = size_t(groups) * nq * splits * sizeof(float2);
   return ws_align(y) + ws_align(ml);
+}
+
+bool attention_fused_supported(const tq_ctx* hk, const tq_ctx* hv) {
+  if (const char* v = std::getenv("TQ_ATTN_FUSED"))
+    if (std::strcmp(v, "0") == 0) return false;
+  return logits_lut128_supported(hk) && hk->hi == 0 && hk->code_bits <= 3 && hv->words == 4 && hv->hi == 0 &&
+         hv->code_bits <= 3 && hk->d == hv->d;
+}
+
+hipError_t launch_attention_fused(const tq_ctx* hk, const tq_ctx* hv, const float* queries, int64_t groups,
+                                  int64_t nq, const uint32_t* kcodes, const uint32_t* ksigns, const float* knorms,
+                                  const float* krnorms, int64_t n, const uint32_t* vcodes, const float* vnorms,
+                                  float scale, void* partials, float* out, float* lse, hipStream_t stream) {
+  const int64_t quads = (nq + 3) / 4;
+  const int64_t pairs = groups * quads;
+  // one workgroup per CU, each on a chunk of one pair's tokens (a multiple
+  // of 64, so that every chunk holds whole value blocks); no chunk is empty
+  int64_t chunks = (hk->cus + pairs - 1) / pairs;
+  int64_t kpb = (n + chunks - 1) / chunks;
+  kpb = (kpb + 63) / 64 * 64;
+  chunks = (n + kpb - 1) / kpb;
+  const int64_t blocks = chunks * pairs;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const size_t ybytes = size_t(groups) * nq * chunks * 128 * sizeof(float);
+  float* part_y = static_cast<float*>(partials);
+  float2* part_ml = reinterpret_cast<float2*>(static_cast<char*>(partials) + ws_align(ybytes));
+  const float kappa = 1.2533141373155002512f / float(hk->d);
+  const ScoreForm fp = value_params(hv);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kFThreads), 0, stream, queries, int(quads), nq,
+                       n, hk->d, hk->d_piT128, hk->d_sT128, kcodes, ksigns, knorms, krnorms, hk->planes, kappa, vcodes,
+                       vnorms, fp, scale, static_cast<int>(chunks), kpb, part_y, part_ml);
+    return hipGetLastError();
+  };
+  auto by_value = [&](auto kbc) {
+    constexpr int KB = decltype(kbc)::value;
+    switch (hv->code_bits * 4 + value_form(hv)) {
+      case 1 * 4 + kSignForm: return go(attn_fused_kernel<KB, 1, kSignForm>);
+      case 1 * 4 + kTwoPiece: return go(attn_fused_kernel<KB, 1, kTwoPiece>);
+      case 2 * 4 + kOnePiece: return go(attn_fused_kernel<KB, 2, kOnePiece>);
+      case 2 * 4 + kTwoPiece: return go(attn_fused_kernel<KB, 2, kTwoPiece>);
+      case 3 * 4 + kTwoPiece: return go(attn_fused_kernel<KB, 3, kTwoPiece>);
+      default: return hipErrorInvalidValue;
+    }
+  };
+  hipError_t e;
+  switch (hk->code_bits) {
+    case 1: e = by_value(std::integral_constant<int, 1>{}); break;
+    case 2: e = by_value(std::integral_constant<int, 2>{}); break;
+    case 3: e = by_value(std::integral_constant<int, 3>{}); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(unsigned(groups * nq)), dim3(kThreads),
+                     size_t(32 * hv->words) * sizeof(float) + size_t(kThreads) * sizeof(float4), stream, part_y, part_ml,
+                     chunks, 32 * hv->words, hv->d, hv->d_pi, out, lse);
+  return hipGetLastError();
 }
 
 hipError_t launch_attention_values(const tq_ctx* hv, const float* scores, int64_t groups, int64_t nq, int64_t n,

@@ -313,6 +313,15 @@ hipError_t launch_pack_values(const tq_ctx* h, const uint32_t* codes, int64_t gr
                               hipStream_t stream);
 // tokens per key split of the value pass, and the bytes of its partial sums
 int64_t attn_split_tokens(const tq_ctx* hv, int64_t groups, int64_t nq, int64_t n);
+// one-kernel decode attention (scores by the byte tables and the value pass
+// together) for a lookup-table key handle with up to 3 index bits and value
+// codes of up to 3 bits at d in (96, 128]; TQ_ATTN_FUSED=0 turns it off.
+// Partials (one split per chunk) fit in the two-kernel form's partials.
+bool attention_fused_supported(const tq_ctx* hk, const tq_ctx* hv);
+hipError_t launch_attention_fused(const tq_ctx* hk, const tq_ctx* hv, const float* queries, int64_t groups,
+                                  int64_t nq, const uint32_t* kcodes, const uint32_t* ksigns, const float* knorms,
+                                  const float* krnorms, int64_t n, const uint32_t* vcodes, const float* vnorms,
+                                  float scale, void* partials, float* out, float* lse, hipStream_t stream);
 size_t attn_partial_bytes(const tq_ctx* hv, int64_t groups, int64_t nq, int64_t n);
 // from scores [groups][nq][n]: softmax(scale s) over each row, weighted sum
 // of the value reconstructions into out [groups][nq][d] and, if lse is not
