@@ -462,8 +462,7 @@ attn_pv_kernel(const float* __restrict__ scores, int64_t nq, int64_t n, const ui
 // The score matrix never leaves the chip.  The waves' (max, sum, partial
 // sums) are combined in LDS into one split per workgroup, in the layout the
 // merge kernel reads.
-constexpr int kFThreads = 512;
-constexpr int kFWaves = kFThreads / 64;
+constexpr int kFPro = 512;  // threads that build the tables (the rest join the key loop)
 
 // a wave's inputs for one batch: the lane's key, and per 32-token block the
 // lane's 8 VB value bytes (octet lane / 16, coordinates lane % 16 + 16 j)
@@ -475,8 +474,10 @@ struct FusedIn {
   float vn;
 };
 
-template <int KB, int VB, int VF>
-__global__ void __launch_bounds__(kFThreads, 1)
+// NTH: 512 or 768 threads (2 or 3 waves per SIMD, as the key loop's
+// registers allow)
+template <int KB, int VB, int VF, int NTH>
+__global__ void __launch_bounds__(NTH, 1)
 attn_fused_kernel(const float* __restrict__ queries, int quads, int64_t nq, int64_t n, int d,
                   const float* __restrict__ piT, const float* __restrict__ sT, const uint32_t* __restrict__ codes,
                   const uint32_t* __restrict__ signs, const float* __restrict__ norms,
@@ -488,9 +489,10 @@ attn_fused_kernel(const float* __restrict__ queries, int quads, int64_t nq, int6
   constexpr int NT = TT::count;
   using Fm = score::Form<VB, VF>;
   constexpr int E = Fm::E;
-  constexpr int kParts = kFThreads / kDim;  // row slices of the query transform
-  constexpr int kPRows = kDim / kParts;     // 32 rows per slice
-  constexpr int kWalk = 256 * 2 * 16 * 4 / kFThreads;
+  constexpr int kFWaves = NTH / 64;
+  constexpr int kParts = kFPro / kDim;   // row slices of the query transform
+  constexpr int kPRows = kDim / kParts;  // 32 rows per slice
+  constexpr int kWalk = 256 * 2 * 16 * 4 / kFPro;
   constexpr int dp = 128;                   // value coordinates per token block row
   __shared__ __align__(16) unsigned char tabs[kTableBytes];
   // the prologue's queries and vectors, then the waves' weight slices
@@ -542,7 +544,8 @@ attn_fused_kernel(const float* __restrict__ queries, int quads, int64_t nq, int6
 
   // ---- prologue: v = Pi q, w = S q, power-of-two scales, byte tables (the
   // scorer's), the value level table, and the chunk's largest value norm
-  const int mj = tid & (kDim - 1), part = tid / kDim;
+  const bool pro = tid < kFPro;  // a table-building thread
+  const int mj = tid & (kDim - 1), part = (tid / kDim) & (kParts - 1);
   const float* pcol = piT + kPRows * part * kDim + mj;
   const float* scol = sT + kPRows * part * kDim + mj;
   const int qi = tid & (kDim - 1), qq = (tid >> 7) & 3;
@@ -551,18 +554,18 @@ attn_fused_kernel(const float* __restrict__ queries, int quads, int64_t nq, int6
   float pv[kPRows], pw[kPRows];
 #pragma unroll
   for (int k = 0; k < kPRows; ++k) {
-    pv[k] = pcol[k * kDim];
-    pw[k] = scol[k * kDim];
+    pv[k] = pro ? pcol[k * kDim] : 0.0f;
+    pw[k] = pro ? scol[k * kDim] : 0.0f;
   }
   FusedIn<KB, VB> cur = load_in(wave);
-  reinterpret_cast<float*>(sh.pro.qs)[qi * 4 + qq] = qok ? qraw : 0.0f;  // 512 threads: every (q, i) once
+  if (pro) reinterpret_cast<float*>(sh.pro.qs)[qi * 4 + qq] = qok ? qraw : 0.0f;  // every (q, i) once
   if (tid == 0) next_batch = kFWaves;
   float nmax = 0.0f;
-  for (int64_t t = kbeg + tid; t < kend; t += kFThreads) nmax = fmaxf(nmax, vnorms[t]);
+  for (int64_t t = kbeg + tid; t < kend; t += NTH) nmax = fmaxf(nmax, vnorms[t]);
   nmax = wave_max(nmax);
   if (lane == 0) nred[wave] = nmax;
   __syncthreads();
-  {
+  if (pro) {
     float av[4] = {0.0f, 0.0f, 0.0f, 0.0f}, aw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int k = 0; k < kPRows; ++k) {
@@ -584,7 +587,7 @@ attn_fused_kernel(const float* __restrict__ queries, int quads, int64_t nq, int6
     }
   }
   __syncthreads();
-  for (int e = tid; e < 2 * 4 * kDim; e += kFThreads) {  // e = (tab * 4 + q) * kDim + j
+  for (int e = tid; e < 2 * 4 * kDim; e += NTH) {  // e = (tab * 4 + q) * kDim + j
     const float* red = reinterpret_cast<const float*>(tabs);
     float sum = 0.0f;
 #pragma unroll
@@ -592,7 +595,7 @@ attn_fused_kernel(const float* __restrict__ queries, int quads, int64_t nq, int6
     sh.pro.vec[e >> 9][(e >> 7) & 3][e & (kDim - 1)] = sum;
   }
   if constexpr (VF != kSignForm) {
-    for (int idx = tid; idx < Fm::kEntries; idx += kFThreads) {
+    for (int idx = tid; idx < Fm::kEntries; idx += NTH) {
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         int level = 0;
@@ -606,8 +609,8 @@ attn_fused_kernel(const float* __restrict__ queries, int quads, int64_t nq, int6
     }
   }
   __syncthreads();
-  {
-    const int tab = wave >> 2, q = wave & 3;  // 8 waves: one (table, query) vector each
+  if (wave < 8) {
+    const int tab = wave >> 2, q = wave & 3;  // waves 0..7: one (table, query) vector each
     const float x0 = sh.pro.vec[tab][q][lane], x1 = sh.pro.vec[tab][q][lane + 64];
     float ss = fmaf(x0, x0, x1 * x1);
 #pragma unroll
@@ -619,7 +622,7 @@ attn_fused_kernel(const float* __restrict__ queries, int quads, int64_t nq, int6
     }
   }
   __syncthreads();
-  {
+  if (pro) {
     constexpr int kSegs = 256 / kWalk, kHi = kWalk / 2;
     const int q = tid & 3, gg = (tid >> 2) & 15, seg = (tid >> 6) & (kSegs - 1), tab = tid / (64 * kSegs);
     const float sc = scale_t[tab][q];
@@ -850,14 +853,14 @@ attn_fused_kernel(const float* __restrict__ queries, int quads, int64_t nq, int6
   }
   __syncthreads();
   {
-    const int row = tid >> 7, coord = tid & 127;  // 512 threads: 4 rows x 128 coordinates
+    const int row = (tid >> 7) & 3, coord = tid & 127;  // threads below 512: 4 rows x 128 coordinates
     float y = 0.0f, l = 0.0f;
 #pragma unroll
     for (int w = 0; w < kFWaves; ++w) {
       y += red[(w * 4 + row) * dp + coord];
       if (coord == 0) l += wmax[w][row] > -INFINITY ? wsum[w][row] * exp2f(wmax[w][row] - mq[row]) : 0.0f;
     }
-    if (row < qc) {
+    if (tid < 4 * dp && row < qc) {
       const int64_t rr = (grp * nq + q0 + row) * chunks + c;
       part_y[rr * dp + coord] = y * (fp.gamma * ldexpf(1.0f, ne));
       if (coord == 0) part_ml[rr] = make_float2(mq[row] * 0.6931471805599453f, l);
@@ -1192,8 +1195,8 @@ hipError_t launch_attention_fused(const tq_ctx* hk, const tq_ctx* hv, const floa
   float2* part_ml = reinterpret_cast<float2*>(static_cast<char*>(partials) + ws_align(ybytes));
   const float kappa = 1.2533141373155002512f / float(hk->d);
   const ScoreForm fp = value_params(hv);
-  auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kFThreads), 0, stream, queries, int(quads), nq,
+  auto go = [&](auto kernel, int nth) {
+    hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(nth), 0, stream, queries, int(quads), nq,
                        n, hk->d, hk->d_piT128, hk->d_sT128, kcodes, ksigns, knorms, krnorms, hk->planes, kappa, vcodes,
                        vnorms, fp, scale, static_cast<int>(chunks), kpb, part_y, part_ml);
     return hipGetLastError();
@@ -1201,11 +1204,12 @@ hipError_t launch_attention_fused(const tq_ctx* hk, const tq_ctx* hv, const floa
   auto by_value = [&](auto kbc) {
     constexpr int KB = decltype(kbc)::value;
     switch (hv->code_bits * 4 + value_form(hv)) {
-      case 1 * 4 + kSignForm: return go(attn_fused_kernel<KB, 1, kSignForm>);
-      case 1 * 4 + kTwoPiece: return go(attn_fused_kernel<KB, 1, kTwoPiece>);
-      case 2 * 4 + kOnePiece: return go(attn_fused_kernel<KB, 2, kOnePiece>);
-      case 2 * 4 + kTwoPiece: return go(attn_fused_kernel<KB, 2, kTwoPiece>);
-      case 3 * 4 + kTwoPiece: return go(attn_fused_kernel<KB, 3, kTwoPiece>);
+      // three waves per SIMD while the key loop fits 168 registers
+      case 1 * 4 + kSignForm: return go(attn_fused_kernel<KB, 1, kSignForm, KB <= 2 ? 768 : 512>, KB <= 2 ? 768 : 512);
+      case 1 * 4 + kTwoPiece: return go(attn_fused_kernel<KB, 1, kTwoPiece, 512>, 512);
+      case 2 * 4 + kOnePiece: return go(attn_fused_kernel<KB, 2, kOnePiece, KB <= 2 ? 768 : 512>, KB <= 2 ? 768 : 512);
+      case 2 * 4 + kTwoPiece: return go(attn_fused_kernel<KB, 2, kTwoPiece, 512>, 512);
+      case 3 * 4 + kTwoPiece: return go(attn_fused_kernel<KB, 3, kTwoPiece, 512>, 512);
       default: return hipErrorInvalidValue;
     }
   };
