@@ -174,7 +174,9 @@ def attention_leg(w, h, keys, queries, packed, seed, stream, reps=10):
     token blocks; every query head attends over its KV head's n tokens with
     scale 1/sqrt(d).  Comparison: inner products of the same queries with
     the unquantized keys, as float32 and as bfloat16.  Times: HIP events on
-    the library's stream, mean of `reps` calls after one warm-up."""
+    the library's stream, mean of `reps` calls after one warm-up; the
+    two-kernel form (TQ_ATTN_FUSED=0) is timed on the same inputs beside
+    the default one-kernel form."""
     import torch
 
     import vector_quantization_quantize_amd as tqm
@@ -207,6 +209,14 @@ def attention_leg(w, h, keys, queries, packed, seed, stream, reps=10):
 
     t_attn = timed(lambda: tqm.tq_attention(h, hv, queries, *packed, vblocks, vn, n=w.n, out=out, lse=lse,
                                             workspace=ws, stream=stream))
+    # the two-kernel form (scores through the workspace, then the value
+    # pass) on the same inputs, for comparison
+    os.environ["TQ_ATTN_FUSED"] = "0"
+    try:
+        t_two = timed(lambda: tqm.tq_attention(h, hv, queries, *packed, vblocks, vn, n=w.n, out=out, lse=lse,
+                                               workspace=ws, stream=stream))
+    finally:
+        del os.environ["TQ_ATTN_FUSED"]
     t_logits = timed(lambda: tqm.tq_logits(h, queries, *packed, n=w.n, scores=scores, workspace=lws,
                                            stream=stream))
     kb = keys.to(torch.bfloat16) if keys.dtype != torch.bfloat16 else keys
@@ -223,7 +233,8 @@ def attention_leg(w, h, keys, queries, packed, seed, stream, reps=10):
     alg = (key_bytes + value_bytes) * tokens + 4 * w.groups * w.nq * (w.d + 1)
     gbs = alg / (t_attn * 1e-3) / 1e9
     dense_b = {"f32": 4 * w.d, "bf16": 2 * w.d}
-    res = {"ms": round(t_attn, 4), "ms_scores": round(t_logits, 4), "ms_values": round(t_attn - t_logits, 4),
+    res = {"ms": round(t_attn, 4), "form": "one kernel: scores stay on chip",
+           "ms_two_kernel": round(t_two, 4), "ms_logits_alone": round(t_logits, 4),
            "tokens_per_s": tokens / (t_attn * 1e-3), "bytes_per_token": key_bytes + value_bytes,
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(gbs / HBM_PEAK_GBS, 4)},

@@ -377,7 +377,7 @@ attn_pv_kernel(const float* __restrict__ scores, int64_t nq, int64_t n, const ui
 #pragma unroll
     for (int k = 0; k < kPairs; ++k) {
       const int r = 2 * k + (lane >> 5);
-      const float w = exp2f(x[k] - ((lane >> 5) ? lm[2 * k + 1] : lm[2 * k]));
+      const float w = __builtin_amdgcn_exp2f(x[k] - ((lane >> 5) ? lm[2 * k + 1] : lm[2 * k]));
       const bool use = tin && r < rows;
       lsum[k] += use ? w : 0.0f;
       const float p = use ? w * nv : 0.0f;
@@ -778,7 +778,8 @@ attn_fused_kernel(const float* __restrict__ queries, int quads, int64_t nq, int6
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const bool use = tin && q < qc;
-      const float w = use ? exp2f(x[q] - lm[q]) : 0.0f;
+      // the hardware exp2 (a weight below 2^-126 of the reference flushes to 0)
+      const float w = use ? __builtin_amdgcn_exp2f(x[q] - lm[q]) : 0.0f;
       lsum[q] += w;
       const float p = w * nv;
       const _Float16 hi = static_cast<_Float16>(p);
