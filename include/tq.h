@@ -344,8 +344,11 @@ TQ_API size_t tq_attention_workspace_size(tq_handle hk, tq_handle hv, int64_t gr
  * tq_pack_values; vnorms: device float [groups][n].  out: device float
  * [groups][nq][d]; lse: device float [groups][nq] or NULL.  n = 0 gives
  * o = 0 and lse = -inf.  workspace: device, at least
- * tq_attention_workspace_size(hk, hv, groups, nq, n) bytes (it holds the
- * score matrix), 256-byte aligned.  Asynchronous on `stream`. */
+ * tq_attention_workspace_size(hk, hv, groups, nq, n) bytes (room for the
+ * score matrix and the per-split partial sums; when the key handle takes
+ * the byte-table scorer, d in (96, 128] with at most 3 index bits, and the
+ * values have at most 3 index bits, the scores stay on chip and only the
+ * partials are used), 256-byte aligned.  Asynchronous on `stream`. */
 TQ_API int tq_attention(tq_handle hk, tq_handle hv, const float* queries, int64_t groups, int64_t nq,
                         const uint32_t* kcodes, const uint32_t* ksigns, const float* knorms,
                         const float* krnorms, const uint32_t* vcodes, const float* vnorms, int64_t n,

@@ -1177,18 +1177,33 @@ bool attention_fused_supported(const tq_ctx* hk, const tq_ctx* hv) {
          hv->code_bits <= 3 && hk->d == hv->d;
 }
 
+namespace {
+// one workgroup per CU, each on a chunk of one pair's tokens (a multiple of
+// 64, so that every chunk holds whole value blocks); no chunk is empty
+void fused_chunks(const tq_ctx* hk, int64_t pairs, int64_t n, int64_t* chunks, int64_t* kpb) {
+  int64_t c = (hk->cus + pairs - 1) / pairs;
+  int64_t k = (n + c - 1) / c;
+  k = (k + 63) / 64 * 64;
+  *kpb = k;
+  *chunks = (n + k - 1) / k;
+}
+}  // namespace
+
+size_t attn_fused_partial_bytes(const tq_ctx* hk, int64_t groups, int64_t nq, int64_t n) {
+  if (n <= 0) return 0;
+  int64_t chunks, kpb;
+  fused_chunks(hk, groups * ((nq + 3) / 4), n, &chunks, &kpb);
+  return ws_align(size_t(groups) * nq * chunks * 128 * sizeof(float)) + ws_align(size_t(groups) * nq * chunks * sizeof(float2));
+}
+
 hipError_t launch_attention_fused(const tq_ctx* hk, const tq_ctx* hv, const float* queries, int64_t groups,
                                   int64_t nq, const uint32_t* kcodes, const uint32_t* ksigns, const float* knorms,
                                   const float* krnorms, int64_t n, const uint32_t* vcodes, const float* vnorms,
                                   float scale, void* partials, float* out, float* lse, hipStream_t stream) {
   const int64_t quads = (nq + 3) / 4;
   const int64_t pairs = groups * quads;
-  // one workgroup per CU, each on a chunk of one pair's tokens (a multiple
-  // of 64, so that every chunk holds whole value blocks); no chunk is empty
-  int64_t chunks = (hk->cus + pairs - 1) / pairs;
-  int64_t kpb = (n + chunks - 1) / chunks;
-  kpb = (kpb + 63) / 64 * 64;
-  chunks = (n + kpb - 1) / kpb;
+  int64_t chunks, kpb;
+  fused_chunks(hk, pairs, n, &chunks, &kpb);
   const int64_t blocks = chunks * pairs;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const size_t ybytes = size_t(groups) * nq * chunks * 128 * sizeof(float);

@@ -721,7 +721,8 @@ int tq_attention(tq_handle hk, tq_handle hv, const float* queries, int64_t group
   const AttnWorkspace w = attn_workspace(hk, hv, groups, nq, n);
   if (workspace_bytes < w.total) return TQ_EINVAL;
   char* base = static_cast<char*>(workspace);
-  if (tqdev::attention_fused_supported(hk, hv)) {
+  if (tqdev::attention_fused_supported(hk, hv) &&
+      tqdev::attn_fused_partial_bytes(hk, groups, nq, n) <= w.partials) {
     // scores stay on chip; the partials take the two-kernel form's place
     const hipError_t e = tqdev::launch_attention_fused(hk, hv, queries, groups, nq, kcodes, ksigns, knorms, krnorms, n,
                                                        vcodes, vnorms, scale, base + w.scores + w.prep, out, lse, s);

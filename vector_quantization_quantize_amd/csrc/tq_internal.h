@@ -316,8 +316,10 @@ int64_t attn_split_tokens(const tq_ctx* hv, int64_t groups, int64_t nq, int64_t 
 // one-kernel decode attention (scores by the byte tables and the value pass
 // together) for a lookup-table key handle with up to 3 index bits and value
 // codes of up to 3 bits at d in (96, 128]; TQ_ATTN_FUSED=0 turns it off.
-// Partials (one split per chunk) fit in the two-kernel form's partials.
+// Its partials (one split per chunk, attn_fused_partial_bytes) take the
+// place of the two-kernel form's; the caller checks that they fit.
 bool attention_fused_supported(const tq_ctx* hk, const tq_ctx* hv);
+size_t attn_fused_partial_bytes(const tq_ctx* hk, int64_t groups, int64_t nq, int64_t n);
 hipError_t launch_attention_fused(const tq_ctx* hk, const tq_ctx* hv, const float* queries, int64_t groups,
                                   int64_t nq, const uint32_t* kcodes, const uint32_t* ksigns, const float* knorms,
                                   const float* krnorms, int64_t n, const uint32_t* vcodes, const float* vnorms,
