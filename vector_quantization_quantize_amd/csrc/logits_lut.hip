@@ -351,7 +351,7 @@ logits_lut128_kernel(const float* __restrict__ queries, int quads, int64_t nq, i
 #pragma unroll
       for (int j = 0; j < NT; ++j) s1 = fmaf(HI ? al_b[j] : pe.alpha[j], acc[j][q], s1);
       const float sw = acc[NT][q] * inv_w[q];
-      if (q < qc) scores[(grp * nq + q0 + q) * n + key] = cur.n * fmaf(corr, sw, s1 * inv_v[q]);
+      if (q < qc) __builtin_nontemporal_store(cur.n * fmaf(corr, sw, s1 * inv_v[q]), &scores[(grp * nq + q0 + q) * n + key]);
     }
     cur = nxt;
     b = bn;

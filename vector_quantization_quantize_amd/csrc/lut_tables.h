@@ -56,12 +56,18 @@ template <int B>
 __device__ __forceinline__ Packed<B> load_key(const uint32_t* __restrict__ codes, const uint32_t* __restrict__ signs,
                                               const float* __restrict__ norms, const float* __restrict__ rnorms,
                                               int64_t key) {
+  // the packed cache is read once per call: non-temporal loads
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  auto nt4 = [](const uint32_t* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  };
   Packed<B> k;
 #pragma unroll
-  for (int p = 0; p < B; ++p) k.plane[p] = *reinterpret_cast<const uint4*>(codes + (key * B + p) * 4);
-  k.sign = *reinterpret_cast<const uint4*>(signs + key * 4);
-  k.n = norms[key];
-  k.rho = rnorms[key];
+  for (int p = 0; p < B; ++p) k.plane[p] = nt4(codes + (key * B + p) * 4);
+  k.sign = nt4(signs + key * 4);
+  k.n = __builtin_nontemporal_load(norms + key);
+  k.rho = __builtin_nontemporal_load(rnorms + key);
   return k;
 }
 
