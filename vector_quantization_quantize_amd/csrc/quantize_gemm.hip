@@ -87,51 +87,39 @@ __device__ __forceinline__ float key_scale(float nk) {
 }
 
 // ---------------------------------------------------------------------------
-// 1. prep: per tile of 128 keys, the norms (float32, a fixed order: each
-// thread's elements in sequence, then a tree over the 4 (float32) or 2
-// (bfloat16) threads of a key) and the keys scaled by 2^s and split into two
-// float16 pieces, written in the rotation's operand layout
-// [key tile][K step][key 128][piece 2][16].  Float32 keys: chunk c in
-// {t, t + 256} is elements 4 (c % 4) .. + 3 of each K step of key c / 4;
-// bfloat16 keys: thread t takes elements 8 (t % 2) .. + 7 of key t / 2.
-// Either way 4 (2) lanes read 64 (32) contiguous bytes of a row.
+// 1. prep: for d > 256 two launches (1a then 1b), else 1b alone in its
+// fused form.
+// 1a. norms: one wave per key; lane l sums the squares of its elements
+// 4 l + 256 i .. + 3 (float32) or 8 l + 512 i .. + 7 (bfloat16) in
+// sequence, then a butterfly over the 64 lanes, all in float32.
 // ---------------------------------------------------------------------------
 template <int KT>
 __global__ void __launch_bounds__(256)
-qg_prep_kernel(const void* __restrict__ keys, int64_t nkeys, int64_t ldk, int d, int ks, int vec_ok,
-               float* __restrict__ norms, uint16_t* __restrict__ kpc) {
-  constexpr int kPer = KT == TQ_F32 ? 2 : 1;  // chunks per thread
-  constexpr int kElems = KT == TQ_F32 ? 4 : 8;  // elements per chunk
-  constexpr int kParts = 16 / kElems;  // chunks per key and K step
-  const int t = threadIdx.x;
-  const int64_t kt = blockIdx.x;
-  int64_t key[kPer];
-  int part[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int c = t + 256 * i;
-    int64_t k = kt * kBN + c / kParts;
-    key[i] = k < nkeys ? k : nkeys - 1;
-    part[i] = c % kParts;
-  }
-  auto load = [&](int i, int s, float (&x)[kElems]) __attribute__((always_inline)) {
-    const int k0 = 16 * s + kElems * part[i];
+qg_norm_kernel(const void* __restrict__ keys, int64_t nkeys, int64_t ldk, int d, int vec_ok,
+               float* __restrict__ norms) {
+  constexpr int kE = KT == TQ_F32 ? 4 : 8;  // elements per lane and round
+  const int lane = threadIdx.x & 63;
+  const int64_t key = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (key >= nkeys) return;  // (whole waves)
+  float ss = 0.0f;
+  for (int e0 = kE * lane; e0 < d; e0 += 64 * kE) {
+    float x[kE];
     if constexpr (KT == TQ_F32) {
-      const float* row = static_cast<const float*>(keys) + key[i] * ldk;
-      if (vec_ok && k0 + 4 <= d) {
-        const float4 v = *reinterpret_cast<const float4*>(row + k0);
+      const float* row = static_cast<const float*>(keys) + key * ldk;
+      if (vec_ok && e0 + 4 <= d) {
+        const float4 v = *reinterpret_cast<const float4*>(row + e0);
         x[0] = v.x;
         x[1] = v.y;
         x[2] = v.z;
         x[3] = v.w;
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = k0 + e < d ? row[k0 + e] : 0.0f;
+        for (int e = 0; e < 4; ++e) x[e] = e0 + e < d ? row[e0 + e] : 0.0f;
       }
     } else {
-      const uint16_t* row = static_cast<const uint16_t*>(keys) + key[i] * ldk;
-      if (vec_ok && k0 + 8 <= d) {
-        const uint4 v = *reinterpret_cast<const uint4*>(row + k0);
+      const uint16_t* row = static_cast<const uint16_t*>(keys) + key * ldk;
+      if (vec_ok && e0 + 8 <= d) {
+        const uint4 v = *reinterpret_cast<const uint4*>(row + e0);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -140,53 +128,141 @@ qg_prep_kernel(const void* __restrict__ keys, int64_t nkeys, int64_t ldk, int d,
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = k0 + e < d ? bf16_to_f32(row[k0 + e]) : 0.0f;
+        for (int e = 0; e < 8; ++e) x[e] = e0 + e < d ? bf16_to_f32(row[e0 + e]) : 0.0f;
       }
     }
-  };
-  float ss[kPer];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) ss[i] = 0.0f;
-  for (int s = 0; s < ks; ++s) {
+    for (int e = 0; e < kE; ++e) ss = fmaf(x[e], x[e], ss);
+  }
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      float x[kElems];
-      load(i, s, x);
+  for (int o = 1; o < 64; o <<= 1) ss += __shfl_xor(ss, o);
+  if (lane == 0) norms[key] = sqrtf(ss);
+}
+
+// ---------------------------------------------------------------------------
+// 1b. pieces: the keys scaled by 2^s and split into two float16 pieces,
+// written in the rotation's operand layout [key tile][K step][key 128]
+// [piece 2][16].  A block takes one key tile and a group of 8 K steps;
+// thread t takes K step t % 8 of the group for keys t / 8 + 32 p (p < 4):
+// the 8 lanes of a key read 512 contiguous bytes (float32) of its row, and
+// a wave writes 8 runs of 8 keys x 64 bytes.  Rows past the end of the
+// keys repeat the last key (their results are never stored).
+// ---------------------------------------------------------------------------
+constexpr int kPieceSteps = 8;  // K steps per pieces block
+
+// elements k0 .. k0 + 15 of a key as float32 (zero past d)
+template <int KT>
+__device__ __forceinline__ void load16(const void* __restrict__ keys, int64_t key, int64_t ldk, int k0, int d,
+                                       int vec_ok, float (&x)[16]) {
+  if constexpr (KT == TQ_F32) {
+    const float* row = static_cast<const float*>(keys) + key * ldk + k0;
+    if (vec_ok && k0 + 16 <= d) {
 #pragma unroll
-      for (int e = 0; e < kElems; ++e) ss[i] = fmaf(x[e], x[e], ss[i]);
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = reinterpret_cast<const float4*>(row)[q];
+        x[4 * q] = v.x;
+        x[4 * q + 1] = v.y;
+        x[4 * q + 2] = v.z;
+        x[4 * q + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) x[e] = k0 + e < d ? row[e] : 0.0f;
+    }
+  } else {
+    const uint16_t* row = static_cast<const uint16_t*>(keys) + key * ldk + k0;
+    if (vec_ok && k0 + 16 <= d) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint4 v = reinterpret_cast<const uint4*>(row)[q];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[8 * q + 2 * e] = bf16_to_f32(uint16_t(w[e] & 0xFFFFu));
+          x[8 * q + 2 * e + 1] = bf16_to_f32(uint16_t(w[e] >> 16));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) x[e] = k0 + e < d ? bf16_to_f32(row[e]) : 0.0f;
     }
   }
-  float scale[kPer];
+}
+
+// the two float16 pieces of 2^s x for K step s of key kl of key tile kt
+__device__ __forceinline__ void put_pieces(uint16_t* __restrict__ kpc, int64_t kt, int ks, int s, int kl,
+                                           const float (&x)[16], float scale) {
+  f16x8 hi[2], lo[2];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-#pragma unroll
-    for (int o = 1; o < kParts; o <<= 1) ss[i] += __shfl_xor(ss[i], o);
-    const float nk = sqrtf(ss[i]);
-    const int64_t k = kt * kBN + (t + 256 * i) / kParts;
-    if (part[i] == 0 && k < nkeys) norms[k] = nk;
-    scale[i] = key_scale(nk);
+  for (int e = 0; e < 16; ++e) {
+    const float v = x[e] * scale;
+    const _Float16 h = static_cast<_Float16>(v);
+    hi[e >> 3][e & 7] = h;
+    lo[e >> 3][e & 7] = static_cast<_Float16>(v - static_cast<float>(h));
   }
-  for (int s = 0; s < ks; ++s) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      float x[kElems];
-      load(i, s, x);
-      _Float16 hi[kElems], lo[kElems];
-#pragma unroll
-      for (int e = 0; e < kElems; ++e) {
-        const float v = x[e] * scale[i];
-        hi[e] = static_cast<_Float16>(v);
-        lo[e] = static_cast<_Float16>(v - static_cast<float>(hi[e]));
-      }
-      _Float16* dst = reinterpret_cast<_Float16*>(kpc) + ((kt * ks + s) * kBN + (t + 256 * i) / kParts) * 32 +
-                      kElems * part[i];
-      if constexpr (KT == TQ_F32) {
-        *reinterpret_cast<f16x4*>(dst) = f16x4{hi[0], hi[1], hi[2], hi[3]};
-        *reinterpret_cast<f16x4*>(dst + 16) = f16x4{lo[0], lo[1], lo[2], lo[3]};
+  f16x8* dst = reinterpret_cast<f16x8*>(kpc + ((kt * ks + s) * kBN + kl) * 32);
+  dst[0] = hi[0];
+  dst[1] = hi[1];
+  dst[2] = lo[0];
+  dst[3] = lo[1];
+}
+
+// FUSED (at most 16 K steps, d <= 256): one block per key tile; thread t
+// takes K steps t % 8 and t % 8 + 8, and the 8 lanes of a key also form
+// its norm (each lane's squares in sequence, then a butterfly over the 8
+// lanes), so the keys are read once.
+template <int KT, bool FUSED>
+__global__ void __launch_bounds__(256)
+qg_pieces_kernel(const void* __restrict__ keys, int64_t nkeys, int64_t ldk, int d, int ks, int vec_ok,
+                 float* __restrict__ norms, uint16_t* __restrict__ kpc) {
+  if constexpr (FUSED) {
+    const int64_t kt = blockIdx.x;
+    const int s0 = threadIdx.x & 7, s1 = s0 + 8;
+#pragma unroll 1
+    for (int j = 0; j < 4; ++j) {
+      const int kl = (threadIdx.x >> 3) + 32 * j;
+      const int64_t k = kt * kBN + kl;
+      const int64_t key = k < nkeys ? k : nkeys - 1;
+      float x0[16], x1[16];
+      if (s0 < ks) {
+        load16<KT>(keys, key, ldk, 16 * s0, d, vec_ok, x0);
       } else {
-        *reinterpret_cast<f16x8*>(dst) = f16x8{hi[0], hi[1], hi[2], hi[3], hi[4], hi[5], hi[6], hi[7]};
-        *reinterpret_cast<f16x8*>(dst + 16) = f16x8{lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]};
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x0[e] = 0.0f;
       }
+      if (s1 < ks) {
+        load16<KT>(keys, key, ldk, 16 * s1, d, vec_ok, x1);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x1[e] = 0.0f;
+      }
+      float ss = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) ss = fmaf(x0[e], x0[e], ss);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) ss = fmaf(x1[e], x1[e], ss);
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) ss += __shfl_xor(ss, o);
+      const float nk = sqrtf(ss);
+      if (s0 == 0 && k < nkeys) norms[key] = nk;
+      const float scale = key_scale(nk);
+      if (s0 < ks) put_pieces(kpc, kt, ks, s0, kl, x0, scale);
+      if (s1 < ks) put_pieces(kpc, kt, ks, s1, kl, x1, scale);
+    }
+  } else {
+    const int groups = (ks + kPieceSteps - 1) / kPieceSteps;
+    const int64_t kt = blockIdx.x / groups;
+    const int sg = int(blockIdx.x - kt * groups);
+    const int s = sg * kPieceSteps + (threadIdx.x & 7);
+    if (s >= ks) return;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kl = (threadIdx.x >> 3) + 32 * j;
+      int64_t key = kt * kBN + kl;
+      key = key < nkeys ? key : nkeys - 1;
+      float x[16];
+      load16<KT>(keys, key, ldk, 16 * s, d, vec_ok, x);
+      put_pieces(kpc, kt, ks, s, kl, x, key_scale(norms[key]));
     }
   }
 }
@@ -433,11 +509,16 @@ struct QArgs {
   Levels base, fine;       // level sets (fine: coordinates below hi)
 };
 
-// Work items are (key tile, coordinate tile) pairs, key tile fastest, and
-// block b takes items b, b + B, b + 2B, ... (B blocks): at any time every
-// block works on the same coordinate tile, whose operand rows (128 x d x 4
-// bytes) then stay in each XCD's L2 instead of all coordinate tiles
-// streaming from the MALL.  A step is one K step of one item; the block's steps run back to back, so the staging
+// Work items are (key tile, coordinate tile) pairs, coordinate tile
+// fastest.  Workgroups go to the 8 XCDs in turn (block b to XCD b % 8), so
+// block b takes the items v, v + B, v + 2B, ... (B blocks) with
+// v = (b % 8) (B / 8) + b / 8: at any time the blocks of one XCD work on a
+// run of consecutive items, i.e. on all coordinate tiles of a few key
+// tiles, and each key tile's operand rows are fetched into that XCD's L2
+// once for all its coordinate tiles (and each coordinate tile's once for
+// the few key tiles) instead of every block streaming its own key tile
+// from the MALL.  Any dispatch order gives the same results.  A step is one
+// K step of one item; the block's steps run back to back, so the staging
 // waves load the next item's operands while the multiplying waves finish
 // the current one.  LDS holds three staged steps: at iteration it the
 // multiplying waves read step it + 1's fragments from LDS while the matrix
@@ -454,38 +535,57 @@ __global__ void __launch_bounds__(kThreads, 1) qgemm_kernel(QArgs a) {
   const bool producer = w >= 4;
   const int wm = w & 1, wn = (w >> 1) & 1, pt = tid - 256;
   const int ks = a.ks;
-  // this block's items: blockIdx.x + j * gridDim.x, j < my_items
+  // this block's items: vb + j * gridDim.x, j < my_items
   const int64_t nb = gridDim.x;
-  const int64_t my_items = a.items > blockIdx.x ? (a.items - blockIdx.x + nb - 1) / nb : 0;
+  const int64_t vb = nb % 8 == 0 ? int64_t(blockIdx.x % 8) * (nb / 8) + blockIdx.x / 8 : int64_t(blockIdx.x);
+  const int64_t my_items = a.items > vb ? (a.items - vb + nb - 1) / nb : 0;
   const int64_t steps = my_items * ks;
   if (tid < kMaxLevels) {
     lv_c[0][tid] = a.base.c[tid];
     lv_c[1][tid] = a.fine.c[tid];
   }
 
+  if (my_items == 0) return;  // (the whole block)
+
   if (producer) {
     // chunk c in {pt, pt + 256} of a step's 512 16-byte chunks (of either
     // operand) is (row c / 4, piece (c / 2) % 2, half c % 2)
-    int64_t f_j = 0;  // item (as its j) and step of the next step to fetch
-    int f_s = 0;
+    // The step to fetch next: item vb + f_j nb (key tile f_kt, coordinate
+    // tile f_ct, advanced incrementally), K step f_s, and its operand rows.
+    const int64_t kt_step = nb / a.nct;
+    const int ct_step = int(nb - kt_step * a.nct);
+    int64_t f_j = 0, f_kt = vb / a.nct;
+    int f_s = 0, f_ct = int(vb - f_kt * a.nct);
+    const uint16_t* f_a = a.atiles + int64_t(f_ct) * ks * kStepHalves;
+    const uint16_t* f_b = a.bsrc + f_kt * ks * kStepHalves;
+    // Every call issues its four loads: a fixed number of loads per step
+    // lets the compiler wait for exactly the slot being staged, not for
+    // loads issued after it.  Past the block's last step the last step is
+    // loaded again (valid addresses, unused data).
     auto fetch = [&]() __attribute__((always_inline)) {
-      // past the block's last step: the last step again (valid addresses, unused data)
-      const int64_t j = f_j < my_items ? f_j : my_items - 1;
-      const int s = f_j < my_items ? f_s : ks - 1;
-      if (++f_s == ks) {
-        f_s = 0;
-        ++f_j;
-      }
-      const int64_t it = blockIdx.x + j * nb;
-      const int ct = int(it / a.tiles);
-      const int64_t kt = it - int64_t(ct) * a.tiles;
       Slot sl;
-      const uint4* ap = reinterpret_cast<const uint4*>(a.atiles + (int64_t(ct) * ks + s) * kStepHalves);
+      const uint4* ap = reinterpret_cast<const uint4*>(f_a);
+      const uint4* bp = reinterpret_cast<const uint4*>(f_b);
       sl.a0 = ap[pt];
       sl.a1 = ap[pt + 256];
-      const uint4* bp = reinterpret_cast<const uint4*>(a.bsrc + (kt * ks + s) * kStepHalves);
       sl.b0 = bp[pt];
       sl.b1 = bp[pt + 256];
+      if (f_s + 1 < ks) {
+        ++f_s;
+        f_a += kStepHalves;
+        f_b += kStepHalves;
+      } else if (f_j + 1 < my_items) {
+        f_s = 0;
+        ++f_j;
+        f_kt += kt_step;
+        f_ct += ct_step;
+        if (f_ct >= a.nct) {
+          f_ct -= a.nct;
+          ++f_kt;
+        }
+        f_a = a.atiles + int64_t(f_ct) * ks * kStepHalves;
+        f_b = a.bsrc + f_kt * ks * kStepHalves;
+      }
       return sl;
     };
     auto stage = [&](int buf, const Slot& sl) __attribute__((always_inline)) {
@@ -498,22 +598,21 @@ __global__ void __launch_bounds__(kThreads, 1) qgemm_kernel(QArgs a) {
       }
     };
     Slot pa0 = fetch(), pa1 = fetch(), pa2 = fetch(), pa3 = fetch(), pa4 = fetch(), pa5 = fetch();
-    if (steps > 0) {
-      stage(0, pa0);
-      pa0 = fetch();  // step 6
-      stage(1, pa1);
-      pa1 = fetch();  // step 7
-    }
+    stage(0, pa0);
+    pa0 = fetch();  // step 6
+    stage(1, pa1);
+    pa1 = fetch();  // step 7
     __syncthreads();
     // iteration it stages step it + 2 (slot (it + 2) % 6) into buffer
-    // (it + 2) % 3, then fetches step it + 8 into that slot
-#define TQ_QG_STEP(D, SLOT)                        \
-  if (it0 + (D) < steps) {                         \
-    stage(int((it0 + (D) + 2) % 3), SLOT);         \
-    SLOT = fetch();                                \
-    __syncthreads();                               \
-  }
-    for (int64_t it0 = 0; it0 < steps; it0 += 6) {
+    // (it + 2) % 3, then fetches step it + 8 into that slot; it0 is a
+    // multiple of 6, so the buffer is (D + 2) % 3.  Full rounds of six run
+    // without conditions, then the last steps one by one.
+#define TQ_QG_STEP(D, SLOT)   \
+  stage(((D) + 2) % 3, SLOT); \
+  SLOT = fetch();             \
+  __syncthreads();
+    int64_t it0 = 0;
+    for (; it0 + 6 <= steps; it0 += 6) {
       TQ_QG_STEP(0, pa2)
       TQ_QG_STEP(1, pa3)
       TQ_QG_STEP(2, pa4)
@@ -521,6 +620,12 @@ __global__ void __launch_bounds__(kThreads, 1) qgemm_kernel(QArgs a) {
       TQ_QG_STEP(4, pa0)
       TQ_QG_STEP(5, pa1)
     }
+    const int64_t left = steps - it0;
+    if (left > 0) { TQ_QG_STEP(0, pa2) }
+    if (left > 1) { TQ_QG_STEP(1, pa3) }
+    if (left > 2) { TQ_QG_STEP(2, pa4) }
+    if (left > 3) { TQ_QG_STEP(3, pa5) }
+    if (left > 4) { TQ_QG_STEP(4, pa0) }
 #undef TQ_QG_STEP
     return;
   }
@@ -554,11 +659,16 @@ __global__ void __launch_bounds__(kThreads, 1) qgemm_kernel(QArgs a) {
   };
   __syncthreads();
   Frags cur = read_frags(0);
-  int64_t m_item = blockIdx.x;
+  int64_t m_item = vb;
   int m_s = 0;
-  for (int64_t it = 0; it < steps; ++it) {
-    Frags nxt = cur;
-    if (it + 1 < steps) nxt = read_frags(int((it + 1) % 3));
+  // A step multiplies the fragments in use and reads the next step's into
+  // load; steps run in pairs that swap the roles (no register copies).  The
+  // item's epilogue follows its last step's barrier.
+  int nbuf = 1;      // buffer of step it + 1
+  int64_t it = 0;    // the block's step
+  auto step = [&](const Frags& cur, Frags& load) __attribute__((always_inline)) {
+    if (it + 1 < steps) load = read_frags(nbuf);
+    nbuf = nbuf == 2 ? 0 : nbuf + 1;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -580,11 +690,15 @@ __global__ void __launch_bounds__(kThreads, 1) qgemm_kernel(QArgs a) {
           }
       }
     }
-    if (m_s == ks) {
+    ++it;
+    __syncthreads();
+  };
+  auto epilogue = [&]() __attribute__((always_inline)) {
+    {
       // the item's epilogue: element e of tile (i, j) is coordinate
       // c0(i) + 16 g + e, key 64 wn + 32 j + kl of the key tile
-      const int ct = int(m_item / a.tiles);
-      const int64_t kt = m_item - int64_t(ct) * a.tiles;
+      const int64_t kt = m_item / a.nct;
+      const int ct = int(m_item - kt * a.nct);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int tkey = 64 * wn + 32 * j + kl;
@@ -694,8 +808,19 @@ __global__ void __launch_bounds__(kThreads, 1) qgemm_kernel(QArgs a) {
       m_s = 0;
       m_item += nb;
     }
-    cur = nxt;
-    __syncthreads();
+  };
+  Frags other;
+  for (int64_t j = 0; j < my_items; ++j) {
+    int s = 0;
+    for (; s + 2 <= ks; s += 2) {
+      step(cur, other);
+      step(other, cur);
+    }
+    if (s < ks) {
+      step(cur, other);
+      cur = other;
+    }
+    epilogue();
   }
 }
 
@@ -918,12 +1043,29 @@ hipError_t launch_quantize_gemm(tq_ctx* h, const void* keys, int key_dtype, int6
       continue;
     }
     // norms and key pieces of the chunk
-    if (key_dtype == TQ_F32)
-      hipLaunchKernelGGL(qg_prep_kernel<TQ_F32>, dim3(uint32_t(tiles)), dim3(256), 0, stream, ck, nc, ldk, d, s.ks,
-                         vec_ok ? 1 : 0, norms + c0, kpc);
-    else
-      hipLaunchKernelGGL(qg_prep_kernel<TQ_BF16>, dim3(uint32_t(tiles)), dim3(256), 0, stream, ck, nc, ldk, d, s.ks,
-                         vec_ok ? 1 : 0, norms + c0, kpc);
+    if (s.ks <= 2 * kPieceSteps) {
+      // norms and pieces in one pass
+      if (key_dtype == TQ_F32)
+        hipLaunchKernelGGL((qg_pieces_kernel<TQ_F32, true>), dim3(uint32_t(tiles)), dim3(256), 0, stream, ck, nc,
+                           ldk, d, s.ks, vec_ok ? 1 : 0, norms + c0, kpc);
+      else
+        hipLaunchKernelGGL((qg_pieces_kernel<TQ_BF16, true>), dim3(uint32_t(tiles)), dim3(256), 0, stream, ck, nc,
+                           ldk, d, s.ks, vec_ok ? 1 : 0, norms + c0, kpc);
+    } else {
+      const uint32_t nblocks = uint32_t((nc + 3) / 4);
+      const uint32_t pblocks = uint32_t(tiles * ((s.ks + kPieceSteps - 1) / kPieceSteps));
+      if (key_dtype == TQ_F32) {
+        hipLaunchKernelGGL(qg_norm_kernel<TQ_F32>, dim3(nblocks), dim3(256), 0, stream, ck, nc, ldk, d,
+                           vec_ok ? 1 : 0, norms + c0);
+        hipLaunchKernelGGL((qg_pieces_kernel<TQ_F32, false>), dim3(pblocks), dim3(256), 0, stream, ck, nc, ldk, d,
+                           s.ks, vec_ok ? 1 : 0, norms + c0, kpc);
+      } else {
+        hipLaunchKernelGGL(qg_norm_kernel<TQ_BF16>, dim3(nblocks), dim3(256), 0, stream, ck, nc, ldk, d,
+                           vec_ok ? 1 : 0, norms + c0);
+        hipLaunchKernelGGL((qg_pieces_kernel<TQ_BF16, false>), dim3(pblocks), dim3(256), 0, stream, ck, nc, ldk, d,
+                           s.ks, vec_ok ? 1 : 0, norms + c0, kpc);
+      }
+    }
     e = hipGetLastError();
     if (e != hipSuccess) break;
     QArgs rot = base, pro = base;
