@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--no-search", action="store_true", help="skip the search (top-k) measurement")
     ap.add_argument("--search-workload", default="search_b2")
     ap.add_argument("--no-split", action="store_true",
-                    help="skip the fractional-width line (2.5 and 3.5 bits, general kernels)")
+                    help="skip the fractional-width line (2.5 and 3.5 bits)")
     ap.add_argument("--no-attention", action="store_true",
                     help="skip the decode-attention and uncompressed-logits measurement")
     ap.add_argument("--no-general", action="store_true",
@@ -89,8 +89,8 @@ def kernel_models(w):
 
 
 def measured_profile(workload):
-    """From the committed rocprofv3 summary, for every kernel whose source is
-    unchanged since it was taken: HBM bytes per launch (FETCH_SIZE and
+    """From the committed rocprofv3 summary, for every kernel whose sources
+    are unchanged since it was taken: HBM bytes per launch (FETCH_SIZE and
     WRITE_SIZE, calibrated) and the matrix cores' busy share of its cycles."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
@@ -102,8 +102,10 @@ def measured_profile(workload):
             continue
         fields = dict(f.split("=", 1) for f in line.split()[1:])
         entry = line.split()[0]
-        src = os.path.join(ROOT, fields["source"])
-        if os.path.exists(src) and hashlib.sha1(open(src, "rb").read()).hexdigest() == fields["sha1"]:
+        # the kernel's sources (comma-separated), hashed in order as one text
+        srcs = [os.path.join(ROOT, f) for f in fields["source"].split(",")]
+        if all(os.path.exists(f) for f in srcs) and \
+                hashlib.sha1(b"".join(open(f, "rb").read() for f in srcs)).hexdigest() == fields["sha1"]:
             traffic[entry] = int(float(fields["fetch_bytes"]) + float(fields["write_bytes"]))
             if "mfma_busy_pct" in fields:
                 mfma_busy[entry] = float(fields["mfma_busy_pct"])
@@ -279,11 +281,11 @@ def dequant_prod_leg(w, h, packed, out, stream, reps=10):
 def split_leg(w, keys, queries, scores, khat, seed, stream, reps=3):
     """Fractional widths (tq_init_split) on the step's keys and queries: the
     first d/2 rotated coordinates with one more index bit, 2.5 and 3.5 bits
-    per coordinate with the sign bit.  Per width: tq_quantize (the general
-    matrix-core quantizer), tq_logits (the general float32 scorer: the
-    lookup-table scorer takes one width only) and tq_dequant_mse (matrix
-    cores), mean of `reps` calls after a warm-up, and the packed bytes per
-    key against the plain handles'."""
+    per coordinate with the sign bit.  Per width: tq_quantize (the d = 128
+    matrix-core quantizer, two waves on the finer level set), tq_logits (the
+    byte-table scorer, the two halves in separate byte phases) and
+    tq_dequant_mse (matrix cores), mean of `reps` calls after a warm-up,
+    and the packed bytes per key against the plain handles'."""
     import torch
 
     import vector_quantization_quantize_amd as tqm
