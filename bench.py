@@ -694,6 +694,31 @@ def main():
         del sets, run
         torch.cuda.empty_cache()
 
+    # a streaming floor for tq_logits in the same run and the same cold
+    # rotation: a plain device copy (the runtime's copy kernel) that moves as
+    # many bytes as tq_logits does (packed inputs read + scores written),
+    # half read and half written
+    moved = in_bytes["tq_logits"] + scores.numel() * scores.element_size()
+    half = (moved // 2 + 15) // 16 * 16
+    r = max(2, -(-(1 << 30) // half))
+    srcs = [torch.ones(half, dtype=torch.uint8, device="cuda") for _ in range(r)]
+    dsts = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(r)]
+    with torch.cuda.stream(stream):
+        for x, y in zip(srcs, dsts):  # warm-up round
+            y.copy_(x)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.cold_reps):
+            for x, y in zip(srcs, dsts):
+                y.copy_(x)
+        b.record(stream)
+        torch.cuda.synchronize()
+    floor_ms = a.elapsed_time(b) / (args.cold_reps * r)
+    floor_bytes = 2 * half
+    del srcs, dsts
+    torch.cuda.empty_cache()
+
     models = kernel_models(w)
     scored = w.groups * w.nq * w.n
     kern = {}
@@ -764,6 +789,12 @@ def main():
         "roofline_logits": roofline("tq_logits"),
         "roofline_by_kernel": {n: roofline(n) for n in names},
     }
+    floor_gbs = floor_bytes / (floor_ms * 1e-3) / 1e9
+    line["roofline_logits"]["stream_floor"] = {
+        "ms": round(floor_ms, 4), "GBps": round(floor_gbs, 1), "frac": round(floor_gbs / HBM_PEAK_GBS, 4),
+        "what": f"plain device copy of {half} bytes (reads {half}, writes {half}: the {floor_bytes} bytes "
+                f"tq_logits moves), cold rotation over {r} copies",
+        "logits_ms_over_floor_ms": round(cold["tq_logits"] / floor_ms, 3)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"], line["parity"] = cpu_baseline(
             w, keys_np, queries_np, min(args.cpu_groups, w.groups), args.seed,
