@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--no-search", action="store_true", help="skip the search (top-k) measurement")
     ap.add_argument("--search-workload", default="search_b2")
     ap.add_argument("--no-split", action="store_true",
-                    help="skip the fractional-width line (2.5 and 3.5 bits)")
+                    help="skip the fractional-width (2.5 and 3.5 bits) and polar-angle lines")
     ap.add_argument("--no-attention", action="store_true",
                     help="skip the decode-attention and uncompressed-logits measurement")
     ap.add_argument("--no-general", action="store_true",
@@ -319,6 +319,49 @@ def split_leg(w, keys, queries, scores, khat, seed, stream, reps=3):
             "keys_scored_per_s": w.groups * w.nq * w.n / (t_l * 1e-3)}
         del packed, lws
         tqm.tq_destroy(h)
+    return res
+
+
+def polar_leg(w, keys, queries, scores, khat, seed, stream, reps=3):
+    """The recursive polar-angle stage 1 (tq_init_polar) on the step's keys
+    and queries: tq_quantize, tq_logits and tq_dequant_mse per call (mean of
+    `reps` after a warm-up), against HBM with the plain handle's packed
+    bytes per key (the angle indices fill the same bit planes)."""
+    import torch
+
+    import vector_quantization_quantize_amd as tqm
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    h = tqm.tq_init_polar(w.d, w.bits, seed)
+    packed = tqm.empty_packed(h, w.total_keys)
+    lws = torch.empty(tqm.tq_logits_workspace_size(h, w.groups, w.nq) // 4 + 64, dtype=torch.float32,
+                      device="cuda")
+    t_q = timed(lambda: tqm.tq_quantize(h, keys, out=packed, stream=stream))
+    t_l = timed(lambda: tqm.tq_logits(h, queries, *packed, n=w.n, scores=scores, workspace=lws, stream=stream))
+    t_d = timed(lambda: tqm.tq_dequant_mse(h, packed[0], packed[2], khat=khat, stream=stream))
+    kb = h.layout.key_bytes
+    n = w.total_keys
+    qb = (w.d * keys.element_size() + kb) * n
+    lb = (kb + 4 * w.nq) * n
+    db = (kb - 4 * ((w.d + 31) // 32) - 4 + 4 * w.d) * n
+    res = {"bits": w.bits, "key_bytes": kb,
+           "tq_quantize_ms": round(t_q, 3), "quantize_hbm_frac": round(qb / (t_q * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "tq_logits_ms": round(t_l, 4), "logits_hbm_frac": round(lb / (t_l * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "keys_scored_per_s": w.groups * w.nq * w.n / (t_l * 1e-3),
+           "tq_dequant_mse_ms": round(t_d, 3), "dequant_hbm_frac": round(db / (t_d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "kernels": "float32 vector kernels (rotation, angle recursion, z_hat composition)"}
+    del packed, lws
+    tqm.tq_destroy(h)
     return res
 
 
@@ -806,6 +849,7 @@ def main():
         line["dequant_prod"] = dequant_prod_leg(w, h, packed, khat, stream)
     if not args.no_split:
         line["fractional_widths"] = split_leg(w, keys, queries, scores, khat, args.seed, stream)
+        line["polar"] = polar_leg(w, keys, queries, scores, khat, args.seed, stream)
     if not args.no_search:
         del keys, queries, packed, scores, ws, khat
         torch.cuda.empty_cache()

@@ -600,7 +600,10 @@ int run_logits(const tq_ctx* h, const float* queries, int64_t groups, int64_t nq
     e = tqdev::launch_query_prep(h, queries, groups * nq, vw, s);
     if (e != hipSuccess) return TQ_EHIP;
     e = sc == Scorer::kMfma    ? tqdev::launch_score_mfma(h, vw, groups, nq, codes, signs, norms, rnorms, n, scores, s)
-        : sc == Scorer::kPolar ? tqdev::launch_logits_polar(h, vw, groups, nq, codes, signs, norms, rnorms, n, scores, s)
+        : sc == Scorer::kPolar
+            ? (tqdev::logits_polar128_supported(h)
+                   ? tqdev::launch_logits_polar128(h, vw, groups, nq, codes, signs, norms, rnorms, n, scores, s)
+                   : tqdev::launch_logits_polar(h, vw, groups, nq, codes, signs, norms, rnorms, n, scores, s))
                                : tqdev::launch_logits_v1(h, vw, groups, nq, codes, signs, norms, rnorms, n, scores, s);
   }
   return e == hipSuccess ? TQ_OK : TQ_EHIP;

@@ -272,6 +272,12 @@ hipError_t launch_logits_polar(const tq_ctx* h, const float* vw, int64_t groups,
                                float* scores, hipStream_t stream);
 hipError_t launch_dequant_polar(const tq_ctx* h, const uint32_t* codes, const float* norms, int64_t n, float* khat,
                                 hipStream_t stream);
+// polar handles at d = 128 with one or two index bits per angle: the
+// byte-table decode scorer (logits_polar.hip)
+bool logits_polar128_supported(const tq_ctx* h);
+hipError_t launch_logits_polar128(const tq_ctx* h, const float* vw, int64_t groups, int64_t nq, const uint32_t* codes,
+                                  const uint32_t* signs, const float* norms, const float* rnorms, int64_t n,
+                                  float* scores, hipStream_t stream);
 // k_tilde = n Pi^T (c[idx] + rho sqrt(pi/2)/d G^T (2 beta - 1)); d = 128 on
 // the matrix cores (dequant_mfma.hip), float32 otherwise (kernels_ref.hip)
 hipError_t launch_dequant_prod_mfma128(const tq_ctx* h, const uint32_t* codes, const uint32_t* signs,
