@@ -380,7 +380,10 @@ attn_pv_kernel(const float* __restrict__ scores, int64_t nq, int64_t n, const ui
       const float w = __builtin_amdgcn_exp2f(x[k] - ((lane >> 5) ? lm[2 * k + 1] : lm[2 * k]));
       const bool use = tin && r < rows;
       lsum[k] += use ? w : 0.0f;
-      const float p = use ? w * nv : 0.0f;
+      float p = use ? w * nv : 0.0f;
+      // p rounded to float32 once: folded into the float16 conversion, hi
+      // would round the exact product and disagree with lo at a tie
+      asm volatile("" : "+v"(p));
       const _Float16 hi = static_cast<_Float16>(p);
       pa[wave][0][r][tl] = hi;
       pa[wave][1][r][tl] = static_cast<_Float16>(p - float(hi));
@@ -781,7 +784,8 @@ attn_fused_kernel(const float* __restrict__ queries, int quads, int64_t nq, int6
       // the hardware exp2 (a weight below 2^-126 of the reference flushes to 0)
       const float w = use ? __builtin_amdgcn_exp2f(x[q] - lm[q]) : 0.0f;
       lsum[q] += w;
-      const float p = w * nv;
+      float p = w * nv;
+      asm volatile("" : "+v"(p));  // one float32 rounding for both pieces (as above)
       const _Float16 hi = static_cast<_Float16>(p);
       sh.pa[wave][0][q][lane] = hi;
       sh.pa[wave][1][q][lane] = static_cast<_Float16>(p - float(hi));

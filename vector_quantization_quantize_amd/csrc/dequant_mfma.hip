@@ -356,6 +356,143 @@ hipError_t launch_split(const tq_ctx* h, const uint32_t* codes, const float* nor
   }
 }
 
+// ---------------------------------------------------------------------------
+// Polar-angle keys (d = 128, 1..4 index bits per angle): k_hat = n Pi^T z_hat
+// with z_hat composed from the angle levels ("TurboQuant tutorial",
+// Cartesian-to-polar part): z_hat_j is the product, over the 7 levels, of
+// the cos or sin (bit l - 1 of j) of the level's value on the path to j.
+// The same matrix-core product as above with the A operand computed instead
+// of looked up: lane l supplies, for key l % 32 and step s, coordinates
+// 8 o .. 8 o + 7 of the octet o = 2 s + l / 32.  The lane forms the path
+// products of the 8 level-4 nodes once per tile (levels 7..5), then per step
+// the octet's 7 angles top down (level 4 factor, level 3, two level-2 and
+// four level-1 angles), scaled by 2^12 and split into float16 hi and lo
+// pieces (22 bits); three passes as in the three-pass form.  Every wave
+// composes the whole key (they differ in output coordinates): the kernel is
+// bound by its writes, not by this arithmetic.
+// ---------------------------------------------------------------------------
+template <int B>
+__global__ void __launch_bounds__(kDqThreads, 2)
+dequant_polar128_kernel(const uint32_t* __restrict__ codes, const float* __restrict__ norms, int64_t n,
+                        const uint4* __restrict__ pi_frag, const float* __restrict__ ptab, float* __restrict__ khat,
+                        int64_t tiles) {
+  constexpr int L = 1 << B;
+  __shared__ float2 lt[7][L];    // (cos, sin) of each level's values
+  __shared__ float4 nrow[4][8];  // per wave: the tile's 32 norms
+  if (threadIdx.x < 7 * L) {
+    const int l = threadIdx.x / L, c = threadIdx.x % L;
+    lt[l][c] = make_float2(ptab[l * kPolarTab + 16 + c], ptab[l * kPolarTab + 32 + c]);
+  }
+  __syncthreads();
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, kl = lane & 31, g = lane >> 5;
+  f16x8 bpi[kSteps][2];
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) bpi[s][q] = __builtin_bit_cast(f16x8, pi_frag[((w * kSteps + s) * 2 + q) * 64 + lane]);
+  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    int64_t key = tile * 32 + kl;
+    key = key < n ? key : n - 1;
+    uint32_t pl[B][4];
+#pragma unroll
+    for (int p = 0; p < B; ++p) {
+      const uint4 u = *reinterpret_cast<const uint4*>(codes + (key * B + p) * 4);
+      pl[p][0] = u.x;
+      pl[p][1] = u.y;
+      pl[p][2] = u.z;
+      pl[p][3] = u.w;
+    }
+    const float nk = norms[key];
+    // index of the angle in slot 32 word + bit (word fixed, bit per lane)
+    auto code = [&](int word, uint32_t bit) __attribute__((always_inline)) {
+      uint32_t c = 0;
+#pragma unroll
+      for (int p = 0; p < B; ++p) c |= __builtin_amdgcn_ubfe(pl[p][word], bit, 1) << p;
+      return c;
+    };
+    // path products of the level-4 nodes, times 2^12: level 7 (slot 126),
+    // level 6 (124, 125), level 5 (120..123)
+    float p4[8];
+    {
+      const float2 c7 = lt[6][code(3, 30)];
+      const float p6[2] = {4096.0f * c7.x, 4096.0f * c7.y};
+#pragma unroll
+      for (int m6 = 0; m6 < 2; ++m6) {
+        const float2 c6 = lt[5][code(3, 28 + m6)];
+        const float p5[2] = {p6[m6] * c6.x, p6[m6] * c6.y};
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int m5 = 2 * m6 + i;
+          const float2 c5 = lt[4][code(3, 24 + m5)];
+          p4[2 * m5] = p5[i] * c5.x;
+          p4[2 * m5 + 1] = p5[i] * c5.y;
+        }
+      }
+    }
+    f32x16 acc = {};
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      // octet o = 2 s + g: its level-4 parent is node s (slot 112 + s), the
+      // octet itself level-3 node o (slot 96 + o), its quads level-2 nodes
+      // 2 o, 2 o + 1 (slots 64 + 2 o ..), its pairs level-1 nodes 4 o .. 4 o + 3
+      const float2 c4 = lt[3][code(3, 16 + s)];
+      const float po = p4[s] * (g ? c4.y : c4.x);
+      const float2 c3 = lt[2][code(3, uint32_t(2 * s) + g)];
+      const float pq[2] = {po * c3.x, po * c3.y};
+      float pp[4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float2 c2 = lt[1][code(2, uint32_t(4 * s + h) + 2 * g)];
+        pp[2 * h] = pq[h] * c2.x;
+        pp[2 * h + 1] = pq[h] * c2.y;
+      }
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float2 c1 = lt[0][code(s >> 2, uint32_t(8 * (s & 3) + i) + 4 * g)];
+        x[2 * i] = pp[i] * c1.x;
+        x[2 * i + 1] = pp[i] * c1.y;
+      }
+      f16x8 ahi, alo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        // x rounded to float32 once and opaque: otherwise the compiler folds
+        // the product into the float16 conversion of hi (one rounding of the
+        // exact product) while lo subtracts hi from the float32 product, and
+        // at a rounding tie the two pieces disagree by a float16 ulp
+        float xe = x[e];
+        asm volatile("" : "+v"(xe));
+        const _Float16 hv = static_cast<_Float16>(xe);
+        ahi[e] = hv;
+        alo[e] = static_cast<_Float16>(xe - static_cast<float>(hv));
+      }
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, bpi[s][0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, bpi[s][1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, bpi[s][0], acc, 0, 0, 0);
+    }
+    // lane holds coordinate 32 w + kl of keys 8 (r / 4) + 4 g + r % 4
+    reinterpret_cast<float*>(nrow[w])[kl] = nk * kOutScale;
+    float o[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = nrow[w][2 * q + g];
+      o[4 * q] = v.x * acc[4 * q];
+      o[4 * q + 1] = v.y * acc[4 * q + 1];
+      o[4 * q + 2] = v.z * acc[4 * q + 2];
+      o[4 * q + 3] = v.w * acc[4 * q + 3];
+    }
+    // rows past row n - 1 of the last tile repeat it
+    float* out = khat + tile * 32 * 128 + 32 * w + kl;
+    const int64_t left = n - 1 - tile * 32;
+    const int last = left < 31 ? static_cast<int>(left) : 31;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kr = 8 * (r >> 2) + 4 * g + (r & 3);
+      __builtin_nontemporal_store(o[r], out + (kr < last ? kr : last) * 128);
+    }
+  }
+}
+
 }  // namespace
 
 bool dequant_mfma128_supported(const tq_ctx* h) {
@@ -398,6 +535,31 @@ hipError_t launch_dequant_prod_mfma128(const tq_ctx* h, const uint32_t* codes, c
     case 4: return launch_b<4, false, true>(h, codes, norms, n, out, stream, signs, rnorms);
     default: return hipErrorInvalidValue;
   }
+}
+
+bool dequant_polar128_supported(const tq_ctx* h) {
+  return h->polar && h->d == 128 && h->words == 4 && h->polar_levels == 7 && h->code_bits >= 1 &&
+         h->code_bits <= 4 && h->d_dq_frag && h->d_polar_tab && !force_reference_kernels();
+}
+
+hipError_t launch_dequant_polar128(const tq_ctx* h, const uint32_t* codes, const float* norms, int64_t n, float* khat,
+                                   hipStream_t stream) {
+  const int64_t tiles = (n + 31) / 32;
+  const int64_t slots = 2 * static_cast<int64_t>(h->cus);
+  const int64_t blocks = tiles < slots ? tiles : slots;
+  const uint4* frag = reinterpret_cast<const uint4*>(h->d_dq_frag);
+  switch (h->code_bits) {
+    case 1: hipLaunchKernelGGL(dequant_polar128_kernel<1>, dim3(uint32_t(blocks)), dim3(kDqThreads), 0, stream, codes,
+                               norms, n, frag, h->d_polar_tab, khat, tiles); break;
+    case 2: hipLaunchKernelGGL(dequant_polar128_kernel<2>, dim3(uint32_t(blocks)), dim3(kDqThreads), 0, stream, codes,
+                               norms, n, frag, h->d_polar_tab, khat, tiles); break;
+    case 3: hipLaunchKernelGGL(dequant_polar128_kernel<3>, dim3(uint32_t(blocks)), dim3(kDqThreads), 0, stream, codes,
+                               norms, n, frag, h->d_polar_tab, khat, tiles); break;
+    case 4: hipLaunchKernelGGL(dequant_polar128_kernel<4>, dim3(uint32_t(blocks)), dim3(kDqThreads), 0, stream, codes,
+                               norms, n, frag, h->d_polar_tab, khat, tiles); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace tqdev

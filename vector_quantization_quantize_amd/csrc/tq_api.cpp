@@ -890,7 +890,9 @@ int tq_dequant_mse(tq_handle h, const uint32_t* codes, const float* norms, int64
   if (!codes || !norms || !khat) return TQ_EINVAL;
   if (check_device(h) != TQ_OK) return TQ_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = h->polar ? tqdev::launch_dequant_polar(h, codes, norms, n, khat, s)
+  const hipError_t e = h->polar ? (tqdev::dequant_polar128_supported(h)
+                                       ? tqdev::launch_dequant_polar128(h, codes, norms, n, khat, s)
+                                       : tqdev::launch_dequant_polar(h, codes, norms, n, khat, s))
                        : (!tqdev::force_reference_kernels() && tqdev::dequant_mfma128_supported(h) &&
                           dequant_rows_aligned(h, codes))
                            ? tqdev::launch_dequant_mfma128(h, codes, norms, n, khat, s)

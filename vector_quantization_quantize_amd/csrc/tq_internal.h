@@ -275,6 +275,10 @@ hipError_t launch_dequant_polar(const tq_ctx* h, const uint32_t* codes, const fl
 // polar handles at d = 128 with one or two index bits per angle: the
 // byte-table decode scorer (logits_polar.hip)
 bool logits_polar128_supported(const tq_ctx* h);
+// ... and its stage-1 reconstruction on the matrix cores (dequant_mfma.hip)
+bool dequant_polar128_supported(const tq_ctx* h);
+hipError_t launch_dequant_polar128(const tq_ctx* h, const uint32_t* codes, const float* norms, int64_t n, float* khat,
+                                   hipStream_t stream);
 hipError_t launch_logits_polar128(const tq_ctx* h, const float* vw, int64_t groups, int64_t nq, const uint32_t* codes,
                                   const uint32_t* signs, const float* norms, const float* rnorms, int64_t n,
                                   float* scores, hipStream_t stream);
