@@ -359,7 +359,9 @@ def polar_leg(w, keys, queries, scores, khat, seed, stream, reps=3):
            "tq_logits_ms": round(t_l, 4), "logits_hbm_frac": round(lb / (t_l * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
            "keys_scored_per_s": w.groups * w.nq * w.n / (t_l * 1e-3),
            "tq_dequant_mse_ms": round(t_d, 3), "dequant_hbm_frac": round(db / (t_d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-           "kernels": "float32 vector kernels (rotation, angle recursion, z_hat composition)"}
+           "kernels": "d = 128: quantize_polar128_kernel (matrix-core rotation and projection, angle "
+                      "recursion in registers), logits_polar128_kernel (byte tables), dequant_polar128_kernel "
+                      "(matrix cores); other d: float32 vector kernels"}
     del packed, lws
     tqm.tq_destroy(h)
     return res

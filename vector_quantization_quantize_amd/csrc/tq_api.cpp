@@ -564,7 +564,9 @@ int tq_quantize(tq_handle h, const void* keys, int32_t key_dtype, int64_t n, int
   // d >= 16: the tiled matrix-core kernels; smaller d: float32 kernels
   hipError_t e;
   if (h->polar)
-    e = tqdev::launch_quantize_polar(h, keys, key_dtype, n, ldk, codes, signs, norms, rnorms, s);
+    e = tqdev::quantize_polar128_supported(h, keys, key_dtype, ldk)
+            ? tqdev::launch_quantize_polar128(h, keys, key_dtype, n, ldk, codes, signs, norms, rnorms, s)
+            : tqdev::launch_quantize_polar(h, keys, key_dtype, n, ldk, codes, signs, norms, rnorms, s);
   else if (tqdev::force_reference_kernels())
     e = tqdev::launch_quantize_v1(h, keys, key_dtype, n, ldk, codes, signs, norms, rnorms, s);
   else if (tqdev::quantize_mfma128_supported(h, keys, key_dtype, ldk, codes, signs, norms, rnorms))

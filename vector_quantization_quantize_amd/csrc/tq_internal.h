@@ -277,6 +277,13 @@ hipError_t launch_dequant_polar(const tq_ctx* h, const uint32_t* codes, const fl
 bool logits_polar128_supported(const tq_ctx* h);
 // ... and its stage-1 reconstruction on the matrix cores (dequant_mfma.hip)
 bool dequant_polar128_supported(const tq_ctx* h);
+// polar handles at d = 128 with a seeded (float16-exact) G, float32 or
+// bf16 keys in 16-byte aligned rows: the matrix-core quantizer
+// (quantize_polar128.hip)
+bool quantize_polar128_supported(const tq_ctx* h, const void* keys, int key_dtype, int64_t ldk);
+hipError_t launch_quantize_polar128(const tq_ctx* h, const void* keys, int key_dtype, int64_t n, int64_t ldk,
+                                    uint32_t* codes, uint32_t* signs, float* norms, float* rnorms,
+                                    hipStream_t stream);
 hipError_t launch_dequant_polar128(const tq_ctx* h, const uint32_t* codes, const float* norms, int64_t n, float* khat,
                                    hipStream_t stream);
 hipError_t launch_logits_polar128(const tq_ctx* h, const float* vw, int64_t groups, int64_t nq, const uint32_t* codes,
