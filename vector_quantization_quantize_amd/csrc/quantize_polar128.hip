@@ -19,7 +19,8 @@
 //   2. rotate: wave w computes output coordinates 32 w .. 32 w + 31 of the
 //      tile from 2^12 Pi (two float16 pieces, in registers for the whole
 //      run) and the key pieces, hi hi + hi lo + lo hi per K step of a
-//      32 x 32 x 16 MFMA; z = acc / (2^12 2^s n) goes to LDS;
+//      32 x 32 x 16 MFMA (bf16 keys have no lo piece: 2 passes); z = acc /
+//      (2^12 2^s n) goes to LDS;
 //   3. encode: 8 lanes per key, lane t owning coordinates 16 t .. 16 t + 15
 //      (levels 1 - 4 inside the lane, levels 5 - 7 across the key's lanes by
 //      shuffles); z_hat top-down, each coordinate's product taken in the
@@ -49,7 +50,6 @@ constexpr int kPT = 256;         // threads per block (4 waves)
 constexpr int kKP = kD + 8;      // halves per staged row (spreads the rows over the LDS banks)
 constexpr int kZP = kD + 4;      // floats per z row
 constexpr int kLevels = 7;       // log2 d
-constexpr float kTwoPi = 6.2831853071795865f;
 
 __device__ __forceinline__ float key_scale128(float nk) {
   if (!(nk > 0.0f)) return 1.0f;
@@ -58,13 +58,38 @@ __device__ __forceinline__ float key_scale128(float nk) {
   return ldexpf(1.0f, 14 - e);
 }
 
-// #{t_i <= a} over the L - 1 thresholds of one level (LDS table)
+// An angle's index #{t_i <= psi}, psi = atan2(y, x), needs no atan2.
+// Levels 2 .. 7: x, y >= 0, so psi and t_i lie in [0, pi / 2], where tan
+// increases: t_i <= psi iff tan t_i <= y / x.  u = y rcp(x) is within
+// 2^-22 of y / x relative, which moves the angle by at most 2^-23
+// sin(2 psi), inside the 1e-6 decision window.  x = 0 < y gives u = +inf
+// (psi = pi / 2, above every threshold); x = y = 0 gives NaN, below every
+// threshold like atan2(0, 0) = 0.
 template <int B>
-__device__ __forceinline__ int angle_code(float a, const float* t) {
-  int c = 0;
+__device__ __forceinline__ int code_quarter(float x, float y, const float* tt) {
+  const float u = y * __builtin_amdgcn_rcpf(x);
+  int k = 0;
 #pragma unroll
-  for (int i = 0; i + 1 < (1 << B); ++i) c += a >= t[i] ? 1 : 0;
-  return c;
+  for (int i = 0; i + 1 < (1 << B); ++i) k += u >= tt[i] ? 1 : 0;
+  return k;
+}
+
+// Level 1: psi in [0, 2 pi).  The sign of sin(psi - t_i) is that of
+// y cos t_i - x sin t_i (off only within about 2^-22 rad of t_i).  psi lies
+// in [pi, 2 pi) (the upper half) when y < 0 or y = 0 > x; a threshold in
+// the other half than psi is below it iff psi is in the upper half, one in
+// the same half is decided by the sign (the difference of two angles of one
+// half is in (-pi, pi)).  atan2(0, 0) = 0 lies below every threshold.
+template <int B>
+__device__ __forceinline__ int code_circle(float x, float y, const float* ct, const float* st, const int* th) {
+  const bool hp = y < 0.0f || (y == 0.0f && x < 0.0f);
+  int k = 0;
+#pragma unroll
+  for (int i = 0; i + 1 < (1 << B); ++i) {
+    const bool ge = fmaf(y, ct[i], -(x * st[i])) >= 0.0f;
+    k += (hp == (th[i] != 0) ? ge : hp) ? 1 : 0;
+  }
+  return x == 0.0f && y == 0.0f ? 0 : k;
 }
 
 // bit q of each code, placed at consecutive bits from 0
@@ -86,9 +111,25 @@ quantize_polar128_kernel(const void* __restrict__ keys, int64_t n, int64_t ldk,
   __shared__ __align__(16) _Float16 sR[2][kTK][kKP];  // residual pieces
   __shared__ __align__(16) float sZ[kTK][kZP];
   __shared__ float sTab[kLevels * kPolarTab];          // per level: thresholds, cos, sin (16 each)
+  __shared__ float sCT[16], sST[16];                    // level 1: cos and sin of each threshold
+  __shared__ int sTH[16];                               // level 1: threshold in [pi, 2 pi)
+  __shared__ float sTT[kLevels][16];                    // levels 2 .. 7: tan of each threshold
   __shared__ float sInv[kTK];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, kl = lane & 31, g = lane >> 5;
   for (int i = tid; i < kLevels * kPolarTab; i += kPT) sTab[i] = ptab[i];
+  if (tid < kLevels * 16) {
+    const int l = tid >> 4, i = tid & 15;
+    const float t = ptab[l * kPolarTab + i];  // +inf past the level's L - 1 thresholds (never used)
+    if (l == 0) {
+      float sn = 0.0f, cs = 0.0f;
+      if (t < 8.0f) sincosf(t, &sn, &cs);
+      sCT[i] = cs;
+      sST[i] = sn;
+      sTH[i] = t >= 3.14159265358979f ? 1 : 0;
+    } else {
+      sTT[l][i] = t < 8.0f ? tanf(t) : INFINITY;
+    }
+  }
 
   // operand fragments of this wave's 32 output rows: K step s, lane l holds
   // row l % 32, halves 8 (l / 32) .. + 7 of the step's 16, per piece
@@ -150,18 +191,22 @@ quantize_polar128_kernel(const void* __restrict__ keys, int64_t n, int64_t ldk,
         sInv[sk] = nk > 0.0f ? 1.0f / (4096.0f * sc * nk) : 0.0f;
         if (k0 + sk < n) norms[k0 + sk] = nk;
       }
+      // a bf16 element times 2^s is a float16 number unless below 2^-38 n
+      // (float16 subnormals): its lo piece is zero and is not kept
       f16x8 hi[2], lo[2];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float v = x[e] * sc;
         const _Float16 h = static_cast<_Float16>(v);
         hi[e >> 3][e & 7] = h;
-        lo[e >> 3][e & 7] = static_cast<_Float16>(v - static_cast<float>(h));
+        if constexpr (KT == TQ_F32) lo[e >> 3][e & 7] = static_cast<_Float16>(v - static_cast<float>(h));
       }
       *reinterpret_cast<f16x8*>(&sK[0][sk][16 * st]) = hi[0];
       *reinterpret_cast<f16x8*>(&sK[0][sk][16 * st + 8]) = hi[1];
-      *reinterpret_cast<f16x8*>(&sK[1][sk][16 * st]) = lo[0];
-      *reinterpret_cast<f16x8*>(&sK[1][sk][16 * st + 8]) = lo[1];
+      if constexpr (KT == TQ_F32) {
+        *reinterpret_cast<f16x8*>(&sK[1][sk][16 * st]) = lo[0];
+        *reinterpret_cast<f16x8*>(&sK[1][sk][16 * st + 8]) = lo[1];
+      }
     }
     __syncthreads();
     // ---- 2. rotate: element e of lane l is coordinate 32 w + 16 g + e of key kl ----
@@ -170,9 +215,11 @@ quantize_polar128_kernel(const void* __restrict__ keys, int64_t n, int64_t ldk,
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const f16x8 bh = *reinterpret_cast<const f16x8*>(&sK[0][kl][16 * s + 8 * g]);
-        const f16x8 bl = *reinterpret_cast<const f16x8*>(&sK[1][kl][16 * s + 8 * g]);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa_h[s], bh, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa_h[s], bl, acc, 0, 0, 0);
+        if constexpr (KT == TQ_F32) {
+          const f16x8 bl = *reinterpret_cast<const f16x8*>(&sK[1][kl][16 * s + 8 * g]);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa_h[s], bl, acc, 0, 0, 0);
+        }
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa_l[s], bh, acc, 0, 0, 0);
       }
       const float inv = sInv[kl];
@@ -202,10 +249,8 @@ quantize_polar128_kernel(const void* __restrict__ keys, int64_t n, int64_t ldk,
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         const float x = z[2 * m], y = z[2 * m + 1];
-        float a = atan2f(y, x);
-        a = a < 0.0f ? a + kTwoPi : a;
-        c1[m] = angle_code<B>(a, T);
-        r1[m] = sqrtf(fmaf(x, x, y * y));
+        c1[m] = code_circle<B>(x, y, sCT, sST, sTH);
+        r1[m] = __builtin_amdgcn_sqrtf(fmaf(x, x, y * y));
       }
       // levels 2 - 4 inside the lane
       int c2[4], c3[2], c4[1];
@@ -213,30 +258,30 @@ quantize_polar128_kernel(const void* __restrict__ keys, int64_t n, int64_t ldk,
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const float x = r1[2 * m], y = r1[2 * m + 1];
-        c2[m] = angle_code<B>(atan2f(y, x), T + kPolarTab);
-        r2[m] = sqrtf(fmaf(x, x, y * y));
+        c2[m] = code_quarter<B>(x, y, sTT[1]);
+        r2[m] = __builtin_amdgcn_sqrtf(fmaf(x, x, y * y));
       }
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const float x = r2[2 * m], y = r2[2 * m + 1];
-        c3[m] = angle_code<B>(atan2f(y, x), T + 2 * kPolarTab);
-        r3[m] = sqrtf(fmaf(x, x, y * y));
+        c3[m] = code_quarter<B>(x, y, sTT[2]);
+        r3[m] = __builtin_amdgcn_sqrtf(fmaf(x, x, y * y));
       }
       {
         const float x = r3[0], y = r3[1];
-        c4[0] = angle_code<B>(atan2f(y, x), T + 3 * kPolarTab);
-        r4 = sqrtf(fmaf(x, x, y * y));
+        c4[0] = code_quarter<B>(x, y, sTT[3]);
+        r4 = __builtin_amdgcn_sqrtf(fmaf(x, x, y * y));
       }
       // levels 5 - 7 across the key's lanes: level l angle i sits in lane
       // et = i (lanes past the level's count compute unused values)
       float x5 = sh(r4, 2 * et), y5 = sh(r4, 2 * et + 1);
-      const int c5 = angle_code<B>(atan2f(y5, x5), T + 4 * kPolarTab);
-      const float r5 = sqrtf(fmaf(x5, x5, y5 * y5));
+      const int c5 = code_quarter<B>(x5, y5, sTT[4]);
+      const float r5 = __builtin_amdgcn_sqrtf(fmaf(x5, x5, y5 * y5));
       const float x6 = sh(r5, 2 * et), y6 = sh(r5, 2 * et + 1);
-      const int c6 = angle_code<B>(atan2f(y6, x6), T + 5 * kPolarTab);
-      const float r6 = sqrtf(fmaf(x6, x6, y6 * y6));
+      const int c6 = code_quarter<B>(x6, y6, sTT[5]);
+      const float r6 = __builtin_amdgcn_sqrtf(fmaf(x6, x6, y6 * y6));
       const float x7 = sh(r6, 0), y7 = sh(r6, 1);
-      const int c7 = angle_code<B>(atan2f(y7, x7), T + 6 * kPolarTab);
+      const int c7 = code_quarter<B>(x7, y7, sTT[6]);
       // z_hat: the lane's block is level-4 node et; its path from the top
       // takes the level-7 angle, level-6 angle et / 4 and level-5 angle
       // et / 2 (cos for an even child, sin for an odd one)
