@@ -150,27 +150,40 @@ quantize_polar128_kernel(const void* __restrict__ keys, int64_t n, int64_t ldk,
   auto sh = [&](float v, int t) { return __shfl(v, eb + 8 * (t & 7)); };
   auto shi = [&](int v, int t) { return __shfl(v, eb + 8 * (t & 7)); };
 
+  // this thread's 16 elements of its key row in tile t (rows past n repeat
+  // row n - 1), as loaded: the next tile's are in flight while this one is
+  // processed
+  constexpr int kRaw = KT == TQ_F32 ? 4 : 2;
+  struct Raw {
+    uint4 v[kRaw];
+  };
+  auto fetch = [&](int64_t t) {
+    const int64_t key = t * kTK + sk < n ? t * kTK + sk : n - 1;
+    const char* row = static_cast<const char*>(keys) + (key * ldk + 16 * st) * (KT == TQ_F32 ? 4 : 2);
+    Raw r;
+#pragma unroll
+    for (int q = 0; q < kRaw; ++q) r.v[q] = reinterpret_cast<const uint4*>(row)[q];
+    return r;
+  };
+  Raw cur = fetch(blockIdx.x < tiles ? blockIdx.x : 0);
   for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
     const int64_t k0 = tile * kTK;
+    const Raw nxt = fetch(tile + gridDim.x < tiles ? tile + gridDim.x : tile);
     // ---- 1. stage ----
     {
-      const int64_t key = k0 + sk < n ? k0 + sk : n - 1;  // rows past n repeat row n - 1
       float x[16];
       if constexpr (KT == TQ_F32) {
-        const float4* row = reinterpret_cast<const float4*>(static_cast<const float*>(keys) + key * ldk + 16 * st);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float4 v = row[q];
-          x[4 * q] = v.x;
-          x[4 * q + 1] = v.y;
-          x[4 * q + 2] = v.z;
-          x[4 * q + 3] = v.w;
+          x[4 * q] = __uint_as_float(cur.v[q].x);
+          x[4 * q + 1] = __uint_as_float(cur.v[q].y);
+          x[4 * q + 2] = __uint_as_float(cur.v[q].z);
+          x[4 * q + 3] = __uint_as_float(cur.v[q].w);
         }
       } else {
-        const uint4* row = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(keys) + key * ldk + 16 * st);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          const uint4 v = row[q];
+          const uint4 v = cur.v[q];
           const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -371,6 +384,7 @@ quantize_polar128_kernel(const void* __restrict__ keys, int64_t n, int64_t ldk,
       const uint32_t other = __shfl_xor(hw, 32);
       if (g == 0 && k0 + kl < n) signs[(k0 + kl) * 4 + w] = hw | (other << 16);
     }
+    cur = nxt;
   }
 }
 
