@@ -367,9 +367,9 @@ hipError_t launch_split(const tq_ctx* h, const uint32_t* codes, const float* nor
 // products of the 8 level-4 nodes once per tile (levels 7..5), then per step
 // the octet's 7 angles top down (level 4 factor, level 3, two level-2 and
 // four level-1 angles), scaled by 2^12 and split into float16 hi and lo
-// pieces (22 bits); three passes as in the three-pass form.  Every wave
-// composes the whole key (they differ in output coordinates): the kernel is
-// bound by its writes, not by this arithmetic.
+// pieces (22 bits); three passes as in the three-pass form.  The waves
+// differ only in output coordinates, so each composes a quarter of the K
+// steps and shares them through LDS.
 // ---------------------------------------------------------------------------
 template <int B>
 __global__ void __launch_bounds__(kDqThreads, 2)
@@ -379,6 +379,8 @@ dequant_polar128_kernel(const uint32_t* __restrict__ codes, const float* __restr
   constexpr int L = 1 << B;
   __shared__ float2 lt[7][L];    // (cos, sin) of each level's values
   __shared__ float4 nrow[4][8];  // per wave: the tile's 32 norms
+  __shared__ f16x8 sa[2][kSteps][2][64];  // [buffer][K step][piece][lane]: the A operand of a tile
+  int buf = 0;
   if (threadIdx.x < 7 * L) {
     const int l = threadIdx.x / L, c = threadIdx.x % L;
     lt[l][c] = make_float2(ptab[l * kPolarTab + 16 + c], ptab[l * kPolarTab + 32 + c]);
@@ -410,33 +412,25 @@ dequant_polar128_kernel(const uint32_t* __restrict__ codes, const float* __restr
       for (int p = 0; p < B; ++p) c |= __builtin_amdgcn_ubfe(pl[p][word], bit, 1) << p;
       return c;
     };
-    // path products of the level-4 nodes, times 2^12: level 7 (slot 126),
-    // level 6 (124, 125), level 5 (120..123)
-    float p4[8];
-    {
-      const float2 c7 = lt[6][code(3, 30)];
-      const float p6[2] = {4096.0f * c7.x, 4096.0f * c7.y};
-#pragma unroll
-      for (int m6 = 0; m6 < 2; ++m6) {
-        const float2 c6 = lt[5][code(3, 28 + m6)];
-        const float p5[2] = {p6[m6] * c6.x, p6[m6] * c6.y};
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int m5 = 2 * m6 + i;
-          const float2 c5 = lt[4][code(3, 24 + m5)];
-          p4[2 * m5] = p5[i] * c5.x;
-          p4[2 * m5 + 1] = p5[i] * c5.y;
-        }
-      }
-    }
-    f32x16 acc = {};
+    // Wave w composes K steps 2 w and 2 w + 1 of the A operand (its lanes'
+    // keys, octets o = 2 s + g) into the tile's LDS buffer; after one
+    // barrier every wave multiplies all 8 steps by its own Pi rows.  Path
+    // products of the level-4 node s, times 2^12: level 7 (slot 126), level
+    // 6 (124 + s / 4), level 5 (120 + s / 2).
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
+      if ((s >> 1) != w) continue;  // (wave-uniform)
+      const float2 c7 = lt[6][code(3, 30)];
+      const float2 c6 = lt[5][code(3, 28 + (s >> 2))];
+      const float2 c5 = lt[4][code(3, 24 + (s >> 1))];
+      const float p6 = 4096.0f * (((s >> 2) & 1) ? c7.y : c7.x);
+      const float p5 = p6 * (((s >> 1) & 1) ? c6.y : c6.x);
+      const float p4 = p5 * ((s & 1) ? c5.y : c5.x);
       // octet o = 2 s + g: its level-4 parent is node s (slot 112 + s), the
       // octet itself level-3 node o (slot 96 + o), its quads level-2 nodes
       // 2 o, 2 o + 1 (slots 64 + 2 o ..), its pairs level-1 nodes 4 o .. 4 o + 3
       const float2 c4 = lt[3][code(3, 16 + s)];
-      const float po = p4[s] * (g ? c4.y : c4.x);
+      const float po = p4 * (g ? c4.y : c4.x);
       const float2 c3 = lt[2][code(3, uint32_t(2 * s) + g)];
       const float pq[2] = {po * c3.x, po * c3.y};
       float pp[4];
@@ -466,10 +460,22 @@ dequant_polar128_kernel(const uint32_t* __restrict__ codes, const float* __restr
         ahi[e] = hv;
         alo[e] = static_cast<_Float16>(xe - static_cast<float>(hv));
       }
+      sa[buf][s][0][lane] = ahi;
+      sa[buf][s][1][lane] = alo;
+    }
+    __syncthreads();
+    f32x16 acc = {};
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      const f16x8 ahi = sa[buf][s][0][lane], alo = sa[buf][s][1][lane];
       acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, bpi[s][0], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, bpi[s][1], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, bpi[s][0], acc, 0, 0, 0);
     }
+    // buffers alternate by tile: a wave writes one while a slower wave may
+    // still read the other, and reaches the one it read before only after
+    // the next tile's barrier
+    buf ^= 1;
     // lane holds coordinate 32 w + kl of keys 8 (r / 4) + 4 g + r % 4
     reinterpret_cast<float*>(nrow[w])[kl] = nk * kOutScale;
     float o[16];
