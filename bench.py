@@ -471,8 +471,9 @@ def quantize_general_leg(seed, reps=5):
     ms per call (mean of `reps` after a warm-up), Mkeys/s, HBM GB/s of keys
     in + packed out, useful matrix flops (4 d^2 per key) and raw matrix
     flops (3 passes of 2 x 128-row tiles x K for Z = Pi K, 2 for P = G R
-    with the seeded float16-exact G) against the bf16
-    matrix-core peak."""
+    with the seeded float16-exact G; rows of 32 per bit word instead of 128
+    per tile where the one-kernel quantizer runs, 96 < d <= 208 with d a
+    multiple of 8) against the bf16 matrix-core peak."""
     import numpy as np
     import torch
 
@@ -519,9 +520,11 @@ def quantize_general_leg(seed, reps=5):
         nct = (dpm + 127) // 128
         packed = 4 * (w.bits - 1) * words + 4 * words + 8
         useful = 4.0 * d * d * n / (ms * 1e-3) / 1e12
-        raw = 2.0 * 128 * nct * (3 * kp + 2 * dpm) * n / (ms * 1e-3) / 1e12
+        rows = dpm if 96 < d <= 208 and d % 8 == 0 else 128 * nct
+        raw = 2.0 * rows * (3 * kp + 2 * dpm) * n / (ms * 1e-3) / 1e12
         gbs = (4 * d + packed) * n / (ms * 1e-3) / 1e9
         res[name] = {"keys": n, "d": d, "bits": w.bits, "ms": round(ms, 3), "Mkeys_per_s": round(n / ms / 1e3, 1),
+                     "kernel": "one-kernel quantizer" if rows == dpm else "tiled general quantizer",
                      "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                      "useful_TFLOPs": round(useful, 1), "useful_mfma_frac": round(useful / BF16_MFMA_PEAK_TFLOPS, 4),
                      "raw_TFLOPs": round(raw, 1), "raw_mfma_frac": round(raw / BF16_MFMA_PEAK_TFLOPS, 4)}

@@ -156,3 +156,57 @@ def test_logits_two_tier_key_split(env):
                         norms[sl].astype(np.float64), rnorms[sl].astype(np.float64))
         bad, worst = parity.score_violations(s[g], ref, queries[g], norms[sl])
         assert bad == 0, (g, worst)
+
+
+@pytest.mark.parametrize("form", ["fused", "tiled"])
+@pytest.mark.parametrize("d,bits,groups,n,key_dtype", [
+    (104, 3, 1, 1000, "f32"), (128, 2, 2, 4097, "f32"), (136, 4, 1, 65, "bf16"), (168, 5, 1, 333, "f32"),
+    (200, 2, 1, 3001, "f32"), (200, 5, 2, 777, "bf16"), (208, 3, 1, 2049, "f32")])
+def test_one_kernel_quantizer(env, form, d, bits, groups, n, key_dtype):
+    """Plain handles at 96 < d <= 208 (d a multiple of 8): the one-kernel
+    matrix-core quantizer, and the tiled general quantizer it replaces there
+    (TQ_QUANTIZER=tiled), on ragged key counts, every bit width, a zero key
+    and norms spread over many binades; codes, signs, norms, rho, scores and
+    reconstructions against the oracle."""
+    torch, tqm, _ = env
+    _announce(f"{form} quantizer d={d} bits={bits} groups={groups} n={n} {key_dtype}")
+    rs = np.random.default_rng(d * 7 + bits + n)
+    keys = rs.standard_normal((groups * n, d)) * np.exp(2.0 * rs.standard_normal((groups * n, 1)))
+    keys[min(5, groups * n - 1)] = 0.0
+    if key_dtype == "bf16":
+        keys = torch.tensor(keys, dtype=torch.float32).bfloat16().float().numpy()
+    queries = rs.standard_normal((groups, 3, d)).astype(np.float32)
+    old = os.environ.get("TQ_QUANTIZER")
+    if form == "tiled":
+        os.environ["TQ_QUANTIZER"] = "tiled"
+    try:
+        rep = check_full(env, d, bits, keys.astype(np.float32) if key_dtype == "f32" else keys, queries,
+                         key_dtype=key_dtype, seed=bits + 1)
+    finally:
+        if old is None:
+            os.environ.pop("TQ_QUANTIZER", None)
+        else:
+            os.environ["TQ_QUANTIZER"] = old
+    print("mismatches", rep.code_mismatch, rep.sign_mismatch, "cascade", rep.cascade_keys)
+
+
+def test_one_kernel_quantizer_strided_rows(env):
+    """Rows strided by ldk > d (16-byte aligned): the one-kernel quantizer
+    reads only the first d elements of each row."""
+    torch, tqm, _ = env
+    from oracle import parity
+    from tests.test_gpu_parity import _params
+    _announce("one-kernel quantizer, strided rows d=200 ldk=212")
+    d, ldk, n, bits = 200, 212, 999, 3
+    rs = np.random.default_rng(4242)
+    keys = rs.standard_normal((n, d)).astype(np.float32)
+    big = np.full((n, ldk), np.nan, dtype=np.float32)   # padding past d must never be read
+    big[:, :d] = keys
+    h = tqm.tq_init(d, bits, 3)
+    pr = _params(d, bits, 3)
+    kd = torch.from_numpy(big).cuda()
+    codes, signs, norms, rnorms = tqm.tq_quantize(h, kd[:, :d])
+    torch.cuda.synchronize()
+    qz = tq.quantize(pr, keys.astype(np.float64))
+    rep = parity.compare_quantize(pr, qz, _cpu(codes), _cpu(signs), _cpu(norms), _cpu(rnorms))
+    assert rep.ok(), rep

@@ -312,6 +312,11 @@ bool tqdev::force_reference_kernels() {
   return v && std::strcmp(v, "ref") == 0;
 }
 
+bool tqdev::force_tiled_quantizer() {
+  const char* v = std::getenv("TQ_QUANTIZER");
+  return v && std::strcmp(v, "tiled") == 0;
+}
+
 namespace {
 
 Scorer pick_scorer(const tq_ctx* h, int64_t nq) {
@@ -571,6 +576,8 @@ int tq_quantize(tq_handle h, const void* keys, int32_t key_dtype, int64_t n, int
     e = tqdev::launch_quantize_v1(h, keys, key_dtype, n, ldk, codes, signs, norms, rnorms, s);
   else if (tqdev::quantize_mfma128_supported(h, keys, key_dtype, ldk, codes, signs, norms, rnorms))
     e = tqdev::launch_quantize_mfma128(h, keys, n, ldk, codes, signs, norms, rnorms, s);
+  else if (tqdev::quantize_fused_supported(h, keys, key_dtype, ldk) && !tqdev::force_tiled_quantizer())
+    e = tqdev::launch_quantize_fused(h, keys, key_dtype, n, ldk, codes, signs, norms, rnorms, s);
   else if (tqdev::quantize_gemm_supported(h))
     e = tqdev::launch_quantize_gemm(h, keys, key_dtype, n, ldk, codes, signs, norms, rnorms, s);
   else
