@@ -520,11 +520,12 @@ def quantize_general_leg(seed, reps=5):
         nct = (dpm + 127) // 128
         packed = 4 * (w.bits - 1) * words + 4 * words + 8
         useful = 4.0 * d * d * n / (ms * 1e-3) / 1e12
-        rows = dpm if 96 < d <= 208 and d % 8 == 0 else 128 * nct
+        one_kernel = 96 < d <= 208 and d % 8 == 0
+        rows = dpm if one_kernel else 128 * nct
         raw = 2.0 * rows * (3 * kp + 2 * dpm) * n / (ms * 1e-3) / 1e12
         gbs = (4 * d + packed) * n / (ms * 1e-3) / 1e9
         res[name] = {"keys": n, "d": d, "bits": w.bits, "ms": round(ms, 3), "Mkeys_per_s": round(n / ms / 1e3, 1),
-                     "kernel": "one-kernel quantizer" if rows == dpm else "tiled general quantizer",
+                     "kernel": "one-kernel quantizer" if one_kernel else "tiled general quantizer",
                      "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                      "useful_TFLOPs": round(useful, 1), "useful_mfma_frac": round(useful / BF16_MFMA_PEAK_TFLOPS, 4),
                      "raw_TFLOPs": round(raw, 1), "raw_mfma_frac": round(raw / BF16_MFMA_PEAK_TFLOPS, 4)}
