@@ -47,7 +47,7 @@ def _cpu(t):
 @pytest.mark.parametrize("d,bits,groups,n,nq,key_dtype", [
     (2, 3, 1, 33, 1, "f32"), (4, 3, 1, 50, 2, "f32"), (16, 2, 2, 300, 3, "f32"), (64, 4, 1, 500, 5, "f32"),
     (128, 3, 2, 1000, 4, "bf16"), (128, 2, 3, 777, 5, "f32"), (128, 3, 1, 65, 3, "bf16"), (128, 4, 1, 300, 6, "f32"),
-    (128, 5, 1, 999, 4, "bf16"), (128, 2, 1, 20001, 2, "bf16"),
+    (128, 5, 1, 999, 4, "bf16"), (128, 2, 1, 20001, 2, "bf16"), (128, 3, 1, 1, 2, "f32"), (128, 4, 2, 31, 3, "bf16"),
     (256, 5, 1, 257, 20, "f32"), (1024, 3, 1, 100, 4, "f32")])
 def test_polar_matches_oracle(env, d, bits, groups, n, nq, key_dtype):
     torch, tqm = env
