@@ -12,10 +12,10 @@
 // larger d take the tiled general quantizer).  The block walks tiles of 32
 // keys:
 //   1. stage: 8 threads per key load its row in 8-element chunks
-//      (coalesced), sum the squares (per-thread runs, then a 3-level tree),
-//      and park the row in LDS; then every thread converts a share of the
-//      tile to float16 pieces hi = f16(2^s k), lo = f16(2^s k - hi) with
-//      2^s n in [2^13, 2^14) (bf16 keys: one exact piece);
+//      (coalesced), sum the squares (per-thread runs, then a 3-level tree)
+//      and store their chunks as float16 pieces hi = f16(2^s k), lo =
+//      f16(2^s k - hi) with 2^s n in [2^13, 2^14) (bf16 keys: one exact
+//      piece);
 //   2. rotate: 32 x 32 x 16 MFMA, hi hi + hi lo + lo hi per K step (bf16:
 //      2 passes), each run of 8 K steps in fresh accumulators added into
 //      float32 running sums; then per element z = acc / (2^12 2^s n),
@@ -43,7 +43,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kTK = 32;                 // keys per tile
 constexpr int kMaxW = 7;                // words (waves) at d <= 208
 constexpr int kRowH = 32 * kMaxW + 8;   // halves per staged row (padding spreads the rows over the LDS banks)
-constexpr int kRawF = 208 + 4;          // floats per parked row
 constexpr int kChunkSteps = 8;          // K steps per fresh accumulator
 
 __device__ __forceinline__ float key_scale_f(float nk) {
@@ -63,11 +62,10 @@ quantize_fused_kernel(const void* __restrict__ keys, int64_t n, int64_t ldk, int
                       float* __restrict__ rnorms) {
   constexpr int kPieces = KT == TQ_F32 ? 2 : 1;
   constexpr int KS2 = 2 * ((KS + 1) / 2);
-  __shared__ __align__(16) float sRaw[kTK][kRawF];         // the tile's rows as loaded
   __shared__ __align__(16) _Float16 sK[kPieces][kTK][kRowH];  // key pieces
   __shared__ __align__(16) _Float16 sR[2][kTK][kRowH];     // residual pieces
   __shared__ float sRho[kMaxW][kTK];                       // rho^2 share of each wave
-  __shared__ float sInv[kTK], sScl[kTK];
+  __shared__ float sInv[kTK];
   __shared__ float sC[kMaxLevels], sT[kMaxLevels];  // levels; thresholds (+inf past L - 2)
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, kl = lane & 31, g = lane >> 5;
   const int nthreads = 64 * W;
@@ -101,70 +99,62 @@ quantize_fused_kernel(const void* __restrict__ keys, int64_t n, int64_t ldk, int
 
   for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
     const int64_t k0 = tile * kTK;
-    // ---- 1. stage: park the rows, norms ----
+    // ---- 1. stage: norms, then the key pieces (zeros past d up to the K steps) ----
     if (stager) {
       const int64_t key = k0 + sk < n ? k0 + sk : n - 1;  // rows past n repeat row n - 1
       const char* rowp = static_cast<const char*>(keys) + key * ldk * kEl;
+      float x[4][8];
       float ss = 0.0f;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int c = st + 8 * m;
         if (c < chunks) {
-          float x[8];
           if constexpr (KT == TQ_F32) {
             const float4 a = reinterpret_cast<const float4*>(rowp)[2 * c];
             const float4 b = reinterpret_cast<const float4*>(rowp)[2 * c + 1];
-            x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-            x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+            x[m][0] = a.x; x[m][1] = a.y; x[m][2] = a.z; x[m][3] = a.w;
+            x[m][4] = b.x; x[m][5] = b.y; x[m][6] = b.z; x[m][7] = b.w;
           } else {
             const uint4 u = reinterpret_cast<const uint4*>(rowp)[c];
             const uint32_t v[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              x[2 * i] = __uint_as_float(v[i] << 16);
-              x[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+              x[m][2 * i] = __uint_as_float(v[i] << 16);
+              x[m][2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
             }
           }
+        } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
-          *reinterpret_cast<float4*>(&sRaw[sk][8 * c]) = make_float4(x[0], x[1], x[2], x[3]);
-          *reinterpret_cast<float4*>(&sRaw[sk][8 * c + 4]) = make_float4(x[4], x[5], x[6], x[7]);
+          for (int e = 0; e < 8; ++e) x[m][e] = 0.0f;
         }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf(x[m][e], x[m][e], ss);
       }
       ss += __shfl_xor(ss, 1);
       ss += __shfl_xor(ss, 2);
       ss += __shfl_xor(ss, 4);
       const float nk = sqrtf(ss);
+      const float sc = key_scale_f(nk);
       if (st == 0) {
-        const float sc = key_scale_f(nk);
-        sScl[sk] = sc;
         sInv[sk] = nk > 0.0f ? 1.0f / (4096.0f * sc * nk) : 0.0f;
         if (k0 + sk < n) norms[k0 + sk] = nk;
       }
-    }
-    __syncthreads();
-    // ---- 1b. pieces: item (key, chunk), zeros past d up to the K steps ----
-    for (int it = tid; it < kTK * 2 * KS; it += nthreads) {
-      const int key = it / (2 * KS), c = it - key * (2 * KS);
-      f16x8 hi, lo;
-      if (c < chunks) {
-        const float sc = sScl[key];
-        const float4 a = *reinterpret_cast<const float4*>(&sRaw[key][8 * c]);
-        const float4 b = *reinterpret_cast<const float4*>(&sRaw[key][8 * c + 4]);
-        const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float v = x[e] * sc;
-          const _Float16 h = static_cast<_Float16>(v);
-          hi[e] = h;
-          lo[e] = static_cast<_Float16>(v - static_cast<float>(h));
+      for (int m = 0; m < 4; ++m) {
+        const int c = st + 8 * m;
+        if (c < 2 * KS) {
+          f16x8 hi, lo;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float v = x[m][e] * sc;
+            const _Float16 h = static_cast<_Float16>(v);
+            hi[e] = h;
+            lo[e] = static_cast<_Float16>(v - static_cast<float>(h));
+          }
+          *reinterpret_cast<f16x8*>(&sK[0][sk][8 * c]) = hi;
+          if constexpr (kPieces == 2) *reinterpret_cast<f16x8*>(&sK[kPieces - 1][sk][8 * c]) = lo;
         }
-      } else {
-        hi = f16x8{};
-        lo = f16x8{};
       }
-      *reinterpret_cast<f16x8*>(&sK[0][key][8 * c]) = hi;
-      if constexpr (kPieces == 2) *reinterpret_cast<f16x8*>(&sK[kPieces - 1][key][8 * c]) = lo;
     }
     __syncthreads();
     // ---- 2. rotate: element e of lane l is coordinate 32 w + 16 g + e of key kl ----
