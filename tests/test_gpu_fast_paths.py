@@ -211,3 +211,30 @@ def test_one_kernel_quantizer_strided_rows(env):
     qz = tq.quantize(pr, keys.astype(np.float64))
     rep = parity.compare_quantize(pr, qz, _cpu(codes), _cpu(signs), _cpu(norms), _cpu(rnorms))
     assert rep.ok(), rep
+
+
+@pytest.mark.parametrize("kind,d,bits,key_dtype", [("plain", 200, 3, "f32"), ("plain", 128, 4, "bf16"),
+                                                   ("polar", 128, 3, "bf16"), ("polar", 128, 2, "f32")])
+def test_new_quantizers_power_of_two_rescaling(env, kind, d, bits, key_dtype):
+    """The one-kernel and polar-angle quantizers split 2^s k with 2^s n in
+    [2^13, 2^14) and square and sum the key in float32, all exact under a
+    power-of-two rescaling that stays in the normal range: keys times
+    2^40 and 2^-40 give the same codes, signs and rho bit for bit and norms
+    times exactly 2^40 and 2^-40."""
+    torch, tqm, _ = env
+    _announce(f"{kind} quantizer rescaling d={d} bits={bits} {key_dtype}")
+    rs = np.random.default_rng(99 + d + bits)
+    keys = rs.standard_normal((1500, d)).astype(np.float32)
+    keys[7] = 0.0
+    h = tqm.tq_init_polar(d, bits, 4) if kind == "polar" else tqm.tq_init(d, bits, 4)
+    dt = torch.bfloat16 if key_dtype == "bf16" else torch.float32
+    base = torch.from_numpy(keys).cuda().to(dt)
+    out0 = [_cpu(t) for t in tqm.tq_quantize(h, base)]
+    for e in (40, -40):
+        scaled = base * (2.0 ** e)          # exact: a power of two, no overflow or subnormal
+        out = [_cpu(t) for t in tqm.tq_quantize(h, scaled)]
+        torch.cuda.synchronize()
+        assert np.array_equal(out[0], out0[0]), "codes"
+        assert np.array_equal(out[1], out0[1]), "signs"
+        assert np.array_equal(out[2], out0[2] * np.float32(2.0 ** e)), "norms"
+        assert np.array_equal(out[3], out0[3]), "rho"
