@@ -19,7 +19,8 @@
 //   2. rotate: 32 x 32 x 16 MFMA, hi hi + hi lo + lo hi per K step (bf16:
 //      2 passes), each run of 8 K steps in fresh accumulators added into
 //      float32 running sums; then per element z = acc / (2^12 2^s n),
-//      bucketize against the thresholds, code bits (16 per lane, the other
+//      bucketize against the thresholds (the middle one, then the half
+//      that z falls in), code bits (16 per lane, the other
 //      16 of the word from lane l ^ 32), r = z - c[idx] and its rho^2
 //      share, r to LDS as float16 pieces of 2^12 r;
 //   3. project: p = (2^10 G) r_hi + (2^10 G) r_lo, sign bits per word;
@@ -73,7 +74,7 @@ quantize_fused_kernel(const void* __restrict__ keys, int64_t n, int64_t ldk, int
     sC[tid] = cb.c[tid];
     sT[tid] = cb.t[tid];
   }
-  const int nthr = cb.levels - 1;
+  const int half = cb.levels / 2;  // M: levels per half of the sorted set
 
   // this wave's operand rows: coordinate tile w / 4, rows 32 (w % 4) + l % 32
   const int ct = w >> 2, row = 32 * (w & 3) + kl;
@@ -183,11 +184,16 @@ quantize_fused_kernel(const void* __restrict__ keys, int64_t n, int64_t ldk, int
       for (int e = 0; e < 16; ++e) {
         const bool valid = c0 + e < d;
         const float z = run[e] * inv;
-        int idx = 0;
+        // idx = #{t_i <= z} over the sorted thresholds, split at the middle
+        // one: z >= t[M - 1] lies at or above t[0 .. M - 1] and only
+        // t[M .. L - 2] remain to count, else below t[M - 1 ..] and only
+        // t[0 .. M - 2] do (M - 1 compares instead of L - 1, same result)
+        const bool upper = z >= sT[half - 1];
+        int idx = upper ? half : 0;
 #pragma unroll
-        for (int q = 0; q < kMaxLevels - 1; ++q) {
-          if (q >= nthr) break;  // (uniform)
-          idx += z >= sT[q] ? 1 : 0;
+        for (int q = 0; q < kMaxLevels / 2 - 1; ++q) {
+          if (q >= half - 1) break;  // (uniform)
+          idx += z >= (upper ? sT[half + q] : sT[q]) ? 1 : 0;
         }
         const float r = valid ? z - sC[idx] : 0.0f;
         idx = valid ? idx : 0;
