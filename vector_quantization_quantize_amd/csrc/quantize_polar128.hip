@@ -65,12 +65,16 @@ __device__ __forceinline__ float key_scale128(float nk) {
 // sin(2 psi), inside the 1e-6 decision window.  x = 0 < y gives u = +inf
 // (psi = pi / 2, above every threshold); x = y = 0 gives NaN, below every
 // threshold like atan2(0, 0) = 0.
+// The count over the sorted tangents splits at the middle one (u >= tt[M -
+// 1] is at or above tt[0 .. M - 1]), so M - 1 more compares finish it.
 template <int B>
 __device__ __forceinline__ int code_quarter(float x, float y, const float* tt) {
+  constexpr int M = 1 << (B - 1);
   const float u = y * __builtin_amdgcn_rcpf(x);
-  int k = 0;
+  const bool up = u >= tt[M - 1];
+  int k = up ? M : 0;
 #pragma unroll
-  for (int i = 0; i + 1 < (1 << B); ++i) k += u >= tt[i] ? 1 : 0;
+  for (int i = 0; i + 1 < M; ++i) k += u >= (up ? tt[M + i] : tt[i]) ? 1 : 0;
   return k;
 }
 
