@@ -472,7 +472,7 @@ def quantize_general_leg(seed, reps=5):
     in + packed out, useful matrix flops (4 d^2 per key) and raw matrix
     flops (3 passes of 2 x 128-row tiles x K for Z = Pi K, 2 for P = G R
     with the seeded float16-exact G; rows of 32 per bit word instead of 128
-    per tile where the one-kernel quantizer runs, 96 < d <= 208 with d a
+    per tile where the one-kernel quantizer runs, 16 <= d <= 208 with d a
     multiple of 8) against the bf16 matrix-core peak."""
     import numpy as np
     import torch
@@ -520,7 +520,7 @@ def quantize_general_leg(seed, reps=5):
         nct = (dpm + 127) // 128
         packed = 4 * (w.bits - 1) * words + 4 * words + 8
         useful = 4.0 * d * d * n / (ms * 1e-3) / 1e12
-        one_kernel = 96 < d <= 208 and d % 8 == 0
+        one_kernel = 16 <= d <= 208 and d % 8 == 0
         rows = dpm if one_kernel else 128 * nct
         raw = 2.0 * rows * (3 * kp + 2 * dpm) * n / (ms * 1e-3) / 1e12
         gbs = (4 * d + packed) * n / (ms * 1e-3) / 1e9

@@ -162,9 +162,10 @@ def test_logits_two_tier_key_split(env):
 @pytest.mark.parametrize("d,bits,groups,n,key_dtype", [
     (104, 3, 1, 1000, "f32"), (128, 2, 2, 4097, "f32"), (136, 4, 1, 65, "bf16"), (168, 5, 1, 333, "f32"),
     (200, 2, 1, 3001, "f32"), (200, 5, 2, 777, "bf16"), (208, 3, 1, 2049, "f32"), (200, 3, 1, 1, "f32"),
-    (128, 2, 1, 31, "bf16")])
+    (128, 2, 1, 31, "bf16"), (16, 2, 1, 100, "f32"), (24, 3, 2, 77, "bf16"), (64, 4, 1, 1000, "f32"),
+    (96, 5, 1, 333, "bf16")])
 def test_one_kernel_quantizer(env, form, d, bits, groups, n, key_dtype):
-    """Plain handles at 96 < d <= 208 (d a multiple of 8): the one-kernel
+    """Plain handles at 16 <= d <= 208 (d a multiple of 8): the one-kernel
     matrix-core quantizer, and the tiled general quantizer it replaces there
     (TQ_QUANTIZER=tiled), on ragged key counts, every bit width, a zero key
     and norms spread over many binades; codes, signs, norms, rho, scores and

@@ -1,12 +1,13 @@
-// One-kernel matrix-core quantizer for 96 < d <= 208 (d a multiple of 8),
+// One-kernel matrix-core quantizer for 16 <= d <= 208 (d a multiple of 8),
 // float32 or bf16 keys, plain handles with a seeded (float16-exact) G.
 //
 // Stages ("TurboQuant tutorial" (gitcode.csdn.net), PolarQuant and QJL
 // sections; "TurboQuant digest" (juejin.cn) section 2):
 //   n = ||k||, z = Pi k / n, idx_j = #{t_i <= z_j}, r = z - c[idx],
 //   rho = ||r||, beta = [G r > 0], packed into bit planes.
-// A block holds W = ceil(d / 32) waves, wave w owning bit word w (output
-// coordinates 32 w .. 32 w + 31) of both products; its rows of 2^12 Pi (two
+// A block holds W = ceil(d / 32) multiplying waves (and at least 4 waves,
+// which all stage), wave w owning bit word w (output coordinates
+// 32 w .. 32 w + 31) of both products; its rows of 2^12 Pi (two
 // float16 pieces) and of 2^10 G (one piece) stay in registers for the whole
 // run (at d <= 208 the fragments of both fit the 256 registers of a wave;
 // larger d take the tiled general quantizer).  The block walks tiles of 32
@@ -69,7 +70,6 @@ quantize_fused_kernel(const void* __restrict__ keys, int64_t n, int64_t ldk, int
   __shared__ float sInv[kTK];
   __shared__ float sC[kMaxLevels], sT[kMaxLevels];  // levels; thresholds (+inf past L - 2)
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, kl = lane & 31, g = lane >> 5;
-  const int nthreads = 64 * W;
   if (tid < kMaxLevels) {
     sC[tid] = cb.c[tid];
     sT[tid] = cb.t[tid];
@@ -159,7 +159,8 @@ quantize_fused_kernel(const void* __restrict__ keys, int64_t n, int64_t ldk, int
     }
     __syncthreads();
     // ---- 2. rotate: element e of lane l is coordinate 32 w + 16 g + e of key kl ----
-    {
+    const bool mult = w < W;  // (wave-uniform) waves past the words only stage
+    if (mult) {
       f32x16 acc = {}, run = {};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
@@ -225,7 +226,7 @@ quantize_fused_kernel(const void* __restrict__ keys, int64_t n, int64_t ldk, int
     }
     __syncthreads();
     // ---- 3. project ----
-    {
+    if (mult) {
       f32x16 acc = {};
 #pragma unroll
       for (int s = 0; s < KS2; ++s) {
@@ -254,9 +255,10 @@ template <int KS>
 hipError_t launch_ks(const tq_ctx* h, const void* keys, int key_dtype, int64_t n, int64_t ldk, uint32_t* codes,
                      uint32_t* signs, float* norms, float* rnorms, hipStream_t stream) {
   const int64_t tiles = (n + kTK - 1) / kTK;
-  const int64_t slots = static_cast<int64_t>(h->cus);
+  // 4 waves and 60 KB of LDS (d <= 128): two blocks share a CU
+  const int64_t slots = static_cast<int64_t>(h->cus) * (h->words <= 4 ? 2 : 1);
   const dim3 grid{static_cast<uint32_t>(tiles < slots ? tiles : slots)};
-  const dim3 block{static_cast<uint32_t>(64 * h->words)};
+  const dim3 block{static_cast<uint32_t>(64 * (h->words > 4 ? h->words : 4))};
   if (key_dtype == TQ_F32)
     hipLaunchKernelGGL((quantize_fused_kernel<TQ_F32, KS>), grid, block, 0, stream, keys, n, ldk, h->d, h->words,
                        h->code_bits, h->d_qpi_tiles, h->d_qg_tiles, h->cb, codes, signs, norms, rnorms);
@@ -270,7 +272,7 @@ hipError_t launch_ks(const tq_ctx* h, const void* keys, int key_dtype, int64_t n
 
 bool quantize_fused_supported(const tq_ctx* h, const void* keys, int key_dtype, int64_t ldk) {
   const int elem = key_dtype == TQ_F32 ? 4 : 2;
-  return !h->polar && !h->hadamard && h->hi == 0 && h->g_f16 && h->d > 96 && h->d <= 208 && h->d % 8 == 0 &&
+  return !h->polar && !h->hadamard && h->hi == 0 && h->g_f16 && h->d >= 16 && h->d <= 208 && h->d % 8 == 0 &&
          h->d_qpi_tiles && h->d_qg_tiles && h->code_bits >= 1 && h->code_bits <= 4 && !force_reference_kernels() &&
          (key_dtype == TQ_F32 || key_dtype == TQ_BF16) && (reinterpret_cast<uintptr_t>(keys) & 15u) == 0 &&
          (ldk * elem) % 16 == 0;
@@ -281,6 +283,12 @@ hipError_t launch_quantize_fused(const tq_ctx* h, const void* keys, int key_dtyp
   switch ((h->d + 15) / 16) {
 #define TQ_QF(KS) \
   case KS: return launch_ks<KS>(h, keys, key_dtype, n, ldk, codes, signs, norms, rnorms, stream);
+    TQ_QF(1)
+    TQ_QF(2)
+    TQ_QF(3)
+    TQ_QF(4)
+    TQ_QF(5)
+    TQ_QF(6)
     TQ_QF(7)
     TQ_QF(8)
     TQ_QF(9)

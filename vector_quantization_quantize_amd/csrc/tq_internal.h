@@ -161,7 +161,7 @@ hipError_t launch_dequant_mfma128(const tq_ctx* h, const uint32_t* codes, const 
 
 // TQ_KERNELS=ref selects the straightforward kernels everywhere (A/B checks)
 bool force_reference_kernels();
-// TQ_QUANTIZER=tiled: plain handles at 96 < d <= 208 take the tiled general
+// TQ_QUANTIZER=tiled: plain handles at 16 <= d <= 208 take the tiled general
 // quantizer instead of the one-kernel form (A/B comparisons, tests of both)
 bool force_tiled_quantizer();
 
@@ -280,7 +280,7 @@ hipError_t launch_dequant_polar(const tq_ctx* h, const uint32_t* codes, const fl
 bool logits_polar128_supported(const tq_ctx* h);
 // ... and its stage-1 reconstruction on the matrix cores (dequant_mfma.hip)
 bool dequant_polar128_supported(const tq_ctx* h);
-// plain handles with 96 < d <= 208, d % 8 == 0, a seeded G, float32 or
+// plain handles with 16 <= d <= 208, d % 8 == 0, a seeded G, float32 or
 // bf16 keys in 16-byte aligned rows: the one-kernel matrix-core quantizer
 // (quantize_fused.hip)
 bool quantize_fused_supported(const tq_ctx* h, const void* keys, int key_dtype, int64_t ldk);
